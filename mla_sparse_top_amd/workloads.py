@@ -1,0 +1,284 @@
+"""Seeded synthetic inputs for sparse MLA attention over a paged latent KV cache.
+
+This module only draws random inputs and lays them out the way the operation consumes them
+("DeepSeek V3/V2 Sparse Flash Attention with Quantization", input/output table: query_nope,
+query_rope, key_nope_2d, key_rope_2d, k_nope_scales, topk_indices, block_table, kv_act_seqs).
+It contains no attention arithmetic. Its one transformation is the INT8 quantisation of the
+cache's nope part, one FP32 scale per 128-element group. That is the cache *write* side: the
+same page's "INT8 quantisation rule" note says the scale comes from the group's absolute
+maximum and the codes span [-128, 127].
+
+All floating data are returned as raw bit patterns (bf16 as uint16), so the GPU path and the
+CPU oracle consume identical bytes.
+
+Draws use ``torch.Generator`` on the CPU. Normals are drawn as float32 and rounded to bfloat16
+by torch (round to nearest even). Distinct top-k indices come from ``torch.randperm``.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+KV_LORA_RANK = 512
+ROPE_DIM = 64
+BLOCK_SIZE = 128
+QUANT_GROUP = 128
+N_GROUPS = KV_LORA_RANK // QUANT_GROUP
+BF16_QNAN = 0x7FC0
+
+# Rows are drawn in chunks so that a pool of a million rows never holds more than one chunk
+# of float32 normals at once.
+_ROW_CHUNK = 1 << 16
+
+
+@dataclasses.dataclass
+class SfaInputs:
+    """One problem instance in the layouts of the operation's input table.
+
+    Shapes (T = batch * s1 query tokens, H = n_q heads, R = num_cache_rows):
+      query_nope     uint16 (T*H, 512)  bf16 bits, row = (b*s1 + s)*H + h
+      query_rope     uint16 (T*H, 64)   bf16 bits
+      key_nope       uint16 (R, 512) bf16 bits, or int8 (R, 512) when kv_dtype == "int8"
+      key_rope       uint16 (R, 64)     bf16 bits
+      k_nope_scales  float32 (R, 4) for int8, else None
+      topk_indices   int32 (T, topk), -1 = padding
+      block_table    int32 (batch, max_blocks_per_batch)
+      kv_act_seqs    int32 (batch,)
+    """
+
+    batch: int
+    s1: int
+    n_q: int
+    topk: int
+    kv_dtype: str
+    query_nope: np.ndarray
+    query_rope: np.ndarray
+    key_nope: np.ndarray
+    key_rope: np.ndarray
+    k_nope_scales: Optional[np.ndarray]
+    topk_indices: np.ndarray
+    block_table: np.ndarray
+    kv_act_seqs: np.ndarray
+    softmax_scale: float
+    poison_blocks: tuple
+    name: str = ""
+
+    @property
+    def n_tokens(self) -> int:
+        return self.batch * self.s1
+
+    @property
+    def num_cache_rows(self) -> int:
+        return int(self.key_rope.shape[0])
+
+    @property
+    def max_blocks_per_batch(self) -> int:
+        return int(self.block_table.shape[1])
+
+    def valid_counts(self) -> np.ndarray:
+        """Number of slots per token that name a position inside its batch's live range."""
+        b = np.arange(self.n_tokens) // self.s1
+        act = self.kv_act_seqs[b][:, None]
+        idx = self.topk_indices
+        return ((idx >= 0) & (idx < act)).sum(axis=1)
+
+
+def _bf16_bits(x: torch.Tensor) -> np.ndarray:
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _normal_bf16(g: torch.Generator, rows: int, cols: int) -> np.ndarray:
+    out = np.empty((rows, cols), dtype=np.uint16)
+    for r0 in range(0, rows, _ROW_CHUNK):
+        r1 = min(rows, r0 + _ROW_CHUNK)
+        out[r0:r1] = _bf16_bits(torch.randn(r1 - r0, cols, generator=g, dtype=torch.float32))
+    return out
+
+
+def quantize_int8_groups(nope_bf16_bits: np.ndarray):
+    """Cache-write quantisation of bf16 latents: per 128-element group, scale = absmax / 127
+    (float32) and code = clamp(round_half_even(x / scale), -128, 127). All-zero groups get
+    scale 0 and code 0."""
+    x = (nope_bf16_bits.astype(np.uint32) << 16).view(np.float32).reshape(-1, N_GROUPS, QUANT_GROUP)
+    absmax = np.abs(x).max(axis=2)
+    scale = (absmax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint(x / safe[:, :, None])
+    q = np.clip(q, -128, 127).astype(np.int8)
+    q[scale == 0] = 0
+    return q.reshape(-1, KV_LORA_RANK), scale
+
+
+def generate(
+    *,
+    batch: int,
+    s1: int,
+    n_q: int,
+    act_seqs: Sequence[int],
+    topk: int,
+    kv_dtype: str = "bf16",
+    seed: int = 0,
+    max_blocks_per_batch: Optional[int] = None,
+    index_mode: str = "uniform",
+    softmax_scale: Optional[float] = None,
+    extra_pool_blocks: int = 0,
+    fixed_block_table: Optional[Sequence[Sequence[int]]] = None,
+    pool_blocks: Optional[int] = None,
+    name: str = "",
+) -> SfaInputs:
+    """Draw one instance.
+
+    index_mode:
+      "uniform" -- every token of batch b takes min(topk, act[b]) distinct positions drawn
+                   uniformly from [0, act[b]), in random order, then -1 padding up to topk.
+      "causal"  -- token s of batch b sits at position p = act[b] - s1 + s and draws
+                   min(topk, p+1) distinct positions from [0, p], then -1 padding.
+
+    The physical pool holds the blocks the batches use (in random order), any extra unused
+    blocks, and one trailing poison block. block_table entries past a batch's last live block
+    point at the poison block. The poison block, and every row of a live block at or past
+    act[b], is filled with NaN (bf16) or NaN scales (int8), so reading one shows up as NaN.
+    """
+    assert kv_dtype in ("bf16", "int8")
+    assert index_mode in ("uniform", "causal")
+    act = [int(a) for a in act_seqs]
+    assert len(act) == batch
+    g = torch.Generator().manual_seed(int(seed))
+    nblk = [math.ceil(a / BLOCK_SIZE) for a in act]
+    mb = max_blocks_per_batch if max_blocks_per_batch is not None else max(1, max(nblk) if nblk else 1)
+    assert all(n <= mb for n in nblk), "kv_act_seqs exceeds max_blocks_per_batch * block_size"
+
+    if fixed_block_table is not None:
+        bt = np.array(fixed_block_table, dtype=np.int32).reshape(batch, mb)
+        n_pool = int(pool_blocks) if pool_blocks is not None else int(bt.max()) + 2
+        used = set(int(v) for b in range(batch) for v in bt[b, : nblk[b]])
+        poison = tuple(sorted(set(range(n_pool)) - used))
+        assert poison, "a fixed block table needs at least one spare block for poison"
+        for b in range(batch):
+            bt[b, nblk[b]:] = poison[-1]
+    else:
+        n_used = sum(nblk)
+        n_pool = n_used + int(extra_pool_blocks) + 1
+        poison = (n_pool - 1,)
+        perm = torch.randperm(n_used + int(extra_pool_blocks), generator=g).numpy().astype(np.int32)
+        bt = np.full((batch, mb), poison[0], dtype=np.int32)
+        off = 0
+        for b in range(batch):
+            bt[b, : nblk[b]] = perm[off: off + nblk[b]]
+            off += nblk[b]
+
+    rows = n_pool * BLOCK_SIZE
+    nope = _normal_bf16(g, rows, KV_LORA_RANK)
+    rope = _normal_bf16(g, rows, ROPE_DIM)
+
+    # Rows nobody may read: the poison blocks, and rows of live blocks past the live length.
+    dead = np.zeros(rows, dtype=bool)
+    for p in poison:
+        dead[p * BLOCK_SIZE:(p + 1) * BLOCK_SIZE] = True
+    for b in range(batch):
+        tail = nblk[b] * BLOCK_SIZE - act[b]
+        if tail > 0:
+            last = int(bt[b, nblk[b] - 1])
+            dead[last * BLOCK_SIZE + (BLOCK_SIZE - tail):(last + 1) * BLOCK_SIZE] = True
+
+    scales = None
+    if kv_dtype == "int8":
+        q, scales = quantize_int8_groups(nope)
+        scales[dead] = np.float32(np.nan)
+        q[dead] = 0
+        key_nope = q
+    else:
+        nope[dead] = BF16_QNAN
+        key_nope = nope
+    rope[dead] = BF16_QNAN
+
+    t_count = batch * s1
+    qn = _normal_bf16(g, t_count * n_q, KV_LORA_RANK)
+    qr = _normal_bf16(g, t_count * n_q, ROPE_DIM)
+
+    idx = np.full((t_count, topk), -1, dtype=np.int32)
+    for t in range(t_count):
+        b, s = divmod(t, s1)
+        if index_mode == "uniform":
+            span = act[b]
+        else:
+            span = max(0, min(act[b], act[b] - s1 + s + 1))
+        k = min(topk, span)
+        if k > 0:
+            idx[t, :k] = torch.randperm(span, generator=g)[:k].numpy().astype(np.int32)
+
+    if softmax_scale is None:
+        softmax_scale = float(np.float32(1.0 / math.sqrt(KV_LORA_RANK + ROPE_DIM)))
+    else:
+        softmax_scale = float(np.float32(softmax_scale))
+
+    return SfaInputs(
+        batch=batch, s1=s1, n_q=n_q, topk=topk, kv_dtype=kv_dtype,
+        query_nope=qn, query_rope=qr, key_nope=key_nope, key_rope=rope, k_nope_scales=scales,
+        topk_indices=idx, block_table=bt, kv_act_seqs=np.array(act, dtype=np.int32),
+        softmax_scale=softmax_scale, poison_blocks=tuple(int(p) for p in poison), name=name,
+    )
+
+
+# ----------------------------------------------------------------------------------------
+# The named workloads. Shapes follow the decode case the pages time their attention ops on
+# (64 sequences, two query tokens per step, 8K of cache) and the page-2 test table.
+# ----------------------------------------------------------------------------------------
+
+def tiny(seed: int = 0) -> SfaInputs:
+    """B=1, S1=1, 16 heads, 256 live positions in 2 blocks mapped [1, 0] over a 4-block pool,
+    64 distinct indices."""
+    return generate(batch=1, s1=1, n_q=16, act_seqs=[256], topk=64, seed=seed,
+                    fixed_block_table=[[1, 0]], pool_blocks=4, name="tiny_b1_s1_h16_topk64")
+
+
+def decode_mtp1(seed: int = 0, kv_dtype: str = "bf16") -> SfaInputs:
+    """B=64, S1=2, 128 heads, 8192 live positions each, 4096-block pool in random order,
+    2048 distinct indices per token."""
+    return generate(batch=64, s1=2, n_q=128, act_seqs=[8192] * 64, topk=2048, kv_dtype=kv_dtype,
+                    seed=seed, name=f"decode_b64_s2_h128_kv8192_topk2048_{kv_dtype}")
+
+
+def decode_mtp1_int8(seed: int = 0) -> SfaInputs:
+    return decode_mtp1(seed=seed, kv_dtype="int8")
+
+
+def varlen_decode(seed: int = 0) -> SfaInputs:
+    """B=32, S1=1, 128 heads, live lengths uniform in [512, 65536], 512 block slots per batch,
+    min(2048, len) distinct indices padded with -1."""
+    g = torch.Generator().manual_seed(10_000 + int(seed))
+    act = torch.randint(512, 65536 + 1, (32,), generator=g).tolist()
+    return generate(batch=32, s1=1, n_q=128, act_seqs=act, topk=2048, seed=seed,
+                    max_blocks_per_batch=512, name="varlen_b32_s1_h128_topk2048")
+
+
+def prefill(seed: int = 0, s1: int = 4096, kv_dtype: str = "bf16") -> SfaInputs:
+    """B=1, S1=4096 query tokens over 4096 live positions in 32 randomly placed blocks; query i
+    takes min(i+1, 2048) distinct positions from [0, i], padded with -1."""
+    return generate(batch=1, s1=s1, n_q=128, act_seqs=[s1], topk=2048, kv_dtype=kv_dtype,
+                    seed=seed, index_mode="causal", name=f"prefill_b1_s{s1}_h128_topk2048_{kv_dtype}")
+
+
+def page_case(name: str, seed: int = 0) -> SfaInputs:
+    """The page-2 test table's shapes (B, S1, N_Q=128, N_KV=1, per-batch lengths, key mode)."""
+    if name == "total_int8_d":
+        return generate(batch=4, s1=2, n_q=128, act_seqs=[65536, 16381, 666, 15], topk=2048,
+                        kv_dtype="int8", seed=seed, max_blocks_per_batch=512, name=name)
+    if name == "per_int8_d":
+        return generate(batch=4, s1=2, n_q=128, act_seqs=[65536] * 4, topk=2048, kv_dtype="int8",
+                        seed=seed, name=name)
+    if name == "per_bf16_d":
+        return generate(batch=4, s1=2, n_q=128, act_seqs=[65536] * 4, topk=2048, kv_dtype="bf16",
+                        seed=seed, name=name)
+    if name == "int8_p":
+        return generate(batch=1, s1=256, n_q=128, act_seqs=[65536], topk=2048, kv_dtype="int8",
+                        seed=seed, index_mode="causal", name=name)
+    raise KeyError(name)
+
+
+PAGE_CASES = ("total_int8_d", "per_int8_d", "per_bf16_d", "int8_p")
