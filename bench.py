@@ -1,0 +1,246 @@
+"""Benchmark: sparse MLA flash attention decode on one MI355X.
+
+Workload (default): B=64 sequences, S1=2 query tokens each (MTP1), 128 query heads over one
+latent KV head, 8192 live cache positions per sequence in a 4096-block paged pool (block 128),
+top-k = 2048 distinct positions per token, bf16 cache. All inputs are seeded and synthetic.
+
+A step is one sfa_decode call over one batch. The timed region runs --steps calls back to
+back. It rotates over --sets independent copies of the inputs; each copy has its own physical
+block order, so its pool sits at different addresses and the 256 MB MALL cannot hold the
+previous call's rows (cold protocol). Inputs are resident in HBM before timing starts.
+
+Prints one JSON line. Extra fields beyond the contract: the per-launch kernel time, gathered
+KV GB/s, TFLOP/s and the roofline object for the attention kernel, plus a CPU baseline: the
+fp64 oracle on a bounded token sample of the same workload, on this host's cores.
+
+Algorithmic work per call (fixed by the workload, not by the implementation):
+  bytes = sum over valid (token, slot) of 1152 (bf16 row: 1024 nope + 128 rope) or 656 (int8:
+          512 + 128 + 16 scale bytes), plus per token Q (n_q*576*2) + out (n_q*512*2) + indices
+          (4*topk)
+  flop  = sum over valid (token, slot) of 2 * n_q * (576 + 512)
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+METRIC = "µs/call + gathered-KV GB/s & TFLOP/s vs roofline, B=64 S1=2 topk=2048 decode"
+
+WORKLOADS = {
+    "decode_b64_s2_bf16": ("decode_mtp1", "bf16", False),
+    "decode_b64_s2_int8": ("decode_mtp1_int8", "int8", False),
+    "varlen_b32_s1_bf16": ("varlen_decode", "bf16", False),
+    "prefill_b1_s4096_bf16": ("prefill", "bf16", True),
+}
+
+
+def algorithmic_work(inp):
+    import numpy as np
+
+    valid = int(np.asarray(inp.valid_counts()).sum())
+    row = 1152 if inp.kv_dtype == "bf16" else 656
+    per_token = inp.n_q * 576 * 2 + inp.n_q * 512 * 2 + 4 * inp.topk
+    nbytes = valid * row + inp.n_tokens * per_token
+    flop = valid * 2 * inp.n_q * (576 + 512)
+    return valid, nbytes, flop
+
+
+def permuted_copy(dev, inp, seed):
+    """A device copy of the inputs with the physical blocks of the pool permuted (and the block
+    table remapped): the same attention problem at different addresses."""
+    import torch
+
+    n_pool = inp.num_cache_rows // 128
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    perm = torch.randperm(n_pool, generator=g).to(dev["key_rope"].device)
+    out = dict(dev)
+    for key in ("key_nope", "key_rope", "k_nope_scales"):
+        t = dev[key]
+        if t is None:
+            continue
+        blocks = t.view(n_pool, 128, -1)
+        moved = torch.empty_like(blocks)
+        moved[perm] = blocks
+        out[key] = moved.view_as(t)
+    out["block_table"] = perm.to(torch.int32)[dev["block_table"].long()].contiguous()
+    return out
+
+
+def traffic_from_profile(kernel_src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was taken on the same
+    kernel source (its recorded hash matches); otherwise None."""
+    path = os.path.join(ROOT, "profiles", "sfa_decode_b64_s2_bf16_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_src_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in ("sfa_kernels.hip", "sfa_internal.h"):
+        h.update(open(os.path.join(ROOT, "mla_sparse_top_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
+def cpu_baseline(inp, gpu_out, seconds: float):
+    """The fp64 oracle on this host, over as many tokens as fit in `seconds`, scaled to a full
+    call. Also compares those tokens with the GPU output."""
+    import numpy as np
+
+    import oracle.sfa_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    got = gpu_out.float().cpu().numpy().astype(np.float64).reshape(inp.n_tokens, inp.n_q, 512)
+    t0 = time.perf_counter()
+    done = 0
+    worst = 0.0
+    fails = 0
+    order = np.random.default_rng(0).permutation(inp.n_tokens)
+    while done < inp.n_tokens and time.perf_counter() - t0 < seconds:
+        t = int(order[done])
+        ref = O.sparse_mla_attention(inp, tokens=[t])[0]
+        rep = O.allclose_report(got[t], ref)
+        worst = max(worst, rep["worst_ratio"])
+        fails += rep["fails"]
+        done += 1
+    el = time.perf_counter() - t0
+    us_per_call = el / done * inp.n_tokens * 1e6
+    return {
+        "value": round(us_per_call, 1), "unit": "us/call", "cores": cores, "kind": "oracle",
+        "blas_threads": blas_threads, "numpy": np.__version__,
+        "sample": f"{done} of {inp.n_tokens} tokens (random order, seed 0) in {el:.1f} s, scaled to one call",
+        "sample_parity": {"tokens": done, "fails": fails, "worst_err_over_bound": round(worst, 4)},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_b64_s2_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated for a cold cache")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget (0 disables)")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sparse attention path has no "
+              f"cross-GPU component in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mla_sparse_top_amd import sfa, workloads
+
+    fn_name, dtype, is_prefill = WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    inp = getattr(workloads, fn_name)(seed=args.seed)
+    gen_s = time.perf_counter() - t_gen
+    print(f"[bench] generated {inp.name} in {gen_s:.1f} s", file=sys.stderr, flush=True)
+    dev0 = sfa.to_device(inp, "cuda")
+    sets = [dev0] + [permuted_copy(dev0, inp, 1000 + i) for i in range(1, max(1, args.sets))]
+    torch.cuda.synchronize()
+    outs = [torch.empty((inp.batch, inp.s1, inp.n_q, 512), dtype=torch.bfloat16, device="cuda") for _ in sets]
+    valid, nbytes, flop = algorithmic_work(inp)
+
+    def step(i):
+        k = i % len(sets)
+        sfa.run(inp, sets[k], prefill_mode=is_prefill, out=outs[k])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # per-launch events on the stream the kernel runs on (torch's current stream)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    whole0, whole1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    whole0.record()
+    for i in range(args.steps):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    whole1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = whole0.elapsed_time(whole1)
+    per_launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    mean_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
+    median_launch_ms = per_launch_ms[len(per_launch_ms) // 2]
+    ms_per_step = total_ms / args.steps
+    us_per_call = ms_per_step * 1e3
+
+    # all rotated copies must give bit-identical outputs (block permutation invariance)
+    same = all(torch.equal(outs[0], o) for o in outs[1:])
+
+    achieved_gbps = nbytes / (mean_launch_ms * 1e-3) / 1e9
+    achieved_tflops = flop / (mean_launch_ms * 1e-3) / 1e12
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profile(src_hash) if args.workload == "decode_b64_s2_bf16" else None
+    if dtype == "bf16" and not is_prefill:
+        roofline = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(us_per_call, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": inp.batch, "s1": inp.s1, "n_q": inp.n_q, "n_kv": 1,
+                   "topk": inp.topk, "kv_len": int(inp.kv_act_seqs.max()), "block_size": 128,
+                   "kv_lora_rank": 512, "rope_dim": 64, "valid_slots": valid, "cold_sets": len(sets)},
+        "kernel_ms_mean": round(mean_launch_ms, 5),
+        "kernel_ms_median": round(median_launch_ms, 5),
+        "gathered_kv_GBps": round(valid * (1152 if dtype == "bf16" else 656) / (mean_launch_ms * 1e-3) / 1e9, 1),
+        "algorithmic_bytes_per_call": nbytes,
+        "algorithmic_flop_per_call": flop,
+        "tflops": round(achieved_tflops, 1),
+        "roofline": roofline,
+        "rotated_outputs_identical": bool(same),
+        "wall_s_timed": round(wall, 3),
+        "kernel_source_sha256": src_hash,
+    }
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(inp, outs[(args.steps - 1) % len(sets)], args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

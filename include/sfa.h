@@ -1,0 +1,164 @@
+/*
+ * sfa.h -- C ABI of libsfa.so: sparse flash attention (SFA) over a paged MLA latent KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("DeepSeek V3/V2 Sparse Flash Attention with Quantization", sections
+ * "Algorithm overview", "Operator specification", "Input/output parameters";
+ * "CANN DeepSeek Indexer attention optimisation", section "Sparse Flash Attention"):
+ *
+ *   For query token t = b*s1 + s and head h, each slot k of topk_indices[t] names a logical
+ *   position j of batch b's cache. Slot k is valid iff 0 <= j < kv_act_seqs[b]. A valid slot
+ *   reads physical row  row = block_table[b][j / 128] * 128 + j % 128.
+ *   Then
+ *     score[k] = softmax_scale * ( q_nope[t,h] . Kn[row] + q_rope[t,h] . Kr[row] )
+ *     out[b,s,h,:] = sum over valid k of softmax_k(score)[k] * Kn[row_k]      (V = k_nope)
+ *   Kn is key_nope_2d. With an INT8 cache it is the dequantised value: the int8 code becomes
+ *   fp32 exactly, is multiplied in fp32 by the scale of its 128-element group, and the product
+ *   is rounded to bf16. The output is rounded to bf16 (round to nearest even).
+ *   A token with no valid slot outputs zeros. Invalid slots may sit anywhere in the row.
+ *
+ * Conventions common to every entry point:
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major buffers. The caller owns
+ *     them and keeps them alive until the work queued on `stream` has finished. The library
+ *     never allocates, frees, or keeps a pointer after it returns.
+ *   - Calls are asynchronous: the library only queues kernels on `stream` and never
+ *     synchronises. A fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - Return value: SFA_OK (0), or a negative sfa_status. Argument errors are found by
+ *     synchronous host-side validation before anything is queued; in that case nothing runs
+ *     and `out` is untouched. SFA_ERR_HIP means a HIP call failed (see sfa_status_string).
+ *   - Data preconditions, not checked on the host:
+ *       * every block_table entry that a valid slot reaches lies in
+ *         [0, num_cache_rows / 128);
+ *       * kv_act_seqs[b] <= max_blocks_per_batch * 128.
+ *     The kernels never dereference a row outside [0, num_cache_rows), nor a block_table
+ *     column at or past max_blocks_per_batch. Slots that would need one are treated as
+ *     masked.
+ *   - Entry points are reentrant. Calls on different streams may overlap if they use
+ *     different output and workspace buffers.
+ */
+#ifndef SFA_H_
+#define SFA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SFA_KV_LORA_RANK 512  /* nope width: query_nope, key_nope_2d, attention_out columns */
+#define SFA_ROPE_DIM 64       /* rope width: query_rope, key_rope_2d columns                 */
+#define SFA_BLOCK_SIZE 128    /* cache rows per page                                        */
+#define SFA_QUANT_GROUP 128   /* INT8 elements sharing one FP32 scale (4 scales per row)     */
+#define SFA_MAX_HEADS 128     /* query heads sharing the single latent KV head               */
+
+typedef enum { SFA_KV_BF16 = 0, SFA_KV_INT8 = 1 } sfa_kv_dtype;
+
+typedef enum {
+  SFA_OK = 0,
+  SFA_ERR_NULL = -1,            /* a required pointer is NULL                                 */
+  SFA_ERR_DIMS = -2,            /* a dimension is outside what the library supports           */
+  SFA_ERR_ALIGN = -3,           /* a tensor pointer is not 16-byte aligned                    */
+  SFA_ERR_WORKSPACE = -4,       /* workspace missing, misaligned, or smaller than required    */
+  SFA_ERR_SCALES = -5,          /* INT8 cache without k_nope_scales                           */
+  SFA_ERR_ALIAS = -6,           /* out (or rows_out) overlaps an input or the workspace       */
+  SFA_ERR_SCALE_VALUE = -7,     /* softmax_scale is not finite                                */
+  SFA_ERR_HIP = -8              /* a HIP runtime call failed                                  */
+} sfa_status;
+
+/* Shapes of one call ("Input/output parameters" table of the SFA-with-quantisation page).
+ * T = batch * s1 query tokens. */
+typedef struct {
+  int32_t batch;                /* B >= 0                                                     */
+  int32_t s1;                   /* query tokens per batch >= 0 (decode: 1 or 2; prefill: many) */
+  int32_t n_q;                  /* query heads: a multiple of 16 in [16, 128]                 */
+  int32_t n_kv;                 /* latent KV heads: must be 1                                 */
+  int32_t kv_lora_rank;         /* must be 512                                                */
+  int32_t rope_dim;             /* must be 64                                                 */
+  int32_t block_size;           /* must be 128                                                */
+  int32_t topk;                 /* slots per token (row length of topk_indices), >= 1         */
+  int32_t max_blocks_per_batch; /* row length of block_table, >= 1                            */
+  int64_t num_cache_rows;       /* block_num * block_size: rows of key_nope_2d / key_rope_2d  */
+  sfa_kv_dtype kv_dtype;        /* SFA_KV_INT8 => k_nope_scales is required                   */
+  int32_t num_splits;           /* 0 = automatic. Otherwise the number of top-k partitions per
+                                   token (raised to ceil(topk/2048) when smaller). Used only for
+                                   tests and tuning; every value gives the same result within
+                                   the accuracy standard. */
+} sfa_dims;
+
+/*
+ * Bytes of device workspace that sfa_decode (is_prefill = 0) or sfa_prefill (is_prefill = 1)
+ * needs for `dims`. Host-only: no GPU is touched. *bytes_out may be 0, in which case the
+ * workspace pointer may be NULL.
+ *
+ * The workspace holds per-partition partial results and one arrival counter per (token, head
+ * group). It needs no initialisation: the library clears the counters it uses, on `stream`,
+ * before each launch. Two calls that may run at the same time need separate workspaces.
+ */
+int sfa_workspace_size(const sfa_dims* dims, int is_prefill, size_t* bytes_out);
+
+/*
+ * Decode-mode SFA ("Decode mode": s1 of 1 or 2, standard softmax over the token's top-k set).
+ *
+ *   query_nope     bf16  (T*n_q, 512)      row (b*s1 + s)*n_q + h
+ *   query_rope     bf16  (T*n_q, 64)
+ *   key_nope_2d    bf16 or int8 (num_cache_rows, 512)
+ *   key_rope_2d    bf16  (num_cache_rows, 64)
+ *   k_nope_scales  fp32  (num_cache_rows, 4)  INT8 only (NULL allowed for bf16)
+ *   topk_indices   int32 (T, topk)           logical positions, -1 = padding
+ *   block_table    int32 (batch, max_blocks_per_batch)
+ *   kv_act_seqs    int32 (batch)
+ *   softmax_scale  multiplies the raw score before the softmax (finite)
+ *   out            bf16  (batch, s1, n_q, 512)   written in full
+ *   workspace      device buffer of >= sfa_workspace_size(dims, 0) bytes, 256-byte aligned,
+ *                  contents need not be initialised (see above)
+ * Every tensor pointer must be 16-byte aligned.
+ *
+ * The top-k set of each token is split into partitions that run in parallel, each with an
+ * online (running max / running sum) softmax over 32-slot tiles. The partials are merged with
+ * the log-sum-exp law in the same kernel: the prefill mode's update rule applied across
+ * partitions.
+ */
+int sfa_decode(const sfa_dims* dims,
+               const void* query_nope, const void* query_rope,
+               const void* key_nope_2d, const void* key_rope_2d, const float* k_nope_scales,
+               const int32_t* topk_indices, const int32_t* block_table, const int32_t* kv_act_seqs,
+               float softmax_scale, void* out,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Prefill-mode SFA ("Prefill mode": many query tokens; an online softmax keeps the running
+ * output, running sum and running max across s2 tiles and normalises at the last tile).
+ * Same arguments and layouts as sfa_decode. Each token runs in one workgroup, with no
+ * partitioning while topk <= 2048, and tokens are scheduled latest-first. In causal prefill
+ * the later tokens hold the most valid slots, so they start first.
+ */
+int sfa_prefill(const sfa_dims* dims,
+                const void* query_nope, const void* query_rope,
+                const void* key_nope_2d, const void* key_rope_2d, const float* k_nope_scales,
+                const int32_t* topk_indices, const int32_t* block_table, const int32_t* kv_act_seqs,
+                float softmax_scale, void* out,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The gather step alone: rows_out (T, topk) int32 receives the physical cache row of every
+ * valid slot and -1 for every masked one (PagedAttention mapping, blocks of 128 rows). It
+ * exposes the index resolution that sfa_decode / sfa_prefill perform internally, so that it
+ * can be checked bit-exactly.
+ */
+int sfa_resolve_rows(const sfa_dims* dims, const int32_t* topk_indices, const int32_t* block_table,
+                     const int32_t* kv_act_seqs, int32_t* rows_out, hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char* sfa_status_string(int status);
+
+/* Number of top-k partitions per token that sfa_decode (is_prefill = 0) or sfa_prefill
+ * (is_prefill = 1) will use for `dims` (host-only). Returns a negative sfa_status on bad dims. */
+int sfa_num_splits(const sfa_dims* dims, int is_prefill);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFA_H_ */

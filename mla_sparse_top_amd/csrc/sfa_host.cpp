@@ -1,0 +1,237 @@
+// C-ABI entry points of libsfa.so: synchronous argument validation, partition choice,
+// workspace layout, kernel launch. Declarations and contracts are in include/sfa.h.
+
+#include "sfa.h"
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "sfa_internal.h"
+
+namespace {
+
+using namespace sfa;
+
+constexpr size_t kAlignWs = 256;
+// Target number of workgroups for decode: the MI355X has 256 compute units and the attention
+// kernel runs one workgroup per CU (its register and LDS footprint allow no more).
+constexpr int kTargetWorkgroups = 256;
+
+int head_groups(const sfa_dims* d) { return (d->n_q + kHeadsPerGroup - 1) / kHeadsPerGroup; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_dims(const sfa_dims* d) {
+  if (!d) return SFA_ERR_NULL;
+  if (d->n_kv != 1 || d->kv_lora_rank != kNope || d->rope_dim != kRope || d->block_size != kBlock)
+    return SFA_ERR_DIMS;
+  if (d->n_q < 16 || d->n_q > SFA_MAX_HEADS || (d->n_q % 16) != 0) return SFA_ERR_DIMS;
+  if (d->batch < 0 || d->s1 < 0) return SFA_ERR_DIMS;
+  if ((int64_t)d->batch * d->s1 > (1 << 24)) return SFA_ERR_DIMS;
+  if (d->topk < 1 || d->topk > kMaxTopk) return SFA_ERR_DIMS;
+  if (d->max_blocks_per_batch < 1 || d->max_blocks_per_batch > (1 << 23)) return SFA_ERR_DIMS;
+  if (d->num_cache_rows < 0 || d->num_cache_rows > INT32_MAX) return SFA_ERR_DIMS;
+  if (d->kv_dtype != SFA_KV_BF16 && d->kv_dtype != SFA_KV_INT8) return SFA_ERR_DIMS;
+  if (d->num_splits < 0 || d->num_splits > kMaxSplits) return SFA_ERR_DIMS;
+  return SFA_OK;
+}
+
+int pick_splits(const sfa_dims* d, int is_prefill) {
+  const int64_t tokens = (int64_t)d->batch * d->s1;
+  const int min_s = (d->topk + kMaxSlots - 1) / kMaxSlots;  // each partition compacts <= 2048 slots
+  int s;
+  if (d->num_splits > 0) {
+    s = d->num_splits;
+  } else if (is_prefill) {
+    s = 1;
+  } else {
+    // Enough (token, partition) work items to give every CU one, but at least 64 slots (two
+    // tiles) per partition.
+    const int64_t items = tokens * head_groups(d);
+    const int64_t want = items > 0 ? (kTargetWorkgroups + items - 1) / items : 1;
+    s = (int)(want < kMaxSplits ? want : kMaxSplits);
+    const int by_len = d->topk / 64 > 0 ? d->topk / 64 : 1;
+    if (s > by_len) s = by_len;
+    if (s < 1) s = 1;
+  }
+  if (s < min_s) s = min_s;
+  return s;
+}
+
+struct WsLayout {
+  size_t part_o, part_ml, counters, total;
+};
+
+WsLayout ws_layout(const sfa_dims* d, int splits) {
+  WsLayout w{0, 0, 0, 0};
+  if (splits <= 1) return w;
+  const size_t groups = (size_t)d->batch * d->s1 * head_groups(d);
+  const size_t items = groups * splits;
+  w.part_o = 0;
+  w.part_ml = align_up(items * kPartialBytes, kAlignWs);
+  w.counters = w.part_ml + align_up(items * kPartialMlBytes, kAlignWs);
+  w.total = w.counters + align_up(groups * sizeof(int32_t), kAlignWs);
+  return w;
+}
+
+// [p, p + n) overlaps [q, q + m)
+bool overlaps(const void* p, size_t n, const void* q, size_t m) {
+  if (!p || !q || n == 0 || m == 0) return false;
+  const uintptr_t a0 = (uintptr_t)p, a1 = a0 + n, b0 = (uintptr_t)q, b1 = b0 + m;
+  return a0 < b1 && b0 < a1;
+}
+
+int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void* qr, const void* kn,
+                  const void* kr, const float* scales, const int32_t* idx, const int32_t* bt,
+                  const int32_t* act, float softmax_scale, void* out, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != SFA_OK) return st;
+  const int64_t tokens = (int64_t)d->batch * d->s1;
+  if (!qn || !qr || !kn || !kr || !idx || !bt || !act || !out) return SFA_ERR_NULL;
+  const bool int8 = d->kv_dtype == SFA_KV_INT8;
+  if (int8 && !scales) return SFA_ERR_SCALES;
+  if (!aligned16(qn) || !aligned16(qr) || !aligned16(kn) || !aligned16(kr) || !aligned16(idx) ||
+      !aligned16(bt) || !aligned16(act) || !aligned16(out) || (int8 && !aligned16(scales)))
+    return SFA_ERR_ALIGN;
+  if (!isfinite(softmax_scale)) return SFA_ERR_SCALE_VALUE;
+
+  const int splits = pick_splits(d, is_prefill);
+  const WsLayout lay = ws_layout(d, splits);
+  if (lay.total > 0) {
+    if (!ws || ws_bytes < lay.total || ((uintptr_t)ws % kAlignWs) != 0) return SFA_ERR_WORKSPACE;
+  }
+
+  const size_t rows = (size_t)d->num_cache_rows;
+  const size_t out_bytes = (size_t)tokens * d->n_q * kNope * 2;
+  const void* ins[] = {qn, qr, kn, kr, scales, idx, bt, act, lay.total ? ws : nullptr};
+  const size_t sizes[] = {(size_t)tokens * d->n_q * kNope * 2,
+                          (size_t)tokens * d->n_q * kRope * 2,
+                          rows * kNope * (int8 ? 1 : 2),
+                          rows * kRope * 2,
+                          int8 ? rows * 4 * sizeof(float) : 0,
+                          (size_t)tokens * d->topk * sizeof(int32_t),
+                          (size_t)d->batch * d->max_blocks_per_batch * sizeof(int32_t),
+                          (size_t)d->batch * sizeof(int32_t),
+                          lay.total};
+  for (int i = 0; i < 9; ++i)
+    if (overlaps(out, out_bytes, ins[i], sizes[i])) return SFA_ERR_ALIAS;
+
+  if (tokens == 0) return SFA_OK;
+
+  KernelArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q_nope = static_cast<const uint16_t*>(qn);
+  a.q_rope = static_cast<const uint16_t*>(qr);
+  a.k_nope = kn;
+  a.k_rope = static_cast<const uint16_t*>(kr);
+  a.k_scales = scales;
+  a.topk_idx = idx;
+  a.block_table = bt;
+  a.act = act;
+  a.out = static_cast<uint16_t*>(out);
+  if (lay.total) {
+    char* base = static_cast<char*>(ws);
+    a.part_o = reinterpret_cast<float*>(base + lay.part_o);
+    a.part_ml = reinterpret_cast<float*>(base + lay.part_ml);
+    a.counters = reinterpret_cast<int32_t*>(base + lay.counters);
+  }
+  a.num_rows = d->num_cache_rows;
+  a.n_tokens = (int32_t)tokens;
+  a.s1 = d->s1;
+  a.n_q = d->n_q;
+  a.topk = d->topk;
+  a.mb = d->max_blocks_per_batch;
+  a.n_splits = splits;
+  a.chunk = (d->topk + splits - 1) / splits;
+  a.reverse = is_prefill ? 1 : 0;
+  a.head_groups = head_groups(d);
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);  // log2(e)
+  return launch_attention(a, int8, stream) == hipSuccess ? SFA_OK : SFA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sfa_workspace_size(const sfa_dims* dims, int is_prefill, size_t* bytes_out) {
+  if (!bytes_out) return SFA_ERR_NULL;
+  const int st = check_dims(dims);
+  if (st != SFA_OK) return st;
+  *bytes_out = ws_layout(dims, pick_splits(dims, is_prefill)).total;
+  return SFA_OK;
+}
+
+int sfa_num_splits(const sfa_dims* dims, int is_prefill) {
+  const int st = check_dims(dims);
+  if (st != SFA_OK) return st;
+  return pick_splits(dims, is_prefill);
+}
+
+int sfa_decode(const sfa_dims* dims, const void* query_nope, const void* query_rope,
+               const void* key_nope_2d, const void* key_rope_2d, const float* k_nope_scales,
+               const int32_t* topk_indices, const int32_t* block_table, const int32_t* kv_act_seqs,
+               float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+               hipStream_t stream) {
+  return run_attention(dims, 0, query_nope, query_rope, key_nope_2d, key_rope_2d, k_nope_scales,
+                       topk_indices, block_table, kv_act_seqs, softmax_scale, out, workspace,
+                       workspace_bytes, stream);
+}
+
+int sfa_prefill(const sfa_dims* dims, const void* query_nope, const void* query_rope,
+                const void* key_nope_2d, const void* key_rope_2d, const float* k_nope_scales,
+                const int32_t* topk_indices, const int32_t* block_table, const int32_t* kv_act_seqs,
+                float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  return run_attention(dims, 1, query_nope, query_rope, key_nope_2d, key_rope_2d, k_nope_scales,
+                       topk_indices, block_table, kv_act_seqs, softmax_scale, out, workspace,
+                       workspace_bytes, stream);
+}
+
+int sfa_resolve_rows(const sfa_dims* dims, const int32_t* topk_indices, const int32_t* block_table,
+                     const int32_t* kv_act_seqs, int32_t* rows_out, hipStream_t stream) {
+  const int st = check_dims(dims);
+  if (st != SFA_OK) return st;
+  if (!topk_indices || !block_table || !kv_act_seqs || !rows_out) return SFA_ERR_NULL;
+  if (!aligned16(topk_indices) || !aligned16(block_table) || !aligned16(kv_act_seqs) || !aligned16(rows_out))
+    return SFA_ERR_ALIGN;
+  const int64_t tokens = (int64_t)dims->batch * dims->s1;
+  const size_t out_bytes = (size_t)tokens * dims->topk * sizeof(int32_t);
+  if (overlaps(rows_out, out_bytes, topk_indices, out_bytes) ||
+      overlaps(rows_out, out_bytes, block_table, (size_t)dims->batch * dims->max_blocks_per_batch * 4) ||
+      overlaps(rows_out, out_bytes, kv_act_seqs, (size_t)dims->batch * 4))
+    return SFA_ERR_ALIAS;
+  if (tokens == 0) return SFA_OK;
+  ResolveArgs a;
+  a.topk_idx = topk_indices;
+  a.block_table = block_table;
+  a.act = kv_act_seqs;
+  a.rows_out = rows_out;
+  a.num_rows = dims->num_cache_rows;
+  a.n_tokens = (int32_t)tokens;
+  a.s1 = dims->s1;
+  a.topk = dims->topk;
+  a.mb = dims->max_blocks_per_batch;
+  return launch_resolve(a, stream) == hipSuccess ? SFA_OK : SFA_ERR_HIP;
+}
+
+const char* sfa_status_string(int status) {
+  switch (status) {
+    case SFA_OK: return "ok";
+    case SFA_ERR_NULL: return "a required pointer is NULL";
+    case SFA_ERR_DIMS: return "unsupported dimensions (n_kv must be 1, kv_lora_rank 512, rope_dim 64, "
+                              "block_size 128, n_q a multiple of 16 in [16,128], topk in [1,32768])";
+    case SFA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case SFA_ERR_WORKSPACE: return "workspace missing, not 256-byte aligned, or smaller than sfa_workspace_size";
+    case SFA_ERR_SCALES: return "INT8 cache requires k_nope_scales";
+    case SFA_ERR_ALIAS: return "output overlaps an input or the workspace";
+    case SFA_ERR_SCALE_VALUE: return "softmax_scale is not finite";
+    case SFA_ERR_HIP: return "a HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI host layer (sfa_host.cpp) and the kernels
+// (sfa_kernels.hip). Not installed, not part of the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace sfa {
+
+constexpr int kNope = 512;          // kv_lora_rank
+constexpr int kRope = 64;           // qk_rope_dim
+constexpr int kBlock = 128;         // rows per cache page
+constexpr int kTile = 32;           // top-k slots per inner tile
+constexpr int kWaves = 4;           // waves per workgroup; each owns 16 query heads
+constexpr int kThreads = kWaves * 64;
+constexpr int kHeadsPerWave = 16;
+constexpr int kHeadsPerGroup = kWaves * kHeadsPerWave;  // heads of one workgroup (64)
+constexpr int kMaxSlots = 2048;     // slots one workgroup compacts (topk partition size cap)
+constexpr int kMaxSplits = 16;      // top-k partitions per token
+constexpr int kMaxTopk = kMaxSlots * kMaxSplits;
+// Partial output of one (token, partition, head group): 4 waves x 32 d-blocks x 64 lanes x float4
+constexpr size_t kPartialBytes = (size_t)kWaves * 32 * 64 * 16;
+constexpr size_t kPartialMlBytes = kHeadsPerGroup * 2 * sizeof(float);
+
+struct KernelArgs {
+  const uint16_t* q_nope;     // bf16 bits (T*n_q, 512)
+  const uint16_t* q_rope;     // bf16 bits (T*n_q, 64)
+  const void* k_nope;         // bf16 bits or int8 (rows, 512)
+  const uint16_t* k_rope;     // bf16 bits (rows, 64)
+  const float* k_scales;      // (rows, 4) for int8
+  const int32_t* topk_idx;    // (T, topk)
+  const int32_t* block_table; // (batch, mb)
+  const int32_t* act;         // (batch)
+  uint16_t* out;              // bf16 bits (T, n_q, 512)
+  float* part_o;              // (T, head_groups, splits) x kPartialBytes
+  float* part_ml;             // (T, head_groups, splits, 64, 2)
+  int32_t* counters;          // (T, head_groups)
+  int64_t num_rows;
+  int32_t n_tokens, s1, n_q, topk, mb, n_splits, chunk, reverse, head_groups;
+  float scale_log2;           // softmax_scale * log2(e)
+};
+
+struct ResolveArgs {
+  const int32_t* topk_idx;
+  const int32_t* block_table;
+  const int32_t* act;
+  int32_t* rows_out;
+  int64_t num_rows;
+  int32_t n_tokens, s1, topk, mb;
+};
+
+hipError_t launch_attention(const KernelArgs& a, bool int8_cache, hipStream_t stream);
+hipError_t launch_resolve(const ResolveArgs& a, hipStream_t stream);
+
+}  // namespace sfa

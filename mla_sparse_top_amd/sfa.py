@@ -1,0 +1,250 @@
+"""Thin ctypes binding over libsfa.so (include/sfa.h). Argument marshalling only: every step of
+the attention runs in the library's HIP kernels. PyTorch supplies device memory and streams.
+
+Importing this module loads the native library and raises ImportError if it has not been built
+(``python -m mla_sparse_top_amd.build``). There is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfa.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m mla_sparse_top_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+KV_LORA_RANK = 512
+ROPE_DIM = 64
+BLOCK_SIZE = 128
+KV_BF16 = 0
+KV_INT8 = 1
+
+STATUS = {
+    0: "SFA_OK", -1: "SFA_ERR_NULL", -2: "SFA_ERR_DIMS", -3: "SFA_ERR_ALIGN", -4: "SFA_ERR_WORKSPACE",
+    -5: "SFA_ERR_SCALES", -6: "SFA_ERR_ALIAS", -7: "SFA_ERR_SCALE_VALUE", -8: "SFA_ERR_HIP",
+}
+
+
+class SfaDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("s1", ctypes.c_int32),
+        ("n_q", ctypes.c_int32),
+        ("n_kv", ctypes.c_int32),
+        ("kv_lora_rank", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("max_blocks_per_batch", ctypes.c_int32),
+        ("num_cache_rows", ctypes.c_int64),
+        ("kv_dtype", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
+_vp = ctypes.c_void_p
+_ATTN_ARGS = [ctypes.POINTER(SfaDims), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp,
+              ctypes.c_size_t, _vp]
+for _name in ("sfa_decode", "sfa_prefill"):
+    getattr(_lib, _name).argtypes = _ATTN_ARGS
+    getattr(_lib, _name).restype = ctypes.c_int
+_lib.sfa_workspace_size.argtypes = [ctypes.POINTER(SfaDims), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+_lib.sfa_workspace_size.restype = ctypes.c_int
+_lib.sfa_num_splits.argtypes = [ctypes.POINTER(SfaDims), ctypes.c_int]
+_lib.sfa_num_splits.restype = ctypes.c_int
+_lib.sfa_resolve_rows.argtypes = [ctypes.POINTER(SfaDims), _vp, _vp, _vp, _vp, _vp]
+_lib.sfa_resolve_rows.restype = ctypes.c_int
+_lib.sfa_status_string.argtypes = [ctypes.c_int]
+_lib.sfa_status_string.restype = ctypes.c_char_p
+
+EXPORTED_SYMBOLS = ("sfa_workspace_size", "sfa_num_splits", "sfa_decode", "sfa_prefill", "sfa_resolve_rows",
+                    "sfa_status_string")
+
+
+class SfaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+def status_string(status: int) -> str:
+    return _lib.sfa_status_string(int(status)).decode()
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def make_dims(*, batch: int, s1: int, n_q: int, topk: int, max_blocks_per_batch: int, num_cache_rows: int,
+              kv_dtype: int = KV_BF16, num_splits: int = 0, n_kv: int = 1, kv_lora_rank: int = KV_LORA_RANK,
+              rope_dim: int = ROPE_DIM, block_size: int = BLOCK_SIZE) -> SfaDims:
+    return SfaDims(batch, s1, n_q, n_kv, kv_lora_rank, rope_dim, block_size, topk, max_blocks_per_batch,
+                   num_cache_rows, kv_dtype, num_splits)
+
+
+def workspace_size(dims: SfaDims, is_prefill: bool = False) -> int:
+    out = ctypes.c_size_t(0)
+    st = _lib.sfa_workspace_size(ctypes.byref(dims), int(bool(is_prefill)), ctypes.byref(out))
+    if st != 0:
+        raise SfaError(st, "sfa_workspace_size")
+    return int(out.value)
+
+
+def num_splits(dims: SfaDims, is_prefill: bool = False) -> int:
+    st = _lib.sfa_num_splits(ctypes.byref(dims), int(bool(is_prefill)))
+    if st < 0:
+        raise SfaError(st, "sfa_num_splits")
+    return st
+
+
+# One zero-filled workspace per device, grown on demand. A completed call leaves the counters it
+# uses at zero, so the buffer can be reused by later calls on the same stream.
+_WORKSPACES: dict = {}
+
+
+def get_workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    key = (device.type, device.index)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, dtypes, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+
+
+def _attention(fn_name: str, query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices,
+               block_table, kv_act_seqs, softmax_scale, *, batch, s1, out=None, workspace=None,
+               num_splits_override=0, stream=None):
+    dev = query_nope.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    t_tokens = batch * s1
+    n_q = query_nope.shape[0] // t_tokens if t_tokens else 0
+    topk = topk_indices.shape[1] if topk_indices.dim() == 2 else 0
+    rows = key_rope.shape[0]
+    _check(query_nope, "query_nope", (torch.bfloat16,), (t_tokens * n_q, KV_LORA_RANK), dev)
+    _check(query_rope, "query_rope", (torch.bfloat16,), (t_tokens * n_q, ROPE_DIM), dev)
+    _check(key_nope, "key_nope", (torch.bfloat16, torch.int8), (rows, KV_LORA_RANK), dev)
+    _check(key_rope, "key_rope", (torch.bfloat16,), (rows, ROPE_DIM), dev)
+    int8 = key_nope.dtype == torch.int8
+    if int8:
+        if k_nope_scales is None:
+            raise ValueError("an int8 key_nope needs k_nope_scales")
+        _check(k_nope_scales, "k_nope_scales", (torch.float32,), (rows, 4), dev)
+    _check(topk_indices, "topk_indices", (torch.int32,), (t_tokens, topk), dev)
+    _check(block_table, "block_table", (torch.int32,), None, dev)
+    _check(kv_act_seqs, "kv_act_seqs", (torch.int32,), (batch,), dev)
+    if block_table.dim() != 2 or block_table.shape[0] != batch:
+        raise ValueError("block_table must be (batch, max_blocks_per_batch)")
+    dims = make_dims(batch=batch, s1=s1, n_q=n_q, topk=topk, max_blocks_per_batch=block_table.shape[1],
+                     num_cache_rows=rows, kv_dtype=KV_INT8 if int8 else KV_BF16, num_splits=num_splits_override)
+    if out is None:
+        out = torch.empty((batch, s1, n_q, KV_LORA_RANK), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", (torch.bfloat16,), (batch, s1, n_q, KV_LORA_RANK), dev)
+    need = workspace_size(dims, fn_name == "sfa_prefill")
+    if workspace is None:
+        workspace = get_workspace(dev, need)
+    elif need:
+        _check(workspace, "workspace", (torch.uint8,), None, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = getattr(_lib, fn_name)(
+        ctypes.byref(dims), _ptr(query_nope), _ptr(query_rope), _ptr(key_nope), _ptr(key_rope),
+        _ptr(k_nope_scales if int8 else None), _ptr(topk_indices), _ptr(block_table), _ptr(kv_act_seqs),
+        ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace) if need else None,
+        ctypes.c_size_t(workspace.numel() if (need and workspace is not None) else 0),
+        ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise SfaError(st, fn_name)
+    return out
+
+
+def decode(query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices, block_table, kv_act_seqs,
+           softmax_scale, *, batch, s1, out=None, workspace=None, num_splits=0, stream=None):
+    """sfa_decode: returns out (batch, s1, n_q, 512) bf16."""
+    return _attention("sfa_decode", query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices,
+                      block_table, kv_act_seqs, softmax_scale, batch=batch, s1=s1, out=out, workspace=workspace,
+                      num_splits_override=num_splits, stream=stream)
+
+
+def prefill(query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices, block_table, kv_act_seqs,
+            softmax_scale, *, batch, s1, out=None, workspace=None, num_splits=0, stream=None):
+    """sfa_prefill: returns out (batch, s1, n_q, 512) bf16."""
+    return _attention("sfa_prefill", query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices,
+                      block_table, kv_act_seqs, softmax_scale, batch=batch, s1=s1, out=out, workspace=workspace,
+                      num_splits_override=num_splits, stream=stream)
+
+
+def resolve_rows(topk_indices, block_table, kv_act_seqs, *, batch, s1, num_cache_rows, rows_out=None,
+                 stream=None):
+    """sfa_resolve_rows: returns rows_out (T, topk) int32, -1 for masked slots."""
+    dev = topk_indices.device
+    t_tokens = batch * s1
+    topk = topk_indices.shape[1]
+    _check(topk_indices, "topk_indices", (torch.int32,), (t_tokens, topk), dev)
+    _check(block_table, "block_table", (torch.int32,), None, dev)
+    _check(kv_act_seqs, "kv_act_seqs", (torch.int32,), (batch,), dev)
+    dims = make_dims(batch=batch, s1=s1, n_q=128, topk=topk, max_blocks_per_batch=block_table.shape[1],
+                     num_cache_rows=num_cache_rows)
+    if rows_out is None:
+        rows_out = torch.empty((t_tokens, topk), dtype=torch.int32, device=dev)
+    _check(rows_out, "rows_out", (torch.int32,), (t_tokens, topk), dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = _lib.sfa_resolve_rows(ctypes.byref(dims), _ptr(topk_indices), _ptr(block_table), _ptr(kv_act_seqs),
+                               _ptr(rows_out), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise SfaError(st, "sfa_resolve_rows")
+    return rows_out
+
+
+def to_device(inp, device="cuda"):
+    """Upload a workloads.SfaInputs instance: bf16 bit patterns become torch.bfloat16 tensors."""
+    import numpy as np
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    kn = bf16(inp.key_nope) if inp.kv_dtype == "bf16" else torch.from_numpy(inp.key_nope).to(device)
+    return {
+        "query_nope": bf16(inp.query_nope),
+        "query_rope": bf16(inp.query_rope),
+        "key_nope": kn,
+        "key_rope": bf16(inp.key_rope),
+        "k_nope_scales": None if inp.k_nope_scales is None else torch.from_numpy(inp.k_nope_scales).to(device),
+        "topk_indices": torch.from_numpy(inp.topk_indices).to(device),
+        "block_table": torch.from_numpy(inp.block_table).to(device),
+        "kv_act_seqs": torch.from_numpy(inp.kv_act_seqs).to(device),
+    }
+
+
+def run(inp, dev_tensors=None, *, prefill_mode=False, num_splits=0, out=None):
+    """Run decode (or prefill) on an uploaded instance; returns the bf16 output tensor."""
+    d = dev_tensors if dev_tensors is not None else to_device(inp)
+    fn = prefill if prefill_mode else decode
+    return fn(d["query_nope"], d["query_rope"], d["key_nope"], d["key_rope"], d["k_nope_scales"], d["topk_indices"],
+              d["block_table"], d["kv_act_seqs"], inp.softmax_scale, batch=inp.batch, s1=inp.s1,
+              num_splits=num_splits, out=out)

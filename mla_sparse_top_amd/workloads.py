@@ -100,18 +100,38 @@ def _normal_bf16(g: torch.Generator, rows: int, cols: int) -> np.ndarray:
     return out
 
 
+def _quantize_rows(x_bf16: torch.Tensor):
+    """Cache-write quantisation of bf16 latents (rows, 512): per 128-element group,
+    scale = absmax / 127 (float32) and code = clamp(round_half_even(x / scale), -128, 127).
+    All-zero groups get scale 0 and code 0."""
+    x = x_bf16.to(torch.float32).reshape(-1, N_GROUPS, QUANT_GROUP)
+    scale = x.abs().amax(dim=2) / 127.0
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    q = torch.round(x / safe[:, :, None]).clamp_(-128, 127)  # torch.round: ties to even
+    q = torch.where((scale > 0)[:, :, None], q, torch.zeros_like(q))
+    return q.to(torch.int8).reshape(-1, KV_LORA_RANK), scale
+
+
 def quantize_int8_groups(nope_bf16_bits: np.ndarray):
-    """Cache-write quantisation of bf16 latents: per 128-element group, scale = absmax / 127
-    (float32) and code = clamp(round_half_even(x / scale), -128, 127). All-zero groups get
-    scale 0 and code 0."""
-    x = (nope_bf16_bits.astype(np.uint32) << 16).view(np.float32).reshape(-1, N_GROUPS, QUANT_GROUP)
-    absmax = np.abs(x).max(axis=2)
-    scale = (absmax / np.float32(127.0)).astype(np.float32)
-    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    q = np.rint(x / safe[:, :, None])
-    q = np.clip(q, -128, 127).astype(np.int8)
-    q[scale == 0] = 0
-    return q.reshape(-1, KV_LORA_RANK), scale
+    """Quantise bf16 bit patterns (rows, 512) -> (int8 codes (rows, 512), float32 scales (rows, 4))."""
+    x = torch.from_numpy(np.ascontiguousarray(nope_bf16_bits).view(np.int16)).view(torch.bfloat16)
+    q, s = _quantize_rows(x)
+    return q.numpy(), s.numpy()
+
+
+def _normal_nope(g: torch.Generator, rows: int, int8: bool):
+    """Draw the cache's nope rows as bf16 N(0,1); for int8 also quantise them, chunk by chunk."""
+    if not int8:
+        return _normal_bf16(g, rows, KV_LORA_RANK), None
+    codes = np.empty((rows, KV_LORA_RANK), dtype=np.int8)
+    scales = np.empty((rows, N_GROUPS), dtype=np.float32)
+    for r0 in range(0, rows, _ROW_CHUNK):
+        r1 = min(rows, r0 + _ROW_CHUNK)
+        xb = torch.randn(r1 - r0, KV_LORA_RANK, generator=g, dtype=torch.float32).to(torch.bfloat16)
+        q, s = _quantize_rows(xb)
+        codes[r0:r1] = q.numpy()
+        scales[r0:r1] = s.numpy()
+    return codes, scales
 
 
 def generate(
@@ -173,7 +193,7 @@ def generate(
             off += nblk[b]
 
     rows = n_pool * BLOCK_SIZE
-    nope = _normal_bf16(g, rows, KV_LORA_RANK)
+    nope, scales = _normal_nope(g, rows, kv_dtype == "int8")
     rope = _normal_bf16(g, rows, ROPE_DIM)
 
     # Rows nobody may read: the poison blocks, and rows of live blocks past the live length.
@@ -186,16 +206,14 @@ def generate(
             last = int(bt[b, nblk[b] - 1])
             dead[last * BLOCK_SIZE + (BLOCK_SIZE - tail):(last + 1) * BLOCK_SIZE] = True
 
-    scales = None
+    dead_rows = np.nonzero(dead)[0]
     if kv_dtype == "int8":
-        q, scales = quantize_int8_groups(nope)
-        scales[dead] = np.float32(np.nan)
-        q[dead] = 0
-        key_nope = q
+        scales[dead_rows] = np.float32(np.nan)
+        nope[dead_rows] = 0
     else:
-        nope[dead] = BF16_QNAN
-        key_nope = nope
-    rope[dead] = BF16_QNAN
+        nope[dead_rows] = BF16_QNAN
+    key_nope = nope
+    rope[dead_rows] = BF16_QNAN
 
     t_count = batch * s1
     qn = _normal_bf16(g, t_count * n_q, KV_LORA_RANK)

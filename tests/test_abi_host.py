@@ -1,0 +1,154 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol include/sfa.h declares,
+sizes workspaces, picks partitions, and rejects bad arguments before anything is queued.
+
+The attention entry points are called only with arguments that fail host validation, so no
+device pointer is dereferenced and no HIP call is made.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mla_sparse_top_amd import sfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sfa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(sfa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declarations_are_exported():
+    declared = _declared_functions()
+    assert set(declared) == set(sfa.EXPORTED_SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", sfa.lib_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\b(sfa_\w+)\b", out))
+    for name in declared:
+        assert name in exported, name
+        assert getattr(sfa._lib, name) is not None
+
+
+def test_library_has_gfx950_code_object():
+    # the HIP fat binary embedded in our own build names its offload target
+    data = open(sfa.lib_path(), "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in data
+
+
+def _dims(**kw):
+    base = dict(batch=64, s1=2, n_q=128, topk=2048, max_blocks_per_batch=64, num_cache_rows=4097 * 128)
+    base.update(kw)
+    return sfa.make_dims(**base)
+
+
+def test_partition_choice():
+    # 64 x 2 tokens x 2 head groups already fill 256 CUs: no top-k partitioning
+    assert sfa.num_splits(_dims()) == 1
+    assert sfa.workspace_size(_dims()) == 0
+    # 32 single-token batches x 2 head groups: 4 partitions
+    assert sfa.num_splits(_dims(batch=32, s1=1)) == 4
+    # one token of 16 heads, 64 slots: partitions need >= 64 slots each
+    assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=64)) == 1
+    assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=2048)) == 16
+    # prefill never partitions while topk <= 2048
+    assert sfa.num_splits(_dims(batch=1, s1=4096), is_prefill=True) == 1
+    # topk > 2048 forces enough partitions that each compacts <= 2048 slots
+    assert sfa.num_splits(_dims(batch=1, s1=4096, topk=5000), is_prefill=True) == 3
+    # explicit override, raised to the minimum
+    assert sfa.num_splits(_dims(num_splits=4)) == 4
+    assert sfa.num_splits(_dims(topk=5000, num_splits=1)) == 3
+
+
+def test_workspace_size_formula():
+    d = _dims(batch=32, s1=1)  # 4 partitions, 2 head groups
+    groups = 32 * 2
+    items = groups * 4
+    part = items * 4 * 32 * 64 * 16
+    ml = items * 64 * 2 * 4
+    cnt = groups * 4
+
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    assert sfa.workspace_size(d) == up(part) + up(ml) + up(cnt)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_kv", 2), ("kv_lora_rank", 256), ("rope_dim", 32), ("block_size", 64), ("n_q", 8), ("n_q", 24),
+    ("n_q", 144), ("topk", 0), ("topk", 40000), ("batch", -1), ("s1", -2), ("max_blocks_per_batch", 0),
+    ("num_cache_rows", -1), ("num_splits", 17), ("num_splits", -1), ("kv_dtype", 3),
+])
+def test_bad_dims_rejected(field, value):
+    d = _dims()
+    setattr(d, field, value)
+    with pytest.raises(sfa.SfaError) as e:
+        sfa.workspace_size(d)
+    assert e.value.status == -2
+
+
+def _call(fn_name, dims, ptrs=None, scale=0.04, ws=None, ws_bytes=0):
+    p = dict(qn=0x100000, qr=0x200000, kn=0x10000000, kr=0x20000000, sc=0x30000000, idx=0x300000,
+             bt=0x400000, act=0x500000, out=0x40000000)
+    if ptrs:
+        p.update(ptrs)
+    vp = lambda v: None if v is None else ctypes.c_void_p(v)  # noqa: E731
+    fn = getattr(sfa._lib, fn_name)
+    return fn(ctypes.byref(dims), vp(p["qn"]), vp(p["qr"]), vp(p["kn"]), vp(p["kr"]), vp(p["sc"]), vp(p["idx"]),
+              vp(p["bt"]), vp(p["act"]), ctypes.c_float(scale), vp(p["out"]), vp(ws), ctypes.c_size_t(ws_bytes),
+              None)
+
+
+SMALL = dict(batch=2, s1=1, n_q=16, topk=64, max_blocks_per_batch=2, num_cache_rows=512)
+
+
+@pytest.mark.parametrize("fn", ["sfa_decode", "sfa_prefill"])
+def test_validation_errors(fn):
+    d = _dims(**SMALL)
+    assert _call(fn, d, {"qn": None}) == -1
+    assert _call(fn, d, {"out": None}) == -1
+    assert _call(fn, d, {"qr": 0x200008}) == -3                       # misaligned
+    assert _call(fn, d, {"out": 0x40000004}) == -3
+    assert _call(fn, d, scale=float("inf")) == -7
+    assert _call(fn, d, scale=float("nan")) == -7
+    assert _call(fn, _dims(**{**SMALL, "kv_dtype": 1}), {"sc": None}) == -5
+    # out overlapping query_nope
+    assert _call(fn, d, {"out": 0x100000 + 4096}) == -6
+    bad = _dims(**SMALL)
+    bad.n_kv = 2
+    assert _call(fn, bad) == -2
+
+
+def test_workspace_errors():
+    d = _dims(batch=1, s1=1, n_q=16, topk=2048, max_blocks_per_batch=16, num_cache_rows=4096)
+    need = sfa.workspace_size(d)
+    assert need > 0
+    assert _call("sfa_decode", d) == -4                                  # missing
+    assert _call("sfa_decode", d, ws=0x50000000, ws_bytes=need - 1) == -4  # too small
+    assert _call("sfa_decode", d, ws=0x50000010, ws_bytes=need) == -4      # not 256-aligned
+    # output inside the workspace
+    assert _call("sfa_decode", d, {"out": 0x50000000 + 4096}, ws=0x50000000, ws_bytes=need) == -6
+
+
+def test_empty_batch_is_a_no_op():
+    # T = 0: validated, nothing to do, no HIP call needed
+    assert _call("sfa_decode", _dims(**{**SMALL, "batch": 0})) == 0
+
+
+def test_resolve_validation():
+    d = _dims(**SMALL)
+    f = sfa._lib.sfa_resolve_rows
+    vp = ctypes.c_void_p
+    assert f(ctypes.byref(d), None, vp(0x400000), vp(0x500000), vp(0x600000), None) == -1
+    assert f(ctypes.byref(d), vp(0x300004), vp(0x400000), vp(0x500000), vp(0x600000), None) == -3
+    assert f(ctypes.byref(d), vp(0x300000), vp(0x400000), vp(0x500000), vp(0x300000), None) == -6
+
+
+def test_status_strings():
+    for code in range(-8, 1):
+        assert sfa.status_string(code)
+    assert sfa.status_string(-99) == "unknown status"
