@@ -15,7 +15,7 @@
 //     are then dense: padding costs no loads and no MFMA, and a tile of invalid slots never runs.
 //   * Gather: each 32-row tile is fetched with LDS-DMA (global_load_lds_dwordx4). One wave
 //     instruction moves one 1 KB nope row, or eight 128 B rope rows, fully coalesced, with no
-//     VGPR staging. Three LDS stages keep two tiles in flight while a third is computed. INT8
+//     VGPR staging. Four LDS stages keep three tiles in flight while a fourth is computed. INT8
 //     rows are fetched to registers a tile ahead instead, dequantised (fp32 multiply by the
 //     group scale, round-to-nearest-even to bf16) and written into the same bf16 LDS layout.
 //   * S^T = K . Q^T with v_mfma_f32_16x16x32_bf16: keys on M, heads on N, d as the reduction.
@@ -66,11 +66,14 @@ constexpr int kRopeRowBytes = kRope * 2;
 constexpr int kNopeTileBytes = kTile * kNopeRowBytes;
 constexpr int kRopeTileBytes = kTile * kRopeRowBytes;
 constexpr int kStageBytes = kNopeTileBytes + kRopeTileBytes;
-constexpr int kStagesBf16 = 3;
+constexpr int kStagesBf16 = 4;
 constexpr int kStagesInt8 = 2;
 constexpr int kDmaPerTile = 9;             // per wave: 8 nope rows + 1 rope instruction
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p stays <= 256 between rescales
 constexpr int kQSteps = (kNope + kRope) / 32;  // 18 MFMA k-steps over d
+// LDS operand loads kept in flight ahead of the MFMA that consumes them
+constexpr int kQkDepth = 6;
+constexpr int kPvDepth = 4;
 
 __device__ __forceinline__ int nope_swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
 __device__ __forceinline__ int rope_swz(int key) { return (key >> 1) & 7; }
@@ -145,50 +148,13 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   if (a.reverse) t = a.n_tokens - 1 - t;
   const int b = t / a.s1;
 
-  // ---- resolve this partition's slots and compact the valid rows into s_rows, in slot order
-  const int lim = min(a.act[b], a.mb * kBlock);
-  const int k0 = sp * a.chunk;
-  const int nslot = max(0, min(a.topk, k0 + a.chunk) - k0);
-  const int32_t* idx = a.topk_idx + (int64_t)t * a.topk + k0;
-  const int32_t* btab = a.block_table + (int64_t)b * a.mb;
-  int n_valid = 0;
-  for (int base = 0; base < nslot; base += kThreads) {
-    const int k = base + tid;
-    bool v = false;
-    int row = 0;
-    if (k < nslot) {
-      const int j = idx[k];
-      if (j >= 0 && j < lim) {
-        const int blk = btab[j >> 7];
-        const int64_t r = (int64_t)blk * kBlock + (j & (kBlock - 1));
-        if (blk >= 0 && r < a.num_rows) {
-          v = true;
-          row = (int)r;
-        }
-      }
-    }
-    const uint64_t mask = __ballot(v);
-    if (lane == 0) s_wcnt[wave] = __popcll(mask);
-    lds_barrier();
-    int off = n_valid, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = s_wcnt[w];
-      off += (w < wave) ? c : 0;
-      tot += c;
-    }
-    if (v) s_rows[off + __popcll(mask & ((1ull << lane) - 1ull))] = row;
-    n_valid += tot;
-    lds_barrier();
-  }
-  const int ntiles = (n_valid + kTile - 1) / kTile;
-
   const int h0 = hg * kHeadsPerGroup + wave * kHeadsPerWave;  // first head of this wave
   const bool wave_active = h0 < a.n_q;                         // wave-uniform
   const int h = h0 + n;                                         // this lane's head
   const bool head_ok = h < a.n_q;
 
-  // ---- Q^T fragments (B operand, k = d): lane (n, kg) holds d in [32c + 8kg, 32c + 8kg + 8)
+  // ---- Q^T fragments (B operand, k = d): lane (n, kg) holds d in [32c + 8kg, 32c + 8kg + 8).
+  // Issued first so that their latency overlaps the slot resolution below.
   bf16x8 qf[kQSteps];
   {
     const bf16x8 zero = {};
@@ -199,7 +165,62 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     for (int c = 0; c < 16; ++c) qf[c] = head_ok ? qn[4 * c + kg] : zero;
 #pragma unroll
     for (int c = 0; c < 2; ++c) qf[16 + c] = head_ok ? qr[4 * c + kg] : zero;
+    // Q is only ever an MFMA B operand, which may come from AGPRs: pin it there and leave the
+    // architectural VGPRs to the in-flight LDS operands of the MFMA pipelines.
+#pragma unroll
+    for (int c = 0; c < kQSteps; ++c) asm volatile("" : "+a"(qf[c]));
   }
+
+  // ---- resolve this partition's slots and compact the valid rows into s_rows, in slot order.
+  // Thread T owns the contiguous slots [8T, 8T+8) of the partition (a partition holds at most
+  // 2048 = 256 x 8 slots): all index loads are issued together, then all block-table loads,
+  // then one workgroup-wide exclusive scan of the per-thread valid counts places the rows.
+  static_assert(kMaxSlots == kThreads * 8, "one pass of 8 slots per thread covers a partition");
+  const int lim = min(a.act[b], a.mb * kBlock);
+  const int k0 = sp * a.chunk;
+  const int nslot = max(0, min(a.topk, k0 + a.chunk) - k0);
+  const int32_t* idx = a.topk_idx + (int64_t)t * a.topk + k0;
+  const int32_t* btab = a.block_table + (int64_t)b * a.mb;
+  int jv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = 8 * tid + i;
+    jv[i] = k < nslot ? idx[k] : -1;
+  }
+  int rowv[8];
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = jv[i];
+    const bool in = j >= 0 && j < lim;
+    const int blk = in ? btab[j >> 7] : -1;
+    const int64_t r = (int64_t)blk * kBlock + (j & (kBlock - 1));
+    const bool v = in && blk >= 0 && r < a.num_rows;
+    rowv[i] = v ? (int)r : -1;
+    cnt += v ? 1 : 0;
+  }
+  // inclusive scan of cnt across the wave, then across waves through LDS
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int up = __shfl_up(incl, d);
+    if (lane >= d) incl += up;
+  }
+  if (lane == 63) s_wcnt[wave] = incl;
+  lds_barrier();
+  int off = incl - cnt, n_valid = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = s_wcnt[w];
+    off += (w < wave) ? c : 0;
+    n_valid += c;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (rowv[i] >= 0) s_rows[off++] = rowv[i];
+  }
+  lds_barrier();
+  const int ntiles = (n_valid + kTile - 1) / kTile;
 
   floatx4 oacc[32];  // O^T block db: lane (n, kg) holds d = 16*db + 4*kg + r of head h
 #pragma unroll
@@ -278,19 +299,25 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     const char* ks = smem + stage * kStageBytes;
     const char* rs = ks + kNopeTileBytes;
     floatx4 s[2] = {floatx4{}, floatx4{}};
+    // A operand of step c (= 2*kstep + kb): key 16*kb + n, logical chunk 4*kstep + kg. Loads run
+    // two MFMAs ahead of their use, and each step is fenced so the scheduler keeps that shape.
+    auto qk_operand = [&](int c) __attribute__((always_inline)) -> bf16x8 {
+      const int kstep = c >> 1, kb = c & 1;
+      const int key = 16 * kb + n;
+      if (kstep < 16)
+        return *reinterpret_cast<const bf16x8*>(ks + key * kNopeRowBytes + 16 * ((4 * kstep + kg) ^ nope_swz(key)));
+      return *reinterpret_cast<const bf16x8*>(rs + key * kRopeRowBytes + 16 * ((4 * (kstep - 16) + kg) ^ rope_swz(key)));
+    };
+    constexpr int kQkOps = 2 * kQSteps;
+    bf16x8 qa[kQkDepth];
 #pragma unroll
-    for (int c = 0; c < kQSteps; ++c) {
+    for (int c = 0; c < kQkDepth; ++c) qa[c] = qk_operand(c);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key = 16 * kb + n;
-        bf16x8 av;
-        if (c < 16) {
-          av = *reinterpret_cast<const bf16x8*>(ks + key * kNopeRowBytes + 16 * ((4 * c + kg) ^ nope_swz(key)));
-        } else {
-          av = *reinterpret_cast<const bf16x8*>(rs + key * kRopeRowBytes + 16 * ((4 * (c - 16) + kg) ^ rope_swz(key)));
-        }
-        s[kb] = mfma16(av, qf[c], s[kb]);
-      }
+    for (int c = 0; c < kQkOps; ++c) {
+      const bf16x8 cur = qa[c % kQkDepth];
+      if (c + kQkDepth < kQkOps) qa[c % kQkDepth] = qk_operand(c + kQkDepth);
+      s[c & 1] = mfma16(cur, qf[c >> 1], s[c & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // result s[kb][r] holds key 16*kb + 4*kg + r of the tile, head h
@@ -314,7 +341,10 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
       const float m_new = need ? mt : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-      for (int db = 0; db < 32; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < 32; ++db) {
+        oacc[db] *= alpha;  // one block at a time keeps the AGPR<->VGPR round trip short
+        __builtin_amdgcn_sched_barrier(0);
+      }
       l_run *= alpha;
       m_run = m_new;
     }
@@ -338,36 +368,49 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
       pl[i] = (__bf16)(p[i] - (float)hb);
     }
 
-#pragma unroll
-    for (int db = 0; db < 32; ++db) {
+    auto pv_operand = [&](int db) __attribute__((always_inline)) -> bf16x8 {
       const int chunk = 2 * db + (tr_sub >> 1);
       const int off = 16 * (chunk ^ tr_swz) + 8 * (tr_sub & 1);
       const shortx4 v0 = lds_tr16(ks + tr_key * kNopeRowBytes + off);
       const shortx4 v1 = lds_tr16(ks + (tr_key + 16) * kNopeRowBytes + off);
-      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      oacc[db] = mfma16(av, ph, oacc[db]);
-      oacc[db] = mfma16(av, pl, oacc[db]);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 va[kPvDepth];
+#pragma unroll
+    for (int db = 0; db < kPvDepth; ++db) va[db] = pv_operand(db);
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      const bf16x8 cur = va[db % kPvDepth];
+      if (db + kPvDepth < 32) va[db % kPvDepth] = pv_operand(db + kPvDepth);
+      oacc[db] = mfma16(cur, ph, oacc[db]);
+      oacc[db] = mfma16(cur, pl, oacc[db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // ---- main loop over tiles
   if (ntiles > 0) {
     if constexpr (!kInt8) {
-      issue_nope_bf16(0, 0);
-      issue_rope(0, 0);
-      if (ntiles > 1) {
-        issue_nope_bf16(1, 1);
-        issue_rope(1, 1);
+#pragma unroll
+      for (int j = 0; j < kStages - 1; ++j) {
+        if (j < ntiles) {
+          issue_nope_bf16(j, j);
+          issue_rope(j, j);
+        }
       }
       for (int i = 0; i < ntiles; ++i) {
-        if (i + 1 < ntiles)
-          wait_vmcnt<kDmaPerTile>();  // tile i landed; tile i+1 may still be in flight
+        // tile i has landed once at most (tiles queued after it) x kDmaPerTile loads remain
+        const int younger = min(kStages - 2, ntiles - 1 - i);
+        if (younger >= 2)
+          wait_vmcnt<2 * kDmaPerTile>();
+        else if (younger == 1)
+          wait_vmcnt<kDmaPerTile>();
         else
           wait_vmcnt<0>();
         lds_barrier();  // every wave's part of tile i is in LDS; tile i-1's stage is free
-        if (i + 2 < ntiles) {
-          issue_nope_bf16(i + 2, (i + 2) % kStages);
-          issue_rope(i + 2, (i + 2) % kStages);
+        if (i + kStages - 1 < ntiles) {
+          issue_nope_bf16(i + kStages - 1, (i + kStages - 1) % kStages);
+          issue_rope(i + kStages - 1, (i + kStages - 1) % kStages);
         }
         if (wave_active) compute_tile(i, i % kStages);
       }
