@@ -38,9 +38,6 @@ def build_command(out_path: str) -> list:
         "-shared",
         # keep packed-fp32 VALU instructions out of the device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA results in VGPRs: the accumulators are rescaled in place by VALU code, and
-        # AGPR-form results would be copied across the register files on every tile
-        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wno-unused-command-line-argument",
         "-I", INCLUDE,
         "-I", CSRC,

@@ -12,15 +12,16 @@ constexpr int kNope = 512;          // kv_lora_rank
 constexpr int kRope = 64;           // qk_rope_dim
 constexpr int kBlock = 128;         // rows per cache page
 constexpr int kTile = 32;           // top-k slots per inner tile
-constexpr int kWaves = 4;           // waves per workgroup; each owns 16 query heads
+constexpr int kWaves = 4;           // waves per workgroup: two pairs, each pair owns 32 heads
 constexpr int kThreads = kWaves * 64;
-constexpr int kHeadsPerWave = 16;
-constexpr int kHeadsPerGroup = kWaves * kHeadsPerWave;  // heads of one workgroup (64)
+constexpr int kHeadsPerPair = 32;
+constexpr int kHeadsPerGroup = 2 * kHeadsPerPair;  // heads of one workgroup (64)
 constexpr int kMaxSlots = 2048;     // slots one workgroup compacts (topk partition size cap)
 constexpr int kMaxSplits = 16;      // top-k partitions per token
 constexpr int kMaxTopk = kMaxSlots * kMaxSplits;
-// Partial output of one (token, partition, head group): 4 waves x 32 d-blocks x 64 lanes x float4
-constexpr size_t kPartialBytes = (size_t)kWaves * 32 * 64 * 16;
+// Partial output of one (token, partition, head group), the register image of the O^T
+// accumulators: 4 waves x 8 blocks of 32 columns x 4 row quads x 64 lanes x float4
+constexpr size_t kPartialBytes = (size_t)kWaves * 8 * 4 * 64 * 16;
 constexpr size_t kPartialMlBytes = kHeadsPerGroup * 2 * sizeof(float);
 
 struct KernelArgs {

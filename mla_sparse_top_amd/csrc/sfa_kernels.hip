@@ -7,29 +7,38 @@
 // scale*S, times V = k_nope. How it is computed here is a gfx950 design of its own:
 //
 //   * A workgroup of 4 waves owns one (token, top-k partition, head group). A head group is 64
-//     of the query heads that share the single latent KV head; each wave holds 16 of them. The
-//     two head groups of a 128-head token are adjacent work items, so they run on the same XCD
-//     and the second one's gather mostly hits that XCD's L2.
+//     of the query heads that share the single latent KV head. The waves form two pairs; a pair
+//     owns 32 heads, and its two waves split the work along d: wave "half" h computes the part
+//     of the scores over its 288 columns of [nope|rope] (nope 256h..256h+255, rope 32h..32h+31)
+//     and accumulates the output columns 256h..256h+255. The two partial score tiles are
+//     summed through LDS, so both waves of a pair see the same scores and run the same softmax.
+//     Every 32-key tile of K and V is thus read from LDS once per pair instead of once per wave,
+//     and the MFMA is the 32x32x16 shape (32 keys x 32 heads).
+//   * The two head groups of a 128-head token are adjacent work items, so they run on the same
+//     XCD and the second one's gather mostly hits that XCD's L2.
 //   * Resolve + compaction: the partition's slots are resolved (index -> block_table -> row),
 //     masked slots are dropped and the valid rows are packed in order into an LDS list. Tiles
 //     are then dense: padding costs no loads and no MFMA, and a tile of invalid slots never runs.
-//   * Gather: each 32-row tile is fetched with LDS-DMA (global_load_lds_dwordx4). One wave
-//     instruction moves one 1 KB nope row, or eight 128 B rope rows, fully coalesced, with no
-//     VGPR staging. Four LDS stages keep three tiles in flight while a fourth is computed. INT8
-//     rows are fetched to registers a tile ahead instead, dequantised (fp32 multiply by the
-//     group scale, round-to-nearest-even to bf16) and written into the same bf16 LDS layout.
-//   * S^T = K . Q^T with v_mfma_f32_16x16x32_bf16: keys on M, heads on N, d as the reduction.
-//     Q sits in registers for the whole partition. Each lane then holds one head and 8 of a
-//     tile's 32 keys, so the softmax row max and row sum need two cross-lane steps.
+//   * Gather: each 32-row tile is fetched with LDS-DMA (global_load_lds_dwordx4) into one of
+//     three LDS stages. One wave instruction moves one 1 KB nope row, or eight 128 B rope rows,
+//     fully coalesced, with no VGPR staging. INT8 rows are fetched to registers instead,
+//     dequantised (fp32 multiply by the group scale, round-to-nearest-even to bf16) and written
+//     into the same bf16 LDS layout.
+//   * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: keys on M, heads on N, d as the reduction.
+//     Q sits in registers for the whole partition. Each lane then holds one head and 16 of a
+//     tile's 32 keys, so the softmax row max and row sum need one cross-lane step.
 //   * Online softmax over tiles (running max / running sum). The running max is only moved
 //     when a tile's max exceeds it by more than 2^8 (exp2 domain), so O is rescaled rarely; the
 //     final O / l is unchanged.
-//   * O^T += V^T . P^T, again 16x16x32 MFMA. P^T comes straight from the S^T accumulator
+//   * O^T += V^T . P^T, again 32x32x16 MFMA. P^T comes straight from the S^T accumulator
 //     registers (no shuffle). V^T fragments are read from the row-major K tile with
 //     ds_read_b64_tr_b16 (LDS transpose read), so no transposed copy exists. P is split into
 //     bf16 hi + lo parts, two MFMAs on the same V fragment, so it keeps about 16 significant
 //     bits instead of 8: a single bf16 P does not meet the 5e-3 / 1e-4 accuracy standard when
 //     few keys carry the weight.
+//   * The loop is software-pipelined: while the MFMAs of the next tile's S^T run, the VALU
+//     computes the current tile's softmax, and then the current tile's PV MFMAs run. One
+//     workgroup barrier per tile.
 //   * Partitions of one (token, head group) merge in the same kernel: each writes its
 //     unnormalised O, its running max and its running sum. The last to arrive (counted with a
 //     device-scope atomic) combines all of them in partition order, so the result does not
@@ -37,10 +46,16 @@
 //     prefill update rule applied across partitions.
 //   * Work items are mapped so that consecutive logical ids land on the same XCD and share its
 //     L2: the hardware deals workgroups to the 8 XCDs round-robin.
+//
+// The MFMAs are issued from inline assembly so that the O accumulators stay in AGPRs and the
+// score accumulators in VGPRs without register-file copies. The compiler does not look inside
+// inline assembly for hazards, so the required wait states are written out next to each use.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "sfa_internal.h"
 
@@ -51,6 +66,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) char lds_char_t;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
 
@@ -58,41 +74,51 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
 //   nope: 32 rows x 1024 B. The 16-byte chunk c of row k sits at chunk c ^ nope_swz(k) (the XOR
 //         only touches the low 4 bits of the chunk index). With this swizzle, neither the
 //         16-byte reads of the QK^T operand (16 rows, same chunk) nor the 8-byte transpose
-//         reads of the PV operand (8 rows x 2 chunks) repeat a bank within one LDS cycle.
-//   rope: 32 rows x 128 B, chunk c of row k at c ^ rope_swz(k). One DMA instruction fills eight
-//         consecutive rope rows.
+//         reads of the PV operand (4 rows x 2 chunks per 16 lanes) repeat a bank.
+//   rope: 32 rows x 128 B, chunk c of row k at c ^ rope_swz(k).
 constexpr int kNopeRowBytes = kNope * 2;
 constexpr int kRopeRowBytes = kRope * 2;
 constexpr int kNopeTileBytes = kTile * kNopeRowBytes;
 constexpr int kRopeTileBytes = kTile * kRopeRowBytes;
 constexpr int kStageBytes = kNopeTileBytes + kRopeTileBytes;
-constexpr int kStagesBf16 = 4;
-constexpr int kStagesInt8 = 2;
-constexpr int kDmaPerTile = 9;             // per wave: 8 nope rows + 1 rope instruction
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: p stays <= 256 between rescales
-constexpr int kQSteps = (kNope + kRope) / 32;  // 18 MFMA k-steps over d
-// LDS operand loads kept in flight ahead of the MFMA that consumes them
-constexpr int kQkDepth = 6;
+constexpr int kStages = 3;
+constexpr int kXBytes = 64 * 16 * 4;           // one wave's partial S^T tile (64 lanes x 16 fp32)
+constexpr float kRescaleThreshold = 8.0f;      // log2 units: p stays <= 256 between rescales
+constexpr int kQkSteps = (kNope + kRope) / 32;  // 18 k-steps of 16 over a wave's 288 columns
+constexpr int kQkDepth = 8;                    // LDS operand loads in flight ahead of the MFMA
 constexpr int kPvDepth = 4;
 
-__device__ __forceinline__ int nope_swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
+static_assert(kStages * kStageBytes + 2 * kWaves * kXBytes + kMaxSlots * 4 + 64 <= 160 * 1024,
+              "LDS budget of one workgroup");
+
+__device__ __forceinline__ int nope_swz(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
 __device__ __forceinline__ int rope_swz(int key) { return (key >> 1) & 7; }
 
 // LDS-DMA of 16 bytes per lane: lane L's bytes land at lds_addr + 16*L. lds_addr must be
-// wave-uniform (it goes through M0). Issued from inline asm so that the compiler does not
-// wait for the whole vector-memory queue before every LDS read. Completion is tracked
-// explicitly with wait_vmcnt, and cross-wave visibility with lds_barrier.
+// wave-uniform (it goes through M0, which the asm declares clobbered; M0 needs one wait state
+// between its write and the DMA). Issued from inline asm so that the compiler does not wait
+// for the whole vector-memory queue before every LDS read. Completion is tracked explicitly
+// with wait_vmcnt, and cross-wave visibility with lds_barrier.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gaddr), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset: used for the
+// nope rows, where one instruction reads one whole cache row.
+__device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gaddr), "s"(lds_addr)
-      : "memory");
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "memory", "m0");
 }
 
 template <int N>
@@ -100,8 +126,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Workgroup barrier that orders LDS traffic only. Outstanding global loads (register prefetch,
-// LDS-DMA into other stages) stay in flight across it.
+// Workgroup barrier that orders LDS traffic only. Outstanding global loads (the register
+// staging of later tiles) stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -113,27 +139,100 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// S^T += K . Q^T steps: the accumulator in VGPRs, the K fragment in VGPRs (fresh from LDS), the
+// Q^T fragment in AGPRs. Consecutive steps accumulate into the same registers, which the
+// hardware chains back to back; the chain starts from 0. The leading pad covers a VALU write of
+// an operand right before (a register copy the compiler may place there).
+__device__ __forceinline__ void mfma_qk_first(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_qk(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+// Before anything else reads the chain's result: a 32x32x16 result needs 12 wait states before
+// a VALU or LDS read of it; this gives 20.
+__device__ __forceinline__ void mfma_qk_drain(floatx16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc));
+}
+
+// O^T += V^T . P^T step on an AGPR-resident accumulator, tied in place. Its operands were just
+// produced by VALU (P^T hi/lo conversion) or LDS, so the MFMA is preceded by 3 wait states.
+__device__ __forceinline__ void mfma_pv(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// O *= alpha on the AGPR-resident accumulators, in place: each element is read to a VGPR,
+// scaled and written back by inline asm, so no compiler-generated VALU ever touches O (which
+// would make the compiler keep O in VGPRs and copy it around every tile). Pads: the last MFMA
+// that wrote O needs 12 wait states before an AGPR read (20 given); the MFMA that next reads O
+// as its accumulator needs 2 after the AGPR write (4 given).
+template <int N>
+__device__ __forceinline__ void rescale_agprs(floatx16 (&acc)[N], float alpha) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+#pragma unroll
+  for (int d = 0; d < N; ++d) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float tmp;
+      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                   : "+a"(acc[d][r]), "=&v"(tmp)
+                   : "v"(alpha));
+    }
+  }
+  asm volatile("s_nop 3" ::: "memory");
+}
+
+// Pins the O accumulators to AGPRs at a point of the program (where O is carried from one tile
+// to the next); without it the register allocator may carry O in VGPRs and copy it around.
+template <int N>
+__device__ __forceinline__ void pin_agprs(floatx16 (&acc)[N]) {
+#pragma unroll
+  for (int d = 0; d < N; ++d) asm volatile("" : "+a"(acc[d]));
+}
+
+// Before compiler-generated code reads O after the MFMAs: 20 wait states after the last write.
+template <int N>
+__device__ __forceinline__ void mfma_pv_drain(floatx16 (&acc)[N]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+  pin_agprs(acc);
 }
 
 __device__ __forceinline__ shortx4 lds_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(lds_char_t*)p);
 }
 
+// Lanes l and l ^ 32 hold the same head: combine their values. v_permlane32_swap hands each lane
+// its partner's value; both results are the same in both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// An INT8 tile's nope rows on their way from HBM to LDS: this wave's 8 rows and their scales.
+struct StagedInt8 {
+  uint2 nope[8];
+  float scale[8];
+};
+
 template <bool kInt8>
 __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const KernelArgs a) {
-  constexpr int kStages = kInt8 ? kStagesInt8 : kStagesBf16;
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
-  __shared__ int32_t s_rows[kMaxSlots];
+  __shared__ __attribute__((aligned(16))) char xbuf[2 * kWaves * kXBytes];
+  __shared__ __attribute__((aligned(16))) int32_t s_rows[kMaxSlots];
   __shared__ int32_t s_wcnt[kWaves];
   __shared__ int32_t s_last;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int lane = tid & 63;
-  const int n = lane & 15;  // row (A operand) or column (B operand, result) of the 16x16 MFMA
-  const int kg = lane >> 4; // k-group of an operand / row quad of a result
+  const int n = lane & 31;  // row (A operand) or column (B operand, result) of the 32x32 MFMA
+  const int g = lane >> 5;  // k-group of an operand / row-quad parity of a result
+  const int pair = wave >> 1;
+  const int half = wave & 1;
 
   // ---- work item: XCD-aware remap of the workgroup id, then (token, partition, head group)
   const int nwg = gridDim.x;
@@ -148,27 +247,42 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   if (a.reverse) t = a.n_tokens - 1 - t;
   const int b = t / a.s1;
 
-  const int h0 = hg * kHeadsPerGroup + wave * kHeadsPerWave;  // first head of this wave
-  const bool wave_active = h0 < a.n_q;                         // wave-uniform
-  const int h = h0 + n;                                         // this lane's head
+  const int hp0 = hg * kHeadsPerGroup + pair * kHeadsPerPair;  // first head of this pair
+  const bool pair_active = hp0 < a.n_q;                         // wave-uniform
+  const int h = hp0 + n;                                         // this lane's head
   const bool head_ok = h < a.n_q;
 
-  // ---- Q^T fragments (B operand, k = d): lane (n, kg) holds d in [32c + 8kg, 32c + 8kg + 8).
+  // The scores are used as fma(S, c, -m) with c = |scale * log2 e|. A negative scale is moved
+  // into Q by flipping the sign bits of its bf16 elements, which is exact.
+  const float c_scale = fabsf(a.scale_log2);
+  const uint32_t q_sign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+
+  // ---- Q^T fragments (B operand, k = d): step c < 16 covers nope chunks 32*half + 2c + {0, 1},
+  // steps 16 and 17 rope chunks 4*half + 2(c - 16) + {0, 1}; lane (n, g) holds chunk +g.
   // Issued first so that their latency overlaps the slot resolution below.
-  bf16x8 qf[kQSteps];
+  bf16x8 qf[kQkSteps];
   {
-    const bf16x8 zero = {};
+    const uint4 zero = {0u, 0u, 0u, 0u};
     const int64_t qrow = (int64_t)t * a.n_q + (head_ok ? h : 0);
-    const bf16x8* qn = reinterpret_cast<const bf16x8*>(a.q_nope + qrow * kNope);
-    const bf16x8* qr = reinterpret_cast<const bf16x8*>(a.q_rope + qrow * kRope);
+    const uint4* qn = reinterpret_cast<const uint4*>(a.q_nope + qrow * kNope);
+    const uint4* qr = reinterpret_cast<const uint4*>(a.q_rope + qrow * kRope);
+    uint4 qv[kQkSteps];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) qf[c] = head_ok ? qn[4 * c + kg] : zero;
+    for (int c = 0; c < 16; ++c) qv[c] = head_ok ? qn[32 * half + 2 * c + g] : zero;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) qf[16 + c] = head_ok ? qr[4 * c + kg] : zero;
-    // Q is only ever an MFMA B operand, which may come from AGPRs: pin it there and leave the
-    // architectural VGPRs to the in-flight LDS operands of the MFMA pipelines.
+    for (int c = 0; c < 2; ++c) qv[16 + c] = head_ok ? qr[4 * half + 2 * c + g] : zero;
 #pragma unroll
-    for (int c = 0; c < kQSteps; ++c) asm volatile("" : "+a"(qf[c]));
+    for (int c = 0; c < kQkSteps; ++c) {
+      qv[c].x ^= q_sign;
+      qv[c].y ^= q_sign;
+      qv[c].z ^= q_sign;
+      qv[c].w ^= q_sign;
+      qf[c] = __builtin_bit_cast(bf16x8, qv[c]);
+    }
+    // Q is only ever an MFMA B operand, which may come from AGPRs: keep it there and leave the
+    // VGPRs to the in-flight LDS operands and the softmax.
+#pragma unroll
+    for (int c = 0; c < kQkSteps; ++c) asm volatile("" : "+a"(qf[c]));
   }
 
   // ---- resolve this partition's slots and compact the valid rows into s_rows, in slot order.
@@ -215,247 +329,431 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     off += (w < wave) ? c : 0;
     n_valid += c;
   }
+  const int ntiles = (n_valid + kTile - 1) / kTile;
+  int last_row = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    if (rowv[i] >= 0) s_rows[off++] = rowv[i];
+    if (rowv[i] >= 0) {
+      s_rows[off++] = rowv[i];
+      last_row = rowv[i];
+    }
+  }
+  // The thread that placed the last valid row repeats it up to the end of the last tile, so
+  // every tile reads 32 real rows; the scores of the repeats are masked out.
+  if (cnt > 0 && off == n_valid) {
+    for (int q = n_valid; q < ntiles * kTile; ++q) s_rows[q] = last_row;
   }
   lds_barrier();
-  const int ntiles = (n_valid + kTile - 1) / kTile;
 
-  floatx4 oacc[32];  // O^T block db: lane (n, kg) holds d = 16*db + 4*kg + r of head h
+  // O^T block dc: reg r holds column d = 256*half + 32*dc + 8*(r/4) + 4g + (r%4) of head h
+  floatx16 oacc[8];
 #pragma unroll
-  for (int db = 0; db < 32; ++db) oacc[db] = floatx4{};
-  float m_run = -INFINITY;
+  for (int dc = 0; dc < 8; ++dc) oacc[dc] = floatx16{};
+  pin_agprs(oacc);
+  float m_run = -INFINITY;  // running max (exp2 domain) that p and O are currently relative to
   float l_run = 0.f;
 
+  // ---- loaders: wave w carries rows 8w..8w+7 of each tile
   const uint32_t smem_lds = (uint32_t)(uintptr_t)((lds_char_t*)smem);
-
-  // ---- loaders
   // rope: lane L fetches chunk ((L & 7) ^ rope_swz(key)) of key = 8*wave + L/8.
-  auto issue_rope = [&](int tile, int stage) __attribute__((always_inline)) {
+  auto issue_rope = [&](int tile, uint32_t stage_off) __attribute__((always_inline)) {
     const int key = wave * 8 + (lane >> 3);
-    const int slot = min(tile * kTile + key, n_valid - 1);
-    const int row = s_rows[slot];
+    const int row = s_rows[tile * kTile + key];
     const char* src = reinterpret_cast<const char*>(a.k_rope) + (int64_t)row * kRopeRowBytes +
                       16 * ((lane & 7) ^ rope_swz(key));
-    dma16(src, __builtin_amdgcn_readfirstlane(smem_lds + stage * kStageBytes + kNopeTileBytes +
-                                              wave * 8 * kRopeRowBytes));
+    dma16(src, smem_lds + stage_off + kNopeTileBytes + wave * 8 * kRopeRowBytes);
   };
-  // bf16 nope: wave w moves rows 8w..8w+7 of the tile, one 1 KB row per instruction; lane L
-  // fills physical chunk L, i.e. fetches logical chunk L ^ nope_swz(key). Slots past n_valid
-  // repeat the last valid row; their scores are masked to -inf, so they contribute exactly zero.
-  auto issue_nope_bf16 = [&](int tile, int stage) __attribute__((always_inline)) {
+  // The wave's 8 rows of a tile, as wave-uniform values (one 32-byte broadcast read).
+  auto tile_rows = [&](int tile, int (&rows)[8]) __attribute__((always_inline)) {
+    const int4* rp = reinterpret_cast<const int4*>(s_rows + tile * kTile + wave * 8);
+    const int4 r0 = rp[0], r1 = rp[1];
+    rows[0] = __builtin_amdgcn_readfirstlane(r0.x);
+    rows[1] = __builtin_amdgcn_readfirstlane(r0.y);
+    rows[2] = __builtin_amdgcn_readfirstlane(r0.z);
+    rows[3] = __builtin_amdgcn_readfirstlane(r0.w);
+    rows[4] = __builtin_amdgcn_readfirstlane(r1.x);
+    rows[5] = __builtin_amdgcn_readfirstlane(r1.y);
+    rows[6] = __builtin_amdgcn_readfirstlane(r1.z);
+    rows[7] = __builtin_amdgcn_readfirstlane(r1.w);
+  };
+  // bf16 nope: one 1 KB row per instruction; lane L fills physical chunk L, i.e. fetches
+  // logical chunk L ^ nope_swz(key).
+  auto issue_nope_bf16 = [&](int tile, uint32_t stage_off) __attribute__((always_inline)) {
+    int rows[8];
+    tile_rows(tile, rows);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int key = wave * 8 + k;
-      const int slot = min(tile * kTile + key, n_valid - 1);
-      const int row = s_rows[slot];
-      const char* src = reinterpret_cast<const char*>(a.k_nope) + (int64_t)row * kNopeRowBytes +
-                        16 * (lane ^ nope_swz(key));
-      dma16(src, __builtin_amdgcn_readfirstlane(smem_lds + stage * kStageBytes + key * kNopeRowBytes));
+      const char* base = reinterpret_cast<const char*>(a.k_nope) + (int64_t)rows[k] * kNopeRowBytes;
+      dma16_sbase(base, (uint32_t)(16 * (lane ^ nope_swz(key))), smem_lds + stage_off + key * kNopeRowBytes);
     }
   };
-  // int8 nope: lane L holds columns [8L, 8L+8) of rows 8w..8w+7 and the scale of group L/16.
-  uint2 q8[8];
-  float sc8[8];
+  // int8 nope: lane L holds columns [8L, 8L+8) of each row and the scale of their group L/16.
+  StagedInt8 st8;
   auto load_nope_int8 = [&](int tile) __attribute__((always_inline)) {
+    int rows[8];
+    tile_rows(tile, rows);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int key = wave * 8 + k;
-      const int slot = min(tile * kTile + key, n_valid - 1);
-      const int row = s_rows[slot];
-      q8[k] = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(a.k_nope) +
-                                              (int64_t)row * kNope + 8 * lane);
-      sc8[k] = a.k_scales[(int64_t)row * 4 + (lane >> 4)];
+      st8.nope[k] = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(a.k_nope) +
+                                                    (int64_t)rows[k] * kNope + 8 * lane);
+      st8.scale[k] = a.k_scales[(int64_t)rows[k] * 4 + (lane >> 4)];
     }
   };
-  // Dequant: code -> fp32 (exact), times the fp32 group scale (RNE), -> bf16 (RNE); the
-  // 16-byte chunk of columns [8L, 8L+8) is chunk L of the row, stored swizzled.
-  auto store_nope_int8 = [&](int stage) __attribute__((always_inline)) {
+  // Dequant: code -> fp32 (exact), times the fp32 group scale (RNE), -> bf16 (RNE); the 16-byte
+  // chunk of columns [8L, 8L+8) is chunk L of the row, stored swizzled.
+  auto store_nope_int8 = [&](uint32_t stage_off) __attribute__((always_inline)) {
+    char* base = smem + stage_off;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int key = wave * 8 + k;
-      const uint32_t lo = q8[k].x, hi = q8[k].y;
-      const float s = sc8[k];
+      const uint32_t lo = st8.nope[k].x, hi = st8.nope[k].y;
+      const float sc = st8.scale[k];
       uint4 v;
-      v.x = pack_bf16x2((float)(int8_t)(lo)*s, (float)(int8_t)(lo >> 8) * s);
-      v.y = pack_bf16x2((float)(int8_t)(lo >> 16) * s, (float)(int8_t)(lo >> 24) * s);
-      v.z = pack_bf16x2((float)(int8_t)(hi)*s, (float)(int8_t)(hi >> 8) * s);
-      v.w = pack_bf16x2((float)(int8_t)(hi >> 16) * s, (float)(int8_t)(hi >> 24) * s);
-      *reinterpret_cast<uint4*>(smem + stage * kStageBytes + key * kNopeRowBytes + 16 * (lane ^ nope_swz(key))) = v;
+      v.x = pack_bf16x2((float)(int8_t)(lo)*sc, (float)(int8_t)(lo >> 8) * sc);
+      v.y = pack_bf16x2((float)(int8_t)(lo >> 16) * sc, (float)(int8_t)(lo >> 24) * sc);
+      v.z = pack_bf16x2((float)(int8_t)(hi)*sc, (float)(int8_t)(hi >> 8) * sc);
+      v.w = pack_bf16x2((float)(int8_t)(hi >> 16) * sc, (float)(int8_t)(hi >> 24) * sc);
+      *reinterpret_cast<uint4*>(base + key * kNopeRowBytes + 16 * (lane ^ nope_swz(key))) = v;
     }
   };
-
-  // ---- one tile: S^T = K Q^T, online softmax, O^T += V^T P^T
-  // QK^T A operand: lane (n, kg) reads key 16*kb + n, logical chunk 4c + kg.
-  // PV A operand (transpose read, instruction half hh): lane (kg, j = n) points at key
-  // 16*hh + 4*kg + j/4 and column 16*db + 4*(j & 3); it receives column 16*db + j of keys
-  // 16*hh + 4*kg + 0..3, which are exactly the keys its P^T operand holds.
-  const int tr_key = 4 * kg + (n >> 2);
-  const int tr_swz = nope_swz(tr_key);  // the same for tr_key + 16
-  const int tr_sub = (n & 3);           // 4-column group inside the 16-column block
-
-  auto compute_tile = [&](int tile, int stage) __attribute__((always_inline)) {
-    const char* ks = smem + stage * kStageBytes;
-    const char* rs = ks + kNopeTileBytes;
-    floatx4 s[2] = {floatx4{}, floatx4{}};
-    // A operand of step c (= 2*kstep + kb): key 16*kb + n, logical chunk 4*kstep + kg. Loads run
-    // two MFMAs ahead of their use, and each step is fenced so the scheduler keeps that shape.
-    auto qk_operand = [&](int c) __attribute__((always_inline)) -> bf16x8 {
-      const int kstep = c >> 1, kb = c & 1;
-      const int key = 16 * kb + n;
-      if (kstep < 16)
-        return *reinterpret_cast<const bf16x8*>(ks + key * kNopeRowBytes + 16 * ((4 * kstep + kg) ^ nope_swz(key)));
-      return *reinterpret_cast<const bf16x8*>(rs + key * kRopeRowBytes + 16 * ((4 * (kstep - 16) + kg) ^ rope_swz(key)));
-    };
-    constexpr int kQkOps = 2 * kQSteps;
-    bf16x8 qa[kQkDepth];
-#pragma unroll
-    for (int c = 0; c < kQkDepth; ++c) qa[c] = qk_operand(c);
-#pragma unroll
-    for (int c = 0; c < kQkOps; ++c) {
-      const bf16x8 cur = qa[c % kQkDepth];
-      if (c + kQkDepth < kQkOps) qa[c % kQkDepth] = qk_operand(c + kQkDepth);
-      s[c & 1] = mfma16(cur, qf[c >> 1], s[c & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // result s[kb][r] holds key 16*kb + 4*kg + r of the tile, head h
-    const int nk = n_valid - tile * kTile;
-    float p[8];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = 16 * kb + 4 * kg + r;
-        const float x = key < nk ? s[kb][r] * a.scale_log2 : -INFINITY;
-        p[4 * kb + r] = x;
-        mt = fmaxf(mt, x);
-      }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool need = mt > m_run + kRescaleThreshold;
-    if (__any(need)) {
-      const float m_new = need ? mt : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int db = 0; db < 32; ++db) {
-        oacc[db] *= alpha;  // one block at a time keeps the AGPR<->VGPR round trip short
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    float ls = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(p[i] - m_run);
-      ls += p[i];
-    }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    l_run += ls;
-
-    // P^T operand: lane (n, kg) element i is key 4kg + i (i < 4) or 16 + 4kg + (i - 4).
-    // hi = bf16(p), lo = bf16(p - hi).
-    bf16x8 ph, pl;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 hb = (__bf16)p[i];
-      ph[i] = hb;
-      pl[i] = (__bf16)(p[i] - (float)hb);
-    }
-
-    auto pv_operand = [&](int db) __attribute__((always_inline)) -> bf16x8 {
-      const int chunk = 2 * db + (tr_sub >> 1);
-      const int off = 16 * (chunk ^ tr_swz) + 8 * (tr_sub & 1);
-      const shortx4 v0 = lds_tr16(ks + tr_key * kNopeRowBytes + off);
-      const shortx4 v1 = lds_tr16(ks + (tr_key + 16) * kNopeRowBytes + off);
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8 va[kPvDepth];
-#pragma unroll
-    for (int db = 0; db < kPvDepth; ++db) va[db] = pv_operand(db);
-#pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      const bf16x8 cur = va[db % kPvDepth];
-      if (db + kPvDepth < 32) va[db % kPvDepth] = pv_operand(db + kPvDepth);
-      oacc[db] = mfma16(cur, ph, oacc[db]);
-      oacc[db] = mfma16(cur, pl, oacc[db]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // ---- main loop over tiles
-  if (ntiles > 0) {
-    if constexpr (!kInt8) {
-#pragma unroll
-      for (int j = 0; j < kStages - 1; ++j) {
-        if (j < ntiles) {
-          issue_nope_bf16(j, j);
-          issue_rope(j, j);
-        }
-      }
-      for (int i = 0; i < ntiles; ++i) {
-        // tile i has landed once at most (tiles queued after it) x kDmaPerTile loads remain
-        const int younger = min(kStages - 2, ntiles - 1 - i);
-        if (younger >= 2)
-          wait_vmcnt<2 * kDmaPerTile>();
-        else if (younger == 1)
-          wait_vmcnt<kDmaPerTile>();
-        else
-          wait_vmcnt<0>();
-        lds_barrier();  // every wave's part of tile i is in LDS; tile i-1's stage is free
-        if (i + kStages - 1 < ntiles) {
-          issue_nope_bf16(i + kStages - 1, (i + kStages - 1) % kStages);
-          issue_rope(i + kStages - 1, (i + kStages - 1) % kStages);
-        }
-        if (wave_active) compute_tile(i, i % kStages);
-      }
+  // Starts the fetch of a tile into a stage (INT8: the nope part into registers, written to the
+  // stage by finish_tile).
+  auto start_tile = [&](int tile, uint32_t stage_off) __attribute__((always_inline)) {
+    if constexpr (kInt8) {
+      load_nope_int8(tile);
     } else {
-      issue_rope(0, 0);
-      load_nope_int8(0);
-      for (int i = 0; i < ntiles; ++i) {
-        wait_vmcnt<0>();
-        store_nope_int8(i & 1);
-        lds_barrier();
-        if (i + 1 < ntiles) {
-          issue_rope(i + 1, (i + 1) & 1);
-          load_nope_int8(i + 1);
-        }
-        if (wave_active) compute_tile(i, i & 1);
+      issue_nope_bf16(tile, stage_off);
+    }
+    issue_rope(tile, stage_off);
+  };
+  // The same in three parts, so that it can be spread between MFMAs.
+  int rows_next[8];
+  auto start_tile_part = [&](int tile, uint32_t stage_off, int part) __attribute__((always_inline)) {
+    if (part == 0) tile_rows(tile, rows_next);
+#pragma unroll
+    for (int k = 3 * part; k < min(8, 3 * part + 3); ++k) {
+      if constexpr (kInt8) {
+        st8.nope[k] = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(a.k_nope) +
+                                                      (int64_t)rows_next[k] * kNope + 8 * lane);
+        st8.scale[k] = a.k_scales[(int64_t)rows_next[k] * 4 + (lane >> 4)];
+      } else {
+        const int key = wave * 8 + k;
+        const char* base = reinterpret_cast<const char*>(a.k_nope) + (int64_t)rows_next[k] * kNopeRowBytes;
+        dma16_sbase(base, (uint32_t)(16 * (lane ^ nope_swz(key))), smem_lds + stage_off + key * kNopeRowBytes);
+      }
+    }
+    if (part == 2) issue_rope(tile, stage_off);
+  };
+  // Completes it: waits for this wave's loads of the tile (INT8: and writes it to the stage).
+  auto finish_tile = [&](uint32_t stage_off) __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    if constexpr (kInt8) store_nope_int8(stage_off);
+  };
+
+  // ---- per-lane LDS offsets of the MFMA operands. The swizzle XOR only touches the low 4 bits
+  // of a chunk index, so the QK^T operand of step c < 16 is qk_off[c & 7] + 256*(c >> 3) and the
+  // PV operand of (dc, kb, q) is pv_off[q][dc & 3] + 256*(dc >> 2) + 16 KB*kb.
+  // QK^T A operand: lane (n, g) reads key n, logical chunk 32*half + 2c + g.
+  // PV A operand via transpose reads: lane (G = lane/16, j = lane%16) of read q points at key
+  // 16*kb + 8*q + 4*g + j/4 and column 256*half + 32*dc + 16*(G & 1) + 4*(j & 3); it receives
+  // column 32*dc + n of keys 16*kb + 8*q + 4*g + 0..3: the keys its P^T operand holds.
+  int qk_off[8], rope_off[2], pv_off[2][4];
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) qk_off[cc] = n * kNopeRowBytes + 512 * half + 16 * ((2 * cc + g) ^ nope_swz(n));
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    rope_off[c] = kNopeTileBytes + n * kRopeRowBytes + 16 * ((4 * half + 2 * c + g) ^ rope_swz(n));
+  {
+    const int j = lane & 15;
+    const int tr_key = 4 * g + (j >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int dl = 0; dl < 4; ++dl) {
+        const int key = tr_key + 8 * q;
+        const int col = 32 * dl + tr_col;  // inside the 128-column group, wave half added below
+        pv_off[q][dl] = key * kNopeRowBytes + 512 * half + 16 * ((col >> 3) ^ nope_swz(key)) + 2 * (col & 7);
       }
     }
   }
 
-  // ---- epilogue: oacc[db][r] is column d = 16*db + 4*kg + r of head h
-  if (a.n_splits == 1) {
-    if (wave_active && head_ok) {
-      const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-      uint16_t* o = a.out + ((int64_t)t * a.n_q + h) * kNope + 4 * kg;
+  const char* smem_c = smem;
+  auto qk_operand = [&](uint32_t stage_off, int c) __attribute__((always_inline)) -> bf16x8 {
+    const char* ks = smem_c + stage_off;
+    if (c < 16) return *reinterpret_cast<const bf16x8*>(ks + qk_off[c & 7] + 256 * (c >> 3));
+    return *reinterpret_cast<const bf16x8*>(ks + rope_off[c - 16]);
+  };
+  // u = 8*kb + dc
+  auto pv_operand = [&](uint32_t stage_off, int u) __attribute__((always_inline)) -> bf16x8 {
+    const int dc = u & 7, kb = u >> 3;
+    const char* ks = smem_c + stage_off + 256 * (dc >> 2) + 16 * kNopeRowBytes * kb;
+    const shortx4 v0 = lds_tr16(ks + pv_off[0][dc & 3]);
+    const shortx4 v1 = lds_tr16(ks + pv_off[1][dc & 3]);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // The partial S^T tile exchange: [parity][wave][row quad][lane] float4.
+  auto x_write = [&](int parity, const floatx16& s) __attribute__((always_inline)) {
+    floatx4* xp = reinterpret_cast<floatx4*>(xbuf + (parity * kWaves + wave) * kXBytes) + lane;
 #pragma unroll
-      for (int db = 0; db < 32; ++db) {
-        uint2 v;
-        v.x = pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv);
-        v.y = pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv);
-        *reinterpret_cast<uint2*>(o + 16 * db) = v;
+    for (int q = 0; q < 4; ++q) xp[64 * q] = floatx4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+  };
+
+  // S^T(tile) over this wave's half of d, into s
+  auto qk_tile = [&](uint32_t stage_off, floatx16& s) __attribute__((always_inline)) {
+    bf16x8 qa[kQkDepth];
+#pragma unroll
+    for (int c = 0; c < kQkDepth; ++c) qa[c] = qk_operand(stage_off, c);
+#pragma unroll
+    for (int c = 0; c < kQkSteps; ++c) {
+      const bf16x8 cur = qa[c % kQkDepth];
+      if (c + kQkDepth < kQkSteps) qa[c % kQkDepth] = qk_operand(stage_off, c + kQkDepth);
+      if (c == 0)
+        mfma_qk_first(s, cur, qf[0]);
+      else
+        mfma_qk(s, cur, qf[c]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  floatx16 s_own;  // this wave's partial S^T of the tile whose softmax runs next
+  // LDS offsets of the three stages: tile ti (PV), tile ti + 1 (S^T), and the free one that
+  // receives tile ti + 2. They rotate every tile.
+  uint32_t off_cur = 0, off_next = kStageBytes, off_free = 2 * kStageBytes;
+  // The last kTail PV steps of a tile run after the barrier that ends its interval, while the
+  // next interval's first LDS reads and DMA issue are in flight. Their V operands are read into
+  // registers before that barrier, so the stage they came from may be refilled right after it.
+  constexpr int kTail = kPvDepth;
+  bf16x8 tail_v[kTail];
+  bf16x8 tail_ph, tail_pl;  // P^T of key half 1, which those steps use
+  auto tail_step = [&](int j) __attribute__((always_inline)) {
+    mfma_pv(oacc[(16 - kTail + j) & 7], tail_v[j], tail_ph);
+    mfma_pv(oacc[(16 - kTail + j) & 7], tail_v[j], tail_pl);
+  };
+
+  // One tile interval:
+  //   1. LDS reads of the partner's partial S^T(ti) and of the first S^T(ti + 1) operands;
+  //   2. the PV tail of tile ti - 1, interleaved with the DMA issue of tile ti + 2 into the
+  //      free stage;
+  //   3. the S^T MFMAs of tile ti + 1 interleaved with the softmax of tile ti;
+  //   4. the PV MFMAs of tile ti up to its tail, with the exchange write of S^T(ti + 1) in
+  //      between;
+  //   5. wait for this wave's DMA of tile ti + 2, barrier.
+  // After the last tile the S^T of a nonexistent tile is computed on stale LDS and thrown away,
+  // which keeps a single copy of this code.
+  auto interval = [&](int ti) __attribute__((always_inline)) {
+    pin_agprs(oacc);
+    const bool do_dma = ti >= 1 && ti + 2 < ntiles;
+    const bool do_tail = ti >= 1 && pair_active;
+    floatx4 xq[4];
+    bf16x8 qa[kQkDepth];
+    if (pair_active) {
+      const floatx4* xp =
+          reinterpret_cast<const floatx4*>(xbuf + ((ti & 1) * kWaves + (wave ^ 1)) * kXBytes) + lane;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xq[q] = xp[64 * q];
+#pragma unroll
+      for (int c = 0; c < kQkDepth; ++c) qa[c] = qk_operand(off_next, c);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int kSlots = kTail > 3 ? kTail : 3;  // three DMA parts, kTail PV steps
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      if (do_dma && j < 3) start_tile_part(ti + 2, off_free, j);
+      if (do_tail && j < kTail) tail_step(j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (pair_active) {
+      floatx16 s_next;
+      auto qk_step = [&](int c) __attribute__((always_inline)) {
+        const bf16x8 cur = qa[c % kQkDepth];
+        if (c + kQkDepth < kQkSteps) qa[c % kQkDepth] = qk_operand(off_next, c + kQkDepth);
+        if (c == 0)
+          mfma_qk_first(s_next, cur, qf[0]);
+        else
+          mfma_qk(s_next, cur, qf[c]);
+      };
+
+      // s[r] is key 8*(r/4) + 4g + (r%4) of the tile, head h
+      const int nk = n_valid - ti * kTile;
+      const bool tail = nk < kTile;  // wave-uniform: only the last tile has masked keys
+      float x[16];
+      qk_step(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = s_own[r] + xq[r >> 2][r & 3];
+      __builtin_amdgcn_sched_barrier(0);
+      qk_step(1);
+      float mx = -INFINITY;
+      if (!tail) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, (8 * (r >> 2) + 4 * g + (r & 3)) < nk ? x[r] : -INFINITY);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      qk_step(2);
+      const float mt = pair_max(mx) * c_scale;  // the tile max in the exp2 domain
+      if (ti == 0) {
+        m_run = mt;  // first tile: O and l are still zero, nothing to rescale
+      } else if (__any(mt > m_run + kRescaleThreshold)) {
+        const bool need = mt > m_run + kRescaleThreshold;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+        if (need) m_run = mt;
+        l_run *= alpha;
+        rescale_agprs(oacc, alpha);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // p = 2^(c*x - m), two per S^T step
+      float p[16];
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) {
+        qk_step(3 + qq);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) p[2 * qq + i] = __builtin_amdgcn_exp2f(fmaf(x[2 * qq + i], c_scale, -m_run));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      qk_step(11);
+      if (tail) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = (8 * (r >> 2) + 4 * g + (r & 3)) < nk ? p[r] : 0.f;
+      }
+      float ls = 0.f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) ls += p[r];
+      __builtin_amdgcn_sched_barrier(0);
+      qk_step(12);
+#pragma unroll
+      for (int r = 8; r < 16; ++r) ls += p[r];
+      __builtin_amdgcn_sched_barrier(0);
+      // P^T operands: hi = p truncated to bf16 (exact), lo = bf16(p - hi) (round to nearest
+      // even), so hi + lo carries about 16 significant bits. For key half kb, element i of lane
+      // (n, g) is result reg 8*kb + i.
+      bf16x8 ph[2], pl[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          qk_step(13 + 2 * kb + hh);
+#pragma unroll
+          for (int i = 2 * hh; i < 2 * hh + 2; ++i) {
+            const float p0 = p[8 * kb + 2 * i], p1 = p[8 * kb + 2 * i + 1];
+            const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
+            hw[i] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+            lw[i] = pack_bf16x2(p0 - __uint_as_float(u0 & 0xffff0000u), p1 - __uint_as_float(u1 & 0xffff0000u));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        ph[kb] = __builtin_bit_cast(bf16x8, uint4{hw[0], hw[1], hw[2], hw[3]});
+        pl[kb] = __builtin_bit_cast(bf16x8, uint4{lw[0], lw[1], lw[2], lw[3]});
+      }
+      qk_step(17);
+      l_run += pair_sum(ls);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // PV(ti) up to its tail, key half 0 then 1; the exchange write of S^T(ti + 1) once its
+      // chain has drained.
+      bf16x8 va[kPvDepth];
+#pragma unroll
+      for (int u = 0; u < kPvDepth; ++u) va[u] = pv_operand(off_cur, u);
+#pragma unroll
+      for (int u = 0; u < 16 - kTail; ++u) {
+        const bf16x8 cur = va[u % kPvDepth];
+        if (u + kPvDepth < 16) va[u % kPvDepth] = pv_operand(off_cur, u + kPvDepth);
+        mfma_pv(oacc[u & 7], cur, ph[u >> 3]);
+        mfma_pv(oacc[u & 7], cur, pl[u >> 3]);
+        if (u == 1) {
+          mfma_qk_drain(s_next);
+          x_write((ti + 1) & 1, s_next);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < kTail; ++j) tail_v[j] = va[(16 - kTail + j) % kPvDepth];
+      tail_ph = ph[1];
+      tail_pl = pl[1];
+      s_own = s_next;
+    }
+    pin_agprs(oacc);
+    // tile ti + 2 must be in LDS for the next interval's S^T MFMAs
+    if (ti + 2 < ntiles) finish_tile(off_free);
+    lds_barrier();
+    const uint32_t o = off_cur;
+    off_cur = off_next;
+    off_next = off_free;
+    off_free = o;
+  };
+
+  // ---- prologue: tiles 0 and 1 in LDS, tile 2 on its way, S^T(0) exchanged
+  if (ntiles > 0) {
+    if constexpr (kInt8) {
+      // one register buffer: each tile's nope is written to LDS before the next is loaded
+      start_tile(0, 0);
+      finish_tile(0);
+      if (ntiles > 1) {
+        start_tile(1, kStageBytes);
+        finish_tile(kStageBytes);
+      }
+    } else {
+      start_tile(0, 0);
+      if (ntiles > 1) start_tile(1, kStageBytes);
+      wait_vmcnt<0>();
+    }
+    if (ntiles > 2) start_tile(2, 2 * kStageBytes);
+    lds_barrier();
+    if (pair_active) {
+      qk_tile(0, s_own);
+      mfma_qk_drain(s_own);
+      x_write(0, s_own);
+    }
+    lds_barrier();
+    for (int ti = 0; ti < ntiles; ++ti) interval(ti);
+    // the PV tail of the last tile
+    if (pair_active) {
+#pragma unroll
+      for (int j = 0; j < kTail; ++j) tail_step(j);
+    }
+  }
+  mfma_pv_drain(oacc);
+
+  // ---- epilogue: oacc[dc][4*rq + e] is column d = 256*half + 32*dc + 8*rq + 4*g + e of head h
+  if (a.n_splits == 1) {
+    if (pair_active && head_ok) {
+      const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+      uint16_t* o = a.out + ((int64_t)t * a.n_q + h) * kNope + 256 * half + 4 * g;
+#pragma unroll
+      for (int dc = 0; dc < 8; ++dc) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          uint2 v;
+          v.x = pack_bf16x2(oacc[dc][4 * rq] * inv, oacc[dc][4 * rq + 1] * inv);
+          v.y = pack_bf16x2(oacc[dc][4 * rq + 2] * inv, oacc[dc][4 * rq + 3] * inv);
+          *reinterpret_cast<uint2*>(o + 32 * dc + 8 * rq) = v;
+        }
       }
     }
     return;
   }
 
-  // Partial of (t, hg, sp) in register-image order: [wave][db][lane] float4.
+  // Partial of (t, hg, sp) in register-image order: [wave][dc][rq][lane] float4. Both waves of a
+  // pair hold the same running max and sum; the half-0 wave records them.
   const int S = a.n_splits;
   const int64_t grp_item = (int64_t)t * a.head_groups + hg;  // (token, head group)
   floatx4* part = reinterpret_cast<floatx4*>(a.part_o);
-  if (wave_active) {
-    floatx4* po = part + ((grp_item * S + sp) * kWaves + wave) * (32 * 64);
+  constexpr int kWaveImage = 8 * 4 * 64;  // float4s per wave
+  if (pair_active) {
+    floatx4* po = part + ((grp_item * S + sp) * kWaves + wave) * kWaveImage;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) po[db * 64 + lane] = oacc[db];
-    if (kg == 0) {
-      float* ml = a.part_ml + ((grp_item * S + sp) * kHeadsPerGroup + wave * kHeadsPerWave + n) * 2;
+    for (int dc = 0; dc < 8; ++dc) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        po[(dc * 4 + rq) * 64 + lane] =
+            floatx4{oacc[dc][4 * rq], oacc[dc][4 * rq + 1], oacc[dc][4 * rq + 2], oacc[dc][4 * rq + 3]};
+    }
+    if (half == 0 && g == 0) {
+      float* ml = a.part_ml + ((grp_item * S + sp) * kHeadsPerGroup + pair * kHeadsPerPair + n) * 2;
       ml[0] = m_run;
       ml[1] = l_run;
     }
@@ -467,19 +765,19 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   if (!s_last) return;
   __threadfence();  // acquire: the other partitions' partials
 
-  if (wave_active) {
+  if (pair_active) {
     float ws[kMaxSplits];
     float mmax = -INFINITY;
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) {
-      if (s < S) mmax = fmaxf(mmax, a.part_ml[((grp_item * S + s) * kHeadsPerGroup + wave * kHeadsPerWave + n) * 2]);
+      if (s < S) mmax = fmaxf(mmax, a.part_ml[((grp_item * S + s) * kHeadsPerGroup + pair * kHeadsPerPair + n) * 2]);
     }
     float lsum = 0.f;
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) {
       ws[s] = 0.f;
       if (s < S) {
-        const float* ml = a.part_ml + ((grp_item * S + s) * kHeadsPerGroup + wave * kHeadsPerWave + n) * 2;
+        const float* ml = a.part_ml + ((grp_item * S + s) * kHeadsPerGroup + pair * kHeadsPerPair + n) * 2;
         const float ms = ml[0];
         const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - mmax);
         ws[s] = w;
@@ -487,22 +785,27 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
       }
     }
     const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    uint16_t* o = a.out + ((int64_t)t * a.n_q + h) * kNope + 4 * kg;
+    uint16_t* o = a.out + ((int64_t)t * a.n_q + h) * kNope + 256 * half + 4 * g;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      floatx4 acc = {};
+    for (int dc = 0; dc < 8; ++dc) {
 #pragma unroll
-      for (int s = 0; s < kMaxSplits; ++s) {
-        if (s < S) {
-          const floatx4 v = (s == sp) ? oacc[db] : part[((grp_item * S + s) * kWaves + wave) * (32 * 64) + db * 64 + lane];
-          acc += ws[s] * v;
+      for (int rq = 0; rq < 4; ++rq) {
+        floatx4 acc = {};
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s) {
+          if (s < S) {
+            const floatx4 v =
+                (s == sp) ? floatx4{oacc[dc][4 * rq], oacc[dc][4 * rq + 1], oacc[dc][4 * rq + 2], oacc[dc][4 * rq + 3]}
+                          : part[((grp_item * S + s) * kWaves + wave) * kWaveImage + (dc * 4 + rq) * 64 + lane];
+            acc += ws[s] * v;
+          }
         }
-      }
-      if (head_ok) {
-        uint2 v;
-        v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-        v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-        *reinterpret_cast<uint2*>(o + 16 * db) = v;
+        if (head_ok) {
+          uint2 v;
+          v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+          v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+          *reinterpret_cast<uint2*>(o + 32 * dc + 8 * rq) = v;
+        }
       }
     }
   }
