@@ -95,30 +95,36 @@ __device__ __forceinline__ int nope_swz(int key) { return ((key & 3) << 2) | ((k
 __device__ __forceinline__ int rope_swz(int key) { return (key >> 1) & 7; }
 
 // LDS-DMA of 16 bytes per lane: lane L's bytes land at lds_addr + 16*L. lds_addr must be
-// wave-uniform (it goes through M0, which the asm declares clobbered; M0 needs one wait state
+// wave-uniform (it goes through M0, which the asm saves and restores; M0 needs one wait state
 // between its write and the DMA). Issued from inline asm so that the compiler does not wait
 // for the whole vector-memory queue before every LDS read. Completion is tracked explicitly
 // with wait_vmcnt, and cross-wave visibility with lds_barrier.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
       : "v"(gaddr), "s"(lds_addr)
-      : "memory", "m0");
+      : "memory");
 }
 
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset: used for the
 // nope rows, where one instruction reads one whole cache row.
 __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(lds_addr)
-      : "memory", "m0");
+      : "memory");
 }
 
 template <int N>
@@ -257,34 +263,6 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   const float c_scale = fabsf(a.scale_log2);
   const uint32_t q_sign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
-  // ---- Q^T fragments (B operand, k = d): step c < 16 covers nope chunks 32*half + 2c + {0, 1},
-  // steps 16 and 17 rope chunks 4*half + 2(c - 16) + {0, 1}; lane (n, g) holds chunk +g.
-  // Issued first so that their latency overlaps the slot resolution below.
-  bf16x8 qf[kQkSteps];
-  {
-    const uint4 zero = {0u, 0u, 0u, 0u};
-    const int64_t qrow = (int64_t)t * a.n_q + (head_ok ? h : 0);
-    const uint4* qn = reinterpret_cast<const uint4*>(a.q_nope + qrow * kNope);
-    const uint4* qr = reinterpret_cast<const uint4*>(a.q_rope + qrow * kRope);
-    uint4 qv[kQkSteps];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) qv[c] = head_ok ? qn[32 * half + 2 * c + g] : zero;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) qv[16 + c] = head_ok ? qr[4 * half + 2 * c + g] : zero;
-#pragma unroll
-    for (int c = 0; c < kQkSteps; ++c) {
-      qv[c].x ^= q_sign;
-      qv[c].y ^= q_sign;
-      qv[c].z ^= q_sign;
-      qv[c].w ^= q_sign;
-      qf[c] = __builtin_bit_cast(bf16x8, qv[c]);
-    }
-    // Q is only ever an MFMA B operand, which may come from AGPRs: keep it there and leave the
-    // VGPRs to the in-flight LDS operands and the softmax.
-#pragma unroll
-    for (int c = 0; c < kQkSteps; ++c) asm volatile("" : "+a"(qf[c]));
-  }
-
   // ---- resolve this partition's slots and compact the valid rows into s_rows, in slot order.
   // Thread T owns the contiguous slots [8T, 8T+8) of the partition (a partition holds at most
   // 2048 = 256 x 8 slots): all index loads are issued together, then all block-table loads,
@@ -301,18 +279,43 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     const int k = 8 * tid + i;
     jv[i] = k < nslot ? idx[k] : -1;
   }
+  int blkv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = jv[i];
+    const bool in = j >= 0 && j < lim;
+    blkv[i] = btab[in ? (j >> 7) : 0];
+  }
+  // ---- Q^T fragments (B operand, k = d): step c < 16 covers nope chunks 32*half + 2c + {0, 1},
+  // steps 16 and 17 rope chunks 4*half + 2(c - 16) + {0, 1}; lane (n, g) holds chunk +g.
+  // Issued after the index and block-table loads: load completion is counted in issue order,
+  // so Q's 147 KB per token must not sit in front of the two dependent index round trips.
+  // The loads are unconditional (a lane past n_q reads head 0's row) and the zeroing of such
+  // lanes happens after the compaction: a conditional load would make the compaction's wait for
+  // its own loads also wait for Q.
+  uint4 qv[kQkSteps];
+  {
+    const int64_t qrow = (int64_t)t * a.n_q + (head_ok ? h : 0);
+    const uint4* qn = reinterpret_cast<const uint4*>(a.q_nope + qrow * kNope);
+    const uint4* qr = reinterpret_cast<const uint4*>(a.q_rope + qrow * kRope);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) qv[c] = qn[32 * half + 2 * c + g];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) qv[16 + c] = qr[4 * half + 2 * c + g];
+  }
   int rowv[8];
   int cnt = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int j = jv[i];
     const bool in = j >= 0 && j < lim;
-    const int blk = in ? btab[j >> 7] : -1;
+    const int blk = blkv[i];
     const int64_t r = (int64_t)blk * kBlock + (j & (kBlock - 1));
     const bool v = in && blk >= 0 && r < a.num_rows;
     rowv[i] = v ? (int)r : -1;
     cnt += v ? 1 : 0;
   }
+
   // inclusive scan of cnt across the wave, then across waves through LDS
   int incl = cnt;
 #pragma unroll
@@ -344,6 +347,21 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     for (int q = n_valid; q < ntiles * kTile; ++q) s_rows[q] = last_row;
   }
   lds_barrier();
+
+  bf16x8 qf[kQkSteps];
+  {
+    const uint32_t keep = head_ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int c = 0; c < kQkSteps; ++c) {
+      const uint4 v = {(qv[c].x ^ q_sign) & keep, (qv[c].y ^ q_sign) & keep, (qv[c].z ^ q_sign) & keep,
+                       (qv[c].w ^ q_sign) & keep};
+      qf[c] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // Q is only ever an MFMA B operand, which may come from AGPRs: keep it there and leave the
+  // VGPRs to the in-flight LDS operands and the softmax.
+#pragma unroll
+  for (int c = 0; c < kQkSteps; ++c) asm volatile("" : "+a"(qf[c]));
 
   // O^T block dc: reg r holds column d = 256*half + 32*dc + 8*(r/4) + 4g + (r%4) of head h
   floatx16 oacc[8];
