@@ -17,6 +17,7 @@ constexpr size_t kAlignWs = 256;
 // Target number of workgroups for decode: the MI355X has 256 compute units and the attention
 // kernel runs one workgroup per CU (its register and LDS footprint allow no more).
 constexpr int kTargetWorkgroups = 256;
+constexpr int kMaxAutoSplits = 8;
 
 int head_groups(const sfa_dims* d) { return (d->n_q + kHeadsPerGroup - 1) / kHeadsPerGroup; }
 
@@ -49,10 +50,12 @@ int pick_splits(const sfa_dims* d, int is_prefill) {
     s = 1;
   } else {
     // Enough (token, partition) work items to give every CU one, but at least 64 slots (two
-    // tiles) per partition.
+    // tiles) per partition and at most kMaxAutoSplits partitions: the last arriver reads every
+    // partition's 128 KB partial, and beyond 8 of them that costs more than the shorter
+    // partitions save (measured at topk 2048, 1 to 16 tokens).
     const int64_t items = tokens * head_groups(d);
     const int64_t want = items > 0 ? (kTargetWorkgroups + items - 1) / items : 1;
-    s = (int)(want < kMaxSplits ? want : kMaxSplits);
+    s = (int)(want < kMaxAutoSplits ? want : kMaxAutoSplits);
     const int by_len = d->topk / 64 > 0 ? d->topk / 64 : 1;
     if (s > by_len) s = by_len;
     if (s < 1) s = 1;

@@ -757,73 +757,87 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
 
   // Partial of (t, hg, sp) in register-image order: [wave][dc][rq][lane] float4. Both waves of a
   // pair hold the same running max and sum; the half-0 wave records them.
+  //
+  // Publication without an L2 write-back: every partial is written with agent-scope stores (the
+  // sc1 form of the store, which the L2 of this XCD writes through instead of holding dirty), so
+  // once this wave's stores are acknowledged (vmcnt 0) they are visible to every XCD, and the
+  // arrival count that follows needs no release fence. (A release fence would write back this
+  // XCD's whole L2, which measured as the dominant cost of the merge.) The last arriver still
+  // takes an agent-scope acquire fence, which drops stale lines from its own L2.
   const int S = a.n_splits;
   const int64_t grp_item = (int64_t)t * a.head_groups + hg;  // (token, head group)
   floatx4* part = reinterpret_cast<floatx4*>(a.part_o);
   constexpr int kWaveImage = 8 * 4 * 64;  // float4s per wave
   if (pair_active) {
-    floatx4* po = part + ((grp_item * S + sp) * kWaves + wave) * kWaveImage;
-#pragma unroll
-    for (int dc = 0; dc < 8; ++dc) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq)
-        po[(dc * 4 + rq) * 64 + lane] =
-            floatx4{oacc[dc][4 * rq], oacc[dc][4 * rq + 1], oacc[dc][4 * rq + 2], oacc[dc][4 * rq + 3]};
-    }
-    if (half == 0 && g == 0) {
-      float* ml = a.part_ml + ((grp_item * S + sp) * kHeadsPerGroup + pair * kHeadsPerPair + n) * 2;
-      ml[0] = m_run;
-      ml[1] = l_run;
-    }
-  }
-  __threadfence();  // release: this partition's partial is visible device-wide
-  lds_barrier();
-  if (tid == 0) s_last = (atomicAdd(a.counters + grp_item, 1) == S - 1) ? 1 : 0;
-  lds_barrier();
-  if (!s_last) return;
-  __threadfence();  // acquire: the other partitions' partials
-
-  if (pair_active) {
-    float ws[kMaxSplits];
-    float mmax = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      if (s < S) mmax = fmaxf(mmax, a.part_ml[((grp_item * S + s) * kHeadsPerGroup + pair * kHeadsPerPair + n) * 2]);
-    }
-    float lsum = 0.f;
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      ws[s] = 0.f;
-      if (s < S) {
-        const float* ml = a.part_ml + ((grp_item * S + s) * kHeadsPerGroup + pair * kHeadsPerPair + n) * 2;
-        const float ms = ml[0];
-        const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - mmax);
-        ws[s] = w;
-        lsum += w * ml[1];
-      }
-    }
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    uint16_t* o = a.out + ((int64_t)t * a.n_q + h) * kNope + 256 * half + 4 * g;
+    floatx4* po = part + ((grp_item * S + sp) * kWaves + wave) * kWaveImage + lane;
 #pragma unroll
     for (int dc = 0; dc < 8; ++dc) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        floatx4 acc = {};
+        const floatx4 v{oacc[dc][4 * rq], oacc[dc][4 * rq + 1], oacc[dc][4 * rq + 2], oacc[dc][4 * rq + 3]};
+        asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(po + (dc * 4 + rq) * 64), "v"(v) : "memory");
+      }
+    }
+    if (half == 0 && g == 0) {
+      uint64_t* ml = reinterpret_cast<uint64_t*>(a.part_ml) + (grp_item * S + sp) * kHeadsPerGroup +
+                     pair * kHeadsPerPair + n;
+      const uint64_t bits = (uint64_t)__float_as_uint(m_run) | ((uint64_t)__float_as_uint(l_run) << 32);
+      __hip_atomic_store(ml, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
+  lds_barrier();
+  if (tid == 0) s_last = (atomicAdd(a.counters + grp_item, 1) == S - 1) ? 1 : 0;
+  lds_barrier();
+  if (!s_last || !pair_active) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other partitions' partials
+
+  // The last arriver combines all S partials (its own included, re-read from memory so that O's
+  // registers are free): the (m, l) of every partition for this lane's head are loaded in one
+  // batch, then O in two halves of 16 float4 per partition, each half's loads issued together.
+  const float2* mlp = reinterpret_cast<const float2*>(a.part_ml) + grp_item * S * kHeadsPerGroup +
+                      pair * kHeadsPerPair + n;
+  float2 mlv[kMaxSplits];
 #pragma unroll
-        for (int s = 0; s < kMaxSplits; ++s) {
-          if (s < S) {
-            const floatx4 v =
-                (s == sp) ? floatx4{oacc[dc][4 * rq], oacc[dc][4 * rq + 1], oacc[dc][4 * rq + 2], oacc[dc][4 * rq + 3]}
-                          : part[((grp_item * S + s) * kWaves + wave) * kWaveImage + (dc * 4 + rq) * 64 + lane];
-            acc += ws[s] * v;
-          }
-        }
-        if (head_ok) {
-          uint2 v;
-          v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-          v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-          *reinterpret_cast<uint2*>(o + 32 * dc + 8 * rq) = v;
-        }
+  for (int s = 0; s < kMaxSplits; ++s) mlv[s] = mlp[(s < S ? s : S - 1) * kHeadsPerGroup];
+  float mmax = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) mmax = s < S ? fmaxf(mmax, mlv[s].x) : mmax;
+  float wv[kMaxSplits];
+  float lsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    wv[s] = (s < S && mlv[s].x != -INFINITY) ? __builtin_amdgcn_exp2f(mlv[s].x - mmax) : 0.f;
+    lsum += wv[s] * mlv[s].y;
+  }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  uint16_t* o = a.out + ((int64_t)t * a.n_q + h) * kNope + 256 * half + 4 * g;
+  const floatx4* pbase = part + (grp_item * S * kWaves + wave) * kWaveImage + lane;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    floatx4 acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma nounroll
+    for (int s = 0; s < S; ++s) {
+      float w = 0.f;
+#pragma unroll
+      for (int u = 0; u < kMaxSplits; ++u) w = (u == s) ? wv[u] : w;
+      const floatx4* ps = pbase + (int64_t)s * kWaves * kWaveImage + hh * 16 * 64;
+      floatx4 buf[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) buf[i] = ps[i * 64];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += w * buf[i];
+    }
+    if (head_ok) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int dc = 4 * hh + i / 4, rq = i % 4;
+        uint2 v;
+        v.x = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
+        v.y = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
+        *reinterpret_cast<uint2*>(o + 32 * dc + 8 * rq) = v;
       }
     }
   }

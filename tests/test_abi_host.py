@@ -54,7 +54,9 @@ def test_partition_choice():
     assert sfa.num_splits(_dims(batch=32, s1=1)) == 4
     # one token of 16 heads, 64 slots: partitions need >= 64 slots each
     assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=64)) == 1
-    assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=2048)) == 16
+    # at most 8 partitions unless topk needs more
+    assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=2048)) == 8
+    assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=30000)) == 15
     # prefill never partitions while topk <= 2048
     assert sfa.num_splits(_dims(batch=1, s1=4096), is_prefill=True) == 1
     # topk > 2048 forces enough partitions that each compacts <= 2048 slots
