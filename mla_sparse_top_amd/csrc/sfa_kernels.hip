@@ -127,6 +127,73 @@ __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, ui
       : "memory");
 }
 
+// The same through a buffer resource (base, byte size): a cache row's byte offset fits in the
+// 32-bit scalar offset whenever the pool is below 4 GiB, which saves the 64-bit address
+// arithmetic per row. Up to three nope rows per call, with one M0 save and restore around them;
+// the shift of the next row's offset fills the wait state after each M0 write.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint64_t nbytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  // dword 2: the size in bytes (callers keep it below 4 GiB); dword 3: the raw-buffer
+  // configuration (32-bit data format, no swizzle, no stride)
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, (uint32_t)nbytes, 0x00020000u};
+}
+// Rows k0, k0 + 1, k0 + 2 of this wave's block of the tile: row k lands at lds_base + k * 1 KB.
+template <int kK0>
+__device__ __forceinline__ void dma16_rows3(const u32x4& rsrc, int r0, int r1, int r2, uint32_t v0, uint32_t v1,
+                                            uint32_t v2, uint32_t lds_base) {
+  uint32_t saved, o0, o1, o2;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_lshl_b32 %1, %8, 10\n\t"
+      "s_add_u32 m0, %11, %12\n\t"
+      "s_lshl_b32 %2, %9, 10\n\t"
+      "buffer_load_dwordx4 %4, %7, %1 offen lds\n\t"
+      "s_add_u32 m0, %11, %13\n\t"
+      "s_lshl_b32 %3, %10, 10\n\t"
+      "buffer_load_dwordx4 %5, %7, %2 offen lds\n\t"
+      "s_add_u32 m0, %11, %14\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %6, %7, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved), "=&s"(o0), "=&s"(o1), "=&s"(o2)
+      : "v"(v0), "v"(v1), "v"(v2), "s"(rsrc), "s"(r0), "s"(r1), "s"(r2), "s"(lds_base), "n"(kK0 * 1024),
+        "n"((kK0 + 1) * 1024), "n"((kK0 + 2) * 1024)
+      : "memory");
+}
+template <int kK0>
+__device__ __forceinline__ void dma16_rows2(const u32x4& rsrc, int r0, int r1, uint32_t v0, uint32_t v1,
+                                            uint32_t lds_base) {
+  uint32_t saved, o0, o1;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_lshl_b32 %1, %6, 10\n\t"
+      "s_add_u32 m0, %8, %9\n\t"
+      "s_lshl_b32 %2, %7, 10\n\t"
+      "buffer_load_dwordx4 %3, %5, %1 offen lds\n\t"
+      "s_add_u32 m0, %8, %10\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %4, %5, %2 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved), "=&s"(o0), "=&s"(o1)
+      : "v"(v0), "v"(v1), "s"(rsrc), "s"(r0), "s"(r1), "s"(lds_base), "n"(kK0 * 1024), "n"((kK0 + 1) * 1024)
+      : "memory");
+}
+// One DMA instruction with a per-lane byte offset into the buffer (the rope rows: eight rows
+// per instruction).
+__device__ __forceinline__ void dma16_voff(const u32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -135,7 +202,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Workgroup barrier that orders LDS traffic only. Outstanding global loads (the register
 // staging of later tiles) stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // s_waitcnt lgkmcnt(0) with vmcnt and expcnt left at their maximum, written as the builtin so
+  // that the compiler's wait-count tracking knows the LDS queue is empty after it
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -147,13 +217,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // S^T += K . Q^T steps: the accumulator in VGPRs, the K fragment in VGPRs (fresh from LDS), the
 // Q^T fragment in AGPRs. Consecutive steps accumulate into the same registers, which the
-// hardware chains back to back; the chain starts from 0. The leading pad covers a VALU write of
-// an operand right before (a register copy the compiler may place there).
+// hardware chains back to back (an exactly overlapping accumulator needs no wait states); the
+// chain starts from 0. The first step's leading pad covers a VALU write of an operand right
+// before it. The later steps read only LDS-loaded K fragments, the Q registers (written once)
+// and the chained accumulator, so they carry no pad; the build checks the generated code for a
+// VALU write of an MFMA operand within two instructions before an unpadded MFMA.
 __device__ __forceinline__ void mfma_qk_first(floatx16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
 }
 __device__ __forceinline__ void mfma_qk(floatx16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
 }
 // Before anything else reads the chain's result: a 32x32x16 result needs 12 wait states before
 // a VALU or LDS read of it; this gives 20.
@@ -224,8 +297,11 @@ struct StagedInt8 {
   float scale[8];
 };
 
-template <bool kInt8>
+// kBufDma: the bf16 nope and rope rows are fetched through buffer resources with 32-bit byte
+// offsets (pools below 4 GiB of nope); otherwise through 64-bit global addresses.
+template <bool kInt8, bool kBufDma>
 __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const KernelArgs a) {
+  static_assert(!(kInt8 && kBufDma), "the INT8 path fetches through global addresses");
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
   __shared__ __attribute__((aligned(16))) char xbuf[2 * kWaves * kXBytes];
   __shared__ __attribute__((aligned(16))) int32_t s_rows[kMaxSlots];
@@ -374,12 +450,18 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   // ---- loaders: wave w carries rows 8w..8w+7 of each tile
   const uint32_t smem_lds = (uint32_t)(uintptr_t)((lds_char_t*)smem);
   // rope: lane L fetches chunk ((L & 7) ^ rope_swz(key)) of key = 8*wave + L/8.
+  const u32x4 rs_nope = make_rsrc(a.k_nope, (uint64_t)a.num_rows * kNopeRowBytes);
+  const u32x4 rs_rope = make_rsrc(a.k_rope, (uint64_t)a.num_rows * kRopeRowBytes);
   auto issue_rope = [&](int tile, uint32_t stage_off) __attribute__((always_inline)) {
     const int key = wave * 8 + (lane >> 3);
     const int row = s_rows[tile * kTile + key];
-    const char* src = reinterpret_cast<const char*>(a.k_rope) + (int64_t)row * kRopeRowBytes +
-                      16 * ((lane & 7) ^ rope_swz(key));
-    dma16(src, smem_lds + stage_off + kNopeTileBytes + wave * 8 * kRopeRowBytes);
+    const uint32_t chunk = 16 * ((lane & 7) ^ rope_swz(key));
+    const uint32_t lds = smem_lds + stage_off + kNopeTileBytes + wave * 8 * kRopeRowBytes;
+    if constexpr (kBufDma) {
+      dma16_voff(rs_rope, (uint32_t)row * kRopeRowBytes + chunk, lds);
+    } else {
+      dma16(reinterpret_cast<const char*>(a.k_rope) + (int64_t)row * kRopeRowBytes + chunk, lds);
+    }
   };
   // The wave's 8 rows of a tile, as wave-uniform values (one 32-byte broadcast read).
   auto tile_rows = [&](int tile, int (&rows)[8]) __attribute__((always_inline)) {
@@ -396,15 +478,31 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   };
   // bf16 nope: one 1 KB row per instruction; lane L fills physical chunk L, i.e. fetches
   // logical chunk L ^ nope_swz(key).
+  // Rows [k0, k1) of the wave's eight; nope_voff[k] is lane L's physical chunk offset in row k.
+  uint32_t nope_voff[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) nope_voff[k] = (uint32_t)(16 * (lane ^ nope_swz(wave * 8 + k)));
+  auto issue_nope_rows = [&](const int (&rows)[8], uint32_t stage_off, int k0, int k1) __attribute__((always_inline)) {
+    const uint32_t lds_base = smem_lds + stage_off + wave * 8 * kNopeRowBytes;
+    if constexpr (kBufDma) {
+      static_assert(kNopeRowBytes == 1024, "row offsets are formed as row << 10");
+      if (k0 == 0 && k1 == 3) dma16_rows3<0>(rs_nope, rows[0], rows[1], rows[2], nope_voff[0], nope_voff[1], nope_voff[2], lds_base);
+      if (k0 == 3 && k1 == 6) dma16_rows3<3>(rs_nope, rows[3], rows[4], rows[5], nope_voff[3], nope_voff[4], nope_voff[5], lds_base);
+      if (k0 == 6 && k1 == 8) dma16_rows2<6>(rs_nope, rows[6], rows[7], nope_voff[6], nope_voff[7], lds_base);
+    } else {
+#pragma unroll
+      for (int k = k0; k < k1; ++k) {
+        const char* base = reinterpret_cast<const char*>(a.k_nope) + (int64_t)rows[k] * kNopeRowBytes;
+        dma16_sbase(base, nope_voff[k], lds_base + k * kNopeRowBytes);
+      }
+    }
+  };
   auto issue_nope_bf16 = [&](int tile, uint32_t stage_off) __attribute__((always_inline)) {
     int rows[8];
     tile_rows(tile, rows);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int key = wave * 8 + k;
-      const char* base = reinterpret_cast<const char*>(a.k_nope) + (int64_t)rows[k] * kNopeRowBytes;
-      dma16_sbase(base, (uint32_t)(16 * (lane ^ nope_swz(key))), smem_lds + stage_off + key * kNopeRowBytes);
-    }
+    issue_nope_rows(rows, stage_off, 0, 3);
+    issue_nope_rows(rows, stage_off, 3, 6);
+    issue_nope_rows(rows, stage_off, 6, 8);
   };
   // int8 nope: lane L holds columns [8L, 8L+8) of each row and the scale of their group L/16.
   StagedInt8 st8;
@@ -449,17 +547,15 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   int rows_next[8];
   auto start_tile_part = [&](int tile, uint32_t stage_off, int part) __attribute__((always_inline)) {
     if (part == 0) tile_rows(tile, rows_next);
+    if constexpr (kInt8) {
 #pragma unroll
-    for (int k = 3 * part; k < min(8, 3 * part + 3); ++k) {
-      if constexpr (kInt8) {
+      for (int k = 3 * part; k < min(8, 3 * part + 3); ++k) {
         st8.nope[k] = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(a.k_nope) +
                                                       (int64_t)rows_next[k] * kNope + 8 * lane);
         st8.scale[k] = a.k_scales[(int64_t)rows_next[k] * 4 + (lane >> 4)];
-      } else {
-        const int key = wave * 8 + k;
-        const char* base = reinterpret_cast<const char*>(a.k_nope) + (int64_t)rows_next[k] * kNopeRowBytes;
-        dma16_sbase(base, (uint32_t)(16 * (lane ^ nope_swz(key))), smem_lds + stage_off + key * kNopeRowBytes);
       }
+    } else {
+      issue_nope_rows(rows_next, stage_off, 3 * part, min(8, 3 * part + 3));
     }
     if (part == 2) issue_rope(tile, stage_off);
   };
@@ -607,8 +703,12 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[r]);
       } else {
+        // keys past the partition's last valid row: -inf scores, so their p is exactly 0
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, (8 * (r >> 2) + 4 * g + (r & 3)) < nk ? x[r] : -INFINITY);
+        for (int r = 0; r < 16; ++r) {
+          x[r] = (8 * (r >> 2) + 4 * g + (r & 3)) < nk ? x[r] : -INFINITY;
+          mx = fmaxf(mx, x[r]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       qk_step(2);
@@ -623,56 +723,50 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
         rescale_agprs(oacc, alpha);
       }
       __builtin_amdgcn_sched_barrier(0);
-      // p = 2^(c*x - m), two per S^T step
+      // p = 2^(c*x - m). Key half 0 (p[0..7]) is finished here, two values per S^T step, so
+      // that its PV steps can start; key half 1 (p[8..15]) is computed under the first PV
+      // steps, whose MFMAs leave the VALU idle.
       float p[16];
+      auto exp_pair = [&](int r) __attribute__((always_inline)) {
 #pragma unroll
-      for (int qq = 0; qq < 8; ++qq) {
-        qk_step(3 + qq);
+        for (int i = 0; i < 2; ++i) p[r + i] = __builtin_amdgcn_exp2f(fmaf(x[r + i], c_scale, -m_run));
+      };
+      // P^T operands: hi = p truncated to bf16 (exact), lo = bf16(p - hi) (round to nearest
+      // even), so hi + lo carries about 16 significant bits. For key half kb, element i of lane
+      // (n, g) is result reg 8*kb + i.
+      uint32_t hw[2][4], lw[2][4];
+      auto split_pair = [&](int kb, int i) __attribute__((always_inline)) {
+        const float p0 = p[8 * kb + 2 * i], p1 = p[8 * kb + 2 * i + 1];
+        const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
+        hw[kb][i] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        lw[kb][i] = pack_bf16x2(p0 - __uint_as_float(u0 & 0xffff0000u), p1 - __uint_as_float(u1 & 0xffff0000u));
+      };
 #pragma unroll
-        for (int i = 0; i < 2; ++i) p[2 * qq + i] = __builtin_amdgcn_exp2f(fmaf(x[2 * qq + i], c_scale, -m_run));
+      for (int qq = 0; qq < 4; ++qq) {
+        qk_step(3 + 2 * qq);
+        exp_pair(2 * qq);
+        __builtin_amdgcn_sched_barrier(0);
+        qk_step(4 + 2 * qq);
+        split_pair(0, qq);
         __builtin_amdgcn_sched_barrier(0);
       }
       qk_step(11);
-      if (tail) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = (8 * (r >> 2) + 4 * g + (r & 3)) < nk ? p[r] : 0.f;
-      }
       float ls = 0.f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) ls += p[r];
       __builtin_amdgcn_sched_barrier(0);
-      qk_step(12);
-#pragma unroll
-      for (int r = 8; r < 16; ++r) ls += p[r];
-      __builtin_amdgcn_sched_barrier(0);
-      // P^T operands: hi = p truncated to bf16 (exact), lo = bf16(p - hi) (round to nearest
-      // even), so hi + lo carries about 16 significant bits. For key half kb, element i of lane
-      // (n, g) is result reg 8*kb + i.
       bf16x8 ph[2], pl[2];
+      ph[0] = __builtin_bit_cast(bf16x8, uint4{hw[0][0], hw[0][1], hw[0][2], hw[0][3]});
+      pl[0] = __builtin_bit_cast(bf16x8, uint4{lw[0][0], lw[0][1], lw[0][2], lw[0][3]});
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          qk_step(13 + 2 * kb + hh);
-#pragma unroll
-          for (int i = 2 * hh; i < 2 * hh + 2; ++i) {
-            const float p0 = p[8 * kb + 2 * i], p1 = p[8 * kb + 2 * i + 1];
-            const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
-            hw[i] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-            lw[i] = pack_bf16x2(p0 - __uint_as_float(u0 & 0xffff0000u), p1 - __uint_as_float(u1 & 0xffff0000u));
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        ph[kb] = __builtin_bit_cast(bf16x8, uint4{hw[0], hw[1], hw[2], hw[3]});
-        pl[kb] = __builtin_bit_cast(bf16x8, uint4{lw[0], lw[1], lw[2], lw[3]});
+      for (int c = 12; c < kQkSteps; ++c) {
+        qk_step(c);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      qk_step(17);
-      l_run += pair_sum(ls);
-      __builtin_amdgcn_sched_barrier(0);
 
       // PV(ti) up to its tail, key half 0 then 1; the exchange write of S^T(ti + 1) once its
-      // chain has drained.
+      // chain has drained; key half 1's p and P^T operands under the key-half-0 steps.
+      static_assert(16 - kTail >= 8, "key half 1's operands are completed by PV step 7");
       bf16x8 va[kPvDepth];
 #pragma unroll
       for (int u = 0; u < kPvDepth; ++u) va[u] = pv_operand(off_cur, u);
@@ -685,6 +779,15 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
         if (u == 1) {
           mfma_qk_drain(s_next);
           x_write((ti + 1) & 1, s_next);
+        }
+        if (u < 4) exp_pair(8 + 2 * u);
+        if (u >= 4 && u < 8) split_pair(1, u - 4);
+        if (u == 7) {
+          ph[1] = __builtin_bit_cast(bf16x8, uint4{hw[1][0], hw[1][1], hw[1][2], hw[1][3]});
+          pl[1] = __builtin_bit_cast(bf16x8, uint4{lw[1][0], lw[1][1], lw[1][2], lw[1][3]});
+#pragma unroll
+          for (int r = 8; r < 16; ++r) ls += p[r];
+          l_run += pair_sum(ls);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -884,8 +987,12 @@ hipError_t launch_attention(const KernelArgs& a, bool int8_cache, hipStream_t st
   const dim3 block(kThreads);
   KernelArgs copy = a;
   void* args[] = {&copy};
-  const void* fn = int8_cache ? reinterpret_cast<const void*>(&sfa_attention_kernel<true>)
-                              : reinterpret_cast<const void*>(&sfa_attention_kernel<false>);
+  // 32-bit byte offsets (and buffer sizes) cover every nope row while the pool holds fewer than
+  // 4 Mi rows (4 GiB)
+  const bool buf_dma = !int8_cache && a.num_rows < (int64_t{1} << 22);
+  const void* fn = int8_cache ? reinterpret_cast<const void*>(&sfa_attention_kernel<true, false>)
+                   : buf_dma  ? reinterpret_cast<const void*>(&sfa_attention_kernel<false, true>)
+                              : reinterpret_cast<const void*>(&sfa_attention_kernel<false, false>);
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

@@ -184,6 +184,35 @@ def test_block_permutation_is_bit_exact():
     assert np.array_equal(got, ref)
 
 
+def test_pool_beyond_4gib_matches_small_pool():
+    """A pool of more than 4 Mi rows (over 4 GiB of nope) takes the 64-bit addressing path of
+    the row fetch; the same problem with its blocks moved there, some below and some above the
+    4 GiB mark, must give the bit-identical result."""
+    inp = W.generate(batch=2, s1=2, n_q=128, act_seqs=[3000, 5000], topk=1024, seed=21,
+                     max_blocks_per_batch=40, extra_pool_blocks=2)
+    sfa = _lib()
+    dev = sfa.to_device(inp)
+    ref = _gpu(inp, dev=dev)
+    _check(inp, ref, label="small pool")
+    n_small = inp.num_cache_rows // 128
+    n_big = (1 << 22) // 128 + 64  # 4 Mi + 8192 rows
+    rng = np.random.default_rng(5)
+    below = rng.choice(np.arange(1000, (1 << 22) // 128), size=n_small // 2, replace=False)
+    above = rng.choice(np.arange((1 << 22) // 128, n_big), size=n_small - n_small // 2, replace=False)
+    place = torch.from_numpy(np.concatenate([below, above]).astype(np.int64)).cuda()
+    big = dict(dev)
+    kn = torch.empty((n_big * 128, 512), dtype=torch.bfloat16, device="cuda")
+    kr = torch.empty((n_big * 128, 64), dtype=torch.bfloat16, device="cuda")
+    kn.view(n_big, 128, 512)[place] = dev["key_nope"].view(n_small, 128, 512)
+    kr.view(n_big, 128, 64)[place] = dev["key_rope"].view(n_small, 128, 64)
+    big["key_nope"], big["key_rope"] = kn, kr
+    big["block_table"] = place.to(torch.int32)[dev["block_table"].long()].contiguous()
+    got = _gpu(inp, dev=big)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    del kn, kr, big
+    torch.cuda.empty_cache()
+
+
 def test_run_to_run_determinism():
     inp = W.generate(batch=8, s1=2, n_q=128, act_seqs=[4000] * 8, topk=2048, seed=10, max_blocks_per_batch=32)
     sfa = _lib()
