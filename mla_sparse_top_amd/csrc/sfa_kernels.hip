@@ -635,9 +635,9 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   // LDS offsets of the three stages: tile ti (PV), tile ti + 1 (S^T), and the free one that
   // receives tile ti + 2. They rotate every tile.
   uint32_t off_cur = 0, off_next = kStageBytes, off_free = 2 * kStageBytes;
-  // The last kTail PV steps of a tile run after the barrier that ends its interval, while the
-  // next interval's first LDS reads and DMA issue are in flight. Their V operands are read into
-  // registers before that barrier, so the stage they came from may be refilled right after it.
+  // The last kTail PV steps of a tile run after the barrier that ends its interval, between the
+  // next interval's S^T steps. Their V operands are read into registers before that barrier, so
+  // the stage they came from may be refilled right after it.
   constexpr int kTail = kPvDepth;
   bf16x8 tail_v[kTail];
   bf16x8 tail_ph, tail_pl;  // P^T of key half 1, which those steps use
@@ -648,9 +648,9 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
 
   // One tile interval:
   //   1. LDS reads of the partner's partial S^T(ti) and of the first S^T(ti + 1) operands;
-  //   2. the PV tail of tile ti - 1, interleaved with the DMA issue of tile ti + 2 into the
-  //      free stage;
-  //   3. the S^T MFMAs of tile ti + 1 interleaved with the softmax of tile ti;
+  //   2. the DMA issue of tile ti + 2 into the free stage;
+  //   3. the S^T MFMAs of tile ti + 1 interleaved with the PV tail of tile ti - 1 and the
+  //      softmax of tile ti;
   //   4. the PV MFMAs of tile ti up to its tail, with the exchange write of S^T(ti + 1) in
   //      between;
   //   5. wait for this wave's DMA of tile ti + 2, barrier.
@@ -671,15 +671,21 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
       for (int c = 0; c < kQkDepth; ++c) qa[c] = qk_operand(off_next, c);
     }
     __builtin_amdgcn_sched_barrier(0);
-    constexpr int kSlots = kTail > 3 ? kTail : 3;  // three DMA parts, kTail PV steps
 #pragma unroll
-    for (int j = 0; j < kSlots; ++j) {
-      if (do_dma && j < 3) start_tile_part(ti + 2, off_free, j);
-      if (do_tail && j < kTail) tail_step(j);
+    for (int j = 0; j < 3; ++j) {
+      if (do_dma) start_tile_part(ti + 2, off_free, j);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (pair_active) {
       floatx16 s_next;
+      // A deferred rescale of O (decided with the tile max) waits for the PV tail of the
+      // previous tile, which is still relative to the old running max.
+      bool rescale = false;
+      float alpha = 1.0f;
+      constexpr int kRescaleAfter = kTail - 1 > 3 ? kTail - 1 : 3;  // after the decision at step 2
+      // S^T step c of tile ti + 1, then (c < kTail) PV tail step c of tile ti - 1: the tail's
+      // operands are in registers, so its MFMAs fill the MFMA pipe while the S^T steps wait on
+      // LDS.
       auto qk_step = [&](int c) __attribute__((always_inline)) {
         const bf16x8 cur = qa[c % kQkDepth];
         if (c + kQkDepth < kQkSteps) qa[c % kQkDepth] = qk_operand(off_next, c + kQkDepth);
@@ -687,6 +693,8 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
           mfma_qk_first(s_next, cur, qf[0]);
         else
           mfma_qk(s_next, cur, qf[c]);
+        if (c < kTail && do_tail) tail_step(c);
+        if (c == kRescaleAfter && rescale) rescale_agprs(oacc, alpha);
       };
 
       // s[r] is key 8*(r/4) + 4g + (r%4) of the tile, head h
@@ -717,10 +725,10 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
         m_run = mt;  // first tile: O and l are still zero, nothing to rescale
       } else if (__any(mt > m_run + kRescaleThreshold)) {
         const bool need = mt > m_run + kRescaleThreshold;
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+        alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
         if (need) m_run = mt;
         l_run *= alpha;
-        rescale_agprs(oacc, alpha);
+        rescale = true;
       }
       __builtin_amdgcn_sched_barrier(0);
       // p = 2^(c*x - m). Key half 0 (p[0..7]) is finished here, two values per S^T step, so
