@@ -81,8 +81,9 @@ def test_resolve_rows_bit_exact(make):
 # small cases: several tiles, ragged tails, head counts, partitions
 # ----------------------------------------------------------------------------------------
 
-def test_tiny_config():
-    inp = W.tiny()
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_config(seed):
+    inp = W.tiny(seed=seed)
     _check(inp, _gpu(inp))
 
 
@@ -225,30 +226,32 @@ def test_run_to_run_determinism():
 # the named workloads at full size
 # ----------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("seed", [0, 1, 2])
 def test_decode_b64_s2_bf16_full(seed):
     inp = W.decode_mtp1(seed=seed)
     _check(inp, _gpu(inp))
 
 
-@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("seed", [0, 1, 2])
 def test_decode_b64_s2_int8_full(seed):
     inp = W.decode_mtp1_int8(seed=seed)
     _check(inp, _gpu(inp))
 
 
-def test_varlen_decode_full():
-    inp = W.varlen_decode(seed=0)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_varlen_decode_full(seed):
+    inp = W.varlen_decode(seed=seed)
     _check(inp, _gpu(inp))
 
 
-def test_prefill_4096_sampled():
-    inp = W.prefill(seed=0)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefill_4096_sampled(seed):
+    inp = W.prefill(seed=seed)
     got = _gpu(inp, prefill=True)
-    rng = np.random.default_rng(0)
+    rng = np.random.default_rng(seed)
     toks = sorted(set([0, 1, 2, 31, 32, 33, 1000, 2046, 2047, 2048, 2049, 4094, 4095]
                       + rng.integers(0, 4096, 24).tolist()))
-    _check(inp, got, tokens=toks, label="prefill4096_sampled")
+    _check(inp, got, tokens=toks, label=f"prefill4096_sampled_seed{seed}")
 
 
 @pytest.mark.parametrize("name", W.PAGE_CASES)
