@@ -849,9 +849,14 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
 
   // ---- epilogue: oacc[dc][4*rq + e] is column d = 256*half + 32*dc + 8*rq + 4*g + e of head h
   if (a.n_splits == 1) {
-    if (pair_active && head_ok) {
+    // The normalised bf16 O of this wave (32 heads x 256 columns) goes through LDS, so that each
+    // store instruction writes two whole 512-byte rows instead of 32 scattered 16-byte pieces.
+    // Layout: 16 KB per wave, row = head, 16-byte chunk c of a row at chunk c ^ row (no bank
+    // conflicts on the row-wise read back). The stages are free once every wave is here.
+    lds_barrier();
+    char* ob = smem + wave * (kHeadsPerPair * 512);
+    if (pair_active) {
       const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-      uint16_t* o = a.out + ((int64_t)t * a.n_q + h) * kNope + 256 * half + 4 * g;
 #pragma unroll
       for (int dc = 0; dc < 8; ++dc) {
 #pragma unroll
@@ -859,8 +864,19 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
           uint2 v;
           v.x = pack_bf16x2(oacc[dc][4 * rq] * inv, oacc[dc][4 * rq + 1] * inv);
           v.y = pack_bf16x2(oacc[dc][4 * rq + 2] * inv, oacc[dc][4 * rq + 3] * inv);
-          *reinterpret_cast<uint2*>(o + 32 * dc + 8 * rq) = v;
+          const int c = 4 * dc + rq;  // columns 8c .. 8c + 7 of the wave's 256
+          *reinterpret_cast<uint2*>(ob + n * 512 + ((c ^ n) & 31) * 16 + 8 * g) = v;
         }
+      }
+      // read back (the wave's own LDS accesses complete in order): lane L takes chunk L % 32 of
+      // row 2i + L / 32
+      const int j = lane & 31;
+      uint16_t* orow = a.out + ((int64_t)t * a.n_q + hp0) * kNope + 256 * half + 8 * j;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 2 * i + g;
+        const uint4 v = *reinterpret_cast<const uint4*>(ob + r * 512 + ((j ^ r) & 31) * 16);
+        if (hp0 + r < a.n_q) *reinterpret_cast<uint4*>(orow + (int64_t)r * kNope) = v;
       }
     }
     return;
