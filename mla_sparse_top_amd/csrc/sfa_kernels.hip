@@ -297,11 +297,10 @@ struct StagedInt8 {
   float scale[8];
 };
 
-// kBufDma: the bf16 nope and rope rows are fetched through buffer resources with 32-bit byte
-// offsets (pools below 4 GiB of nope); otherwise through 64-bit global addresses.
+// kBufDma: cache rows (nope, rope, INT8 scales) are fetched through buffer resources with
+// 32-bit byte offsets (pools below 4 Mi rows); otherwise through 64-bit global addresses.
 template <bool kInt8, bool kBufDma>
 __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const KernelArgs a) {
-  static_assert(!(kInt8 && kBufDma), "the INT8 path fetches through global addresses");
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
   __shared__ __attribute__((aligned(16))) char xbuf[2 * kWaves * kXBytes];
   __shared__ __attribute__((aligned(16))) int32_t s_rows[kMaxSlots];
@@ -506,15 +505,27 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   };
   // int8 nope: lane L holds columns [8L, 8L+8) of each row and the scale of their group L/16.
   StagedInt8 st8;
+  // lane L loads bytes [8L, 8L+8) of the row and the scale of group L/16
+  const __amdgpu_buffer_rsrc_t rb_code = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.k_nope), 0, kInt8 ? (int)(a.num_rows * kNope) : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb_scale = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.k_scales), 0, kInt8 ? (int)(a.num_rows * 16) : 0, 0x00020000);
+  auto load_int8_row = [&](int k, int row) __attribute__((always_inline)) {
+    if constexpr (kBufDma) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rb_code, 8 * lane, row << 9, 0);
+      st8.nope[k] = uint2{v[0], v[1]};
+      st8.scale[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb_scale, 4 * (lane >> 4), row << 4, 0));
+    } else {
+      st8.nope[k] = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(a.k_nope) +
+                                                    (int64_t)row * kNope + 8 * lane);
+      st8.scale[k] = a.k_scales[(int64_t)row * 4 + (lane >> 4)];
+    }
+  };
   auto load_nope_int8 = [&](int tile) __attribute__((always_inline)) {
     int rows[8];
     tile_rows(tile, rows);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      st8.nope[k] = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(a.k_nope) +
-                                                    (int64_t)rows[k] * kNope + 8 * lane);
-      st8.scale[k] = a.k_scales[(int64_t)rows[k] * 4 + (lane >> 4)];
-    }
+    for (int k = 0; k < 8; ++k) load_int8_row(k, rows[k]);
   };
   // Dequant: code -> fp32 (exact), times the fp32 group scale (RNE), -> bf16 (RNE); the 16-byte
   // chunk of columns [8L, 8L+8) is chunk L of the row, stored swizzled.
@@ -549,11 +560,7 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     if (part == 0) tile_rows(tile, rows_next);
     if constexpr (kInt8) {
 #pragma unroll
-      for (int k = 3 * part; k < min(8, 3 * part + 3); ++k) {
-        st8.nope[k] = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(a.k_nope) +
-                                                      (int64_t)rows_next[k] * kNope + 8 * lane);
-        st8.scale[k] = a.k_scales[(int64_t)rows_next[k] * 4 + (lane >> 4)];
-      }
+      for (int k = 3 * part; k < min(8, 3 * part + 3); ++k) load_int8_row(k, rows_next[k]);
     } else {
       issue_nope_rows(rows_next, stage_off, 3 * part, min(8, 3 * part + 3));
     }
@@ -1011,12 +1018,13 @@ hipError_t launch_attention(const KernelArgs& a, bool int8_cache, hipStream_t st
   const dim3 block(kThreads);
   KernelArgs copy = a;
   void* args[] = {&copy};
-  // 32-bit byte offsets (and buffer sizes) cover every nope row while the pool holds fewer than
-  // 4 Mi rows (4 GiB)
-  const bool buf_dma = !int8_cache && a.num_rows < (int64_t{1} << 22);
-  const void* fn = int8_cache ? reinterpret_cast<const void*>(&sfa_attention_kernel<true, false>)
-                   : buf_dma  ? reinterpret_cast<const void*>(&sfa_attention_kernel<false, true>)
-                              : reinterpret_cast<const void*>(&sfa_attention_kernel<false, false>);
+  // 32-bit byte offsets (and buffer sizes) cover every cache row while the pool holds fewer
+  // than 4 Mi rows (4 GiB of bf16 nope)
+  const bool buf = a.num_rows < (int64_t{1} << 22);
+  const void* fn = int8_cache ? (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<true, true>)
+                                     : reinterpret_cast<const void*>(&sfa_attention_kernel<true, false>))
+                              : (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<false, true>)
+                                     : reinterpret_cast<const void*>(&sfa_attention_kernel<false, false>));
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

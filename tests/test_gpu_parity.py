@@ -185,11 +185,12 @@ def test_block_permutation_is_bit_exact():
     assert np.array_equal(got, ref)
 
 
-def test_pool_beyond_4gib_matches_small_pool():
-    """A pool of more than 4 Mi rows (over 4 GiB of nope) takes the 64-bit addressing path of
-    the row fetch; the same problem with its blocks moved there, some below and some above the
-    4 GiB mark, must give the bit-identical result."""
-    inp = W.generate(batch=2, s1=2, n_q=128, act_seqs=[3000, 5000], topk=1024, seed=21,
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+def test_pool_beyond_4gib_matches_small_pool(kv_dtype):
+    """A pool of more than 4 Mi rows (over 4 GiB of bf16 nope) takes the 64-bit addressing path
+    of the row fetch; the same problem with its blocks moved there, some below and some above
+    row 4 Mi, must give the bit-identical result."""
+    inp = W.generate(batch=2, s1=2, n_q=128, act_seqs=[3000, 5000], topk=1024, seed=21, kv_dtype=kv_dtype,
                      max_blocks_per_batch=40, extra_pool_blocks=2)
     sfa = _lib()
     dev = sfa.to_device(inp)
@@ -202,15 +203,17 @@ def test_pool_beyond_4gib_matches_small_pool():
     above = rng.choice(np.arange((1 << 22) // 128, n_big), size=n_small - n_small // 2, replace=False)
     place = torch.from_numpy(np.concatenate([below, above]).astype(np.int64)).cuda()
     big = dict(dev)
-    kn = torch.empty((n_big * 128, 512), dtype=torch.bfloat16, device="cuda")
-    kr = torch.empty((n_big * 128, 64), dtype=torch.bfloat16, device="cuda")
-    kn.view(n_big, 128, 512)[place] = dev["key_nope"].view(n_small, 128, 512)
-    kr.view(n_big, 128, 64)[place] = dev["key_rope"].view(n_small, 128, 64)
-    big["key_nope"], big["key_rope"] = kn, kr
+    for key, width in (("key_nope", 512), ("key_rope", 64), ("k_nope_scales", 4)):
+        small = dev[key]
+        if small is None:
+            continue
+        t = torch.empty((n_big * 128, width), dtype=small.dtype, device="cuda")
+        t.view(n_big, 128, width)[place] = small.view(n_small, 128, width)
+        big[key] = t
     big["block_table"] = place.to(torch.int32)[dev["block_table"].long()].contiguous()
     got = _gpu(inp, dev=big)
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
-    del kn, kr, big
+    del big
     torch.cuda.empty_cache()
 
 
