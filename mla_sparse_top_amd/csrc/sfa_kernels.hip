@@ -234,10 +234,11 @@ __device__ __forceinline__ void mfma_qk_drain(floatx16& acc) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc));
 }
 
-// O^T += V^T . P^T step on an AGPR-resident accumulator, tied in place. Its operands were just
-// produced by VALU (P^T hi/lo conversion) or LDS, so the MFMA is preceded by 3 wait states.
+// O^T += V^T . P^T step on an AGPR-resident accumulator, tied in place, with no pad: its V^T
+// operand comes from LDS or from register copies made before the tile barrier, and its P^T
+// operands are converted several instructions ahead (the assembly test holds this).
 __device__ __forceinline__ void mfma_pv(floatx16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // O *= alpha on the AGPR-resident accumulators, in place: each element is read to a VGPR,
