@@ -336,7 +336,10 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
 
   // The scores are used as fma(S, c, -m) with c = |scale * log2 e|. A negative scale is moved
   // into Q by flipping the sign bits of its bf16 elements, which is exact.
-  const float c_scale = fabsf(a.scale_log2);
+  // Masked keys carry a score of -inf, which c * (-inf) keeps at -inf only for c > 0. A zero
+  // scale is therefore raised to 1e-30: every |c * (x - m)| then stays far below 2^-24 for any
+  // finite score, so each valid key still gets p = exp2(0) = 1 exactly, as with c = 0.
+  const float c_scale = fmaxf(fabsf(a.scale_log2), 1e-30f);
   const uint32_t q_sign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // ---- resolve this partition's slots and compact the valid rows into s_rows, in slot order.

@@ -135,6 +135,72 @@ def test_all_masked_tokens_give_zeros():
     _check(inp, _gpu(inp, num_splits=2), label="masked_tokens_split2")
 
 
+def _f32(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32)
+
+
+def _same_heads_sorted(inp, descending):
+    """Every head of a token gets head 0's query, and each token's valid slots are ordered by
+    their (now common) raw score. Ascending, the running max rises tile after tile, so the
+    online softmax rescales O again and again; descending, it never moves after the first tile.
+    The result is order-independent, so the oracle needs no change."""
+    T, H = inp.n_tokens, inp.n_q
+    qn = inp.query_nope.reshape(T, H, 512).copy()
+    qr = inp.query_rope.reshape(T, H, 64).copy()
+    qn[:] = qn[:, :1]
+    qr[:] = qr[:, :1]
+    rows = O.resolve_rows(inp.topk_indices, inp.block_table, inp.kv_act_seqs, inp.s1)
+    kn, kr = _f32(inp.key_nope), _f32(inp.key_rope)
+    idx = inp.topk_indices.copy()
+    for t in range(T):
+        valid = rows[t] >= 0
+        r = rows[t][valid]
+        score = kn[r] @ _f32(qn[t, 0]) + kr[r] @ _f32(qr[t, 0])
+        order = np.argsort(-score if descending else score, kind="stable")
+        n = int(valid.sum())
+        idx[t, :n] = inp.topk_indices[t][valid][order]
+        idx[t, n:] = -1
+    return W.SfaInputs(**{**inp.__dict__, "query_nope": qn.reshape(T * H, 512),
+                          "query_rope": qr.reshape(T * H, 64), "topk_indices": idx})
+
+
+@pytest.mark.parametrize("descending", [False, True])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_rising_and_falling_running_max(descending, splits):
+    # softmax scale 2: the sorted scores climb by more than the rescale threshold per tile
+    base = W.generate(batch=2, s1=1, n_q=64, act_seqs=[4096, 3000], topk=1024, seed=31, softmax_scale=2.0,
+                      max_blocks_per_batch=32)
+    inp = _same_heads_sorted(base, descending)
+    _check(inp, _gpu(inp, num_splits=splits), label=f"sorted_desc{int(descending)}_splits{splits}")
+
+
+@pytest.mark.parametrize("scale", [-0.05, 0.0])
+def test_negative_and_zero_scale(scale):
+    # a negative scale is folded into Q's sign bits; scale 0 makes every score equal (the
+    # output is the plain mean of the selected value rows)
+    inp = W.generate(batch=2, s1=2, n_q=128, act_seqs=[2500, 900], topk=700, seed=32, softmax_scale=scale,
+                     max_blocks_per_batch=20)
+    _check(inp, _gpu(inp), label=f"scale{scale}")
+
+
+def test_duplicate_and_scattered_invalid_indices():
+    # duplicates count once per occurrence; -1, negative and past-the-end indices may sit
+    # anywhere in the row
+    inp = W.generate(batch=3, s1=2, n_q=80, act_seqs=[1000, 300, 2000], topk=600, seed=33,
+                     max_blocks_per_batch=16)
+    rng = np.random.default_rng(33)
+    idx = inp.topk_indices.copy()
+    for t in range(inp.n_tokens):
+        act = int(inp.kv_act_seqs[t // inp.s1])
+        row = rng.integers(0, act, size=inp.topk)                       # with repeats
+        bad = rng.random(inp.topk) < 0.2
+        row[bad] = rng.choice([-1, -7, act, act + 5, 1 << 30], size=int(bad.sum()))
+        idx[t] = row
+    moved = W.SfaInputs(**{**inp.__dict__, "topk_indices": idx.astype(np.int32)})
+    _check(moved, _gpu(moved), label="dups_scattered_invalid")
+    _check(moved, _gpu(moved, num_splits=2), label="dups_scattered_invalid_split2")
+
+
 def test_prefill_entry_small():
     inp = W.prefill(s1=300)
     _check(inp, _gpu(inp, prefill=True), label="prefill300")
