@@ -300,3 +300,101 @@ def page_case(name: str, seed: int = 0) -> SfaInputs:
 
 
 PAGE_CASES = ("total_int8_d", "per_int8_d", "per_bf16_d", "int8_p")
+
+
+# ----------------------------------------------------------------------------------------
+# Lightning Indexer inputs ("CANN DeepSeek Indexer attention optimisation", sections "Indexer
+# Prolog" and "Lightning Indexer"): per query token, index queries for each index head and the
+# head weights; per cache position, one index key, in a paged cache with the same block table
+# and live lengths as the latent cache.
+# ----------------------------------------------------------------------------------------
+
+INDEX_HEADS = 64
+INDEX_DIM = 128
+
+
+@dataclasses.dataclass
+class IndexerInputs:
+    """Shapes (T = batch * s1, H = index heads, D = index head dim, R = cache rows):
+      q_index      uint16 (T*H, D)   bf16 bits, row t*H + h
+      weights      float32 (T, H)
+      k_index      uint16 (R, D)     bf16 bits
+      block_table  int32 (batch, max_blocks_per_batch)
+      kv_act_seqs  int32 (batch,)
+    """
+
+    batch: int
+    s1: int
+    n_heads: int
+    head_dim: int
+    topk: int
+    q_index: np.ndarray
+    weights: np.ndarray
+    k_index: np.ndarray
+    block_table: np.ndarray
+    kv_act_seqs: np.ndarray
+    name: str = ""
+
+    @property
+    def n_tokens(self) -> int:
+        return self.batch * self.s1
+
+    @property
+    def num_cache_rows(self) -> int:
+        return int(self.k_index.shape[0])
+
+    @property
+    def max_blocks_per_batch(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def n_positions(self) -> int:
+        return self.max_blocks_per_batch * BLOCK_SIZE
+
+
+def indexer_generate(*, batch: int, s1: int, act_seqs: Sequence[int], topk: int, seed: int = 0,
+                     n_heads: int = INDEX_HEADS, head_dim: int = INDEX_DIM,
+                     max_blocks_per_batch: Optional[int] = None, extra_pool_blocks: int = 0,
+                     name: str = "") -> IndexerInputs:
+    """q_index and k_index are N(0,1) rounded to bf16. The head weights are N(0,1) times
+    1/sqrt(n_heads * head_dim), the normalisation the Indexer Prolog applies to its weights.
+    The pool holds the batches' blocks in a random order, any extra blocks and one trailing
+    poison block; block_table entries past a batch's live blocks point at the poison block,
+    and the poison block and every row of a live block at or past the live length are NaN."""
+    act = [int(a) for a in act_seqs]
+    assert len(act) == batch
+    g = torch.Generator().manual_seed(50_000 + int(seed))
+    nblk = [math.ceil(a / BLOCK_SIZE) for a in act]
+    mb = max_blocks_per_batch if max_blocks_per_batch is not None else max(1, max(nblk) if nblk else 1)
+    assert all(n <= mb for n in nblk), "kv_act_seqs exceeds max_blocks_per_batch * block_size"
+    n_used = sum(nblk)
+    n_pool = n_used + int(extra_pool_blocks) + 1
+    poison = n_pool - 1
+    perm = torch.randperm(n_used + int(extra_pool_blocks), generator=g).numpy().astype(np.int32)
+    bt = np.full((batch, mb), poison, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        bt[b, : nblk[b]] = perm[off: off + nblk[b]]
+        off += nblk[b]
+    rows = n_pool * BLOCK_SIZE
+    k = _normal_bf16(g, rows, head_dim)
+    k[poison * BLOCK_SIZE:] = BF16_QNAN
+    for b in range(batch):
+        tail = nblk[b] * BLOCK_SIZE - act[b]
+        if tail > 0:
+            last = int(bt[b, nblk[b] - 1])
+            k[last * BLOCK_SIZE + (BLOCK_SIZE - tail):(last + 1) * BLOCK_SIZE] = BF16_QNAN
+    t_count = batch * s1
+    q = _normal_bf16(g, t_count * n_heads, head_dim)
+    w = (torch.randn(t_count, n_heads, generator=g, dtype=torch.float32)
+         * float(1.0 / math.sqrt(n_heads * head_dim))).numpy()
+    return IndexerInputs(batch=batch, s1=s1, n_heads=n_heads, head_dim=head_dim, topk=topk, q_index=q,
+                         weights=w, k_index=k, block_table=bt, kv_act_seqs=np.array(act, dtype=np.int32),
+                         name=name)
+
+
+def indexer_decode(seed: int = 0) -> IndexerInputs:
+    """The decode shape of the attention workload: B=64, S1=2, 8192 live positions each in a
+    4096-block pool, 64 index heads of 128 dims, top-k 2048."""
+    return indexer_generate(batch=64, s1=2, act_seqs=[8192] * 64, topk=2048, seed=seed,
+                            name="indexer_b64_s2_h64_d128_kv8192_topk2048")
