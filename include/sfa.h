@@ -157,6 +157,60 @@ const char* sfa_status_string(int status);
  * (is_prefill = 1) will use for `dims` (host-only). Returns a negative sfa_status on bad dims. */
 int sfa_num_splits(const sfa_dims* dims, int is_prefill);
 
+/*
+ * ---- Lightning Indexer and top-k selection: the step that produces topk_indices ----
+ *
+ * "CANN DeepSeek Indexer attention optimisation", sections "Lightning Indexer" and "Sparse
+ * Flash Attention": for query token i and cache position j the index score is
+ *     I[i, j] = sum over index heads h of w[i, h] * ReLU(q_index[i, h] . k_index[j]),
+ * and token i attends to the k positions with the largest I[i, :]. The index keys live in a
+ * paged cache with the same block table and live lengths as the latent cache (the operator's
+ * prototype passes index_k_cache beside block_table and act_seqs).
+ *
+ * The conventions of the attention entry points hold: device pointers, 16-byte alignment,
+ * asynchronous on `stream`, synchronous host validation with the same status codes, no
+ * allocation. Position j of batch b is live iff 0 <= j < kv_act_seqs[b] (both tokens of an
+ * MTP pair share the bound); the same data preconditions on block_table apply.
+ */
+typedef struct {
+  int32_t batch;
+  int32_t s1;                   /* query tokens per batch; T = batch * s1                       */
+  int32_t n_heads;              /* index heads: must be 64                                      */
+  int32_t head_dim;             /* index head dim: must be 128                                  */
+  int32_t block_size;           /* must be 128                                                  */
+  int32_t max_blocks_per_batch; /* row length of block_table; positions per token = 128 * this  */
+  int64_t num_cache_rows;       /* rows of index_k_cache                                        */
+  int32_t topk;                 /* positions selected per token (>= 1)                          */
+} sfa_indexer_dims;
+
+/*
+ * Index scores.
+ *   q_index        bf16  (T*64, 128)    row t*64 + h
+ *   k_index_cache  bf16  (num_cache_rows, 128)
+ *   weights        fp32  (T, 64)        the per-token head weights w[i, :]
+ *   block_table    int32 (batch, max_blocks_per_batch)
+ *   kv_act_seqs    int32 (batch)
+ *   scores         fp32  (T, max_blocks_per_batch*128), written in full: I[t, j] for live j,
+ *                  -inf for every other position
+ * Dot products accumulate in fp32 from exact bf16 products; ReLU, weighting and the head sum
+ * are fp32.
+ */
+int sfa_indexer_scores(const sfa_indexer_dims* dims, const void* q_index, const void* k_index_cache,
+                       const float* weights, const int32_t* block_table, const int32_t* kv_act_seqs,
+                       float* scores, hipStream_t stream);
+
+/*
+ * Top-k selection over the scores of sfa_indexer_scores (same dims and kv_act_seqs).
+ *   topk_indices   int32 (T, topk)  output: the logical positions of the topk largest scores
+ *                  of each token's live positions, in no particular order. With fewer live
+ *                  positions than topk, all of them are selected (in position order) and the
+ *                  rest of the row is -1. The result can be passed straight to sfa_decode.
+ * Among scores equal to the k-th largest, the lowest positions are taken. The selection is
+ * exact on the fp32 scores given.
+ */
+int sfa_topk_select(const sfa_indexer_dims* dims, const float* scores, const int32_t* kv_act_seqs,
+                    int32_t* topk_indices, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,8 +62,26 @@ _lib.sfa_resolve_rows.restype = ctypes.c_int
 _lib.sfa_status_string.argtypes = [ctypes.c_int]
 _lib.sfa_status_string.restype = ctypes.c_char_p
 
+class SfaIndexerDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("s1", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_batch", ctypes.c_int32),
+        ("num_cache_rows", ctypes.c_int64),
+        ("topk", ctypes.c_int32),
+    ]
+
+
+_lib.sfa_indexer_scores.argtypes = [ctypes.POINTER(SfaIndexerDims), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.sfa_indexer_scores.restype = ctypes.c_int
+_lib.sfa_topk_select.argtypes = [ctypes.POINTER(SfaIndexerDims), _vp, _vp, _vp, _vp]
+_lib.sfa_topk_select.restype = ctypes.c_int
+
 EXPORTED_SYMBOLS = ("sfa_workspace_size", "sfa_num_splits", "sfa_decode", "sfa_prefill", "sfa_resolve_rows",
-                    "sfa_status_string")
+                    "sfa_status_string", "sfa_indexer_scores", "sfa_topk_select")
 
 
 class SfaError(RuntimeError):
@@ -248,3 +266,87 @@ def run(inp, dev_tensors=None, *, prefill_mode=False, num_splits=0, out=None):
     return fn(d["query_nope"], d["query_rope"], d["key_nope"], d["key_rope"], d["k_nope_scales"], d["topk_indices"],
               d["block_table"], d["kv_act_seqs"], inp.softmax_scale, batch=inp.batch, s1=inp.s1,
               num_splits=num_splits, out=out)
+
+
+# ---- Lightning Indexer ---------------------------------------------------------------------
+
+INDEX_HEADS = 64
+INDEX_DIM = 128
+
+
+def make_indexer_dims(*, batch: int, s1: int, max_blocks_per_batch: int, num_cache_rows: int, topk: int,
+                      n_heads: int = INDEX_HEADS, head_dim: int = INDEX_DIM, block_size: int = BLOCK_SIZE):
+    return SfaIndexerDims(batch, s1, n_heads, head_dim, block_size, max_blocks_per_batch, num_cache_rows, topk)
+
+
+def indexer_scores(q_index, k_index_cache, weights, block_table, kv_act_seqs, *, batch, s1, topk=1,
+                   scores=None, stream=None):
+    """sfa_indexer_scores: returns scores (batch*s1, max_blocks_per_batch*128) fp32."""
+    dev = q_index.device
+    t_tokens = batch * s1
+    rows = k_index_cache.shape[0]
+    mb = block_table.shape[1]
+    _check(q_index, "q_index", (torch.bfloat16,), (t_tokens * INDEX_HEADS, INDEX_DIM), dev)
+    _check(k_index_cache, "k_index_cache", (torch.bfloat16,), (rows, INDEX_DIM), dev)
+    _check(weights, "weights", (torch.float32,), (t_tokens, INDEX_HEADS), dev)
+    _check(block_table, "block_table", (torch.int32,), (batch, mb), dev)
+    _check(kv_act_seqs, "kv_act_seqs", (torch.int32,), (batch,), dev)
+    dims = make_indexer_dims(batch=batch, s1=s1, max_blocks_per_batch=mb, num_cache_rows=rows, topk=topk)
+    if scores is None:
+        scores = torch.empty((t_tokens, mb * BLOCK_SIZE), dtype=torch.float32, device=dev)
+    _check(scores, "scores", (torch.float32,), (t_tokens, mb * BLOCK_SIZE), dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = _lib.sfa_indexer_scores(ctypes.byref(dims), _ptr(q_index), _ptr(k_index_cache), _ptr(weights),
+                                 _ptr(block_table), _ptr(kv_act_seqs), _ptr(scores), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise SfaError(st, "sfa_indexer_scores")
+    return scores
+
+
+def topk_select(scores, kv_act_seqs, *, batch, s1, topk, out=None, stream=None):
+    """sfa_topk_select: returns topk_indices (batch*s1, topk) int32 (unsorted, -1 padded)."""
+    dev = scores.device
+    t_tokens = batch * s1
+    n_pos = scores.shape[1]
+    _check(scores, "scores", (torch.float32,), (t_tokens, n_pos), dev)
+    _check(kv_act_seqs, "kv_act_seqs", (torch.int32,), (batch,), dev)
+    if n_pos % BLOCK_SIZE:
+        raise ValueError("scores must have a multiple of 128 columns")
+    dims = make_indexer_dims(batch=batch, s1=s1, max_blocks_per_batch=n_pos // BLOCK_SIZE, num_cache_rows=0,
+                             topk=topk)
+    if out is None:
+        out = torch.empty((t_tokens, topk), dtype=torch.int32, device=dev)
+    _check(out, "topk_indices", (torch.int32,), (t_tokens, topk), dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = _lib.sfa_topk_select(ctypes.byref(dims), _ptr(scores), _ptr(kv_act_seqs), _ptr(out),
+                              ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise SfaError(st, "sfa_topk_select")
+    return out
+
+
+def indexer_to_device(inp, device="cuda"):
+    """Upload a workloads.IndexerInputs instance."""
+    import numpy as np
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    return {
+        "q_index": bf16(inp.q_index),
+        "k_index": bf16(inp.k_index),
+        "weights": torch.from_numpy(np.ascontiguousarray(inp.weights)).to(device),
+        "block_table": torch.from_numpy(inp.block_table).to(device),
+        "kv_act_seqs": torch.from_numpy(inp.kv_act_seqs).to(device),
+    }
+
+
+def run_indexer(inp, dev_tensors=None):
+    """Scores and top-k of an uploaded IndexerInputs instance: (scores, topk_indices)."""
+    d = dev_tensors if dev_tensors is not None else indexer_to_device(inp)
+    sc = indexer_scores(d["q_index"], d["k_index"], d["weights"], d["block_table"], d["kv_act_seqs"],
+                        batch=inp.batch, s1=inp.s1, topk=inp.topk)
+    idx = topk_select(sc, d["kv_act_seqs"], batch=inp.batch, s1=inp.s1, topk=inp.topk)
+    return sc, idx

@@ -154,3 +154,49 @@ def test_status_strings():
     for code in range(-8, 1):
         assert sfa.status_string(code)
     assert sfa.status_string(-99) == "unknown status"
+
+
+# ---- Lightning Indexer entry points: host validation only (no pointer is dereferenced) ----
+
+def _idims(**kw):
+    base = dict(batch=2, s1=2, max_blocks_per_batch=4, num_cache_rows=1024, topk=64)
+    base.update(kw)
+    return sfa.make_indexer_dims(**base)
+
+
+def _iscores(dims, **ptrs):
+    p = dict(q=0x100000, k=0x10000000, w=0x200000, bt=0x300000, act=0x400000, scores=0x40000000)
+    p.update(ptrs)
+    vp = lambda v: None if v is None else ctypes.c_void_p(v)  # noqa: E731
+    return sfa._lib.sfa_indexer_scores(ctypes.byref(dims), vp(p["q"]), vp(p["k"]), vp(p["w"]), vp(p["bt"]),
+                                       vp(p["act"]), vp(p["scores"]), None)
+
+
+def _iselect(dims, **ptrs):
+    p = dict(scores=0x40000000, act=0x400000, out=0x50000000)
+    p.update(ptrs)
+    vp = lambda v: None if v is None else ctypes.c_void_p(v)  # noqa: E731
+    return sfa._lib.sfa_topk_select(ctypes.byref(dims), vp(p["scores"]), vp(p["act"]), vp(p["out"]), None)
+
+
+@pytest.mark.parametrize("field,value", [("n_heads", 32), ("head_dim", 64), ("block_size", 64), ("topk", 0),
+                                         ("batch", -1), ("s1", -1), ("max_blocks_per_batch", 0),
+                                         ("num_cache_rows", -1)])
+def test_indexer_bad_dims_rejected(field, value):
+    d = _idims()
+    setattr(d, field, value)
+    assert _iscores(d) == -2
+    assert _iselect(d) == -2
+
+
+def test_indexer_validation_errors():
+    d = _idims()
+    assert _iscores(d, q=None) == -1
+    assert _iscores(d, scores=None) == -1
+    assert _iscores(d, w=0x200004) == -3                 # misaligned
+    assert _iscores(d, scores=0x100000 + 4096) == -6     # scores overlapping q_index
+    assert _iselect(d, out=None) == -1
+    assert _iselect(d, out=0x50000008) == -3
+    assert _iselect(d, out=0x40000000 + 64) == -6        # indices overlapping the scores
+    empty = _idims(batch=0)
+    assert _iscores(empty) == 0 and _iselect(empty) == 0
