@@ -143,6 +143,138 @@ def cpu_baseline(inp, gpu_out, seconds: float):
     }
 
 
+def warm_up(step, args, torch):
+    """Untimed calls before timing: exactly --warmup if given, else at least 10 calls and at
+    least --warmup-seconds (from idle, the GPU needs time to raise its clocks)."""
+    n_warm = 0
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step(n_warm)
+            n_warm += 1
+    else:
+        t_w = time.perf_counter()
+        while n_warm < 10 or time.perf_counter() - t_w < args.warmup_seconds:
+            for _ in range(10):
+                step(n_warm)
+                n_warm += 1
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n_warm
+
+
+INDEXER_METRIC = "µs/call (index scores + top-k select) vs roofline, B=64 S1=2 kv=8192 topk=2048 indexer"
+
+
+def bench_indexer(args):
+    """The Lightning Indexer step that produces topk_indices: sfa_indexer_scores then
+    sfa_topk_select, on the decode shape (64 sequences x 2 tokens, 8192 live positions, 64
+    index heads x 128 dims, top-k 2048). Cold protocol as for attention: --sets copies of the
+    index-key pool, each in its own physical block order."""
+    import numpy as np
+    import torch
+
+    import oracle.indexer_oracle as IO
+    from mla_sparse_top_amd import sfa, workloads
+
+    inp = workloads.indexer_decode(seed=args.seed)
+    print(f"[bench] generated the indexer inputs, {inp.n_tokens} tokens x {inp.n_positions} positions", file=sys.stderr,
+          flush=True)
+    dev0 = sfa.indexer_to_device(inp)
+    n_pool = inp.num_cache_rows // 128
+    sets = [dev0]
+    for i in range(1, max(1, args.sets)):
+        g = torch.Generator(device="cpu").manual_seed(1000 + i)
+        perm = torch.randperm(n_pool, generator=g).to("cuda")
+        d = dict(dev0)
+        moved = torch.empty_like(dev0["k_index"].view(n_pool, 128, -1))
+        moved[perm] = dev0["k_index"].view(n_pool, 128, -1)
+        d["k_index"] = moved.view_as(dev0["k_index"])
+        d["block_table"] = perm.to(torch.int32)[dev0["block_table"].long()].contiguous()
+        sets.append(d)
+    T, n_pos, K = inp.n_tokens, inp.n_positions, inp.topk
+    scores = [torch.empty((T, n_pos), dtype=torch.float32, device="cuda") for _ in sets]
+    outs = [torch.empty((T, K), dtype=torch.int32, device="cuda") for _ in sets]
+
+    def step(i, ev=None):
+        k = i % len(sets)
+        d = sets[k]
+        sfa.indexer_scores(d["q_index"], d["k_index"], d["weights"], d["block_table"], d["kv_act_seqs"],
+                           batch=inp.batch, s1=inp.s1, topk=K, scores=scores[k])
+        if ev is not None:
+            ev.record()
+        sfa.topk_select(scores[k], d["kv_act_seqs"], batch=inp.batch, s1=inp.s1, topk=K, out=outs[k])
+
+    n_warm = warm_up(step, args, torch)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    whole0, whole1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    whole0.record()
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(i, ev[i][1])
+        ev[i][2].record()
+    whole1.record()
+    torch.cuda.synchronize()
+    us_per_call = whole0.elapsed_time(whole1) / args.steps * 1e3
+    score_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    select_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    same = all(torch.equal(outs[0], o) for o in outs[1:]) and all(torch.equal(scores[0], s) for s in scores[1:])
+
+    live = int(sum(int(inp.kv_act_seqs[t // inp.s1]) for t in range(T)))
+    live_keys = int(inp.kv_act_seqs.sum())
+    score_bytes = live_keys * 128 * 2 + T * (64 * 128 * 2 + 64 * 4) + T * n_pos * 4
+    score_flop = live * (2 * 64 * 128 + 2 * 64)
+    gbps = score_bytes / (score_ms * 1e-3) / 1e9
+    rec = {
+        "metric": INDEXER_METRIC,
+        "value": round(us_per_call, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": n_warm,
+        "ms_per_step": round(us_per_call / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": inp.batch, "s1": inp.s1, "index_heads": inp.n_heads,
+                   "index_dim": inp.head_dim, "kv_len": int(inp.kv_act_seqs.max()), "block_size": 128,
+                   "topk": K, "cold_sets": len(sets)},
+        "scores_kernel_ms_mean": round(score_ms, 5),
+        "select_kernel_ms_mean": round(select_ms, 5),
+        "algorithmic_bytes_scores": score_bytes,
+        "algorithmic_flop_scores": score_flop,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "scores_tflops": round(score_flop / (score_ms * 1e-3) / 1e12, 1),
+        "rotated_outputs_identical": bool(same),
+    }
+    if args.cpu_seconds > 0:
+        # the oracle (fp64 scores, then the selection) over whole tokens until the budget is spent
+        got_sc = scores[(args.steps - 1) % len(sets)].cpu().numpy()
+        got_idx = outs[(args.steps - 1) % len(sets)].cpu().numpy()
+        q = inp.q_index.reshape(T, inp.n_heads, inp.head_dim)
+        order = np.random.default_rng(0).permutation(T)
+        t0 = time.perf_counter()
+        done, bad = 0, 0
+        while done == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            t = int(order[done % T])
+            b = t // inp.s1
+            ref = IO.indexer_scores(q[t:t + 1], inp.weights[t:t + 1], inp.k_index, inp.block_table[b:b + 1],
+                                    inp.kv_act_seqs[b:b + 1], 1, n_pos)
+            IO.topk_positions(ref, K)
+            if done < T:
+                bad += len(IO.check_topk(got_idx[t:t + 1], got_sc[t:t + 1].astype(np.float64), K)["bad"])
+            done += 1
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(el / done * T * 1e6, 1), "unit": "us/call", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle", "sample": f"{done} token evaluations (scores + selection, random "
+                               f"order, seed 0) in {el:.1f} s, scaled to one call of {T} tokens",
+                               "selection_rows_checked": min(done, T), "selection_rows_bad": bad}
+    print(json.dumps(rec), flush=True)
+
+
 def copy_calibration(mib: int, steps: int):
     """A plain copy of a known size: it reads and writes exactly mib MiB per launch, so the HBM
     byte counters read on it give the factor that turns their readings into bytes."""
@@ -172,7 +304,7 @@ def main():
                     help="untimed calls before the timed region (default: at least 10 and at least "
                          "--warmup-seconds of calls, so the GPU clocks have left their idle state)")
     ap.add_argument("--warmup-seconds", type=float, default=0.5)
-    ap.add_argument("--workload", default="decode_b64_s2_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="decode_b64_s2_bf16", choices=sorted(WORKLOADS) + ["indexer_b64_s2"])
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated for a cold cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget (0 disables)")
     ap.add_argument("--seed", type=int, default=0)
@@ -190,6 +322,10 @@ def main():
 
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib, args.steps)
+        return
+
+    if args.workload == "indexer_b64_s2":
+        bench_indexer(args)
         return
 
     from mla_sparse_top_amd import sfa, workloads
@@ -212,20 +348,7 @@ def main():
     # Warm-up. From idle, the GPU takes a while to raise its clocks: measured on the default
     # decode workload, the kernel runs ~150 us per call after 10 warm-up calls and ~126 us after
     # 1,000 or more. Without an explicit --warmup, calls run until --warmup-seconds have passed.
-    n_warm = 0
-    if args.warmup is not None:
-        for _ in range(args.warmup):
-            step(n_warm)
-            n_warm += 1
-    else:
-        t_w = time.perf_counter()
-        while n_warm < 10 or time.perf_counter() - t_w < args.warmup_seconds:
-            for _ in range(10):
-                step(n_warm)
-                n_warm += 1
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    args.warmup = n_warm
+    args.warmup = warm_up(step, args, torch)
 
     # per-launch events on the stream the kernel runs on (torch's current stream)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]

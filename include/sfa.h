@@ -205,8 +205,9 @@ int sfa_indexer_scores(const sfa_indexer_dims* dims, const void* q_index, const 
  *                  of each token's live positions, in no particular order. With fewer live
  *                  positions than topk, all of them are selected (in position order) and the
  *                  rest of the row is -1. The result can be passed straight to sfa_decode.
- * Among scores equal to the k-th largest, the lowest positions are taken. The selection is
- * exact on the fp32 scores given.
+ * Among scores equal to the k-th largest, the lowest positions are taken (-0.0 equals +0.0).
+ * The selection is exact on the fp32 scores given. A NaN score ranks by its sign bit: above
+ * +inf when positive, below -inf when negative (sfa_indexer_scores never writes one).
  */
 int sfa_topk_select(const sfa_indexer_dims* dims, const float* scores, const int32_t* kv_act_seqs,
                     int32_t* topk_indices, hipStream_t stream);

@@ -37,6 +37,10 @@ IndexerArgs base_args(const sfa_indexer_dims* d) {
   a.n_pos = d->max_blocks_per_batch * kIdxBlock;
   a.chunks = (d->s1 + kIdxTokenChunk - 1) / kIdxTokenChunk;
   a.topk = d->topk;
+  // about four workgroups per CU over the whole grid, each running a few pages so that its
+  // staged queries serve several pages of keys
+  const int64_t pages = (int64_t)a.batch * a.chunks * a.mb;
+  a.pages_per_wg = (int)(pages / 1024 < 1 ? 1 : (pages / 1024 > kIdxMaxPagesPerWg ? kIdxMaxPagesPerWg : pages / 1024));
   return a;
 }
 

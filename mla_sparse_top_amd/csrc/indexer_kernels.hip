@@ -6,19 +6,22 @@
 // the k positions with the largest I[i, :] are the token's top-k set for sparse attention.
 // How it is computed here:
 //
-//   * Scores: a workgroup owns one 128-position page of one batch and up to 8 of its query
-//     tokens. Each wave takes 32 positions. Their index keys (32 rows x 256 bytes, one
-//     contiguous run of the page) are loaded straight into the B operand layout of
-//     v_mfma_f32_32x32x16_bf16 and stay in registers while the wave runs the tokens: per token,
-//     S^T = Q . K^T with the 64 heads on M (two 32-head blocks) and the positions on N, 8
-//     k-steps over the 128 dims. Each lane then holds one position and 16 heads of each block,
-//     so the ReLU, the head weighting and the sum over heads are in-lane, plus one cross-lane
-//     add. Positions past the live length (and whole dead pages) score -inf.
-//   * Top-k: one workgroup per token runs a most-significant-digit-first radix select over the
-//     scores' order-preserving 32-bit keys: four 8-bit histogram passes in LDS find the k-th
-//     largest key exactly and how many of the keys equal to it belong to the top k. A last pass
-//     writes the positions above that key, then the first of the equal ones in position
-//     order, at offsets from block-wide prefix sums. The output is unsorted.
+//   * Scores: a workgroup owns up to 4 query tokens of one batch and a run of that batch's
+//     128-position pages. It first copies the tokens' index queries (16 KB each) and head
+//     weights into LDS. Each wave then takes 32 positions of every page: their index keys (32
+//     rows x 256 bytes, one contiguous run of the page) are loaded straight into the B operand
+//     layout of v_mfma_f32_32x32x16_bf16, the next page's keys in flight while this page runs.
+//     Per token, S^T = Q . K^T has the 64 heads on M (two 32-head blocks, A operand read from
+//     LDS) and the positions on N, 8 k-steps over the 128 dims. Each lane then holds one
+//     position and 16 heads of each block, so the ReLU, the head weighting and the sum over
+//     heads are in-lane, plus one cross-lane add. Positions past the live length (and whole
+//     dead pages) score -inf.
+//   * Top-k: one workgroup of 1024 threads per token runs a most-significant-digit-first radix
+//     select over the scores' order-preserving 32-bit keys, held in LDS when a token has at most
+//     32768 positions. Three histogram passes (12, 10 and 10 bits) find the k-th largest key
+//     exactly and how many of the keys equal to it belong to the top k. A last pass writes the
+//     positions above that key, then the first of the equal ones in position order, at offsets
+//     from block-wide prefix sums. The output is unsorted.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -33,70 +36,157 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kScoreThreads = 256;  // 4 waves x 32 positions = one page
-constexpr int kSelectThreads = 256;
+constexpr int kRowPieces = kIdxDim * 2 / 16;  // 16-byte pieces of a 256-byte q or k row
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectWaves = kSelectThreads / 64;
 
-__global__ void __launch_bounds__(kScoreThreads) indexer_scores_kernel(const IndexerArgs a) {
-  const int jb = blockIdx.x;                  // logical page
-  const int b = blockIdx.y / a.chunks;
-  const int c = blockIdx.y - b * a.chunks;
-  const int t0 = b * a.s1 + c * kIdxTokenChunk;
-  const int t1 = min(b * a.s1 + a.s1, t0 + kIdxTokenChunk);
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 31;  // position within the wave's 32 (B operand column, result column)
-  const int g = lane >> 5;  // k-group of the operands / row-quad parity of the result
-  const int pos = jb * kIdxBlock + wave * 32 + n;
-  const int lim = min(a.act[b], a.n_pos);
+// Buffer resource over the index keys of one page: 128 rows x 256 bytes from the page's first
+// row, or an empty range (every load returns zeros) for a page that is not read.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* k, int blk) {
+  const uint16_t* base = blk >= 0 ? k + (int64_t)blk * kIdxBlock * kIdxDim : k;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, blk >= 0 ? kIdxBlock * kIdxDim * 2 : 0,
+                                           0x00020000);
+}
 
-  int blk = -1;
-  if (jb * kIdxBlock < lim) blk = a.block_table[(int64_t)b * a.mb + jb];
-  if (blk < 0 || (int64_t)(blk + 1) * kIdxBlock > a.num_rows) {
-    // a page with no live position (or an invalid block-table entry): every score is -inf
-    for (int t = t0; t < t1; ++t)
-      if (g == 0) a.scores[(int64_t)t * a.n_pos + pos] = -INFINITY;
-    return;
-  }
-
-  // K^T operand (B[k][n]): lane (n, g) holds dims 16*ks + 8*g .. +7 of this position's key
-  const uint4* krow = reinterpret_cast<const uint4*>(a.k + ((int64_t)blk * kIdxBlock + wave * 32 + n) * kIdxDim);
-  bf16x8 kop[8];
+// Index keys of one wave's 32 positions of a page, in the B operand layout: lane (n, g) holds
+// dims 16*ks + 8*g .. +7 of position n's key in kop[ks].
+__device__ __forceinline__ void load_keys(bf16x8 (&kop)[8], __amdgpu_buffer_rsrc_t r, int wave, int n, int g) {
+  const int voff = (wave * 32 + n) * kIdxDim * 2 + g * 16;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) kop[ks] = __builtin_bit_cast(bf16x8, krow[2 * ks + g]);
+  for (int ks = 0; ks < 8; ++ks)
+    kop[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff + ks * 32, 0, 0));
+}
 
-  for (int t = t0; t < t1; ++t) {
-    // Q operand (A[m][k]): lane (n, g) holds dims 16*ks + 8*g .. +7 of head 32*hb + n
-    const uint4* q0 = reinterpret_cast<const uint4*>(a.q + ((int64_t)t * kIdxHeads + n) * kIdxDim);
-    const uint4* q1 = q0 + 32 * kIdxDim / 8;
+// Physical block of logical page p, or -1 when the page holds no live position or the table
+// entry does not name a block inside the cache.
+__device__ __forceinline__ int page_block(const IndexerArgs& a, int b, int p, int lim) {
+  if (p * kIdxBlock >= lim) return -1;
+  const int blk = a.block_table[(int64_t)b * a.mb + p];
+  return (blk < 0 || (int64_t)(blk + 1) * kIdxBlock > a.num_rows) ? -1 : blk;
+}
+
+// Scores of one page for the workgroup's NT tokens; q_s holds the tokens' queries with the
+// 16-byte pieces of head h's row XOR-swizzled by (h & 15), w_s their head weights.
+template <int NT>
+__device__ __forceinline__ void score_page(const IndexerArgs& a, const bf16x8 (&kop)[8], bool live_page, int p,
+                                           int t0, int lim, const uint4* q_s, const float4* w_s, int wave, int n,
+                                           int g) {
+  const int pos = p * kIdxBlock + wave * 32 + n;
+  const bool live = live_page && pos < lim;
+#pragma unroll
+  for (int tok = 0; tok < NT; ++tok) {
+    // one token at a time: keeps the register footprint of a single token's accumulators and
+    // lets the compiler count the outstanding key loads exactly
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4* qa = q_s + (tok * kIdxHeads + n) * kRowPieces;  // head n
+    const uint4* qb = qa + 32 * kRowPieces;                        // head 32 + n
     floatx16 acc0 = {}, acc1 = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q0[2 * ks + g]), kop[ks], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q1[2 * ks + g]), kop[ks], acc1, 0, 0, 0);
+      const int piece = (2 * ks + g) ^ (n & 15);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[piece]), kop[ks], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qb[piece]), kop[ks], acc1, 0, 0, 0);
     }
     // acc_hb[r] is head 32*hb + 8*(r/4) + 4*g + (r%4) at this lane's position
-    const float4* wr = reinterpret_cast<const float4*>(a.w + (int64_t)t * kIdxHeads);
-    float s = 0.f;
+    const float4* wr = w_s + tok * (kIdxHeads / 4);
+    float v = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 w0 = wr[2 * q + g];      // heads 8q + 4g .. +3
       const float4 w1 = wr[8 + 2 * q + g];  // heads 32 + 8q + 4g .. +3
-      s += w0.x * fmaxf(acc0[4 * q], 0.f) + w0.y * fmaxf(acc0[4 * q + 1], 0.f) +
+      v += w0.x * fmaxf(acc0[4 * q], 0.f) + w0.y * fmaxf(acc0[4 * q + 1], 0.f) +
            w0.z * fmaxf(acc0[4 * q + 2], 0.f) + w0.w * fmaxf(acc0[4 * q + 3], 0.f);
-      s += w1.x * fmaxf(acc1[4 * q], 0.f) + w1.y * fmaxf(acc1[4 * q + 1], 0.f) +
+      v += w1.x * fmaxf(acc1[4 * q], 0.f) + w1.y * fmaxf(acc1[4 * q + 1], 0.f) +
            w1.z * fmaxf(acc1[4 * q + 2], 0.f) + w1.w * fmaxf(acc1[4 * q + 3], 0.f);
     }
-    s += __shfl_xor(s, 32);  // the other 32 heads of each block sit in the partner lane
-    if (g == 0) a.scores[(int64_t)t * a.n_pos + pos] = pos < lim ? s : -INFINITY;
+    v += __shfl_xor(v, 32);  // the other 32 heads of each block sit in the partner lane
+    if (g == 0) a.scores[(int64_t)(t0 + tok) * a.n_pos + pos] = live ? v : -INFINITY;
   }
 }
 
-// Order-preserving map of a float onto uint32: a larger float gives a larger key.
+template <int NT>
+__device__ __forceinline__ void scores_body(const IndexerArgs& a, uint4* q_s, float4* w_s, const int (&blk)[kIdxMaxPagesPerWg],
+                                            int t0, int p0, int p1, int lim) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 31;  // position within the wave's 32 (B operand column, result column)
+  const int g = lane >> 5;  // k-group of the operands / row-quad parity of the result
+
+  // The first batch of query pieces and the weights are requested before the first page's keys,
+  // so that (loads return in order) staging them does not wait for the keys. Every thread loads
+  // and stores a weight vector (clamped index, w_s has a slot per thread) so that the load is
+  // unconditional and queues with the others.
+  constexpr int kQ = NT * kIdxHeads * kRowPieces / kScoreThreads;  // 16-byte pieces per thread
+  constexpr int kStep = kQ < 8 ? kQ : 8;                            // staged 8 at a time
+  const uint4* qg = reinterpret_cast<const uint4*>(a.q) + (int64_t)t0 * kIdxHeads * kRowPieces;
+  const float4 wv = reinterpret_cast<const float4*>(a.w + (int64_t)t0 * kIdxHeads)[min(tid, NT * kIdxHeads / 4 - 1)];
+  bf16x8 kbuf[2][8];
+#pragma unroll
+  for (int j0 = 0; j0 < kQ; j0 += kStep) {
+    uint4 qv[kStep];
+#pragma unroll
+    for (int j = 0; j < kStep; ++j) qv[j] = qg[tid + (j0 + j) * kScoreThreads];
+    if (j0 == 0) load_keys(kbuf[0], page_rsrc(a.k, blk[0]), wave, n, g);
+#pragma unroll
+    for (int j = 0; j < kStep; ++j) {
+      const int i = tid + (j0 + j) * kScoreThreads;
+      const int h = (i / kRowPieces) & (kIdxHeads - 1);
+      q_s[(i & ~(kRowPieces - 1)) | ((i & (kRowPieces - 1)) ^ (h & 15))] = qv[j];
+    }
+  }
+  w_s[tid] = wv;
+  __syncthreads();
+
+#pragma unroll
+  for (int i = 0; i < kIdxMaxPagesPerWg; ++i) {
+    if (p0 + i >= p1) break;
+    if (i + 1 < kIdxMaxPagesPerWg) load_keys(kbuf[(i + 1) & 1], page_rsrc(a.k, blk[i + 1]), wave, n, g);
+    score_page<NT>(a, kbuf[i & 1], blk[i] >= 0, p0 + i, t0, lim, q_s, w_s, wave, n, g);
+  }
+}
+
+__global__ void __launch_bounds__(kScoreThreads) indexer_scores_kernel(const IndexerArgs a) {
+  extern __shared__ uint4 q_s[];  // nt tokens x 64 heads x 16 pieces
+  __shared__ float4 w_s[kScoreThreads];  // the first nt * 16 hold the tokens' head weights
+  const int b = blockIdx.y / a.chunks;
+  const int c = blockIdx.y - b * a.chunks;
+  const int t0 = b * a.s1 + c * kIdxTokenChunk;
+  const int nt = min(kIdxTokenChunk, a.s1 - c * kIdxTokenChunk);
+  const int p0 = blockIdx.x * a.pages_per_wg;
+  const int p1 = min(a.mb, p0 + a.pages_per_wg);
+  const int lim = min(a.act[b], a.n_pos);
+
+  if (p0 * kIdxBlock >= lim) {  // nothing live in the whole run of pages
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int p = p0; p < p1; ++p)
+      for (int tok = 0; tok < nt; ++tok)
+        if (lane < 32) a.scores[(int64_t)(t0 + tok) * a.n_pos + p * kIdxBlock + wave * 32 + lane] = -INFINITY;
+    return;
+  }
+  // every block number of the run is read up front (uniform loads, before any store), and the
+  // page loop is unrolled, so that the loop never waits on a table read queued behind key loads
+  int blk[kIdxMaxPagesPerWg];
+#pragma unroll
+  for (int i = 0; i < kIdxMaxPagesPerWg; ++i) blk[i] = p0 + i < p1 ? page_block(a, b, p0 + i, lim) : -1;
+  switch (nt) {
+    case 1: scores_body<1>(a, q_s, w_s, blk, t0, p0, p1, lim); break;
+    case 2: scores_body<2>(a, q_s, w_s, blk, t0, p0, p1, lim); break;
+    case 3: scores_body<3>(a, q_s, w_s, blk, t0, p0, p1, lim); break;
+    default: scores_body<4>(a, q_s, w_s, blk, t0, p0, p1, lim); break;
+  }
+}
+
+// Order-preserving map of a float onto uint32: a larger float gives a larger key, and -0.0 and
+// +0.0 give the same key.
 __device__ __forceinline__ uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive prefix sum of v over the workgroup (kSelectThreads threads); `tmp` holds 4 ints.
+// Inclusive prefix sum of v over the workgroup (kSelectThreads threads); `tmp` holds one int
+// per wave.
 __device__ __forceinline__ int block_inclusive_scan(int v, int* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -108,16 +198,22 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* tmp) {
   __syncthreads();
   int add = 0;
 #pragma unroll
-  for (int w = 0; w < kSelectThreads / 64; ++w) add += (w < wave) ? tmp[w] : 0;
+  for (int w = 0; w < kSelectWaves; ++w) add += (w < wave) ? tmp[w] : 0;
   __syncthreads();
   return v + add;
 }
 
+struct SelectShared {
+  uint32_t hist[4096];
+  int scan_tmp[kSelectWaves];
+  uint32_t digit;
+  int remaining;
+};
+
+template <bool kCached>
 __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const IndexerArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ int scan_tmp[kSelectThreads / 64];
-  __shared__ uint32_t s_digit;
-  __shared__ int s_remaining;
+  __shared__ SelectShared sh;
+  __shared__ uint32_t keys[kCached ? kIdxSelCache : 1];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int b = t / a.s1;
@@ -130,31 +226,55 @@ __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const Index
     for (int i = tid; i < K; i += kSelectThreads) out[i] = i < n ? i : -1;
     return;
   }
+  if (kCached) {  // rows are 512-byte aligned (n_pos is a multiple of 128)
+    const float4* sc4 = reinterpret_cast<const float4*>(sc);
+    for (int i = tid; i < (n + 3) / 4; i += kSelectThreads) {
+      const float4 v = sc4[i];
+      keys[4 * i] = order_key(v.x);
+      keys[4 * i + 1] = order_key(v.y);
+      keys[4 * i + 2] = order_key(v.z);
+      keys[4 * i + 3] = order_key(v.w);
+    }
+  }
+  auto key_at = [&](int i) -> uint32_t { return kCached ? keys[i] : order_key(sc[i]); };
 
-  // k-th largest key, digit by digit from the top
+  // k-th largest key, digit by digit from the top: bits 31..20, 19..10, 9..0
   uint32_t prefix = 0, mask = 0;
-  int remaining = K;  // how many still to take among keys matching the prefix
+  int remaining = K;  // how many still to take among keys matching the prefix (<= their count)
 #pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    hist[tid] = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 0 ? 4096 : 1024;
+    for (int i = tid; i < nb; i += kSelectThreads) sh.hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kSelectThreads) {
-      const uint32_t key = order_key(sc[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      const uint32_t key = key_at(i);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
     }
     __syncthreads();
-    // thread tid looks at digit 255 - tid: its inclusive sum counts the keys at or above it
-    const int h = (int)hist[255 - tid];
-    const int incl = block_inclusive_scan(h, scan_tmp);
-    if (incl >= remaining && incl - h < remaining) {
-      s_digit = 255u - (uint32_t)tid;
-      s_remaining = remaining - (incl - h);
+    // thread tid takes digits nb-1-per*tid down to nb-per-per*tid; the inclusive scan of the
+    // group sums counts every matching key at or above the group's lowest digit
+    const int per = nb / kSelectThreads;
+    const int top = nb - 1 - per * tid;
+    int sum = 0;
+    for (int j = 0; j < per; ++j) sum += (int)sh.hist[top - j];
+    const int incl = block_inclusive_scan(sum, sh.scan_tmp);
+    if (incl >= remaining && incl - sum < remaining) {
+      int acc = incl - sum;
+      for (int j = 0; j < per; ++j) {
+        const int h = (int)sh.hist[top - j];
+        if (acc + h >= remaining) {
+          sh.digit = (uint32_t)(top - j);
+          sh.remaining = remaining - acc;
+          break;
+        }
+        acc += h;
+      }
     }
     __syncthreads();
-    prefix |= s_digit << shift;
-    mask |= 255u << shift;
-    remaining = s_remaining;
+    prefix |= sh.digit << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
+    remaining = sh.remaining;
     __syncthreads();
   }
   // prefix is the k-th largest key; `remaining` of the keys equal to it are taken, the first
@@ -165,15 +285,15 @@ __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const Index
   const int i0 = min(n, tid * chunk), i1 = min(n, i0 + chunk);
   int gt = 0, eq = 0;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t key = order_key(sc[i]);
+    const uint32_t key = key_at(i);
     gt += key > kth ? 1 : 0;
     eq += key == kth ? 1 : 0;
   }
-  int off_gt = block_inclusive_scan(gt, scan_tmp) - gt;
-  int off_eq = block_inclusive_scan(eq, scan_tmp) - eq;
+  int off_gt = block_inclusive_scan(gt, sh.scan_tmp) - gt;
+  int off_eq = block_inclusive_scan(eq, sh.scan_tmp) - eq;
   const int base_eq = K - need;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t key = order_key(sc[i]);
+    const uint32_t key = key_at(i);
     if (key > kth) {
       out[off_gt++] = i;
     } else if (key == kth) {
@@ -186,10 +306,12 @@ __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const Index
 }  // namespace
 
 hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.mb, (unsigned)(a.batch * a.chunks));
+  const int spans = (a.mb + a.pages_per_wg - 1) / a.pages_per_wg;
+  const dim3 grid((unsigned)spans, (unsigned)(a.batch * a.chunks));
+  const size_t lds = (size_t)min(a.s1, kIdxTokenChunk) * kIdxHeads * kRowPieces * sizeof(uint4);
   IndexerArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&indexer_scores_kernel), grid, dim3(kScoreThreads), args, 0,
+  return hipLaunchKernel(reinterpret_cast<const void*>(&indexer_scores_kernel), grid, dim3(kScoreThreads), args, lds,
                          stream);
 }
 
@@ -197,8 +319,9 @@ hipError_t launch_topk_select(const IndexerArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.batch * a.s1));
   IndexerArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&topk_select_kernel), grid, dim3(kSelectThreads), args, 0,
-                         stream);
+  const void* fn = a.n_pos <= kIdxSelCache ? reinterpret_cast<const void*>(&topk_select_kernel<true>)
+                                           : reinterpret_cast<const void*>(&topk_select_kernel<false>);
+  return hipLaunchKernel(fn, grid, dim3(kSelectThreads), args, 0, stream);
 }
 
 }  // namespace sfa

@@ -52,6 +52,18 @@ def _oracle(inp):
     return ref, mag
 
 
+def _ties_take_lowest(sel, scores):
+    """Among the scores equal to the lowest selected one, the selected positions are the lowest."""
+    for t in range(sel.shape[0]):
+        pos = sel[t][sel[t] >= 0]
+        if len(pos) == 0:
+            continue
+        kth = scores[t][pos].min()
+        eq = np.nonzero(scores[t] == kth)[0]
+        taken = np.sort(np.intersect1d(pos, eq))
+        assert np.array_equal(taken, eq[:len(taken)]), t
+
+
 def _check(inp, label):
     sfa = _lib()
     sc, idx = sfa.run_indexer(inp)
@@ -69,6 +81,7 @@ def _check(inp, label):
     # the selection, in the kernel's precision
     rep = IO.check_topk(sel, got, inp.topk)
     assert rep["bad"] == [], (label, rep["bad"][:5])
+    _ties_take_lowest(sel, got)
     # the selection against the fp64 scores: differences only inside the bound near the k-th value
     for t in range(inp.n_tokens):
         pos = sel[t][sel[t] >= 0]
@@ -100,6 +113,30 @@ def test_many_tokens_per_batch():
     _check(inp, "s1_19")
 
 
+def test_tokens_beyond_one_chunk():
+    # s1 = 5: one workgroup takes 4 tokens, another the fifth; s1 = 3 takes 3 at once
+    _check(W.indexer_generate(batch=2, s1=5, act_seqs=[900, 300], topk=200, seed=7, max_blocks_per_batch=8),
+           "s1_5")
+    _check(W.indexer_generate(batch=2, s1=3, act_seqs=[640, 1000], topk=333, seed=8, max_blocks_per_batch=8),
+           "s1_3")
+
+
+def test_several_pages_per_workgroup_ragged():
+    # 14 x 301 pages: each workgroup runs 4 pages, the last run of a batch is short, and the
+    # lengths give dead runs, dead pages inside a run and partial pages
+    rng = np.random.default_rng(11)
+    act = [int(v) for v in rng.integers(1, 301 * 128, size=14)]
+    act[0], act[1], act[2], act[3] = 0, 100, 128 * 4, 301 * 128
+    inp = W.indexer_generate(batch=14, s1=3, act_seqs=act, topk=1500, seed=11, max_blocks_per_batch=301)
+    _check(inp, "pages_per_wg_4")
+
+
+def test_rows_longer_than_the_lds_key_cache():
+    # 313 pages = 40064 positions per token: the selection reads its keys from global memory
+    inp = W.indexer_generate(batch=2, s1=1, act_seqs=[40000, 33000], topk=3000, seed=12, max_blocks_per_batch=313)
+    _check(inp, "uncached_select")
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_decode_shape_full(seed):
     _check(W.indexer_decode(seed=seed), f"decode_b64_s2_seed{seed}")
@@ -117,6 +154,31 @@ def test_select_ties_take_lowest_positions():
     assert set(out[0].tolist()) == set(range(100, 110)) | set(range(30))
     assert sorted(out[1].tolist()) == list(range(40))
     assert sorted(out[2].tolist()) == list(range(0, 80, 2))
+
+
+@pytest.mark.parametrize("n_pos", [8192, 40960])
+def test_select_large_ties_and_signs(n_pos):
+    # every score equal, then scores that differ only in their lowest bits, then mixed signs,
+    # then -0.0 beside +0.0; both the LDS-cached and the global-memory selection
+    sfa = _lib()
+    g = torch.Generator().manual_seed(5)
+    sc = torch.zeros((4, n_pos), dtype=torch.float32)
+    sc[0] = 0.75
+    base = torch.full((n_pos,), 1.0).view(torch.int32)
+    sc[1] = (base + torch.randint(0, 8, (n_pos,), generator=g, dtype=torch.int32)).view(torch.float32)
+    sc[2] = torch.randn(n_pos, generator=g)
+    sc[3, ::2] = -0.0
+    sc[3, 1::2] = 0.0
+    act = torch.full((4,), n_pos - 5, dtype=torch.int32)
+    K = 1000
+    out = sfa.topk_select(sc.cuda(), act.cuda(), batch=4, s1=1, topk=K).cpu().numpy()
+    scn = sc.numpy().astype(np.float64)
+    rep = IO.check_topk(out, np.where(np.arange(n_pos) < n_pos - 5, scn, -np.inf), K)
+    assert rep["bad"] == []
+    _ties_take_lowest(out, scn)
+    assert sorted(out[0].tolist()) == list(range(K))          # ties: the lowest positions
+    # row 3: -0.0 and +0.0 are equal scores, so again the lowest positions
+    assert sorted(out[3].tolist()) == list(range(K))
 
 
 def test_end_to_end_indexer_topk_attention():
