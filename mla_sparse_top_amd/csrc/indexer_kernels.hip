@@ -19,9 +19,11 @@
 //   * Top-k: one workgroup of 1024 threads per token runs a most-significant-digit-first radix
 //     select over the scores' order-preserving 32-bit keys, held in LDS when a token has at most
 //     32768 positions. Three histogram passes (12, 10 and 10 bits) find the k-th largest key
-//     exactly and how many of the keys equal to it belong to the top k. A last pass writes the
-//     positions above that key, then the first of the equal ones in position order, at offsets
-//     from block-wide prefix sums. The output is unsorted.
+//     exactly and how many of the keys equal to it belong to the top k; when the k-th key's
+//     12-bit bin holds at most 1024 keys, the last two passes run over that bin's keys alone. A
+//     last pass writes the positions above that key, then the first of the equal ones in
+//     position order, at offsets from block-wide prefix sums. The row is staged in LDS and stored
+//     whole when topk <= 4096. The output is unsorted.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -60,9 +62,8 @@ __device__ __forceinline__ void load_keys(bf16x8 (&kop)[8], __amdgpu_buffer_rsrc
 // Physical block of logical page p, or -1 when the page holds no live position or the table
 // entry does not name a block inside the cache.
 __device__ __forceinline__ int page_block(const IndexerArgs& a, int b, int p, int lim) {
-  if (p * kIdxBlock >= lim) return -1;
-  const int blk = a.block_table[(int64_t)b * a.mb + p];
-  return (blk < 0 || (int64_t)(blk + 1) * kIdxBlock > a.num_rows) ? -1 : blk;
+  const int blk = a.block_table[(int64_t)b * a.mb + p];  // p < mb: always inside the table
+  return (p * kIdxBlock >= lim || blk < 0 || (int64_t)(blk + 1) * kIdxBlock > a.num_rows) ? -1 : blk;
 }
 
 // Scores of one page for the workgroup's NT tokens; q_s holds the tokens' queries with the
@@ -75,31 +76,28 @@ __device__ __forceinline__ void score_page(const IndexerArgs& a, const bf16x8 (&
   const bool live = live_page && pos < lim;
 #pragma unroll
   for (int tok = 0; tok < NT; ++tok) {
-    // one token at a time: keeps the register footprint of a single token's accumulators and
-    // lets the compiler count the outstanding key loads exactly
-    __builtin_amdgcn_sched_barrier(0);
-    const uint4* qa = q_s + (tok * kIdxHeads + n) * kRowPieces;  // head n
-    const uint4* qb = qa + 32 * kRowPieces;                        // head 32 + n
-    floatx16 acc0 = {}, acc1 = {};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int piece = (2 * ks + g) ^ (n & 15);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[piece]), kop[ks], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qb[piece]), kop[ks], acc1, 0, 0, 0);
-    }
-    // acc_hb[r] is head 32*hb + 8*(r/4) + 4*g + (r%4) at this lane's position
-    const float4* wr = w_s + tok * (kIdxHeads / 4);
+    // one token and one 32-head block at a time: a single 16-register accumulator, and the
+    // compiler can count the outstanding key loads exactly
     float v = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 w0 = wr[2 * q + g];      // heads 8q + 4g .. +3
-      const float4 w1 = wr[8 + 2 * q + g];  // heads 32 + 8q + 4g .. +3
-      v += w0.x * fmaxf(acc0[4 * q], 0.f) + w0.y * fmaxf(acc0[4 * q + 1], 0.f) +
-           w0.z * fmaxf(acc0[4 * q + 2], 0.f) + w0.w * fmaxf(acc0[4 * q + 3], 0.f);
-      v += w1.x * fmaxf(acc1[4 * q], 0.f) + w1.y * fmaxf(acc1[4 * q + 1], 0.f) +
-           w1.z * fmaxf(acc1[4 * q + 2], 0.f) + w1.w * fmaxf(acc1[4 * q + 3], 0.f);
+    for (int hb = 0; hb < 2; ++hb) {
+      __builtin_amdgcn_sched_barrier(0);
+      const uint4* qh = q_s + (tok * kIdxHeads + 32 * hb + n) * kRowPieces;  // head 32*hb + n
+      floatx16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qh[(2 * ks + g) ^ (n & 15)]), kop[ks],
+                                                      acc, 0, 0, 0);
+      // acc[r] is head 32*hb + 8*(r/4) + 4*g + (r%4) at this lane's position
+      const float4* wr = w_s + tok * (kIdxHeads / 4) + 8 * hb;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 w = wr[2 * q + g];  // heads 32*hb + 8q + 4g .. +3
+        v += w.x * fmaxf(acc[4 * q], 0.f) + w.y * fmaxf(acc[4 * q + 1], 0.f) + w.z * fmaxf(acc[4 * q + 2], 0.f) +
+             w.w * fmaxf(acc[4 * q + 3], 0.f);
+      }
     }
-    v += __shfl_xor(v, 32);  // the other 32 heads of each block sit in the partner lane
+    v += __shfl_xor(v, 32);  // the other 16 heads of each row quad sit in the partner lane
     if (g == 0) a.scores[(int64_t)(t0 + tok) * a.n_pos + pos] = live ? v : -INFINITY;
   }
 }
@@ -146,14 +144,24 @@ __device__ __forceinline__ void scores_body(const IndexerArgs& a, uint4* q_s, fl
   }
 }
 
-__global__ void __launch_bounds__(kScoreThreads) indexer_scores_kernel(const IndexerArgs a) {
+// Accumulators in arch VGPRs (no AGPRs) within a budget of four waves per SIMD (128 registers).
+// Measured: a split VGPR/AGPR allocation of 148 registers ran only two waves per SIMD, where 154
+// arch VGPRs ran three.
+__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) indexer_scores_kernel(const IndexerArgs a) {
   extern __shared__ uint4 q_s[];  // nt tokens x 64 heads x 16 pieces
   __shared__ float4 w_s[kScoreThreads];  // the first nt * 16 hold the tokens' head weights
-  const int b = blockIdx.y / a.chunks;
-  const int c = blockIdx.y - b * a.chunks;
+  // Consecutive workgroups go to the 8 XCDs in turn. Renumber them so that each XCD runs whole
+  // rows of the grid (all page runs of the same tokens): a token's queries then reach one XCD's
+  // L2 instead of all eight.
+  const unsigned n_wg = gridDim.x * gridDim.y;
+  unsigned id = blockIdx.y * gridDim.x + blockIdx.x;
+  if ((n_wg & 7u) == 0) id = (id & 7u) * (n_wg >> 3) + (id >> 3);
+  const int row = (int)(id / gridDim.x);  // b * chunks + c
+  const int b = row / a.chunks;
+  const int c = row - b * a.chunks;
   const int t0 = b * a.s1 + c * kIdxTokenChunk;
   const int nt = min(kIdxTokenChunk, a.s1 - c * kIdxTokenChunk);
-  const int p0 = blockIdx.x * a.pages_per_wg;
+  const int p0 = (int)(id - (unsigned)row * gridDim.x) * a.pages_per_wg;
   const int p1 = min(a.mb, p0 + a.pages_per_wg);
   const int lim = min(a.act[b], a.n_pos);
 
@@ -204,18 +212,23 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* tmp) {
 }
 
 struct SelectShared {
-  uint32_t hist[4096];
+  uint32_t hist[4096];           // digit histogram; afterwards the output row is staged here
+  uint32_t cand[kSelectThreads]; // keys of the k-th key's 12-bit bin, when it holds at most 1024
   int scan_tmp[kSelectWaves];
   uint32_t digit;
   int remaining;
+  int bin_count;
+  int n_cand;
 };
+constexpr int kSelectStage = 4096;  // rows with topk up to this are staged in LDS, then stored whole
 
 template <bool kCached>
 __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const IndexerArgs a) {
   __shared__ SelectShared sh;
-  __shared__ uint32_t keys[kCached ? kIdxSelCache : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kCached ? kIdxSelCache : 4];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int b = t / a.s1;
   const int n = max(0, min(a.act[b], a.n_pos));
   const int K = a.topk;
@@ -230,26 +243,29 @@ __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const Index
     const float4* sc4 = reinterpret_cast<const float4*>(sc);
     for (int i = tid; i < (n + 3) / 4; i += kSelectThreads) {
       const float4 v = sc4[i];
-      keys[4 * i] = order_key(v.x);
-      keys[4 * i + 1] = order_key(v.y);
-      keys[4 * i + 2] = order_key(v.z);
-      keys[4 * i + 3] = order_key(v.w);
+      reinterpret_cast<uint4*>(keys)[i] = uint4{order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w)};
     }
   }
   auto key_at = [&](int i) -> uint32_t { return kCached ? keys[i] : order_key(sc[i]); };
 
-  // k-th largest key, digit by digit from the top: bits 31..20, 19..10, 9..0
+  // One most-significant-digit radix step: the digit at `shift` (nb bins) that holds the k-th
+  // largest of the keys matching (prefix, mask), and how many keys of that digit are still to
+  // be taken. The keys are all n positions, or the compacted candidates (one per thread).
   uint32_t prefix = 0, mask = 0;
   int remaining = K;  // how many still to take among keys matching the prefix (<= their count)
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 0 ? 4096 : 1024;
+  auto radix_step = [&](int shift, int nb, bool from_cand, int nc) {
     for (int i = tid; i < nb; i += kSelectThreads) sh.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kSelectThreads) {
-      const uint32_t key = key_at(i);
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+    if (from_cand) {
+      if (tid < nc) {
+        const uint32_t key = sh.cand[tid];
+        if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+    } else {
+      for (int i = tid; i < n; i += kSelectThreads) {
+        const uint32_t key = key_at(i);
+        if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
     }
     __syncthreads();
     // thread tid takes digits nb-1-per*tid down to nb-per-per*tid; the inclusive scan of the
@@ -266,21 +282,52 @@ __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const Index
         if (acc + h >= remaining) {
           sh.digit = (uint32_t)(top - j);
           sh.remaining = remaining - acc;
+          sh.bin_count = h;
           break;
         }
         acc += h;
       }
     }
+    if (tid == 0) sh.n_cand = 0;
     __syncthreads();
     prefix |= sh.digit << shift;
     mask |= (uint32_t)(nb - 1) << shift;
     remaining = sh.remaining;
+  };
+
+  // Digit 1 (bits 31..20) over every key. When the k-th key's bin holds at most one key per
+  // thread (the usual case), its keys are compacted and digits 2 and 3 (bits 19..10, 9..0) run
+  // over them alone; otherwise over every key again.
+  radix_step(20, 4096, false, 0);
+  const bool compact = sh.bin_count <= kSelectThreads;
+  __syncthreads();  // every thread has read sh before it is written again
+  int nc = 0;
+  if (compact) {
+    for (int i0 = 0; i0 < n; i0 += kSelectThreads) {
+      const int i = i0 + tid;
+      const bool hit = i < n && (key_at(i) & 0xfff00000u) == prefix;
+      const uint64_t m = __ballot(hit);
+      int base = 0;
+      if (lane == 0 && m) base = atomicAdd(&sh.n_cand, __popcll(m));
+      base = __shfl(base, 0);
+      if (hit) sh.cand[base + __popcll(m & ((1ull << lane) - 1))] = key_at(i);
+    }
     __syncthreads();
+    nc = sh.n_cand;
   }
+  radix_step(10, 1024, compact, nc);
+  __syncthreads();
+  radix_step(0, 1024, compact, nc);
+  __syncthreads();
+
   // prefix is the k-th largest key; `remaining` of the keys equal to it are taken, the first
   // ones in position order, after the K - remaining keys above it
   const uint32_t kth = prefix;
   const int need = remaining;
+  const bool stage = K <= kSelectStage;
+  int32_t* const dst = stage ? reinterpret_cast<int32_t*>(sh.hist) : out;
+  // contiguous runs of positions per thread, so that prefix sums over threads follow position
+  // order; with fewer than 32768 positions both counts share one 32-bit scan
   const int chunk = (n + kSelectThreads - 1) / kSelectThreads;
   const int i0 = min(n, tid * chunk), i1 = min(n, i0 + chunk);
   int gt = 0, eq = 0;
@@ -289,17 +336,29 @@ __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const Index
     gt += key > kth ? 1 : 0;
     eq += key == kth ? 1 : 0;
   }
-  int off_gt = block_inclusive_scan(gt, sh.scan_tmp) - gt;
-  int off_eq = block_inclusive_scan(eq, sh.scan_tmp) - eq;
+  int off_gt, off_eq;
+  if (n < 32768) {
+    const int packed = (gt << 16) | eq;
+    const int excl = block_inclusive_scan(packed, sh.scan_tmp) - packed;
+    off_gt = excl >> 16;
+    off_eq = excl & 0xffff;
+  } else {
+    off_gt = block_inclusive_scan(gt, sh.scan_tmp) - gt;
+    off_eq = block_inclusive_scan(eq, sh.scan_tmp) - eq;
+  }
   const int base_eq = K - need;
   for (int i = i0; i < i1; ++i) {
     const uint32_t key = key_at(i);
     if (key > kth) {
-      out[off_gt++] = i;
+      dst[off_gt++] = i;
     } else if (key == kth) {
-      if (off_eq < need) out[base_eq + off_eq] = i;
+      if (off_eq < need) dst[base_eq + off_eq] = i;
       ++off_eq;
     }
+  }
+  if (stage) {
+    __syncthreads();
+    for (int i = tid; i < K; i += kSelectThreads) out[i] = dst[i];
   }
 }
 
