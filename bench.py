@@ -78,10 +78,10 @@ def permuted_copy(dev, inp, seed):
     return out
 
 
-def traffic_from_profile(kernel_src_hash: str):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was taken on the same
-    kernel source (its recorded hash matches); otherwise None."""
-    path = os.path.join(ROOT, "profiles", "sfa_decode_b64_s2_bf16_traffic.txt")
+def traffic_from_profile(kernel_src_hash: str, name: str = "sfa_decode_b64_s2_bf16_traffic.txt"):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary under profiles/, if it was taken
+    on the same kernel source (its recorded hash matches); otherwise None."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -92,11 +92,11 @@ def traffic_from_profile(kernel_src_hash: str):
     return float(m_bytes.group(1))
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(names=("sfa_kernels.hip", "sfa_internal.h")) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in ("sfa_kernels.hip", "sfa_internal.h"):
+    for name in names:
         h.update(open(os.path.join(ROOT, "mla_sparse_top_amd", "csrc", name), "rb").read())
     return h.hexdigest()
 
@@ -220,6 +220,7 @@ def bench_indexer(args):
     select_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
     same = all(torch.equal(outs[0], o) for o in outs[1:]) and all(torch.equal(scores[0], s) for s in scores[1:])
 
+    src_hash = kernel_source_hash(("indexer_kernels.hip", "indexer_internal.h"))
     live = int(sum(int(inp.kv_act_seqs[t // inp.s1]) for t in range(T)))
     live_keys = int(inp.kv_act_seqs.sum())
     score_bytes = live_keys * 128 * 2 + T * (64 * 128 * 2 + 64 * 4) + T * n_pos * 4
@@ -246,9 +247,11 @@ def bench_indexer(args):
         "algorithmic_bytes_scores": score_bytes,
         "algorithmic_flop_scores": score_flop,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profile(src_hash, "indexer_scores_b64_s2_traffic.txt")},
         "scores_tflops": round(score_flop / (score_ms * 1e-3) / 1e12, 1),
         "rotated_outputs_identical": bool(same),
+        "kernel_source_sha256": src_hash,
     }
     if args.cpu_seconds > 0:
         # the oracle (fp64 scores, then the selection) over whole tokens until the budget is spent
