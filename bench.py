@@ -278,6 +278,121 @@ def bench_indexer(args):
     print(json.dumps(rec), flush=True)
 
 
+CACHE_WORKLOADS = {
+    "cache_write_b64_s8192_int8": ("cache_fill", "int8"),
+    "cache_write_b64_s8192_bf16": ("cache_fill", "bf16"),
+    "cache_write_b64_s2_int8": ("cache_decode_step", "int8"),
+}
+
+
+def bench_cache_write(args):
+    """The cache write (sfa_cache_write): new latent rows into the paged cache, INT8 quantised per
+    128-element group or copied as bf16. Default shape: every position of the decode workload's
+    cache (64 sequences x 8192 tokens, 524,288 rows). The rows read and written per call (about
+    1 GB) already exceed the 256 MB last-level cache; --sets copies are still rotated."""
+    import numpy as np
+    import torch
+
+    import oracle.cache_oracle as CO
+    from mla_sparse_top_amd import sfa, workloads
+
+    fn_name, dtype = CACHE_WORKLOADS[args.workload]
+    inp = getattr(workloads, fn_name)(seed=args.seed, kv_dtype=dtype)
+    print(f"[bench] generated {inp.name}", file=sys.stderr, flush=True)
+    sets = [sfa.cache_to_device(inp) for _ in range(max(1, min(args.sets, 2)))]
+    torch.cuda.synchronize()
+
+    def step(i):
+        sfa.run_cache_write(inp, sets[i % len(sets)])
+
+    n_warm = warm_up(step, args, torch)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    whole0, whole1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    whole0.record()
+    for i in range(args.steps):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    whole1.record()
+    torch.cuda.synchronize()
+    us_per_call = whole0.elapsed_time(whole1) / args.steps * 1e3
+    launch_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps
+    n_w = inp.n_written()
+    per_row = (1024 + 128 + 4 + 4) + (512 + 16 + 128 if dtype == "int8" else 1024 + 128)
+    nbytes = n_w * per_row
+    gbps = nbytes / (launch_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash(("cache_kernels.hip", "cache_internal.h"))
+    rec = {
+        "metric": f"us/call + GB/s vs HBM roofline, {args.workload}",
+        "value": round(us_per_call, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": n_warm,
+        "ms_per_step": round(us_per_call / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": inp.batch, "s1": inp.s1, "rows_written": n_w,
+                   "pool_rows": inp.num_cache_rows, "block_size": 128, "kv_lora_rank": 512, "rope_dim": 64,
+                   "quant_group": 128 if dtype == "int8" else None, "cold_sets": len(sets)},
+        "kernel_ms_mean": round(launch_ms, 5),
+        "algorithmic_bytes_per_call": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profile(src_hash, f"{args.workload}_traffic.txt")},
+        "kernel_source_sha256": src_hash,
+    }
+    if args.cpu_seconds > 0:
+        # the oracle over chunks of 4096 tokens (random chunk order) until the budget is spent,
+        # scaled to the whole call; each chunk's rows are compared with the GPU's cache
+        d = sets[(args.steps - 1) % len(sets)]
+        kn = d["key_nope"].cpu()
+        kn = kn.numpy() if dtype == "int8" else kn.view(torch.int16).numpy().view(np.uint16)
+        kr = d["key_rope"].cpu().view(torch.int16).numpy().view(np.uint16)
+        ks = None if d["k_nope_scales"] is None else d["k_nope_scales"].cpu().numpy()
+        T = inp.n_tokens
+        chunk = min(4096, T)
+        n_chunks = (T + chunk - 1) // chunk
+        order = np.random.default_rng(0).permutation(n_chunks)
+        t0 = time.perf_counter()
+        done_tok, bad = 0, 0
+        i = 0
+        while i == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            c = int(order[i % n_chunks])
+            t_lo, t_hi = c * chunk, min(T, (c + 1) * chunk)
+            b0 = t_lo // inp.s1
+            b1 = (t_hi - 1) // inp.s1 + 1
+            sub_pos = inp.positions[t_lo:t_hi]
+            # the chunk as its own call: its tokens and the block-table rows of their batches
+            # (a chunk holds whole batches, or lies inside one batch)
+            assert (t_lo % inp.s1 == 0 and (t_hi - t_lo) % inp.s1 == 0) or b1 - b0 == 1
+            rows = CO.target_rows(sub_pos, inp.block_table[b0:b1], inp.s1, inp.num_cache_rows)
+            sel = np.nonzero(rows >= 0)[0]
+            if dtype == "int8":
+                codes, scales = CO.quantize_groups(inp.new_nope[t_lo:t_hi][sel])
+                if i < n_chunks:
+                    bad += int(np.any(kn[rows[sel]] != codes, axis=1).sum())
+                    bad += int(np.any(ks[rows[sel]].view(np.uint32) != scales.view(np.uint32), axis=1).sum())
+            elif i < n_chunks:
+                bad += int(np.any(kn[rows[sel]] != inp.new_nope[t_lo:t_hi][sel], axis=1).sum())
+            if i < n_chunks:
+                bad += int(np.any(kr[rows[sel]] != inp.new_rope[t_lo:t_hi][sel], axis=1).sum())
+            done_tok += t_hi - t_lo
+            i += 1
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(el / done_tok * T * 1e6, 1), "unit": "us/call",
+                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "sample": f"{done_tok} tokens in chunks of {chunk} (random chunk order, seed 0) in "
+                               f"{el:.1f} s, scaled to one call of {T} tokens",
+                               "sample_rows_checked": min(done_tok, T), "sample_rows_bad": bad}
+    print(json.dumps(rec), flush=True)
+
+
 def copy_calibration(mib: int, steps: int):
     """A plain copy of a known size: it reads and writes exactly mib MiB per launch, so the HBM
     byte counters read on it give the factor that turns their readings into bytes."""
@@ -307,7 +422,8 @@ def main():
                     help="untimed calls before the timed region (default: at least 10 and at least "
                          "--warmup-seconds of calls, so the GPU clocks have left their idle state)")
     ap.add_argument("--warmup-seconds", type=float, default=0.5)
-    ap.add_argument("--workload", default="decode_b64_s2_bf16", choices=sorted(WORKLOADS) + ["indexer_b64_s2"])
+    ap.add_argument("--workload", default="decode_b64_s2_bf16",
+                    choices=sorted(WORKLOADS) + ["indexer_b64_s2"] + sorted(CACHE_WORKLOADS))
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated for a cold cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget (0 disables)")
     ap.add_argument("--seed", type=int, default=0)
@@ -329,6 +445,9 @@ def main():
 
     if args.workload == "indexer_b64_s2":
         bench_indexer(args)
+        return
+    if args.workload in CACHE_WORKLOADS:
+        bench_cache_write(args)
         return
 
     from mla_sparse_top_amd import sfa, workloads

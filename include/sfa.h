@@ -150,6 +150,44 @@ int sfa_prefill(const sfa_dims* dims,
 int sfa_resolve_rows(const sfa_dims* dims, const int32_t* topk_indices, const int32_t* block_table,
                      const int32_t* kv_act_seqs, int32_t* rows_out, hipStream_t stream);
 
+/*
+ * ---- Cache write: the step that fills the latent cache ----
+ *
+ * "DeepSeek V3/V2 Sparse Flash Attention with Quantization", sections "Algorithm overview"
+ * (PagedAttention) and "INT8 quantisation rule". New token t = b*s1 + s carries one latent row
+ * (512 nope + 64 rope, bf16) for logical position p = positions[t] of batch b; it is written at
+ * physical row block_table[b][p / 128] * 128 + p % 128 of the cache that sfa_decode and
+ * sfa_prefill read.
+ *   BF16 cache: nope and rope are copied bit for bit.
+ *   INT8 cache: rope is copied; each 128-element group of nope is quantised as
+ *     scale = absmax(group) / 127             (fp32, IEEE division, round to nearest even)
+ *     code  = clamp(round_half_even(x / scale), -128, 127)   (x / scale one fp32 division)
+ *   and an all-zero group stores scale 0 and codes 0. The attention's dequant chain then reads
+ *   code * scale rounded to bf16.
+ *
+ *   dims           batch, s1, kv_lora_rank (512), rope_dim (64), block_size (128),
+ *                  max_blocks_per_batch, num_cache_rows and kv_dtype are used; n_q, n_kv, topk
+ *                  and num_splits are ignored. T = batch * s1 may be up to 2^26.
+ *   new_nope       bf16  (T, 512)
+ *   new_rope       bf16  (T, 64)
+ *   positions      int32 (T)
+ *   block_table    int32 (batch, max_blocks_per_batch)
+ *   key_nope_2d    bf16 or int8 (num_cache_rows, 512)   written in place
+ *   key_rope_2d    bf16  (num_cache_rows, 64)           written in place
+ *   k_nope_scales  fp32  (num_cache_rows, 4)            written in place; INT8 only (NULL for bf16)
+ *
+ * A token is not written when p < 0, p >= max_blocks_per_batch * 128, its block_table entry is
+ * negative, or its row is outside [0, num_cache_rows). Rows no token targets are untouched.
+ * Preconditions, not checked: no two written tokens target the same row (which of them lands is
+ * otherwise unspecified); the nope values are finite. Errors: SFA_ERR_NULL, SFA_ERR_DIMS,
+ * SFA_ERR_SCALES (INT8 without scales), SFA_ERR_ALIGN (any pointer not 16-byte aligned),
+ * SFA_ERR_ALIAS (an output overlaps an input or another output), SFA_ERR_HIP. Asynchronous on
+ * `stream`, no allocation, like every entry point.
+ */
+int sfa_cache_write(const sfa_dims* dims, const void* new_nope, const void* new_rope, const int32_t* positions,
+                    const int32_t* block_table, void* key_nope_2d, void* key_rope_2d, float* k_nope_scales,
+                    hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char* sfa_status_string(int status);
 

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libsfa.so")
-SOURCES = ["sfa_kernels.hip", "sfa_host.cpp", "indexer_kernels.hip", "indexer_host.cpp"]
+SOURCES = ["sfa_kernels.hip", "sfa_host.cpp", "indexer_kernels.hip", "indexer_host.cpp", "cache_kernels.hip",
+           "cache_host.cpp"]
 
 
 def hipcc_path() -> str:

@@ -80,8 +80,11 @@ _lib.sfa_indexer_scores.restype = ctypes.c_int
 _lib.sfa_topk_select.argtypes = [ctypes.POINTER(SfaIndexerDims), _vp, _vp, _vp, _vp]
 _lib.sfa_topk_select.restype = ctypes.c_int
 
+_lib.sfa_cache_write.argtypes = [ctypes.POINTER(SfaDims), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.sfa_cache_write.restype = ctypes.c_int
+
 EXPORTED_SYMBOLS = ("sfa_workspace_size", "sfa_num_splits", "sfa_decode", "sfa_prefill", "sfa_resolve_rows",
-                    "sfa_status_string", "sfa_indexer_scores", "sfa_topk_select")
+                    "sfa_status_string", "sfa_indexer_scores", "sfa_topk_select", "sfa_cache_write")
 
 
 class SfaError(RuntimeError):
@@ -239,6 +242,40 @@ def resolve_rows(topk_indices, block_table, kv_act_seqs, *, batch, s1, num_cache
     return rows_out
 
 
+def cache_write(new_nope, new_rope, positions, block_table, key_nope, key_rope, k_nope_scales=None, *, batch, s1,
+                stream=None):
+    """sfa_cache_write: writes the new latent rows into the paged cache tensors in place (an int8
+    key_nope is quantised per 128-element group into it and k_nope_scales). Returns key_nope."""
+    dev = new_nope.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    t_tokens = batch * s1
+    rows = key_rope.shape[0]
+    _check(new_nope, "new_nope", (torch.bfloat16,), (t_tokens, KV_LORA_RANK), dev)
+    _check(new_rope, "new_rope", (torch.bfloat16,), (t_tokens, ROPE_DIM), dev)
+    _check(positions, "positions", (torch.int32,), (t_tokens,), dev)
+    _check(block_table, "block_table", (torch.int32,), None, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != batch:
+        raise ValueError("block_table must be (batch, max_blocks_per_batch)")
+    _check(key_nope, "key_nope", (torch.bfloat16, torch.int8), (rows, KV_LORA_RANK), dev)
+    _check(key_rope, "key_rope", (torch.bfloat16,), (rows, ROPE_DIM), dev)
+    int8 = key_nope.dtype == torch.int8
+    if int8:
+        if k_nope_scales is None:
+            raise ValueError("an int8 key_nope needs k_nope_scales")
+        _check(k_nope_scales, "k_nope_scales", (torch.float32,), (rows, 4), dev)
+    dims = make_dims(batch=batch, s1=s1, n_q=128, topk=1, max_blocks_per_batch=block_table.shape[1],
+                     num_cache_rows=rows, kv_dtype=KV_INT8 if int8 else KV_BF16)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = _lib.sfa_cache_write(ctypes.byref(dims), _ptr(new_nope), _ptr(new_rope), _ptr(positions), _ptr(block_table),
+                              _ptr(key_nope), _ptr(key_rope), _ptr(k_nope_scales if int8 else None),
+                              ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise SfaError(st, "sfa_cache_write")
+    return key_nope
+
+
 def to_device(inp, device="cuda"):
     """Upload a workloads.SfaInputs instance: bf16 bit patterns become torch.bfloat16 tensors."""
     import numpy as np
@@ -341,6 +378,30 @@ def indexer_to_device(inp, device="cuda"):
         "block_table": torch.from_numpy(inp.block_table).to(device),
         "kv_act_seqs": torch.from_numpy(inp.kv_act_seqs).to(device),
     }
+
+
+def cache_to_device(inp, device="cuda"):
+    """Upload a workloads.CacheWriteInputs instance (the cache tensors are fresh copies)."""
+    import numpy as np
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    return {
+        "new_nope": bf16(inp.new_nope),
+        "new_rope": bf16(inp.new_rope),
+        "positions": torch.from_numpy(inp.positions).to(device),
+        "block_table": torch.from_numpy(inp.block_table).to(device),
+        "key_nope": bf16(inp.key_nope) if inp.kv_dtype == "bf16" else torch.from_numpy(inp.key_nope).to(device),
+        "key_rope": bf16(inp.key_rope),
+        "k_nope_scales": None if inp.k_nope_scales is None else torch.from_numpy(inp.k_nope_scales).to(device),
+    }
+
+
+def run_cache_write(inp, d):
+    """sfa_cache_write on an uploaded CacheWriteInputs instance (writes d's cache tensors)."""
+    return cache_write(d["new_nope"], d["new_rope"], d["positions"], d["block_table"], d["key_nope"], d["key_rope"],
+                       d["k_nope_scales"], batch=inp.batch, s1=inp.s1)
 
 
 def run_indexer(inp, dev_tensors=None):

@@ -4,9 +4,10 @@ This module only draws random inputs and lays them out the way the operation con
 ("DeepSeek V3/V2 Sparse Flash Attention with Quantization", input/output table: query_nope,
 query_rope, key_nope_2d, key_rope_2d, k_nope_scales, topk_indices, block_table, kv_act_seqs).
 It contains no attention arithmetic. Its one transformation is the INT8 quantisation of the
-cache's nope part, one FP32 scale per 128-element group. That is the cache *write* side: the
-same page's "INT8 quantisation rule" note says the scale comes from the group's absolute
-maximum and the codes span [-128, 127].
+cache's nope part, one FP32 scale per 128-element group, which gives the INT8 attention
+workloads their inputs (the same page's "INT8 quantisation rule": the scale comes from the
+group's absolute maximum and the codes span [-128, 127]). The cache-write kernel is checked
+against its own oracle (oracle/cache_oracle.py), never against this module.
 
 All floating data are returned as raw bit patterns (bf16 as uint16), so the GPU path and the
 CPU oracle consume identical bytes.
@@ -398,3 +399,106 @@ def indexer_decode(seed: int = 0) -> IndexerInputs:
     4096-block pool, 64 index heads of 128 dims, top-k 2048."""
     return indexer_generate(batch=64, s1=2, act_seqs=[8192] * 64, topk=2048, seed=seed,
                             name="indexer_b64_s2_h64_d128_kv8192_topk2048")
+
+
+# ----------------------------------------------------------------------------------------
+# Cache-write inputs ("DeepSeek V3/V2 Sparse Flash Attention with Quantization", sections
+# "Algorithm overview" and "INT8 quantisation rule"): new latent rows for each new token, the
+# logical position each one takes, a block table, and the existing cache they are written into.
+# Only random draws and layout here; the existing INT8 cache holds random codes and scales.
+# ----------------------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class CacheWriteInputs:
+    """Shapes (T = batch * s1, R = cache rows):
+      new_nope     uint16 (T, 512)  bf16 bits
+      new_rope     uint16 (T, 64)   bf16 bits
+      positions    int32 (T,)       logical position of token t in batch t // s1 (-1: not written)
+      block_table  int32 (batch, max_blocks_per_batch)
+      key_nope     uint16 (R, 512) bf16 bits, or int8 (R, 512)
+      key_rope     uint16 (R, 64)
+      k_nope_scales float32 (R, 4) or None
+    """
+
+    batch: int
+    s1: int
+    kv_dtype: str
+    new_nope: np.ndarray
+    new_rope: np.ndarray
+    positions: np.ndarray
+    block_table: np.ndarray
+    key_nope: np.ndarray
+    key_rope: np.ndarray
+    k_nope_scales: Optional[np.ndarray]
+    name: str = ""
+
+    @property
+    def n_tokens(self) -> int:
+        return self.batch * self.s1
+
+    @property
+    def num_cache_rows(self) -> int:
+        return int(self.key_rope.shape[0])
+
+    def n_written(self) -> int:
+        p = self.positions.astype(np.int64)
+        mb = self.block_table.shape[1]
+        b = np.arange(self.n_tokens) // self.s1
+        ok = (p >= 0) & (p < mb * BLOCK_SIZE)
+        blk = np.where(ok, self.block_table[b, np.where(ok, p, 0) // BLOCK_SIZE], -1).astype(np.int64)
+        ok &= (blk >= 0) & (blk * BLOCK_SIZE + np.where(ok, p, 0) % BLOCK_SIZE < self.num_cache_rows)
+        return int(ok.sum())
+
+
+def cache_write_generate(*, batch: int, s1: int, n_pool_blocks: int, max_blocks_per_batch: int,
+                         kv_dtype: str = "int8", seed: int = 0, positions: Optional[np.ndarray] = None,
+                         block_table: Optional[np.ndarray] = None, value_scale: float = 1.0,
+                         name: str = "") -> CacheWriteInputs:
+    """New rows are N(0,1) * value_scale rounded to bf16. Unless given, the block table is a
+    random permutation of the pool's blocks (it needs n_pool_blocks >= batch * mb) and each
+    batch's s1 tokens take distinct random positions in [0, mb * 128). The existing cache is
+    random bytes (bf16: random bit patterns; INT8: random codes, scales uniform in [0, 1))."""
+    g = torch.Generator().manual_seed(70_000 + int(seed))
+    mb = int(max_blocks_per_batch)
+    if block_table is None:
+        assert n_pool_blocks >= batch * mb
+        block_table = torch.randperm(n_pool_blocks, generator=g)[: batch * mb].view(batch, mb).numpy()
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    if positions is None:
+        positions = np.concatenate([torch.randperm(mb * BLOCK_SIZE, generator=g)[:s1].numpy()
+                                    for _ in range(batch)]) if batch * s1 else np.zeros(0)
+    positions = np.ascontiguousarray(positions, dtype=np.int32)
+    t = batch * s1
+    nn = np.empty((t, KV_LORA_RANK), dtype=np.uint16)
+    for r0 in range(0, t, _ROW_CHUNK):
+        r1 = min(t, r0 + _ROW_CHUNK)
+        nn[r0:r1] = _bf16_bits(torch.randn(r1 - r0, KV_LORA_RANK, generator=g) * float(value_scale))
+    nr = _normal_bf16(g, t, ROPE_DIM)
+    rows = n_pool_blocks * BLOCK_SIZE
+    kr = torch.randint(0, 1 << 16, (rows, ROPE_DIM), generator=g, dtype=torch.int32).numpy().astype(np.uint16)
+    if kv_dtype == "int8":
+        kn = torch.randint(-128, 128, (rows, KV_LORA_RANK), generator=g, dtype=torch.int8).numpy()
+        ks = torch.rand(rows, N_GROUPS, generator=g).numpy()
+    else:
+        kn = torch.randint(0, 1 << 16, (rows, KV_LORA_RANK), generator=g, dtype=torch.int32).numpy().astype(np.uint16)
+        ks = None
+    return CacheWriteInputs(batch=batch, s1=s1, kv_dtype=kv_dtype, new_nope=nn, new_rope=nr, positions=positions,
+                            block_table=block_table, key_nope=kn, key_rope=kr, k_nope_scales=ks, name=name)
+
+
+def cache_fill(seed: int = 0, kv_dtype: str = "int8") -> CacheWriteInputs:
+    """Every position of the decode workload's cache written at once (a prefill of 64 sequences
+    of 8192 tokens): B=64, S1=8192, positions 0..8191 in order, the block table a random
+    permutation of a 4096-block pool (524,288 rows)."""
+    pos = np.tile(np.arange(8192, dtype=np.int32), 64)
+    return cache_write_generate(batch=64, s1=8192, n_pool_blocks=4096, max_blocks_per_batch=64, kv_dtype=kv_dtype,
+                                seed=seed, positions=pos, name=f"cache_write_b64_s8192_{kv_dtype}")
+
+
+def cache_decode_step(seed: int = 0, kv_dtype: str = "int8") -> CacheWriteInputs:
+    """The decode step's write: B=64 sequences, S1=2 new tokens at positions 8190 and 8191, into
+    the decode workload's 4096-block pool."""
+    pos = np.tile(np.array([8190, 8191], dtype=np.int32), 64)
+    return cache_write_generate(batch=64, s1=2, n_pool_blocks=4096, max_blocks_per_batch=64, kv_dtype=kv_dtype,
+                                seed=seed, positions=pos, name=f"cache_write_b64_s2_{kv_dtype}")

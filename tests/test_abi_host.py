@@ -200,3 +200,38 @@ def test_indexer_validation_errors():
     assert _iselect(d, out=0x40000000 + 64) == -6        # indices overlapping the scores
     empty = _idims(batch=0)
     assert _iscores(empty) == 0 and _iselect(empty) == 0
+
+
+def _cw(dims, **kw):
+    p = dict(nn=0x100000, nr=0x200000, pos=0x300000, bt=0x400000, kn=0x10000000, kr=0x20000000, sc=0x30000000)
+    p.update(kw)
+    vp = lambda v: None if v is None else ctypes.c_void_p(v)  # noqa: E731
+    return sfa._lib.sfa_cache_write(ctypes.byref(dims), vp(p["nn"]), vp(p["nr"]), vp(p["pos"]), vp(p["bt"]),
+                                    vp(p["kn"]), vp(p["kr"]), vp(p["sc"]), None)
+
+
+def test_cache_write_validation():
+    cw = dict(batch=2, s1=2, n_q=16, topk=1, max_blocks_per_batch=2, num_cache_rows=512)
+    d = _dims(**cw)
+    d8 = _dims(**{**cw, "kv_dtype": 1})
+    assert _cw(d, nn=None) == -1
+    assert _cw(d, kr=None) == -1
+    assert _cw(d8, sc=None) == -5                        # INT8 cache without scales
+    assert _cw(d, pos=0x300004) == -3                    # misaligned
+    assert _cw(d8, sc=0x30000008) == -3
+    assert _cw(d, kn=0x100000 + 1024) == -6              # cache overlaps new_nope
+    assert _cw(d8, sc=0x10000000 + 4096) == -6           # scales inside key_nope
+    assert _cw(d, kr=0x10000000 + 16) == -6              # rope inside nope
+    bad = _dims(**cw)
+    bad.block_size = 64
+    assert _cw(bad) == -2
+    bad = _dims(**cw)
+    bad.kv_dtype = 7
+    assert _cw(bad) == -2
+    # n_q, topk and num_splits are not the write's business: odd values are accepted
+    odd = _dims(**cw)
+    odd.n_q, odd.topk, odd.n_kv = 3, 0, 5
+    assert _cw(odd, **{"nn": None}) == -1                # still validated up to the pointers
+    # nothing to write: no HIP call
+    assert _cw(_dims(**{**cw, "batch": 0})) == 0
+    assert _cw(_dims(**{**cw, "num_cache_rows": 0})) == 0
