@@ -156,9 +156,11 @@ def _check(t: torch.Tensor, name: str, dtypes, shape=None, device=None):
         raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
 
 
-def _attention(fn_name: str, query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices,
-               block_table, kv_act_seqs, softmax_scale, *, batch, s1, out=None, workspace=None,
-               num_splits_override=0, stream=None):
+def _marshal_attention(fn_name: str, query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices,
+                       block_table, kv_act_seqs, softmax_scale, *, batch, s1, out=None, workspace=None,
+                       num_splits_override=0, stream=None):
+    """Checks the tensors and builds the C argument tuple of sfa_decode / sfa_prefill.
+    Returns (args, out, keepalive)."""
     dev = query_nope.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on a GPU device")
@@ -192,15 +194,42 @@ def _attention(fn_name: str, query_nope, query_rope, key_nope, key_rope, k_nope_
         _check(workspace, "workspace", (torch.uint8,), None, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    st = getattr(_lib, fn_name)(
-        ctypes.byref(dims), _ptr(query_nope), _ptr(query_rope), _ptr(key_nope), _ptr(key_rope),
-        _ptr(k_nope_scales if int8 else None), _ptr(topk_indices), _ptr(block_table), _ptr(kv_act_seqs),
-        ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace) if need else None,
-        ctypes.c_size_t(workspace.numel() if (need and workspace is not None) else 0),
-        ctypes.c_void_p(stream.cuda_stream))
+    args = (ctypes.byref(dims), _ptr(query_nope), _ptr(query_rope), _ptr(key_nope), _ptr(key_rope),
+            _ptr(k_nope_scales if int8 else None), _ptr(topk_indices), _ptr(block_table), _ptr(kv_act_seqs),
+            ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace) if need else None,
+            ctypes.c_size_t(workspace.numel() if (need and workspace is not None) else 0),
+            ctypes.c_void_p(stream.cuda_stream))
+    keep = (dims, query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices, block_table, kv_act_seqs,
+            out, workspace, stream)
+    return args, out, keep
+
+
+def _attention(fn_name: str, *tensors, **kw):
+    args, out, _keep = _marshal_attention(fn_name, *tensors, **kw)
+    st = getattr(_lib, fn_name)(*args)
     if st != 0:
         raise SfaError(st, fn_name)
     return out
+
+
+class PreparedCall:
+    """One entry point bound to fixed tensors, for loops that repeat the same call (a serving
+    step, a benchmark). The Python checks and the argument marshalling run once, here; each
+    call only invokes the C function, which still validates its arguments on the host and
+    queues the kernels on the bound stream. The tensors are kept alive by this object; their
+    contents may change between calls, their storage must not."""
+
+    def __init__(self, calls, out, keep):
+        self._calls = calls  # [(c function, args, name)]
+        self.out = out
+        self._keep = keep
+
+    def __call__(self):
+        for fn, args, name in self._calls:
+            st = fn(*args)
+            if st != 0:
+                raise SfaError(st, name)
+        return self.out
 
 
 def decode(query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices, block_table, kv_act_seqs,
@@ -217,6 +246,18 @@ def prefill(query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indi
     return _attention("sfa_prefill", query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices,
                       block_table, kv_act_seqs, softmax_scale, batch=batch, s1=s1, out=out, workspace=workspace,
                       num_splits_override=num_splits, stream=stream)
+
+
+def prepare_decode(query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices, block_table,
+                   kv_act_seqs, softmax_scale, *, batch, s1, out=None, workspace=None, num_splits=0, stream=None,
+                   prefill_mode=False) -> PreparedCall:
+    """sfa_decode (or sfa_prefill) bound to these tensors: returns a PreparedCall whose call queues
+    the attention and returns out."""
+    name = "sfa_prefill" if prefill_mode else "sfa_decode"
+    args, out, keep = _marshal_attention(name, query_nope, query_rope, key_nope, key_rope, k_nope_scales,
+                                         topk_indices, block_table, kv_act_seqs, softmax_scale, batch=batch, s1=s1,
+                                         out=out, workspace=workspace, num_splits_override=num_splits, stream=stream)
+    return PreparedCall([(getattr(_lib, name), args, name)], out, keep)
 
 
 def resolve_rows(topk_indices, block_table, kv_act_seqs, *, batch, s1, num_cache_rows, rows_out=None,
@@ -242,10 +283,8 @@ def resolve_rows(topk_indices, block_table, kv_act_seqs, *, batch, s1, num_cache
     return rows_out
 
 
-def cache_write(new_nope, new_rope, positions, block_table, key_nope, key_rope, k_nope_scales=None, *, batch, s1,
-                stream=None):
-    """sfa_cache_write: writes the new latent rows into the paged cache tensors in place (an int8
-    key_nope is quantised per 128-element group into it and k_nope_scales). Returns key_nope."""
+def _marshal_cache_write(new_nope, new_rope, positions, block_table, key_nope, key_rope, k_nope_scales, *, batch,
+                        s1, stream=None):
     dev = new_nope.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on a GPU device")
@@ -268,9 +307,18 @@ def cache_write(new_nope, new_rope, positions, block_table, key_nope, key_rope, 
                      num_cache_rows=rows, kv_dtype=KV_INT8 if int8 else KV_BF16)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    st = _lib.sfa_cache_write(ctypes.byref(dims), _ptr(new_nope), _ptr(new_rope), _ptr(positions), _ptr(block_table),
-                              _ptr(key_nope), _ptr(key_rope), _ptr(k_nope_scales if int8 else None),
-                              ctypes.c_void_p(stream.cuda_stream))
+    args = (ctypes.byref(dims), _ptr(new_nope), _ptr(new_rope), _ptr(positions), _ptr(block_table), _ptr(key_nope),
+            _ptr(key_rope), _ptr(k_nope_scales if int8 else None), ctypes.c_void_p(stream.cuda_stream))
+    return args, (dims, new_nope, new_rope, positions, block_table, key_nope, key_rope, k_nope_scales, stream)
+
+
+def cache_write(new_nope, new_rope, positions, block_table, key_nope, key_rope, k_nope_scales=None, *, batch, s1,
+                stream=None):
+    """sfa_cache_write: writes the new latent rows into the paged cache tensors in place (an int8
+    key_nope is quantised per 128-element group into it and k_nope_scales). Returns key_nope."""
+    args, _keep = _marshal_cache_write(new_nope, new_rope, positions, block_table, key_nope, key_rope, k_nope_scales,
+                                       batch=batch, s1=s1, stream=stream)
+    st = _lib.sfa_cache_write(*args)
     if st != 0:
         raise SfaError(st, "sfa_cache_write")
     return key_nope
@@ -296,6 +344,14 @@ def to_device(inp, device="cuda"):
     }
 
 
+def prepare_run(inp, dev_tensors, *, prefill_mode=False, num_splits=0, out=None) -> PreparedCall:
+    """prepare_decode on an uploaded instance."""
+    d = dev_tensors
+    return prepare_decode(d["query_nope"], d["query_rope"], d["key_nope"], d["key_rope"], d["k_nope_scales"],
+                          d["topk_indices"], d["block_table"], d["kv_act_seqs"], inp.softmax_scale, batch=inp.batch,
+                          s1=inp.s1, num_splits=num_splits, out=out, prefill_mode=prefill_mode)
+
+
 def run(inp, dev_tensors=None, *, prefill_mode=False, num_splits=0, out=None):
     """Run decode (or prefill) on an uploaded instance; returns the bf16 output tensor."""
     d = dev_tensors if dev_tensors is not None else to_device(inp)
@@ -316,9 +372,8 @@ def make_indexer_dims(*, batch: int, s1: int, max_blocks_per_batch: int, num_cac
     return SfaIndexerDims(batch, s1, n_heads, head_dim, block_size, max_blocks_per_batch, num_cache_rows, topk)
 
 
-def indexer_scores(q_index, k_index_cache, weights, block_table, kv_act_seqs, *, batch, s1, topk=1,
-                   scores=None, stream=None):
-    """sfa_indexer_scores: returns scores (batch*s1, max_blocks_per_batch*128) fp32."""
+def _marshal_indexer_scores(q_index, k_index_cache, weights, block_table, kv_act_seqs, *, batch, s1, topk=1,
+                            scores=None, stream=None):
     dev = q_index.device
     t_tokens = batch * s1
     rows = k_index_cache.shape[0]
@@ -334,15 +389,12 @@ def indexer_scores(q_index, k_index_cache, weights, block_table, kv_act_seqs, *,
     _check(scores, "scores", (torch.float32,), (t_tokens, mb * BLOCK_SIZE), dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    st = _lib.sfa_indexer_scores(ctypes.byref(dims), _ptr(q_index), _ptr(k_index_cache), _ptr(weights),
-                                 _ptr(block_table), _ptr(kv_act_seqs), _ptr(scores), ctypes.c_void_p(stream.cuda_stream))
-    if st != 0:
-        raise SfaError(st, "sfa_indexer_scores")
-    return scores
+    args = (ctypes.byref(dims), _ptr(q_index), _ptr(k_index_cache), _ptr(weights), _ptr(block_table),
+            _ptr(kv_act_seqs), _ptr(scores), ctypes.c_void_p(stream.cuda_stream))
+    return args, scores, (dims, q_index, k_index_cache, weights, block_table, kv_act_seqs, scores, stream)
 
 
-def topk_select(scores, kv_act_seqs, *, batch, s1, topk, out=None, stream=None):
-    """sfa_topk_select: returns topk_indices (batch*s1, topk) int32 (unsorted, -1 padded)."""
+def _marshal_topk_select(scores, kv_act_seqs, *, batch, s1, topk, out=None, stream=None):
     dev = scores.device
     t_tokens = batch * s1
     n_pos = scores.shape[1]
@@ -357,11 +409,54 @@ def topk_select(scores, kv_act_seqs, *, batch, s1, topk, out=None, stream=None):
     _check(out, "topk_indices", (torch.int32,), (t_tokens, topk), dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    st = _lib.sfa_topk_select(ctypes.byref(dims), _ptr(scores), _ptr(kv_act_seqs), _ptr(out),
-                              ctypes.c_void_p(stream.cuda_stream))
+    args = (ctypes.byref(dims), _ptr(scores), _ptr(kv_act_seqs), _ptr(out), ctypes.c_void_p(stream.cuda_stream))
+    return args, out, (dims, scores, kv_act_seqs, out, stream)
+
+
+def indexer_scores(q_index, k_index_cache, weights, block_table, kv_act_seqs, *, batch, s1, topk=1,
+                   scores=None, stream=None):
+    """sfa_indexer_scores: returns scores (batch*s1, max_blocks_per_batch*128) fp32."""
+    args, scores, _keep = _marshal_indexer_scores(q_index, k_index_cache, weights, block_table, kv_act_seqs,
+                                                  batch=batch, s1=s1, topk=topk, scores=scores, stream=stream)
+    st = _lib.sfa_indexer_scores(*args)
+    if st != 0:
+        raise SfaError(st, "sfa_indexer_scores")
+    return scores
+
+
+def topk_select(scores, kv_act_seqs, *, batch, s1, topk, out=None, stream=None):
+    """sfa_topk_select: returns topk_indices (batch*s1, topk) int32 (unsorted, -1 padded)."""
+    args, out, _keep = _marshal_topk_select(scores, kv_act_seqs, batch=batch, s1=s1, topk=topk, out=out,
+                                            stream=stream)
+    st = _lib.sfa_topk_select(*args)
     if st != 0:
         raise SfaError(st, "sfa_topk_select")
     return out
+
+
+def prepare_indexer_scores(q_index, k_index_cache, weights, block_table, kv_act_seqs, *, batch, s1, topk=1,
+                           scores=None, stream=None) -> PreparedCall:
+    """sfa_indexer_scores bound to these tensors (a PreparedCall returning the scores)."""
+    args, scores, keep = _marshal_indexer_scores(q_index, k_index_cache, weights, block_table, kv_act_seqs,
+                                                 batch=batch, s1=s1, topk=topk, scores=scores, stream=stream)
+    return PreparedCall([(_lib.sfa_indexer_scores, args, "sfa_indexer_scores")], scores, keep)
+
+
+def prepare_topk_select(scores, kv_act_seqs, *, batch, s1, topk, out=None, stream=None) -> PreparedCall:
+    """sfa_topk_select bound to these tensors (a PreparedCall returning topk_indices)."""
+    args, out, keep = _marshal_topk_select(scores, kv_act_seqs, batch=batch, s1=s1, topk=topk, out=out,
+                                           stream=stream)
+    return PreparedCall([(_lib.sfa_topk_select, args, "sfa_topk_select")], out, keep)
+
+
+def prepare_indexer(q_index, k_index_cache, weights, block_table, kv_act_seqs, *, batch, s1, topk, scores=None,
+                    out=None, stream=None) -> PreparedCall:
+    """sfa_indexer_scores then sfa_topk_select bound to these tensors: a PreparedCall that queues
+    both and returns topk_indices."""
+    sc = prepare_indexer_scores(q_index, k_index_cache, weights, block_table, kv_act_seqs, batch=batch, s1=s1,
+                                topk=topk, scores=scores, stream=stream)
+    sel = prepare_topk_select(sc.out, kv_act_seqs, batch=batch, s1=s1, topk=topk, out=out, stream=stream)
+    return PreparedCall(sc._calls + sel._calls, sel.out, (sc, sel))
 
 
 def indexer_to_device(inp, device="cuda"):
@@ -396,6 +491,14 @@ def cache_to_device(inp, device="cuda"):
         "key_rope": bf16(inp.key_rope),
         "k_nope_scales": None if inp.k_nope_scales is None else torch.from_numpy(inp.k_nope_scales).to(device),
     }
+
+
+def prepare_cache_write(new_nope, new_rope, positions, block_table, key_nope, key_rope, k_nope_scales=None, *,
+                        batch, s1, stream=None) -> PreparedCall:
+    """sfa_cache_write bound to these tensors (a PreparedCall returning key_nope)."""
+    args, keep = _marshal_cache_write(new_nope, new_rope, positions, block_table, key_nope, key_rope, k_nope_scales,
+                                      batch=batch, s1=s1, stream=stream)
+    return PreparedCall([(_lib.sfa_cache_write, args, "sfa_cache_write")], key_nope, keep)
 
 
 def run_cache_write(inp, d):
