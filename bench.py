@@ -92,6 +92,25 @@ def traffic_from_profile(kernel_src_hash: str, name: str = "sfa_decode_b64_s2_bf
     return float(m_bytes.group(1))
 
 
+def mfma_from_profile(kernel_src_hash: str, workload: str):
+    """MFMA counters of the attention kernel on `workload` from the committed rocprofv3 summary
+    profiles/sfa_attention_mfma_utilisation.txt, if it was taken on the same kernel source."""
+    path = os.path.join(ROOT, "profiles", "sfa_attention_mfma_utilisation.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
+    if not m_hash or m_hash.group(1) != kernel_src_hash:
+        return None
+    out = {}
+    for key in ("mfma_flop_per_launch", "mfma_busy_fraction"):
+        m = re.search(re.escape(f"{workload}.{key}") + r":\s*([0-9.eE+]+)", txt)
+        if not m:
+            return None
+        out[key] = float(m.group(1))
+    return out
+
+
 def kernel_source_hash(names=("sfa_kernels.hip", "sfa_internal.h")) -> str:
     import hashlib
 
@@ -556,8 +575,17 @@ def main():
         "roofline": roofline,
         "rotated_outputs_identical": bool(same),
         "wall_s_timed": round(wall, 3),
+        "mfma": None,
         "kernel_source_sha256": src_hash,
     }
+    mf = mfma_from_profile(src_hash, args.workload)
+    if mf is not None:
+        # MFMA unit busy fraction (rocprofv3 counters) and the issued MFMA rate (hi/lo split of P
+        # included) against the dense bf16 peak, at this run's kernel time
+        issued = mf["mfma_flop_per_launch"] / (mean_launch_ms * 1e-3) / 1e12
+        rec["mfma"] = {"busy_fraction": mf["mfma_busy_fraction"], "issued_tflops": round(issued, 1),
+                       "issued_frac_of_peak": round(issued / BF16_PEAK_TFLOPS, 4),
+                       "source": "profiles/sfa_attention_mfma_utilisation.txt"}
     if args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(inp, outs[(args.steps - 1) % len(sets)], args.cpu_seconds)
     print(json.dumps(rec), flush=True)
