@@ -826,7 +826,10 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     off_free = o;
   };
 
-  // ---- prologue: tiles 0 and 1 in LDS, tile 2 on its way, S^T(0) exchanged
+  // ---- prologue: tiles 0 and 1 in LDS, tile 2 on its way, S^T(0) exchanged.
+  // DMA instructions per tile and wave on the bf16 path: 8 nope rows (one each) and one for the
+  // wave's 8 rope rows, on both the buffer-resource and the 64-bit path.
+  constexpr int kDmaPerTile = 9;
   if (ntiles > 0) {
     if constexpr (kInt8) {
       // one register buffer: each tile's nope is written to LDS before the next is loaded
@@ -837,16 +840,31 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
         finish_tile(kStageBytes);
       }
     } else {
+      // Tiles 0, 1 and 2 are fetched together, and S^T(0) waits for tile 0 alone: a wave issues
+      // kDmaPerTile DMA instructions per tile, and vector-memory loads complete in issue order.
       start_tile(0, 0);
       if (ntiles > 1) start_tile(1, kStageBytes);
-      wait_vmcnt<0>();
+      if (ntiles > 2) start_tile(2, 2 * kStageBytes);
+      if (ntiles > 2)
+        wait_vmcnt<2 * kDmaPerTile>();
+      else if (ntiles > 1)
+        wait_vmcnt<kDmaPerTile>();
+      else
+        wait_vmcnt<0>();
     }
-    if (ntiles > 2) start_tile(2, 2 * kStageBytes);
+    if (kInt8 && ntiles > 2) start_tile(2, 2 * kStageBytes);
     lds_barrier();
     if (pair_active) {
       qk_tile(0, s_own);
       mfma_qk_drain(s_own);
       x_write(0, s_own);
+    }
+    // tile 1 must be in LDS for the first interval's S^T; tile 2 may still be on its way
+    if constexpr (!kInt8) {
+      if (ntiles > 2)
+        wait_vmcnt<kDmaPerTile>();
+      else
+        wait_vmcnt<0>();
     }
     lds_barrier();
     for (int ti = 0; ti < ntiles; ++ti) interval(ti);
