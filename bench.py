@@ -447,6 +447,42 @@ def copy_calibration(mib: int, steps: int):
           flush=True)
 
 
+def mfma_probe(workgroups: int = 512, iters: int = 20000):
+    """Dense bf16 MFMA throughput this GPU sustains on v_mfma_f32_32x32x16_bf16 (the attention
+    kernel's instruction): libsfa_probe.so keeps four independent accumulator chains per wave,
+    two waves per SIMD. Context for the published 2.5 PFLOP/s peak, not the attention path."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "mla_sparse_top_amd", "libsfa_probe.so"))
+    lib.sfa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sfa_probe_mfma.restype = ctypes.c_int
+    out = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch(n):
+        st = lib.sfa_probe_mfma(workgroups, n, ctypes.c_void_p(out.data_ptr()), stream)
+        if st != 0:
+            raise RuntimeError(f"sfa_probe_mfma failed: {st}")
+
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < 0.5:  # raise the clocks
+        launch(iters)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    launch(iters)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flop = workgroups * 4 * iters * 4 * 32768
+    tflops = flop / (ms * 1e-3) / 1e12
+    print(json.dumps({"mfma_probe": "v_mfma_f32_32x32x16_bf16", "workgroups": workgroups, "iters": iters,
+                      "ms": round(ms, 4), "tflops": round(tflops, 1),
+                      "frac_of_published_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,6 +496,8 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated for a cold cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget (0 disables)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="measure the dense bf16 MFMA throughput (libsfa_probe.so) and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the attention bench, run --steps plain device copies of this many MiB "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -472,6 +510,9 @@ def main():
 
     import torch
 
+    if args.mfma_probe:
+        mfma_probe()
+        return
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib, args.steps)
         return

@@ -18,6 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libsfa.so")
+# measurement context only (an MFMA throughput probe), kept out of the attention library
+PROBE_LIB_PATH = os.path.join(PKG, "libsfa_probe.so")
+PROBE_SOURCES = ["probe_mfma.hip"]
 SOURCES = ["sfa_kernels.hip", "sfa_host.cpp", "indexer_kernels.hip", "indexer_host.cpp", "cache_kernels.hip",
            "cache_host.cpp"]
 
@@ -29,7 +32,8 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm under /opt/rocm)")
 
 
-def build_command(out_path: str) -> list:
+def build_command(out_path: str, sources=None) -> list:
+    sources = SOURCES if sources is None else sources
     return [
         hipcc_path(),
         "--offload-arch=gfx950",
@@ -42,14 +46,14 @@ def build_command(out_path: str) -> list:
         "-Wno-unused-command-line-argument",
         "-I", INCLUDE,
         "-I", CSRC,
-        *[os.path.join(CSRC, s) for s in SOURCES],
+        *[os.path.join(CSRC, s) for s in sources],
         "-o", out_path,
     ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = build_command(tmp)
+def _build_one(lib_path: str, sources, verbose: bool) -> str:
+    tmp = lib_path + ".tmp"
+    cmd = build_command(tmp, sources)
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True)
@@ -59,8 +63,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build(verbose: bool = False) -> str:
+    """Builds libsfa.so (the attention, indexer and cache-write kernels behind the C ABI) and
+    libsfa_probe.so (the MFMA throughput probe used for measurement context)."""
+    _build_one(PROBE_LIB_PATH, PROBE_SOURCES, verbose)
+    return _build_one(LIB_PATH, SOURCES, verbose)
 
 
 if __name__ == "__main__":

@@ -235,3 +235,16 @@ def test_cache_write_validation():
     # nothing to write: no HIP call
     assert _cw(_dims(**{**cw, "batch": 0})) == 0
     assert _cw(_dims(**{**cw, "num_cache_rows": 0})) == 0
+
+
+def test_probe_library_is_separate_and_exports_its_entry():
+    """The MFMA throughput probe is measurement context: its own library, not in libsfa.so."""
+    from mla_sparse_top_amd import build as B
+
+    assert os.path.exists(B.PROBE_LIB_PATH)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.PROBE_LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert "sfa_probe_mfma" in out
+    main = subprocess.run(["nm", "-D", "--defined-only", sfa.lib_path()], capture_output=True, text=True,
+                          check=True).stdout
+    assert "sfa_probe_mfma" not in main
