@@ -112,11 +112,16 @@ def mfma_from_profile(kernel_src_hash: str, workload: str):
 
 
 def kernel_source_hash(names=("sfa_kernels.hip", "sfa_internal.h")) -> str:
+    """sha256 of the kernel sources with their comments removed, so that a profile stays tied to
+    the code it measured across edits of comments only."""
     import hashlib
 
     h = hashlib.sha256()
     for name in names:
-        h.update(open(os.path.join(ROOT, "mla_sparse_top_amd", "csrc", name), "rb").read())
+        text = open(os.path.join(ROOT, "mla_sparse_top_amd", "csrc", name)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(text.encode())
     return h.hexdigest()
 
 

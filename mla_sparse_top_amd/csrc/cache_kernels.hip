@@ -50,8 +50,8 @@ __global__ void __launch_bounds__(kCwWaves * 64) cache_write_kernel(const CacheW
   const int wave = threadIdx.x >> 6;
   const int t0 = (blockIdx.x * kCwWaves + wave) * kCwRowsPerWave;
 
-  // ---- lane i < 8 resolves token t0 + i: its position is loaded first; the new rows, which do
-  // not depend on where they go, are loaded next; then the block-table entry. Vector loads
+  // ---- lane i < kCwRowsPerWave resolves token t0 + i: its position is loaded first; the new
+  // rows, which do not depend on where they go, are loaded next; then the block-table entry. Vector loads
   // complete in issue order, so the block-table read waits only for the position, and its round
   // trip overlaps the row reads.
   static_assert(kCwRowsPerWave <= 64 && (kCwRowsPerWave & (kCwRowsPerWave - 1)) == 0, "one lane per token of the wave");
