@@ -39,6 +39,7 @@ BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA, published (2.5 PFLOP/s
 METRIC = "µs/call + gathered-KV GB/s & TFLOP/s vs roofline, B=64 S1=2 topk=2048 decode"
 
 WORKLOADS = {
+    "tiny_b1_s1_bf16": ("tiny", "bf16", False),
     "decode_b64_s2_bf16": ("decode_mtp1", "bf16", False),
     "decode_b64_s2_int8": ("decode_mtp1_int8", "int8", False),
     "varlen_b32_s1_bf16": ("varlen_decode", "bf16", False),
