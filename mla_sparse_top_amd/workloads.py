@@ -502,3 +502,133 @@ def cache_decode_step(seed: int = 0, kv_dtype: str = "int8") -> CacheWriteInputs
     pos = np.tile(np.array([8190, 8191], dtype=np.int32), 64)
     return cache_write_generate(batch=64, s1=2, n_pool_blocks=4096, max_blocks_per_batch=64, kv_dtype=kv_dtype,
                                 seed=seed, positions=pos, name=f"cache_write_b64_s2_{kv_dtype}")
+
+
+# ----------------------------------------------------------------------------------------
+# Sliding-window + compressed-cache attention inputs ("NPU DeepSeek-V4 model PyPTO fused-operator
+# optimisation", section "FA-class operators: SWA, CFA and SCFA"): per sequence an original
+# cache (ori_kv, a window of it is read) and a compressed cache (cmp_kv, compress_ratio times
+# shorter), both as rows of one paged pool with their own block tables.
+# ----------------------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class WindowInputs:
+    """Shapes (T = batch * s1):
+      query_nope/query_rope  uint16 (T*n_q, 512/64)     bf16 bits
+      key_nope/key_rope      the shared pool, as in SfaInputs (k_nope_scales for int8)
+      cmp_indices            int32 (T, topk_cmp) or None  compressed-entry indices, -1 padded
+      block_table_ori/_cmp   int32 (batch, mb_ori/mb_cmp)
+      ori_len, cmp_len       int32 (batch,)
+    """
+
+    batch: int
+    s1: int
+    n_q: int
+    window: int
+    topk_cmp: int
+    kv_dtype: str
+    query_nope: np.ndarray
+    query_rope: np.ndarray
+    key_nope: np.ndarray
+    key_rope: np.ndarray
+    k_nope_scales: Optional[np.ndarray]
+    cmp_indices: Optional[np.ndarray]
+    block_table_ori: np.ndarray
+    block_table_cmp: np.ndarray
+    ori_len: np.ndarray
+    cmp_len: np.ndarray
+    softmax_scale: float
+    name: str = ""
+
+    @property
+    def n_tokens(self) -> int:
+        return self.batch * self.s1
+
+    @property
+    def num_cache_rows(self) -> int:
+        return int(self.key_rope.shape[0])
+
+
+def window_generate(*, batch: int, s1: int, n_q: int, ori_lens: Sequence[int], window: int, ratio: int = 4,
+                    cmp_mode: str = "sparse", topk_cmp: int = 0, kv_dtype: str = "bf16", seed: int = 0,
+                    name: str = "") -> WindowInputs:
+    """cmp_mode: "none" (SWA: window only), "all" (CFA: every causal compressed entry, in order)
+    or "sparse" (SCFA: min(topk_cmp, causal) distinct causal entries in random order). A query at
+    position p sees the compressed entries c with (c + 1) * ratio <= p + 1 (entry c summarises
+    positions c*ratio .. c*ratio + ratio - 1). cmp_len[b] = ori_len[b] // ratio. Both caches' blocks
+    are drawn in one random order from a shared pool with one trailing NaN poison block, which
+    every unused block-table entry names; rows past a cache's length are NaN too."""
+    assert kv_dtype in ("bf16", "int8") and cmp_mode in ("none", "all", "sparse")
+    g = torch.Generator().manual_seed(90_000 + int(seed))
+    ori = [int(v) for v in ori_lens]
+    cmp_len = [v // ratio for v in ori]
+    nb_o = [math.ceil(v / BLOCK_SIZE) for v in ori]
+    nb_c = [math.ceil(v / BLOCK_SIZE) for v in cmp_len]
+    mb_o, mb_c = max(1, max(nb_o)), max(1, max(nb_c))
+    n_used = sum(nb_o) + sum(nb_c)
+    poison = n_used
+    perm = torch.randperm(n_used, generator=g).numpy().astype(np.int32)
+    bt_o = np.full((batch, mb_o), poison, dtype=np.int32)
+    bt_c = np.full((batch, mb_c), poison, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        bt_o[b, :nb_o[b]] = perm[off:off + nb_o[b]]
+        off += nb_o[b]
+        bt_c[b, :nb_c[b]] = perm[off:off + nb_c[b]]
+        off += nb_c[b]
+    rows = (n_used + 1) * BLOCK_SIZE
+    nope, scales = _normal_nope(g, rows, kv_dtype == "int8")
+    rope = _normal_bf16(g, rows, ROPE_DIM)
+    dead = np.zeros(rows, dtype=bool)
+    dead[poison * BLOCK_SIZE:] = True
+    for b in range(batch):
+        for bt, nb, ln in ((bt_o, nb_o[b], ori[b]), (bt_c, nb_c[b], cmp_len[b])):
+            tail = nb * BLOCK_SIZE - ln
+            if nb and tail > 0:
+                last = int(bt[b, nb - 1])
+                dead[last * BLOCK_SIZE + (BLOCK_SIZE - tail):(last + 1) * BLOCK_SIZE] = True
+    dead_rows = np.nonzero(dead)[0]
+    if kv_dtype == "int8":
+        scales[dead_rows] = np.float32(np.nan)
+        nope[dead_rows] = 0
+    else:
+        nope[dead_rows] = BF16_QNAN
+    rope[dead_rows] = BF16_QNAN
+    t_count = batch * s1
+    qn = _normal_bf16(g, t_count * n_q, KV_LORA_RANK)
+    qr = _normal_bf16(g, t_count * n_q, ROPE_DIM)
+    cmp_idx = None
+    if cmp_mode != "none":
+        causal = [max(0, (ori[t // s1] - s1 + t % s1 + 1) // ratio) for t in range(t_count)]
+        k = max(causal) if cmp_mode == "all" else int(topk_cmp)
+        cmp_idx = np.full((t_count, max(1, k)), -1, dtype=np.int32)
+        for t in range(t_count):
+            n = causal[t]
+            if cmp_mode == "all":
+                cmp_idx[t, :n] = np.arange(n, dtype=np.int32)
+            elif n > 0:
+                m = min(k, n)
+                cmp_idx[t, :m] = torch.randperm(n, generator=g)[:m].numpy().astype(np.int32)
+    scale = float(np.float32(1.0 / math.sqrt(KV_LORA_RANK + ROPE_DIM)))
+    return WindowInputs(batch=batch, s1=s1, n_q=n_q, window=int(window),
+                        topk_cmp=0 if cmp_idx is None else int(cmp_idx.shape[1]), kv_dtype=kv_dtype,
+                        query_nope=qn, query_rope=qr, key_nope=nope, key_rope=rope, k_nope_scales=scales,
+                        cmp_indices=cmp_idx, block_table_ori=bt_o, block_table_cmp=bt_c,
+                        ori_len=np.array(ori, dtype=np.int32), cmp_len=np.array(cmp_len, dtype=np.int32),
+                        softmax_scale=scale, name=name)
+
+
+def swa_decode(seed: int = 0, kv_dtype: str = "bf16") -> WindowInputs:
+    """SWA at the pages' timed shape (64 sequences, 2 query tokens, 8K of cache): a 128-position
+    window, no compressed cache (the window size is a reading; the page gives none)."""
+    return window_generate(batch=64, s1=2, n_q=128, ori_lens=[8192] * 64, window=128, cmp_mode="none",
+                           kv_dtype=kv_dtype, seed=seed, name=f"swa_b64_s2_w128_{kv_dtype}")
+
+
+def scfa_decode(seed: int = 0, kv_dtype: str = "bf16") -> WindowInputs:
+    """SCFA at the pages' timed shape with compress_ratio 4: a 128-position window plus 512
+    compressed entries per token picked from the 2048 causal ones (window size and top-k are
+    readings; 512 entries of ratio 4 cover 2048 original positions, the top-k of the SFA page)."""
+    return window_generate(batch=64, s1=2, n_q=128, ori_lens=[8192] * 64, window=128, ratio=4, cmp_mode="sparse",
+                           topk_cmp=512, kv_dtype=kv_dtype, seed=seed, name=f"scfa_b64_s2_w128_k512_{kv_dtype}")
