@@ -188,6 +188,56 @@ int sfa_cache_write(const sfa_dims* dims, const void* new_nope, const void* new_
                     const int32_t* block_table, void* key_nope_2d, void* key_rope_2d, float* k_nope_scales,
                     hipStream_t stream);
 
+/*
+ * ---- Sliding-window + compressed-cache attention: SWA, CFA and SCFA ----
+ *
+ * "NPU DeepSeek-V4 model PyPTO fused-operator optimisation", section "FA-class operators: SWA,
+ * CFA and SCFA": a query reads a sliding window of the original cache (ori_kv) and, for CFA and
+ * SCFA, entries of the compressed cache (cmp_kv): every causal one (CFA) or those a sparse
+ * index list selects (SCFA). SWA has the window alone. The attention over the union of the two
+ * row sets is the one of sfa_decode (same scores, softmax, V = nope, accuracy and output).
+ *
+ *   Query token t = b*s1 + s sits at position p = ori_len[b] - s1 + s. Its rows are
+ *     - the original-cache positions max(0, p - window + 1) .. p, through block_table_ori;
+ *     - cmp_indices[t, i] for i < topk_cmp, valid iff 0 <= c < cmp_len[b], through
+ *       block_table_cmp (-1 or out-of-range entries are masked anywhere in the row; for CFA the
+ *       caller lists every causal entry, for SCFA the selected ones).
+ *   Both caches are rows of one paged pool (key_nope_2d, key_rope_2d, k_nope_scales as in
+ *   sfa_decode, blocks of 128 rows); each has its own block table and length.
+ *
+ *   query_nope/query_rope/out/key_*    as for sfa_decode
+ *   cmp_indices      int32 (T, topk_cmp)                    NULL when topk_cmp == 0
+ *   block_table_ori  int32 (batch, max_blocks_ori)
+ *   block_table_cmp  int32 (batch, max_blocks_cmp)          NULL when topk_cmp == 0
+ *   ori_len, cmp_len int32 (batch)                          cmp_len NULL when topk_cmp == 0
+ *   workspace        device, 256-byte aligned, >= sfa_window_workspace_size bytes: the combined
+ *                    gather list, block table and lengths a pre-pass kernel writes, then the
+ *                    workspace of the attention itself. Calls that overlap on one workspace race.
+ *
+ * The pre-pass and the attention are queued on `stream`; nothing is allocated. Errors as for
+ * sfa_decode, plus SFA_ERR_DIMS for window < 0, topk_cmp < 0, window + topk_cmp < 1 (or above
+ * the attention's top-k limit), max_blocks_ori < 1, or topk_cmp > 0 with max_blocks_cmp < 1.
+ * Preconditions as for sfa_decode, on both block tables; also ori_len[b] >= s1 for a full window
+ * (positions below 0 are simply absent).
+ */
+typedef struct {
+  int32_t batch, s1, n_q, n_kv, kv_lora_rank, rope_dim, block_size;  /* as in sfa_dims         */
+  int32_t window;          /* original-cache positions each query reads, >= 0               */
+  int32_t topk_cmp;        /* row length of cmp_indices, >= 0 (0: SWA, no compressed source)  */
+  int32_t max_blocks_ori;  /* row length of block_table_ori, >= 1                            */
+  int32_t max_blocks_cmp;  /* row length of block_table_cmp (>= 1 when topk_cmp > 0)         */
+  int64_t num_cache_rows;  /* rows of the shared pool                                        */
+  sfa_kv_dtype kv_dtype;
+  int32_t num_splits;      /* as in sfa_dims (0 = automatic)                                 */
+} sfa_window_dims;
+
+int sfa_window_workspace_size(const sfa_window_dims* dims, size_t* bytes_out);
+int sfa_window_decode(const sfa_window_dims* dims, const void* query_nope, const void* query_rope,
+                      const void* key_nope_2d, const void* key_rope_2d, const float* k_nope_scales,
+                      const int32_t* cmp_indices, const int32_t* block_table_ori, const int32_t* block_table_cmp,
+                      const int32_t* ori_len, const int32_t* cmp_len, float softmax_scale, void* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char* sfa_status_string(int status);
 

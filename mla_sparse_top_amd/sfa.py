@@ -83,8 +83,34 @@ _lib.sfa_topk_select.restype = ctypes.c_int
 _lib.sfa_cache_write.argtypes = [ctypes.POINTER(SfaDims), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.sfa_cache_write.restype = ctypes.c_int
 
+class SfaWindowDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("s1", ctypes.c_int32),
+        ("n_q", ctypes.c_int32),
+        ("n_kv", ctypes.c_int32),
+        ("kv_lora_rank", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("topk_cmp", ctypes.c_int32),
+        ("max_blocks_ori", ctypes.c_int32),
+        ("max_blocks_cmp", ctypes.c_int32),
+        ("num_cache_rows", ctypes.c_int64),
+        ("kv_dtype", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
+_lib.sfa_window_workspace_size.argtypes = [ctypes.POINTER(SfaWindowDims), ctypes.POINTER(ctypes.c_size_t)]
+_lib.sfa_window_workspace_size.restype = ctypes.c_int
+_lib.sfa_window_decode.argtypes = [ctypes.POINTER(SfaWindowDims), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.sfa_window_decode.restype = ctypes.c_int
+
 EXPORTED_SYMBOLS = ("sfa_workspace_size", "sfa_num_splits", "sfa_decode", "sfa_prefill", "sfa_resolve_rows",
-                    "sfa_status_string", "sfa_indexer_scores", "sfa_topk_select", "sfa_cache_write")
+                    "sfa_status_string", "sfa_indexer_scores", "sfa_topk_select", "sfa_cache_write",
+                    "sfa_window_workspace_size", "sfa_window_decode")
 
 
 class SfaError(RuntimeError):
@@ -322,6 +348,114 @@ def cache_write(new_nope, new_rope, positions, block_table, key_nope, key_rope, 
     if st != 0:
         raise SfaError(st, "sfa_cache_write")
     return key_nope
+
+
+def window_workspace_size(dims: SfaWindowDims) -> int:
+    out = ctypes.c_size_t(0)
+    st = _lib.sfa_window_workspace_size(ctypes.byref(dims), ctypes.byref(out))
+    if st != 0:
+        raise SfaError(st, "sfa_window_workspace_size")
+    return int(out.value)
+
+
+def _marshal_window(query_nope, query_rope, key_nope, key_rope, k_nope_scales, cmp_indices, block_table_ori,
+                    block_table_cmp, ori_len, cmp_len, softmax_scale, *, batch, s1, window, out=None, workspace=None,
+                    num_splits=0, stream=None):
+    dev = query_nope.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    t_tokens = batch * s1
+    n_q = query_nope.shape[0] // t_tokens if t_tokens else 0
+    rows = key_rope.shape[0]
+    _check(query_nope, "query_nope", (torch.bfloat16,), (t_tokens * n_q, KV_LORA_RANK), dev)
+    _check(query_rope, "query_rope", (torch.bfloat16,), (t_tokens * n_q, ROPE_DIM), dev)
+    _check(key_nope, "key_nope", (torch.bfloat16, torch.int8), (rows, KV_LORA_RANK), dev)
+    _check(key_rope, "key_rope", (torch.bfloat16,), (rows, ROPE_DIM), dev)
+    int8 = key_nope.dtype == torch.int8
+    if int8:
+        if k_nope_scales is None:
+            raise ValueError("an int8 key_nope needs k_nope_scales")
+        _check(k_nope_scales, "k_nope_scales", (torch.float32,), (rows, 4), dev)
+    _check(block_table_ori, "block_table_ori", (torch.int32,), None, dev)
+    _check(ori_len, "ori_len", (torch.int32,), (batch,), dev)
+    topk_cmp = 0 if cmp_indices is None else int(cmp_indices.shape[1])
+    if topk_cmp:
+        _check(cmp_indices, "cmp_indices", (torch.int32,), (t_tokens, topk_cmp), dev)
+        _check(block_table_cmp, "block_table_cmp", (torch.int32,), None, dev)
+        _check(cmp_len, "cmp_len", (torch.int32,), (batch,), dev)
+    dims = SfaWindowDims(batch, s1, n_q, 1, KV_LORA_RANK, ROPE_DIM, BLOCK_SIZE, int(window), topk_cmp,
+                         block_table_ori.shape[1], block_table_cmp.shape[1] if topk_cmp else 0, rows,
+                         KV_INT8 if int8 else KV_BF16, num_splits)
+    if out is None:
+        out = torch.empty((batch, s1, n_q, KV_LORA_RANK), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", (torch.bfloat16,), (batch, s1, n_q, KV_LORA_RANK), dev)
+    need = window_workspace_size(dims)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)  # the pre-pass fills every byte it reads
+    _check(workspace, "workspace", (torch.uint8,), None, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    args = (ctypes.byref(dims), _ptr(query_nope), _ptr(query_rope), _ptr(key_nope), _ptr(key_rope),
+            _ptr(k_nope_scales if int8 else None), _ptr(cmp_indices if topk_cmp else None), _ptr(block_table_ori),
+            _ptr(block_table_cmp if topk_cmp else None), _ptr(ori_len), _ptr(cmp_len if topk_cmp else None),
+            ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+            ctypes.c_void_p(stream.cuda_stream))
+    keep = (dims, query_nope, query_rope, key_nope, key_rope, k_nope_scales, cmp_indices, block_table_ori,
+            block_table_cmp, ori_len, cmp_len, out, workspace, stream)
+    return args, out, keep
+
+
+def window_decode(*tensors, **kw):
+    """sfa_window_decode (SWA / CFA / SCFA): returns out (batch, s1, n_q, 512) bf16."""
+    args, out, _keep = _marshal_window(*tensors, **kw)
+    st = _lib.sfa_window_decode(*args)
+    if st != 0:
+        raise SfaError(st, "sfa_window_decode")
+    return out
+
+
+def prepare_window_decode(*tensors, **kw) -> PreparedCall:
+    """sfa_window_decode bound to these tensors (a PreparedCall returning out)."""
+    args, out, keep = _marshal_window(*tensors, **kw)
+    return PreparedCall([(_lib.sfa_window_decode, args, "sfa_window_decode")], out, keep)
+
+
+def window_to_device(inp, device="cuda"):
+    """Upload a workloads.WindowInputs instance."""
+    import numpy as np
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    cmp = inp.cmp_indices is not None
+    return {
+        "query_nope": bf16(inp.query_nope),
+        "query_rope": bf16(inp.query_rope),
+        "key_nope": bf16(inp.key_nope) if inp.kv_dtype == "bf16" else torch.from_numpy(inp.key_nope).to(device),
+        "key_rope": bf16(inp.key_rope),
+        "k_nope_scales": None if inp.k_nope_scales is None else torch.from_numpy(inp.k_nope_scales).to(device),
+        "cmp_indices": torch.from_numpy(inp.cmp_indices).to(device) if cmp else None,
+        "block_table_ori": torch.from_numpy(inp.block_table_ori).to(device),
+        "block_table_cmp": torch.from_numpy(inp.block_table_cmp).to(device) if cmp else None,
+        "ori_len": torch.from_numpy(inp.ori_len).to(device),
+        "cmp_len": torch.from_numpy(inp.cmp_len).to(device) if cmp else None,
+    }
+
+
+def _window_args(inp, d):
+    return (d["query_nope"], d["query_rope"], d["key_nope"], d["key_rope"], d["k_nope_scales"], d["cmp_indices"],
+            d["block_table_ori"], d["block_table_cmp"], d["ori_len"], d["cmp_len"], inp.softmax_scale)
+
+
+def run_window(inp, d=None, *, num_splits=0, out=None):
+    """sfa_window_decode on an uploaded WindowInputs instance."""
+    d = d if d is not None else window_to_device(inp)
+    return window_decode(*_window_args(inp, d), batch=inp.batch, s1=inp.s1, window=inp.window, out=out,
+                         num_splits=num_splits)
+
+
+def prepare_window_run(inp, d, *, out=None) -> PreparedCall:
+    return prepare_window_decode(*_window_args(inp, d), batch=inp.batch, s1=inp.s1, window=inp.window, out=out)
 
 
 def to_device(inp, device="cuda"):

@@ -248,3 +248,45 @@ def test_probe_library_is_separate_and_exports_its_entry():
     main = subprocess.run(["nm", "-D", "--defined-only", sfa.lib_path()], capture_output=True, text=True,
                           check=True).stdout
     assert "sfa_probe_mfma" not in main
+
+
+def _wdims(**kw):
+    base = dict(batch=2, s1=2, n_q=16, n_kv=1, kv_lora_rank=512, rope_dim=64, block_size=128, window=8, topk_cmp=4,
+                max_blocks_ori=2, max_blocks_cmp=1, num_cache_rows=1024, kv_dtype=0, num_splits=0)
+    base.update(kw)
+    return sfa.SfaWindowDims(*[base[f] for f, _ in sfa.SfaWindowDims._fields_])
+
+
+def _wcall(dims, ws_bytes=None, **kw):
+    p = dict(qn=0x100000, qr=0x200000, kn=0x10000000, kr=0x20000000, sc=0x30000000, ci=0x400000, bo=0x500000,
+             bc=0x600000, ol=0x700000, cl=0x800000, out=0x40000000, ws=0x50000000)
+    p.update(kw)
+    vp = lambda v: None if v is None else ctypes.c_void_p(v)  # noqa: E731
+    if ws_bytes is None:
+        ws_bytes = 1 << 30
+    return sfa._lib.sfa_window_decode(ctypes.byref(dims), vp(p["qn"]), vp(p["qr"]), vp(p["kn"]), vp(p["kr"]),
+                                      vp(p["sc"]), vp(p["ci"]), vp(p["bo"]), vp(p["bc"]), vp(p["ol"]), vp(p["cl"]),
+                                      ctypes.c_float(0.05), vp(p["out"]), vp(p["ws"]), ctypes.c_size_t(ws_bytes), None)
+
+
+def test_window_validation():
+    d = _wdims()
+    need = sfa.window_workspace_size(d)
+    assert need >= 2 * 2 * (8 + 4) * 4
+    assert _wcall(d, qn=None) == -1
+    assert _wcall(d, ci=None) == -1                         # topk_cmp > 0 needs the compressed source
+    # SWA (topk_cmp == 0) takes no compressed source: the null pointers pass, and the missing
+    # workspace is what fails (every call here fails validation, so nothing is ever launched)
+    assert _wcall(_wdims(topk_cmp=0, max_blocks_cmp=0), ci=None, bc=None, cl=None, ws=None) == -4
+    assert _wcall(_wdims(kv_dtype=1), sc=None) == -5
+    assert _wcall(d, bo=0x500004) == -3
+    assert _wcall(d, ws=0x50000010) == -4                   # workspace not 256-byte aligned
+    assert _wcall(d, ws_bytes=need - 1) == -4
+    assert _wcall(d, out=0x100000 + 64) == -6               # out over query_nope
+    assert _wcall(d, out=0x50000000 + 256) == -6            # out inside the workspace
+    assert _wcall(_wdims(window=-1)) == -2
+    assert _wcall(_wdims(window=0, topk_cmp=0)) == -2
+    assert _wcall(_wdims(max_blocks_cmp=0)) == -2           # topk_cmp > 0 without a compressed table
+    assert _wcall(_wdims(block_size=64)) == -2              # the attention's own dims are checked too
+    assert _wcall(_wdims(window=40000)) == -2               # above the attention's top-k limit
+    assert _wcall(_wdims(batch=0), ws_bytes=need) == 0      # nothing to do, nothing queued

@@ -1,0 +1,81 @@
+"""GPU parity of the sliding-window + compressed-cache attention variants (sfa_window_decode:
+SWA, CFA, SCFA) against the CPU oracle (oracle/window_oracle.py), at the attention's accuracy
+standard (|got - ref| <= 1e-4 + 5e-3 |ref| on every element), plus exact closed forms."""
+
+import numpy as np
+import pytest
+
+import oracle.sfa_oracle as O
+import oracle.window_oracle as WO
+from mla_sparse_top_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(sfa, inp, tokens=None, splits=0):
+    out = sfa.run_window(inp, num_splits=splits).float().cpu().numpy().astype(np.float64)
+    ref = WO.window_attention(inp, tokens=tokens)
+    got = out.reshape(inp.n_tokens, inp.n_q, 512)
+    if tokens is not None:
+        got = got[list(tokens)]
+    else:
+        ref = ref.reshape(inp.n_tokens, inp.n_q, 512)
+    rep = O.allclose_report(got, ref)
+    assert rep["fails"] == 0, rep
+    return out
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+@pytest.mark.parametrize("mode", ["none", "all", "sparse"])
+def test_small_variants(sfa_lib, kv_dtype, mode):
+    # ragged lengths; windows that reach below position 0; compressed lists with -1 padding
+    inp = W.window_generate(batch=3, s1=2, n_q=32, ori_lens=[700, 40, 2], window=64, ratio=4, cmp_mode=mode,
+                            topk_cmp=24, kv_dtype=kv_dtype, seed=1)
+    _check(sfa_lib, inp)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4])
+def test_partitions_agree(sfa_lib, splits):
+    inp = W.window_generate(batch=2, s1=2, n_q=64, ori_lens=[3000, 1500], window=700, ratio=4, cmp_mode="sparse",
+                            topk_cmp=300, seed=2)
+    _check(sfa_lib, inp, splits=splits)
+
+
+def test_one_position_window_is_the_value_row_bit_exact(sfa_lib):
+    inp = W.window_generate(batch=2, s1=2, n_q=16, ori_lens=[300, 129], window=1, cmp_mode="none", seed=3)
+    out = sfa_lib.run_window(inp).view(dtype=__import__("torch").int16).cpu().numpy().view(np.uint16)
+    for t in range(4):
+        b, s = divmod(t, 2)
+        p = int(inp.ori_len[b]) - 2 + s
+        row = int(inp.block_table_ori[b, p // 128]) * 128 + p % 128
+        assert np.array_equal(out[b, s], np.broadcast_to(inp.key_nope[row], (16, 512)))
+
+
+def test_window_only_equals_sparse_decode_bit_exact(sfa_lib):
+    """SWA through the pre-pass gives the same bits as sfa_decode given the window positions as
+    its top-k list (the same kernel on the same gather list)."""
+    import torch
+
+    inp = W.window_generate(batch=2, s1=2, n_q=32, ori_lens=[500, 200], window=96, cmp_mode="none", seed=4)
+    got = sfa_lib.run_window(inp)
+    idx = np.full((4, 96), -1, dtype=np.int32)
+    for t in range(4):
+        p = int(inp.ori_len[t // 2]) - 2 + t % 2
+        w = WO.window_positions(p, 96)
+        idx[t, :len(w)] = w
+    d = sfa_lib.window_to_device(inp)
+    ref = sfa_lib.decode(d["query_nope"], d["query_rope"], d["key_nope"], d["key_rope"], None,
+                         torch.from_numpy(idx).cuda(), d["block_table_ori"], d["ori_len"], inp.softmax_scale,
+                         batch=2, s1=2)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+def test_swa_decode_shape_full(sfa_lib):
+    _check(sfa_lib, W.swa_decode(seed=0))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+def test_scfa_decode_shape_sampled(sfa_lib, kv_dtype):
+    inp = W.scfa_decode(seed=1, kv_dtype=kv_dtype)
+    _check(sfa_lib, inp, tokens=range(0, inp.n_tokens, 9))
