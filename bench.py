@@ -311,6 +311,129 @@ def bench_indexer(args):
     print(json.dumps(rec), flush=True)
 
 
+WINDOW_WORKLOADS = {
+    "swa_b64_s2_w128_bf16": ("swa_decode", "bf16"),
+    "scfa_b64_s2_w128_k512_bf16": ("scfa_decode", "bf16"),
+    "scfa_b64_s2_w128_k512_int8": ("scfa_decode", "int8"),
+}
+
+
+def bench_window(args):
+    """The sliding-window + compressed-cache variants (sfa_window_decode: pre-pass + sparse
+    attention) at the pages' timed shape: 64 sequences x 2 query tokens, 8K of original cache,
+    window 128; SCFA adds 512 of the 2048 causal compressed entries (compress_ratio 4). --sets
+    copies of the pool in different block orders are rotated (both block tables remapped)."""
+    import numpy as np
+    import torch
+
+    import oracle.sfa_oracle as O
+    import oracle.window_oracle as WO
+    from mla_sparse_top_amd import sfa, workloads
+
+    fn_name, dtype = WINDOW_WORKLOADS[args.workload]
+    inp = getattr(workloads, fn_name)(seed=args.seed, kv_dtype=dtype)
+    print(f"[bench] generated {inp.name}", file=sys.stderr, flush=True)
+    dev0 = sfa.window_to_device(inp)
+    n_pool = inp.num_cache_rows // 128
+    sets = [dev0]
+    for i in range(1, max(1, args.sets)):
+        g = torch.Generator(device="cpu").manual_seed(1000 + i)
+        perm = torch.randperm(n_pool, generator=g).to("cuda")
+        d = dict(dev0)
+        for key in ("key_nope", "key_rope", "k_nope_scales"):
+            if dev0[key] is None:
+                continue
+            blocks = dev0[key].view(n_pool, 128, -1)
+            moved = torch.empty_like(blocks)
+            moved[perm] = blocks
+            d[key] = moved.view_as(dev0[key])
+        p32 = perm.to(torch.int32)
+        d["block_table_ori"] = p32[dev0["block_table_ori"].long()].contiguous()
+        if dev0["block_table_cmp"] is not None:
+            d["block_table_cmp"] = p32[dev0["block_table_cmp"].long()].contiguous()
+        sets.append(d)
+    outs = [torch.empty((inp.batch, inp.s1, inp.n_q, 512), dtype=torch.bfloat16, device="cuda") for _ in sets]
+    calls = [sfa.prepare_window_run(inp, d, out=o) for d, o in zip(sets, outs)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        calls[i % len(calls)]()
+
+    n_warm = warm_up(step, args, torch)
+    whole0, whole1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    whole0.record()
+    for i in range(args.steps):
+        step(i)
+    whole1.record()
+    torch.cuda.synchronize()
+    us_per_call = whole0.elapsed_time(whole1) / args.steps * 1e3
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    launch_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps
+    same = all(torch.equal(outs[0], o) for o in outs[1:])
+
+    T = inp.n_tokens
+    valid = sum(len(WO.token_rows(t, inp.s1, inp.window, inp.cmp_indices, inp.block_table_ori, inp.block_table_cmp,
+                                  inp.ori_len, inp.cmp_len, inp.num_cache_rows)) for t in range(T))
+    row = 1152 if dtype == "bf16" else 656
+    nbytes = valid * row + T * (inp.n_q * 576 * 2 + inp.n_q * 512 * 2 + 4 * inp.topk_cmp)
+    flop = valid * 2 * inp.n_q * (576 + 512)
+    gbps = nbytes / (launch_ms * 1e-3) / 1e9
+    tflops = flop / (launch_ms * 1e-3) / 1e12
+    rec = {
+        "metric": f"us/call + GB/s & TFLOP/s vs roofline, {args.workload}",
+        "value": round(us_per_call, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": n_warm,
+        "ms_per_step": round(us_per_call / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": inp.batch, "s1": inp.s1, "n_q": inp.n_q,
+                   "window": inp.window, "topk_cmp": inp.topk_cmp, "ori_len": int(inp.ori_len.max()),
+                   "compress_ratio": 4, "valid_slots": valid, "cold_sets": len(sets)},
+        "kernel_ms_mean": round(launch_ms, 5),
+        "algorithmic_bytes_per_call": nbytes,
+        "algorithmic_flop_per_call": flop,
+        "tflops": round(tflops, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "rotated_outputs_identical": bool(same),
+        "context_pages_one_die_us": 65 if fn_name == "swa_decode" else 160,
+    }
+    if args.cpu_seconds > 0:
+        got = outs[(args.steps - 1) % len(sets)].float().cpu().numpy().astype(np.float64).reshape(T, inp.n_q, 512)
+        order = np.random.default_rng(0).permutation(T)
+        t0 = time.perf_counter()
+        done, fails, worst = 0, 0, 0.0
+        while done == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            t = int(order[done % T])
+            ref = WO.window_attention(inp, tokens=[t])[0]
+            if done < T:
+                rep = O.allclose_report(got[t], ref)
+                fails += rep["fails"]
+                worst = max(worst, rep["worst_ratio"])
+            done += 1
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(el / done * T * 1e6, 1), "unit": "us/call",
+                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "sample": f"{done} token evaluations (random order, seed 0) in {el:.1f} s, scaled to "
+                               f"one call of {T} tokens",
+                               "sample_parity": {"tokens": min(done, T), "fails": fails,
+                                                 "worst_err_over_bound": round(worst, 4)}}
+    print(json.dumps(rec), flush=True)
+
+
 CACHE_WORKLOADS = {
     "cache_write_b64_s8192_int8": ("cache_fill", "int8"),
     "cache_write_b64_s8192_bf16": ("cache_fill", "bf16"),
@@ -498,7 +621,7 @@ def main():
                          "--warmup-seconds of calls, so the GPU clocks have left their idle state)")
     ap.add_argument("--warmup-seconds", type=float, default=0.5)
     ap.add_argument("--workload", default="decode_b64_s2_bf16",
-                    choices=sorted(WORKLOADS) + ["indexer_b64_s2"] + sorted(CACHE_WORKLOADS))
+                    choices=sorted(WORKLOADS) + ["indexer_b64_s2"] + sorted(CACHE_WORKLOADS) + sorted(WINDOW_WORKLOADS))
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated for a cold cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget (0 disables)")
     ap.add_argument("--seed", type=int, default=0)
@@ -528,6 +651,9 @@ def main():
         return
     if args.workload in CACHE_WORKLOADS:
         bench_cache_write(args)
+        return
+    if args.workload in WINDOW_WORKLOADS:
+        bench_window(args)
         return
 
     from mla_sparse_top_amd import sfa, workloads
