@@ -210,13 +210,15 @@ int sfa_cache_write(const sfa_dims* dims, const void* new_nope, const void* new_
  *   block_table_ori  int32 (batch, max_blocks_ori)
  *   block_table_cmp  int32 (batch, max_blocks_cmp)          NULL when topk_cmp == 0
  *   ori_len, cmp_len int32 (batch)                          cmp_len NULL when topk_cmp == 0
- *   workspace        device, 256-byte aligned, >= sfa_window_workspace_size bytes: the combined
- *                    gather list, block table and lengths a pre-pass kernel writes, then the
- *                    workspace of the attention itself. Calls that overlap on one workspace race.
+ *   workspace        as for sfa_decode, sized by sfa_window_workspace_size (0 bytes, and NULL
+ *                    allowed, when the slots need no partitions)
  *
- * The pre-pass and the attention are queued on `stream`; nothing is allocated. Errors as for
- * sfa_decode, plus SFA_ERR_DIMS for window < 0, topk_cmp < 0, window + topk_cmp < 1 (or above
- * the attention's top-k limit), max_blocks_ori < 1, or topk_cmp > 0 with max_blocks_cmp < 1.
+ * The window and the compressed list form the slot list of the sparse attention kernel: the
+ * kernel resolves both in its own prologue (original positions through block_table_ori,
+ * compressed entries through block_table_cmp) and runs unchanged after it. Queued on `stream`;
+ * nothing is allocated. Errors as for sfa_decode, plus SFA_ERR_DIMS for window < 0,
+ * topk_cmp < 0, window + topk_cmp < 1 (or above the attention's top-k limit),
+ * max_blocks_ori < 1, or topk_cmp > 0 with max_blocks_cmp < 1.
  * Preconditions as for sfa_decode, on both block tables; also ori_len[b] >= s1 for a full window
  * (positions below 0 are simply absent).
  */

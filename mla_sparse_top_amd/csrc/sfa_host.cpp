@@ -87,19 +87,30 @@ bool overlaps(const void* p, size_t n, const void* q, size_t m) {
   return a0 < b1 && b0 < a1;
 }
 
+// The second source of the window variants (sfa_window_decode); null for sfa_decode/prefill.
+struct WindowSource {
+  int32_t window, topk_cmp, mb_cmp;
+  const int32_t* bt_cmp;
+  const int32_t* cmp_len;
+};
+
 int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void* qr, const void* kn,
                   const void* kr, const float* scales, const int32_t* idx, const int32_t* bt,
                   const int32_t* act, float softmax_scale, void* out, void* ws, size_t ws_bytes,
-                  hipStream_t stream) {
+                  hipStream_t stream, const WindowSource* win = nullptr) {
   int st = check_dims(d);
   if (st != SFA_OK) return st;
   const int64_t tokens = (int64_t)d->batch * d->s1;
-  if (!qn || !qr || !kn || !kr || !idx || !bt || !act || !out) return SFA_ERR_NULL;
+  // the window variants take no index list when they have no compressed source (SWA)
+  const bool need_idx = !win || win->topk_cmp > 0;
+  if (!qn || !qr || !kn || !kr || (need_idx && !idx) || !bt || !act || !out) return SFA_ERR_NULL;
+  if (win && win->topk_cmp > 0 && (!win->bt_cmp || !win->cmp_len)) return SFA_ERR_NULL;
   const bool int8 = d->kv_dtype == SFA_KV_INT8;
   if (int8 && !scales) return SFA_ERR_SCALES;
   if (!aligned16(qn) || !aligned16(qr) || !aligned16(kn) || !aligned16(kr) || !aligned16(idx) ||
       !aligned16(bt) || !aligned16(act) || !aligned16(out) || (int8 && !aligned16(scales)))
     return SFA_ERR_ALIGN;
+  if (win && win->topk_cmp > 0 && (!aligned16(win->bt_cmp) || !aligned16(win->cmp_len))) return SFA_ERR_ALIGN;
   if (!isfinite(softmax_scale)) return SFA_ERR_SCALE_VALUE;
 
   const int splits = pick_splits(d, is_prefill);
@@ -110,17 +121,21 @@ int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void*
 
   const size_t rows = (size_t)d->num_cache_rows;
   const size_t out_bytes = (size_t)tokens * d->n_q * kNope * 2;
-  const void* ins[] = {qn, qr, kn, kr, scales, idx, bt, act, lay.total ? ws : nullptr};
+  const int64_t idx_cols = win ? win->topk_cmp : d->topk;
+  const void* ins[] = {qn, qr, kn, kr, scales, idx, bt, act, lay.total ? ws : nullptr,
+                       win ? win->bt_cmp : nullptr, win ? win->cmp_len : nullptr};
   const size_t sizes[] = {(size_t)tokens * d->n_q * kNope * 2,
                           (size_t)tokens * d->n_q * kRope * 2,
                           rows * kNope * (int8 ? 1 : 2),
                           rows * kRope * 2,
                           int8 ? rows * 4 * sizeof(float) : 0,
-                          (size_t)tokens * d->topk * sizeof(int32_t),
+                          (size_t)tokens * idx_cols * sizeof(int32_t),
                           (size_t)d->batch * d->max_blocks_per_batch * sizeof(int32_t),
                           (size_t)d->batch * sizeof(int32_t),
-                          lay.total};
-  for (int i = 0; i < 9; ++i)
+                          lay.total,
+                          win ? (size_t)d->batch * win->mb_cmp * sizeof(int32_t) : 0,
+                          win ? (size_t)d->batch * sizeof(int32_t) : 0};
+  for (int i = 0; i < 11; ++i)
     if (overlaps(out, out_bytes, ins[i], sizes[i])) return SFA_ERR_ALIAS;
 
   if (tokens == 0) return SFA_OK;
@@ -153,12 +168,65 @@ int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void*
   a.reverse = is_prefill ? 1 : 0;
   a.head_groups = head_groups(d);
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);  // log2(e)
-  return launch_attention(a, int8, stream) == hipSuccess ? SFA_OK : SFA_ERR_HIP;
+  if (win) {
+    a.window = win->window;
+    a.mb_cmp = win->topk_cmp > 0 ? win->mb_cmp : 0;
+    a.block_table_cmp = win->topk_cmp > 0 ? win->bt_cmp : nullptr;
+    a.act_cmp = win->topk_cmp > 0 ? win->cmp_len : nullptr;
+  }
+  return launch_attention(a, int8, win != nullptr, stream) == hipSuccess ? SFA_OK : SFA_ERR_HIP;
+}
+
+int check_window_dims(const sfa_window_dims* d) {
+  if (!d) return SFA_ERR_NULL;
+  if (d->window < 0 || d->topk_cmp < 0 || d->window + (int64_t)d->topk_cmp < 1) return SFA_ERR_DIMS;
+  if (d->max_blocks_ori < 1 || d->max_blocks_cmp < 0) return SFA_ERR_DIMS;
+  if (d->topk_cmp > 0 && (d->max_blocks_cmp < 1 || d->max_blocks_cmp > (1 << 23))) return SFA_ERR_DIMS;
+  return SFA_OK;
+}
+
+// The attention dims of a window call: its slots are the window followed by the compressed list.
+sfa_dims window_attention_dims(const sfa_window_dims* w) {
+  sfa_dims c{};
+  c.batch = w->batch;
+  c.s1 = w->s1;
+  c.n_q = w->n_q;
+  c.n_kv = w->n_kv;
+  c.kv_lora_rank = w->kv_lora_rank;
+  c.rope_dim = w->rope_dim;
+  c.block_size = w->block_size;
+  c.topk = (int32_t)((int64_t)w->window + w->topk_cmp > INT32_MAX ? INT32_MAX : w->window + w->topk_cmp);
+  c.max_blocks_per_batch = w->max_blocks_ori;
+  c.num_cache_rows = w->num_cache_rows;
+  c.kv_dtype = w->kv_dtype;
+  c.num_splits = w->num_splits;
+  return c;
 }
 
 }  // namespace
 
 extern "C" {
+
+int sfa_window_workspace_size(const sfa_window_dims* dims, size_t* bytes_out) {
+  const int st = check_window_dims(dims);
+  if (st != SFA_OK) return st;
+  const sfa_dims c = window_attention_dims(dims);
+  return sfa_workspace_size(&c, 0, bytes_out);
+}
+
+int sfa_window_decode(const sfa_window_dims* dims, const void* query_nope, const void* query_rope,
+                      const void* key_nope_2d, const void* key_rope_2d, const float* k_nope_scales,
+                      const int32_t* cmp_indices, const int32_t* block_table_ori, const int32_t* block_table_cmp,
+                      const int32_t* ori_len, const int32_t* cmp_len, float softmax_scale, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_window_dims(dims);
+  if (st != SFA_OK) return st;
+  const sfa_dims c = window_attention_dims(dims);
+  WindowSource w{dims->window, dims->topk_cmp, dims->max_blocks_cmp, block_table_cmp, cmp_len};
+  return run_attention(&c, 0, query_nope, query_rope, key_nope_2d, key_rope_2d, k_nope_scales,
+                       dims->topk_cmp > 0 ? cmp_indices : nullptr, block_table_ori, ori_len, softmax_scale, out,
+                       workspace, workspace_bytes, stream, &w);
+}
 
 int sfa_workspace_size(const sfa_dims* dims, int is_prefill, size_t* bytes_out) {
   if (!bytes_out) return SFA_ERR_NULL;

@@ -40,6 +40,13 @@ struct KernelArgs {
   int64_t num_rows;
   int32_t n_tokens, s1, n_q, topk, mb, n_splits, chunk, reverse, head_groups;
   float scale_log2;           // softmax_scale * log2(e)
+  // Window variants (the kernel instantiated with its window flag): slot g < window of token
+  // t = b*s1 + s is original-cache position act[b] - s1 + s - window + 1 + g, through
+  // block_table / act / mb; slot g >= window is compressed entry topk_idx[t][g - window] (row
+  // length topk - window), live iff below act_cmp[b], through block_table_cmp / mb_cmp.
+  const int32_t* block_table_cmp;
+  const int32_t* act_cmp;
+  int32_t mb_cmp, window;
 };
 
 struct ResolveArgs {
@@ -51,7 +58,7 @@ struct ResolveArgs {
   int32_t n_tokens, s1, topk, mb;
 };
 
-hipError_t launch_attention(const KernelArgs& a, bool int8_cache, hipStream_t stream);
+hipError_t launch_attention(const KernelArgs& a, bool int8_cache, bool window_slots, hipStream_t stream);
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t stream);
 
 }  // namespace sfa

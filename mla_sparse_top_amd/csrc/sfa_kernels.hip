@@ -300,7 +300,9 @@ struct StagedInt8 {
 
 // kBufDma: cache rows (nope, rope, INT8 scales) are fetched through buffer resources with
 // 32-bit byte offsets (pools below 4 Mi rows); otherwise through 64-bit global addresses.
-template <bool kInt8, bool kBufDma>
+// kWindow: the window variants' slot list (see KernelArgs), resolved here instead of read from
+// topk_indices; the rest of the kernel is the same.
+template <bool kInt8, bool kBufDma, bool kWindow>
 __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const KernelArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
   __shared__ __attribute__((aligned(16))) char xbuf[2 * kWaves * kXBytes];
@@ -350,20 +352,46 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   const int lim = min(a.act[b], a.mb * kBlock);
   const int k0 = sp * a.chunk;
   const int nslot = max(0, min(a.topk, k0 + a.chunk) - k0);
-  const int32_t* idx = a.topk_idx + (int64_t)t * a.topk + k0;
   const int32_t* btab = a.block_table + (int64_t)b * a.mb;
   int jv[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int k = 8 * tid + i;
-    jv[i] = k < nslot ? idx[k] : -1;
-  }
+  bool livev[8];  // the slot names a live position of its cache
   int blkv[8];
+  if constexpr (!kWindow) {
+    const int32_t* idx = a.topk_idx + (int64_t)t * a.topk + k0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = jv[i];
-    const bool in = j >= 0 && j < lim;
-    blkv[i] = btab[in ? (j >> 7) : 0];
+    for (int i = 0; i < 8; ++i) {
+      const int k = 8 * tid + i;
+      jv[i] = k < nslot ? idx[k] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = jv[i];
+      livev[i] = j >= 0 && j < lim;
+      blkv[i] = btab[livev[i] ? (j >> 7) : 0];
+    }
+  } else {
+    // slot g < window: original-cache position p - window + 1 + g of the query at position
+    // p = act[b] - s1 + s (negative when the window reaches below 0); slot g >= window:
+    // compressed entry topk_idx[t][g - window] through the compressed block table
+    const int p = a.act[b] - a.s1 + (t - b * a.s1);
+    const int topk_cmp = a.topk - a.window;
+    const int32_t* cidx = a.topk_idx + (int64_t)t * topk_cmp;
+    const int lim_c = a.mb_cmp > 0 ? min(a.act_cmp[b], a.mb_cmp * kBlock) : 0;
+    const int32_t* btab_c = a.block_table_cmp + (int64_t)b * a.mb_cmp;
+    bool cmpv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = 8 * tid + i;
+      const int gs = k0 + k;
+      cmpv[i] = gs >= a.window;
+      jv[i] = k >= nslot ? -1 : (cmpv[i] ? cidx[gs - a.window] : p - a.window + 1 + gs);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = jv[i];
+      livev[i] = j >= 0 && j < (cmpv[i] ? lim_c : lim);
+      blkv[i] = livev[i] ? (cmpv[i] ? btab_c : btab)[j >> 7] : -1;
+    }
   }
   // ---- Q^T fragments (B operand, k = d): step c < 16 covers nope chunks 32*half + 2c + {0, 1},
   // steps 16 and 17 rope chunks 4*half + 2(c - 16) + {0, 1}; lane (n, g) holds chunk +g.
@@ -387,7 +415,7 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int j = jv[i];
-    const bool in = j >= 0 && j < lim;
+    const bool in = livev[i];
     const int blk = blkv[i];
     const int64_t r = (int64_t)blk * kBlock + (j & (kBlock - 1));
     const bool v = in && blk >= 0 && r < a.num_rows;
@@ -1026,7 +1054,7 @@ __global__ void __launch_bounds__(256) sfa_resolve_kernel(const ResolveArgs a) {
 
 }  // namespace
 
-hipError_t launch_attention(const KernelArgs& a, bool int8_cache, hipStream_t stream) {
+hipError_t launch_attention(const KernelArgs& a, bool int8_cache, bool window_slots, hipStream_t stream) {
   if (a.n_splits > 1) {
     const int64_t n = (int64_t)a.n_tokens * a.head_groups;
     int32_t* counters = a.counters;
@@ -1043,10 +1071,17 @@ hipError_t launch_attention(const KernelArgs& a, bool int8_cache, hipStream_t st
   // 32-bit byte offsets (and buffer sizes) cover every cache row while the pool holds fewer
   // than 4 Mi rows (4 GiB of bf16 nope)
   const bool buf = a.num_rows < (int64_t{1} << 22);
-  const void* fn = int8_cache ? (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<true, true>)
-                                     : reinterpret_cast<const void*>(&sfa_attention_kernel<true, false>))
-                              : (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<false, true>)
-                                     : reinterpret_cast<const void*>(&sfa_attention_kernel<false, false>));
+  const void* fn;
+  if (window_slots)
+    fn = int8_cache ? (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<true, true, true>)
+                           : reinterpret_cast<const void*>(&sfa_attention_kernel<true, false, true>))
+                    : (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<false, true, true>)
+                           : reinterpret_cast<const void*>(&sfa_attention_kernel<false, false, true>));
+  else
+    fn = int8_cache ? (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<true, true, false>)
+                           : reinterpret_cast<const void*>(&sfa_attention_kernel<true, false, false>))
+                    : (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<false, true, false>)
+                           : reinterpret_cast<const void*>(&sfa_attention_kernel<false, false, false>));
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

@@ -390,16 +390,17 @@ def _marshal_window(query_nope, query_rope, key_nope, key_rope, k_nope_scales, c
         out = torch.empty((batch, s1, n_q, KV_LORA_RANK), dtype=torch.bfloat16, device=dev)
     _check(out, "out", (torch.bfloat16,), (batch, s1, n_q, KV_LORA_RANK), dev)
     need = window_workspace_size(dims)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)  # the pre-pass fills every byte it reads
-    _check(workspace, "workspace", (torch.uint8,), None, dev)
+    if workspace is None and need:
+        workspace = get_workspace(dev, need)
+    if workspace is not None:
+        _check(workspace, "workspace", (torch.uint8,), None, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     args = (ctypes.byref(dims), _ptr(query_nope), _ptr(query_rope), _ptr(key_nope), _ptr(key_rope),
             _ptr(k_nope_scales if int8 else None), _ptr(cmp_indices if topk_cmp else None), _ptr(block_table_ori),
             _ptr(block_table_cmp if topk_cmp else None), _ptr(ori_len), _ptr(cmp_len if topk_cmp else None),
-            ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
-            ctypes.c_void_p(stream.cuda_stream))
+            ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel() if workspace is not None else 0), ctypes.c_void_p(stream.cuda_stream))
     keep = (dims, query_nope, query_rope, key_nope, key_rope, k_nope_scales, cmp_indices, block_table_ori,
             block_table_cmp, ori_len, cmp_len, out, workspace, stream)
     return args, out, keep

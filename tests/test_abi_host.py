@@ -270,23 +270,28 @@ def _wcall(dims, ws_bytes=None, **kw):
 
 
 def test_window_validation():
-    d = _wdims()
+    # num_splits = 2 forces partitions, so the call needs a workspace; every call below fails
+    # host validation, so nothing is ever launched
+    d = _wdims(num_splits=2)
     need = sfa.window_workspace_size(d)
-    assert need >= 2 * 2 * (8 + 4) * 4
+    assert need > 0
+    assert sfa.window_workspace_size(_wdims()) == 0          # one partition: no workspace
     assert _wcall(d, qn=None) == -1
-    assert _wcall(d, ci=None) == -1                         # topk_cmp > 0 needs the compressed source
+    assert _wcall(d, ci=None) == -1                          # topk_cmp > 0 needs the compressed source
     # SWA (topk_cmp == 0) takes no compressed source: the null pointers pass, and the missing
-    # workspace is what fails (every call here fails validation, so nothing is ever launched)
-    assert _wcall(_wdims(topk_cmp=0, max_blocks_cmp=0), ci=None, bc=None, cl=None, ws=None) == -4
-    assert _wcall(_wdims(kv_dtype=1), sc=None) == -5
+    # workspace is what fails
+    assert _wcall(_wdims(topk_cmp=0, max_blocks_cmp=0, num_splits=2), ci=None, bc=None, cl=None, ws=None) == -4
+    assert _wcall(_wdims(kv_dtype=1, num_splits=2), sc=None) == -5
     assert _wcall(d, bo=0x500004) == -3
-    assert _wcall(d, ws=0x50000010) == -4                   # workspace not 256-byte aligned
+    assert _wcall(d, bc=0x600004) == -3
+    assert _wcall(d, ws=0x50000010) == -4                    # workspace not 256-byte aligned
     assert _wcall(d, ws_bytes=need - 1) == -4
-    assert _wcall(d, out=0x100000 + 64) == -6               # out over query_nope
-    assert _wcall(d, out=0x50000000 + 256) == -6            # out inside the workspace
+    assert _wcall(d, out=0x100000 + 64) == -6                # out over query_nope
+    assert _wcall(d, out=0x600000 - 64) == -6                # out over block_table_cmp
+    assert _wcall(d, out=0x50000000 + 256) == -6             # out inside the workspace
     assert _wcall(_wdims(window=-1)) == -2
     assert _wcall(_wdims(window=0, topk_cmp=0)) == -2
-    assert _wcall(_wdims(max_blocks_cmp=0)) == -2           # topk_cmp > 0 without a compressed table
-    assert _wcall(_wdims(block_size=64)) == -2              # the attention's own dims are checked too
-    assert _wcall(_wdims(window=40000)) == -2               # above the attention's top-k limit
-    assert _wcall(_wdims(batch=0), ws_bytes=need) == 0      # nothing to do, nothing queued
+    assert _wcall(_wdims(max_blocks_cmp=0)) == -2            # topk_cmp > 0 without a compressed table
+    assert _wcall(_wdims(block_size=64)) == -2               # the attention's own dims are checked too
+    assert _wcall(_wdims(window=40000)) == -2                # above the attention's top-k limit
+    assert _wcall(_wdims(batch=0, num_splits=2), ws_bytes=need) == 0  # nothing to do, nothing queued

@@ -52,8 +52,8 @@ def test_one_position_window_is_the_value_row_bit_exact(sfa_lib):
 
 
 def test_window_only_equals_sparse_decode_bit_exact(sfa_lib):
-    """SWA through the pre-pass gives the same bits as sfa_decode given the window positions as
-    its top-k list (the same kernel on the same gather list)."""
+    """SWA gives the same bits as sfa_decode given the window positions as its top-k list: the
+    window instantiation resolves the same rows in the same order."""
     import torch
 
     inp = W.window_generate(batch=2, s1=2, n_q=32, ori_lens=[500, 200], window=96, cmp_mode="none", seed=4)
