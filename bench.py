@@ -320,9 +320,10 @@ WINDOW_WORKLOADS = {
 
 def bench_window(args):
     """The sliding-window + compressed-cache variants (sfa_window_decode: the sparse attention
-    kernel resolving window and compressed slots itself) at the pages' timed shape: 64 sequences x 2 query tokens, 8K of original cache,
-    window 128; SCFA adds 512 of the 2048 causal compressed entries (compress_ratio 4). --sets
-    copies of the pool in different block orders are rotated (both block tables remapped)."""
+    kernel resolving window and compressed slots itself) at the pages' timed shape: 64 sequences
+    x 2 query tokens, 8K of original cache, window 128; SCFA adds 512 of the 2048 causal
+    compressed entries (compress_ratio 4). --sets copies of the pool in different block orders
+    are rotated (both block tables remapped)."""
     import numpy as np
     import torch
 
