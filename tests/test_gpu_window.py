@@ -79,3 +79,12 @@ def test_swa_decode_shape_full(sfa_lib):
 def test_scfa_decode_shape_sampled(sfa_lib, kv_dtype):
     inp = W.scfa_decode(seed=1, kv_dtype=kv_dtype)
     _check(sfa_lib, inp, tokens=range(0, inp.n_tokens, 9))
+
+
+@pytest.mark.parametrize("mode", ["none", "sparse"])
+def test_prefill_form(sfa_lib, mode):
+    """Prefill is s1 = ori_len: query s sits at position s, so early queries have short windows
+    (down to one position) and few causal compressed entries (none below position 3)."""
+    inp = W.window_generate(batch=1, s1=300, n_q=16, ori_lens=[300], window=64, ratio=4, cmp_mode=mode, topk_cmp=16,
+                            seed=7)
+    _check(sfa_lib, inp)
