@@ -311,6 +311,140 @@ def bench_indexer(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_decode_step(args):
+    """One decode step of one layer at B=64, S1=2, 8K of cache, chained on one stream: the cache
+    write of the 128 new latent rows (positions 8190 and 8191), the indexer's scores and top-k
+    (2048 of 8192), and the sparse attention over the selected rows (bf16 cache). --sets
+    copies of both pools in different block orders are rotated."""
+    import numpy as np
+    import torch
+
+    import oracle.cache_oracle as CO
+    import oracle.indexer_oracle as IO
+    import oracle.sfa_oracle as O
+    from mla_sparse_top_amd import sfa, workloads
+
+    lat = workloads.decode_mtp1(seed=args.seed)
+    idx_inp = workloads.indexer_decode(seed=args.seed)
+    pos = np.tile(np.array([8190, 8191], dtype=np.int32), 64)
+    new = workloads.cache_write_generate(batch=64, s1=2, n_pool_blocks=1, max_blocks_per_batch=lat.block_table.shape[1],
+                                         kv_dtype="bf16", seed=args.seed, positions=pos, block_table=lat.block_table)
+    print("[bench] generated the decode-step inputs", file=sys.stderr, flush=True)
+    T, K = lat.n_tokens, lat.topk
+    lat0 = sfa.to_device(lat)
+    ix0 = sfa.indexer_to_device(idx_inp)
+    nw = sfa.cache_to_device(new)
+    sets = []
+    for i in range(max(1, args.sets)):
+        if i == 0:
+            ld, xd = lat0, ix0
+        else:
+            ld = permuted_copy(lat0, lat, 1000 + i)
+            g = torch.Generator(device="cpu").manual_seed(2000 + i)
+            n_pool = idx_inp.num_cache_rows // 128
+            perm = torch.randperm(n_pool, generator=g).to("cuda")
+            xd = dict(ix0)
+            moved = torch.empty_like(ix0["k_index"].view(n_pool, 128, -1))
+            moved[perm] = ix0["k_index"].view(n_pool, 128, -1)
+            xd["k_index"] = moved.view_as(ix0["k_index"])
+            xd["block_table"] = perm.to(torch.int32)[ix0["block_table"].long()].contiguous()
+        topk = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        out = torch.empty((lat.batch, lat.s1, lat.n_q, 512), dtype=torch.bfloat16, device="cuda")
+        cw = sfa.prepare_cache_write(nw["new_nope"], nw["new_rope"], nw["positions"], ld["block_table"], ld["key_nope"],
+                                     ld["key_rope"], None, batch=64, s1=2)
+        ix = sfa.prepare_indexer(xd["q_index"], xd["k_index"], xd["weights"], xd["block_table"], xd["kv_act_seqs"],
+                                 batch=64, s1=2, topk=K, out=topk)
+        at = sfa.prepare_decode(ld["query_nope"], ld["query_rope"], ld["key_nope"], ld["key_rope"], None, topk,
+                                ld["block_table"], ld["kv_act_seqs"], lat.softmax_scale, batch=64, s1=2, out=out)
+        sets.append((cw, ix, at, topk, out))
+    torch.cuda.synchronize()
+
+    def step(i):
+        cw, ix, at, _, _ = sets[i % len(sets)]
+        cw()
+        ix()
+        at()
+
+    n_warm = warm_up(step, args, torch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    valid, attn_bytes, attn_flop = algorithmic_work(lat)
+    idx_bytes = int(idx_inp.kv_act_seqs.sum()) * 256 + T * (64 * 128 * 2 + 64 * 4) + T * idx_inp.n_positions * 4
+    cw_bytes = T * (1160 + 1152)
+    nbytes = attn_bytes + idx_bytes + cw_bytes
+    gbps = nbytes / (us * 1e-6) / 1e9
+    rec = {
+        "metric": "us/step (cache write + indexer + sparse attention), B=64 S1=2 8K decode",
+        "value": round(us, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": n_warm,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": 64, "s1": 2, "n_q": 128, "index_heads": 64, "topk": K,
+                   "kv_len": 8192, "cold_sets": len(sets)},
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+    if args.cpu_seconds > 0:
+        # one more step on copy 0, then the oracles on sampled tokens: the written cache, the
+        # selection (an exact top-k of the kernel's own scores), and the attention over the
+        # selected rows of the written cache
+        cw, ix, at, topk, out = sets[0]
+        cw()
+        ix()
+        at()
+        torch.cuda.synchronize()
+        got_idx = topk.cpu().numpy()
+        got_sc = ix._keep[0].out.cpu().numpy().astype(np.float64)
+        got = out.float().cpu().numpy().astype(np.float64).reshape(T, lat.n_q, 512)
+        kn, kr, _ = CO.cache_write(new.new_nope, new.new_rope, new.positions, new.block_table, 2, lat.key_nope,
+                                   lat.key_rope)
+        q_idx = idx_inp.q_index.reshape(T, idx_inp.n_heads, idx_inp.head_dim)
+        order = np.random.default_rng(0).permutation(T)
+        t0 = time.perf_counter()
+        done, fails, worst, bad_sel = 0, 0, 0.0, 0
+        while done == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            t = int(order[done % T])
+            b = t // 2
+            ref_sc = IO.indexer_scores(q_idx[t:t + 1], idx_inp.weights[t:t + 1], idx_inp.k_index,
+                                       idx_inp.block_table[b:b + 1], idx_inp.kv_act_seqs[b:b + 1], 1,
+                                       idx_inp.n_positions)
+            IO.topk_positions(ref_sc, K)
+            rows = O.resolve_rows(got_idx[t:t + 1], lat.block_table[b:b + 1], lat.kv_act_seqs[b:b + 1], 1)[0]
+            kn_g, kr_g = O.gather_latents(rows[rows >= 0], kn, kr, None)
+            qn = O.bf16_bits_to_f64(lat.query_nope[t * lat.n_q:(t + 1) * lat.n_q])
+            qr = O.bf16_bits_to_f64(lat.query_rope[t * lat.n_q:(t + 1) * lat.n_q])
+            ref = O.sparse_mla_attention_token(qn, qr, kn_g, kr_g, lat.softmax_scale)
+            if done < T:
+                rep = O.allclose_report(got[t], ref)
+                fails += rep["fails"]
+                worst = max(worst, rep["worst_ratio"])
+                bad_sel += len(IO.check_topk(got_idx[t:t + 1], got_sc[t:t + 1], K)["bad"])
+            done += 1
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(el / done * T * 1e6, 1), "unit": "us/step",
+                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "sample": f"{done} token evaluations (indexer scores + selection + attention over the "
+                               f"written cache, random order, seed 0) in {el:.1f} s, scaled to one step of {T} tokens",
+                               "sample_parity": {"tokens": min(done, T), "attention_fails": fails,
+                                                 "worst_err_over_bound": round(worst, 4),
+                                                 "selection_rows_bad": bad_sel}}
+    print(json.dumps(rec), flush=True)
+
+
 WINDOW_WORKLOADS = {
     "swa_b64_s2_w128_bf16": ("swa_decode", "bf16"),
     "scfa_b64_s2_w128_k512_bf16": ("scfa_decode", "bf16"),
@@ -622,7 +756,8 @@ def main():
                          "--warmup-seconds of calls, so the GPU clocks have left their idle state)")
     ap.add_argument("--warmup-seconds", type=float, default=0.5)
     ap.add_argument("--workload", default="decode_b64_s2_bf16",
-                    choices=sorted(WORKLOADS) + ["indexer_b64_s2"] + sorted(CACHE_WORKLOADS) + sorted(WINDOW_WORKLOADS))
+                    choices=sorted(WORKLOADS) + ["indexer_b64_s2", "decode_step_b64_s2"] + sorted(CACHE_WORKLOADS)
+                    + sorted(WINDOW_WORKLOADS))
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated for a cold cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget (0 disables)")
     ap.add_argument("--seed", type=int, default=0)
@@ -655,6 +790,9 @@ def main():
         return
     if args.workload in WINDOW_WORKLOADS:
         bench_window(args)
+        return
+    if args.workload == "decode_step_b64_s2":
+        bench_decode_step(args)
         return
 
     from mla_sparse_top_amd import sfa, workloads
