@@ -88,3 +88,38 @@ def test_prefill_form(sfa_lib, mode):
     inp = W.window_generate(batch=1, s1=300, n_q=16, ori_lens=[300], window=64, ratio=4, cmp_mode=mode, topk_cmp=16,
                             seed=7)
     _check(sfa_lib, inp)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+def test_pool_beyond_4gib_matches_small_pool(sfa_lib, kv_dtype):
+    """The window instantiation with 64-bit row addressing (a pool of more than 4 Mi rows): the
+    same SCFA problem with its blocks moved there, some below and some above row 4 Mi, gives the
+    bit-identical result."""
+    import torch
+
+    inp = W.window_generate(batch=2, s1=2, n_q=64, ori_lens=[3000, 1400], window=200, ratio=4, cmp_mode="sparse",
+                            topk_cmp=150, kv_dtype=kv_dtype, seed=8)
+    d = sfa_lib.window_to_device(inp)
+    ref = sfa_lib.run_window(inp, d).clone()
+    n_small = inp.num_cache_rows // 128
+    n_big = (1 << 22) // 128 + 64
+    rng = np.random.default_rng(9)
+    below = rng.choice(np.arange(1000, (1 << 22) // 128), size=n_small // 2, replace=False)
+    above = rng.choice(np.arange((1 << 22) // 128, n_big), size=n_small - n_small // 2, replace=False)
+    place = torch.from_numpy(np.concatenate([below, above]).astype(np.int64)).cuda()
+    big = dict(d)
+    for key, width in (("key_nope", 512), ("key_rope", 64), ("k_nope_scales", 4)):
+        small = d[key]
+        if small is None:
+            continue
+        t = torch.empty((n_big * 128, width), dtype=small.dtype, device="cuda")
+        t.view(n_big, 128, width)[place] = small.view(n_small, 128, width)
+        big[key] = t
+    p32 = place.to(torch.int32)
+    big["block_table_ori"] = p32[d["block_table_ori"].long()].contiguous()
+    big["block_table_cmp"] = p32[d["block_table_cmp"].long()].contiguous()
+    got = sfa_lib.run_window(inp, big)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    del big
+    torch.cuda.empty_cache()
