@@ -240,10 +240,19 @@ __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const Index
     return;
   }
   if (kCached) {  // rows are 512-byte aligned (n_pos is a multiple of 128)
+    // the keys are staged in LDS and histogrammed on their top 12 bits (the first radix digit)
+    // in the same pass
+    for (int i = tid; i < 4096; i += kSelectThreads) sh.hist[i] = 0;
+    __syncthreads();
     const float4* sc4 = reinterpret_cast<const float4*>(sc);
     for (int i = tid; i < (n + 3) / 4; i += kSelectThreads) {
       const float4 v = sc4[i];
-      reinterpret_cast<uint4*>(keys)[i] = uint4{order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w)};
+      const uint4 k4 = uint4{order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w)};
+      reinterpret_cast<uint4*>(keys)[i] = k4;
+      atomicAdd(&sh.hist[k4.x >> 20], 1u);
+      if (4 * i + 1 < n) atomicAdd(&sh.hist[k4.y >> 20], 1u);
+      if (4 * i + 2 < n) atomicAdd(&sh.hist[k4.z >> 20], 1u);
+      if (4 * i + 3 < n) atomicAdd(&sh.hist[k4.w >> 20], 1u);
     }
   }
   auto key_at = [&](int i) -> uint32_t { return kCached ? keys[i] : order_key(sc[i]); };
@@ -253,7 +262,8 @@ __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const Index
   // be taken. The keys are all n positions, or the compacted candidates (one per thread).
   uint32_t prefix = 0, mask = 0;
   int remaining = K;  // how many still to take among keys matching the prefix (<= their count)
-  auto radix_step = [&](int shift, int nb, bool from_cand, int nc) {
+  auto radix_step = [&](int shift, int nb, bool from_cand, int nc, bool counted) {
+    if (!counted) {
     for (int i = tid; i < nb; i += kSelectThreads) sh.hist[i] = 0;
     __syncthreads();
     if (from_cand) {
@@ -266,6 +276,7 @@ __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const Index
         const uint32_t key = key_at(i);
         if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
       }
+    }
     }
     __syncthreads();
     // thread tid takes digits nb-1-per*tid down to nb-per-per*tid; the inclusive scan of the
@@ -298,26 +309,27 @@ __global__ void __launch_bounds__(kSelectThreads) topk_select_kernel(const Index
   // Digit 1 (bits 31..20) over every key. When the k-th key's bin holds at most one key per
   // thread (the usual case), its keys are compacted and digits 2 and 3 (bits 19..10, 9..0) run
   // over them alone; otherwise over every key again.
-  radix_step(20, 4096, false, 0);
+  radix_step(20, 4096, false, 0, kCached);
   const bool compact = sh.bin_count <= kSelectThreads;
   __syncthreads();  // every thread has read sh before it is written again
   int nc = 0;
   if (compact) {
-    for (int i0 = 0; i0 < n; i0 += kSelectThreads) {
-      const int i = i0 + tid;
-      const bool hit = i < n && (key_at(i) & 0xfff00000u) == prefix;
-      const uint64_t m = __ballot(hit);
-      int base = 0;
-      if (lane == 0 && m) base = atomicAdd(&sh.n_cand, __popcll(m));
-      base = __shfl(base, 0);
-      if (hit) sh.cand[base + __popcll(m & ((1ull << lane) - 1))] = key_at(i);
+    // each thread's hits (positions tid, tid + 1024, ...) go to offsets from one block-wide scan
+    int hits = 0;
+    for (int i = tid; i < n; i += kSelectThreads) hits += (key_at(i) & 0xfff00000u) == prefix ? 1 : 0;
+    const int incl = block_inclusive_scan(hits, sh.scan_tmp);
+    int o = incl - hits;
+    for (int i = tid; i < n; i += kSelectThreads) {
+      const uint32_t key = key_at(i);
+      if ((key & 0xfff00000u) == prefix) sh.cand[o++] = key;
     }
+    if (tid == kSelectThreads - 1) sh.n_cand = incl;
     __syncthreads();
     nc = sh.n_cand;
   }
-  radix_step(10, 1024, compact, nc);
+  radix_step(10, 1024, compact, nc, false);
   __syncthreads();
-  radix_step(0, 1024, compact, nc);
+  radix_step(0, 1024, compact, nc, false);
   __syncthreads();
 
   // prefix is the k-th largest key; `remaining` of the keys equal to it are taken, the first
