@@ -632,3 +632,93 @@ def scfa_decode(seed: int = 0, kv_dtype: str = "bf16") -> WindowInputs:
     readings; 512 entries of ratio 4 cover 2048 original positions, the top-k of the SFA page)."""
     return window_generate(batch=64, s1=2, n_q=128, ori_lens=[8192] * 64, window=128, ratio=4, cmp_mode="sparse",
                            topk_cmp=512, kv_dtype=kv_dtype, seed=seed, name=f"scfa_b64_s2_w128_k512_{kv_dtype}")
+
+
+# ----------------------------------------------------------------------------------------
+# Compressor inputs ("NPU DeepSeek-V4 model PyPTO fused-operator optimisation", section
+# "Compressor"): the fp32 outputs of the two projections for the new tokens, the per-sequence
+# state, the gate's position embedding, the RMSNorm weight, RoPE tables, and the compressed
+# pool that receives the entries.
+# ----------------------------------------------------------------------------------------
+
+COMPRESS_CHANNELS = KV_LORA_RANK + ROPE_DIM
+
+
+@dataclasses.dataclass
+class CompressInputs:
+    batch: int
+    s1: int
+    ratio: int
+    kv: np.ndarray              # float32 (T, 576)
+    score: np.ndarray           # float32 (T, 576)
+    ape: np.ndarray             # float32 (ratio, 576)
+    gamma: np.ndarray           # float32 (576)
+    eps: float
+    rope_cos: np.ndarray        # float32 (rope_positions, 32)
+    rope_sin: np.ndarray        # float32 (rope_positions, 32)
+    start_pos: np.ndarray       # int32 (B)
+    kv_state: np.ndarray        # float32 (B, ratio, 576)
+    score_state: np.ndarray     # float32 (B, ratio, 576)
+    block_table_cmp: np.ndarray  # int32 (B, max_blocks)
+    key_nope: np.ndarray        # uint16 (rows, 512): the compressed pool's bf16 bits before the step
+    key_rope: np.ndarray        # uint16 (rows, 64)
+    name: str = ""
+
+    @property
+    def num_cache_rows(self) -> int:
+        return int(self.key_nope.shape[0])
+
+    @property
+    def rope_positions(self) -> int:
+        return int(self.rope_cos.shape[0])
+
+
+def rope_tables(n_pos: int, base: float = 10000.0):
+    """cos and sin of p * base^(-2i/64) for p < n_pos, i < 32, computed in float64 and rounded
+    to float32 (the usual rotary frequencies; the tables are inputs of the step)."""
+    inv = base ** (-np.arange(0, ROPE_DIM, 2, dtype=np.float64) / ROPE_DIM)
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def compress_generate(*, batch: int, s1: int, ratio: int, start_pos: Sequence[int], rope_positions: int,
+                      max_blocks: int, n_pool_blocks: Optional[int] = None, seed: int = 0,
+                      score_scale: float = 1.0, block_table: Optional[np.ndarray] = None,
+                      name: str = "") -> CompressInputs:
+    """kv, score, kv_state and score_state are N(0,1) float32 (scores times score_scale); ape is
+    N(0, 0.1^2); gamma is 1 + N(0, 0.1^2); eps 1e-6. Unless given, the block table is a random
+    permutation of the pool's blocks, and the pool holds random bf16 bit patterns, so a row the
+    step should not touch shows up if it changes."""
+    g = torch.Generator().manual_seed(90_000 + int(seed))
+    c = COMPRESS_CHANNELS
+    t = batch * s1
+    n_pool_blocks = batch * max_blocks if n_pool_blocks is None else int(n_pool_blocks)
+    if block_table is None:
+        assert n_pool_blocks >= batch * max_blocks
+        block_table = torch.randperm(n_pool_blocks, generator=g)[: batch * max_blocks].view(batch, max_blocks).numpy()
+    kv = torch.randn(t, c, generator=g).numpy()
+    score = (torch.randn(t, c, generator=g) * float(score_scale)).numpy()
+    ape = (torch.randn(ratio, c, generator=g) * 0.1).numpy()
+    gamma = (1.0 + torch.randn(c, generator=g) * 0.1).numpy()
+    kv_state = torch.randn(batch, ratio, c, generator=g).numpy()
+    score_state = (torch.randn(batch, ratio, c, generator=g) * float(score_scale)).numpy()
+    cos, sin = rope_tables(rope_positions)
+    rows = n_pool_blocks * BLOCK_SIZE
+    kn = torch.randint(0, 1 << 16, (rows, KV_LORA_RANK), generator=g, dtype=torch.int32).numpy().astype(np.uint16)
+    kr = torch.randint(0, 1 << 16, (rows, ROPE_DIM), generator=g, dtype=torch.int32).numpy().astype(np.uint16)
+    f32 = lambda x: np.ascontiguousarray(x, dtype=np.float32)  # noqa: E731
+    return CompressInputs(batch=batch, s1=s1, ratio=int(ratio), kv=f32(kv), score=f32(score), ape=f32(ape),
+                          gamma=f32(gamma), eps=1e-6, rope_cos=cos, rope_sin=sin,
+                          start_pos=np.ascontiguousarray(start_pos, dtype=np.int32), kv_state=f32(kv_state),
+                          score_state=f32(score_state),
+                          block_table_cmp=np.ascontiguousarray(block_table, dtype=np.int32),
+                          key_nope=kn, key_rope=kr, name=name)
+
+
+def compress_decode(seed: int = 0, ratio: int = 4) -> CompressInputs:
+    """The decode step of the page's compressor case (64 sequences, MTP 1 so two new tokens,
+    every sequence compressing): positions 8190 and 8191, so 8191 closes a window of ratio 4
+    and writes compressed entry 2047, the last of the 2048 entries the SCFA workload reads.
+    The compressed pool has 16 blocks of 128 entries per sequence."""
+    return compress_generate(batch=64, s1=2, ratio=ratio, start_pos=[8190] * 64, rope_positions=8192,
+                             max_blocks=2048 // BLOCK_SIZE, seed=seed, name=f"compress_b64_s2_r{ratio}")
