@@ -302,6 +302,63 @@ int sfa_indexer_scores(const sfa_indexer_dims* dims, const void* q_index, const 
 int sfa_topk_select(const sfa_indexer_dims* dims, const float* scores, const int32_t* kv_act_seqs,
                     int32_t* topk_indices, hipStream_t stream);
 
+/*
+ * ---- Compressor: the step that fills the compressed cache the window attention reads ----
+ *
+ * "NPU DeepSeek-V4 model PyPTO fused-operator optimisation", section "Compressor", its
+ * computation steps. The two projections of the new tokens' hidden states (plain GEMMs, done
+ * by the caller) arrive as kv and score. Token t = b*s1 + s at position p = start_pos[b] + s,
+ * taken in order of s, refreshes slot p % ratio of its sequence's state:
+ *     kv_state[b][slot] = kv[t]        score_state[b][slot] = score[t] + ape[slot]   (fp32 add)
+ * When p + 1 is a multiple of ratio, the state is pooled into compressed entry
+ * c = (p + 1) / ratio - 1:
+ *     x[ch] = sum over slots r of softmax_r(score_state[b][r][ch]) * kv_state[b][r][ch]
+ *     y     = x / sqrt(mean over the 576 channels of x^2 + eps) * gamma
+ *     y[512 + 2i], y[513 + 2i]  rotated by the angle with cosine rope_cos[p][i] and sine
+ *                               rope_sin[p][i] (i < 32; adjacent pairs)
+ * and y is stored as bf16 (round to nearest even): channels 0..511 to key_nope_2d and 512..575
+ * to key_rope_2d, at row block_table_cmp[b][c / 128] * 128 + c % 128 (the row layout of the
+ * cache sfa_window_decode reads). The page's rotate = true branch (a Hadamard transform) is not
+ * provided. The softmax, sum, norm and rotation are fp32.
+ *
+ *   dims              channels must be 576, block_size 128; ratio in [1, 1024]; T = batch*s1
+ *                     up to 2^26; max_blocks = row length of block_table_cmp
+ *   kv, score         fp32  (T, 576)
+ *   ape               fp32  (ratio, 576)      added to the score of the slot it is indexed by
+ *   gamma             fp32  (576)
+ *   eps               finite, >= 0
+ *   rope_cos/sin      fp32  (rope_positions, 32)
+ *   start_pos         int32 (batch)
+ *   kv_state,
+ *   score_state       fp32  (batch, ratio, 576), read and refreshed in place
+ *   block_table_cmp   int32 (batch, max_blocks)
+ *   key_nope_2d       bf16  (num_cache_rows, 512)   written in place
+ *   key_rope_2d       bf16  (num_cache_rows, 64)    written in place
+ *
+ * With batch * s1 = 0 the call reads nothing and returns SFA_OK (the pointers may then be NULL).
+ * A token with p < 0 or p >= rope_positions is skipped (no refresh, no entry). An entry is not
+ * written when c >= max_blocks * 128, its block entry is negative, or its row is outside
+ * [0, num_cache_rows); the state is still refreshed. Precondition, not checked: the inputs are
+ * finite. Errors: SFA_ERR_NULL, SFA_ERR_DIMS, SFA_ERR_ALIGN (any pointer not 16-byte aligned),
+ * SFA_ERR_ALIAS (an output overlaps an input or another output), SFA_ERR_HIP. Asynchronous on
+ * `stream`, no allocation.
+ */
+typedef struct {
+  int32_t batch;
+  int32_t s1;                   /* new tokens per sequence                                      */
+  int32_t channels;             /* must be 576 (kv_lora_rank + rope_dim)                        */
+  int32_t ratio;                /* compression ratio                                            */
+  int32_t rope_positions;       /* rows of rope_cos and rope_sin                                */
+  int32_t max_blocks;           /* row length of block_table_cmp                                */
+  int32_t block_size;           /* must be 128                                                  */
+  int64_t num_cache_rows;       /* rows of the compressed pool                                  */
+} sfa_compress_dims;
+
+int sfa_compress(const sfa_compress_dims* dims, const float* kv, const float* score, const float* ape,
+                 const float* gamma, float eps, const float* rope_cos, const float* rope_sin,
+                 const int32_t* start_pos, float* kv_state, float* score_state, const int32_t* block_table_cmp,
+                 void* key_nope_2d, void* key_rope_2d, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -108,9 +108,28 @@ _lib.sfa_window_decode.argtypes = [ctypes.POINTER(SfaWindowDims), _vp, _vp, _vp,
                                    ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.sfa_window_decode.restype = ctypes.c_int
 
+
+
+class SfaCompressDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("s1", ctypes.c_int32),
+        ("channels", ctypes.c_int32),
+        ("ratio", ctypes.c_int32),
+        ("rope_positions", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_cache_rows", ctypes.c_int64),
+    ]
+
+
+_lib.sfa_compress.argtypes = [ctypes.POINTER(SfaCompressDims), _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                              _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.sfa_compress.restype = ctypes.c_int
+
 EXPORTED_SYMBOLS = ("sfa_workspace_size", "sfa_num_splits", "sfa_decode", "sfa_prefill", "sfa_resolve_rows",
                     "sfa_status_string", "sfa_indexer_scores", "sfa_topk_select", "sfa_cache_write",
-                    "sfa_window_workspace_size", "sfa_window_decode")
+                    "sfa_window_workspace_size", "sfa_window_decode", "sfa_compress")
 
 
 class SfaError(RuntimeError):
@@ -649,3 +668,91 @@ def run_indexer(inp, dev_tensors=None):
                         batch=inp.batch, s1=inp.s1, topk=inp.topk)
     idx = topk_select(sc, d["kv_act_seqs"], batch=inp.batch, s1=inp.s1, topk=inp.topk)
     return sc, idx
+
+
+# ---- compressor -------------------------------------------------------------------------
+
+COMPRESS_CHANNELS = KV_LORA_RANK + ROPE_DIM
+
+
+def _marshal_compress(kv, score, ape, gamma, eps, rope_cos, rope_sin, start_pos, kv_state, score_state,
+                      block_table_cmp, key_nope, key_rope, *, batch, s1, stream=None):
+    dev = kv.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    t_tokens = batch * s1
+    c = COMPRESS_CHANNELS
+    ratio = ape.shape[0]
+    n_pos = rope_cos.shape[0]
+    rows = key_rope.shape[0]
+    f32 = (torch.float32,)
+    _check(kv, "kv", f32, (t_tokens, c), dev)
+    _check(score, "score", f32, (t_tokens, c), dev)
+    _check(ape, "ape", f32, (ratio, c), dev)
+    _check(gamma, "gamma", f32, (c,), dev)
+    _check(rope_cos, "rope_cos", f32, (n_pos, ROPE_DIM // 2), dev)
+    _check(rope_sin, "rope_sin", f32, (n_pos, ROPE_DIM // 2), dev)
+    _check(start_pos, "start_pos", (torch.int32,), (batch,), dev)
+    _check(kv_state, "kv_state", f32, (batch, ratio, c), dev)
+    _check(score_state, "score_state", f32, (batch, ratio, c), dev)
+    _check(block_table_cmp, "block_table_cmp", (torch.int32,), None, dev)
+    if block_table_cmp.dim() != 2 or block_table_cmp.shape[0] != batch:
+        raise ValueError("block_table_cmp must be (batch, max_blocks)")
+    _check(key_nope, "key_nope", (torch.bfloat16,), (rows, KV_LORA_RANK), dev)
+    _check(key_rope, "key_rope", (torch.bfloat16,), (rows, ROPE_DIM), dev)
+    dims = SfaCompressDims(batch=batch, s1=s1, channels=c, ratio=ratio, rope_positions=n_pos,
+                           max_blocks=block_table_cmp.shape[1], block_size=BLOCK_SIZE, num_cache_rows=rows)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    args = (ctypes.byref(dims), _ptr(kv), _ptr(score), _ptr(ape), _ptr(gamma), ctypes.c_float(eps), _ptr(rope_cos),
+            _ptr(rope_sin), _ptr(start_pos), _ptr(kv_state), _ptr(score_state), _ptr(block_table_cmp),
+            _ptr(key_nope), _ptr(key_rope), ctypes.c_void_p(stream.cuda_stream))
+    keep = (dims, kv, score, ape, gamma, rope_cos, rope_sin, start_pos, kv_state, score_state, block_table_cmp,
+            key_nope, key_rope, stream)
+    return args, keep
+
+
+def compress(kv, score, ape, gamma, eps, rope_cos, rope_sin, start_pos, kv_state, score_state, block_table_cmp,
+             key_nope, key_rope, *, batch, s1, stream=None):
+    """sfa_compress: refreshes kv_state / score_state in place and writes the compressed entries
+    of the windows the new tokens close into key_nope / key_rope. Returns key_nope."""
+    args, _keep = _marshal_compress(kv, score, ape, gamma, eps, rope_cos, rope_sin, start_pos, kv_state, score_state,
+                                    block_table_cmp, key_nope, key_rope, batch=batch, s1=s1, stream=stream)
+    st = _lib.sfa_compress(*args)
+    if st != 0:
+        raise SfaError(st, "sfa_compress")
+    return key_nope
+
+
+def compress_to_device(inp, device="cuda"):
+    """Upload a workloads.CompressInputs instance (state and pool tensors are fresh copies)."""
+    import numpy as np
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    return {"kv": t(inp.kv), "score": t(inp.score), "ape": t(inp.ape), "gamma": t(inp.gamma),
+            "rope_cos": t(inp.rope_cos), "rope_sin": t(inp.rope_sin), "start_pos": t(inp.start_pos),
+            "kv_state": t(inp.kv_state), "score_state": t(inp.score_state),
+            "block_table_cmp": t(inp.block_table_cmp), "key_nope": bf16(inp.key_nope), "key_rope": bf16(inp.key_rope)}
+
+
+def _compress_tensors(d):
+    return (d["kv"], d["score"], d["ape"], d["gamma"])
+
+
+def run_compress(inp, d):
+    """sfa_compress on an uploaded CompressInputs instance (updates d's state and pool tensors)."""
+    return compress(*_compress_tensors(d), inp.eps, d["rope_cos"], d["rope_sin"], d["start_pos"], d["kv_state"],
+                    d["score_state"], d["block_table_cmp"], d["key_nope"], d["key_rope"], batch=inp.batch, s1=inp.s1)
+
+
+def prepare_compress(inp, d, stream=None) -> PreparedCall:
+    """sfa_compress bound to an uploaded CompressInputs instance (a PreparedCall returning key_nope)."""
+    args, keep = _marshal_compress(*_compress_tensors(d), inp.eps, d["rope_cos"], d["rope_sin"], d["start_pos"],
+                                   d["kv_state"], d["score_state"], d["block_table_cmp"], d["key_nope"],
+                                   d["key_rope"], batch=inp.batch, s1=inp.s1, stream=stream)
+    return PreparedCall([(_lib.sfa_compress, args, "sfa_compress")], d["key_nope"], keep)

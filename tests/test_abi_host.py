@@ -295,3 +295,42 @@ def test_window_validation():
     assert _wcall(_wdims(block_size=64)) == -2               # the attention's own dims are checked too
     assert _wcall(_wdims(window=40000)) == -2                # above the attention's top-k limit
     assert _wcall(_wdims(batch=0, num_splits=2), ws_bytes=need) == 0  # nothing to do, nothing queued
+
+
+def _cdims(**kw):
+    base = dict(batch=2, s1=2, channels=576, ratio=4, rope_positions=64, max_blocks=2, block_size=128,
+                num_cache_rows=512)
+    base.update(kw)
+    return sfa.SfaCompressDims(**base)
+
+
+def _cmp(dims, eps=1e-6, **kw):
+    """sfa_compress with fake, well-separated device addresses; every case here fails validation
+    (or has nothing to do), so nothing is launched."""
+    p = dict(kv=0x1000000, sc=0x2000000, ape=0x3000000, g=0x3100000, cos=0x3200000, sin=0x3300000, sp=0x3400000,
+             ks=0x4000000, ss=0x5000000, bt=0x6000000, kn=0x10000000, kr=0x20000000)
+    p.update(kw)
+    vp = lambda x: ctypes.c_void_p(x)  # noqa: E731
+    return sfa._lib.sfa_compress(ctypes.byref(dims), vp(p["kv"]), vp(p["sc"]), vp(p["ape"]), vp(p["g"]),
+                                 ctypes.c_float(eps), vp(p["cos"]), vp(p["sin"]), vp(p["sp"]), vp(p["ks"]),
+                                 vp(p["ss"]), vp(p["bt"]), vp(p["kn"]), vp(p["kr"]), None)
+
+
+def test_compress_validation():
+    d = _cdims()
+    for name in ("kv", "sc", "ape", "g", "cos", "sin", "sp", "ks", "ss", "bt", "kn", "kr"):
+        assert _cmp(d, **{name: None}) == -1, name
+    assert _cmp(d, sp=0x3400004) == -3                   # misaligned
+    assert _cmp(d, kr=0x20000008) == -3
+    assert _cmp(d, ks=0x1000000 + 4096) == -6            # state overlaps kv
+    assert _cmp(d, ss=0x4000000 + 16) == -6              # score state inside kv state
+    assert _cmp(d, kn=0x3400000) == -6                   # pool over start_pos
+    assert _cmp(d, kr=0x10000000 + 1024) == -6           # rope rows inside nope rows
+    for field, value in (("channels", 512), ("block_size", 64), ("ratio", 0), ("ratio", 1025), ("batch", -1),
+                         ("s1", -1), ("max_blocks", 0), ("rope_positions", -1), ("num_cache_rows", -1)):
+        assert _cmp(_cdims(**{field: value})) == -2, field
+    assert _cmp(d, eps=-1.0) == -2
+    assert _cmp(d, eps=float("nan")) == -2
+    assert _cmp(d, eps=float("inf")) == -2
+    assert _cmp(_cdims(batch=0)) == 0                    # nothing to do: no HIP call
+    assert _cmp(_cdims(s1=0)) == 0

@@ -1,0 +1,130 @@
+"""GPU parity of the compressor (sfa_compress) against the CPU oracle (oracle/compress_oracle.py).
+
+The refreshed state is a copy plus one fp32 addition, so it must be bit-exact. Each compressed
+row is fp32 arithmetic (softmax over the slots, sum, RMS, rotation) rounded once to bf16; the
+oracle is float64. The bar is the attention's: |gpu - ref| <= 1e-4 + 5e-3 * |ref| for every
+element (a bf16 rounding moves a value by at most 2^-8 of itself, under the 5e-3 bound, and the
+fp32 arithmetic adds ~1e-6). Every pool row no entry targets must be unchanged, bit for bit. The
+full-size case is the benchmark's workload in the same launch configuration.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.compress_oracle as C
+import oracle.sfa_oracle as O
+from mla_sparse_top_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(sfa_lib, inp, d=None):
+    import torch
+
+    d = sfa_lib.compress_to_device(inp) if d is None else d
+    sfa_lib.run_compress(inp, d)
+    torch.cuda.synchronize()
+    return d
+
+
+def _host(d):
+    import torch
+
+    bits = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    return d["kv_state"].cpu().numpy(), d["score_state"].cpu().numpy(), bits(d["key_nope"]), bits(d["key_rope"])
+
+
+def _assert_matches(inp, got, want=None, pool=None):
+    ks, ss, kn, kr = got
+    wks, wss, entries = C.compress(inp) if want is None else want
+    np.testing.assert_array_equal(ks.view(np.uint32), wks.view(np.uint32))
+    np.testing.assert_array_equal(ss.view(np.uint32), wss.view(np.uint32))
+    base_n, base_r = (inp.key_nope, inp.key_rope) if pool is None else pool
+    written = {}
+    for b, c, row, y in entries:
+        if row >= 0:
+            written[row] = (b, c, y)
+    untouched = np.ones(kn.shape[0], dtype=bool)
+    untouched[list(written)] = False
+    np.testing.assert_array_equal(kn[untouched], base_n[untouched])
+    np.testing.assert_array_equal(kr[untouched], base_r[untouched])
+    for row, (b, c, y) in written.items():
+        g = np.concatenate([O.bf16_bits_to_f64(kn[row]), O.bf16_bits_to_f64(kr[row])])
+        err = np.abs(g - y)
+        bound = 1e-4 + 5e-3 * np.abs(y)
+        bad = np.nonzero(err > bound)[0]
+        assert bad.size == 0, (f"entry (b={b}, c={c}) row {row}: {bad.size} channels off, first {bad[:4]}, "
+                               f"worst ratio {np.max(err / bound):.3f}")
+    return len(written)
+
+
+def test_decode_workload_full_size(sfa_lib):
+    """64 sequences, two new tokens each, ratio 4: every sequence closes a window (entry 2047)."""
+    inp = W.compress_decode(seed=0)
+    n = _assert_matches(inp, _host(_run(sfa_lib, inp)))
+    assert n == 64
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_decode_workload_seeds(sfa_lib, seed):
+    inp = W.compress_decode(seed=seed)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 64
+
+
+def test_ratio_128_peaky_scores(sfa_lib):
+    """A long window (128 slots, the loop over slots with no unrolled tail) and scores spread
+    wide enough that a few slots carry each channel."""
+    inp = W.compress_generate(batch=8, s1=1, ratio=128, start_pos=[127 + 128 * k for k in range(8)],
+                              rope_positions=2048, max_blocks=2, seed=3, score_scale=4.0)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 8
+
+
+def test_tokens_span_two_windows(sfa_lib):
+    """Seven tokens at ratio 4 (positions 5..11): two entries in one call, the second pooling
+    slots refreshed earlier in the same call; every slot is refreshed and the last writer wins."""
+    inp = W.compress_generate(batch=3, s1=7, ratio=4, start_pos=[5, 5, 5], rope_positions=64, max_blocks=2, seed=4)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 6
+
+
+def test_ratio_one_every_token_emits(sfa_lib):
+    inp = W.compress_generate(batch=4, s1=3, ratio=1, start_pos=[0, 10, 100, 250], rope_positions=256,
+                              max_blocks=2, seed=5)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 12
+
+
+def test_ragged_positions_and_unwritable_entries(sfa_lib):
+    """Mixed start positions: before position 0, past the RoPE tables, an entry whose block is
+    negative, an entry past the block table, and an entry whose row is past the pool."""
+    starts = [-3, 60, 6, 6, 1021, 6]
+    inp = W.compress_generate(batch=6, s1=4, ratio=2, start_pos=starts, rope_positions=64, max_blocks=2,
+                              n_pool_blocks=12, seed=6)
+    inp.block_table_cmp[2, 0] = -1                 # sequence 2: its entries (3, 4) sit in block 0
+    inp.rope_cos = W.rope_tables(1024)[0]          # sequence 4 reaches entry 511, past the table
+    inp.rope_sin = W.rope_tables(1024)[1]
+    inp.block_table_cmp[5, 0] = 12                 # a row past the 12-block pool
+    n = _assert_matches(inp, _host(_run(sfa_lib, inp)))
+    assert n == 2 + 2         # sequences 1 (61 and 63 close) and 3; 0 closes none; 2, 4, 5 write none
+
+
+def test_state_carries_across_calls(sfa_lib):
+    """Two calls in a row, the second reading the state the first refreshed."""
+    inp = W.compress_generate(batch=4, s1=3, ratio=4, start_pos=[4] * 4, rope_positions=64, max_blocks=2, seed=7)
+    d = _run(sfa_lib, inp)
+    ks1, ss1, e1 = C.compress(inp)
+    got1 = _host(d)
+    _assert_matches(inp, got1, (ks1, ss1, e1))
+    nxt = W.compress_generate(batch=4, s1=3, ratio=4, start_pos=[7] * 4, rope_positions=64, max_blocks=2, seed=8)
+    nxt.kv_state, nxt.score_state = ks1, ss1
+    nxt.block_table_cmp, nxt.ape, nxt.gamma = inp.block_table_cmp, inp.ape, inp.gamma
+    for k in ("kv", "score"):
+        d[k].copy_(sfa_lib.compress_to_device(nxt)[k])
+    d["start_pos"].fill_(7)
+    got2 = _host(_run(sfa_lib, nxt, d))
+    _assert_matches(nxt, got2, pool=(got1[2], got1[3]))
+
+
+def test_no_tokens_is_a_no_op(sfa_lib):
+    inp = W.compress_generate(batch=2, s1=0, ratio=4, start_pos=[3, 3], rope_positions=64, max_blocks=2, seed=9)
+    got = _host(_run(sfa_lib, inp))
+    np.testing.assert_array_equal(got[0], inp.kv_state)
+    np.testing.assert_array_equal(got[2], inp.key_nope)
