@@ -128,3 +128,34 @@ def test_no_tokens_is_a_no_op(sfa_lib):
     got = _host(_run(sfa_lib, inp))
     np.testing.assert_array_equal(got[0], inp.kv_state)
     np.testing.assert_array_equal(got[2], inp.key_nope)
+
+
+def test_compressed_entry_feeds_scfa(sfa_lib):
+    """One SCFA decode step after the compressor, on one shared pool: each sequence's second new
+    token closes a window, the compressor writes that newest compressed entry, and the token's
+    compressed list names it. The rows match the compressor oracle (and every other pool row is
+    unchanged); the attention over the pool the GPU wrote matches the window oracle."""
+    import torch
+
+    import oracle.window_oracle as WO
+
+    ratio = 4
+    win = W.window_generate(batch=2, s1=2, n_q=32, ori_lens=[512, 300], window=64, ratio=ratio, cmp_mode="sparse",
+                            topk_cmp=24, seed=11)
+    for b in range(win.batch):
+        win.cmp_indices[b * win.s1 + 1, 0] = int(win.cmp_len[b]) - 1   # closed by position ori_len - 1
+    cmp = W.compress_generate(batch=2, s1=2, ratio=ratio, start_pos=[int(v) - 2 for v in win.ori_len],
+                              rope_positions=1024, max_blocks=win.block_table_cmp.shape[1], seed=12)
+    cmp.block_table_cmp, cmp.key_nope, cmp.key_rope = win.block_table_cmp, win.key_nope, win.key_rope
+    dw = sfa_lib.window_to_device(win)
+    dc = sfa_lib.compress_to_device(cmp)
+    dc["key_nope"], dc["key_rope"] = dw["key_nope"], dw["key_rope"]
+    sfa_lib.run_compress(cmp, dc)
+    out = sfa_lib.run_window(win, dw)
+    torch.cuda.synchronize()
+    got = _host(dc)
+    assert _assert_matches(cmp, got) == 2
+    win.key_nope, win.key_rope = got[2], got[3]
+    ref = WO.window_attention(win)
+    rep = O.allclose_report(out.float().cpu().numpy().astype(np.float64).reshape(ref.shape), ref)
+    assert rep["fails"] == 0, rep
