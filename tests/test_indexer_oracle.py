@@ -9,6 +9,7 @@ planted wrong selections. Planted mistakes in copies of the oracle must each fai
 """
 
 import math
+import struct
 
 import numpy as np
 import pytest
@@ -22,6 +23,18 @@ def _small(seed=0, act=(300, 77), s1=2, heads=3, dim=8, topk=50, extra=2):
                               head_dim=dim, max_blocks_per_batch=3, extra_pool_blocks=extra)
 
 
+def _bf16_scalar(bits) -> float:
+    """bf16 bits to a Python float through struct: an independent route from the oracle's
+    numpy bit shift (the four bytes of the binary32 pattern hi:lo:0:0, big-endian)."""
+    b = int(bits) & 0xFFFF
+    return struct.unpack(">f", bytes([b >> 8, b & 0xFF, 0, 0]))[0]
+
+
+def _bf16_array(bits) -> np.ndarray:
+    flat = np.asarray(bits).reshape(-1)
+    return np.array([_bf16_scalar(x) for x in flat], dtype=np.float64).reshape(np.shape(bits))
+
+
 def _scores(inp, fn=None):
     fn = fn or IO.indexer_scores
     T = inp.n_tokens
@@ -33,8 +46,8 @@ def test_scores_match_scalar_brute_force():
     inp = _small(seed=1)
     got = _scores(inp)
     T, H, D = inp.n_tokens, inp.n_heads, inp.head_dim
-    q = IO.bf16_bits_to_f64(inp.q_index).reshape(T, H, D)
-    k = IO.bf16_bits_to_f64(inp.k_index)
+    q = _bf16_array(inp.q_index).reshape(T, H, D)
+    k = _bf16_array(inp.k_index)
     for t in range(T):
         b = t // inp.s1
         for j in range(0, inp.n_positions, 7):
@@ -60,10 +73,46 @@ def test_closed_forms_self_and_negated_key():
     q = np.repeat(inp.k_index[row][None, :], T, axis=0)
     inp.q_index = q
     inp.weights = np.ones((T, 1), dtype=np.float32)
-    kj = IO.bf16_bits_to_f64(inp.k_index[row])
+    kj = _bf16_array(inp.k_index[row])
     assert _scores(inp)[0, j] == pytest.approx(float(kj @ kj), rel=1e-15)
     inp.q_index = q ^ np.uint16(0x8000)  # flip every sign bit: q = -k_j
     assert _scores(inp)[0, j] == 0.0
+
+
+# bf16 is the upper half of an IEEE binary32 (sign, 8 exponent bits with bias 127, 7 stored
+# fraction bits); each value below is worked out by hand from that definition.
+_BF16_CASES = [
+    (0x0000, 0.0), (0x3F80, 1.0), (0xBF80, -1.0), (0x4000, 2.0), (0x3FC0, 1.5), (0x3F00, 0.5),
+    (0x4049, 3.140625),                              # 2 * (1 + 73/128)
+    (0xC2F7, -123.5),                                # -(2^6) * (1 + 119/128)
+    (0x0080, math.ldexp(1.0, -126)),                 # smallest normal
+    (0x0001, math.ldexp(1.0, -133)),                 # smallest subnormal: 2^-126 * 2^-7
+    (0x007F, math.ldexp(127.0, -133)),               # largest subnormal
+    (0x7F7F, math.ldexp(255.0, 120)),                # largest finite: 2^127 * (1 + 127/128)
+    (0x7F80, math.inf), (0xFF80, -math.inf),
+]
+
+
+@pytest.mark.parametrize("bits,value", _BF16_CASES)
+def test_bf16_bits_to_f64_hand_worked(bits, value):
+    got = IO.bf16_bits_to_f64(np.array([bits], dtype=np.uint16))
+    assert got.dtype == np.float64 and got[0] == value
+
+
+def test_bf16_bits_to_f64_sign_zero_and_nan():
+    got = IO.bf16_bits_to_f64(np.array([0x8000, 0x7FC0, 0xFFC1], dtype=np.uint16))
+    assert got[0] == 0.0 and math.copysign(1.0, got[0]) == -1.0
+    assert np.isnan(got[1]) and np.isnan(got[2])
+
+
+def test_bf16_bits_to_f64_every_pattern_matches_struct_route():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = IO.bf16_bits_to_f64(bits)
+    want = np.array(struct.unpack(">65536f", b"".join(bytes([b >> 8, b & 0xFF, 0, 0]) for b in range(65536))))
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
 
 
 def test_one_hot_weights_select_a_head():
@@ -183,6 +232,38 @@ def _inclusive_bound(q_bits, w, k_bits, bt, act, s1, n):
         if a < n:
             out[t, a] = 0.0
     return out
+
+
+_real_decode = IO.bf16_bits_to_f64
+
+
+def _decode_shift_15(bits):
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def _decode_drops_sign(bits):
+    return np.abs(_real_decode(bits))
+
+
+def _decode_byte_swapped(bits):
+    return _real_decode(np.asarray(bits, dtype=np.uint16).byteswap())
+
+
+@pytest.mark.parametrize("mutant", [_decode_shift_15, _decode_drops_sign, _decode_byte_swapped])
+def test_pins_catch_planted_decode_mistakes(mutant, monkeypatch):
+    monkeypatch.setattr(IO, "bf16_bits_to_f64", mutant)
+    pins = [test_scores_match_scalar_brute_force, test_closed_forms_self_and_negated_key,
+            test_bf16_bits_to_f64_every_pattern_matches_struct_route,
+            lambda: [test_bf16_bits_to_f64_hand_worked(b, v) for b, v in _BF16_CASES]]
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    # the score pins see the mutant through the oracle's own use of the decode
+    assert caught >= 2, mutant.__name__
 
 
 @pytest.mark.parametrize("mutant", [_relu_after_weight, _no_relu, _swapped_block_math, _inclusive_bound])
