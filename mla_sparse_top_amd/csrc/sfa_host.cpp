@@ -19,8 +19,6 @@ constexpr size_t kAlignWs = 256;
 constexpr int kTargetWorkgroups = 256;
 constexpr int kMaxAutoSplits = 8;
 
-int head_groups(const sfa_dims* d) { return (d->n_q + kHeadsPerGroup - 1) / kHeadsPerGroup; }
-
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -51,9 +49,8 @@ int pick_splits(const sfa_dims* d, int is_prefill) {
   } else {
     // Enough (token, partition) work items to give every CU one, but at least 64 slots (two
     // tiles) per partition and at most kMaxAutoSplits partitions: the last arriver reads every
-    // partition's 128 KB partial, and beyond 8 of them that costs more than the shorter
-    // partitions save (measured at topk 2048, 1 to 16 tokens).
-    const int64_t items = tokens * head_groups(d);
+    // partition's 256 KB partial.
+    const int64_t items = tokens;
     const int64_t want = items > 0 ? (kTargetWorkgroups + items - 1) / items : 1;
     s = (int)(want < kMaxAutoSplits ? want : kMaxAutoSplits);
     const int by_len = d->topk / 64 > 0 ? d->topk / 64 : 1;
@@ -71,7 +68,7 @@ struct WsLayout {
 WsLayout ws_layout(const sfa_dims* d, int splits) {
   WsLayout w{0, 0, 0, 0};
   if (splits <= 1) return w;
-  const size_t groups = (size_t)d->batch * d->s1 * head_groups(d);
+  const size_t groups = (size_t)d->batch * d->s1;
   const size_t items = groups * splits;
   w.part_o = 0;
   w.part_ml = align_up(items * kPartialBytes, kAlignWs);
@@ -166,7 +163,6 @@ int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void*
   a.n_splits = splits;
   a.chunk = (d->topk + splits - 1) / splits;
   a.reverse = is_prefill ? 1 : 0;
-  a.head_groups = head_groups(d);
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);  // log2(e)
   if (win) {
     a.window = win->window;

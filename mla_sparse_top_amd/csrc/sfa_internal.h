@@ -12,17 +12,17 @@ constexpr int kNope = 512;          // kv_lora_rank
 constexpr int kRope = 64;           // qk_rope_dim
 constexpr int kBlock = 128;         // rows per cache page
 constexpr int kTile = 32;           // top-k slots per inner tile
-constexpr int kWaves = 4;           // waves per workgroup: two pairs, each pair owns 32 heads
+constexpr int kWaves = 4;           // waves per workgroup, one per SIMD
 constexpr int kThreads = kWaves * 64;
-constexpr int kHeadsPerPair = 32;
-constexpr int kHeadsPerGroup = 2 * kHeadsPerPair;  // heads of one workgroup (64)
+constexpr int kHeadsPerWave = 32;   // each wave owns 32 heads over the whole 576-wide d
+constexpr int kMaxHeads = kWaves * kHeadsPerWave;  // one workgroup covers every head of a token
 constexpr int kMaxSlots = 2048;     // slots one workgroup compacts (topk partition size cap)
 constexpr int kMaxSplits = 16;      // top-k partitions per token
 constexpr int kMaxTopk = kMaxSlots * kMaxSplits;
-// Partial output of one (token, partition, head group), the register image of the O^T
-// accumulators: 4 waves x 8 blocks of 32 columns x 4 row quads x 64 lanes x float4
-constexpr size_t kPartialBytes = (size_t)kWaves * 8 * 4 * 64 * 16;
-constexpr size_t kPartialMlBytes = kHeadsPerGroup * 2 * sizeof(float);
+// Partial output of one (token, partition): the register image of the O^T accumulators,
+// 4 waves x 16 blocks of 32 columns x 4 row quads x 64 lanes x float4 (256 KB)
+constexpr size_t kPartialBytes = (size_t)kWaves * 16 * 4 * 64 * 16;
+constexpr size_t kPartialMlBytes = kMaxHeads * 2 * sizeof(float);
 
 struct KernelArgs {
   const uint16_t* q_nope;     // bf16 bits (T*n_q, 512)
@@ -34,11 +34,11 @@ struct KernelArgs {
   const int32_t* block_table; // (batch, mb)
   const int32_t* act;         // (batch)
   uint16_t* out;              // bf16 bits (T, n_q, 512)
-  float* part_o;              // (T, head_groups, splits) x kPartialBytes
-  float* part_ml;             // (T, head_groups, splits, 64, 2)
-  int32_t* counters;          // (T, head_groups)
+  float* part_o;              // (T, splits) x kPartialBytes
+  float* part_ml;             // (T, splits, 128, 2): running max and sum per head
+  int32_t* counters;          // (T): arrivals of the token's partitions
   int64_t num_rows;
-  int32_t n_tokens, s1, n_q, topk, mb, n_splits, chunk, reverse, head_groups;
+  int32_t n_tokens, s1, n_q, topk, mb, n_splits, chunk, reverse;
   float scale_log2;           // softmax_scale * log2(e)
   // Window variants (the kernel instantiated with its window flag): slot g < window of token
   // t = b*s1 + s is original-cache position act[b] - s1 + s - window + 1 + g, through

@@ -47,11 +47,12 @@ def _dims(**kw):
 
 
 def test_partition_choice():
-    # 64 x 2 tokens x 2 head groups already fill 256 CUs: no top-k partitioning
-    assert sfa.num_splits(_dims()) == 1
-    assert sfa.workspace_size(_dims()) == 0
-    # 32 single-token batches x 2 head groups: 4 partitions
-    assert sfa.num_splits(_dims(batch=32, s1=1)) == 4
+    # one workgroup per (token, partition): 64 x 2 tokens need 2 partitions to fill 256 CUs
+    assert sfa.num_splits(_dims()) == 2
+    # 32 single-token batches: 8 partitions
+    assert sfa.num_splits(_dims(batch=32, s1=1)) == 8
+    # 256 tokens or more already fill the CUs
+    assert sfa.num_splits(_dims(batch=128, s1=2)) == 1
     # one token of 16 heads, 64 slots: partitions need >= 64 slots each
     assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=64)) == 1
     # at most 8 partitions unless topk needs more
@@ -67,17 +68,18 @@ def test_partition_choice():
 
 
 def test_workspace_size_formula():
-    d = _dims(batch=32, s1=1)  # 4 partitions, 2 head groups
-    groups = 32 * 2
-    items = groups * 4
-    part = items * 4 * 32 * 64 * 16
-    ml = items * 64 * 2 * 4
-    cnt = groups * 4
+    d = _dims(batch=32, s1=1)  # 8 partitions
+    tokens = 32
+    items = tokens * 8
+    part = items * 4 * 16 * 4 * 64 * 16   # 4 waves x 16 column blocks x 4 row quads x 64 lanes x float4
+    ml = items * 128 * 2 * 4              # (max, sum) per head
+    cnt = tokens * 4
 
     def up(x):
         return (x + 255) // 256 * 256
 
     assert sfa.workspace_size(d) == up(part) + up(ml) + up(cnt)
+    assert sfa.workspace_size(_dims(batch=128, s1=2)) == 0
 
 
 @pytest.mark.parametrize("field,value", [
