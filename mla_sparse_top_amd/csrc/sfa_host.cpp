@@ -73,7 +73,7 @@ WsLayout ws_layout(const sfa_dims* d, int splits) {
   w.part_o = 0;
   w.part_ml = align_up(items * kPartialBytes, kAlignWs);
   w.counters = w.part_ml + align_up(items * kPartialMlBytes, kAlignWs);
-  w.total = w.counters + align_up(groups * sizeof(int32_t), kAlignWs);
+  w.total = w.counters + align_up(2 * groups * sizeof(int32_t), kAlignWs);
   return w;
 }
 

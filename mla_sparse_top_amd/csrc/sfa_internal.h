@@ -36,7 +36,7 @@ struct KernelArgs {
   uint16_t* out;              // bf16 bits (T, n_q, 512)
   float* part_o;              // (T, splits) x kPartialBytes
   float* part_ml;             // (T, splits, 128, 2): running max and sum per head
-  int32_t* counters;          // (T): arrivals of the token's partitions
+  int32_t* counters;          // (2, T): arrivals, then partials published, per token
   int64_t num_rows;
   int32_t n_tokens, s1, n_q, topk, mb, n_splits, chunk, reverse;
   float scale_log2;           // softmax_scale * log2(e)

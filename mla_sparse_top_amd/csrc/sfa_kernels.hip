@@ -88,9 +88,12 @@ constexpr int kCodeTileBytes = kTile * kNope;        // 16 KB
 constexpr int kCodeBufBytes = kCodeTileBytes + kWaves * 256;
 constexpr float kRescaleThreshold = 8.0f;           // log2 units: p stays <= 256 between rescales
 constexpr int kQkSteps = (kNope + kRope) / 16;      // 36 k-steps of 16 over the 576 columns
-constexpr int kQkDepth = 6;                         // LDS operand loads in flight ahead of the MFMA
-constexpr int kPvDepth = 4;
+constexpr int kQkDepth = 4;                         // LDS operand loads in flight ahead of the MFMA
+constexpr int kPvDepth = 3;
 constexpr int kOutWaveBytes = kHeadsPerWave * kNopeRowBytes;  // a wave's bf16 output rows (32 KB)
+// Bound on the last arriver's wait for the other partitions' partials (each try sleeps ~128
+// clocks): far beyond the time a partial takes to be stored.
+constexpr int kSpinLimit = 1 << 24;
 
 template <bool kInt8>
 struct Lds {
@@ -145,6 +148,23 @@ __device__ __forceinline__ void dma_rows4(const u32x4& rsrc, int r0, int r1, int
       : "=&s"(saved), "=&s"(o0), "=&s"(o1), "=&s"(o2), "=&s"(o3)
       : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(rsrc), "s"(r0), "s"(r1), "s"(r2), "s"(r3), "s"(lds_base),
         "n"(kK0 * 1024), "n"((kK0 + 1) * 1024), "n"((kK0 + 2) * 1024), "n"((kK0 + 3) * 1024)
+      : "memory");
+}
+template <int kK0>
+__device__ __forceinline__ void dma_rows2(const u32x4& rsrc, int r0, int r1, uint32_t v0, uint32_t v1, uint32_t lds_base) {
+  uint32_t saved, o0, o1;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_lshl_b32 %1, %6, 10\n\t"
+      "s_add_u32 m0, %8, %9\n\t"
+      "s_lshl_b32 %2, %7, 10\n\t"
+      "buffer_load_dwordx4 %3, %5, %1 offen lds\n\t"
+      "s_add_u32 m0, %8, %10\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %4, %5, %2 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved), "=&s"(o0), "=&s"(o1)
+      : "v"(v0), "v"(v1), "s"(rsrc), "s"(r0), "s"(r1), "s"(lds_base), "n"(kK0 * 1024), "n"((kK0 + 1) * 1024)
       : "memory");
 }
 // One DMA instruction with a per-lane byte offset into the buffer.
@@ -224,6 +244,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// The lane id, recomputed where it is used (two VALU instructions): a volatile statement is
+// not hoisted out of the tile loop, so values derived from it are not kept live (or spilled)
+// across the loop.
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v;
   v[0] = (__bf16)lo;  // v_cvt_pk_bf16_f32: round to nearest even
@@ -243,6 +272,11 @@ __device__ __forceinline__ void mfma_qk_first(floatx16& acc, const bf16x8& a, co
 }
 __device__ __forceinline__ void mfma_qk(floatx16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// A chained step right after a branch target: the pad keeps the rule of two wait states before
+// every MFMA whose predecessor cannot be seen in straight-line code.
+__device__ __forceinline__ void mfma_qk_pad(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 // The last step of a chain, with the pad its result needs before a VALU or LDS read (18 wait
 // states for a 32x32x16 result; 20 given) in the same statement, so that no copy of the result
@@ -496,11 +530,12 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   const u32x4 rs_rope = make_rsrc(a.k_rope, (uint64_t)a.num_rows * kRopeRowBytes);
   const u32x4 rs_scale = make_rsrc(a.k_scales, kInt8 ? (uint64_t)a.num_rows * 16 : 0);
   // lane L's row: key 8w + L/8 of the tile (rope DMA; its readlanes give the wave's 8 rows)
-  auto lane_row = [&](int tile) -> int { return s_rows[tile * kTile + wave * 8 + (lane >> 3)]; };
+  auto lane_row = [&](int tile) -> int { return s_rows[tile * kTile + wave * 8 + (lane_id_here() >> 3)]; };
   // rope: lane L fetches chunk ((L & 7) ^ rope_swz(key)) of key = 8w + L/8
   auto issue_rope = [&](int row, uint32_t stage) __attribute__((always_inline)) {
-    const int key = wave * 8 + (lane >> 3);
-    const uint32_t chunk = 16 * ((lane & 7) ^ rope_swz(key));
+    const int ln = lane_id_here();
+    const int key = wave * 8 + (ln >> 3);
+    const uint32_t chunk = 16 * ((ln & 7) ^ rope_swz(key));
     const uint32_t lds = smem_lds + stage + kNopeTileBytes + wave * 8 * kRopeRowBytes;
     if constexpr (kBufDma) {
       dma16_voff(rs_rope, (uint32_t)row * kRopeRowBytes + chunk, lds);
@@ -557,6 +592,53 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   };
   // DMA instructions per tile and wave: bf16 8 nope rows + 1 rope; INT8 4 code + 1 scale + 1 rope
   constexpr int kDmaPerTile = kInt8 ? 6 : 9;
+  // The same DMA in five pieces, to be spread between MFMAs: piece k < 4 moves the wave's rows
+  // 2k and 2k + 1 (bf16 nope rows, or INT8 codes), piece 4 the rope rows (and INT8 scales).
+  auto issue_piece = [&](int tile, int row, int k) __attribute__((always_inline)) {
+    const uint32_t stage = stage_of(tile);
+    if (k == 4) {
+      if constexpr (kInt8) {
+        const uint32_t sb = smem_lds + codes_of(tile) + kCodeTileBytes + wave * 256;
+        const int ln = lane_id_here();
+        const int srow = s_rows[tile * kTile + wave * 8 + ((ln & 31) >> 2)];
+        if constexpr (kBufDma) {
+          dma4_voff(rs_scale, (uint32_t)srow * 16 + 4 * (ln & 3), sb);
+        } else {
+          dma4_g(reinterpret_cast<const char*>(a.k_scales) + (int64_t)srow * 16 + 4 * (ln & 3), sb);
+        }
+      }
+      issue_rope(row, stage);
+      return;
+    }
+    const int r0 = __builtin_amdgcn_readlane(row, 16 * k);      // key 2k of the wave's 8
+    const int r1 = __builtin_amdgcn_readlane(row, 16 * k + 8);  // key 2k + 1
+    const int ln = lane_id_here();
+    if constexpr (kInt8) {
+      const uint32_t cb = smem_lds + codes_of(tile) + wave * 4096;
+      const int rr = (ln >> 5) ? r1 : r0;
+      if constexpr (kBufDma) {
+        dma16_voff(rs_nope, (uint32_t)rr * kNope + 16 * (ln & 31), cb + k * 1024);
+      } else {
+        dma16_g(reinterpret_cast<const int8_t*>(a.k_nope) + (int64_t)rr * kNope + 16 * (ln & 31), cb + k * 1024);
+      }
+    } else {
+      const uint32_t lds_base = smem_lds + stage + wave * 8 * kNopeRowBytes;
+      const uint32_t vo0 = (uint32_t)(16 * ln) ^ (uint32_t)(16 * nope_swz(wave * 8 + 2 * k));
+      const uint32_t vo1 = (uint32_t)(16 * ln) ^ (uint32_t)(16 * nope_swz(wave * 8 + 2 * k + 1));
+      if constexpr (kBufDma) {
+        switch (k) {
+          case 0: dma_rows2<0>(rs_nope, r0, r1, vo0, vo1, lds_base); break;
+          case 1: dma_rows2<2>(rs_nope, r0, r1, vo0, vo1, lds_base); break;
+          case 2: dma_rows2<4>(rs_nope, r0, r1, vo0, vo1, lds_base); break;
+          default: dma_rows2<6>(rs_nope, r0, r1, vo0, vo1, lds_base); break;
+        }
+      } else {
+        const char* kn = reinterpret_cast<const char*>(a.k_nope);
+        dma16_sbase(kn + (int64_t)r0 * kNopeRowBytes, vo0, lds_base + 2 * k * kNopeRowBytes);
+        dma16_sbase(kn + (int64_t)r1 * kNopeRowBytes, vo1, lds_base + (2 * k + 1) * kNopeRowBytes);
+      }
+    }
+  };
   auto issue_tile = [&](int tile, int row) __attribute__((always_inline)) {
     if constexpr (kInt8) {
       issue_int8(row, tile);
@@ -656,14 +738,83 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     }
   };
 
-  floatx16 s_cur;  // raw S^T of the tile whose softmax runs next
+  // The P^T operands of the tile whose P.V runs next (hi and lo per key half): the softmax of a
+  // tile runs one interval before its P.V.
+  bf16x8 ph[2], pl[2];
+  // The softmax of one tile in 19 pieces, placed between MFMAs. Scores s[r] are key
+  // 8*(r/4) + 4g + (r%4) of the tile, head h; nk = valid keys of the tile. Produces the P^T
+  // operands (oh, ol), updates the running max and sum, and decides the O rescale (alpha).
+  struct Soft {
+    float x[16];
+    float mx, ls;
+    uint32_t hw[2][4], lw[2][4];
+  };
+  auto soft_piece = [&](int c, bool first, int nk, const floatx16& sc, Soft& st, bf16x8 (&oh)[2],
+                        bf16x8 (&ol)[2], float& alpha, bool& rescale) __attribute__((always_inline)) {
+    if (c == 0) {
+      st.mx = -INFINITY;
+      st.ls = 0.f;
+      if (nk >= kTile) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          st.x[r] = sc[r];
+          st.mx = fmaxf(st.mx, st.x[r]);
+        }
+      } else {
+        // keys past the partition's last valid row: -inf scores, so their p is exactly 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          st.x[r] = (8 * (r >> 2) + 4 * g + (r & 3)) < nk ? sc[r] : -INFINITY;
+          st.mx = fmaxf(st.mx, st.x[r]);
+        }
+      }
+    } else if (c == 1) {
+      const float mt = pair_max(st.mx) * c_scale;  // the tile max in the exp2 domain
+      if (first) {
+        m_run = mt;  // first tile: O and l are still zero, nothing to rescale
+      } else if (__any(mt > m_run + kRescaleThreshold)) {
+        const bool need = mt > m_run + kRescaleThreshold;
+        alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+        if (need) m_run = mt;
+        l_run *= alpha;
+        rescale = true;
+      }
+    } else if (c >= 2 && c < 10) {
+      // p = 2^(c*x - m), two per piece (in place of x)
+      const int r = 2 * (c - 2);
+      st.x[r] = __builtin_amdgcn_exp2f(fmaf(st.x[r], c_scale, -m_run));
+      st.x[r + 1] = __builtin_amdgcn_exp2f(fmaf(st.x[r + 1], c_scale, -m_run));
+    } else if (c >= 10 && c < 18) {
+      // P^T operands: hi = p truncated to bf16 (exact), lo = bf16(p - hi) (round to nearest
+      // even), so hi + lo carries about 16 significant bits. For key half kb, element i of
+      // lane (n, g) is result reg 8*kb + i.
+      const int kb = (c - 10) >> 2, i = (c - 10) & 3;
+      const float p0 = st.x[8 * kb + 2 * i], p1 = st.x[8 * kb + 2 * i + 1];
+      const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
+      st.ls += p0 + p1;
+      st.hw[kb][i] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+      st.lw[kb][i] = pack_bf16x2(p0 - __uint_as_float(u0 & 0xffff0000u), p1 - __uint_as_float(u1 & 0xffff0000u));
+    } else if (c == 18) {
+      l_run += pair_sum(st.ls);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        oh[kb] = __builtin_bit_cast(bf16x8, uint4{st.hw[kb][0], st.hw[kb][1], st.hw[kb][2], st.hw[kb][3]});
+        ol[kb] = __builtin_bit_cast(bf16x8, uint4{st.lw[kb][0], st.lw[kb][1], st.lw[kb][2], st.lw[kb][3]});
+      }
+    }
+  };
+  constexpr int kSoftPieces = 19;
 
-  // One tile interval (tile i: softmax and P.V; tile i + 1: S^T):
-  //   1. the row read of the tile whose DMA this interval issues, and the first S^T operands;
-  //   2. the S^T MFMAs of tile i + 1 with the softmax of tile i and that DMA issue between them;
-  //   3. an O rescale when the running max moved (rare);
-  //   4. the P.V MFMAs of tile i (INT8: with the dequantisation of tile i + 2 between them);
-  //   5. the wait for the DMA the next interval needs, and the barrier.
+  // One tile interval (tile i: P.V; tile i + 1: S^T and softmax), with the LDS reads of the two
+  // kinds of MFMA spread over the whole interval (S^T operands at full LDS rate and the P.V
+  // transpose reads together need about as many LDS clocks as the MFMAs take):
+  //   A. the 36 S^T(i + 1) steps, each followed by one P.V(i) MFMA of key half 0 (32 of them),
+  //      with the DMA of a later tile issued in five pieces between them (INT8: and the
+  //      dequantisation of tile i + 2);
+  //   B. the 32 P.V(i) MFMAs of key half 1 with the softmax of tile i + 1 between them;
+  //   C. an O rescale when tile i + 1 moved the running max (rare), after the P.V MFMAs, which
+  //      still use the old max;
+  //   D. the wait for the DMA the next interval needs, and the barrier.
   // bf16 issues tile i + 3 into the stage tile i - 1 left; INT8 issues the codes of tile i + 3
   // into the code buffer tile i + 1 left, and its rope rows into tile i's stage, whose rope part
   // S^T(i) has finished with.
@@ -673,162 +824,130 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     const bool do_dma = ti + 3 < ntiles;
     int row_dma = 0;
     if (do_dma) row_dma = lane_row(ti + 3);
-    const uint32_t st_next = stage_of(ti + 1);
-    const uint32_t kst = kbase + st_next, rst = rbase + st_next;
-    bf16x8 qa[kQkDepth];
-    floatx16 s_next;
-    if (kHasNext && wave_active) {
-#pragma unroll
-      for (int c = 0; c < kQkDepth; ++c) qa[c] = qk_operand(kst, rst, c);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // s[r] is key 8*(r/4) + 4g + (r%4) of the tile, head h
-    const int nk = n_valid - ti * kTile;
-    const bool tail = nk < kTile;  // wave-uniform: only the last tile has masked keys
-    float x[16], p[16];
-    float mx = -INFINITY, mt = 0.f, alpha = 1.0f, ls = 0.f;
-    bool rescale = false;
-    uint32_t hw[2][4], lw[2][4];
-    bf16x8 ph[2], pl[2];
-    // the softmax of tile i in pieces, placed between S^T steps (or run back to back in the
-    // last interval, which has no S^T to overlap)
-    auto soft_piece = [&](int c) __attribute__((always_inline)) {
-      if (c == 0) {
-        if (!tail) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            x[r] = s_cur[r];
-            mx = fmaxf(mx, x[r]);
-          }
-        } else {
-          // keys past the partition's last valid row: -inf scores, so their p is exactly 0
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            x[r] = (8 * (r >> 2) + 4 * g + (r & 3)) < nk ? s_cur[r] : -INFINITY;
-            mx = fmaxf(mx, x[r]);
-          }
-        }
-      } else if (c == 1) {
-        mt = pair_max(mx) * c_scale;  // the tile max in the exp2 domain
-        if (ti == 0) {
-          m_run = mt;  // first tile: O and l are still zero, nothing to rescale
-        } else if (__any(mt > m_run + kRescaleThreshold)) {
-          const bool need = mt > m_run + kRescaleThreshold;
-          alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
-          if (need) m_run = mt;
-          l_run *= alpha;
-          rescale = true;
-        }
-      } else if (c >= 2 && c < 10) {
-        // p = 2^(c*x - m), two per piece
-        const int r = 2 * (c - 2);
-        p[r] = __builtin_amdgcn_exp2f(fmaf(x[r], c_scale, -m_run));
-        p[r + 1] = __builtin_amdgcn_exp2f(fmaf(x[r + 1], c_scale, -m_run));
-      } else if (c >= 10 && c < 18) {
-        // P^T operands: hi = p truncated to bf16 (exact), lo = bf16(p - hi) (round to nearest
-        // even), so hi + lo carries about 16 significant bits. For key half kb, element i of
-        // lane (n, g) is result reg 8*kb + i.
-        const int kb = (c - 10) >> 2, i = (c - 10) & 3;
-        const float p0 = p[8 * kb + 2 * i], p1 = p[8 * kb + 2 * i + 1];
-        const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
-        hw[kb][i] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-        lw[kb][i] = pack_bf16x2(p0 - __uint_as_float(u0 & 0xffff0000u), p1 - __uint_as_float(u1 & 0xffff0000u));
-      } else if (c == 18) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ls += p[r];
-        l_run += pair_sum(ls);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          ph[kb] = __builtin_bit_cast(bf16x8, uint4{hw[kb][0], hw[kb][1], hw[kb][2], hw[kb][3]});
-          pl[kb] = __builtin_bit_cast(bf16x8, uint4{lw[kb][0], lw[kb][1], lw[kb][2], lw[kb][3]});
-        }
-      }
-    };
-    auto dma_piece = [&](int c) __attribute__((always_inline)) {
-      if (c == 20 && do_dma) issue_tile(ti + 3, row_dma);
-    };
-
     const uint32_t st_cur = stage_of(ti);
     const uint32_t v0 = vbase[0] + st_cur, v1 = vbase[1] + st_cur;
     bf16x8 va[kPvDepth];
+    floatx16 s_next;
+    // INT8: tile i + 2's codes (fetched in the previous interval) are dequantised in part A,
+    // from step 10 on. Without a tile i + 2 the same code runs on stale codes into the stage
+    // tile i + 2 would use, which nothing reads before it is refilled: the loop has no branch.
+    if (wave_active) {
+#pragma unroll
+      for (int u = 0; u < kPvDepth; ++u) va[u] = pv_operand(v0, v1, u);
+    }
     if (kHasNext && wave_active) {
+      const uint32_t st_next = stage_of(ti + 1);
+      const uint32_t kst = kbase + st_next, rst = rbase + st_next;
+      bf16x8 qa[kQkDepth];
+#pragma unroll
+      for (int c = 0; c < kQkDepth; ++c) qa[c] = qk_operand(kst, rst, c);
+      __builtin_amdgcn_sched_barrier(0);
+      // part A: S^T step c, then P.V MFMA c of key half 0 (u = c / 2, hi for even c, lo for odd)
 #pragma unroll
       for (int c = 0; c < kQkSteps; ++c) {
         const bf16x8 cur = qa[c % kQkDepth];
         if (c + kQkDepth < kQkSteps) qa[c % kQkDepth] = qk_operand(kst, rst, c + kQkDepth);
-        // the first P.V operands, read under the last S^T steps
-        if (c >= kQkSteps - kPvDepth) va[c - (kQkSteps - kPvDepth)] = pv_operand(v0, v1, c - (kQkSteps - kPvDepth));
         if (c == 0)
           mfma_qk_first(s_next, cur, qf[0]);
-        else if (c + 1 < kQkSteps)
-          mfma_qk(s_next, cur, qf[c]);
-        else
+        else if (c + 1 == kQkSteps)
           mfma_qk_last(s_next, cur, qf[c]);
-        soft_piece(c);
-        dma_piece(c);
+        else if (c % 7 == 5)
+          mfma_qk_pad(s_next, cur, qf[c]);  // follows the conditional DMA piece of step c - 1
+        else
+          mfma_qk(s_next, cur, qf[c]);
+        if (c < 32) {
+          const int u = c >> 1;
+          const bf16x8 vcur = va[u % kPvDepth];
+          if (c & 1) {
+            mfma_pv(oacc[u], vcur, pl[0]);
+            if (u + kPvDepth < 32) va[u % kPvDepth] = pv_operand(v0, v1, u + kPvDepth);
+          } else {
+            mfma_pv(oacc[u], vcur, ph[0]);
+          }
+        }
+        if constexpr (kInt8) {
+          if (c == 10) {
+            // tile i + 2's DMA is complete once at most this interval's first piece (one
+            // instruction, issued at step 4) is still in flight
+            if (do_dma)
+              wait_vmcnt<1>();
+            else
+              wait_vmcnt<0>();
+          }
+          if (c >= 10 && (c - 10) % 8 == 0) dequant_part(ti + 2, (c - 10) / 8);
+        }
+        if (do_dma && c % 7 == 4) issue_piece(ti + 3, row_dma, c / 7);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
+      // no S^T to overlap (the last interval, or a wave without heads): the INT8 dequantisation
+      // of tile i + 2 first (no DMA of this interval is in flight yet), then this interval's DMA
+      if constexpr (kInt8) {
+        if (ti + 2 < ntiles) {
+          wait_vmcnt<0>();
+          dequant_tile(ti + 2);
+        }
+      }
+      if (do_dma) {
+#pragma unroll
+        for (int k = 0; k < 5; ++k) issue_piece(ti + 3, row_dma, k);
+      }
       if (wave_active) {
 #pragma unroll
-        for (int c = 0; c < 19; ++c) soft_piece(c);
+        for (int u = 0; u < 16; ++u) {
+          const bf16x8 vcur = va[u % kPvDepth];
+          if (u + kPvDepth < 32) va[u % kPvDepth] = pv_operand(v0, v1, u + kPvDepth);
+          mfma_pv(oacc[u], vcur, ph[0]);
+          mfma_pv(oacc[u], vcur, pl[0]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      dma_piece(20);
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (wave_active) {
-      if (rescale) rescale_agprs(oacc, alpha);
-      __builtin_amdgcn_sched_barrier(0);
-
-      // INT8: tile i + 2's codes must be in LDS before its dequantisation under these MFMAs.
-      // Without a tile i + 2 the same code runs on stale codes into the stage tile i + 2 would
-      // use, which nothing reads before it is refilled: the P.V loop then has no branch.
-      if constexpr (kInt8) {
-        if (do_dma)
-          wait_vmcnt<kDmaPerTile>();
-        else
-          wait_vmcnt<0>();
-      }
-      if (!kHasNext) {
+      // part B: key half 1 of P.V(i), the softmax of tile i + 1 between its MFMAs
+      Soft st;
+      bf16x8 nh[2], nl[2];
+      float alpha = 1.0f;
+      bool rescale = false;
+      const int nk = n_valid - (ti + 1) * kTile;
 #pragma unroll
-        for (int u = 0; u < kPvDepth; ++u) va[u] = pv_operand(v0, v1, u);
-      }
-#pragma unroll
-      for (int u = 0; u < 32; ++u) {
+      for (int u = 16; u < 32; ++u) {
         const bf16x8 cur = va[u % kPvDepth];
         if (u + kPvDepth < 32) va[u % kPvDepth] = pv_operand(v0, v1, u + kPvDepth);
-        mfma_pv(oacc[u & 15], cur, ph[u >> 4]);
-        mfma_pv(oacc[u & 15], cur, pl[u >> 4]);
-        if constexpr (kInt8) {
-          if ((u & 7) == 4) dequant_part(ti + 2, u >> 3);
+        mfma_pv(oacc[u & 15], cur, ph[1]);
+        if (kHasNext) {
+          const int c0 = 2 * (u - 16) - 1;  // pieces 2(u-16) - 1 and 2(u-16): 0 .. 18 over u = 16 .. 25
+          if (c0 >= 0 && c0 < kSoftPieces) soft_piece(c0, false, nk, s_next, st, nh, nl, alpha, rescale);
+        }
+        mfma_pv(oacc[u & 15], cur, pl[1]);
+        if (kHasNext) {
+          const int c1 = 2 * (u - 16);
+          if (c1 < kSoftPieces) soft_piece(c1, false, nk, s_next, st, nh, nl, alpha, rescale);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-    } else if constexpr (kInt8) {
-      // a wave without heads still dequantises the rows it fetched
-      if (ti + 2 < ntiles) {
-        if (do_dma)
-          wait_vmcnt<kDmaPerTile>();
-        else
-          wait_vmcnt<0>();
-        dequant_tile(ti + 2);
+      if constexpr (kHasNext) {
+        ph[0] = nh[0];
+        ph[1] = nh[1];
+        pl[0] = nl[0];
+        pl[1] = nl[1];
       }
+      if (rescale) rescale_agprs(oacc, alpha);
     }
-    if constexpr (kHasNext) s_cur = s_next;
     pin_agprs(oacc);
-    // bf16: tile i + 2 must be in LDS for the next interval's S^T MFMAs (INT8 waited above)
-    if constexpr (!kInt8) {
-      if (ti + 2 < ntiles) {
-        if (do_dma)
-          wait_vmcnt<kDmaPerTile>();
-        else
-          wait_vmcnt<0>();
-      }
+    // tile i + 2 must be in LDS for the next interval's S^T MFMAs (INT8: its rope rows; its nope
+    // part this wave wrote itself)
+    if (ti + 2 < ntiles) {
+      if (do_dma)
+        wait_vmcnt<kDmaPerTile>();
+      else
+        wait_vmcnt<0>();
     }
     lds_barrier();
   };
 
-  // ---- prologue: the first tiles in flight; Q to bf16 operands; S^T(0).
+  // ---- prologue: the first tiles in flight; Q to bf16 operands; S^T(0) and its softmax.
   if (ntiles > 0) {
     if constexpr (kInt8) {
       // tiles 0 and 1 by DMA, dequantised in order; then tile 2's DMA
@@ -876,8 +995,14 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     }
     lds_barrier();
     if (wave_active) {
-      qk_tile(stage_of(0), s_cur);
-      mfma_drain(s_cur);
+      floatx16 s0;
+      qk_tile(stage_of(0), s0);
+      mfma_drain(s0);
+      Soft st;
+      float alpha = 1.0f;
+      bool rescale = false;
+#pragma unroll
+      for (int c = 0; c < kSoftPieces; ++c) soft_piece(c, true, n_valid, s0, st, ph, pl, alpha, rescale);
     }
     // INT8 refills tile 0's rope rows (with tile 3) in the first interval: every wave must be
     // done with S^T(0) first
@@ -925,50 +1050,66 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     return;
   }
 
-  // Partial of (t, sp) in register-image order: [wave][dc][rq][lane] float4.
+  // Partitions of one token: each takes an arrival ticket first. All but the last publish their
+  // partial (unnormalised O in register-image order [wave][dc][rq][lane] float4, and the running
+  // max and sum per head) and then count themselves ready; the last waits for that count and
+  // merges, with its own partial still in registers, so it never writes one. The wait is safe:
+  // every partition it waits for has already taken its ticket, so it is running and only has
+  // its stores left to do. A spin limit still bounds the wait.
   //
-  // Publication without an L2 write-back: every partial is written with agent-scope stores (the
-  // sc1 form of the store, which the L2 of this XCD writes through instead of holding dirty), so
-  // once this wave's stores are acknowledged (vmcnt 0) they are visible to every XCD, and the
-  // arrival count that follows needs no release fence. (A release fence would write back this
-  // XCD's whole L2.) The last arriver takes an agent-scope acquire fence, which drops stale
-  // lines from its own L2.
+  // Publication without an L2 write-back: the partials are written with agent-scope stores (the
+  // sc1 form, which the L2 of this XCD writes through instead of holding dirty), so once this
+  // wave's stores are acknowledged (vmcnt 0) they are visible to every XCD, and the ready count
+  // that follows needs no release fence. (A release fence would write back this XCD's whole L2.)
+  // The last arriver takes an agent-scope acquire fence, which drops stale lines from its own L2.
   const int S = a.n_splits;
+  int32_t* arrive = a.counters + t;
+  int32_t* ready = a.counters + a.n_tokens + t;
+  if (tid == 0) s_last = (__hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1) ? 1 : 0;
+  lds_barrier();
   floatx4* part = reinterpret_cast<floatx4*>(a.part_o);
   constexpr int kWaveImage = 16 * 4 * 64;  // float4s per wave
-  if (wave_active) {
-    floatx4* po = part + (((int64_t)t * S + sp) * kWaves + wave) * kWaveImage + lane;
+  if (!s_last) {
+    if (wave_active) {
+      floatx4* po = part + (((int64_t)t * S + sp) * kWaves + wave) * kWaveImage + lane;
 #pragma unroll
-    for (int dc = 0; dc < 16; ++dc) {
+      for (int dc = 0; dc < 16; ++dc) {
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const floatx4 v = agpr_quad(oacc[dc], rq);
-        // A VALU write of a 128-bit store's data registers needs a wait state after the store;
-        // the compiler does not see the store inside the asm, so the pad is part of it.
-        asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(po + (dc * 4 + rq) * 64), "v"(v)
-                     : "memory");
+        for (int rq = 0; rq < 4; ++rq) {
+          const floatx4 v = agpr_quad(oacc[dc], rq);
+          // A VALU write of a 128-bit store's data registers needs a wait state after the store;
+          // the compiler does not see the store inside the asm, so the pad is part of it.
+          asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(po + (dc * 4 + rq) * 64), "v"(v)
+                       : "memory");
+        }
+      }
+      if (g == 0) {
+        uint64_t* ml = reinterpret_cast<uint64_t*>(a.part_ml) + ((int64_t)t * S + sp) * kMaxHeads + h;
+        const uint64_t bits = (uint64_t)__float_as_uint(m_run) | ((uint64_t)__float_as_uint(l_run) << 32);
+        __hip_atomic_store(ml, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    if (g == 0) {
-      uint64_t* ml = reinterpret_cast<uint64_t*>(a.part_ml) + ((int64_t)t * S + sp) * kMaxHeads + h;
-      const uint64_t bits = (uint64_t)__float_as_uint(m_run) | ((uint64_t)__float_as_uint(l_run) << 32);
-      __hip_atomic_store(ml, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
+    lds_barrier();
+    if (tid == 0) __hip_atomic_fetch_add(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (tid == 0) {
+    for (int spin = 0; spin < kSpinLimit; ++spin) {
+      if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S - 1) break;
+      __builtin_amdgcn_s_sleep(2);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
   lds_barrier();
-  if (tid == 0) s_last = (atomicAdd(a.counters + t, 1) == S - 1) ? 1 : 0;
-  lds_barrier();
-  if (!s_last || !wave_active) return;
+  if (!wave_active) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other partitions' partials
 
-  // The last arriver combines all S partials in partition order (its own from its registers,
-  // which hold the same values it stored): the (m, l) of every partition for this lane's head
-  // first, then O four column blocks at a time.
+  // The last arriver combines all S partials in partition order (its own from its registers):
+  // the (m, l) of every partition for this lane's head first, then O four column blocks at a time.
   const float2* mlp = reinterpret_cast<const float2*>(a.part_ml) + (int64_t)t * S * kMaxHeads + h;
   float2 mlv[kMaxSplits];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) mlv[s] = mlp[(s < S ? s : S - 1) * kMaxHeads];
+  for (int s = 0; s < kMaxSplits; ++s) mlv[s] = (s == sp) ? make_float2(m_run, l_run) : mlp[(s < S ? s : S - 1) * kMaxHeads];
   float mmax = -INFINITY;
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) mmax = s < S ? fmaxf(mmax, mlv[s].x) : mmax;
@@ -981,6 +1122,28 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   const floatx4* pbase = part + ((int64_t)t * S * kWaves + wave) * kWaveImage + lane;
+  if (S == 2) {
+    // Two partitions: O = w0 O0 + w1 O1, summed in partition order whichever of the two arrived
+    // last. The other partial is read in two batches of 32 loads per lane.
+    const int so = 1 - sp;
+    const float w_own = sp == 0 ? wv[0] : wv[1], w_oth = sp == 0 ? wv[1] : wv[0];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const floatx4* ps = pbase + (int64_t)so * kWaves * kWaveImage + 32 * hh * 64;
+      floatx4 buf[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) buf[i] = ps[i * 64];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int dc = 8 * hh + (i >> 2), rq = i & 3;
+        const floatx4 own = w_own * agpr_quad(oacc[dc], rq);
+        const floatx4 oth = w_oth * buf[i];
+        put_out(dc, rq, (sp == 0 ? own + oth : oth + own) * inv);
+      }
+    }
+    flush_out();
+    return;
+  }
 #pragma unroll
   for (int hh = 0; hh < 4; ++hh) {  // column blocks 4hh .. 4hh + 3
     floatx4 acc[16];
@@ -1012,8 +1175,8 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   flush_out();
 }
 
-// Clears the per-token arrival counters before an attention launch that merges partitions. A
-// fill kernel rather than a memset, so that the call can be recorded in a graph.
+// Clears the per-token arrival and ready counters before an attention launch that merges
+// partitions. A fill kernel rather than a memset, so that the call can be recorded in a graph.
 __global__ void __launch_bounds__(256) sfa_zero_kernel(int32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -1041,7 +1204,7 @@ __global__ void __launch_bounds__(256) sfa_resolve_kernel(const ResolveArgs a) {
 
 hipError_t launch_attention(const KernelArgs& a, bool int8_cache, bool window_slots, hipStream_t stream) {
   if (a.n_splits > 1) {
-    const int64_t n = a.n_tokens;
+    const int64_t n = 2 * (int64_t)a.n_tokens;
     int32_t* counters = a.counters;
     int64_t count = n;
     void* zargs[] = {&counters, &count};
