@@ -88,8 +88,8 @@ constexpr int kCodeTileBytes = kTile * kNope;        // 16 KB
 constexpr int kCodeBufBytes = kCodeTileBytes + kWaves * 256;
 constexpr float kRescaleThreshold = 8.0f;           // log2 units: p stays <= 256 between rescales
 constexpr int kQkSteps = (kNope + kRope) / 16;      // 36 k-steps of 16 over the 576 columns
-constexpr int kQkDepth = 4;                         // LDS operand loads in flight ahead of the MFMA
-constexpr int kPvDepth = 3;
+constexpr int kQkDepthBf16 = 4;
+constexpr int kPvDepthBf16 = 3;
 constexpr int kOutWaveBytes = kHeadsPerWave * kNopeRowBytes;  // a wave's bf16 output rows (32 KB)
 // Bound on the last arriver's wait for the other partitions' partials (each try sleeps ~128
 // clocks): far beyond the time a partial takes to be stored.
@@ -370,6 +370,10 @@ __device__ __forceinline__ float pair_sum(float x) {
 template <bool kInt8, bool kBufDma, bool kWindow>
 __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const KernelArgs a) {
   using L = Lds<kInt8>;
+  // S^T operand loads in flight ahead of the MFMA (INT8 keeps one fewer: its dequantisation
+  // needs the registers)
+  constexpr int kQkDepth = kInt8 ? 3 : kQkDepthBf16;
+  constexpr int kPvDepth = kInt8 ? 2 : kPvDepthBf16;
   __shared__ __attribute__((aligned(1024))) char smem[L::kBytes];
   __shared__ __attribute__((aligned(16))) int32_t s_rows[kMaxSlots];
   __shared__ int32_t s_wcnt[kWaves];
@@ -651,34 +655,47 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   // layout of the tile's stage: code -> fp32 (exact), times the fp32 group scale (one rounding:
   // fma((code + 128), s, -128 s) is the exact product rounded once), -> bf16 (RNE). Lane L takes
   // 16 codes of key 2m + L/32 per step m, which become logical chunks 2(L % 32) and +1 of its row.
-  auto dequant_part = [&](int tile, int m) __attribute__((always_inline)) {
+  // The dequantisation of one tile runs in four parts (the wave's rows 2m and 2m + 1), each split
+  // into a read of its codes and scale and two halves of 8 codes that are converted and stored,
+  // so that the three can sit between different MFMAs.
+  struct Int8Part {
+    u32x4 c;        // lane L: codes 16(L % 32) .. +15 of key 2m + L / 32 of the wave's 8
+    float sc;       // the scale of their group
+    uint32_t dst;   // LDS byte address of logical chunk 2(L % 32) of that key's bf16 row
+  };
+  auto dq_load = [&](int tile, int m) __attribute__((always_inline)) -> Int8Part {
     const lds_char_t* cb = smem_p + codes_of(tile) + wave * 4096;
     const lds_char_t* sb = smem_p + codes_of(tile) + kCodeTileBytes + wave * 256;
-    lds_char_t* st = (lds_char_t*)smem_p + stage_of(tile);
-    {
-      const u32x4 c = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(cb + m * 1024 + 16 * lane);
-      const int kk = 2 * m + g;
-      const float sc = *reinterpret_cast<const __attribute__((address_space(3))) float*>(sb + kk * 16 + 4 * (n >> 3));
-      const float nb = -128.0f * sc;
-      const uint32_t w4[4] = {c[0] ^ 0x80808080u, c[1] ^ 0x80808080u, c[2] ^ 0x80808080u, c[3] ^ 0x80808080u};
-      uint32_t o[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float f0 = fmaf((float)(w4[q] & 0xffu), sc, nb);
-        const float f1 = fmaf((float)((w4[q] >> 8) & 0xffu), sc, nb);
-        const float f2 = fmaf((float)((w4[q] >> 16) & 0xffu), sc, nb);
-        const float f3 = fmaf((float)(w4[q] >> 24), sc, nb);
-        o[2 * q] = pack_bf16x2(f0, f1);
-        o[2 * q + 1] = pack_bf16x2(f2, f3);
-      }
-      const int key = wave * 8 + kk;
-      const int sw = nope_swz(key);
-      lds_char_t* row = st + key * kNopeRowBytes;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(row + 16 * ((2 * n) ^ sw)) =
+    const int ln = lane_id_here();
+    Int8Part q;
+    q.c = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(cb + m * 1024 + 16 * ln);
+    q.sc = *reinterpret_cast<const __attribute__((address_space(3))) float*>(sb + (2 * m + (ln >> 5)) * 16 +
+                                                                              4 * ((ln & 31) >> 3));
+    const int key = wave * 8 + 2 * m + (ln >> 5);
+    // the row starts on a 1 KB boundary, so chunk 2(L % 32) + 1 is at dst ^ 16
+    q.dst = stage_of(tile) + key * kNopeRowBytes + 16 * ((2 * (ln & 31)) ^ nope_swz(key));
+    return q;
+  };
+  // Quarter qq: codes 16(L % 32) + 4qq .. +3 become two bf16 pairs of o; after the second
+  // quarter of a half (qq odd) the 16-byte logical chunk 2(L % 32) + qq / 2 of the row is stored.
+  auto dq_quarter = [&](int qq, const Int8Part& q, uint32_t (&o)[4]) __attribute__((always_inline)) {
+    const uint32_t w = q.c[qq] ^ 0x80808080u;
+    const float nb = -128.0f * q.sc;
+    const float f0 = fmaf((float)(w & 0xffu), q.sc, nb);
+    const float f1 = fmaf((float)((w >> 8) & 0xffu), q.sc, nb);
+    const float f2 = fmaf((float)((w >> 16) & 0xffu), q.sc, nb);
+    const float f3 = fmaf((float)(w >> 24), q.sc, nb);
+    o[2 * (qq & 1)] = pack_bf16x2(f0, f1);
+    o[2 * (qq & 1) + 1] = pack_bf16x2(f2, f3);
+    if (qq & 1)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((lds_char_t*)smem_p + (q.dst ^ (16u * (qq >> 1)))) =
           u32x4{o[0], o[1], o[2], o[3]};
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(row + 16 * ((2 * n + 1) ^ sw)) =
-          u32x4{o[4], o[5], o[6], o[7]};
-    }
+  };
+  auto dequant_part = [&](int tile, int m) __attribute__((always_inline)) {
+    const Int8Part q = dq_load(tile, m);
+    uint32_t o[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) dq_quarter(qq, q, o);
   };
   auto dequant_tile = [&](int tile) __attribute__((always_inline)) {
 #pragma unroll
@@ -839,6 +856,8 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
       const uint32_t st_next = stage_of(ti + 1);
       const uint32_t kst = kbase + st_next, rst = rbase + st_next;
       bf16x8 qa[kQkDepth];
+      Int8Part dq_part;
+      uint32_t dq_out[4];
 #pragma unroll
       for (int c = 0; c < kQkDepth; ++c) qa[c] = qk_operand(kst, rst, c);
       __builtin_amdgcn_sched_barrier(0);
@@ -866,15 +885,18 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
           }
         }
         if constexpr (kInt8) {
-          if (c == 10) {
-            // tile i + 2's DMA is complete once at most this interval's first piece (one
-            // instruction, issued at step 4) is still in flight
+          // part m's codes are read at step 6 + 8m and converted a quarter at a time at steps
+          // 8 + 8m .. 11 + 8m
+          if (c == 6) {
+            // tile i + 2's codes and scales have landed once at most its rope instruction (its
+            // last) and this interval's first piece (one instruction, step 4) are in flight
             if (do_dma)
-              wait_vmcnt<1>();
+              wait_vmcnt<2>();
             else
-              wait_vmcnt<0>();
+              wait_vmcnt<1>();
           }
-          if (c >= 10 && (c - 10) % 8 == 0) dequant_part(ti + 2, (c - 10) / 8);
+          if (c >= 6 && (c - 6) % 8 == 0) dq_part = dq_load(ti + 2, (c - 6) / 8);
+          if (c >= 8 && (c - 8) % 8 < 4) dq_quarter((c - 8) % 8, dq_part, dq_out);
         }
         if (do_dma && c % 7 == 4) issue_piece(ti + 3, row_dma, c / 7);
         __builtin_amdgcn_sched_barrier(0);
