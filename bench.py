@@ -4,8 +4,8 @@ Workload (default): B=64 sequences, S1=2 query tokens each (MTP1), 128 query hea
 latent KV head, 8192 live cache positions per sequence in a 4096-block paged pool (block 128),
 top-k = 2048 distinct positions per token, bf16 cache. All inputs are seeded and synthetic.
 
-A step is one sfa_decode call over one batch. Untimed warm-up calls run first (by default for
-at least 0.5 s, so that the GPU clocks have left their idle state). The timed region then runs
+A step is one sfa_decode call over one batch. Untimed warm-up calls run first (at least --warmup
+calls and at least 1 s of calls, so that the GPU clocks have left their idle state). The timed region then runs
 --steps calls back to back. It rotates over --sets independent copies of the inputs; each copy has its own physical
 block order, so its pool sits at different addresses and the 256 MB MALL cannot hold the
 previous call's rows (cold protocol). Inputs are resident in HBM before timing starts.
@@ -169,21 +169,18 @@ def cpu_baseline(inp, gpu_out, seconds: float):
 
 
 def warm_up(step, args, torch):
-    """Untimed calls before timing: exactly --warmup if given, else at least 10 calls and at
-    least --warmup-seconds (from idle, the GPU needs time to raise its clocks)."""
+    """Untimed calls before timing: at least --warmup calls (10 when not given) and, in any case,
+    calls for at least --warmup-seconds. From idle the GPU needs time to raise its clocks, so a
+    short call count alone would time a GPU that is still clocking up. Returns the number of
+    calls made."""
+    n_min = 10 if args.warmup is None else args.warmup
     n_warm = 0
-    if args.warmup is not None:
-        for _ in range(args.warmup):
+    t_w = time.perf_counter()
+    while n_warm < n_min or time.perf_counter() - t_w < args.warmup_seconds:
+        for _ in range(10):
             step(n_warm)
             n_warm += 1
-    else:
-        t_w = time.perf_counter()
-        while n_warm < 10 or time.perf_counter() - t_w < args.warmup_seconds:
-            for _ in range(10):
-                step(n_warm)
-                n_warm += 1
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
     return n_warm
 
 
@@ -861,9 +858,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed calls before the timed region (default: at least 10 and at least "
-                         "--warmup-seconds of calls, so the GPU clocks have left their idle state)")
-    ap.add_argument("--warmup-seconds", type=float, default=0.5)
+                    help="least number of untimed calls before the timed region (default 10); calls go on "
+                         "until --warmup-seconds have also passed, so the GPU clocks have left their idle state")
+    ap.add_argument("--warmup-seconds", type=float, default=1.0)
     ap.add_argument("--workload", default="decode_b64_s2_bf16",
                     choices=sorted(WORKLOADS) + ["indexer_b64_s2", "decode_step_b64_s2"] + sorted(CACHE_WORKLOADS)
                     + sorted(WINDOW_WORKLOADS) + sorted(COMPRESS_WORKLOADS))
@@ -928,8 +925,8 @@ def main():
         calls[i % len(sets)]()
 
     # Warm-up. From idle, the GPU takes a while to raise its clocks: measured on the default
-    # decode workload, the kernel runs ~150 us per call after 10 warm-up calls and ~126 us after
-    # 1,000 or more. Without an explicit --warmup, calls run until --warmup-seconds have passed.
+    # decode workload, a call takes ~25 us longer after 10 warm-up calls than after 1,000 or more,
+    # so the warm-up always lasts --warmup-seconds as well as --warmup calls.
     args.warmup = warm_up(step, args, torch)
 
     # the timed region: --steps calls back to back between two events on the launch stream

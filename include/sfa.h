@@ -92,9 +92,9 @@ typedef struct {
  * needs for `dims`. Host-only: no GPU is touched. *bytes_out may be 0, in which case the
  * workspace pointer may be NULL.
  *
- * The workspace holds per-partition partial results and one arrival counter per (token, head
- * group). It needs no initialisation: the library clears the counters it uses, on `stream`,
- * before each launch. Two calls that may run at the same time need separate workspaces.
+ * The workspace holds per-partition partial results and two counters per token (partitions
+ * arrived, partials published). It needs no initialisation: the library clears the counters
+ * it uses, on `stream`, before each launch. Two calls that may run at the same time need separate workspaces.
  */
 int sfa_workspace_size(const sfa_dims* dims, int is_prefill, size_t* bytes_out);
 

@@ -168,18 +168,28 @@ def num_splits(dims: SfaDims, is_prefill: bool = False) -> int:
     return st
 
 
-# One zero-filled workspace per device, grown on demand. A completed call leaves the counters it
-# uses at zero, so the buffer can be reused by later calls on the same stream.
+# One workspace per (device, stream), grown on demand. Each call clears the counters it uses on
+# its own stream before its kernels run, so calls queued on one stream can share a buffer; calls
+# on different streams may overlap, so they never share one.
 _WORKSPACES: dict = {}
 
 
-def get_workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+def get_workspace(device: torch.device, nbytes: int, stream=None) -> Optional[torch.Tensor]:
+    """The cached workspace of (device, stream) with at least nbytes, or None for nbytes == 0.
+    stream defaults to the device's current stream."""
     if nbytes == 0:
         return None
-    key = (device.type, device.index)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    key = (device.type, device.index, stream.cuda_stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        # The library clears what must start at zero on the call's stream, so no fill is needed.
+        # The allocator ties a block to the stream current at allocation; record the stream the
+        # kernels use so that the block is not handed out again while they may still run.
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if stream.cuda_stream != torch.cuda.current_stream(device).cuda_stream:
+            ws.record_stream(stream)
         _WORKSPACES[key] = ws
     return ws
 
@@ -233,12 +243,12 @@ def _marshal_attention(fn_name: str, query_nope, query_rope, key_nope, key_rope,
         out = torch.empty((batch, s1, n_q, KV_LORA_RANK), dtype=torch.bfloat16, device=dev)
     _check(out, "out", (torch.bfloat16,), (batch, s1, n_q, KV_LORA_RANK), dev)
     need = workspace_size(dims, fn_name == "sfa_prefill")
-    if workspace is None:
-        workspace = get_workspace(dev, need)
-    elif need:
-        _check(workspace, "workspace", (torch.uint8,), None, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = get_workspace(dev, need, stream)
+    elif need:
+        _check(workspace, "workspace", (torch.uint8,), None, dev)
     args = (ctypes.byref(dims), _ptr(query_nope), _ptr(query_rope), _ptr(key_nope), _ptr(key_rope),
             _ptr(k_nope_scales if int8 else None), _ptr(topk_indices), _ptr(block_table), _ptr(kv_act_seqs),
             ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace) if need else None,
@@ -409,12 +419,12 @@ def _marshal_window(query_nope, query_rope, key_nope, key_rope, k_nope_scales, c
         out = torch.empty((batch, s1, n_q, KV_LORA_RANK), dtype=torch.bfloat16, device=dev)
     _check(out, "out", (torch.bfloat16,), (batch, s1, n_q, KV_LORA_RANK), dev)
     need = window_workspace_size(dims)
-    if workspace is None and need:
-        workspace = get_workspace(dev, need)
-    if workspace is not None:
-        _check(workspace, "workspace", (torch.uint8,), None, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None and need:
+        workspace = get_workspace(dev, need, stream)
+    if workspace is not None:
+        _check(workspace, "workspace", (torch.uint8,), None, dev)
     args = (ctypes.byref(dims), _ptr(query_nope), _ptr(query_rope), _ptr(key_nope), _ptr(key_rope),
             _ptr(k_nope_scales if int8 else None), _ptr(cmp_indices if topk_cmp else None), _ptr(block_table_ori),
             _ptr(block_table_cmp if topk_cmp else None), _ptr(ori_len), _ptr(cmp_len if topk_cmp else None),

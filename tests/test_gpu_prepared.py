@@ -55,3 +55,34 @@ def test_prepared_cache_write_matches_plain_call(sfa_lib):
     assert torch.equal(a["key_nope"], b["key_nope"])
     assert np.array_equal(a["key_rope"].view(torch.int16).cpu().numpy(), b["key_rope"].view(torch.int16).cpu().numpy())
     assert np.array_equal(a["k_nope_scales"].cpu().numpy().view(np.uint32), b["k_nope_scales"].cpu().numpy().view(np.uint32))
+
+
+def test_concurrent_decodes_on_two_streams(sfa_lib):
+    """Decodes queued on two streams at once, each with the binding's cached workspace, give the
+    same bits as the same calls run one after the other: the streams never share a workspace."""
+    import torch
+
+    inps = [W.generate(batch=4, s1=2, n_q=128, act_seqs=[6000, 4100, 3000, 5000], topk=2048, seed=s)
+            for s in (21, 22)]
+    devs = [sfa_lib.to_device(i) for i in inps]
+    refs = [sfa_lib.run(i, d, num_splits=4).clone() for i, d in zip(inps, devs)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(r) for r in refs]
+    for _ in range(4):
+        for o in outs:
+            o.fill_(0)
+        # both streams wait for the fills, then run with no ordering between them
+        ev = torch.cuda.Event()
+        ev.record()
+        for st, i, d, o in zip(streams, inps, devs, outs):
+            st.wait_event(ev)
+            for _rep in range(3):
+                sfa_lib.decode(d["query_nope"], d["query_rope"], d["key_nope"], d["key_rope"], d["k_nope_scales"],
+                               d["topk_indices"], d["block_table"], d["kv_act_seqs"], i.softmax_scale,
+                               batch=i.batch, s1=i.s1, num_splits=4, out=o, stream=st)
+        torch.cuda.synchronize()
+        for o, r in zip(outs, refs):
+            assert torch.equal(o.view(torch.int16), r.view(torch.int16))
+    keys = [k for k in sfa_lib._WORKSPACES if k[2] in (streams[0].cuda_stream, streams[1].cuda_stream)]
+    assert len(keys) == 2
