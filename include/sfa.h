@@ -64,7 +64,9 @@ typedef enum {
   SFA_ERR_SCALES = -5,          /* INT8 cache without k_nope_scales                           */
   SFA_ERR_ALIAS = -6,           /* out (or rows_out) overlaps an input or the workspace       */
   SFA_ERR_SCALE_VALUE = -7,     /* softmax_scale is not finite                                */
-  SFA_ERR_HIP = -8              /* a HIP runtime call failed                                  */
+  SFA_ERR_HIP = -8,             /* a HIP runtime call failed                                  */
+  SFA_ERR_SCRATCH_LIMIT = -9    /* sfa_decode_noalloc: the call needs more than its fixed
+                                   scratch (SFA_NOALLOC_SCRATCH_BYTES)                         */
 } sfa_status;
 
 /* Shapes of one call ("Input/output parameters" table of the SFA-with-quantisation page).
@@ -126,6 +128,30 @@ int sfa_decode(const sfa_dims* dims,
                const int32_t* topk_indices, const int32_t* block_table, const int32_t* kv_act_seqs,
                float softmax_scale, void* out,
                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sfa_decode without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, layouts, results and errors are those of sfa_decode. The workspace that
+ * sfa_decode would take is instead a fixed array inside this library, SFA_NOALLOC_SCRATCH_BYTES
+ * bytes per GPU, held by every GPU the library runs on until the process ends. Its device
+ * address is looked up on the first call on each device. The call allocates and frees nothing.
+ *   - A call whose sfa_workspace_size(dims, 0) exceeds SFA_NOALLOC_SCRATCH_BYTES returns
+ *     SFA_ERR_SCRATCH_LIMIT and queues nothing; a smaller dims.num_splits needs less.
+ *     The limit covers decode of 64 sequences x 2 query tokens x top-k 2048 with the automatic
+ *     partition choice (256 partitions of 256 KB each).
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap on one GPU (on
+ *     different streams, or from different threads) race and give wrong results. Calls queued
+ *     on one stream are ordered and safe. The array keeps the last call's contents; each call
+ *     clears, on `stream` and with a kernel, the counters it needs at zero.
+ */
+#define SFA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+int sfa_decode_noalloc(const sfa_dims* dims,
+                       const void* query_nope, const void* query_rope,
+                       const void* key_nope_2d, const void* key_rope_2d, const float* k_nope_scales,
+                       const int32_t* topk_indices, const int32_t* block_table, const int32_t* kv_act_seqs,
+                       float softmax_scale, void* out, hipStream_t stream);
 
 /*
  * Prefill-mode SFA ("Prefill mode": many query tokens; an online softmax keeps the running

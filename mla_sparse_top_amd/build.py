@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(PKG, "libsfa.so")
 # measurement context only (an MFMA throughput probe), kept out of the attention library
 PROBE_LIB_PATH = os.path.join(PKG, "libsfa_probe.so")
 PROBE_SOURCES = ["probe_mfma.hip"]
-SOURCES = ["sfa_kernels.hip", "sfa_host.cpp", "indexer_kernels.hip", "indexer_host.cpp", "cache_kernels.hip",
-           "cache_host.cpp", "compress_kernels.hip", "compress_host.cpp"]
+SOURCES = ["sfa_kernels.hip", "sfa_host.cpp", "sfa_noalloc.hip", "indexer_kernels.hip", "indexer_host.cpp",
+           "cache_kernels.hip", "cache_host.cpp", "compress_kernels.hip", "compress_host.cpp"]
 
 
 def hipcc_path() -> str:

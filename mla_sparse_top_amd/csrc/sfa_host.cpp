@@ -297,6 +297,8 @@ const char* sfa_status_string(int status) {
     case SFA_ERR_ALIAS: return "output overlaps an input or the workspace";
     case SFA_ERR_SCALE_VALUE: return "softmax_scale is not finite";
     case SFA_ERR_HIP: return "a HIP runtime call failed";
+    case SFA_ERR_SCRATCH_LIMIT: return "the call needs more workspace than sfa_decode_noalloc's fixed scratch "
+                                       "(SFA_NOALLOC_SCRATCH_BYTES); lower num_splits or use sfa_decode";
     default: return "unknown status";
   }
 }

@@ -27,6 +27,7 @@ KV_INT8 = 1
 STATUS = {
     0: "SFA_OK", -1: "SFA_ERR_NULL", -2: "SFA_ERR_DIMS", -3: "SFA_ERR_ALIGN", -4: "SFA_ERR_WORKSPACE",
     -5: "SFA_ERR_SCALES", -6: "SFA_ERR_ALIAS", -7: "SFA_ERR_SCALE_VALUE", -8: "SFA_ERR_HIP",
+    -9: "SFA_ERR_SCRATCH_LIMIT",
 }
 
 
@@ -53,6 +54,10 @@ _ATTN_ARGS = [ctypes.POINTER(SfaDims), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, c
 for _name in ("sfa_decode", "sfa_prefill"):
     getattr(_lib, _name).argtypes = _ATTN_ARGS
     getattr(_lib, _name).restype = ctypes.c_int
+_lib.sfa_decode_noalloc.argtypes = _ATTN_ARGS[:11] + [_vp]
+_lib.sfa_decode_noalloc.restype = ctypes.c_int
+# fixed scratch of sfa_decode_noalloc per GPU (SFA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 72 << 20
 _lib.sfa_workspace_size.argtypes = [ctypes.POINTER(SfaDims), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
 _lib.sfa_workspace_size.restype = ctypes.c_int
 _lib.sfa_num_splits.argtypes = [ctypes.POINTER(SfaDims), ctypes.c_int]
@@ -129,7 +134,7 @@ _lib.sfa_compress.restype = ctypes.c_int
 
 EXPORTED_SYMBOLS = ("sfa_workspace_size", "sfa_num_splits", "sfa_decode", "sfa_prefill", "sfa_resolve_rows",
                     "sfa_status_string", "sfa_indexer_scores", "sfa_topk_select", "sfa_cache_write",
-                    "sfa_window_workspace_size", "sfa_window_decode", "sfa_compress")
+                    "sfa_window_workspace_size", "sfa_window_decode", "sfa_compress", "sfa_decode_noalloc")
 
 
 class SfaError(RuntimeError):
@@ -214,8 +219,8 @@ def _check(t: torch.Tensor, name: str, dtypes, shape=None, device=None):
 def _marshal_attention(fn_name: str, query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices,
                        block_table, kv_act_seqs, softmax_scale, *, batch, s1, out=None, workspace=None,
                        num_splits_override=0, stream=None):
-    """Checks the tensors and builds the C argument tuple of sfa_decode / sfa_prefill.
-    Returns (args, out, keepalive)."""
+    """Checks the tensors and builds the C argument tuple of sfa_decode / sfa_prefill, or of
+    sfa_decode_noalloc (no workspace arguments). Returns (args, out, keepalive)."""
     dev = query_nope.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on a GPU device")
@@ -242,9 +247,16 @@ def _marshal_attention(fn_name: str, query_nope, query_rope, key_nope, key_rope,
     if out is None:
         out = torch.empty((batch, s1, n_q, KV_LORA_RANK), dtype=torch.bfloat16, device=dev)
     _check(out, "out", (torch.bfloat16,), (batch, s1, n_q, KV_LORA_RANK), dev)
-    need = workspace_size(dims, fn_name == "sfa_prefill")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if fn_name == "sfa_decode_noalloc":
+        args = (ctypes.byref(dims), _ptr(query_nope), _ptr(query_rope), _ptr(key_nope), _ptr(key_rope),
+                _ptr(k_nope_scales if int8 else None), _ptr(topk_indices), _ptr(block_table), _ptr(kv_act_seqs),
+                ctypes.c_float(softmax_scale), _ptr(out), ctypes.c_void_p(stream.cuda_stream))
+        keep = (dims, query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices, block_table,
+                kv_act_seqs, out, stream)
+        return args, out, keep
+    need = workspace_size(dims, fn_name == "sfa_prefill")
     if workspace is None:
         workspace = get_workspace(dev, need, stream)
     elif need:
@@ -300,6 +312,16 @@ def prefill(query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indi
     """sfa_prefill: returns out (batch, s1, n_q, 512) bf16."""
     return _attention("sfa_prefill", query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices,
                       block_table, kv_act_seqs, softmax_scale, batch=batch, s1=s1, out=out, workspace=workspace,
+                      num_splits_override=num_splits, stream=stream)
+
+
+def decode_noalloc(query_nope, query_rope, key_nope, key_rope, k_nope_scales, topk_indices, block_table,
+                   kv_act_seqs, softmax_scale, *, batch, s1, out=None, num_splits=0, stream=None):
+    """sfa_decode_noalloc: sfa_decode with the library's fixed per-GPU scratch as its workspace
+    (no device allocation by the library; out is allocated here only when not given). Calls
+    that overlap on one GPU share that scratch and must not run at the same time."""
+    return _attention("sfa_decode_noalloc", query_nope, query_rope, key_nope, key_rope, k_nope_scales,
+                      topk_indices, block_table, kv_act_seqs, softmax_scale, batch=batch, s1=s1, out=out,
                       num_splits_override=num_splits, stream=stream)
 
 

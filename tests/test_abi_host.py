@@ -153,7 +153,7 @@ def test_resolve_validation():
 
 
 def test_status_strings():
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert sfa.status_string(code)
     assert sfa.status_string(-99) == "unknown status"
 
@@ -336,3 +336,21 @@ def test_compress_validation():
     assert _cmp(d, eps=float("inf")) == -2
     assert _cmp(_cdims(batch=0)) == 0                    # nothing to do: no HIP call
     assert _cmp(_cdims(s1=0)) == 0
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    # top-k 32768 forces 16 partitions per token: 128 tokens x 16 x 256 KB is far beyond the
+    # fixed scratch, rejected on the host before any HIP call
+    d = _dims(batch=64, s1=2, n_q=128, topk=32768, max_blocks_per_batch=256, num_cache_rows=4097 * 128)
+    assert sfa.workspace_size(d) > sfa.NOALLOC_SCRATCH_BYTES
+    vp = ctypes.c_void_p
+    p = [vp(0x100000 + i * 0x10000000) for i in range(8)]
+    f = sfa._lib.sfa_decode_noalloc
+    assert f(ctypes.byref(d), *p, ctypes.c_float(1.0), vp(0x7000000000), None) == -9
+    assert "scratch" in sfa.status_string(-9)
+    # the default decode shape fits
+    assert sfa.workspace_size(_dims()) <= sfa.NOALLOC_SCRATCH_BYTES
+    # argument errors are sfa_decode's
+    s = _dims(**SMALL)
+    assert f(ctypes.byref(s), None, *p[1:], ctypes.c_float(1.0), vp(0x7000000000), None) == -1
+    assert f(ctypes.byref(s), *p, ctypes.c_float(float("nan")), vp(0x7000000000), None) == -7
