@@ -722,3 +722,83 @@ def compress_decode(seed: int = 0, ratio: int = 4) -> CompressInputs:
     The compressed pool has 16 blocks of 128 entries per sequence."""
     return compress_generate(batch=64, s1=2, ratio=ratio, start_pos=[8190] * 64, rope_positions=8192,
                              max_blocks=2048 // BLOCK_SIZE, seed=seed, name=f"compress_b64_s2_r{ratio}")
+
+
+# ---- MLA prolog ------------------------------------------------------------------------
+# The hidden state of the new tokens, the projection weights (random, scaled so that every
+# product has unit variance), the RMSNorm scales, positions and RoPE tables.
+# ----------------------------------------------------------------------------------------
+
+PROLOG_ROPE = ROPE_DIM
+
+
+@dataclasses.dataclass
+class PrologInputs:
+    tokens: int
+    n_q: int
+    x: np.ndarray               # uint16 bf16 bits (T, hidden)
+    w_dq: np.ndarray            # uint16 (q_lora_rank, hidden)
+    gamma_cq: np.ndarray        # uint16 (q_lora_rank)
+    w_uq_qr: np.ndarray         # uint16 (n_q * (nope_dim + 64), q_lora_rank)
+    w_uk: np.ndarray            # uint16 (n_q, 512, nope_dim)
+    w_dkv_kr: np.ndarray        # uint16 (576, hidden)
+    gamma_ckv: np.ndarray       # uint16 (512)
+    positions: np.ndarray       # int32 (T)
+    rope_cos: np.ndarray        # float32 (rope_positions, 32)
+    rope_sin: np.ndarray        # float32 (rope_positions, 32)
+    eps: float
+    name: str = ""
+
+    @property
+    def hidden(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def q_lora_rank(self) -> int:
+        return int(self.w_dq.shape[0])
+
+    @property
+    def nope_dim(self) -> int:
+        return int(self.w_uk.shape[2])
+
+    @property
+    def rope_positions(self) -> int:
+        return int(self.rope_cos.shape[0])
+
+
+def _scaled_bf16(g: torch.Generator, shape, std: float) -> np.ndarray:
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    out = np.empty((rows, shape[-1]), dtype=np.uint16)
+    for r0 in range(0, rows, _ROW_CHUNK):
+        r1 = min(rows, r0 + _ROW_CHUNK)
+        out[r0:r1] = _bf16_bits(torch.randn(r1 - r0, shape[-1], generator=g, dtype=torch.float32) * std)
+    return out.reshape(shape)
+
+
+def prolog_generate(*, tokens: int, n_q: int, hidden: int = 7168, q_lora_rank: int = 1536, nope_dim: int = 128,
+                    positions: Optional[Sequence[int]] = None, rope_positions: int = 8192, seed: int = 0,
+                    name: str = "") -> PrologInputs:
+    """x is N(0,1); each weight is N(0, 1/fan_in) so that every product has unit variance; the
+    RMSNorm scales are 1 + N(0, 0.1^2); all rounded to bf16. Positions default to the decode
+    step's 8190, 8191 alternating (two new tokens per sequence); eps is 1e-6."""
+    g = torch.Generator().manual_seed(110_000 + int(seed))
+    x = _scaled_bf16(g, (tokens, hidden), 1.0)
+    w_dq = _scaled_bf16(g, (q_lora_rank, hidden), hidden ** -0.5)
+    gamma_cq = _bf16_bits(1.0 + torch.randn(q_lora_rank, generator=g) * 0.1)
+    w_uq_qr = _scaled_bf16(g, (n_q * (nope_dim + PROLOG_ROPE), q_lora_rank), q_lora_rank ** -0.5)
+    w_uk = _scaled_bf16(g, (n_q, KV_LORA_RANK, nope_dim), nope_dim ** -0.5)
+    w_dkv_kr = _scaled_bf16(g, (KV_LORA_RANK + PROLOG_ROPE, hidden), hidden ** -0.5)
+    gamma_ckv = _bf16_bits(1.0 + torch.randn(KV_LORA_RANK, generator=g) * 0.1)
+    if positions is None:
+        positions = [8190 + (t % 2) for t in range(tokens)]
+    cos, sin = rope_tables(rope_positions)
+    return PrologInputs(tokens=int(tokens), n_q=int(n_q), x=x, w_dq=w_dq, gamma_cq=gamma_cq, w_uq_qr=w_uq_qr,
+                        w_uk=w_uk, w_dkv_kr=w_dkv_kr, gamma_ckv=gamma_ckv,
+                        positions=np.ascontiguousarray(positions, dtype=np.int32), rope_cos=cos, rope_sin=sin,
+                        eps=1e-6, name=name)
+
+
+def prolog_decode(seed: int = 0) -> PrologInputs:
+    """The decode step's prolog: 64 sequences x 2 new tokens (MTP 1), 128 heads, hidden 7168,
+    query rank 1536, nope head dim 128, positions 8190 and 8191."""
+    return prolog_generate(tokens=128, n_q=128, seed=seed, name="mla_prolog_b64_s2")
