@@ -385,6 +385,65 @@ int sfa_compress(const sfa_compress_dims* dims, const float* kv, const float* sc
                  const int32_t* start_pos, float* kv_state, float* score_state, const int32_t* block_table_cmp,
                  void* key_nope_2d, void* key_rope_2d, hipStream_t stream);
 
+/*
+ * MLA prolog: the new tokens' hidden states to the absorbed query that sfa_decode reads and the
+ * latent row that sfa_cache_write stores ("CANN DeepSeek Indexer attention optimisation",
+ * section "MLA Prolog" and the prolog's parameter list: DeepSeek V3's structure with weight
+ * absorption in decode; "NPU DeepSeek-V4 model PyPTO fused-operator optimisation", section
+ * "MlaProlog", computation steps: down-projection, RMSNorm, up-projection, interleaved RoPE on
+ * the last rope_dim channels; the key a projection, RMSNorm, RoPE). For token t with hidden row
+ * x and position p = positions[t]:
+ *
+ *   cq         = RMSNorm(x . w_dq^T) * gamma_cq                              (Q channels)
+ *   u          = cq . w_uq_qr^T; head h: qn = u[h*(Dn+64) + 0 .. Dn), qp = u[h*(Dn+64) + Dn .. +64)
+ *   q_nope[t,h] = qn . w_uk[h]^T                                             (512 channels)
+ *   q_rope[t,h] = RoPE(qp, p)
+ *   kv         = x . w_dkv_kr^T; kv_nope[t] = RMSNorm(kv[0..512)) * gamma_ckv; kv_rope[t] = RoPE(kv[512..576), p)
+ *
+ * RMSNorm(v) = v / sqrt(mean(v^2) + eps). RoPE turns each adjacent pair (2i, 2i+1) by the angle
+ * whose cosine and sine are rope_cos[p][i] and rope_sin[p][i]; a token with p outside
+ * [0, rope_positions) gets zero q_rope and kv_rope. The products accumulate in fp32; cq and qn
+ * are carried between the steps as bf16 hi + lo pairs (about 16 significant bits), not
+ * rounded to bf16. The outputs are rounded to bf16 (nearest even).
+ *
+ *   x          bf16 (T, H)
+ *   w_dq       bf16 (Q, H)              (out_features, in_features), as every weight here
+ *   gamma_cq   bf16 (Q)
+ *   w_uq_qr    bf16 (n_q*(Dn+64), Q)   head h owns rows h*(Dn+64) .. +Dn+64: nope, then rope
+ *   w_uk       bf16 (n_q, 512, Dn)     w_uk[h][c][d] weighs qn[d] into q_nope[c]
+ *   w_dkv_kr   bf16 (576, H)           rows 0..511 the latent row, 512..575 the rotary key
+ *   gamma_ckv  bf16 (512)
+ *   positions  int32 (T)
+ *   rope_cos, rope_sin  fp32 (rope_positions, 32)
+ *   q_nope     bf16 (T*n_q, 512)       row t*n_q + h: sfa_decode's query_nope
+ *   q_rope     bf16 (T*n_q, 64)        sfa_decode's query_rope
+ *   kv_nope    bf16 (T, 512), kv_rope bf16 (T, 64): sfa_cache_write's new_nope / new_rope
+ *   workspace  >= sfa_mla_prolog_workspace_size bytes, 256-byte aligned, no initialisation
+ *
+ * Errors: SFA_ERR_NULL, SFA_ERR_DIMS, SFA_ERR_ALIGN (any pointer not 16-byte aligned),
+ * SFA_ERR_WORKSPACE, SFA_ERR_ALIAS (an output overlaps an input, another output or the
+ * workspace), SFA_ERR_HIP. With T = 0 nothing is read or queued and the pointers may be NULL.
+ * Asynchronous on `stream`, no allocation. Two calls that may overlap need separate
+ * workspaces.
+ */
+typedef struct {
+  int32_t tokens;               /* T >= 0 new tokens                                          */
+  int32_t hidden;               /* H: a multiple of 64 in [256, 65536]                        */
+  int32_t q_lora_rank;          /* Q: a multiple of 64 in [256, 4096]                         */
+  int32_t n_q;                  /* query heads in [1, 128]                                    */
+  int32_t qk_nope_dim;          /* Dn: per-head nope width before absorption, a multiple of 16
+                                   in [64, 512]                                               */
+  int32_t rope_positions;       /* rows of rope_cos and rope_sin, >= 1                        */
+  float eps;                    /* RMSNorm epsilon, finite and >= 0                           */
+} sfa_prolog_dims;
+
+int sfa_mla_prolog_workspace_size(const sfa_prolog_dims* dims, size_t* bytes_out);
+int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq, const void* gamma_cq,
+                   const void* w_uq_qr, const void* w_uk, const void* w_dkv_kr, const void* gamma_ckv,
+                   const int32_t* positions, const float* rope_cos, const float* rope_sin, void* q_nope,
+                   void* q_rope, void* kv_nope, void* kv_rope, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

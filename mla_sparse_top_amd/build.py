@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(PKG, "libsfa.so")
 PROBE_LIB_PATH = os.path.join(PKG, "libsfa_probe.so")
 PROBE_SOURCES = ["probe_mfma.hip"]
 SOURCES = ["sfa_kernels.hip", "sfa_host.cpp", "sfa_noalloc.hip", "indexer_kernels.hip", "indexer_host.cpp",
-           "cache_kernels.hip", "cache_host.cpp", "compress_kernels.hip", "compress_host.cpp"]
+           "cache_kernels.hip", "cache_host.cpp", "compress_kernels.hip", "compress_host.cpp", "prolog_kernels.hip",
+           "prolog_host.cpp"]
 
 
 def hipcc_path() -> str:

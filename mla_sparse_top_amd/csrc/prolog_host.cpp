@@ -1,0 +1,214 @@
+// C-ABI entry points of the MLA prolog (sfa_mla_prolog_workspace_size, sfa_mla_prolog):
+// synchronous argument validation, the k split of the down-projections, workspace layout, and
+// the four launches. Declarations and contracts are in include/sfa.h.
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "prolog_internal.h"
+#include "sfa.h"
+
+namespace {
+
+using namespace sfa;
+
+constexpr size_t kAlign = 256;
+constexpr int kTargetWorkgroups = 256;  // one per compute unit of the MI355X
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* p, size_t n, const void* q, size_t m) {
+  if (!p || !q || n == 0 || m == 0) return false;
+  const uintptr_t a0 = (uintptr_t)p, a1 = a0 + n, b0 = (uintptr_t)q, b1 = b0 + m;
+  return a0 < b1 && b0 < a1;
+}
+
+int check(const sfa_prolog_dims* d) {
+  if (!d) return SFA_ERR_NULL;
+  if (d->tokens < 0 || d->tokens > (1 << 20)) return SFA_ERR_DIMS;
+  // every wave's k range must hold at least 4 steps of 16 (its load pipeline depth)
+  if (d->hidden < 256 || d->hidden > (1 << 16) || d->hidden % 64) return SFA_ERR_DIMS;
+  if (d->q_lora_rank < 256 || d->q_lora_rank > 4096 || d->q_lora_rank % 64) return SFA_ERR_DIMS;
+  if (d->n_q < 1 || d->n_q > SFA_MAX_HEADS) return SFA_ERR_DIMS;
+  if (d->qk_nope_dim < 64 || d->qk_nope_dim > 512 || d->qk_nope_dim % 16) return SFA_ERR_DIMS;
+  if (d->rope_positions < 1) return SFA_ERR_DIMS;
+  if (!(d->eps >= 0.0f) || !isfinite(d->eps)) return SFA_ERR_DIMS;
+  return SFA_OK;
+}
+
+// k splits of the down-projections: enough workgroups for every compute unit, each split's
+// k range a whole number of 64-wide units (16 per wave) and at least 4 of them, so that every
+// wave has the 4 k-steps its load pipeline keeps in flight
+int down_splits(const sfa_prolog_dims* d) {
+  const int tiles = (d->q_lora_rank + kPrLatent + kPrRope) / kPrFeatTile;
+  const int tok_blocks = (d->tokens + kPrTokBlock - 1) / kPrTokBlock;
+  const int units = d->hidden / 64;
+  int s = 1;
+  while ((int64_t)tiles * tok_blocks * s < kTargetWorkgroups) {
+    int n = s + 1;
+    while (n <= units && units % n) ++n;
+    if (n > units || units / n < 4) break;
+    s = n;
+  }
+  return s;
+}
+
+struct Layout {
+  size_t part, cq_hi, cq_lo, qn_hi, qn_lo, total;
+};
+
+Layout layout(const sfa_prolog_dims* d, int splits) {
+  const size_t t = (size_t)d->tokens;
+  Layout l{};
+  size_t o = 0;
+  l.part = o;
+  o += align_up((size_t)splits * t * (d->q_lora_rank + kPrLatent + kPrRope) * 4, kAlign);
+  l.cq_hi = o;
+  o += align_up(t * d->q_lora_rank * 2, kAlign);
+  l.cq_lo = o;
+  o += align_up(t * d->q_lora_rank * 2, kAlign);
+  l.qn_hi = o;
+  o += align_up(t * d->n_q * d->qk_nope_dim * 2, kAlign);
+  l.qn_lo = o;
+  o += align_up(t * d->n_q * d->qk_nope_dim * 2, kAlign);
+  l.total = t ? o : 0;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sfa_mla_prolog_workspace_size(const sfa_prolog_dims* dims, size_t* bytes_out) {
+  if (!bytes_out) return SFA_ERR_NULL;
+  const int st = check(dims);
+  if (st != SFA_OK) return st;
+  *bytes_out = layout(dims, down_splits(dims)).total;
+  return SFA_OK;
+}
+
+int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq, const void* gamma_cq,
+                   const void* w_uq_qr, const void* w_uk, const void* w_dkv_kr, const void* gamma_ckv,
+                   const int32_t* positions, const float* rope_cos, const float* rope_sin, void* q_nope,
+                   void* q_rope, void* kv_nope, void* kv_rope, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  const int st = check(dims);
+  if (st != SFA_OK) return st;
+  if (dims->tokens == 0) return SFA_OK;  // nothing to read or write; pointers may be NULL
+  const void* ins[] = {x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, positions, rope_cos, rope_sin};
+  void* outs[] = {q_nope, q_rope, kv_nope, kv_rope};
+  for (const void* p : ins)
+    if (!p) return SFA_ERR_NULL;
+  for (const void* p : outs)
+    if (!p) return SFA_ERR_NULL;
+  for (const void* p : ins)
+    if (!aligned16(p)) return SFA_ERR_ALIGN;
+  for (const void* p : outs)
+    if (!aligned16(p)) return SFA_ERR_ALIGN;
+  const int splits = down_splits(dims);
+  const Layout lay = layout(dims, splits);
+  if (lay.total > 0 && (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace % kAlign) != 0))
+    return SFA_ERR_WORKSPACE;
+
+  const size_t t = (size_t)dims->tokens, h = (size_t)dims->hidden, q = (size_t)dims->q_lora_rank;
+  const size_t n = (size_t)dims->n_q, dn = (size_t)dims->qk_nope_dim, np = (size_t)dims->rope_positions;
+  const size_t in_bytes[] = {t * h * 2, q * h * 2, q * 2, n * (dn + kPrRope) * q * 2, n * kPrLatent * dn * 2,
+                             (size_t)(kPrLatent + kPrRope) * h * 2, kPrLatent * 2, t * 4, np * 32 * 4, np * 32 * 4};
+  const size_t out_bytes[] = {t * n * kPrLatent * 2, t * n * kPrRope * 2, t * kPrLatent * 2, t * kPrRope * 2};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 10; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return SFA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SFA_ERR_ALIAS;
+    if (overlaps(outs[i], out_bytes[i], workspace, lay.total)) return SFA_ERR_ALIAS;
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + lay.part);
+  uint16_t* cq_hi = reinterpret_cast<uint16_t*>(ws + lay.cq_hi);
+  uint16_t* cq_lo = reinterpret_cast<uint16_t*>(ws + lay.cq_lo);
+  uint16_t* qn_hi = reinterpret_cast<uint16_t*>(ws + lay.qn_hi);
+  uint16_t* qn_lo = reinterpret_cast<uint16_t*>(ws + lay.qn_lo);
+  const int tok_blocks = (int)((t + kPrTokBlock - 1) / kPrTokBlock);
+
+  PrologGemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.tokens = (int32_t)t;
+  g.tok_blocks = tok_blocks;
+  g.positions = positions;
+  g.rope_cos = rope_cos;
+  g.rope_sin = rope_sin;
+  g.rope_positions = dims->rope_positions;
+  g.n_q = dims->n_q;
+  g.dn = dims->qk_nope_dim;
+
+  // 1. both down-projections, k split into `splits` ranges: fp32 partial sums
+  PrologGemmArgs g1 = g;
+  g1.w0 = static_cast<const uint16_t*>(w_dq);
+  g1.w1 = static_cast<const uint16_t*>(w_dkv_kr);
+  g1.f_split = (int32_t)q;
+  g1.n_feat = (int32_t)(q + kPrLatent + kPrRope);
+  g1.k = (int32_t)h;
+  g1.n_split = splits;
+  g1.k_chunk = (int32_t)(h / splits);
+  g1.b_hi = static_cast<const uint16_t*>(x);
+  g1.b_stride = (int64_t)h;
+  g1.part = part;
+  if (launch_prolog_gemm(g1, 0, stream) != hipSuccess) return SFA_ERR_HIP;
+
+  // 2. partial sums, RMSNorms, the key's RoPE
+  PrologNormArgs nm;
+  nm.part = part;
+  nm.n_split = splits;
+  nm.tokens = (int32_t)t;
+  nm.q_rank = (int32_t)q;
+  nm.gamma_cq = static_cast<const uint16_t*>(gamma_cq);
+  nm.gamma_ckv = static_cast<const uint16_t*>(gamma_ckv);
+  nm.eps = dims->eps;
+  nm.cq_hi = cq_hi;
+  nm.cq_lo = cq_lo;
+  nm.kv_nope = static_cast<uint16_t*>(kv_nope);
+  nm.kv_rope = static_cast<uint16_t*>(kv_rope);
+  nm.positions = positions;
+  nm.rope_cos = rope_cos;
+  nm.rope_sin = rope_sin;
+  nm.rope_positions = dims->rope_positions;
+  if (launch_prolog_norm(nm, stream) != hipSuccess) return SFA_ERR_HIP;
+
+  // 3. query up-projection: nope parts (hi/lo) and rotated rope parts
+  PrologGemmArgs g2 = g;
+  g2.w0 = static_cast<const uint16_t*>(w_uq_qr);
+  g2.w1 = g2.w0;
+  g2.n_feat = (int32_t)(n * (dn + kPrRope));
+  g2.f_split = g2.n_feat;
+  g2.k = (int32_t)q;
+  g2.n_split = 1;
+  g2.k_chunk = (int32_t)q;
+  g2.b_hi = cq_hi;
+  g2.b_lo = cq_lo;
+  g2.b_stride = (int64_t)q;
+  g2.qn_hi = qn_hi;
+  g2.qn_lo = qn_lo;
+  g2.q_rope = static_cast<uint16_t*>(q_rope);
+  if (launch_prolog_gemm(g2, 1, stream) != hipSuccess) return SFA_ERR_HIP;
+
+  // 4. absorption into the 512 latent channels per head
+  PrologGemmArgs g3 = g;
+  g3.w0 = static_cast<const uint16_t*>(w_uk);
+  g3.w1 = g3.w0;
+  g3.n_feat = kPrLatent;
+  g3.f_split = kPrLatent;
+  g3.k = (int32_t)dn;
+  g3.n_split = 1;
+  g3.k_chunk = (int32_t)dn;
+  g3.b_hi = qn_hi;
+  g3.b_lo = qn_lo;
+  g3.b_stride = (int64_t)(n * dn);
+  g3.q_nope = static_cast<uint16_t*>(q_nope);
+  if (launch_prolog_gemm(g3, 2, stream) != hipSuccess) return SFA_ERR_HIP;
+  return SFA_OK;
+}
+
+}  // extern "C"

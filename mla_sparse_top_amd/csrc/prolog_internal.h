@@ -1,0 +1,61 @@
+// Internal interface between the MLA prolog's C-ABI layer (prolog_host.cpp) and its kernels
+// (prolog_kernels.hip). Not installed, not part of the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace sfa {
+
+constexpr int kPrLatent = 512;      // latent row (kv_lora_rank)
+constexpr int kPrRope = 64;         // rotary channels
+constexpr int kPrTokBlock = 128;    // tokens per workgroup (4 MFMA blocks of 32)
+constexpr int kPrFeatTile = 64;     // features per workgroup in the split-K GEMMs (2 MFMA blocks)
+constexpr int kPrAbsTile = 256;     // features per workgroup of the absorption (4 waves x 64)
+
+// One launch of the weight-streaming GEMM: out[t, f] = sum over k of W[f, k] * B[t, k] for the
+// workgroup's features, tokens and k range; the epilogue depends on the mode.
+struct PrologGemmArgs {
+  const uint16_t* w0;        // bf16 (rows, k): features [0, f_split)
+  const uint16_t* w1;        // bf16 (rows, k): features [f_split, n_feat), row f - f_split
+  const uint16_t* b_hi;      // bf16 activations, token row stride b_stride elements
+  const uint16_t* b_lo;      // low halves (hi + lo carries the fp32 value), or null
+  int64_t b_stride;
+  int32_t f_split, n_feat, k, tokens, n_split, k_chunk, tok_blocks;
+  // mode 0: fp32 partial sums (n_split, tokens, n_feat)
+  float* part;
+  // mode 1: per-head nope part as hi/lo bf16 (tokens, n_q, dn); rotary part -> q_rope
+  uint16_t* qn_hi;
+  uint16_t* qn_lo;
+  uint16_t* q_rope;          // bf16 (tokens * n_q, 64)
+  // mode 2: absorbed query
+  uint16_t* q_nope;          // bf16 (tokens * n_q, 512)
+  const int32_t* positions;  // (tokens)
+  const float* rope_cos;     // (rope_positions, 32)
+  const float* rope_sin;
+  int32_t rope_positions, n_q, dn;
+};
+
+// The per-token vector step after the down-projections: sums the partials, RMSNorm of the
+// query part (hi/lo bf16 out) and of the latent row (bf16 out), RoPE of the rotary key.
+struct PrologNormArgs {
+  const float* part;         // (n_split, tokens, q_rank + 576)
+  int32_t n_split, tokens, q_rank;
+  const uint16_t* gamma_cq;  // bf16 (q_rank)
+  const uint16_t* gamma_ckv; // bf16 (512)
+  float eps;
+  uint16_t* cq_hi;           // bf16 (tokens, q_rank)
+  uint16_t* cq_lo;
+  uint16_t* kv_nope;         // bf16 (tokens, 512)
+  uint16_t* kv_rope;         // bf16 (tokens, 64)
+  const int32_t* positions;
+  const float* rope_cos;
+  const float* rope_sin;
+  int32_t rope_positions;
+};
+
+hipError_t launch_prolog_gemm(const PrologGemmArgs& a, int mode, hipStream_t stream);
+hipError_t launch_prolog_norm(const PrologNormArgs& a, hipStream_t stream);
+
+}  // namespace sfa

@@ -132,9 +132,29 @@ _lib.sfa_compress.argtypes = [ctypes.POINTER(SfaCompressDims), _vp, _vp, _vp, _v
                               _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.sfa_compress.restype = ctypes.c_int
 
+class SfaPrologDims(ctypes.Structure):
+    _fields_ = [
+        ("tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("q_lora_rank", ctypes.c_int32),
+        ("n_q", ctypes.c_int32),
+        ("qk_nope_dim", ctypes.c_int32),
+        ("rope_positions", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+    ]
+
+
+_lib.sfa_mla_prolog_workspace_size.argtypes = [ctypes.POINTER(SfaPrologDims), ctypes.POINTER(ctypes.c_size_t)]
+_lib.sfa_mla_prolog_workspace_size.restype = ctypes.c_int
+_lib.sfa_mla_prolog.argtypes = [ctypes.POINTER(SfaPrologDims)] + [_vp] * 15 + [ctypes.c_size_t, _vp]
+_lib.sfa_mla_prolog.restype = ctypes.c_int
+
+
+
 EXPORTED_SYMBOLS = ("sfa_workspace_size", "sfa_num_splits", "sfa_decode", "sfa_prefill", "sfa_resolve_rows",
                     "sfa_status_string", "sfa_indexer_scores", "sfa_topk_select", "sfa_cache_write",
-                    "sfa_window_workspace_size", "sfa_window_decode", "sfa_compress", "sfa_decode_noalloc")
+                    "sfa_window_workspace_size", "sfa_window_decode", "sfa_compress", "sfa_decode_noalloc",
+                    "sfa_mla_prolog_workspace_size", "sfa_mla_prolog")
 
 
 class SfaError(RuntimeError):
@@ -788,3 +808,104 @@ def prepare_compress(inp, d, stream=None) -> PreparedCall:
                                    d["kv_state"], d["score_state"], d["block_table_cmp"], d["key_nope"],
                                    d["key_rope"], batch=inp.batch, s1=inp.s1, stream=stream)
     return PreparedCall([(_lib.sfa_compress, args, "sfa_compress")], d["key_nope"], keep)
+
+
+# ---- MLA prolog -------------------------------------------------------------------------
+
+def prolog_workspace_size(dims: SfaPrologDims) -> int:
+    out = ctypes.c_size_t(0)
+    st = _lib.sfa_mla_prolog_workspace_size(ctypes.byref(dims), ctypes.byref(out))
+    if st != 0:
+        raise SfaError(st, "sfa_mla_prolog_workspace_size")
+    return out.value
+
+
+def _marshal_prolog(x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, positions, rope_cos, rope_sin, eps, *,
+                    out=None, workspace=None, stream=None):
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    t, hidden = x.shape
+    q = w_dq.shape[0]
+    n_q, lat, dn = w_uk.shape
+    n_pos = rope_cos.shape[0]
+    b16 = (torch.bfloat16,)
+    _check(x, "x", b16, (t, hidden), dev)
+    _check(w_dq, "w_dq", b16, (q, hidden), dev)
+    _check(gamma_cq, "gamma_cq", b16, (q,), dev)
+    _check(w_uq_qr, "w_uq_qr", b16, (n_q * (dn + ROPE_DIM), q), dev)
+    _check(w_uk, "w_uk", b16, (n_q, KV_LORA_RANK, dn), dev)
+    _check(w_dkv_kr, "w_dkv_kr", b16, (KV_LORA_RANK + ROPE_DIM, hidden), dev)
+    _check(gamma_ckv, "gamma_ckv", b16, (KV_LORA_RANK,), dev)
+    _check(positions, "positions", (torch.int32,), (t,), dev)
+    _check(rope_cos, "rope_cos", (torch.float32,), (n_pos, ROPE_DIM // 2), dev)
+    _check(rope_sin, "rope_sin", (torch.float32,), (n_pos, ROPE_DIM // 2), dev)
+    dims = SfaPrologDims(t, hidden, q, n_q, dn, n_pos, float(eps))
+    shapes = ((t * n_q, KV_LORA_RANK), (t * n_q, ROPE_DIM), (t, KV_LORA_RANK), (t, ROPE_DIM))
+    if out is None:
+        out = tuple(torch.empty(sh, dtype=torch.bfloat16, device=dev) for sh in shapes)
+    for o, sh, name in zip(out, shapes, ("q_nope", "q_rope", "kv_nope", "kv_rope")):
+        _check(o, name, b16, sh, dev)
+    need = prolog_workspace_size(dims)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    if workspace is None and need:
+        workspace = get_workspace(dev, need, stream)
+    if workspace is not None:
+        _check(workspace, "workspace", (torch.uint8,), None, dev)
+    args = (ctypes.byref(dims), _ptr(x), _ptr(w_dq), _ptr(gamma_cq), _ptr(w_uq_qr), _ptr(w_uk), _ptr(w_dkv_kr),
+            _ptr(gamma_ckv), _ptr(positions), _ptr(rope_cos), _ptr(rope_sin), *[_ptr(o) for o in out],
+            _ptr(workspace) if need else None, ctypes.c_size_t(workspace.numel() if (need and workspace is not None)
+                                                            else 0),
+            ctypes.c_void_p(stream.cuda_stream))
+    keep = (dims, x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, positions, rope_cos, rope_sin, out,
+            workspace, stream)
+    return args, out, keep
+
+
+def mla_prolog(x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, positions, rope_cos, rope_sin, eps, *,
+               out=None, workspace=None, stream=None):
+    """sfa_mla_prolog: returns (q_nope (T*n_q, 512), q_rope (T*n_q, 64), kv_nope (T, 512),
+    kv_rope (T, 64)), all bf16."""
+    args, out, _keep = _marshal_prolog(x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, positions, rope_cos,
+                                       rope_sin, eps, out=out, workspace=workspace, stream=stream)
+    st = _lib.sfa_mla_prolog(*args)
+    if st != 0:
+        raise SfaError(st, "sfa_mla_prolog")
+    return out
+
+
+def prepare_mla_prolog(*tensors, **kw) -> PreparedCall:
+    """sfa_mla_prolog bound to these tensors (a PreparedCall returning the output tuple)."""
+    args, out, keep = _marshal_prolog(*tensors, **kw)
+    return PreparedCall([(_lib.sfa_mla_prolog, args, "sfa_mla_prolog")], out, keep)
+
+
+def prolog_to_device(inp, device="cuda"):
+    """Upload a workloads.PrologInputs instance."""
+    import numpy as np
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    return {
+        "x": bf16(inp.x), "w_dq": bf16(inp.w_dq), "gamma_cq": bf16(inp.gamma_cq), "w_uq_qr": bf16(inp.w_uq_qr),
+        "w_uk": bf16(inp.w_uk), "w_dkv_kr": bf16(inp.w_dkv_kr), "gamma_ckv": bf16(inp.gamma_ckv),
+        "positions": torch.from_numpy(inp.positions).to(device),
+        "rope_cos": torch.from_numpy(inp.rope_cos).to(device), "rope_sin": torch.from_numpy(inp.rope_sin).to(device),
+    }
+
+
+def _prolog_args(inp, d):
+    return (d["x"], d["w_dq"], d["gamma_cq"], d["w_uq_qr"], d["w_uk"], d["w_dkv_kr"], d["gamma_ckv"], d["positions"],
+            d["rope_cos"], d["rope_sin"], inp.eps)
+
+
+def run_prolog(inp, d=None, *, out=None):
+    """sfa_mla_prolog on an uploaded PrologInputs instance."""
+    d = d if d is not None else prolog_to_device(inp)
+    return mla_prolog(*_prolog_args(inp, d), out=out)
+
+
+def prepare_prolog_run(inp, d, *, out=None) -> PreparedCall:
+    return prepare_mla_prolog(*_prolog_args(inp, d), out=out)

@@ -354,3 +354,57 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
     s = _dims(**SMALL)
     assert f(ctypes.byref(s), None, *p[1:], ctypes.c_float(1.0), vp(0x7000000000), None) == -1
     assert f(ctypes.byref(s), *p, ctypes.c_float(float("nan")), vp(0x7000000000), None) == -7
+
+
+def _prolog_dims(**kw):
+    base = dict(tokens=128, hidden=7168, q_lora_rank=1536, n_q=128, qk_nope_dim=128, rope_positions=8192, eps=1e-6)
+    base.update(kw)
+    return sfa.SfaPrologDims(**base)
+
+
+def _prolog_call(d, over=None, ws=0x7000000000, ws_bytes=None):
+    vp = ctypes.c_void_p
+    names = ["x", "w_dq", "gcq", "w_uq", "w_uk", "w_dkv", "gckv", "pos", "cos", "sin", "qn", "qr", "kn", "kr"]
+    p = {n: 0x100000000 * (i + 1) for i, n in enumerate(names)}
+    p.update(over or {})
+    if ws_bytes is None:
+        ws_bytes = sfa.prolog_workspace_size(d)
+    return sfa._lib.sfa_mla_prolog(ctypes.byref(d), *[vp(p[n]) if p[n] is not None else None for n in names],
+                                   vp(ws) if ws else None, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_prolog_workspace_and_splits():
+    # decode shape: 33 feature tiles x 8 k splits of the down-projections; partials, cq and the
+    # per-head nope parts as hi/lo pairs
+    d = _prolog_dims()
+    part = 8 * 128 * (1536 + 576) * 4
+    cq = 2 * 128 * 1536 * 2
+    qn = 2 * 128 * 128 * 128 * 2
+    assert sfa.prolog_workspace_size(d) == part + cq + qn
+    assert sfa.prolog_workspace_size(_prolog_dims(tokens=0)) == 0
+
+
+@pytest.mark.parametrize("field,value", [("hidden", 128), ("hidden", 7200), ("q_lora_rank", 128), ("q_lora_rank", 8192),
+                                         ("n_q", 0), ("n_q", 129), ("qk_nope_dim", 48), ("qk_nope_dim", 136),
+                                         ("rope_positions", 0), ("eps", -1.0), ("eps", float("nan")), ("tokens", -1)])
+def test_prolog_bad_dims_rejected(field, value):
+    d = _prolog_dims(**{field: value})
+    out = ctypes.c_size_t(0)
+    assert sfa._lib.sfa_mla_prolog_workspace_size(ctypes.byref(d), ctypes.byref(out)) == -2
+    assert _prolog_call(d, ws_bytes=0) == -2
+
+
+def test_prolog_validation_errors():
+    d = _prolog_dims()
+    assert _prolog_call(d, {"x": None}) == -1
+    assert _prolog_call(d, {"kr": None}) == -1
+    assert _prolog_call(d, {"w_uk": 0x100000008}) == -3
+    assert _prolog_call(d, ws=None) == -4
+    assert _prolog_call(d, ws=0x7000000010) == -4
+    need = sfa.prolog_workspace_size(d)
+    assert _prolog_call(d, ws_bytes=need - 1) == -4
+    assert _prolog_call(d, {"qn": 0x100000000 * 2 + 4096}) == -6     # q_nope inside w_dq
+    assert _prolog_call(d, {"kn": 0x7000000000 + 4096}) == -6          # kv_nope inside the workspace
+    assert _prolog_call(d, {"kr": 0x100000000 * 13 + 64}) == -6        # kv_rope inside kv_nope
+    # no tokens: nothing is read, NULL pointers are fine
+    assert _prolog_call(_prolog_dims(tokens=0), {n: None for n in ("x", "qn")}, ws=None, ws_bytes=0) == 0
