@@ -444,6 +444,7 @@ def bench_decode_step(args):
 
 WINDOW_WORKLOADS = {
     "swa_b64_s2_w128_bf16": ("swa_decode", "bf16"),
+    "cfa_b64_s2_w128_r128_bf16": ("cfa_decode", "bf16"),
     "scfa_b64_s2_w128_k512_bf16": ("scfa_decode", "bf16"),
     "scfa_b64_s2_w128_k512_int8": ("scfa_decode", "int8"),
 }
@@ -452,8 +453,8 @@ WINDOW_WORKLOADS = {
 def bench_window(args):
     """The sliding-window + compressed-cache variants (sfa_window_decode: the sparse attention
     kernel resolving window and compressed slots itself) at the pages' timed shape: 64 sequences
-    x 2 query tokens, 8K of original cache, window 128; SCFA adds 512 of the 2048 causal
-    compressed entries (compress_ratio 4). --sets copies of the pool in different block orders
+    x 2 query tokens, 8K of original cache, window 128; CFA adds every causal compressed entry
+    at compress_ratio 128 (64), SCFA 512 of the 2048 causal entries at compress_ratio 4. --sets copies of the pool in different block orders
     are rotated (both block tables remapped)."""
     import numpy as np
     import torch
@@ -533,15 +534,17 @@ def bench_window(args):
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": inp.batch, "s1": inp.s1, "n_q": inp.n_q,
                    "window": inp.window, "topk_cmp": inp.topk_cmp, "ori_len": int(inp.ori_len.max()),
-                   "compress_ratio": 4, "valid_slots": valid, "cold_sets": len(sets)},
+                   "compress_ratio": (int(inp.ori_len[0]) // int(inp.cmp_len[0])) if inp.topk_cmp else None,
+                   "valid_slots": valid, "cold_sets": len(sets)},
         "kernel_ms_mean": round(launch_ms, 5),
         "algorithmic_bytes_per_call": nbytes,
         "algorithmic_flop_per_call": flop,
         "tflops": round(tflops, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profile(kernel_source_hash(), f"{args.workload}_traffic.txt")},
         "rotated_outputs_identical": bool(same),
-        "context_pages_one_die_us": 65 if fn_name == "swa_decode" else 160,
+        "context_pages_one_die_us": {"swa_decode": 65, "cfa_decode": 90, "scfa_decode": 160}[fn_name],
     }
     if args.cpu_seconds > 0:
         got = outs[(args.steps - 1) % len(sets)].float().cpu().numpy().astype(np.float64).reshape(T, inp.n_q, 512)
@@ -796,6 +799,111 @@ def bench_compress(args):
     print(json.dumps(rec), flush=True)
 
 
+PROLOG_WORKLOADS = {"mla_prolog_b64_s2": "prolog_decode"}
+
+
+def prolog_work(inp):
+    """Bytes and flops the MLA prolog must move and do per call: every weight once, the hidden
+    rows, the four outputs, the positions and the RoPE table rows used; the four products."""
+    t, h, q, n, dn = inp.tokens, inp.hidden, inp.q_lora_rank, inp.n_q, inp.nope_dim
+    weights = (q * h + n * (dn + 64) * q + n * 512 * dn + 576 * h + q + 512) * 2
+    rows = len({int(p) for p in inp.positions if 0 <= int(p) < inp.rope_positions})
+    nbytes = weights + t * h * 2 + t * n * 576 * 2 + t * 576 * 2 + t * 4 + rows * 32 * 4 * 2
+    flop = 2 * t * (h * (q + 576) + q * n * (dn + 64) + n * 512 * dn)
+    return nbytes, flop
+
+
+def bench_prolog(args):
+    """The MLA prolog (sfa_mla_prolog) of the decode step: 64 sequences x 2 new tokens, hidden
+    7168, query rank 1536, 128 heads. The call streams ~122 MB of weights; it rotates over --sets
+    copies of them so that the 256 MB MALL cannot serve the previous call's weights."""
+    import numpy as np
+    import torch
+
+    import oracle.prolog_oracle as PO
+    from mla_sparse_top_amd import sfa, workloads
+
+    inp = getattr(workloads, PROLOG_WORKLOADS[args.workload])(seed=args.seed)
+    print(f"[bench] generated {inp.name}", file=sys.stderr, flush=True)
+    d0 = sfa.prolog_to_device(inp)
+    sets = [d0] + [{k: v.clone() for k, v in d0.items()} for _ in range(1, max(1, args.sets))]
+    outs = [tuple(torch.empty_like(o) for o in sfa.run_prolog(inp, d0)) for _ in sets]
+    calls = [sfa.prepare_prolog_run(inp, sets[k], out=outs[k]) for k in range(len(sets))]
+    torch.cuda.synchronize()
+
+    def step(i):
+        calls[i % len(sets)]()
+
+    n_warm = warm_up(step, args, torch)
+    whole0, whole1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    whole0.record()
+    for i in range(args.steps):
+        step(i)
+    whole1.record()
+    torch.cuda.synchronize()
+    us_per_call = whole0.elapsed_time(whole1) / args.steps * 1e3
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    launch_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps
+    same = all(all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(outs[0], o))
+               for o in outs[1:])
+    nbytes, flop = prolog_work(inp)
+    gbps = nbytes / (launch_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash(("prolog_kernels.hip", "prolog_internal.h"))
+    rec = {
+        "metric": f"us/call + GB/s vs HBM roofline, {args.workload}",
+        "value": round(us_per_call, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": n_warm,
+        "ms_per_step": round(us_per_call / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": inp.tokens, "hidden": inp.hidden,
+                   "q_lora_rank": inp.q_lora_rank, "n_q": inp.n_q, "qk_nope_dim": inp.nope_dim,
+                   "cold_sets": len(sets)},
+        "kernel_ms_mean": round(launch_ms, 5),
+        "algorithmic_bytes_per_call": nbytes,
+        "algorithmic_flop_per_call": flop,
+        "tflops": round(flop / (launch_ms * 1e-3) / 1e12, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profile(src_hash, f"{args.workload}_traffic.txt")},
+        "rotated_outputs_identical": bool(same),
+        "kernel_source_sha256": src_hash,
+    }
+    if args.cpu_seconds > 0:
+        # the oracle over the whole call until the budget is spent; its first result is checked
+        # against the GPU's outputs element by element
+        got = [PO.bf16_bits_to_f64(o.cpu().view(torch.int16).numpy().view(np.uint16)) for o in outs[0]]
+        t0 = time.perf_counter()
+        runs, bad = 0, 0
+        while runs == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            want = PO.mla_prolog(inp.x, inp.w_dq, inp.gamma_cq, inp.w_uq_qr, inp.w_uk, inp.w_dkv_kr, inp.gamma_ckv,
+                                 inp.positions, inp.rope_cos, inp.rope_sin, inp.eps, inp.n_q)
+            if runs == 0:
+                for g, w in zip(got, want):
+                    w = w.reshape(g.shape)
+                    bad += int((np.abs(g - w) > 1e-4 + 5e-3 * np.abs(w)).sum())
+            runs += 1
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(el / runs * 1e6, 1), "unit": "us/call",
+                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "sample": f"the whole call ({inp.tokens} tokens) {runs} times in {el:.1f} s",
+                               "sample_elements_bad": bad}
+    print(json.dumps(rec), flush=True)
+
+
 def copy_calibration(mib: int, steps: int):
     """A plain copy of a known size: it reads and writes exactly mib MiB per launch, so the HBM
     byte counters read on it give the factor that turns their readings into bytes."""
@@ -863,7 +971,7 @@ def main():
     ap.add_argument("--warmup-seconds", type=float, default=1.0)
     ap.add_argument("--workload", default="decode_b64_s2_bf16",
                     choices=sorted(WORKLOADS) + ["indexer_b64_s2", "decode_step_b64_s2"] + sorted(CACHE_WORKLOADS)
-                    + sorted(WINDOW_WORKLOADS) + sorted(COMPRESS_WORKLOADS))
+                    + sorted(WINDOW_WORKLOADS) + sorted(COMPRESS_WORKLOADS) + sorted(PROLOG_WORKLOADS))
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated for a cold cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget (0 disables)")
     ap.add_argument("--seed", type=int, default=0)
@@ -899,6 +1007,9 @@ def main():
         return
     if args.workload in COMPRESS_WORKLOADS:
         bench_compress(args)
+        return
+    if args.workload in PROLOG_WORKLOADS:
+        bench_prolog(args)
         return
     if args.workload == "decode_step_b64_s2":
         bench_decode_step(args)
@@ -962,7 +1073,8 @@ def main():
     achieved_gbps = nbytes / (mean_launch_ms * 1e-3) / 1e9
     achieved_tflops = flop / (mean_launch_ms * 1e-3) / 1e12
     src_hash = kernel_source_hash()
-    traffic = traffic_from_profile(src_hash) if args.workload == "decode_b64_s2_bf16" else None
+    traffic = traffic_from_profile(src_hash, "sfa_decode_b64_s2_bf16_traffic.txt" if args.workload == "decode_b64_s2_bf16"
+                                   else f"{args.workload}_traffic.txt")
     if dtype == "bf16" and not is_prefill:
         roofline = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}

@@ -428,10 +428,10 @@ int sfa_compress(const sfa_compress_dims* dims, const float* kv, const float* sc
  */
 typedef struct {
   int32_t tokens;               /* T >= 0 new tokens                                          */
-  int32_t hidden;               /* H: a multiple of 64 in [256, 65536]                        */
-  int32_t q_lora_rank;          /* Q: a multiple of 64 in [256, 4096]                         */
+  int32_t hidden;               /* H: a multiple of 64 in [64, 65536]                         */
+  int32_t q_lora_rank;          /* Q: a multiple of 64 in [64, 4096]                          */
   int32_t n_q;                  /* query heads in [1, 128]                                    */
-  int32_t qk_nope_dim;          /* Dn: per-head nope width before absorption, a multiple of 16
+  int32_t qk_nope_dim;          /* Dn: per-head nope width before absorption, a multiple of 64
                                    in [64, 512]                                               */
   int32_t rope_positions;       /* rows of rope_cos and rope_sin, >= 1                        */
   float eps;                    /* RMSNorm epsilon, finite and >= 0                           */

@@ -29,31 +29,28 @@ bool overlaps(const void* p, size_t n, const void* q, size_t m) {
 int check(const sfa_prolog_dims* d) {
   if (!d) return SFA_ERR_NULL;
   if (d->tokens < 0 || d->tokens > (1 << 20)) return SFA_ERR_DIMS;
-  // every wave's k range must hold at least 4 steps of 16 (its load pipeline depth)
-  if (d->hidden < 256 || d->hidden > (1 << 16) || d->hidden % 64) return SFA_ERR_DIMS;
-  if (d->q_lora_rank < 256 || d->q_lora_rank > 4096 || d->q_lora_rank % 64) return SFA_ERR_DIMS;
+  // the GEMMs walk k in chunks of 64
+  if (d->hidden < 64 || d->hidden > (1 << 16) || d->hidden % 64) return SFA_ERR_DIMS;
+  if (d->q_lora_rank < 64 || d->q_lora_rank > 4096 || d->q_lora_rank % 64) return SFA_ERR_DIMS;
   if (d->n_q < 1 || d->n_q > SFA_MAX_HEADS) return SFA_ERR_DIMS;
-  if (d->qk_nope_dim < 64 || d->qk_nope_dim > 512 || d->qk_nope_dim % 16) return SFA_ERR_DIMS;
+  if (d->qk_nope_dim < 64 || d->qk_nope_dim > 512 || d->qk_nope_dim % 64) return SFA_ERR_DIMS;
   if (d->rope_positions < 1) return SFA_ERR_DIMS;
   if (!(d->eps >= 0.0f) || !isfinite(d->eps)) return SFA_ERR_DIMS;
   return SFA_OK;
 }
 
-// k splits of the down-projections: enough workgroups for every compute unit, each split's
-// k range a whole number of 64-wide units (16 per wave) and at least 4 of them, so that every
-// wave has the 4 k-steps its load pipeline keeps in flight
+// k splits of the down-projections: as many as keep the launch within one workgroup per
+// compute unit (a second round of workgroups would run on an almost idle GPU), each split a
+// whole number of 64-wide chunks
 int down_splits(const sfa_prolog_dims* d) {
-  const int tiles = (d->q_lora_rank + kPrLatent + kPrRope) / kPrFeatTile;
-  const int tok_blocks = (d->tokens + kPrTokBlock - 1) / kPrTokBlock;
+  const int feat = 32 * kPrFb0;
+  const int64_t tiles = (d->q_lora_rank + kPrLatent + kPrRope + feat - 1) / feat;
+  const int64_t tok_blocks = (d->tokens + kPrTokBlock - 1) / kPrTokBlock;
   const int units = d->hidden / 64;
-  int s = 1;
-  while ((int64_t)tiles * tok_blocks * s < kTargetWorkgroups) {
-    int n = s + 1;
-    while (n <= units && units % n) ++n;
-    if (n > units || units / n < 4) break;
-    s = n;
-  }
-  return s;
+  int best = 1;
+  for (int s = 1; s <= units; ++s)
+    if (units % s == 0 && tiles * tok_blocks * s <= kTargetWorkgroups) best = s;
+  return best;
 }
 
 struct Layout {

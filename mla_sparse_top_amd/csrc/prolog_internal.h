@@ -11,8 +11,11 @@ namespace sfa {
 constexpr int kPrLatent = 512;      // latent row (kv_lora_rank)
 constexpr int kPrRope = 64;         // rotary channels
 constexpr int kPrTokBlock = 128;    // tokens per workgroup (4 MFMA blocks of 32)
-constexpr int kPrFeatTile = 64;     // features per workgroup in the split-K GEMMs (2 MFMA blocks)
-constexpr int kPrAbsTile = 256;     // features per workgroup of the absorption (4 waves x 64)
+// 32-feature MFMA blocks per workgroup of each GEMM: the down-projections (64 features; with
+// their k split, 33 tiles x 7 splits at hidden 7168), the query up-projection (96 features: 256
+// tiles at 128 heads) and the absorption (256 of a head's 512 channels: 256 tiles at 128 heads)
+constexpr int kPrFb0 = 2, kPrFb1 = 3, kPrFb2 = 8;
+constexpr int prolog_feat_blocks(int mode) { return mode == 0 ? kPrFb0 : mode == 1 ? kPrFb1 : kPrFb2; }
 
 // One launch of the weight-streaming GEMM: out[t, f] = sum over k of W[f, k] * B[t, k] for the
 // workgroup's features, tokens and k range; the epilogue depends on the mode.

@@ -12,10 +12,9 @@
 //
 // How it is computed here (four launches on one stream):
 //   1. prolog_gemm_kernel<0>: both down-projections as one weight-streaming GEMM over the
-//      features of w_dq then w_dkv_kr. Weights go from HBM straight into the A operand of
-//      v_mfma_f32_32x32x16_bf16 (32 features x 16 k per instruction), activations into the B
-//      operand (32 tokens). A workgroup owns 64 features x 128 tokens x one k range; its four
-//      waves split that range and sum their accumulators through LDS; the k ranges of one
+//      features of w_dq then w_dkv_kr: weights in the A operand of v_mfma_f32_32x32x16_bf16
+//      (32 features x 16 k), activations in the B operand (32 tokens), both staged through
+//      LDS. A workgroup owns 64 features x 128 tokens x one k range; the k ranges of one
 //      feature tile are separate workgroups that write fp32 partial sums.
 //   2. prolog_norm_kernel: one workgroup per token sums the partials, applies both RMSNorms
 //      and the key's RoPE, and writes cq as a bf16 hi + lo pair (hi = bf16(v), lo = bf16(v -
@@ -23,9 +22,9 @@
 //   3. prolog_gemm_kernel<1>: the query up-projection over cq (two MFMAs per step, hi and lo).
 //      Its epilogue writes each head's nope part as a hi + lo pair and rotates the rotary part.
 //   4. prolog_gemm_kernel<2>: the absorption, per head a 512 x dn weight over the nope part
-//      (hi and lo), each wave owning 64 of a workgroup's 256 output channels.
-// Loads use buffer descriptors whose range ends at the last token, so the rows of a partial
-// token block read zeros and are never stored.
+//      (hi and lo), in tiles of 64 output channels.
+// Operands reach LDS through buffer descriptors whose range ends at the last token (or weight
+// row), so the rows of a partial block read zeros, and their outputs are never stored.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -41,21 +40,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kFm = 2;     // 32-feature MFMA blocks per wave
-constexpr int kTn = 4;     // 32-token MFMA blocks per wave
-constexpr int kDepth = 4;  // k-steps whose loads are in flight ahead of the MFMAs
-constexpr int kTiles = kFm * kTn;
 constexpr int kNormMaxChunks = 5;  // float4 chunks per thread in the norm step: q_rank <= 4096
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-__device__ __forceinline__ bf16x8 load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
 
 // two floats -> two bf16 (round to nearest even) in one dword, first in the low half
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -88,182 +76,296 @@ __device__ __forceinline__ u32x2 rope4(const floatx4 v, int p, int np, const flo
                pack2(v[2] * c1 - v[3] * s1, v[2] * s1 + v[3] * c1)};
 }
 
+// Buffer resource over [base, base + bytes): loads at or past the end read zeros.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  // dword 2: the size in bytes; dword 3: raw-buffer configuration (32-bit data format, no
+  // swizzle, no stride)
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// LDS-DMA: lane L's 16 bytes from the buffer at voff + soff land at LDS address lds + 16 * L.
+// M0 is saved and restored around the instruction and needs one wait state after its write.
+// Issued from inline asm so that the compiler does not wait for the whole vector-memory queue
+// before LDS reads; completion is waited for explicitly (wait_vmcnt), visibility to the other
+// waves comes from the barrier after that wait.
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most n groups of kPer vector-memory instructions are outstanding (n <= 6).
+template <int kPer>
+__device__ __forceinline__ void wait_groups(int n) {
+  if (n >= 6)
+    wait_vmcnt<6 * kPer>();
+  else if (n == 5)
+    wait_vmcnt<5 * kPer>();
+  else if (n == 4)
+    wait_vmcnt<4 * kPer>();
+  else if (n == 3)
+    wait_vmcnt<3 * kPer>();
+  else if (n == 2)
+    wait_vmcnt<2 * kPer>();
+  else if (n == 1)
+    wait_vmcnt<kPer>();
+  else
+    wait_vmcnt<0>();
+}
+
+// Workgroup barrier that orders LDS traffic only: outstanding DMA stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_s_barrier();
+}
+
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+__device__ __forceinline__ bf16x8 lds16(const lds_char_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
+}
+
 // Mode 0: down-projections (fp32 partials). Mode 1: query up-projection (B = cq hi/lo).
 // Mode 2: absorption (B = the heads' nope parts hi/lo).
-template <int kMode>
+//
+// A workgroup owns 32 * kFb features x 128 tokens and walks its k range in chunks of 64 (one
+// 128-byte line per row). Wave w owns tokens 32w .. 32w + 31 and all the workgroup's features,
+// so its accumulators are whole sums. Weight rows and token rows reach LDS by LDS-DMA, eight
+// rows x 128 bytes per instruction, the 16-byte piece p of row r stored at position p ^ (r & 7)
+// so that the operand reads are free of bank conflicts. Waves 0 and 1 issue the weights' DMA
+// (from HBM, through a deep ring), waves 2 and 3 the token rows' (from L2, a shallow ring):
+// a wave's loads complete in issue order, so a wave that waits for one stream never waits
+// for the other. The outputs are staged through LDS and stored as whole rows.
+template <int kMode, int kFb>
+struct GemmShape {
+  static constexpr bool kLo = kMode != 0;
+  static constexpr int kFeat = 32 * kFb;
+  static constexpr int kWBytes = kFeat * 128;                  // weight rows of a chunk
+  static constexpr int kABytes = kPrTokBlock * 128;            // token rows of a chunk (hi or lo)
+  static constexpr int kAStage = kABytes * (kLo ? 2 : 1);
+  static constexpr int kTStages = kMode == 2 ? 2 : 3;
+  static constexpr int kWFit = (152 * 1024 - kTStages * kAStage) / kWBytes;
+  static constexpr int kWStages = kWFit > 8 ? 8 : kWFit;
+  static constexpr int kLdsBytes = kWStages * kWBytes + kTStages * kAStage;
+  static constexpr int kWDma = 2 * kFb;                        // per weight wave and chunk
+  static constexpr int kTDma = 16 * (kLo ? 2 : 1) / 2;         // per token wave and chunk
+  // output staging: 128 token rows of the workgroup's features (fp32 partials, bf16 q_nope),
+  // each row padded by 16 bytes so that the 32 rows a store instruction touches spread over
+  // the LDS banks
+  static constexpr int kOutRow = kFeat * (kMode == 0 ? 4 : 2);
+  static constexpr int kOutStride = kOutRow + 16;
+  static_assert(kWStages >= 2 && kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(kMode == 1 || kPrTokBlock * kOutStride <= kLdsBytes, "output staging fits");
+  static_assert(kWDma * (kWStages - 2) <= 63 && kTDma * (kTStages - 2) <= 63, "vmcnt range");
+};
+
+template <int kMode, int kFb>
 __global__ void __launch_bounds__(kThreads, 1) prolog_gemm_kernel(const PrologGemmArgs a) {
-  constexpr bool kLo = kMode != 0;
-  constexpr bool kSplitWaves = kMode != 2;
-  __shared__ floatx4 red[kSplitWaves ? 4 : 1][kTiles * 4][64];
+  using G = GemmShape<kMode, kFb>;
+  constexpr bool kLo = G::kLo;
+  constexpr int kFeat = G::kFeat, kWBytes = G::kWBytes, kABytes = G::kABytes, kAStage = G::kAStage;
+  constexpr int kWStages = G::kWStages, kTStages = G::kTStages;
+  __shared__ __attribute__((aligned(1024))) char smem[G::kLdsBytes];
+  const lds_char_t* lds = (const lds_char_t*)smem;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  const uint32_t abase = lds_base + kWStages * kWBytes;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 31, hb = lane >> 5;
 
-  // workgroup -> (token block, feature tile / head, k split)
+  // workgroup -> (token block, feature tile or head and tile, k split)
   int id = blockIdx.x;
   int split = 0, head = 0, f0;
   if (kMode == 2) {
-    const int half = id % (kPrLatent / kPrAbsTile);
-    id /= kPrLatent / kPrAbsTile;
+    constexpr int per_head = kPrLatent / kFeat;
+    f0 = (id % per_head) * kFeat;
+    id /= per_head;
     head = id % a.n_q;
     id /= a.n_q;
-    f0 = half * kPrAbsTile + wave * (kFm * 32);
   } else {
     split = id % a.n_split;
     id /= a.n_split;
-    const int tiles = (a.n_feat + kPrFeatTile - 1) / kPrFeatTile;
-    f0 = (id % tiles) * kPrFeatTile;
+    const int tiles = (a.n_feat + kFeat - 1) / kFeat;
+    f0 = (id % tiles) * kFeat;
     id /= tiles;
   }
   const int tb0 = id * kPrTokBlock;
   const int rows = min(kPrTokBlock, a.tokens - tb0);
 
-  // weights of this tile: rows f0 .. f0 + 63 (mode 2: head's 512 x dn block)
+  // weights of this tile: kFeat rows (features f0 ..) of k elements
   const uint16_t* wbase;
   uint32_t wrows;
   if (kMode == 2) {
     wbase = a.w0 + ((size_t)head * kPrLatent + f0) * a.k;
-    wrows = kFm * 32;
+    wrows = kFeat;
   } else if (f0 < a.f_split) {
     wbase = a.w0 + (size_t)f0 * a.k;
-    wrows = min(kPrFeatTile, a.f_split - f0);
+    wrows = min(kFeat, a.f_split - f0);
   } else {
     wbase = a.w1 + (size_t)(f0 - a.f_split) * a.k;
-    wrows = min(kPrFeatTile, a.n_feat - f0);
+    wrows = min(kFeat, a.n_feat - f0);
   }
-  const __amdgpu_buffer_rsrc_t rw = rsrc(wbase, wrows * (uint32_t)a.k * 2u);
-  const size_t boff = (size_t)tb0 * a.b_stride + (kMode == 2 ? (size_t)head * a.dn : 0);
-  const uint32_t bbytes = (uint32_t)(((size_t)(rows - 1) * a.b_stride + a.k) * 2);
-  const __amdgpu_buffer_rsrc_t rbh = rsrc(a.b_hi + boff, bbytes);
-  const __amdgpu_buffer_rsrc_t rbl = rsrc(kLo ? a.b_lo + boff : a.b_hi + boff, bbytes);
+  const int kc0 = kMode == 2 ? 0 : split * a.k_chunk;
+  const int nch = (kMode == 2 ? a.k : a.k_chunk) / 64;
 
-  // this wave's k range
-  const int kw = kSplitWaves ? a.k_chunk / 4 : a.k;
-  const int kw0 = kSplitWaves ? split * a.k_chunk + wave * kw : 0;
-  const int steps = kw / 16;
+  // DMA lane geometry: lane L carries row (L >> 3) of an 8-row group and stores its piece at
+  // position L & 7, so it loads piece (L & 7) ^ (L >> 3) of its row
+  const uint32_t drow = (uint32_t)(lane >> 3);
+  const uint32_t dpiece = 16u * ((uint32_t)(lane & 7) ^ drow);
+  const bool w_wave = wave < 2;
+  u32x4 rs0, rs1;
+  uint32_t row_bytes;
+  if (w_wave) {
+    rs0 = make_rsrc(wbase, wrows * (uint32_t)a.k * 2u);
+    rs1 = rs0;
+    row_bytes = (uint32_t)a.k * 2u;
+  } else {
+    const size_t boff = (size_t)tb0 * a.b_stride + (kMode == 2 ? (size_t)head * a.dn : 0);
+    const uint32_t bbytes = (uint32_t)(((size_t)(rows - 1) * a.b_stride + a.k) * 2);
+    rs0 = make_rsrc(a.b_hi + boff, bbytes);
+    rs1 = make_rsrc(kLo ? a.b_lo + boff : a.b_hi + boff, bbytes);
+    row_bytes = (uint32_t)a.b_stride * 2u;
+  }
+  const int half = wave & 1;  // which half of the rows this wave's DMA covers
 
-  uint32_t voa[kFm], vob[kTn];
+  // chunk c's DMA share of this wave: weight waves take 8-row groups half, half + 2, ... of the
+  // kFeat weight rows; token waves take token rows 64 * half .. + 63 (hi, then lo)
+  auto issue = [&](int c) __attribute__((always_inline)) {
+    const uint32_t kb = (uint32_t)(kc0 + 64 * c) * 2u;
+    if (w_wave) {
+      const uint32_t st = lds_base + (uint32_t)((c % kWStages) * kWBytes);
 #pragma unroll
-  for (int fm = 0; fm < kFm; ++fm) voa[fm] = (uint32_t)(((32 * fm + r) * a.k + 8 * hb) * 2);
-#pragma unroll
-  for (int tb = 0; tb < kTn; ++tb) vob[tb] = (uint32_t)(((size_t)(32 * tb + r) * a.b_stride + 8 * hb) * 2);
-
-  floatx16 acc[kFm][kTn];
-#pragma unroll
-  for (int fm = 0; fm < kFm; ++fm)
-#pragma unroll
-    for (int tb = 0; tb < kTn; ++tb) acc[fm][tb] = floatx16{};
-
-  bf16x8 ra[kDepth][kFm], rb[kDepth][kTn], rl[kDepth][kLo ? kTn : 1];
-  auto load = [&](int slot, int s) __attribute__((always_inline)) {
-    const uint32_t kb = (uint32_t)(kw0 + 16 * s) * 2u;
-#pragma unroll
-    for (int fm = 0; fm < kFm; ++fm) ra[slot][fm] = load8(rw, voa[fm], kb);
-#pragma unroll
-    for (int tb = 0; tb < kTn; ++tb) {
-      rb[slot][tb] = load8(rbh, vob[tb], kb);
-      if (kLo) rl[slot][tb] = load8(rbl, vob[tb], kb);
-    }
-  };
-  auto mfmas = [&](int slot) __attribute__((always_inline)) {
-#pragma unroll
-    for (int fm = 0; fm < kFm; ++fm)
-#pragma unroll
-      for (int tb = 0; tb < kTn; ++tb) {
-        acc[fm][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot][fm], rb[slot][tb], acc[fm][tb], 0, 0, 0);
-        if (kLo)
-          acc[fm][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot][fm], rl[slot][tb], acc[fm][tb], 0, 0, 0);
+      for (int i = 0; i < 2 * kFb; ++i) {
+        const uint32_t row0 = (uint32_t)(8 * (half + 2 * i));
+        dma16(rs0, (row0 + drow) * row_bytes + dpiece, kb, st + row0 * 128u);
       }
+    } else {
+      const uint32_t st = abase + (uint32_t)((c % kTStages) * kAStage);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t row0 = (uint32_t)(64 * half + 8 * i);
+        dma16(rs0, (row0 + drow) * row_bytes + dpiece, kb, st + row0 * 128u);
+        if (kLo) dma16(rs1, (row0 + drow) * row_bytes + dpiece, kb, st + kABytes + row0 * 128u);
+      }
+    }
   };
-  // steps >= kDepth (the host keeps every wave's k range at least kDepth * 16 long): the loads
-  // of kDepth steps are in flight while a step's MFMAs run; the main loop has no branches, so
-  // each step waits only for its own loads
+  const int depth = w_wave ? kWStages : kTStages;
+  // wait for this wave's DMA of chunk c, leaving the later chunks it has issued in flight
+  auto wait_for = [&](int c) __attribute__((always_inline)) {
+    const int ahead = min(depth - 2, nch - 1 - c);
+    if (w_wave)
+      wait_groups<G::kWDma>(ahead);
+    else
+      wait_groups<G::kTDma>(ahead);
+  };
+
+  floatx16 acc[kFb];
 #pragma unroll
-  for (int j = 0; j < kDepth; ++j) load(j, j);
-  int s = 0;
-  for (; s + 2 * kDepth <= steps; s += kDepth) {
+  for (int fb = 0; fb < kFb; ++fb) acc[fb] = floatx16{};
+
+  for (int c = 0; c < depth - 1; ++c)
+    if (c < nch) issue(c);
+  const int wave_row = 32 * wave + r;
+  const uint32_t rsw = 16u * (uint32_t)(r & 7);
+  for (int c = 0; c < nch; ++c) {
+    wait_for(c);
+    lds_barrier();  // chunk c visible to every wave; chunk c - 1's slots free again
+    if (c + depth - 1 < nch) issue(c + depth - 1);
+    const lds_char_t* ws = lds + (c % kWStages) * kWBytes;
+    const lds_char_t* as = lds + kWStages * kWBytes + (c % kTStages) * kAStage + wave_row * 128;
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
-      mfmas(j);
-      load(j, s + j + kDepth);
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t pos = (16u * (uint32_t)(2 * s + hb)) ^ rsw;
+      const bf16x8 bv = lds16(as + pos);
+      bf16x8 lv;
+      if (kLo) lv = lds16(as + kABytes + pos);
+#pragma unroll
+      for (int fb = 0; fb < kFb; ++fb) {
+        const bf16x8 av = lds16(ws + (32 * fb + r) * 128 + pos);
+        acc[fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[fb], 0, 0, 0);
+        if (kLo) acc[fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, lv, acc[fb], 0, 0, 0);
+      }
     }
   }
-#pragma unroll
-  for (int j = 0; j < kDepth; ++j) {
-    mfmas(j);
-    if (s + j + kDepth < steps) load(j, s + j + kDepth);
-  }
-  s += kDepth;
-#pragma unroll
-  for (int j = 0; j < kDepth; ++j)
-    if (s + j < steps) mfmas(j);
 
-  // Output tile (fm, tb): lane holds token 32*tb + r and, in register 4*g + e, feature
-  // 32*fm + 8*g + 4*hb + e.
-  auto epilogue = [&](int fm, int tb, const floatx4 (&v)[4]) __attribute__((always_inline)) {
-    const int t = tb0 + 32 * tb + r;
+  // Output block fb: lane holds token 32 * wave + r and, in register 4 * g + e, feature
+  // 32 * fb + 8 * g + 4 * hb + e.
+  if (kMode == 1) {
+    const int t = tb0 + wave_row;
     if (t >= a.tokens) return;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int f = f0 + 32 * fm + 8 * g + 4 * hb;
-      if (kMode == 0) {
-        *reinterpret_cast<floatx4*>(a.part + ((size_t)split * a.tokens + t) * a.n_feat + f) = v[g];
-      } else if (kMode == 1) {
+    for (int fb = 0; fb < kFb; ++fb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const floatx4 v = floatx4{acc[fb][4 * g], acc[fb][4 * g + 1], acc[fb][4 * g + 2], acc[fb][4 * g + 3]};
+        const int f = f0 + 32 * fb + 8 * g + 4 * hb;
         if (f >= a.n_feat) continue;
         const int per = a.dn + kPrRope;
         const int h = f / per, j = f - h * per;
         const size_t row = (size_t)t * a.n_q + h;
         if (j < a.dn) {
           u32x2 hi, lo;
-          split4(v[g], hi, lo);
+          split4(v, hi, lo);
           *reinterpret_cast<u32x2*>(a.qn_hi + row * a.dn + j) = hi;
           *reinterpret_cast<u32x2*>(a.qn_lo + row * a.dn + j) = lo;
         } else {
           const int jr = j - a.dn;
           *reinterpret_cast<u32x2*>(a.q_rope + row * kPrRope + jr) =
-              rope4(v[g], a.positions[t], a.rope_positions, a.rope_cos, a.rope_sin, jr >> 1);
+              rope4(v, a.positions[t], a.rope_positions, a.rope_cos, a.rope_sin, jr >> 1);
         }
-      } else {
-        const size_t row = (size_t)t * a.n_q + head;
-        *reinterpret_cast<u32x2*>(a.q_nope + row * kPrLatent + f) =
-            u32x2{pack2(v[g][0], v[g][1]), pack2(v[g][2], v[g][3])};
       }
     }
-  };
+    return;
+  }
 
-  if (kSplitWaves) {
-    // sum the four waves' partial tiles: every wave stores its tiles, then wave w sums tiles
-    // 2w and 2w + 1 over the four copies and runs their epilogue
+  // modes 0 and 2: stage the wave's 32 token rows in LDS (its own rows: no other wave reads
+  // them), then store whole rows, 16 bytes per lane
+  wait_vmcnt<0>();
+  lds_barrier();  // every wave is done with the operand slots
+  constexpr int kRow = G::kOutRow, kStride = G::kOutStride;
+  char* orow = smem + (size_t)wave * 32 * kStride;
 #pragma unroll
-    for (int i = 0; i < kTiles; ++i)
+  for (int fb = 0; fb < kFb; ++fb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const floatx16& x = acc[i / kTn][i % kTn];
-        red[wave][i * 4 + g][lane] = floatx4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
-      }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = 2 * wave + q;
-      floatx4 v[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        v[g] = red[0][i * 4 + g][lane];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) v[g] += red[w][i * 4 + g][lane];
-      }
-      epilogue(i / kTn, i % kTn, v);
+    for (int g = 0; g < 4; ++g) {
+      const int fl = 32 * fb + 8 * g + 4 * hb;  // feature within the tile
+      if (kMode == 0)
+        *reinterpret_cast<floatx4*>(orow + r * kStride + fl * 4) =
+            floatx4{acc[fb][4 * g], acc[fb][4 * g + 1], acc[fb][4 * g + 2], acc[fb][4 * g + 3]};
+      else
+        *reinterpret_cast<u32x2*>(orow + r * kStride + fl * 2) =
+            u32x2{pack2(acc[fb][4 * g], acc[fb][4 * g + 1]), pack2(acc[fb][4 * g + 2], acc[fb][4 * g + 3])};
     }
-  } else {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are done before its reads
+  constexpr int kPieces = kRow / 16;   // 16-byte pieces per row
+  const int nvalid = kMode == 0 ? min(kFeat, a.n_feat - f0) * 4 / 16 : kPieces;
 #pragma unroll
-    for (int i = 0; i < kTiles; ++i) {
-      const floatx16& x = acc[i / kTn][i % kTn];
-      floatx4 v[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) v[g] = floatx4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
-      epilogue(i / kTn, i % kTn, v);
-    }
+  for (int i = 0; i < 32 * kPieces / 64; ++i) {
+    const int idx = i * 64 + lane;
+    const int rr = idx / kPieces, pc = idx % kPieces;
+    const int t = tb0 + 32 * wave + rr;
+    if (t >= a.tokens || pc >= nvalid) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(orow + rr * kStride + pc * 16);
+    char* dst;
+    if (kMode == 0)
+      dst = reinterpret_cast<char*>(a.part + ((size_t)split * a.tokens + t) * a.n_feat + f0) + pc * 16;
+    else
+      dst = reinterpret_cast<char*>(a.q_nope + ((size_t)t * a.n_q + head) * kPrLatent + f0) + pc * 16;
+    *reinterpret_cast<u32x4*>(dst) = v;
   }
 }
 
@@ -284,20 +386,28 @@ __global__ void __launch_bounds__(kThreads) prolog_norm_kernel(const PrologNormA
   const int nf = a.q_rank + kPrLatent + kPrRope;
   const int nq4 = a.q_rank / 4, nkv4 = nq4 + kPrLatent / 4, nch = nf / 4;
   floatx4 v[kNormMaxChunks];
+#pragma unroll
+  for (int i = 0; i < kNormMaxChunks; ++i) v[i] = floatx4{};
+  // the splits' partials: the chunks' loads of one split are independent, and the split loop
+  // is unrolled, so all of them are in flight together
+#pragma unroll 4
+  for (int s = 0; s < a.n_split; ++s) {
+    const float* src = a.part + ((size_t)s * a.tokens + t) * nf;
+#pragma unroll
+    for (int i = 0; i < kNormMaxChunks; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      if (c < nch) v[i] += *reinterpret_cast<const floatx4*>(src + 4 * c);
+    }
+  }
   float ssq = 0.f, skv = 0.f;
 #pragma unroll
   for (int i = 0; i < kNormMaxChunks; ++i) {
     const int c = threadIdx.x + i * kThreads;
-    v[i] = floatx4{};
-    if (c < nch) {
-      for (int s = 0; s < a.n_split; ++s)
-        v[i] += *reinterpret_cast<const floatx4*>(a.part + ((size_t)s * a.tokens + t) * nf + 4 * c);
-      const float sq = v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
-      if (c < nq4)
-        ssq += sq;
-      else if (c < nkv4)
-        skv += sq;
-    }
+    const float sq = v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+    if (c < nq4)
+      ssq += sq;
+    else if (c < nkv4)
+      skv += sq;
   }
   const float inv_q = 1.0f / sqrtf(block_sum(ssq, sh) / (float)a.q_rank + a.eps);
   const float inv_kv = 1.0f / sqrtf(block_sum(skv, sh) / (float)kPrLatent + a.eps);
@@ -333,17 +443,18 @@ __global__ void __launch_bounds__(kThreads) prolog_norm_kernel(const PrologNormA
 }  // namespace
 
 hipError_t launch_prolog_gemm(const PrologGemmArgs& a, int mode, hipStream_t stream) {
+  const int feat = 32 * prolog_feat_blocks(mode);
   int grid;
   if (mode == 2)
-    grid = a.tok_blocks * a.n_q * (kPrLatent / kPrAbsTile);
+    grid = a.tok_blocks * a.n_q * (kPrLatent / feat);
   else
-    grid = a.tok_blocks * ((a.n_feat + kPrFeatTile - 1) / kPrFeatTile) * a.n_split;
+    grid = a.tok_blocks * ((a.n_feat + feat - 1) / feat) * a.n_split;
   if (mode == 0)
-    hipLaunchKernelGGL(prolog_gemm_kernel<0>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prolog_gemm_kernel<0, kPrFb0>), dim3(grid), dim3(kThreads), 0, stream, a);
   else if (mode == 1)
-    hipLaunchKernelGGL(prolog_gemm_kernel<1>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prolog_gemm_kernel<1, kPrFb1>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(prolog_gemm_kernel<2>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prolog_gemm_kernel<2, kPrFb2>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -626,6 +626,14 @@ def swa_decode(seed: int = 0, kv_dtype: str = "bf16") -> WindowInputs:
                            kv_dtype=kv_dtype, seed=seed, name=f"swa_b64_s2_w128_{kv_dtype}")
 
 
+def cfa_decode(seed: int = 0, kv_dtype: str = "bf16") -> WindowInputs:
+    """CFA at the pages' timed shape with compress_ratio 128: a 128-position window plus every
+    causal compressed entry (63 or 64 of the 64 entries that 8K positions give at ratio 128; the
+    window size is a reading, the same as SWA's and SCFA's)."""
+    return window_generate(batch=64, s1=2, n_q=128, ori_lens=[8192] * 64, window=128, ratio=128, cmp_mode="all",
+                           kv_dtype=kv_dtype, seed=seed, name=f"cfa_b64_s2_w128_r128_{kv_dtype}")
+
+
 def scfa_decode(seed: int = 0, kv_dtype: str = "bf16") -> WindowInputs:
     """SCFA at the pages' timed shape with compress_ratio 4: a 128-position window plus 512
     compressed entries per token picked from the 2048 causal ones (window size and top-k are

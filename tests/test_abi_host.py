@@ -374,18 +374,18 @@ def _prolog_call(d, over=None, ws=0x7000000000, ws_bytes=None):
 
 
 def test_prolog_workspace_and_splits():
-    # decode shape: 33 feature tiles x 8 k splits of the down-projections; partials, cq and the
-    # per-head nope parts as hi/lo pairs
+    # decode shape: 33 feature tiles x 7 k splits of the down-projections (231 workgroups, one
+    # round on 256 compute units); partials, cq and the per-head nope parts as hi/lo pairs
     d = _prolog_dims()
-    part = 8 * 128 * (1536 + 576) * 4
+    part = 7 * 128 * (1536 + 576) * 4
     cq = 2 * 128 * 1536 * 2
     qn = 2 * 128 * 128 * 128 * 2
     assert sfa.prolog_workspace_size(d) == part + cq + qn
     assert sfa.prolog_workspace_size(_prolog_dims(tokens=0)) == 0
 
 
-@pytest.mark.parametrize("field,value", [("hidden", 128), ("hidden", 7200), ("q_lora_rank", 128), ("q_lora_rank", 8192),
-                                         ("n_q", 0), ("n_q", 129), ("qk_nope_dim", 48), ("qk_nope_dim", 136),
+@pytest.mark.parametrize("field,value", [("hidden", 0), ("hidden", 7200), ("q_lora_rank", 32), ("q_lora_rank", 8192),
+                                         ("n_q", 0), ("n_q", 129), ("qk_nope_dim", 48), ("qk_nope_dim", 144),
                                          ("rope_positions", 0), ("eps", -1.0), ("eps", float("nan")), ("tokens", -1)])
 def test_prolog_bad_dims_rejected(field, value):
     d = _prolog_dims(**{field: value})
