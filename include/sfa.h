@@ -95,8 +95,8 @@ typedef struct {
  * workspace pointer may be NULL.
  *
  * The workspace holds per-partition partial results and two counters per token (partitions
- * arrived, partials published). It needs no initialisation: the library clears the counters
- * it uses, on `stream`, before each launch. Two calls that may run at the same time need separate workspaces.
+ * arrived, partials published). It needs no initialisation: every call tags its counters with
+ * a 48-bit generation of its own, so whatever the buffer held before counts as zero.
  */
 int sfa_workspace_size(const sfa_dims* dims, int is_prefill, size_t* bytes_out);
 
@@ -143,8 +143,8 @@ int sfa_decode(const sfa_dims* dims,
  *     partition choice (256 partitions of 256 KB each).
  *   - Every call on one GPU shares that GPU's array: calls that may overlap on one GPU (on
  *     different streams, or from different threads) race and give wrong results. Calls queued
- *     on one stream are ordered and safe. The array keeps the last call's contents; each call
- *     clears, on `stream` and with a kernel, the counters it needs at zero.
+ *     on one stream are ordered and safe. The array keeps the last call's contents; nothing
+ *     in it needs clearing, since each call tags its counters with a generation of its own.
  */
 #define SFA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
 int sfa_decode_noalloc(const sfa_dims* dims,

@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "sfa_internal.h"
 
 namespace {
@@ -73,7 +75,7 @@ WsLayout ws_layout(const sfa_dims* d, int splits) {
   w.part_o = 0;
   w.part_ml = align_up(items * kPartialBytes, kAlignWs);
   w.counters = w.part_ml + align_up(items * kPartialMlBytes, kAlignWs);
-  w.total = w.counters + align_up(2 * groups * sizeof(int32_t), kAlignWs);
+  w.total = w.counters + align_up(2 * groups * sizeof(uint64_t), kAlignWs);
   return w;
 }
 
@@ -152,8 +154,14 @@ int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void*
     char* base = static_cast<char*>(ws);
     a.part_o = reinterpret_cast<float*>(base + lay.part_o);
     a.part_ml = reinterpret_cast<float*>(base + lay.part_ml);
-    a.counters = reinterpret_cast<int32_t*>(base + lay.counters);
+    a.counters = reinterpret_cast<uint64_t*>(base + lay.counters);
   }
+  // a generation of its own for every call (48 bits, never 0): the merge counters of earlier
+  // calls, or any other workspace contents, do not count for this one
+  static std::atomic<uint64_t> next_gen{1};
+  uint64_t gen = next_gen.fetch_add(1, std::memory_order_relaxed) & ((uint64_t{1} << 48) - 1);
+  if (gen == 0) gen = next_gen.fetch_add(1, std::memory_order_relaxed) & ((uint64_t{1} << 48) - 1);
+  a.gen = gen;
   a.num_rows = d->num_cache_rows;
   a.n_tokens = (int32_t)tokens;
   a.s1 = d->s1;

@@ -36,7 +36,9 @@ struct KernelArgs {
   uint16_t* out;              // bf16 bits (T, n_q, 512)
   float* part_o;              // (T, splits) x kPartialBytes
   float* part_ml;             // (T, splits, 128, 2): running max and sum per head
-  int32_t* counters;          // (2, T): arrivals, then partials published, per token
+  uint64_t* counters;         // (2, T): arrivals, then partials published, per token, each
+                              // tagged with the call's generation
+  uint64_t gen;               // this call's generation: 48 bits, never 0
   int64_t num_rows;
   int32_t n_tokens, s1, n_q, topk, mb, n_splits, chunk, reverse;
   float scale_log2;           // softmax_scale * log2(e)

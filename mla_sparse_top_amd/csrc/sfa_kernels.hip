@@ -18,10 +18,11 @@
 //     are then dense: padding costs no loads and no MFMA, and a tile of invalid slots never runs.
 //   * Gather: bf16 tiles go HBM -> LDS by DMA (buffer_load ... lds), one 1 KB nope row per wave
 //     instruction and eight 128 B rope rows per instruction, into four LDS stages, so a tile is
-//     requested two tile intervals before its S^T runs. INT8 codes and scales go by DMA into two
-//     code buffers; each wave dequantises the 8 rows it fetched (int8 -> fp32, times the fp32
-//     group scale, round-to-nearest-even to bf16) into the bf16 tile layout, under the P.V MFMAs
-//     of an earlier tile (three bf16 stages).
+//     requested three tile intervals before its S^T runs; a tile's DMA goes out in five pieces
+//     spread over the interval. INT8 codes and scales go by DMA into two code buffers; each wave
+//     dequantises the 8 rows it fetched (int8 -> fp32, times the fp32 group scale,
+//     round-to-nearest-even to bf16) into the bf16 tile layout, in small steps between the S^T
+//     MFMAs of the interval (three bf16 stages).
 //   * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: keys on M, heads on N, d as the reduction.
 //     Each lane then holds one head and 16 of a tile's 32 keys, so the softmax row max and row
 //     sum need one cross-lane step (v_permlane32_swap).
@@ -34,12 +35,13 @@
 //     bf16 hi + lo parts, two MFMAs on the same V fragment, so it keeps about 16 significant
 //     bits instead of 8: a single bf16 P does not meet the 5e-3 / 1e-4 accuracy standard when
 //     few keys carry the weight.
-//   * Software pipeline, one barrier per tile: while the MFMAs of tile i+1's S^T run, the VALU
-//     computes tile i's softmax and the wave issues the DMA of a later tile; then tile i's P.V
-//     MFMAs run.
-//   * Partitions of one token merge in the same kernel: each writes its unnormalised O, its
-//     running max and its running sum. The last to arrive (counted with a device-scope atomic)
-//     combines all of them in partition order, so the result does not depend on arrival order:
+//   * Software pipeline, one barrier per tile interval: the 36 S^T steps of tile i+1 alternate
+//     with the P.V steps of tile i's first 16 keys; then tile i's last 16 keys' P.V steps run
+//     while the VALU computes tile i+1's softmax, so MFMA and VALU work overlap in every phase.
+//   * Partitions of one token merge in the same kernel: each takes an arrival ticket; all but
+//     the last write their unnormalised O, running max and running sum and count themselves
+//     ready. The last to arrive combines all of them in partition order (its own from
+//     registers), so the result does not depend on arrival order:
 //     O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j. This is the prefill update rule applied
 //     across partitions.
 //   * Work items are mapped so that consecutive logical ids land on the same XCD and share its
@@ -91,6 +93,24 @@ constexpr int kQkSteps = (kNope + kRope) / 16;      // 36 k-steps of 16 over the
 constexpr int kQkDepthBf16 = 4;
 constexpr int kPvDepthBf16 = 3;
 constexpr int kOutWaveBytes = kHeadsPerWave * kNopeRowBytes;  // a wave's bf16 output rows (32 KB)
+// Per-token counters of the partition merge: 64-bit words holding (generation << 16) | count.
+// Every call carries its own 48-bit generation, so a word left by another call, or any other
+// contents of the workspace, carries another generation and counts as zero: the workspace needs
+// no clearing before a call. tagged_add returns the count before its increment.
+__device__ __forceinline__ uint64_t tagged_count(uint64_t* p, uint64_t gen) {
+  const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (v >> 16) == gen ? (v & 0xffffu) : 0;
+}
+__device__ __forceinline__ uint64_t tagged_add(uint64_t* p, uint64_t gen) {
+  uint64_t old = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const uint64_t cnt = (old >> 16) == gen ? (old & 0xffffu) : 0;
+    if (__hip_atomic_compare_exchange_strong(p, &old, (gen << 16) | (cnt + 1), __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return cnt;
+  }
+}
+
 // Bound on the last arriver's wait for the other partitions' partials (each try sleeps ~128
 // clocks): far beyond the time a partial takes to be stored.
 constexpr int kSpinLimit = 1 << 24;
@@ -1085,9 +1105,9 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   // that follows needs no release fence. (A release fence would write back this XCD's whole L2.)
   // The last arriver takes an agent-scope acquire fence, which drops stale lines from its own L2.
   const int S = a.n_splits;
-  int32_t* arrive = a.counters + t;
-  int32_t* ready = a.counters + a.n_tokens + t;
-  if (tid == 0) s_last = (__hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1) ? 1 : 0;
+  uint64_t* arrive = a.counters + t;
+  uint64_t* ready = a.counters + a.n_tokens + t;
+  if (tid == 0) s_last = tagged_add(arrive, a.gen) == (uint64_t)(S - 1) ? 1 : 0;
   lds_barrier();
   floatx4* part = reinterpret_cast<floatx4*>(a.part_o);
   constexpr int kWaveImage = 16 * 4 * 64;  // float4s per wave
@@ -1113,14 +1133,18 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
     lds_barrier();
-    if (tid == 0) __hip_atomic_fetch_add(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) tagged_add(ready, a.gen);
     return;
   }
   if (tid == 0) {
     for (int spin = 0; spin < kSpinLimit; ++spin) {
-      if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S - 1) break;
+      if (tagged_count(ready, a.gen) >= (uint64_t)(S - 1)) break;
       __builtin_amdgcn_s_sleep(2);
     }
+    // every partition of this token has taken its ticket and counted itself ready: nothing
+    // else touches the two words in this call, and cleared they cannot match a later call
+    __hip_atomic_store(arrive, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ready, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   lds_barrier();
   if (!wave_active) return;
@@ -1131,7 +1155,8 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   const float2* mlp = reinterpret_cast<const float2*>(a.part_ml) + (int64_t)t * S * kMaxHeads + h;
   float2 mlv[kMaxSplits];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) mlv[s] = (s == sp) ? make_float2(m_run, l_run) : mlp[(s < S ? s : S - 1) * kMaxHeads];
+  for (int s = 0; s < kMaxSplits; ++s)
+    mlv[s] = s == sp ? make_float2(m_run, l_run) : s < S ? mlp[s * kMaxHeads] : make_float2(-INFINITY, 0.f);
   float mmax = -INFINITY;
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) mmax = s < S ? fmaxf(mmax, mlv[s].x) : mmax;
@@ -1140,7 +1165,7 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     wv[s] = (s < S && mlv[s].x != -INFINITY) ? __builtin_amdgcn_exp2f(mlv[s].x - mmax) : 0.f;
-    lsum += wv[s] * mlv[s].y;
+    lsum += s < S ? wv[s] * mlv[s].y : 0.f;
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   const floatx4* pbase = part + ((int64_t)t * S * kWaves + wave) * kWaveImage + lane;
@@ -1197,13 +1222,6 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   flush_out();
 }
 
-// Clears the per-token arrival and ready counters before an attention launch that merges
-// partitions. A fill kernel rather than a memset, so that the call can be recorded in a graph.
-__global__ void __launch_bounds__(256) sfa_zero_kernel(int32_t* p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
-
 // rows_out[t, k] = physical row of slot k, or -1. The same predicate as the attention
 // kernel's compaction step.
 __global__ void __launch_bounds__(256) sfa_resolve_kernel(const ResolveArgs a) {
@@ -1225,15 +1243,6 @@ __global__ void __launch_bounds__(256) sfa_resolve_kernel(const ResolveArgs a) {
 }  // namespace
 
 hipError_t launch_attention(const KernelArgs& a, bool int8_cache, bool window_slots, hipStream_t stream) {
-  if (a.n_splits > 1) {
-    const int64_t n = 2 * (int64_t)a.n_tokens;
-    int32_t* counters = a.counters;
-    int64_t count = n;
-    void* zargs[] = {&counters, &count};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&sfa_zero_kernel),
-                                         dim3((unsigned)((n + 255) / 256)), dim3(256), zargs, 0, stream);
-    if (e != hipSuccess) return e;
-  }
   const dim3 grid((unsigned)(a.n_tokens * a.n_splits));
   const dim3 block(kThreads);
   KernelArgs copy = a;

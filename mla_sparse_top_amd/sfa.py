@@ -193,9 +193,9 @@ def num_splits(dims: SfaDims, is_prefill: bool = False) -> int:
     return st
 
 
-# One workspace per (device, stream), grown on demand. Each call clears the counters it uses on
-# its own stream before its kernels run, so calls queued on one stream can share a buffer; calls
-# on different streams may overlap, so they never share one.
+# One workspace per (device, stream), grown on demand. Calls queued on one stream run one after
+# the other and can share a buffer (each call tags its counters with a generation of its own, so
+# no clearing is needed); calls on different streams may overlap, so they never share one.
 _WORKSPACES: dict = {}
 
 
@@ -209,7 +209,7 @@ def get_workspace(device: torch.device, nbytes: int, stream=None) -> Optional[to
     key = (device.type, device.index, stream.cuda_stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        # The library clears what must start at zero on the call's stream, so no fill is needed.
+        # The contents need no initialisation (the library's counters are generation-tagged).
         # The allocator ties a block to the stream current at allocation; record the stream the
         # kernels use so that the block is not handed out again while they may still run.
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)

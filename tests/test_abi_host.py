@@ -73,7 +73,7 @@ def test_workspace_size_formula():
     items = tokens * 8
     part = items * 4 * 16 * 4 * 64 * 16   # 4 waves x 16 column blocks x 4 row quads x 64 lanes x float4
     ml = items * 128 * 2 * 4              # (max, sum) per head
-    cnt = 2 * tokens * 4                   # arrival and ready counters per token
+    cnt = 2 * tokens * 8                   # arrival and ready counters per token (64-bit, tagged)
 
     def up(x):
         return (x + 255) // 256 * 256

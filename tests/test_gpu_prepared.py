@@ -86,3 +86,37 @@ def test_concurrent_decodes_on_two_streams(sfa_lib):
             assert torch.equal(o.view(torch.int16), r.view(torch.int16))
     keys = [k for k in sfa_lib._WORKSPACES if k[2] in (streams[0].cuda_stream, streams[1].cuda_stream)]
     assert len(keys) == 2
+
+
+def test_workspace_contents_do_not_matter(sfa_lib):
+    """The merge counters in the workspace carry each call's own generation: a workspace full of
+    arbitrary bytes (or of an earlier call with other shapes) gives the same bits as a fresh one."""
+    import torch
+
+    inp = W.generate(batch=5, s1=2, n_q=128, act_seqs=[6000, 300, 4100, 2048, 8000], topk=2048, seed=41)
+    d = sfa_lib.to_device(inp)
+    args = (d["query_nope"], d["query_rope"], d["key_nope"], d["key_rope"], d["k_nope_scales"], d["topk_indices"],
+            d["block_table"], d["kv_act_seqs"], inp.softmax_scale)
+    need = sfa_lib.workspace_size(sfa_lib.make_dims(batch=5, s1=2, n_q=128, topk=2048,
+                                                    max_blocks_per_batch=d["block_table"].shape[1],
+                                                    num_cache_rows=d["key_rope"].shape[0], num_splits=4))
+    ref = sfa_lib.decode(*args, batch=5, s1=2, num_splits=4,
+                         workspace=torch.zeros(need, dtype=torch.uint8, device="cuda")).clone()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for fill in ("ones", "random", "reuse"):
+        ws = torch.empty(need + 4096, dtype=torch.uint8, device="cuda")
+        if fill == "ones":
+            ws.fill_(255)
+        elif fill == "random":
+            ws.random_(0, 256, generator=g)
+        else:
+            # an earlier call with other shapes and partition count leaves its partials here
+            small = W.generate(batch=2, s1=1, n_q=64, act_seqs=[900, 4000], topk=1024, seed=42)
+            ds = sfa_lib.to_device(small)
+            sfa_lib.decode(ds["query_nope"], ds["query_rope"], ds["key_nope"], ds["key_rope"], None,
+                           ds["topk_indices"], ds["block_table"], ds["kv_act_seqs"], small.softmax_scale, batch=2,
+                           s1=1, num_splits=8, workspace=ws)
+        for _ in range(2):
+            out = sfa_lib.decode(*args, batch=5, s1=2, num_splits=4, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), fill
