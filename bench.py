@@ -486,7 +486,7 @@ def bench_window(args):
             d["block_table_cmp"] = p32[dev0["block_table_cmp"].long()].contiguous()
         sets.append(d)
     outs = [torch.empty((inp.batch, inp.s1, inp.n_q, 512), dtype=torch.bfloat16, device="cuda") for _ in sets]
-    calls = [sfa.prepare_window_run(inp, d, out=o) for d, o in zip(sets, outs)]
+    calls = [sfa.prepare_window_run(inp, d, out=o, num_splits=args.num_splits) for d, o in zip(sets, outs)]
     torch.cuda.synchronize()
 
     def step(i):
@@ -975,6 +975,8 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated for a cold cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget (0 disables)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="attention workloads: top-k partitions per token (0 = the library's automatic choice)")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="measure the dense bf16 MFMA throughput (libsfa_probe.so) and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -1030,7 +1032,8 @@ def main():
 
     # one prepared call per rotated copy: the Python checks and marshalling happen once, each
     # step only enters the C ABI (which validates on the host and queues the kernels)
-    calls = [sfa.prepare_run(inp, sets[k], prefill_mode=is_prefill, out=outs[k]) for k in range(len(sets))]
+    calls = [sfa.prepare_run(inp, sets[k], prefill_mode=is_prefill, out=outs[k], num_splits=args.num_splits)
+             for k in range(len(sets))]
 
     def step(i):
         calls[i % len(sets)]()

@@ -1172,8 +1172,9 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   if (S == 2) {
     // Two partitions: O = w0 O0 + w1 O1, summed in partition order whichever of the two arrived
     // last. The other partial is read in two batches of 32 loads per lane.
+    // The arithmetic has one shape whichever partition is this one (w0 * O0, then w1 * O1 added
+    // with one fused multiply-add), so the result does not depend on the arrival order.
     const int so = 1 - sp;
-    const float w_own = sp == 0 ? wv[0] : wv[1], w_oth = sp == 0 ? wv[1] : wv[0];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const floatx4* ps = pbase + (int64_t)so * kWaves * kWaveImage + 32 * hh * 64;
@@ -1183,9 +1184,12 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int dc = 8 * hh + (i >> 2), rq = i & 3;
-        const floatx4 own = w_own * agpr_quad(oacc[dc], rq);
-        const floatx4 oth = w_oth * buf[i];
-        put_out(dc, rq, (sp == 0 ? own + oth : oth + own) * inv);
+        const floatx4 own = agpr_quad(oacc[dc], rq);
+        const floatx4 o0 = sp == 0 ? own : buf[i], o1 = sp == 0 ? buf[i] : own;
+        floatx4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wv[1], o1[e], wv[0] * o0[e]);
+        put_out(dc, rq, acc * inv);
       }
     }
     flush_out();
@@ -1201,11 +1205,15 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
       float w = 0.f;
 #pragma unroll
       for (int u = 0; u < kMaxSplits; ++u) w = (u == s) ? wv[u] : w;
+      // acc = fma(w, O_s, acc) in partition order, the same operations whether O_s comes from
+      // this partition's registers or from memory
       if (s == sp) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int dc = 4 * hh + (i >> 2), rq = i & 3;
-          acc[i] += w * agpr_quad(oacc[dc], rq);
+          const floatx4 o = agpr_quad(oacc[dc], rq);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] = __builtin_fmaf(w, o[e], acc[i][e]);
         }
       } else {
         const floatx4* ps = pbase + (int64_t)s * kWaves * kWaveImage + 16 * hh * 64;
@@ -1213,7 +1221,9 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
 #pragma unroll
         for (int i = 0; i < 16; ++i) buf[i] = ps[i * 64];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] += w * buf[i];
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] = __builtin_fmaf(w, buf[i][e], acc[i][e]);
       }
     }
 #pragma unroll

@@ -526,8 +526,9 @@ def run_window(inp, d=None, *, num_splits=0, out=None):
                          num_splits=num_splits)
 
 
-def prepare_window_run(inp, d, *, out=None) -> PreparedCall:
-    return prepare_window_decode(*_window_args(inp, d), batch=inp.batch, s1=inp.s1, window=inp.window, out=out)
+def prepare_window_run(inp, d, *, out=None, num_splits=0) -> PreparedCall:
+    return prepare_window_decode(*_window_args(inp, d), batch=inp.batch, s1=inp.s1, window=inp.window, out=out,
+                                 num_splits=num_splits)
 
 
 def to_device(inp, device="cuda"):

@@ -49,14 +49,16 @@ def _dims(**kw):
 def test_partition_choice():
     # one workgroup per (token, partition): 64 x 2 tokens need 2 partitions to fill 256 CUs
     assert sfa.num_splits(_dims()) == 2
-    # 32 single-token batches: 8 partitions
-    assert sfa.num_splits(_dims(batch=32, s1=1)) == 8
+    # 32 single-token batches would want 8, but a partition needs >= 512 slots: 4
+    assert sfa.num_splits(_dims(batch=32, s1=1)) == 4
     # 256 tokens or more already fill the CUs
     assert sfa.num_splits(_dims(batch=128, s1=2)) == 1
-    # one token of 16 heads, 64 slots: partitions need >= 64 slots each
+    # short lists are not partitioned (a window of 128 slots, 64 slots)
+    assert sfa.num_splits(_dims(batch=64, s1=2, topk=128)) == 1
     assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=64)) == 1
     # at most 8 partitions unless topk needs more
-    assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=2048)) == 8
+    assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=2048)) == 4
+    assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=8192)) == 8
     assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=30000)) == 15
     # prefill never partitions while topk <= 2048
     assert sfa.num_splits(_dims(batch=1, s1=4096), is_prefill=True) == 1
@@ -68,9 +70,9 @@ def test_partition_choice():
 
 
 def test_workspace_size_formula():
-    d = _dims(batch=32, s1=1)  # 8 partitions
+    d = _dims(batch=32, s1=1)  # 4 partitions
     tokens = 32
-    items = tokens * 8
+    items = tokens * 4
     part = items * 4 * 16 * 4 * 64 * 16   # 4 waves x 16 column blocks x 4 row quads x 64 lanes x float4
     ml = items * 128 * 2 * 4              # (max, sum) per head
     cnt = 2 * tokens * 8                   # arrival and ready counters per token (64-bit, tagged)

@@ -283,12 +283,15 @@ def test_pool_beyond_4gib_matches_small_pool(kv_dtype):
     torch.cuda.empty_cache()
 
 
-def test_run_to_run_determinism():
+@pytest.mark.parametrize("splits", [2, 3, 4])
+def test_run_to_run_determinism(splits):
+    """Which partition arrives last varies from run to run; the merged bits must not."""
     inp = W.generate(batch=8, s1=2, n_q=128, act_seqs=[4000] * 8, topk=2048, seed=10, max_blocks_per_batch=32)
     sfa = _lib()
     dev = sfa.to_device(inp)
-    outs = [_gpu(inp, dev=dev, num_splits=4).view(torch.int16).cpu().numpy() for _ in range(3)]
-    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    outs = [_gpu(inp, dev=dev, num_splits=splits).view(torch.int16).cpu().numpy() for _ in range(6)]
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
 
 
 # ----------------------------------------------------------------------------------------

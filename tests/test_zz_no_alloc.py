@@ -18,7 +18,7 @@ def test_noalloc_matches_decode_on_two_calls(sfa_lib):
 
     big = W.generate(batch=8, s1=2, n_q=128, act_seqs=[8192, 5000, 3000, 8000, 2048, 7000, 6500, 4096], topk=2048,
                      seed=31)
-    small = W.generate(batch=2, s1=1, n_q=64, act_seqs=[900, 300], topk=512, kv_dtype="int8", seed=32)
+    small = W.generate(batch=2, s1=1, n_q=64, act_seqs=[1900, 300], topk=1024, kv_dtype="int8", seed=32)
     for inp in (big, small):
         d = sfa_lib.to_device(inp)
         dims_need = sfa_lib.workspace_size(sfa_lib.make_dims(
