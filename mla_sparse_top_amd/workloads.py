@@ -668,9 +668,10 @@ class CompressInputs:
     kv_state: np.ndarray        # float32 (B, ratio, 576)
     score_state: np.ndarray     # float32 (B, ratio, 576)
     block_table_cmp: np.ndarray  # int32 (B, max_blocks)
-    key_nope: np.ndarray        # uint16 (rows, 512): the compressed pool's bf16 bits before the step
-    key_rope: np.ndarray        # uint16 (rows, 64)
+    key_nope: np.ndarray        # uint16 (rows, 512), or (rows, 128) for 128 channels: the pool's bf16 bits
+    key_rope: Optional[np.ndarray]  # uint16 (rows, 64); None for 128 channels
     name: str = ""
+    rotate: bool = False        # the Hadamard transform after RoPE (128 channels)
 
     @property
     def num_cache_rows(self) -> int:
@@ -679,6 +680,10 @@ class CompressInputs:
     @property
     def rope_positions(self) -> int:
         return int(self.rope_cos.shape[0])
+
+    @property
+    def channels(self) -> int:
+        return int(self.kv.shape[1])
 
 
 def rope_tables(n_pos: int, base: float = 10000.0):
@@ -692,13 +697,13 @@ def rope_tables(n_pos: int, base: float = 10000.0):
 def compress_generate(*, batch: int, s1: int, ratio: int, start_pos: Sequence[int], rope_positions: int,
                       max_blocks: int, n_pool_blocks: Optional[int] = None, seed: int = 0,
                       score_scale: float = 1.0, block_table: Optional[np.ndarray] = None,
-                      name: str = "") -> CompressInputs:
+                      name: str = "", channels: int = COMPRESS_CHANNELS, rotate: bool = False) -> CompressInputs:
     """kv, score, kv_state and score_state are N(0,1) float32 (scores times score_scale); ape is
     N(0, 0.1^2); gamma is 1 + N(0, 0.1^2); eps 1e-6. Unless given, the block table is a random
     permutation of the pool's blocks, and the pool holds random bf16 bit patterns, so a row the
     step should not touch shows up if it changes."""
     g = torch.Generator().manual_seed(90_000 + int(seed))
-    c = COMPRESS_CHANNELS
+    c = int(channels)
     t = batch * s1
     n_pool_blocks = batch * max_blocks if n_pool_blocks is None else int(n_pool_blocks)
     if block_table is None:
@@ -712,15 +717,17 @@ def compress_generate(*, batch: int, s1: int, ratio: int, start_pos: Sequence[in
     score_state = (torch.randn(batch, ratio, c, generator=g) * float(score_scale)).numpy()
     cos, sin = rope_tables(rope_positions)
     rows = n_pool_blocks * BLOCK_SIZE
-    kn = torch.randint(0, 1 << 16, (rows, KV_LORA_RANK), generator=g, dtype=torch.int32).numpy().astype(np.uint16)
-    kr = torch.randint(0, 1 << 16, (rows, ROPE_DIM), generator=g, dtype=torch.int32).numpy().astype(np.uint16)
+    wide = c - ROPE_DIM if c == COMPRESS_CHANNELS else c
+    kn = torch.randint(0, 1 << 16, (rows, wide), generator=g, dtype=torch.int32).numpy().astype(np.uint16)
+    kr = (torch.randint(0, 1 << 16, (rows, ROPE_DIM), generator=g, dtype=torch.int32).numpy().astype(np.uint16)
+          if c == COMPRESS_CHANNELS else None)
     f32 = lambda x: np.ascontiguousarray(x, dtype=np.float32)  # noqa: E731
     return CompressInputs(batch=batch, s1=s1, ratio=int(ratio), kv=f32(kv), score=f32(score), ape=f32(ape),
                           gamma=f32(gamma), eps=1e-6, rope_cos=cos, rope_sin=sin,
                           start_pos=np.ascontiguousarray(start_pos, dtype=np.int32), kv_state=f32(kv_state),
                           score_state=f32(score_state),
                           block_table_cmp=np.ascontiguousarray(block_table, dtype=np.int32),
-                          key_nope=kn, key_rope=kr, name=name)
+                          key_nope=kn, key_rope=kr, name=name, rotate=bool(rotate))
 
 
 def compress_decode(seed: int = 0, ratio: int = 4) -> CompressInputs:
@@ -810,3 +817,12 @@ def prolog_decode(seed: int = 0) -> PrologInputs:
     """The decode step's prolog: 64 sequences x 2 new tokens (MTP 1), 128 heads, hidden 7168,
     query rank 1536, nope head dim 128, positions 8190 and 8191."""
     return prolog_generate(tokens=128, n_q=128, seed=seed, name="mla_prolog_b64_s2")
+
+
+def compress_index_decode(seed: int = 0, ratio: int = 4) -> CompressInputs:
+    """The page's D = 128 compressor configuration (the index keys the Lightning Indexer scores
+    over the compressed cache) on the same decode step: 64 sequences, positions 8190 and 8191,
+    ratio 4, rotate = true."""
+    return compress_generate(batch=64, s1=2, ratio=ratio, start_pos=[8190] * 64, rope_positions=8192,
+                             max_blocks=2048 // BLOCK_SIZE, seed=seed, channels=128, rotate=True,
+                             name=f"compress_b64_s2_r{ratio}_c128_rot")

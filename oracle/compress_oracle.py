@@ -8,16 +8,17 @@ What it computes ("NPU DeepSeek-V4 model PyPTO fused-operator optimisation", sec
 score = X W_gate + ape, refresh a per-sequence state (kv_state, score_state). When position p
 closes a window (p + 1 is a multiple of the compression ratio), the state is pooled into one
 compressed entry: for every channel, the softmax of score_state over the state's slots weights
-kv_state, and the weighted sum over the slots is RMS-normalised and then rotated (RoPE). The
-rotate = true branch (a Hadamard transform) is not taken: the page's worked case is ratio 4
-without rotation.
+kv_state, and the weighted sum over the slots is RMS-normalised and then rotated (RoPE). With
+rotate = true the row then goes through a Hadamard transform.
 
 Readings (the page gives the formula, not these details; each is listed with its reason in the
 design notes):
   * the projections are plain GEMMs outside this step: kv and score arrive as fp32 (T, C), the
     precision the page gives the matmul outputs;
-  * C = 576 channels, the row of the compressed cache the window attention reads: 512 nope
-    channels, then 64 rope channels;
+  * C = 576 channels, the row of the compressed cache the window attention reads (512 nope
+    channels, then 64 rope channels), or C = 128, the row of a compressed index-key cache (the
+    page's D = 128 configuration, whose keys the Lightning Indexer scores); the last 64 channels
+    are the rotary ones in both;
   * the state of sequence b holds `ratio` slots of C channels; the token at position p writes
     slot p mod ratio; ape is (ratio, C), indexed by that slot; the stored score is the fp32 sum
     score + ape[slot];
@@ -33,17 +34,22 @@ design notes):
   * RoPE on the 64 rope channels, as 32 adjacent pairs (2i, 2i+1) rotated by the angle whose
     cosine and sine are row p, column i of the caller's tables (p = the closing token's
     position);
+  * rotate = true (C = 128 only, a power of two): after RoPE the row is multiplied by the
+    Sylvester Hadamard matrix of order C (rows in natural order, H_2n = [[H_n, H_n],
+    [H_n, -H_n]]) scaled by 1/sqrt(C), an orthogonal and self-inverse map;
   * the row is stored as bf16, rounded to nearest even.
 
 The arithmetic is float64 except the stored score (an fp32 addition, as stored). Pinned by
 tests/test_compress_oracle.py against closed forms (one slot, equal scores, a dominant slot, a
 quarter-turn rotation), an invariant (unit RMS under rotation), a pure-Python scalar brute
-force, and planted mistakes.
+force, and planted mistakes; the Hadamard step by an explicit butterfly transform, its first
+rows, self-inversion and norm preservation.
 """
 
 from __future__ import annotations
 
 import numpy as np
+import scipy.linalg
 
 CHANNELS = 576
 NOPE = 512
@@ -104,10 +110,20 @@ def rope_pairs(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
     return out
 
 
-def compressed_row(kv_slots, score_slots, gamma, eps, cos, sin) -> np.ndarray:
-    """RoPE(RMSNorm(pool)) for one closed window: float64 (C,)."""
+def hadamard_rotate(y: np.ndarray) -> np.ndarray:
+    """H y / sqrt(n), H the Sylvester Hadamard matrix of order n = len(y) (a power of two)."""
+    y = np.asarray(y, dtype=np.float64)
+    n = y.shape[0]
+    return scipy.linalg.hadamard(n).astype(np.float64) @ y / np.sqrt(n)
+
+
+def compressed_row(kv_slots, score_slots, gamma, eps, cos, sin, rotate: bool = False) -> np.ndarray:
+    """RoPE(RMSNorm(pool)) for one closed window, then the Hadamard transform when rotate is set:
+    float64 (C,). The last ROPE channels are the rotary ones."""
     y = rms_norm(pool(kv_slots, score_slots), gamma, eps)
-    y[NOPE:] = rope_pairs(y[NOPE:], cos, sin)
+    y[-ROPE:] = rope_pairs(y[-ROPE:], cos, sin)
+    if rotate:
+        y = hadamard_rotate(y)
     return y
 
 
@@ -134,6 +150,7 @@ def compress(inp):
             score_state[b, slot] = (inp.score[t].astype(np.float32) + inp.ape[slot].astype(np.float32)).astype(np.float32)
             if closes_window(p, ratio):
                 c = entry_index(p, ratio)
-                y = compressed_row(kv_state[b], score_state[b], inp.gamma, inp.eps, inp.rope_cos[p], inp.rope_sin[p])
+                y = compressed_row(kv_state[b], score_state[b], inp.gamma, inp.eps, inp.rope_cos[p], inp.rope_sin[p],
+                                   bool(getattr(inp, "rotate", False)))
                 entries.append((b, c, entry_row(inp.block_table_cmp[b], c, inp.num_cache_rows), y))
     return kv_state, score_state, entries

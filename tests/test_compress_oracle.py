@@ -8,6 +8,7 @@ import math
 
 import numpy as np
 import pytest
+import scipy.linalg
 
 from mla_sparse_top_amd import workloads as W
 from oracle import compress_oracle as C
@@ -15,9 +16,9 @@ from oracle import compress_oracle as C
 C_ = C.CHANNELS
 
 
-def _small(seed=0, *, ratio=4, s1=2, start=6, batch=2, n_pos=64, score_scale=1.0):
+def _small(seed=0, *, ratio=4, s1=2, start=6, batch=2, n_pos=64, score_scale=1.0, channels=576, rotate=False):
     return W.compress_generate(batch=batch, s1=s1, ratio=ratio, start_pos=[start] * batch, rope_positions=n_pos,
-                               max_blocks=2, seed=seed, score_scale=score_scale)
+                               max_blocks=2, seed=seed, score_scale=score_scale, channels=channels, rotate=rotate)
 
 
 def _rope_complex(x, cos, sin):
@@ -92,8 +93,25 @@ def _pin_quarter_turn():
     np.testing.assert_array_equal(C.rope_pairs(v, np.ones(32), np.zeros(32)), v)
 
 
+def _fwht(v):
+    """Hadamard transform by the butterfly: for strides h = 1, 2, 4, ..., each pair (i, i + h) with
+    bit h of i clear becomes (a + b, a - b); then the 1/sqrt(n) scale."""
+    v = list(v)
+    n = len(v)
+    h = 1
+    while h < n:
+        for i in range(n):
+            if i & h == 0:
+                a, b = v[i], v[i + h]
+                v[i], v[i + h] = a + b, a - b
+        h *= 2
+    return [u / math.sqrt(n) for u in v]
+
+
 def _brute(x):
     """Pure-Python scalar loops over the same steps."""
+    C_ = x.channels
+    R0 = C_ - 64
     ratio, n_pos = x.ratio, x.rope_cos.shape[0]
     kvs = [[[float(v) for v in x.kv_state[b, r]] for r in range(ratio)] for b in range(x.batch)]
     scs = [[[float(v) for v in x.score_state[b, r]] for r in range(ratio)] for b in range(x.batch)]
@@ -116,22 +134,59 @@ def _brute(x):
             ms = sum(v * v for v in y) / C_
             y = [y[ch] / math.sqrt(ms + x.eps) * float(x.gamma[ch]) for ch in range(C_)]
             for i in range(32):
-                a, bb = y[512 + 2 * i], y[513 + 2 * i]
+                a, bb = y[R0 + 2 * i], y[R0 + 1 + 2 * i]
                 co, si = float(x.rope_cos[p, i]), float(x.rope_sin[p, i])
-                y[512 + 2 * i], y[513 + 2 * i] = a * co - bb * si, a * si + bb * co
+                y[R0 + 2 * i], y[R0 + 1 + 2 * i] = a * co - bb * si, a * si + bb * co
+            if x.rotate:
+                y = _fwht(y)
             out.append((b, (p + 1) // ratio - 1, y))
     return kvs, scs, out
 
 
 def _pin_brute_force():
-    x = _small(seed=3, ratio=3, s1=5, start=1, n_pos=5)   # positions 1..5; 5 is past the tables
-    ks, ss, e = C.compress(x)
-    bk, bs, be = _brute(x)
-    np.testing.assert_array_equal(ks, np.array(bk, dtype=np.float32))
-    np.testing.assert_array_equal(ss, np.array(bs, dtype=np.float32))
-    assert [(b, c) for b, c, _, _ in e] == [(b, c) for b, c, _ in be] == [(0, 0), (1, 0)]
-    for (_, _, _, y), (_, _, yb) in zip(e, be):
-        np.testing.assert_allclose(y, yb, rtol=1e-12, atol=1e-12)
+    for ch, rot in ((576, False), (128, False), (128, True)):
+        x = _small(seed=3, ratio=3, s1=5, start=1, n_pos=5, channels=ch, rotate=rot)  # positions 1..5; 5 past the tables
+        ks, ss, e = C.compress(x)
+        bk, bs, be = _brute(x)
+        np.testing.assert_array_equal(ks, np.array(bk, dtype=np.float32))
+        np.testing.assert_array_equal(ss, np.array(bs, dtype=np.float32))
+        assert [(b, c) for b, c, _, _ in e] == [(b, c) for b, c, _ in be] == [(0, 0), (1, 0)]
+        for (_, _, _, y), (_, _, yb) in zip(e, be):
+            np.testing.assert_allclose(y, yb, rtol=1e-12, atol=1e-12)
+
+
+def _pin_hadamard_rows():
+    """The transform's first rows in natural (Sylvester) order: e_0 -> all 1/sqrt(n), e_1 ->
+    alternating +-1/sqrt(n), e_2 -> (+, +, -, -, ...); it is its own inverse and keeps norms."""
+    n = 128
+    e = np.eye(n)
+    np.testing.assert_allclose(C.hadamard_rotate(e[0]), np.full(n, n ** -0.5), rtol=1e-15)
+    np.testing.assert_allclose(C.hadamard_rotate(e[1]), np.tile([1.0, -1.0], n // 2) * n ** -0.5, rtol=1e-15)
+    np.testing.assert_allclose(C.hadamard_rotate(e[2]), np.tile([1.0, 1.0, -1.0, -1.0], n // 4) * n ** -0.5,
+                               rtol=1e-15)
+    v = np.random.default_rng(7).standard_normal(n)
+    np.testing.assert_allclose(C.hadamard_rotate(C.hadamard_rotate(v)), v, rtol=1e-12, atol=1e-13)
+    assert abs(np.linalg.norm(C.hadamard_rotate(v)) - np.linalg.norm(v)) < 1e-12
+    for m in (2, 8, 64):
+        w = np.random.default_rng(m).standard_normal(m)
+        np.testing.assert_allclose(C.hadamard_rotate(w), _fwht(w), rtol=1e-12, atol=1e-13)
+
+
+def _pin_rotated_one_slot():
+    """ratio 1, 128 channels, rotate: the entry is H(RoPE(RMSNorm(kv)))/sqrt(128) of the token,
+    rebuilt here with the butterfly on a quarter-turn rotation."""
+    x = _small(ratio=1, s1=1, start=9, channels=128, rotate=True)
+    x.eps = 0.0
+    x.gamma[:] = 1.0
+    x.rope_cos[9], x.rope_sin[9] = 0.0, 1.0
+    _, _, e = C.compress(x)
+    assert len(e) == 2
+    for b, c, _, y in e:
+        kv = x.kv[b].astype(np.float64)
+        want = kv * math.sqrt(128) / np.linalg.norm(kv)
+        a, bb = want[64::2].copy(), want[65::2].copy()
+        want[64::2], want[65::2] = -bb, a
+        np.testing.assert_allclose(y, _fwht(want), rtol=1e-12, atol=1e-12)
 
 
 def _pin_refresh_and_emission():
@@ -163,7 +218,7 @@ def _pin_skips_and_rows():
 
 
 PINS = [_pin_one_slot, _pin_equal_scores_mean, _pin_per_channel_dominant_slot, _pin_unit_rms, _pin_quarter_turn,
-        _pin_brute_force, _pin_refresh_and_emission, _pin_skips_and_rows]
+        _pin_brute_force, _pin_refresh_and_emission, _pin_skips_and_rows, _pin_hadamard_rows, _pin_rotated_one_slot]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__[5:] for p in PINS])
@@ -187,7 +242,24 @@ def _axis_channels(kv_slots, score_slots):
     return (w * np.asarray(kv_slots, dtype=np.float64)).sum(axis=0)
 
 
-_ORIG = {n: getattr(C, n) for n in ("pool", "rope_pairs", "rms_norm")}
+_ORIG = {n: getattr(C, n) for n in ("pool", "rope_pairs", "rms_norm", "hadamard_rotate", "compressed_row")}
+
+
+def _walsh_sequency(y):
+    """rows ordered by sign changes (Walsh order) instead of the natural order"""
+    y = np.asarray(y, np.float64)
+    n = len(y)
+    h = scipy.linalg.hadamard(n)
+    order = np.argsort([np.count_nonzero(np.diff(r) != 0) for r in h], kind="stable")
+    return h[order] @ y / np.sqrt(n)
+
+
+def _rotate_before_rope(kv_slots, score_slots, gamma, eps, cos, sin, rotate=False):
+    y = C.rms_norm(C.pool(kv_slots, score_slots), gamma, eps)
+    if rotate:
+        y = C.hadamard_rotate(y)
+    y[-64:] = C.rope_pairs(y[-64:], cos, sin)
+    return y
 
 MUTANTS = {
     "softmax over channels": ("pool", _axis_channels),
@@ -199,6 +271,10 @@ MUTANTS = {
     "emits on p % ratio == 0": ("closes_window", lambda p, r: p % r == 0),
     "entry index off by one": ("entry_index", lambda p, r: (p + 1) // r),
     "pool is the plain mean": ("pool", lambda kv, sc: np.asarray(kv, np.float64).mean(axis=0)),
+    "hadamard without 1/sqrt(n)": ("hadamard_rotate", lambda y: _ORIG["hadamard_rotate"](y) * np.sqrt(len(y))),
+    "hadamard in sequency order": ("hadamard_rotate", _walsh_sequency),
+    "hadamard before RoPE": ("compressed_row", _rotate_before_rope),
+    "rotate flag ignored": ("compressed_row", lambda *a, rotate=False: _ORIG["compressed_row"](*a[:6], False)),
 }
 
 
