@@ -690,14 +690,15 @@ def bench_cache_write(args):
     print(json.dumps(rec), flush=True)
 
 
-COMPRESS_WORKLOADS = {"compress_b64_s2_r4": 4}
+COMPRESS_WORKLOADS = {"compress_b64_s2_r4": ("compress_decode", 4),
+                      "compress_b64_s2_r4_c128_rot": ("compress_index_decode", 4)}
 
 
 def compress_algorithmic_bytes(inp) -> int:
     """Bytes the compressor must move per call: every valid token's kv and score rows; for every
     entry, the state slots not refreshed earlier in the call, its RoPE row, its block-table entry
     and the bf16 row it writes; each refreshed slot's final value; start_pos, ape and gamma."""
-    c = 576
+    c = inp.channels
     total = inp.batch * 4 + inp.ratio * c * 4 + c * 4
     n_pos = inp.rope_cos.shape[0]
     for b in range(inp.batch):
@@ -722,7 +723,8 @@ def bench_compress(args):
     import oracle.sfa_oracle as SO
     from mla_sparse_top_amd import sfa, workloads
 
-    inp = workloads.compress_decode(seed=args.seed, ratio=COMPRESS_WORKLOADS[args.workload])
+    fn_name, ratio = COMPRESS_WORKLOADS[args.workload]
+    inp = getattr(workloads, fn_name)(seed=args.seed, ratio=ratio)
     print(f"[bench] generated {inp.name}", file=sys.stderr, flush=True)
     d = sfa.compress_to_device(inp)
     call = sfa.prepare_compress(inp, d)
@@ -765,7 +767,8 @@ def bench_compress(args):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": inp.batch, "s1": inp.s1, "ratio": inp.ratio,
-                   "channels": 576, "start_pos": int(inp.start_pos[0]), "entries_per_call": inp.batch},
+                   "channels": inp.channels, "rotate": bool(inp.rotate), "start_pos": int(inp.start_pos[0]),
+                   "entries_per_call": inp.batch},
         "kernel_ms_mean": round(launch_ms, 5),
         "algorithmic_bytes_per_call": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -777,7 +780,7 @@ def bench_compress(args):
         # the oracle over the whole call, repeated until the budget is spent; its first result is
         # compared with the GPU's pool rows and state
         kn = d["key_nope"].cpu().view(torch.int16).numpy().view(np.uint16)
-        kr = d["key_rope"].cpu().view(torch.int16).numpy().view(np.uint16)
+        kr = None if d["key_rope"] is None else d["key_rope"].cpu().view(torch.int16).numpy().view(np.uint16)
         ks = d["kv_state"].cpu().numpy()
         t0 = time.perf_counter()
         runs, bad = 0, 0
@@ -788,7 +791,8 @@ def bench_compress(args):
                 for _, _, row, y in entries:
                     if row < 0:
                         continue
-                    g = np.concatenate([SO.bf16_bits_to_f64(kn[row]), SO.bf16_bits_to_f64(kr[row])])
+                    g = (np.concatenate([SO.bf16_bits_to_f64(kn[row]), SO.bf16_bits_to_f64(kr[row])])
+                         if kr is not None else SO.bf16_bits_to_f64(kn[row]))
                     bad += int(np.any(np.abs(g - y) > 1e-4 + 5e-3 * np.abs(y)))
             runs += 1
         el = time.perf_counter() - t0

@@ -339,27 +339,32 @@ int sfa_topk_select(const sfa_indexer_dims* dims, const float* scores, const int
  * When p + 1 is a multiple of ratio, the state is pooled into compressed entry
  * c = (p + 1) / ratio - 1:
  *     x[ch] = sum over slots r of softmax_r(score_state[b][r][ch]) * kv_state[b][r][ch]
- *     y     = x / sqrt(mean over the 576 channels of x^2 + eps) * gamma
- *     y[512 + 2i], y[513 + 2i]  rotated by the angle with cosine rope_cos[p][i] and sine
- *                               rope_sin[p][i] (i < 32; adjacent pairs)
- * and y is stored as bf16 (round to nearest even): channels 0..511 to key_nope_2d and 512..575
- * to key_rope_2d, at row block_table_cmp[b][c / 128] * 128 + c % 128 (the row layout of the
- * cache sfa_window_decode reads). The page's rotate = true branch (a Hadamard transform) is not
- * provided. The softmax, sum, norm and rotation are fp32.
+ *     y     = x / sqrt(mean over the C channels of x^2 + eps) * gamma
+ *     y[C - 64 + 2i], y[C - 63 + 2i]  rotated by the angle with cosine rope_cos[p][i] and sine
+ *                                     rope_sin[p][i] (i < 32; adjacent pairs)
+ * With rotate = 1 (128 channels only) y then becomes H y / sqrt(128), H the Sylvester Hadamard
+ * matrix in natural order (H_2n = [[H_n, H_n], [H_n, -H_n]]), the page's rotate = true branch.
+ * y is stored as bf16 (round to nearest even) at row block_table_cmp[b][c / 128] * 128 + c % 128:
+ * with 576 channels, channels 0..511 to key_nope_2d and 512..575 to key_rope_2d (the row layout
+ * of the cache sfa_window_decode reads); with 128 channels (the page's D = 128 configuration,
+ * an index-key row for the Lightning Indexer), the whole row to key_nope_2d, rows of 128
+ * (key_rope_2d is not used and may be NULL). The softmax, sum, norm and rotations are fp32.
  *
- *   dims              channels must be 576, block_size 128; ratio in [1, 1024]; T = batch*s1
- *                     up to 2^26; max_blocks = row length of block_table_cmp
- *   kv, score         fp32  (T, 576)
- *   ape               fp32  (ratio, 576)      added to the score of the slot it is indexed by
- *   gamma             fp32  (576)
+ *   dims              channels C = 576 or 128, rotate 0 or 1 (1 only with 128), block_size
+ *                     128; ratio in [1, 1024]; T = batch*s1 up to 2^26; max_blocks = row
+ *                     length of block_table_cmp
+ *   kv, score         fp32  (T, C)
+ *   ape               fp32  (ratio, C)        added to the score of the slot it is indexed by
+ *   gamma             fp32  (C)
  *   eps               finite, >= 0
  *   rope_cos/sin      fp32  (rope_positions, 32)
  *   start_pos         int32 (batch)
  *   kv_state,
- *   score_state       fp32  (batch, ratio, 576), read and refreshed in place
+ *   score_state       fp32  (batch, ratio, C), read and refreshed in place
  *   block_table_cmp   int32 (batch, max_blocks)
- *   key_nope_2d       bf16  (num_cache_rows, 512)   written in place
- *   key_rope_2d       bf16  (num_cache_rows, 64)    written in place
+ *   key_nope_2d       bf16  (num_cache_rows, 512), or (num_cache_rows, 128) for C = 128,
+ *                     written in place
+ *   key_rope_2d       bf16  (num_cache_rows, 64) written in place (C = 576 only)
  *
  * With batch * s1 = 0 the call reads nothing and returns SFA_OK (the pointers may then be NULL).
  * A token with p < 0 or p >= rope_positions is skipped (no refresh, no entry). An entry is not
@@ -372,11 +377,12 @@ int sfa_topk_select(const sfa_indexer_dims* dims, const float* scores, const int
 typedef struct {
   int32_t batch;
   int32_t s1;                   /* new tokens per sequence                                      */
-  int32_t channels;             /* must be 576 (kv_lora_rank + rope_dim)                        */
+  int32_t channels;             /* 576 (kv_lora_rank + rope_dim) or 128 (an index-key row)       */
   int32_t ratio;                /* compression ratio                                            */
   int32_t rope_positions;       /* rows of rope_cos and rope_sin                                */
   int32_t max_blocks;           /* row length of block_table_cmp                                */
   int32_t block_size;           /* must be 128                                                  */
+  int32_t rotate;               /* 0, or 1: the Hadamard transform after RoPE (128 channels)    */
   int64_t num_cache_rows;       /* rows of the compressed pool                                  */
 } sfa_compress_dims;
 

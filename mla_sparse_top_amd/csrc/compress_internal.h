@@ -7,26 +7,25 @@
 
 namespace sfa {
 
-constexpr int kCmpChannels = 576;            // 512 nope + 64 rope
-constexpr int kCmpThreads = 192;             // three waves; thread i owns channels i, i+192, i+384
-constexpr int kCmpPerThread = kCmpChannels / kCmpThreads;
 
 struct CompressArgs {
-  const float* kv;              // (T, 576)
-  const float* score;           // (T, 576)
-  const float* ape;             // (ratio, 576)
-  const float* gamma;           // (576)
+  const float* kv;              // (T, C), C = channels
+  const float* score;           // (T, C)
+  const float* ape;             // (ratio, C)
+  const float* gamma;           // (C)
   const float* rope_cos;        // (rope_positions, 32)
   const float* rope_sin;        // (rope_positions, 32)
   const int32_t* start_pos;     // (batch)
-  float* kv_state;              // (batch, ratio, 576)
-  float* score_state;           // (batch, ratio, 576)
+  float* kv_state;              // (batch, ratio, C)
+  float* score_state;           // (batch, ratio, C)
   const int32_t* block_table;   // (batch, mb)
-  uint16_t* key_nope;           // bf16 bits (rows, 512)
-  uint16_t* key_rope;           // bf16 bits (rows, 64)
+  uint16_t* key_nope;           // bf16 bits (rows, 512), or (rows, 128) for C = 128
+  uint16_t* key_rope;           // bf16 bits (rows, 64); unused for C = 128
   int64_t num_rows;
   float eps;
   int32_t batch, s1, ratio, rope_positions, mb;
+  int32_t channels;             // 576 or 128
+  int32_t rotate;               // 128 channels: the Hadamard transform after RoPE
 };
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);

@@ -5,14 +5,17 @@
 // X W_gate, to which the slot's position embedding ape is added here) of each new token refresh
 // the sequence's state; when position p + 1 is a multiple of the compression ratio, the state
 // is pooled into one compressed entry. Per channel, the softmax over the state's slots of the
-// scores weights the kv values; the weighted sum is RMS-normalised over its 576 channels (times
+// scores weights the kv values; the weighted sum is RMS-normalised over its channels (times
 // gamma), its last 64 channels are rotated in adjacent pairs by the RoPE angle of position p,
-// and the row is stored as bf16 at the entry's row of the compressed pool.
+// with rotate = true the row then goes through the Sylvester Hadamard transform scaled by
+// 1/sqrt(n), and the row is stored as bf16 at the entry's row of the compressed pool. Rows are
+// 576 channels (the attention cache row: 512 to key_nope, 64 to key_rope) or 128 (an index-key
+// row, the page's D = 128 configuration, whole to key_nope).
 //
-// How: one workgroup per sequence, three waves, each thread owning three channels, so every
-// per-channel step (refresh, online softmax over the slots, scaling) runs in registers with no
-// communication; the RMS needs one block reduction, and RoPE pairs are adjacent lanes of the
-// third wave (one xor shuffle). The tokens of a sequence are taken in order. A slot written
+// How: one workgroup per sequence, each thread owning a few channels, so every per-channel step
+// (refresh, online softmax over the slots, scaling) runs in registers with no communication;
+// the RMS needs one block reduction, RoPE pairs are adjacent lanes of the last wave (one xor
+// shuffle), and the Hadamard transform's butterflies are xor shuffles across one wave. The tokens of a sequence are taken in order. A slot written
 // earlier in the same call is read from the token's inputs rather than from the state, and only
 // each slot's last writer stores it, so no address is both written and read in one call.
 
@@ -34,44 +37,51 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-__global__ void __launch_bounds__(kCmpThreads) compress_kernel(const CompressArgs a) {
+// kC channels: 576 (the attention cache row, three waves, thread i owning channels i, i + 192,
+// i + 384) or 128 (an index-key row, one wave, lane i owning channels i and i + 64). The rotary
+// channels, the last 64, are the last register of the last wave's lanes in both.
+template <int kC, bool kRotate>
+__global__ void __launch_bounds__(kC == 576 ? 192 : 64) compress_kernel(const CompressArgs a) {
+  constexpr int kT = kC == 576 ? 192 : 64;  // threads
+  constexpr int kPer = kC / kT;             // channels per thread
+  constexpr int kWaves = kT / 64;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  __shared__ float part[kCmpThreads / 64];
+  __shared__ float part[kWaves];
 
   const int64_t p0 = a.start_pos[b];
   // tokens with 0 <= p < rope_positions: a contiguous range of s
   const int64_t s_lo = p0 < 0 ? -p0 : 0;
   const int64_t s_hi = min((int64_t)a.s1, (int64_t)a.rope_positions - p0);
-  const int64_t C = kCmpChannels;
+  const int64_t C = kC;
 
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int p = (int)(p0 + s);
     const int64_t t = (int64_t)b * a.s1 + s;
     const int slot = p % a.ratio;
-    float kv_t[kCmpPerThread], sc_t[kCmpPerThread];
+    float kv_t[kPer], sc_t[kPer];
 #pragma unroll
-    for (int k = 0; k < kCmpPerThread; ++k) {
-      const int c = tid + k * kCmpThreads;
+    for (int k = 0; k < kPer; ++k) {
+      const int c = tid + k * kT;
       kv_t[k] = a.kv[t * C + c];
       sc_t[k] = a.score[t * C + c] + a.ape[(int64_t)slot * C + c];
     }
     if (s + a.ratio >= s_hi) {  // no later token of this call refreshes this slot
       const int64_t o = ((int64_t)b * a.ratio + slot) * C;
 #pragma unroll
-      for (int k = 0; k < kCmpPerThread; ++k) {
-        a.kv_state[o + tid + k * kCmpThreads] = kv_t[k];
-        a.score_state[o + tid + k * kCmpThreads] = sc_t[k];
+      for (int k = 0; k < kPer; ++k) {
+        a.kv_state[o + tid + k * kT] = kv_t[k];
+        a.score_state[o + tid + k * kT] = sc_t[k];
       }
     }
     if ((p + 1) % a.ratio != 0) continue;  // uniform over the workgroup
 
     // ---- pool: online softmax over the slots, per channel
-    float m[kCmpPerThread], l[kCmpPerThread], acc[kCmpPerThread];
+    float m[kPer], l[kPer], acc[kPer];
 #pragma unroll
-    for (int k = 0; k < kCmpPerThread; ++k) {
+    for (int k = 0; k < kPer; ++k) {
       m[k] = sc_t[k];
       l[k] = 1.0f;
       acc[k] = kv_t[k];
@@ -80,25 +90,25 @@ __global__ void __launch_bounds__(kCmpThreads) compress_kernel(const CompressArg
       if (r == slot) continue;
       const int64_t back = (slot - r + a.ratio) % a.ratio;  // slot r was last refreshed at p - back
       const int64_t sp = s - back;
-      float kr[kCmpPerThread], sr[kCmpPerThread];
+      float kr[kPer], sr[kPer];
       if (sp >= s_lo) {  // by a token of this call: take its inputs
         const int64_t tp = (int64_t)b * a.s1 + sp;
 #pragma unroll
-        for (int k = 0; k < kCmpPerThread; ++k) {
-          const int c = tid + k * kCmpThreads;
+        for (int k = 0; k < kPer; ++k) {
+          const int c = tid + k * kT;
           kr[k] = a.kv[tp * C + c];
           sr[k] = a.score[tp * C + c] + a.ape[(int64_t)r * C + c];
         }
       } else {           // before this call: the stored state, which this call has not written
         const int64_t o = ((int64_t)b * a.ratio + r) * C;
 #pragma unroll
-        for (int k = 0; k < kCmpPerThread; ++k) {
-          kr[k] = a.kv_state[o + tid + k * kCmpThreads];
-          sr[k] = a.score_state[o + tid + k * kCmpThreads];
+        for (int k = 0; k < kPer; ++k) {
+          kr[k] = a.kv_state[o + tid + k * kT];
+          sr[k] = a.score_state[o + tid + k * kT];
         }
       }
 #pragma unroll
-      for (int k = 0; k < kCmpPerThread; ++k) {
+      for (int k = 0; k < kPer; ++k) {
         const float mn = fmaxf(m[k], sr[k]);
         const float e_old = expf(m[k] - mn), e_new = expf(sr[k] - mn);
         l[k] = l[k] * e_old + e_new;
@@ -106,32 +116,55 @@ __global__ void __launch_bounds__(kCmpThreads) compress_kernel(const CompressArg
         m[k] = mn;
       }
     }
-    float x[kCmpPerThread], ss = 0.0f;
+    float x[kPer], ss = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kCmpPerThread; ++k) {
+    for (int k = 0; k < kPer; ++k) {
       x[k] = acc[k] / l[k];
       ss += x[k] * x[k];
     }
 
-    // ---- RMSNorm over the 576 channels
+    // ---- RMSNorm over the kC channels
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, 64);
-    if (lane == 0) part[wave] = ss;
-    __syncthreads();
-    const float total = part[0] + part[1] + part[2];
-    __syncthreads();  // part is rewritten by the next entry
-    const float inv = 1.0f / sqrtf(total / (float)kCmpChannels + a.eps);
-    float y[kCmpPerThread];
+    float total = ss;
+    if (kWaves > 1) {
+      if (lane == 0) part[wave] = ss;
+      __syncthreads();
+      total = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kCmpPerThread; ++k) y[k] = x[k] * inv * a.gamma[tid + k * kCmpThreads];
+      for (int w = 0; w < kWaves; ++w) total += part[w];
+      __syncthreads();  // part is rewritten by the next entry
+    }
+    const float inv = 1.0f / sqrtf(total / (float)kC + a.eps);
+    float y[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) y[k] = x[k] * inv * a.gamma[tid + k * kT];
 
-    // ---- RoPE: channel 512 + j is y[2] of thread 128 + j (the third wave); pair j/2 rotates by
-    // the angle of column j/2 of row p.
-    const float partner = __shfl_xor(y[2], 1, 64);
-    if (wave == 2) {
+    // ---- RoPE: channel kC - 64 + j is the last register of lane j of the last wave; pair j/2
+    // rotates by the angle of column j/2 of row p.
+    const float partner = __shfl_xor(y[kPer - 1], 1, 64);
+    if (wave == kWaves - 1) {
       const int i = lane >> 1;
       const float co = a.rope_cos[(int64_t)p * (kRope / 2) + i], si = a.rope_sin[(int64_t)p * (kRope / 2) + i];
-      y[2] = (lane & 1) ? fmaf(partner, si, y[2] * co) : fmaf(-partner, si, y[2] * co);
+      y[kPer - 1] = (lane & 1) ? fmaf(partner, si, y[kPer - 1] * co) : fmaf(-partner, si, y[kPer - 1] * co);
+    }
+
+    // ---- Hadamard transform (128 channels): the stride-64 butterfly is within a lane (channels
+    // lane and lane + 64), the strides 32 .. 1 between lanes; then the 1/sqrt(128) scale.
+    if (kRotate) {
+      const float u0 = y[0] + y[1], u1 = y[0] - y[1];
+      y[0] = u0;
+      y[1] = u1;
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float q = __shfl_xor(y[k], d, 64);
+          y[k] = (lane & d) ? q - y[k] : y[k] + q;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) y[k] *= 0.08838834764831845f;  // 1/sqrt(128)
     }
 
     // ---- store at the entry's row
@@ -141,19 +174,29 @@ __global__ void __launch_bounds__(kCmpThreads) compress_kernel(const CompressArg
     if (blk < 0) continue;
     const int64_t row = (int64_t)blk * 128 + (c_entry & 127);
     if (row >= a.num_rows) continue;
-    a.key_nope[row * kNope + tid] = bf16_rne(y[0]);
-    a.key_nope[row * kNope + tid + kCmpThreads] = bf16_rne(y[1]);
-    if (wave < 2)
-      a.key_nope[row * kNope + tid + 2 * kCmpThreads] = bf16_rne(y[2]);
-    else
-      a.key_rope[row * kRope + lane] = bf16_rne(y[2]);
+    if (kC == 576) {
+      a.key_nope[row * kNope + tid] = bf16_rne(y[0]);
+      a.key_nope[row * kNope + tid + kT] = bf16_rne(y[1]);
+      if (wave < 2)
+        a.key_nope[row * kNope + tid + 2 * kT] = bf16_rne(y[kPer - 1]);
+      else
+        a.key_rope[row * kRope + lane] = bf16_rne(y[kPer - 1]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) a.key_nope[row * kC + tid + k * kT] = bf16_rne(y[k]);
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(compress_kernel, dim3(a.batch), dim3(kCmpThreads), 0, stream, a);
+  if (a.channels == 576)
+    hipLaunchKernelGGL((compress_kernel<576, false>), dim3(a.batch), dim3(192), 0, stream, a);
+  else if (a.rotate)
+    hipLaunchKernelGGL((compress_kernel<128, true>), dim3(a.batch), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((compress_kernel<128, false>), dim3(a.batch), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

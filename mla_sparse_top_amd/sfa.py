@@ -124,6 +124,7 @@ class SfaCompressDims(ctypes.Structure):
         ("rope_positions", ctypes.c_int32),
         ("max_blocks", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
+        ("rotate", ctypes.c_int32),
         ("num_cache_rows", ctypes.c_int64),
     ]
 
@@ -729,15 +730,17 @@ COMPRESS_CHANNELS = KV_LORA_RANK + ROPE_DIM
 
 
 def _marshal_compress(kv, score, ape, gamma, eps, rope_cos, rope_sin, start_pos, kv_state, score_state,
-                      block_table_cmp, key_nope, key_rope, *, batch, s1, stream=None):
+                      block_table_cmp, key_nope, key_rope, *, batch, s1, rotate=False, stream=None):
     dev = kv.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on a GPU device")
     t_tokens = batch * s1
-    c = COMPRESS_CHANNELS
+    c = kv.shape[1]
+    if c not in (COMPRESS_CHANNELS, 128):
+        raise ValueError("kv must have 576 or 128 channels")
     ratio = ape.shape[0]
     n_pos = rope_cos.shape[0]
-    rows = key_rope.shape[0]
+    rows = key_nope.shape[0]
     f32 = (torch.float32,)
     _check(kv, "kv", f32, (t_tokens, c), dev)
     _check(score, "score", f32, (t_tokens, c), dev)
@@ -751,10 +754,15 @@ def _marshal_compress(kv, score, ape, gamma, eps, rope_cos, rope_sin, start_pos,
     _check(block_table_cmp, "block_table_cmp", (torch.int32,), None, dev)
     if block_table_cmp.dim() != 2 or block_table_cmp.shape[0] != batch:
         raise ValueError("block_table_cmp must be (batch, max_blocks)")
-    _check(key_nope, "key_nope", (torch.bfloat16,), (rows, KV_LORA_RANK), dev)
-    _check(key_rope, "key_rope", (torch.bfloat16,), (rows, ROPE_DIM), dev)
+    if c == COMPRESS_CHANNELS:
+        _check(key_nope, "key_nope", (torch.bfloat16,), (rows, KV_LORA_RANK), dev)
+        _check(key_rope, "key_rope", (torch.bfloat16,), (rows, ROPE_DIM), dev)
+    else:
+        _check(key_nope, "key_nope", (torch.bfloat16,), (rows, c), dev)
+        key_rope = None
     dims = SfaCompressDims(batch=batch, s1=s1, channels=c, ratio=ratio, rope_positions=n_pos,
-                           max_blocks=block_table_cmp.shape[1], block_size=BLOCK_SIZE, num_cache_rows=rows)
+                           max_blocks=block_table_cmp.shape[1], block_size=BLOCK_SIZE, rotate=int(bool(rotate)),
+                           num_cache_rows=rows)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     args = (ctypes.byref(dims), _ptr(kv), _ptr(score), _ptr(ape), _ptr(gamma), ctypes.c_float(eps), _ptr(rope_cos),
@@ -766,11 +774,13 @@ def _marshal_compress(kv, score, ape, gamma, eps, rope_cos, rope_sin, start_pos,
 
 
 def compress(kv, score, ape, gamma, eps, rope_cos, rope_sin, start_pos, kv_state, score_state, block_table_cmp,
-             key_nope, key_rope, *, batch, s1, stream=None):
+             key_nope, key_rope, *, batch, s1, rotate=False, stream=None):
     """sfa_compress: refreshes kv_state / score_state in place and writes the compressed entries
-    of the windows the new tokens close into key_nope / key_rope. Returns key_nope."""
+    of the windows the new tokens close into key_nope / key_rope (576 channels) or key_nope alone
+    (128 channels; key_rope may be None). Returns key_nope."""
     args, _keep = _marshal_compress(kv, score, ape, gamma, eps, rope_cos, rope_sin, start_pos, kv_state, score_state,
-                                    block_table_cmp, key_nope, key_rope, batch=batch, s1=s1, stream=stream)
+                                    block_table_cmp, key_nope, key_rope, batch=batch, s1=s1, rotate=rotate,
+                                    stream=stream)
     st = _lib.sfa_compress(*args)
     if st != 0:
         raise SfaError(st, "sfa_compress")
@@ -790,7 +800,8 @@ def compress_to_device(inp, device="cuda"):
     return {"kv": t(inp.kv), "score": t(inp.score), "ape": t(inp.ape), "gamma": t(inp.gamma),
             "rope_cos": t(inp.rope_cos), "rope_sin": t(inp.rope_sin), "start_pos": t(inp.start_pos),
             "kv_state": t(inp.kv_state), "score_state": t(inp.score_state),
-            "block_table_cmp": t(inp.block_table_cmp), "key_nope": bf16(inp.key_nope), "key_rope": bf16(inp.key_rope)}
+            "block_table_cmp": t(inp.block_table_cmp), "key_nope": bf16(inp.key_nope),
+            "key_rope": None if inp.key_rope is None else bf16(inp.key_rope)}
 
 
 def _compress_tensors(d):
@@ -800,14 +811,15 @@ def _compress_tensors(d):
 def run_compress(inp, d):
     """sfa_compress on an uploaded CompressInputs instance (updates d's state and pool tensors)."""
     return compress(*_compress_tensors(d), inp.eps, d["rope_cos"], d["rope_sin"], d["start_pos"], d["kv_state"],
-                    d["score_state"], d["block_table_cmp"], d["key_nope"], d["key_rope"], batch=inp.batch, s1=inp.s1)
+                    d["score_state"], d["block_table_cmp"], d["key_nope"], d["key_rope"], batch=inp.batch, s1=inp.s1,
+                    rotate=inp.rotate)
 
 
 def prepare_compress(inp, d, stream=None) -> PreparedCall:
     """sfa_compress bound to an uploaded CompressInputs instance (a PreparedCall returning key_nope)."""
     args, keep = _marshal_compress(*_compress_tensors(d), inp.eps, d["rope_cos"], d["rope_sin"], d["start_pos"],
                                    d["kv_state"], d["score_state"], d["block_table_cmp"], d["key_nope"],
-                                   d["key_rope"], batch=inp.batch, s1=inp.s1, stream=stream)
+                                   d["key_rope"], batch=inp.batch, s1=inp.s1, rotate=inp.rotate, stream=stream)
     return PreparedCall([(_lib.sfa_compress, args, "sfa_compress")], d["key_nope"], keep)
 
 

@@ -338,6 +338,14 @@ def test_compress_validation():
     assert _cmp(d, eps=float("inf")) == -2
     assert _cmp(_cdims(batch=0)) == 0                    # nothing to do: no HIP call
     assert _cmp(_cdims(s1=0)) == 0
+    # the Hadamard branch needs a power-of-two width: 128 channels only
+    assert _cmp(_cdims(rotate=1)) == -2
+    assert _cmp(_cdims(rotate=2)) == -2
+    assert _cmp(_cdims(channels=128, rotate=2)) == -2
+    # 128 channels: the row goes whole to key_nope_2d, key_rope_2d may be NULL (validated only)
+    c128 = _cdims(channels=128, rotate=1)
+    assert _cmp(c128, kn=None) == -1
+    assert _cmp(c128, ks=0x1000000 + 1024) == -6          # state overlaps kv (2 KB at 128 channels)
 
 
 def test_noalloc_rejects_calls_beyond_its_scratch():

@@ -30,7 +30,7 @@ def _run(sfa_lib, inp, d=None):
 def _host(d):
     import torch
 
-    bits = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    bits = lambda t: None if t is None else t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
     return d["kv_state"].cpu().numpy(), d["score_state"].cpu().numpy(), bits(d["key_nope"]), bits(d["key_rope"])
 
 
@@ -47,9 +47,11 @@ def _assert_matches(inp, got, want=None, pool=None):
     untouched = np.ones(kn.shape[0], dtype=bool)
     untouched[list(written)] = False
     np.testing.assert_array_equal(kn[untouched], base_n[untouched])
-    np.testing.assert_array_equal(kr[untouched], base_r[untouched])
+    if kr is not None:
+        np.testing.assert_array_equal(kr[untouched], base_r[untouched])
     for row, (b, c, y) in written.items():
-        g = np.concatenate([O.bf16_bits_to_f64(kn[row]), O.bf16_bits_to_f64(kr[row])])
+        g = (np.concatenate([O.bf16_bits_to_f64(kn[row]), O.bf16_bits_to_f64(kr[row])]) if kr is not None
+             else O.bf16_bits_to_f64(kn[row]))
         err = np.abs(g - y)
         bound = 1e-4 + 5e-3 * np.abs(y)
         bad = np.nonzero(err > bound)[0]
@@ -159,3 +161,34 @@ def test_compressed_entry_feeds_scfa(sfa_lib):
     ref = WO.window_attention(win)
     rep = O.allclose_report(out.float().cpu().numpy().astype(np.float64).reshape(ref.shape), ref)
     assert rep["fails"] == 0, rep
+
+
+# ---- 128-channel rows (index keys) and the rotate = true branch (Hadamard transform) ----
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_index_keys_rotated_full_size(sfa_lib, seed):
+    """The page's D = 128 configuration with rotate = true on the decode step: 64 sequences,
+    positions 8190 and 8191, ratio 4, every sequence closing a window."""
+    inp = W.compress_index_decode(seed=seed)
+    assert inp.channels == 128 and inp.rotate
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 64
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+def test_index_keys_windows_and_ragged_positions(sfa_lib, rotate):
+    """128 channels, with and without the transform: seven tokens spanning two windows, a
+    sequence starting before position 0 and one running past the RoPE tables."""
+    inp = W.compress_generate(batch=4, s1=7, ratio=4, start_pos=[5, -2, 58, 5], rope_positions=64, max_blocks=2,
+                              seed=13, channels=128, rotate=rotate)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 2 + 1 + 2 + 2
+
+
+def test_index_keys_ratio_one_peaky(sfa_lib):
+    """Ratio 1 (every token emits, so the entry is the token's own normalised, rotated and
+    transformed row) and ratio 128 with peaky scores, both rotated."""
+    inp = W.compress_generate(batch=3, s1=2, ratio=1, start_pos=[0, 40, 90], rope_positions=128, max_blocks=2,
+                              seed=14, channels=128, rotate=True)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 6
+    inp = W.compress_generate(batch=4, s1=1, ratio=128, start_pos=[127 + 128 * k for k in range(4)],
+                              rope_positions=1024, max_blocks=2, seed=15, score_scale=4.0, channels=128, rotate=True)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 4
