@@ -826,3 +826,70 @@ def compress_index_decode(seed: int = 0, ratio: int = 4) -> CompressInputs:
     return compress_generate(batch=64, s1=2, ratio=ratio, start_pos=[8190] * 64, rope_positions=8192,
                              max_blocks=2048 // BLOCK_SIZE, seed=seed, channels=128, rotate=True,
                              name=f"compress_b64_s2_r{ratio}_c128_rot")
+
+
+# ---- Indexer prolog ----------------------------------------------------------------------
+
+@dataclasses.dataclass
+class IndexerPrologInputs:
+    tokens: int
+    n_heads: int
+    x: np.ndarray               # uint16 bf16 bits (T, hidden)
+    qr: np.ndarray              # uint16 (T, q_lora_rank): the normalised query of the MLA prolog
+    w_idx_qb: np.ndarray        # uint16 (n_heads * head_dim, q_lora_rank)
+    w_idx_k: np.ndarray         # uint16 (head_dim, hidden)
+    ln_gamma_k: np.ndarray      # uint16 (head_dim)
+    ln_beta_k: np.ndarray       # uint16 (head_dim)
+    w_idx_proj: np.ndarray      # uint16 (n_heads, hidden)
+    positions: np.ndarray       # int32 (T)
+    rope_cos: np.ndarray        # float32 (rope_positions, 32)
+    rope_sin: np.ndarray
+    eps: float
+    rotate: bool
+    name: str = ""
+
+    @property
+    def hidden(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def q_lora_rank(self) -> int:
+        return int(self.qr.shape[1])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.w_idx_k.shape[0])
+
+    @property
+    def rope_positions(self) -> int:
+        return int(self.rope_cos.shape[0])
+
+
+def indexer_prolog_generate(*, tokens: int, hidden: int = 7168, q_lora_rank: int = 1536, n_heads: int = 64,
+                            head_dim: int = 128, positions: Optional[Sequence[int]] = None,
+                            rope_positions: int = 8192, rotate: bool = True, seed: int = 0,
+                            name: str = "") -> IndexerPrologInputs:
+    """x and qr are N(0,1) (qr stands for the MLA prolog's RMS-normalised query); each weight is
+    N(0, 1/fan_in); the LayerNorm scale is 1 + N(0, 0.1^2) and its shift N(0, 0.1^2); all bf16.
+    Positions default to 8190, 8191 alternating; eps is 1e-6."""
+    g = torch.Generator().manual_seed(120_000 + int(seed))
+    x = _scaled_bf16(g, (tokens, hidden), 1.0)
+    qr = _scaled_bf16(g, (tokens, q_lora_rank), 1.0)
+    w_qb = _scaled_bf16(g, (n_heads * head_dim, q_lora_rank), q_lora_rank ** -0.5)
+    w_k = _scaled_bf16(g, (head_dim, hidden), hidden ** -0.5)
+    gamma = _bf16_bits(1.0 + torch.randn(head_dim, generator=g) * 0.1)
+    beta = _bf16_bits(torch.randn(head_dim, generator=g) * 0.1)
+    w_proj = _scaled_bf16(g, (n_heads, hidden), hidden ** -0.5)
+    if positions is None:
+        positions = [8190 + (t % 2) for t in range(tokens)]
+    cos, sin = rope_tables(rope_positions)
+    return IndexerPrologInputs(tokens=int(tokens), n_heads=int(n_heads), x=x, qr=qr, w_idx_qb=w_qb, w_idx_k=w_k,
+                               ln_gamma_k=gamma, ln_beta_k=beta, w_idx_proj=w_proj,
+                               positions=np.ascontiguousarray(positions, dtype=np.int32), rope_cos=cos, rope_sin=sin,
+                               eps=1e-6, rotate=bool(rotate), name=name)
+
+
+def indexer_prolog_decode(seed: int = 0) -> IndexerPrologInputs:
+    """The decode step's indexer prolog: 64 sequences x 2 new tokens, hidden 7168, query rank
+    1536, 64 index heads of 128, with the Hadamard transform."""
+    return indexer_prolog_generate(tokens=128, seed=seed, name="indexer_prolog_b64_s2")

@@ -43,7 +43,8 @@ Readings (each is listed with its reason in the design notes):
 
 Pinned by tests/test_prolog_oracle.py: a pure-Python scalar brute force on tiny shapes, closed
 forms (identity absorption, quarter-turn and zero-angle rotation, scale invariance of the
-normalised outputs, unit mean square), head permutation, and planted mistakes.
+normalised outputs, unit mean square), head permutation, and planted mistakes. The indexer
+prolog at the end of this module is pinned in tests/test_indexer_prolog_oracle.py.
 """
 
 from __future__ import annotations
@@ -128,3 +129,59 @@ def mla_prolog(x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, positions,
     kv_rope = rope_interleaved(kv[:, LATENT:LATENT + ROPE], cos, sin)
     kv_rope[~live] = 0.0
     return q_nope, q_rope, kv_nope, kv_rope
+
+
+# ---- Indexer prolog ---------------------------------------------------------------------
+# "CANN DeepSeek Indexer attention optimisation", section "Indexer Prolog": the index query of
+# head h is RoPE(RMSNorm(X W_qa) W_qb), the index key RoPE(LayerNorm(X W_k)); RoPE only on the
+# second half of the head dimension; the per-head weights w_h of the Lightning Indexer come from
+# a projection of x. "NPU DeepSeek-V4 model PyPTO fused-operator optimisation", section
+# "IndexerProlog": the query's rotary part is the part after nope_dim, the result goes through
+# a Hadamard transform, and the weights are x . weights_proj times 1 / sqrt(heads * head_dim).
+# Readings: qr (RMSNorm(X W_qa) times its scale) is the MLA prolog's normalised query, taken
+# as a bf16 input; LayerNorm(v) = (v - mean) / sqrt(var + eps) * gamma + beta, with the
+# population variance; rotate applies the same Sylvester Hadamard transform (scaled by
+# 1/sqrt(head_dim)) to the query of every head and to the key, after RoPE; the V4 page's INT8
+# quantisation of the query is not applied (the Lightning Indexer here scores bf16 queries).
+
+def hadamard_last(v: np.ndarray) -> np.ndarray:
+    """H v / sqrt(n) over the last axis, H the Sylvester Hadamard matrix of order n (symmetric,
+    natural order), n a power of two."""
+    import scipy.linalg
+
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[-1]
+    return v @ scipy.linalg.hadamard(n).astype(np.float64) / np.sqrt(n)
+
+
+def layer_norm(v: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float) -> np.ndarray:
+    """(v - mean) / sqrt(var + eps) * gamma + beta over the last axis (population variance)."""
+    v = np.asarray(v, dtype=np.float64)
+    mu = v.mean(axis=-1, keepdims=True)
+    var = ((v - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (v - mu) / np.sqrt(var + float(eps)) * np.asarray(gamma, np.float64) + np.asarray(beta, np.float64)
+
+
+def indexer_prolog(x, qr, w_idx_qb, w_idx_k, ln_gamma_k, ln_beta_k, w_idx_proj, positions, rope_cos, rope_sin,
+                   eps, n_heads: int, rotate: bool):
+    """bf16 inputs as uint16 bits: x (T, H), qr (T, Q), w_idx_qb (n_heads*D, Q), w_idx_k (D, H),
+    ln_gamma_k / ln_beta_k (D), w_idx_proj (n_heads, H). Returns float64 before the outputs'
+    rounding: q_index (T, n_heads, D), k_index (T, D), weights (T, n_heads)."""
+    X = bf16_bits_to_f64(x)
+    t = X.shape[0]
+    wk = bf16_bits_to_f64(w_idx_k)
+    d = wk.shape[0]
+    cos, sin, live = rope_rows(positions, rope_cos, rope_sin)
+    half = d - ROPE
+
+    q = (bf16_bits_to_f64(qr) @ bf16_bits_to_f64(w_idx_qb).T).reshape(t, n_heads, d)
+    q[:, :, half:] = rope_interleaved(q[:, :, half:], cos[:, None, :], sin[:, None, :])
+    q[~live, :, half:] = 0.0
+    k = layer_norm(X @ wk.T, bf16_bits_to_f64(ln_gamma_k), bf16_bits_to_f64(ln_beta_k), eps)
+    k[:, half:] = rope_interleaved(k[:, half:], cos, sin)
+    k[~live, half:] = 0.0
+    if rotate:
+        q = hadamard_last(q)
+        k = hadamard_last(k)
+    w = (X @ bf16_bits_to_f64(w_idx_proj).T) / np.sqrt(n_heads * d)
+    return q, k, w
