@@ -803,15 +803,21 @@ def bench_compress(args):
     print(json.dumps(rec), flush=True)
 
 
-PROLOG_WORKLOADS = {"mla_prolog_b64_s2": "prolog_decode"}
+PROLOG_WORKLOADS = {"mla_prolog_b64_s2": "prolog_decode", "indexer_prolog_b64_s2": "indexer_prolog_decode"}
 
 
 def prolog_work(inp):
-    """Bytes and flops the MLA prolog must move and do per call: every weight once, the hidden
-    rows, the four outputs, the positions and the RoPE table rows used; the four products."""
+    """Bytes and flops the MLA prolog (or the indexer prolog) must move and do per call: every
+    weight once, the inputs, the outputs, the positions and the RoPE table rows used; the
+    products."""
+    rows = len({int(p) for p in inp.positions if 0 <= int(p) < inp.rope_positions})
+    if hasattr(inp, "w_idx_qb"):
+        t, h, q, n, d = inp.tokens, inp.hidden, inp.q_lora_rank, inp.n_heads, inp.head_dim
+        weights = (n * d * q + d * h + 2 * d + n * h) * 2
+        nbytes = weights + t * h * 2 + t * q * 2 + t * n * d * 2 + t * d * 2 + t * n * 4 + t * 4 + rows * 32 * 4 * 2
+        return nbytes, 2 * t * (q * n * d + h * (d + n))
     t, h, q, n, dn = inp.tokens, inp.hidden, inp.q_lora_rank, inp.n_q, inp.nope_dim
     weights = (q * h + n * (dn + 64) * q + n * 512 * dn + 576 * h + q + 512) * 2
-    rows = len({int(p) for p in inp.positions if 0 <= int(p) < inp.rope_positions})
     nbytes = weights + t * h * 2 + t * n * 576 * 2 + t * 576 * 2 + t * 4 + rows * 32 * 4 * 2
     flop = 2 * t * (h * (q + 576) + q * n * (dn + 64) + n * 512 * dn)
     return nbytes, flop
@@ -829,10 +835,14 @@ def bench_prolog(args):
 
     inp = getattr(workloads, PROLOG_WORKLOADS[args.workload])(seed=args.seed)
     print(f"[bench] generated {inp.name}", file=sys.stderr, flush=True)
-    d0 = sfa.prolog_to_device(inp)
+    indexer = hasattr(inp, "w_idx_qb")
+    to_dev = sfa.indexer_prolog_to_device if indexer else sfa.prolog_to_device
+    run = sfa.run_indexer_prolog if indexer else sfa.run_prolog
+    prep = sfa.prepare_indexer_prolog_run if indexer else sfa.prepare_prolog_run
+    d0 = to_dev(inp)
     sets = [d0] + [{k: v.clone() for k, v in d0.items()} for _ in range(1, max(1, args.sets))]
-    outs = [tuple(torch.empty_like(o) for o in sfa.run_prolog(inp, d0)) for _ in sets]
-    calls = [sfa.prepare_prolog_run(inp, sets[k], out=outs[k]) for k in range(len(sets))]
+    outs = [tuple(torch.empty_like(o) for o in run(inp, d0)) for _ in sets]
+    calls = [prep(inp, sets[k], out=outs[k]) for k in range(len(sets))]
     torch.cuda.synchronize()
 
     def step(i):
@@ -855,8 +865,7 @@ def bench_prolog(args):
         ends[i].record()
     torch.cuda.synchronize()
     launch_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps
-    same = all(all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(outs[0], o))
-               for o in outs[1:])
+    same = all(all(torch.equal(a, b) for a, b in zip(outs[0], o)) for o in outs[1:])
     nbytes, flop = prolog_work(inp)
     gbps = nbytes / (launch_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash(("prolog_kernels.hip", "prolog_internal.h"))
@@ -873,9 +882,12 @@ def bench_prolog(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": inp.tokens, "hidden": inp.hidden,
-                   "q_lora_rank": inp.q_lora_rank, "n_q": inp.n_q, "qk_nope_dim": inp.nope_dim,
-                   "cold_sets": len(sets)},
+        "config": ({"workload": args.workload, "tokens": inp.tokens, "hidden": inp.hidden,
+                    "q_lora_rank": inp.q_lora_rank, "n_heads": inp.n_heads, "head_dim": inp.head_dim,
+                    "rotate": inp.rotate, "cold_sets": len(sets)} if indexer else
+                   {"workload": args.workload, "tokens": inp.tokens, "hidden": inp.hidden,
+                    "q_lora_rank": inp.q_lora_rank, "n_q": inp.n_q, "qk_nope_dim": inp.nope_dim,
+                    "cold_sets": len(sets)}),
         "kernel_ms_mean": round(launch_ms, 5),
         "algorithmic_bytes_per_call": nbytes,
         "algorithmic_flop_per_call": flop,
@@ -889,12 +901,18 @@ def bench_prolog(args):
     if args.cpu_seconds > 0:
         # the oracle over the whole call until the budget is spent; its first result is checked
         # against the GPU's outputs element by element
-        got = [PO.bf16_bits_to_f64(o.cpu().view(torch.int16).numpy().view(np.uint16)) for o in outs[0]]
+        got = [PO.bf16_bits_to_f64(o.cpu().view(torch.int16).numpy().view(np.uint16)) if o.dtype == torch.bfloat16
+               else o.cpu().numpy().astype(np.float64) for o in outs[0]]
         t0 = time.perf_counter()
         runs, bad = 0, 0
         while runs == 0 or time.perf_counter() - t0 < args.cpu_seconds:
-            want = PO.mla_prolog(inp.x, inp.w_dq, inp.gamma_cq, inp.w_uq_qr, inp.w_uk, inp.w_dkv_kr, inp.gamma_ckv,
-                                 inp.positions, inp.rope_cos, inp.rope_sin, inp.eps, inp.n_q)
+            if indexer:
+                want = PO.indexer_prolog(inp.x, inp.qr, inp.w_idx_qb, inp.w_idx_k, inp.ln_gamma_k, inp.ln_beta_k,
+                                         inp.w_idx_proj, inp.positions, inp.rope_cos, inp.rope_sin, inp.eps,
+                                         inp.n_heads, inp.rotate)
+            else:
+                want = PO.mla_prolog(inp.x, inp.w_dq, inp.gamma_cq, inp.w_uq_qr, inp.w_uk, inp.w_dkv_kr,
+                                     inp.gamma_ckv, inp.positions, inp.rope_cos, inp.rope_sin, inp.eps, inp.n_q)
             if runs == 0:
                 for g, w in zip(got, want):
                     w = w.reshape(g.shape)

@@ -424,6 +424,7 @@ int sfa_compress(const sfa_compress_dims* dims, const float* kv, const float* sc
  *   q_nope     bf16 (T*n_q, 512)       row t*n_q + h: sfa_decode's query_nope
  *   q_rope     bf16 (T*n_q, 64)        sfa_decode's query_rope
  *   kv_nope    bf16 (T, 512), kv_rope bf16 (T, 64): sfa_cache_write's new_nope / new_rope
+ *   cq_out     bf16 (T, Q), or NULL: cq rounded to bf16 (the indexer prolog's qr input)
  *   workspace  >= sfa_mla_prolog_workspace_size bytes, 256-byte aligned, no initialisation
  *
  * Errors: SFA_ERR_NULL, SFA_ERR_DIMS, SFA_ERR_ALIGN (any pointer not 16-byte aligned),
@@ -447,8 +448,55 @@ int sfa_mla_prolog_workspace_size(const sfa_prolog_dims* dims, size_t* bytes_out
 int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq, const void* gamma_cq,
                    const void* w_uq_qr, const void* w_uk, const void* w_dkv_kr, const void* gamma_ckv,
                    const int32_t* positions, const float* rope_cos, const float* rope_sin, void* q_nope,
-                   void* q_rope, void* kv_nope, void* kv_rope, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream);
+                   void* q_rope, void* kv_nope, void* kv_rope, void* cq_out, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Indexer prolog: the new tokens' inputs of the Lightning Indexer ("CANN DeepSeek Indexer
+ * attention optimisation", section "Indexer Prolog": the index query RoPE(RMSNorm(X W_qa) W_qb),
+ * the index key RoPE(LayerNorm(X W_k)), RoPE on the second half of the head dimension, the
+ * head weights from a projection of x; "NPU DeepSeek-V4 model PyPTO fused-operator
+ * optimisation", section "IndexerProlog": the Hadamard transform after RoPE and the weights'
+ * 1/sqrt(heads * head_dim) scale). For token t with hidden row x, normalised query qr (the MLA
+ * prolog's cq: sfa_mla_prolog's cq_out) and position p:
+ *
+ *   q[h]    = (qr . W_qb^T)[h*128 .. h*128 + 128)                  per index head h
+ *   k       = LayerNorm(x . W_k^T) = (v - mean) / sqrt(var + eps) * ln_gamma + ln_beta
+ *   channels 64 + 2i, 65 + 2i of q[h] and k turn by the angle of rope_cos[p][i], rope_sin[p][i]
+ *   (zeros when p is outside the tables); with rotate = 1, q[h] and k then become H v / sqrt(128),
+ *   H the Sylvester Hadamard matrix (the same map on both: every q . k is unchanged)
+ *   weights[h] = (x . W_proj^T)[h] / sqrt(n_heads * 128)
+ *
+ * The products accumulate in fp32; q_index and k_index are rounded to bf16, weights stay fp32.
+ * The V4 page's INT8 quantisation of the query is not applied (sfa_indexer_scores takes bf16).
+ *
+ *   x           bf16 (T, H)          qr          bf16 (T, Q)
+ *   w_idx_qb    bf16 (n_heads*128, Q)              w_idx_k     bf16 (128, H)
+ *   ln_gamma_k, ln_beta_k  bf16 (128)             w_idx_proj  bf16 (n_heads, H)
+ *   positions   int32 (T)            rope_cos, rope_sin  fp32 (rope_positions, 32)
+ *   q_index     bf16 (T*n_heads, 128): sfa_indexer_scores' q_index
+ *   k_index     bf16 (T, 128): the new rows of its index-key cache
+ *   weights     fp32 (T, n_heads): sfa_indexer_scores' weights
+ *   workspace   >= sfa_indexer_prolog_workspace_size bytes, 256-byte aligned, no initialisation
+ *
+ * Errors as sfa_mla_prolog's. With T = 0 nothing is read or queued and the pointers may be NULL.
+ */
+typedef struct {
+  int32_t tokens;               /* T >= 0                                                     */
+  int32_t hidden;               /* H: a multiple of 64 in [256, 65536]                        */
+  int32_t q_lora_rank;          /* Q: a multiple of 64 in [256, 4096]                         */
+  int32_t n_heads;              /* index heads: must be 64                                    */
+  int32_t head_dim;             /* must be 128                                                */
+  int32_t rope_positions;       /* rows of rope_cos and rope_sin, >= 1                        */
+  int32_t rotate;               /* 0, or 1: the Hadamard transform of query and key           */
+  float eps;                    /* LayerNorm epsilon, finite and >= 0                         */
+} sfa_indexer_prolog_dims;
+
+int sfa_indexer_prolog_workspace_size(const sfa_indexer_prolog_dims* dims, size_t* bytes_out);
+int sfa_indexer_prolog(const sfa_indexer_prolog_dims* dims, const void* x, const void* qr, const void* w_idx_qb,
+                       const void* w_idx_k, const void* ln_gamma_k, const void* ln_beta_k, const void* w_idx_proj,
+                       const int32_t* positions, const float* rope_cos, const float* rope_sin, void* q_index,
+                       void* k_index, float* weights, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

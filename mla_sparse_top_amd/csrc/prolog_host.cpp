@@ -1,6 +1,7 @@
-// C-ABI entry points of the MLA prolog (sfa_mla_prolog_workspace_size, sfa_mla_prolog):
-// synchronous argument validation, the k split of the down-projections, workspace layout, and
-// the four launches. Declarations and contracts are in include/sfa.h.
+// C-ABI entry points of the MLA prolog (sfa_mla_prolog_workspace_size, sfa_mla_prolog) and of
+// the indexer prolog (sfa_indexer_prolog_workspace_size, sfa_indexer_prolog): synchronous
+// argument validation, the k splits of the projections, workspace layouts, and the launches.
+// Declarations and contracts are in include/sfa.h.
 
 #include <math.h>
 #include <stdint.h>
@@ -75,6 +76,49 @@ Layout layout(const sfa_prolog_dims* d, int splits) {
   return l;
 }
 
+// ---- indexer prolog
+
+constexpr int kIpDim = 128;  // index head width (the Lightning Indexer's)
+
+int check_ip(const sfa_indexer_prolog_dims* d) {
+  if (!d) return SFA_ERR_NULL;
+  if (d->tokens < 0 || d->tokens > (1 << 20)) return SFA_ERR_DIMS;
+  if (d->hidden < 256 || d->hidden > (1 << 16) || d->hidden % 64) return SFA_ERR_DIMS;
+  if (d->q_lora_rank < 256 || d->q_lora_rank > 4096 || d->q_lora_rank % 64) return SFA_ERR_DIMS;
+  if (d->n_heads != 64 || d->head_dim != kIpDim) return SFA_ERR_DIMS;
+  if (d->rope_positions < 1 || (d->rotate != 0 && d->rotate != 1)) return SFA_ERR_DIMS;
+  if (!(d->eps >= 0.0f) || !isfinite(d->eps)) return SFA_ERR_DIMS;
+  return SFA_OK;
+}
+
+// k splits of one of the indexer prolog's projections: the largest that keeps the launch
+// within one round of workgroups and every split at least 4 chunks of 64
+int ip_splits(int64_t tiles, int64_t tok_blocks, int k) {
+  const int units = k / 64;
+  int best = 1;
+  for (int s = 1; s <= units; ++s)
+    if (units % s == 0 && units / s >= 4 && tiles * tok_blocks * s <= kTargetWorkgroups) best = s;
+  return best;
+}
+
+struct IpLayout {
+  size_t part_q, part_kw, total;
+  int split_q, split_kw;
+};
+
+IpLayout ip_layout(const sfa_indexer_prolog_dims* d) {
+  const int64_t t = d->tokens, tok_blocks = (t + kPrTokBlock - 1) / kPrTokBlock;
+  const int feat = 32 * kPrFb0;
+  const int64_t nq = (int64_t)d->n_heads * kIpDim, nkw = kIpDim + d->n_heads;
+  IpLayout l{};
+  l.split_q = ip_splits((nq + feat - 1) / feat, tok_blocks, d->q_lora_rank);
+  l.split_kw = ip_splits((nkw + feat - 1) / feat, tok_blocks, d->hidden);
+  l.part_q = 0;
+  l.part_kw = align_up((size_t)l.split_q * t * nq * 4, kAlign);
+  l.total = t ? l.part_kw + align_up((size_t)l.split_kw * t * nkw * 4, kAlign) : 0;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,8 +134,8 @@ int sfa_mla_prolog_workspace_size(const sfa_prolog_dims* dims, size_t* bytes_out
 int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq, const void* gamma_cq,
                    const void* w_uq_qr, const void* w_uk, const void* w_dkv_kr, const void* gamma_ckv,
                    const int32_t* positions, const float* rope_cos, const float* rope_sin, void* q_nope,
-                   void* q_rope, void* kv_nope, void* kv_rope, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
+                   void* q_rope, void* kv_nope, void* kv_rope, void* cq_out, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
   const int st = check(dims);
   if (st != SFA_OK) return st;
   if (dims->tokens == 0) return SFA_OK;  // nothing to read or write; pointers may be NULL
@@ -105,6 +149,7 @@ int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq,
     if (!aligned16(p)) return SFA_ERR_ALIGN;
   for (const void* p : outs)
     if (!aligned16(p)) return SFA_ERR_ALIGN;
+  if (cq_out && !aligned16(cq_out)) return SFA_ERR_ALIGN;
   const int splits = down_splits(dims);
   const Layout lay = layout(dims, splits);
   if (lay.total > 0 && (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace % kAlign) != 0))
@@ -121,7 +166,11 @@ int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq,
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SFA_ERR_ALIAS;
     if (overlaps(outs[i], out_bytes[i], workspace, lay.total)) return SFA_ERR_ALIAS;
+    if (overlaps(outs[i], out_bytes[i], cq_out, t * q * 2)) return SFA_ERR_ALIAS;
   }
+  for (int j = 0; j < 10; ++j)
+    if (overlaps(cq_out, t * q * 2, ins[j], in_bytes[j])) return SFA_ERR_ALIAS;
+  if (overlaps(cq_out, t * q * 2, workspace, lay.total)) return SFA_ERR_ALIAS;
   char* ws = static_cast<char*>(workspace);
   float* part = reinterpret_cast<float*>(ws + lay.part);
   uint16_t* cq_hi = reinterpret_cast<uint16_t*>(ws + lay.cq_hi);
@@ -168,6 +217,7 @@ int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq,
   nm.cq_lo = cq_lo;
   nm.kv_nope = static_cast<uint16_t*>(kv_nope);
   nm.kv_rope = static_cast<uint16_t*>(kv_rope);
+  nm.cq_out = static_cast<uint16_t*>(cq_out);
   nm.positions = positions;
   nm.rope_cos = rope_cos;
   nm.rope_sin = rope_sin;
@@ -206,6 +256,104 @@ int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq,
   g3.q_nope = static_cast<uint16_t*>(q_nope);
   if (launch_prolog_gemm(g3, 2, stream) != hipSuccess) return SFA_ERR_HIP;
   return SFA_OK;
+}
+
+int sfa_indexer_prolog_workspace_size(const sfa_indexer_prolog_dims* dims, size_t* bytes_out) {
+  if (!bytes_out) return SFA_ERR_NULL;
+  const int st = check_ip(dims);
+  if (st != SFA_OK) return st;
+  *bytes_out = ip_layout(dims).total;
+  return SFA_OK;
+}
+
+int sfa_indexer_prolog(const sfa_indexer_prolog_dims* dims, const void* x, const void* qr, const void* w_idx_qb,
+                       const void* w_idx_k, const void* ln_gamma_k, const void* ln_beta_k, const void* w_idx_proj,
+                       const int32_t* positions, const float* rope_cos, const float* rope_sin, void* q_index,
+                       void* k_index, float* weights, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_ip(dims);
+  if (st != SFA_OK) return st;
+  if (dims->tokens == 0) return SFA_OK;  // nothing to read or write; pointers may be NULL
+  const void* ins[] = {x, qr, w_idx_qb, w_idx_k, ln_gamma_k, ln_beta_k, w_idx_proj, positions, rope_cos, rope_sin};
+  void* outs[] = {q_index, k_index, weights};
+  for (const void* p : ins)
+    if (!p) return SFA_ERR_NULL;
+  for (const void* p : outs)
+    if (!p) return SFA_ERR_NULL;
+  for (const void* p : ins)
+    if (!aligned16(p)) return SFA_ERR_ALIGN;
+  for (const void* p : outs)
+    if (!aligned16(p)) return SFA_ERR_ALIGN;
+  const IpLayout lay = ip_layout(dims);
+  if (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace % kAlign) != 0) return SFA_ERR_WORKSPACE;
+  const size_t t = (size_t)dims->tokens, h = (size_t)dims->hidden, q = (size_t)dims->q_lora_rank;
+  const size_t nh = (size_t)dims->n_heads, np = (size_t)dims->rope_positions;
+  const size_t in_bytes[] = {t * h * 2, t * q * 2, nh * kIpDim * q * 2, kIpDim * h * 2, kIpDim * 2, kIpDim * 2,
+                             nh * h * 2, t * 4, np * 32 * 4, np * 32 * 4};
+  const size_t out_bytes[] = {t * nh * kIpDim * 2, t * kIpDim * 2, t * nh * 4};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 10; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return SFA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SFA_ERR_ALIAS;
+    if (overlaps(outs[i], out_bytes[i], workspace, lay.total)) return SFA_ERR_ALIAS;
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* part_q = reinterpret_cast<float*>(ws + lay.part_q);
+  float* part_kw = reinterpret_cast<float*>(ws + lay.part_kw);
+
+  PrologGemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.tokens = (int32_t)t;
+  g.tok_blocks = (int)((t + kPrTokBlock - 1) / kPrTokBlock);
+
+  // index query: qr . W_qb^T, fp32 partial sums over `split_q` k ranges
+  PrologGemmArgs g1 = g;
+  g1.w0 = static_cast<const uint16_t*>(w_idx_qb);
+  g1.w1 = g1.w0;
+  g1.n_feat = (int32_t)(nh * kIpDim);
+  g1.f_split = g1.n_feat;
+  g1.k = (int32_t)q;
+  g1.n_split = lay.split_q;
+  g1.k_chunk = (int32_t)(q / lay.split_q);
+  g1.b_hi = static_cast<const uint16_t*>(qr);
+  g1.b_stride = (int64_t)q;
+  g1.part = part_q;
+  if (launch_prolog_gemm(g1, 0, stream) != hipSuccess) return SFA_ERR_HIP;
+
+  // key and weight projections of x: rows of W_k, then of W_proj
+  PrologGemmArgs g2 = g;
+  g2.w0 = static_cast<const uint16_t*>(w_idx_k);
+  g2.w1 = static_cast<const uint16_t*>(w_idx_proj);
+  g2.f_split = kIpDim;
+  g2.n_feat = (int32_t)(kIpDim + nh);
+  g2.k = (int32_t)h;
+  g2.n_split = lay.split_kw;
+  g2.k_chunk = (int32_t)(h / lay.split_kw);
+  g2.b_hi = static_cast<const uint16_t*>(x);
+  g2.b_stride = (int64_t)h;
+  g2.part = part_kw;
+  if (launch_prolog_gemm(g2, 0, stream) != hipSuccess) return SFA_ERR_HIP;
+
+  IndexerFinishArgs f;
+  f.part_q = part_q;
+  f.part_kw = part_kw;
+  f.split_q = lay.split_q;
+  f.split_kw = lay.split_kw;
+  f.tokens = (int32_t)t;
+  f.n_heads = (int32_t)nh;
+  f.rotate = dims->rotate;
+  f.ln_gamma = static_cast<const uint16_t*>(ln_gamma_k);
+  f.ln_beta = static_cast<const uint16_t*>(ln_beta_k);
+  f.eps = dims->eps;
+  f.w_scale = (float)(1.0 / sqrt((double)nh * kIpDim));
+  f.positions = positions;
+  f.rope_cos = rope_cos;
+  f.rope_sin = rope_sin;
+  f.rope_positions = dims->rope_positions;
+  f.q_index = static_cast<uint16_t*>(q_index);
+  f.k_index = static_cast<uint16_t*>(k_index);
+  f.weights = weights;
+  return launch_indexer_finish(f, stream) == hipSuccess ? SFA_OK : SFA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -52,13 +52,35 @@ struct PrologNormArgs {
   uint16_t* cq_lo;
   uint16_t* kv_nope;         // bf16 (tokens, 512)
   uint16_t* kv_rope;         // bf16 (tokens, 64)
+  uint16_t* cq_out;          // bf16 (tokens, q_rank), or null: cq rounded to bf16
   const int32_t* positions;
   const float* rope_cos;
   const float* rope_sin;
   int32_t rope_positions;
 };
 
+// The indexer prolog's per-token step: sums the split partials of the index query (n_heads x
+// 128 per token) and of the key and weight projections (128 + n_heads), then LayerNorm of the
+// key, RoPE on the second half of every 128-wide vector, the optional Hadamard transform, and
+// the weights' scale.
+struct IndexerFinishArgs {
+  const float* part_q;       // (split_q, tokens, n_heads * 128)
+  const float* part_kw;      // (split_kw, tokens, 128 + n_heads)
+  int32_t split_q, split_kw, tokens, n_heads, rotate;
+  const uint16_t* ln_gamma;  // bf16 (128)
+  const uint16_t* ln_beta;   // bf16 (128)
+  float eps, w_scale;
+  const int32_t* positions;
+  const float* rope_cos;
+  const float* rope_sin;
+  int32_t rope_positions;
+  uint16_t* q_index;         // bf16 (tokens * n_heads, 128)
+  uint16_t* k_index;         // bf16 (tokens, 128)
+  float* weights;            // fp32 (tokens, n_heads)
+};
+
 hipError_t launch_prolog_gemm(const PrologGemmArgs& a, int mode, hipStream_t stream);
+hipError_t launch_indexer_finish(const IndexerFinishArgs& a, hipStream_t stream);
 hipError_t launch_prolog_norm(const PrologNormArgs& a, hipStream_t stream);
 
 }  // namespace sfa

@@ -426,6 +426,7 @@ __global__ void __launch_bounds__(kThreads) prolog_norm_kernel(const PrologNormA
       split4(y, hi, lo);
       *reinterpret_cast<u32x2*>(a.cq_hi + (size_t)t * a.q_rank + 4 * c) = hi;
       *reinterpret_cast<u32x2*>(a.cq_lo + (size_t)t * a.q_rank + 4 * c) = lo;
+      if (a.cq_out) *reinterpret_cast<u32x2*>(a.cq_out + (size_t)t * a.q_rank + 4 * c) = hi;
     } else if (c < nkv4) {
       const int j = 4 * (c - nq4);
       floatx4 y;
@@ -440,7 +441,97 @@ __global__ void __launch_bounds__(kThreads) prolog_norm_kernel(const PrologNormA
   }
 }
 
+// One 128-wide vector per wave pass: lane L holds channels L and L + 64. Channel 64 + 2i and
+// 65 + 2i (lanes 2i and 2i + 1, second register) turn by the angle of column i of row p (zeros
+// outside the tables); then, with rotate, the Sylvester Hadamard transform scaled by
+// 1/sqrt(128): the stride-64 butterfly within the lane, the strides 32 .. 1 across lanes.
+__device__ __forceinline__ void rope_hadamard128(float (&y)[2], int lane, int p, const IndexerFinishArgs& a) {
+  const float partner = __shfl_xor(y[1], 1, 64);
+  if (p < 0 || p >= a.rope_positions) {
+    y[1] = 0.0f;
+  } else {
+    const int i = lane >> 1;
+    const float co = a.rope_cos[(size_t)p * 32 + i], si = a.rope_sin[(size_t)p * 32 + i];
+    y[1] = (lane & 1) ? fmaf(partner, si, y[1] * co) : fmaf(-partner, si, y[1] * co);
+  }
+  if (a.rotate) {
+    const float u0 = y[0] + y[1], u1 = y[0] - y[1];
+    y[0] = u0;
+    y[1] = u1;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float q = __shfl_xor(y[k], d, 64);
+        y[k] = (lane & d) ? q - y[k] : y[k] + q;
+      }
+    }
+    y[0] *= 0.08838834764831845f;  // 1/sqrt(128)
+    y[1] *= 0.08838834764831845f;
+  }
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+// One workgroup (4 waves) per token: wave w takes heads w, w + 4, ... of the query; wave 0 then
+// the key (LayerNorm over its 128 channels), wave 1 the head weights.
+__global__ void __launch_bounds__(kThreads) indexer_finish_kernel(const IndexerFinishArgs a) {
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int p = a.positions[t];
+  const int nq = a.n_heads * 128;
+  for (int h = wave; h < a.n_heads; h += 4) {
+    float y[2] = {0.0f, 0.0f};
+    for (int s = 0; s < a.split_q; ++s) {
+      const float* src = a.part_q + ((size_t)s * a.tokens + t) * nq + h * 128;
+      y[0] += src[lane];
+      y[1] += src[64 + lane];
+    }
+    rope_hadamard128(y, lane, p, a);
+    uint16_t* dst = a.q_index + ((size_t)t * a.n_heads + h) * 128;
+    dst[lane] = bf16_bits(y[0]);
+    dst[64 + lane] = bf16_bits(y[1]);
+  }
+  const int nkw = 128 + a.n_heads;
+  if (wave == 0) {
+    float y[2] = {0.0f, 0.0f};
+    for (int s = 0; s < a.split_kw; ++s) {
+      const float* src = a.part_kw + ((size_t)s * a.tokens + t) * nkw;
+      y[0] += src[lane];
+      y[1] += src[64 + lane];
+    }
+    float sum = y[0] + y[1];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
+    const float mu = sum * (1.0f / 128.0f);
+    const float d0 = y[0] - mu, d1 = y[1] - mu;
+    float sq = d0 * d0 + d1 * d1;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) sq += __shfl_xor(sq, d, 64);
+    const float inv = 1.0f / sqrtf(sq * (1.0f / 128.0f) + a.eps);
+    const __bf16* g = reinterpret_cast<const __bf16*>(a.ln_gamma);
+    const __bf16* b = reinterpret_cast<const __bf16*>(a.ln_beta);
+    y[0] = d0 * inv * (float)g[lane] + (float)b[lane];
+    y[1] = d1 * inv * (float)g[64 + lane] + (float)b[64 + lane];
+    rope_hadamard128(y, lane, p, a);
+    a.k_index[(size_t)t * 128 + lane] = bf16_bits(y[0]);
+    a.k_index[(size_t)t * 128 + 64 + lane] = bf16_bits(y[1]);
+  } else if (wave == 1) {
+    for (int h = lane; h < a.n_heads; h += 64) {
+      float w = 0.0f;
+      for (int s = 0; s < a.split_kw; ++s) w += a.part_kw[((size_t)s * a.tokens + t) * nkw + 128 + h];
+      a.weights[(size_t)t * a.n_heads + h] = w * a.w_scale;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_indexer_finish(const IndexerFinishArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(indexer_finish_kernel, dim3(a.tokens), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_prolog_gemm(const PrologGemmArgs& a, int mode, hipStream_t stream) {
   const int feat = 32 * prolog_feat_blocks(mode);

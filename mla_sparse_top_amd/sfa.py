@@ -147,15 +147,36 @@ class SfaPrologDims(ctypes.Structure):
 
 _lib.sfa_mla_prolog_workspace_size.argtypes = [ctypes.POINTER(SfaPrologDims), ctypes.POINTER(ctypes.c_size_t)]
 _lib.sfa_mla_prolog_workspace_size.restype = ctypes.c_int
-_lib.sfa_mla_prolog.argtypes = [ctypes.POINTER(SfaPrologDims)] + [_vp] * 15 + [ctypes.c_size_t, _vp]
+_lib.sfa_mla_prolog.argtypes = [ctypes.POINTER(SfaPrologDims)] + [_vp] * 16 + [ctypes.c_size_t, _vp]
 _lib.sfa_mla_prolog.restype = ctypes.c_int
+
+
+class SfaIndexerPrologDims(ctypes.Structure):
+    _fields_ = [
+        ("tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("q_lora_rank", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rope_positions", ctypes.c_int32),
+        ("rotate", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+    ]
+
+
+_lib.sfa_indexer_prolog_workspace_size.argtypes = [ctypes.POINTER(SfaIndexerPrologDims),
+                                                   ctypes.POINTER(ctypes.c_size_t)]
+_lib.sfa_indexer_prolog_workspace_size.restype = ctypes.c_int
+_lib.sfa_indexer_prolog.argtypes = [ctypes.POINTER(SfaIndexerPrologDims)] + [_vp] * 14 + [ctypes.c_size_t, _vp]
+_lib.sfa_indexer_prolog.restype = ctypes.c_int
 
 
 
 EXPORTED_SYMBOLS = ("sfa_workspace_size", "sfa_num_splits", "sfa_decode", "sfa_prefill", "sfa_resolve_rows",
                     "sfa_status_string", "sfa_indexer_scores", "sfa_topk_select", "sfa_cache_write",
                     "sfa_window_workspace_size", "sfa_window_decode", "sfa_compress", "sfa_decode_noalloc",
-                    "sfa_mla_prolog_workspace_size", "sfa_mla_prolog")
+                    "sfa_mla_prolog_workspace_size", "sfa_mla_prolog", "sfa_indexer_prolog_workspace_size",
+                    "sfa_indexer_prolog")
 
 
 class SfaError(RuntimeError):
@@ -834,7 +855,7 @@ def prolog_workspace_size(dims: SfaPrologDims) -> int:
 
 
 def _marshal_prolog(x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, positions, rope_cos, rope_sin, eps, *,
-                    out=None, workspace=None, stream=None):
+                    out=None, workspace=None, stream=None, cq_out=None):
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on a GPU device")
@@ -866,22 +887,24 @@ def _marshal_prolog(x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, posit
         workspace = get_workspace(dev, need, stream)
     if workspace is not None:
         _check(workspace, "workspace", (torch.uint8,), None, dev)
+    if cq_out is not None:
+        _check(cq_out, "cq_out", b16, (t, q), dev)
     args = (ctypes.byref(dims), _ptr(x), _ptr(w_dq), _ptr(gamma_cq), _ptr(w_uq_qr), _ptr(w_uk), _ptr(w_dkv_kr),
-            _ptr(gamma_ckv), _ptr(positions), _ptr(rope_cos), _ptr(rope_sin), *[_ptr(o) for o in out],
+            _ptr(gamma_ckv), _ptr(positions), _ptr(rope_cos), _ptr(rope_sin), *[_ptr(o) for o in out], _ptr(cq_out),
             _ptr(workspace) if need else None, ctypes.c_size_t(workspace.numel() if (need and workspace is not None)
                                                             else 0),
             ctypes.c_void_p(stream.cuda_stream))
     keep = (dims, x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, positions, rope_cos, rope_sin, out,
-            workspace, stream)
+            cq_out, workspace, stream)
     return args, out, keep
 
 
 def mla_prolog(x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, positions, rope_cos, rope_sin, eps, *,
-               out=None, workspace=None, stream=None):
+               out=None, workspace=None, stream=None, cq_out=None):
     """sfa_mla_prolog: returns (q_nope (T*n_q, 512), q_rope (T*n_q, 64), kv_nope (T, 512),
-    kv_rope (T, 64)), all bf16."""
+    kv_rope (T, 64)), all bf16; cq_out (T, Q) bf16, when given, receives cq rounded to bf16."""
     args, out, _keep = _marshal_prolog(x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, positions, rope_cos,
-                                       rope_sin, eps, out=out, workspace=workspace, stream=stream)
+                                       rope_sin, eps, out=out, workspace=workspace, stream=stream, cq_out=cq_out)
     st = _lib.sfa_mla_prolog(*args)
     if st != 0:
         raise SfaError(st, "sfa_mla_prolog")
@@ -914,11 +937,109 @@ def _prolog_args(inp, d):
             d["rope_cos"], d["rope_sin"], inp.eps)
 
 
-def run_prolog(inp, d=None, *, out=None):
+def run_prolog(inp, d=None, *, out=None, cq_out=None):
     """sfa_mla_prolog on an uploaded PrologInputs instance."""
     d = d if d is not None else prolog_to_device(inp)
-    return mla_prolog(*_prolog_args(inp, d), out=out)
+    return mla_prolog(*_prolog_args(inp, d), out=out, cq_out=cq_out)
 
 
 def prepare_prolog_run(inp, d, *, out=None) -> PreparedCall:
     return prepare_mla_prolog(*_prolog_args(inp, d), out=out)
+
+
+# ---- indexer prolog ---------------------------------------------------------------------
+
+def indexer_prolog_workspace_size(dims: SfaIndexerPrologDims) -> int:
+    out = ctypes.c_size_t(0)
+    st = _lib.sfa_indexer_prolog_workspace_size(ctypes.byref(dims), ctypes.byref(out))
+    if st != 0:
+        raise SfaError(st, "sfa_indexer_prolog_workspace_size")
+    return out.value
+
+
+def _marshal_indexer_prolog(x, qr, w_idx_qb, w_idx_k, ln_gamma_k, ln_beta_k, w_idx_proj, positions, rope_cos,
+                            rope_sin, eps, *, rotate=True, out=None, workspace=None, stream=None):
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    t, hidden = x.shape
+    q = qr.shape[1]
+    d = w_idx_k.shape[0]
+    nh = w_idx_proj.shape[0]
+    n_pos = rope_cos.shape[0]
+    b16 = (torch.bfloat16,)
+    _check(x, "x", b16, (t, hidden), dev)
+    _check(qr, "qr", b16, (t, q), dev)
+    _check(w_idx_qb, "w_idx_qb", b16, (nh * d, q), dev)
+    _check(w_idx_k, "w_idx_k", b16, (d, hidden), dev)
+    _check(ln_gamma_k, "ln_gamma_k", b16, (d,), dev)
+    _check(ln_beta_k, "ln_beta_k", b16, (d,), dev)
+    _check(w_idx_proj, "w_idx_proj", b16, (nh, hidden), dev)
+    _check(positions, "positions", (torch.int32,), (t,), dev)
+    _check(rope_cos, "rope_cos", (torch.float32,), (n_pos, ROPE_DIM // 2), dev)
+    _check(rope_sin, "rope_sin", (torch.float32,), (n_pos, ROPE_DIM // 2), dev)
+    dims = SfaIndexerPrologDims(t, hidden, q, nh, d, n_pos, int(bool(rotate)), float(eps))
+    if out is None:
+        out = (torch.empty((t * nh, d), dtype=torch.bfloat16, device=dev),
+               torch.empty((t, d), dtype=torch.bfloat16, device=dev),
+               torch.empty((t, nh), dtype=torch.float32, device=dev))
+    _check(out[0], "q_index", b16, (t * nh, d), dev)
+    _check(out[1], "k_index", b16, (t, d), dev)
+    _check(out[2], "weights", (torch.float32,), (t, nh), dev)
+    need = indexer_prolog_workspace_size(dims)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    if workspace is None and need:
+        workspace = get_workspace(dev, need, stream)
+    if workspace is not None:
+        _check(workspace, "workspace", (torch.uint8,), None, dev)
+    args = (ctypes.byref(dims), _ptr(x), _ptr(qr), _ptr(w_idx_qb), _ptr(w_idx_k), _ptr(ln_gamma_k), _ptr(ln_beta_k),
+            _ptr(w_idx_proj), _ptr(positions), _ptr(rope_cos), _ptr(rope_sin), *[_ptr(o) for o in out],
+            _ptr(workspace) if need else None,
+            ctypes.c_size_t(workspace.numel() if (need and workspace is not None) else 0),
+            ctypes.c_void_p(stream.cuda_stream))
+    keep = (dims, x, qr, w_idx_qb, w_idx_k, ln_gamma_k, ln_beta_k, w_idx_proj, positions, rope_cos, rope_sin, out,
+            workspace, stream)
+    return args, out, keep
+
+
+def indexer_prolog(*tensors, **kw):
+    """sfa_indexer_prolog: returns (q_index (T*64, 128) bf16, k_index (T, 128) bf16,
+    weights (T, 64) fp32)."""
+    args, out, _keep = _marshal_indexer_prolog(*tensors, **kw)
+    st = _lib.sfa_indexer_prolog(*args)
+    if st != 0:
+        raise SfaError(st, "sfa_indexer_prolog")
+    return out
+
+
+def prepare_indexer_prolog(*tensors, **kw) -> PreparedCall:
+    args, out, keep = _marshal_indexer_prolog(*tensors, **kw)
+    return PreparedCall([(_lib.sfa_indexer_prolog, args, "sfa_indexer_prolog")], out, keep)
+
+
+def indexer_prolog_to_device(inp, device="cuda"):
+    """Upload a workloads.IndexerPrologInputs instance."""
+    import numpy as np
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    return {k: bf16(getattr(inp, k)) for k in ("x", "qr", "w_idx_qb", "w_idx_k", "ln_gamma_k", "ln_beta_k",
+                                                 "w_idx_proj")} | {
+        "positions": torch.from_numpy(inp.positions).to(device),
+        "rope_cos": torch.from_numpy(inp.rope_cos).to(device), "rope_sin": torch.from_numpy(inp.rope_sin).to(device)}
+
+
+def _indexer_prolog_args(inp, d):
+    return (d["x"], d["qr"], d["w_idx_qb"], d["w_idx_k"], d["ln_gamma_k"], d["ln_beta_k"], d["w_idx_proj"],
+            d["positions"], d["rope_cos"], d["rope_sin"], inp.eps)
+
+
+def run_indexer_prolog(inp, d=None, *, out=None):
+    d = d if d is not None else indexer_prolog_to_device(inp)
+    return indexer_prolog(*_indexer_prolog_args(inp, d), rotate=inp.rotate, out=out)
+
+
+def prepare_indexer_prolog_run(inp, d, *, out=None) -> PreparedCall:
+    return prepare_indexer_prolog(*_indexer_prolog_args(inp, d), rotate=inp.rotate, out=out)

@@ -374,8 +374,9 @@ def _prolog_dims(**kw):
 
 def _prolog_call(d, over=None, ws=0x7000000000, ws_bytes=None):
     vp = ctypes.c_void_p
-    names = ["x", "w_dq", "gcq", "w_uq", "w_uk", "w_dkv", "gckv", "pos", "cos", "sin", "qn", "qr", "kn", "kr"]
+    names = ["x", "w_dq", "gcq", "w_uq", "w_uk", "w_dkv", "gckv", "pos", "cos", "sin", "qn", "qr", "kn", "kr", "cq"]
     p = {n: 0x100000000 * (i + 1) for i, n in enumerate(names)}
+    p["cq"] = None
     p.update(over or {})
     if ws_bytes is None:
         ws_bytes = sfa.prolog_workspace_size(d)
@@ -418,3 +419,45 @@ def test_prolog_validation_errors():
     assert _prolog_call(d, {"kr": 0x100000000 * 13 + 64}) == -6        # kv_rope inside kv_nope
     # no tokens: nothing is read, NULL pointers are fine
     assert _prolog_call(_prolog_dims(tokens=0), {n: None for n in ("x", "qn")}, ws=None, ws_bytes=0) == 0
+    # the optional cq output: aligned, overlapping nothing
+    assert _prolog_call(d, {"cq": 0x100000000 * 15 + 8}) == -3
+    assert _prolog_call(d, {"cq": 0x100000000 * 1 + 64}) == -6      # inside x
+    assert _prolog_call(d, {"cq": 0x7000000000 + 4096}) == -6        # inside the workspace
+
+
+def _ip_dims(**kw):
+    base = dict(tokens=128, hidden=7168, q_lora_rank=1536, n_heads=64, head_dim=128, rope_positions=8192, rotate=1,
+                eps=1e-6)
+    base.update(kw)
+    return sfa.SfaIndexerPrologDims(**base)
+
+
+def _ip_call(d, over=None, ws=0x7000000000, ws_bytes=None):
+    vp = ctypes.c_void_p
+    names = ["x", "qr", "wqb", "wk", "g", "b", "wp", "pos", "cos", "sin", "q", "k", "w"]
+    p = {n: 0x100000000 * (i + 1) for i, n in enumerate(names)}
+    p.update(over or {})
+    if ws_bytes is None:
+        ws_bytes = sfa.indexer_prolog_workspace_size(d)
+    return sfa._lib.sfa_indexer_prolog(ctypes.byref(d), *[vp(p[n]) if p[n] is not None else None for n in names],
+                                       vp(ws) if ws else None, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_indexer_prolog_workspace_and_validation():
+    d = _ip_dims()
+    # index query partials: 128 tiles x 2 k splits; key and weight partials: 3 tiles x 28 splits
+    assert sfa.indexer_prolog_workspace_size(d) == 2 * 128 * 8192 * 4 + 28 * 128 * 192 * 4
+    assert sfa.indexer_prolog_workspace_size(_ip_dims(tokens=0)) == 0
+    for field, value in (("n_heads", 32), ("head_dim", 64), ("rotate", 2), ("hidden", 200), ("q_lora_rank", 100),
+                         ("eps", -1.0), ("rope_positions", 0), ("tokens", -1)):
+        out = ctypes.c_size_t(0)
+        assert sfa._lib.sfa_indexer_prolog_workspace_size(ctypes.byref(_ip_dims(**{field: value})),
+                                                          ctypes.byref(out)) == -2, field
+    assert _ip_call(d, {"qr": None}) == -1
+    assert _ip_call(d, {"w": None}) == -1
+    assert _ip_call(d, {"wk": 0x100000000 * 4 + 2}) == -3
+    assert _ip_call(d, ws=None) == -4
+    assert _ip_call(d, ws_bytes=sfa.indexer_prolog_workspace_size(d) - 1) == -4
+    assert _ip_call(d, {"q": 0x100000000 * 2 + 256}) == -6           # q_index inside qr
+    assert _ip_call(d, {"w": 0x7000000000 + 1024}) == -6             # weights inside the workspace
+    assert _ip_call(_ip_dims(tokens=0), {"x": None, "q": None}, ws=None, ws_bytes=0) == 0
