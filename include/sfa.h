@@ -94,9 +94,11 @@ typedef struct {
  * needs for `dims`. Host-only: no GPU is touched. *bytes_out may be 0, in which case the
  * workspace pointer may be NULL.
  *
- * The workspace holds per-partition partial results and two counters per token (partitions
- * arrived, partials published). It needs no initialisation: every call tags its counters with
- * a 48-bit generation of its own, so whatever the buffer held before counts as zero.
+ * The workspace holds per-partition partial results and fourteen 64-bit counter words per
+ * token (partitions arrived, partials published, and the flags of the two-partition merge, in
+ * which each partition merges half of the heads). It needs no initialisation: every call tags
+ * its counters with a 48-bit generation of its own, so whatever the buffer held before counts
+ * as zero.
  */
 int sfa_workspace_size(const sfa_dims* dims, int is_prefill, size_t* bytes_out);
 

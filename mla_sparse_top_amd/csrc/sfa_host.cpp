@@ -5,6 +5,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -79,8 +80,45 @@ WsLayout ws_layout(const sfa_dims* d, int splits) {
   w.part_o = 0;
   w.part_ml = align_up(items * kPartialBytes, kAlignWs);
   w.counters = w.part_ml + align_up(items * kPartialMlBytes, kAlignWs);
-  w.total = w.counters + align_up(2 * groups * sizeof(uint64_t), kAlignWs);
+  w.total = w.counters + align_up(kCounterWords * groups * sizeof(uint64_t), kAlignWs);
   return w;
+}
+
+// Compute units and wall-clock rate (kHz) of the device a stream belongs to, looked up once per
+// device (0 when the runtime cannot tell).
+struct DeviceInfo {
+  int cus;
+  int64_t clock_khz;
+};
+DeviceInfo device_info(hipStream_t stream) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int64_t> cache[kMaxDevices];  // cus << 40 | kHz, 0 = not looked up yet
+  int dev = 0;
+  if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return DeviceInfo{0, 0};
+  int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0, khz = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || cus <= 0 || khz <= 0)
+      return DeviceInfo{0, 0};
+    v = ((int64_t)cus << 40) | khz;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return DeviceInfo{(int)(v >> 40), v & ((int64_t{1} << 40) - 1)};
+}
+
+// The first arriver's wait for the other partition in the paired merge: long against the
+// spread of two equal partitions' finishing times (a few microseconds), short enough that a
+// partner that is not running costs little. SFA_PAIR_WAIT_NS overrides it (nanoseconds; 0 turns
+// the paired merge off), so that both outcomes of the wait can be exercised.
+constexpr int64_t kPairWaitNanos = 50000;
+int64_t pair_wait_nanos() {
+  const char* e = getenv("SFA_PAIR_WAIT_NS");
+  if (!e || !*e) return kPairWaitNanos;
+  char* end = nullptr;
+  const long long v = strtoll(e, &end, 10);
+  return (end && *end == 0 && v >= 0) ? (int64_t)v : kPairWaitNanos;
 }
 
 // [p, p + n) overlaps [q, q + m)
@@ -176,6 +214,16 @@ int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void*
   a.chunk = (d->topk + splits - 1) / splits;
   a.reverse = is_prefill ? 1 : 0;
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);  // log2(e)
+  if (splits == 2) {
+    // the paired merge needs both partitions of a token running at once: every workgroup of
+    // the grid (one per compute unit) resident
+    const DeviceInfo di = device_info(stream);
+    const int64_t ns = pair_wait_nanos();
+    if (di.cus > 0 && 2 * tokens <= di.cus && ns > 0) {
+      const int64_t ticks = di.clock_khz * ns / 1000000;
+      a.pair_wait_ticks = ticks > 0 ? ticks : 1;
+    }
+  }
   if (win) {
     a.window = win->window;
     a.mb_cmp = win->topk_cmp > 0 ? win->mb_cmp : 0;

@@ -114,6 +114,8 @@ __device__ __forceinline__ uint64_t tagged_add(uint64_t* p, uint64_t gen) {
 // Bound on the last arriver's wait for the other partitions' partials (each try sleeps ~128
 // clocks): far beyond the time a partial takes to be stored.
 constexpr int kSpinLimit = 1 << 24;
+// The first arriver's decision on the heads of one of its waves (paired merge).
+constexpr uint64_t kMergedByFirst = 1, kPublishedByFirst = 2;
 
 template <bool kInt8>
 struct Lds {
@@ -1092,46 +1094,143 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     return;
   }
 
-  // Partitions of one token: each takes an arrival ticket first. All but the last publish their
-  // partial (unnormalised O in register-image order [wave][dc][rq][lane] float4, and the running
-  // max and sum per head) and then count themselves ready; the last waits for that count and
-  // merges, with its own partial still in registers, so it never writes one. The wait is safe:
-  // every partition it waits for has already taken its ticket, so it is running and only has
-  // its stores left to do. A spin limit still bounds the wait.
+  // Partitions of one token: each takes an arrival ticket first, and whoever merges a head
+  // combines the partials in partition order, so the result does not depend on the arrival
+  // order or on who merges. Two protocols:
+  //
+  // Paired (two partitions, every workgroup of the grid resident at once): each wave's 32 heads
+  // are merged by one of the two, the first arriver taking waves 0 and 1 and the last arriver
+  // waves 2 and 3; each publishes only the waves the other merges (128 KB instead of 256), so
+  // the two halves of the merge run side by side. The first arriver waits a bounded time for
+  // the other's partial of its waves (the other may not have started); on a time-out it
+  // publishes its own partial of those waves too and leaves their merge to the last arriver,
+  // which waits for that decision (the first arriver is running, so the wait ends).
+  //
+  // Otherwise: all but the last publish their whole partial (unnormalised O in register-image
+  // order [wave][dc][rq][lane] float4, and the running max and sum per head) and count
+  // themselves ready; the last waits for that count and merges, with its own partial still in
+  // registers. That wait is safe too: every partition it waits for has taken its ticket. A spin
+  // limit still bounds every wait.
   //
   // Publication without an L2 write-back: the partials are written with agent-scope stores (the
   // sc1 form, which the L2 of this XCD writes through instead of holding dirty), so once this
-  // wave's stores are acknowledged (vmcnt 0) they are visible to every XCD, and the ready count
-  // that follows needs no release fence. (A release fence would write back this XCD's whole L2.)
-  // The last arriver takes an agent-scope acquire fence, which drops stale lines from its own L2.
+  // wave's stores are acknowledged (vmcnt 0) they are visible to every XCD, and the flag or
+  // count that follows needs no release fence. (A release fence would write back this XCD's
+  // whole L2.) A merging wave takes an agent-scope acquire fence, which drops stale lines from
+  // its own L2, before it reads a partial.
   const int S = a.n_splits;
-  uint64_t* arrive = a.counters + t;
-  uint64_t* ready = a.counters + a.n_tokens + t;
+  uint64_t* const cw = a.counters + (int64_t)t * kCounterWords;
+  uint64_t* arrive = cw + kCntArrive;
+  uint64_t* ready = cw + kCntReady;
   if (tid == 0) s_last = tagged_add(arrive, a.gen) == (uint64_t)(S - 1) ? 1 : 0;
   lds_barrier();
   floatx4* part = reinterpret_cast<floatx4*>(a.part_o);
   constexpr int kWaveImage = 16 * 4 * 64;  // float4s per wave
-  if (!s_last) {
-    if (wave_active) {
-      floatx4* po = part + (((int64_t)t * S + sp) * kWaves + wave) * kWaveImage + lane;
+  // this wave's partial: its O image and its heads' running max and sum
+  auto publish = [&]() __attribute__((always_inline)) {
+    floatx4* po = part + (((int64_t)t * S + sp) * kWaves + wave) * kWaveImage + lane;
 #pragma unroll
-      for (int dc = 0; dc < 16; ++dc) {
+    for (int dc = 0; dc < 16; ++dc) {
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const floatx4 v = agpr_quad(oacc[dc], rq);
-          // A VALU write of a 128-bit store's data registers needs a wait state after the store;
-          // the compiler does not see the store inside the asm, so the pad is part of it.
-          asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(po + (dc * 4 + rq) * 64), "v"(v)
-                       : "memory");
-        }
-      }
-      if (g == 0) {
-        uint64_t* ml = reinterpret_cast<uint64_t*>(a.part_ml) + ((int64_t)t * S + sp) * kMaxHeads + h;
-        const uint64_t bits = (uint64_t)__float_as_uint(m_run) | ((uint64_t)__float_as_uint(l_run) << 32);
-        __hip_atomic_store(ml, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int rq = 0; rq < 4; ++rq) {
+        const floatx4 v = agpr_quad(oacc[dc], rq);
+        // A VALU write of a 128-bit store's data registers needs a wait state after the store;
+        // the compiler does not see the store inside the asm, so the pad is part of it.
+        asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(po + (dc * 4 + rq) * 64), "v"(v)
+                     : "memory");
       }
     }
+    if (g == 0) {
+      uint64_t* ml = reinterpret_cast<uint64_t*>(a.part_ml) + ((int64_t)t * S + sp) * kMaxHeads + h;
+      const uint64_t bits = (uint64_t)__float_as_uint(m_run) | ((uint64_t)__float_as_uint(l_run) << 32);
+      __hip_atomic_store(ml, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
+  };
+  // Two partitions: O = w0 O0 + w1 O1 for this wave's heads, with partition so's partial read
+  // from the workspace in two batches of 32 loads per lane. The arithmetic has one shape
+  // whichever partition is this one (w0 * O0, then w1 * O1 added with one fused multiply-add).
+  auto merge_pair = [&](int so) __attribute__((always_inline)) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other partition's partial
+    const float2 other = reinterpret_cast<const float2*>(a.part_ml)[((int64_t)t * 2 + so) * kMaxHeads + h];
+    const float2 ml0 = sp == 0 ? make_float2(m_run, l_run) : other;
+    const float2 ml1 = sp == 0 ? other : make_float2(m_run, l_run);
+    const float mmax = fmaxf(ml0.x, ml1.x);
+    const float w0 = ml0.x != -INFINITY ? __builtin_amdgcn_exp2f(ml0.x - mmax) : 0.f;
+    const float w1 = ml1.x != -INFINITY ? __builtin_amdgcn_exp2f(ml1.x - mmax) : 0.f;
+    const float lsum = __builtin_fmaf(w1, ml1.y, w0 * ml0.y);
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    const floatx4* ps0 = part + (((int64_t)t * 2 + so) * kWaves + wave) * kWaveImage + lane;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const floatx4* ps = ps0 + 32 * hh * 64;
+      floatx4 buf[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) buf[i] = ps[i * 64];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int dc = 8 * hh + (i >> 2), rq = i & 3;
+        const floatx4 own = agpr_quad(oacc[dc], rq);
+        const floatx4 o0 = sp == 0 ? own : buf[i], o1 = sp == 0 ? buf[i] : own;
+        floatx4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w1, o1[e], w0 * o0[e]);
+        put_out(dc, rq, acc * inv);
+      }
+    }
+    flush_out();
+  };
+  // Lane 0 polls a tagged word until it reaches `want` (or, with a deadline, until the wall
+  // clock passes it); the wave gets lane 0's last reading.
+  auto poll = [&](uint64_t* p, uint64_t deadline) __attribute__((always_inline)) -> int {
+    int v = 0;
+    if (lane == 0) {
+      for (int spin = 0; spin < kSpinLimit; ++spin) {
+        v = (int)tagged_count(p, a.gen);
+        if (v != 0 || (deadline != 0 && wall_clock64() > deadline)) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    return __builtin_amdgcn_readlane(v, 0);
+  };
+
+  if (S == 2 && a.pair_wait_ticks > 0) {
+    if (!wave_active) return;
+    const bool last = s_last != 0;
+    const int so = 1 - sp;
+    const bool first_merges = wave < kWaves / 2;  // this wave's heads are the first arriver's
+    uint64_t* pub_mine = cw + kCntPublished + sp * kWaves + wave;
+    uint64_t* pub_other = cw + kCntPublished + so * kWaves + wave;
+    uint64_t* decision = cw + kCntDecision + wave;
+    if (last != first_merges) {  // this wave merges its heads
+      if (last) {
+        // the first arriver publishes these waves before anything else
+        poll(pub_other, 0);
+        merge_pair(so);
+        return;
+      }
+      const uint64_t deadline = wall_clock64() + (uint64_t)a.pair_wait_ticks;
+      if (poll(pub_other, deadline) == 0) {
+        // the other partition has not arrived: publish and let it merge these heads
+        publish();
+        if (lane == 0) __hip_atomic_store(decision, (a.gen << 16) | kPublishedByFirst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+      }
+      if (lane == 0) __hip_atomic_store(decision, (a.gen << 16) | kMergedByFirst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      merge_pair(so);
+      return;
+    }
+    publish();
+    if (lane == 0) __hip_atomic_store(pub_mine, (a.gen << 16) | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!last) return;
+    // the first arriver's waves 0 and 1 decide who merges these heads
+    if (poll(decision, 0) == (int)kMergedByFirst) return;
+    merge_pair(so);
+    return;
+  }
+
+  if (!s_last) {
+    if (wave_active) publish();
     lds_barrier();
     if (tid == 0) tagged_add(ready, a.gen);
     return;
@@ -1148,6 +1247,10 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   }
   lds_barrier();
   if (!wave_active) return;
+  if (S == 2) {
+    merge_pair(1 - sp);
+    return;
+  }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other partitions' partials
 
   // The last arriver combines all S partials in partition order (its own from its registers):
@@ -1169,32 +1272,6 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   const floatx4* pbase = part + ((int64_t)t * S * kWaves + wave) * kWaveImage + lane;
-  if (S == 2) {
-    // Two partitions: O = w0 O0 + w1 O1, summed in partition order whichever of the two arrived
-    // last. The other partial is read in two batches of 32 loads per lane.
-    // The arithmetic has one shape whichever partition is this one (w0 * O0, then w1 * O1 added
-    // with one fused multiply-add), so the result does not depend on the arrival order.
-    const int so = 1 - sp;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const floatx4* ps = pbase + (int64_t)so * kWaves * kWaveImage + 32 * hh * 64;
-      floatx4 buf[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) buf[i] = ps[i * 64];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int dc = 8 * hh + (i >> 2), rq = i & 3;
-        const floatx4 own = agpr_quad(oacc[dc], rq);
-        const floatx4 o0 = sp == 0 ? own : buf[i], o1 = sp == 0 ? buf[i] : own;
-        floatx4 acc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wv[1], o1[e], wv[0] * o0[e]);
-        put_out(dc, rq, acc * inv);
-      }
-    }
-    flush_out();
-    return;
-  }
 #pragma unroll
   for (int hh = 0; hh < 4; ++hh) {  // column blocks 4hh .. 4hh + 3
     floatx4 acc[16];

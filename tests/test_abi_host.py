@@ -75,7 +75,8 @@ def test_workspace_size_formula():
     items = tokens * 4
     part = items * 4 * 16 * 4 * 64 * 16   # 4 waves x 16 column blocks x 4 row quads x 64 lanes x float4
     ml = items * 128 * 2 * 4              # (max, sum) per head
-    cnt = 2 * tokens * 8                   # arrival and ready counters per token (64-bit, tagged)
+    cnt = 14 * tokens * 8                  # counter words per token (64-bit, tagged): arrival, ready,
+                                           # 8 published flags and 4 decisions of the two-partition merge
 
     def up(x):
         return (x + 255) // 256 * 256
