@@ -15,9 +15,12 @@
 // How: one workgroup per sequence, each thread owning a few channels, so every per-channel step
 // (refresh, online softmax over the slots, scaling) runs in registers with no communication;
 // the RMS needs one block reduction, RoPE pairs are adjacent lanes of the last wave (one xor
-// shuffle), and the Hadamard transform's butterflies are xor shuffles across one wave. The tokens of a sequence are taken in order. A slot written
-// earlier in the same call is read from the token's inputs rather than from the state, and only
-// each slot's last writer stores it, so no address is both written and read in one call.
+// shuffle), and the Hadamard transform's butterflies are xor shuffles across one wave. The
+// tokens of a sequence are taken in order. A slot written earlier in the same call is read from
+// the token's inputs rather than from the state, and only each slot's last writer stores it, so
+// no address is both written and read in one call; every load can therefore be issued early, and
+// the loads of a chunk of tokens, and of a batch of slots, go out together. The work is a few
+// dependent memory round trips per sequence, not bandwidth: more workgroups would not shorten it.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -57,133 +60,159 @@ __global__ void __launch_bounds__(kC == 576 ? 192 : 64) compress_kernel(const Co
   const int64_t s_hi = min((int64_t)a.s1, (int64_t)a.rope_positions - p0);
   const int64_t C = kC;
 
-  for (int64_t s = s_lo; s < s_hi; ++s) {
-    const int p = (int)(p0 + s);
-    const int64_t t = (int64_t)b * a.s1 + s;
-    const int slot = p % a.ratio;
-    float kv_t[kPer], sc_t[kPer];
+  // Tokens are taken in chunks: the inputs of a chunk are loaded together, and the slots a
+  // pooling reads are loaded kSlotBatch at a time, so that a call waits on few memory round
+  // trips (each load's address depends on nothing loaded).
+  constexpr int kTokChunk = 4;
+  constexpr int kSlotBatch = 8;
+  for (int64_t s0 = s_lo; s0 < s_hi; s0 += kTokChunk) {
+    float kv_c[kTokChunk][kPer], sc_c[kTokChunk][kPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int c = tid + k * kT;
-      kv_t[k] = a.kv[t * C + c];
-      sc_t[k] = a.score[t * C + c] + a.ape[(int64_t)slot * C + c];
-    }
-    if (s + a.ratio >= s_hi) {  // no later token of this call refreshes this slot
-      const int64_t o = ((int64_t)b * a.ratio + slot) * C;
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        a.kv_state[o + tid + k * kT] = kv_t[k];
-        a.score_state[o + tid + k * kT] = sc_t[k];
-      }
-    }
-    if ((p + 1) % a.ratio != 0) continue;  // uniform over the workgroup
-
-    // ---- pool: online softmax over the slots, per channel
-    float m[kPer], l[kPer], acc[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      m[k] = sc_t[k];
-      l[k] = 1.0f;
-      acc[k] = kv_t[k];
-    }
-    for (int r = 0; r < a.ratio; ++r) {
-      if (r == slot) continue;
-      const int64_t back = (slot - r + a.ratio) % a.ratio;  // slot r was last refreshed at p - back
-      const int64_t sp = s - back;
-      float kr[kPer], sr[kPer];
-      if (sp >= s_lo) {  // by a token of this call: take its inputs
-        const int64_t tp = (int64_t)b * a.s1 + sp;
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-          const int c = tid + k * kT;
-          kr[k] = a.kv[tp * C + c];
-          sr[k] = a.score[tp * C + c] + a.ape[(int64_t)r * C + c];
-        }
-      } else {           // before this call: the stored state, which this call has not written
-        const int64_t o = ((int64_t)b * a.ratio + r) * C;
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-          kr[k] = a.kv_state[o + tid + k * kT];
-          sr[k] = a.score_state[o + tid + k * kT];
-        }
-      }
+    for (int j = 0; j < kTokChunk; ++j) {
+      if (s0 + j >= s_hi) break;
+      const int64_t t = (int64_t)b * a.s1 + s0 + j;
+      const int slot = (int)((p0 + s0 + j) % a.ratio);
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        const float mn = fmaxf(m[k], sr[k]);
-        const float e_old = expf(m[k] - mn), e_new = expf(sr[k] - mn);
-        l[k] = l[k] * e_old + e_new;
-        acc[k] = acc[k] * e_old + e_new * kr[k];
-        m[k] = mn;
+        const int c = tid + k * kT;
+        kv_c[j][k] = a.kv[t * C + c];
+        sc_c[j][k] = a.score[t * C + c] + a.ape[(int64_t)slot * C + c];
       }
     }
-    float x[kPer], ss = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      x[k] = acc[k] / l[k];
-      ss += x[k] * x[k];
-    }
-
-    // ---- RMSNorm over the kC channels
+    for (int j = 0; j < kTokChunk; ++j) {
+      const int64_t s = s0 + j;
+      if (s >= s_hi) break;
+      const int p = (int)(p0 + s);
+      const int slot = p % a.ratio;
+      const float* kv_t = kv_c[j];
+      const float* sc_t = sc_c[j];
+      if (s + a.ratio >= s_hi) {  // no later token of this call refreshes this slot
+        const int64_t o = ((int64_t)b * a.ratio + slot) * C;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, 64);
-    float total = ss;
-    if (kWaves > 1) {
-      if (lane == 0) part[wave] = ss;
-      __syncthreads();
-      total = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) total += part[w];
-      __syncthreads();  // part is rewritten by the next entry
-    }
-    const float inv = 1.0f / sqrtf(total / (float)kC + a.eps);
-    float y[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) y[k] = x[k] * inv * a.gamma[tid + k * kT];
-
-    // ---- RoPE: channel kC - 64 + j is the last register of lane j of the last wave; pair j/2
-    // rotates by the angle of column j/2 of row p.
-    const float partner = __shfl_xor(y[kPer - 1], 1, 64);
-    if (wave == kWaves - 1) {
-      const int i = lane >> 1;
-      const float co = a.rope_cos[(int64_t)p * (kRope / 2) + i], si = a.rope_sin[(int64_t)p * (kRope / 2) + i];
-      y[kPer - 1] = (lane & 1) ? fmaf(partner, si, y[kPer - 1] * co) : fmaf(-partner, si, y[kPer - 1] * co);
-    }
-
-    // ---- Hadamard transform (128 channels): the stride-64 butterfly is within a lane (channels
-    // lane and lane + 64), the strides 32 .. 1 between lanes; then the 1/sqrt(128) scale.
-    if (kRotate) {
-      const float u0 = y[0] + y[1], u1 = y[0] - y[1];
-      y[0] = u0;
-      y[1] = u1;
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float q = __shfl_xor(y[k], d, 64);
-          y[k] = (lane & d) ? q - y[k] : y[k] + q;
+        for (int k = 0; k < kPer; ++k) {
+          a.kv_state[o + tid + k * kT] = kv_t[k];
+          a.score_state[o + tid + k * kT] = sc_t[k];
         }
       }
-#pragma unroll
-      for (int k = 0; k < 2; ++k) y[k] *= 0.08838834764831845f;  // 1/sqrt(128)
-    }
+      if ((p + 1) % a.ratio != 0) continue;  // uniform over the workgroup
 
-    // ---- store at the entry's row
-    const int64_t c_entry = (p + 1) / a.ratio - 1;
-    if (c_entry >= (int64_t)a.mb * 128) continue;
-    const int blk = a.block_table[(int64_t)b * a.mb + (c_entry >> 7)];
-    if (blk < 0) continue;
-    const int64_t row = (int64_t)blk * 128 + (c_entry & 127);
-    if (row >= a.num_rows) continue;
-    if (kC == 576) {
-      a.key_nope[row * kNope + tid] = bf16_rne(y[0]);
-      a.key_nope[row * kNope + tid + kT] = bf16_rne(y[1]);
-      if (wave < 2)
-        a.key_nope[row * kNope + tid + 2 * kT] = bf16_rne(y[kPer - 1]);
-      else
-        a.key_rope[row * kRope + lane] = bf16_rne(y[kPer - 1]);
-    } else {
+      // ---- pool: online softmax over the slots, per channel
+      float m[kPer], l[kPer], acc[kPer];
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) a.key_nope[row * kC + tid + k * kT] = bf16_rne(y[k]);
+      for (int k = 0; k < kPer; ++k) {
+        m[k] = sc_t[k];
+        l[k] = 1.0f;
+        acc[k] = kv_t[k];
+      }
+      // the other slots r = slot + 1 .. slot + ratio - 1 (mod ratio), kSlotBatch at a time
+      for (int r0 = 1; r0 < a.ratio; r0 += kSlotBatch) {
+        float kr[kSlotBatch][kPer], sr[kSlotBatch][kPer];
+#pragma unroll
+        for (int i = 0; i < kSlotBatch; ++i) {
+          if (r0 + i >= a.ratio) break;
+          const int r = (slot + r0 + i) % a.ratio;
+          const int64_t back = a.ratio - r0 - i;  // slot r was last refreshed at p - back
+          const int64_t sp = s - back;
+          if (sp >= s_lo) {  // by a token of this call: take its inputs
+            const int64_t tp = (int64_t)b * a.s1 + sp;
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+              const int c = tid + k * kT;
+              kr[i][k] = a.kv[tp * C + c];
+              sr[i][k] = a.score[tp * C + c] + a.ape[(int64_t)r * C + c];
+            }
+          } else {           // before this call: the stored state, which this call has not written
+            const int64_t o = ((int64_t)b * a.ratio + r) * C;
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+              kr[i][k] = a.kv_state[o + tid + k * kT];
+              sr[i][k] = a.score_state[o + tid + k * kT];
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kSlotBatch; ++i) {
+          if (r0 + i >= a.ratio) break;
+#pragma unroll
+          for (int k = 0; k < kPer; ++k) {
+            const float mn = fmaxf(m[k], sr[i][k]);
+            const float e_old = expf(m[k] - mn), e_new = expf(sr[i][k] - mn);
+            l[k] = l[k] * e_old + e_new;
+            acc[k] = acc[k] * e_old + e_new * kr[i][k];
+            m[k] = mn;
+          }
+        }
+      }
+      float x[kPer], ss = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        x[k] = acc[k] / l[k];
+        ss += x[k] * x[k];
+      }
+
+      // ---- RMSNorm over the kC channels
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, 64);
+      float total = ss;
+      if (kWaves > 1) {
+        if (lane == 0) part[wave] = ss;
+        __syncthreads();
+        total = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) total += part[w];
+        __syncthreads();  // part is rewritten by the next entry
+      }
+      const float inv = 1.0f / sqrtf(total / (float)kC + a.eps);
+      float y[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) y[k] = x[k] * inv * a.gamma[tid + k * kT];
+
+      // ---- RoPE: channel kC - 64 + j is the last register of lane j of the last wave; pair j/2
+      // rotates by the angle of column j/2 of row p.
+      const float partner = __shfl_xor(y[kPer - 1], 1, 64);
+      if (wave == kWaves - 1) {
+        const int i = lane >> 1;
+        const float co = a.rope_cos[(int64_t)p * (kRope / 2) + i], si = a.rope_sin[(int64_t)p * (kRope / 2) + i];
+        y[kPer - 1] = (lane & 1) ? fmaf(partner, si, y[kPer - 1] * co) : fmaf(-partner, si, y[kPer - 1] * co);
+      }
+
+      // ---- Hadamard transform (128 channels): the stride-64 butterfly is within a lane (channels
+      // lane and lane + 64), the strides 32 .. 1 between lanes; then the 1/sqrt(128) scale.
+      if (kRotate) {
+        const float u0 = y[0] + y[1], u1 = y[0] - y[1];
+        y[0] = u0;
+        y[1] = u1;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float q = __shfl_xor(y[k], d, 64);
+            y[k] = (lane & d) ? q - y[k] : y[k] + q;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) y[k] *= 0.08838834764831845f;  // 1/sqrt(128)
+      }
+
+      // ---- store at the entry's row
+      const int64_t c_entry = (p + 1) / a.ratio - 1;
+      if (c_entry >= (int64_t)a.mb * 128) continue;
+      const int blk = a.block_table[(int64_t)b * a.mb + (c_entry >> 7)];
+      if (blk < 0) continue;
+      const int64_t row = (int64_t)blk * 128 + (c_entry & 127);
+      if (row >= a.num_rows) continue;
+      if (kC == 576) {
+        a.key_nope[row * kNope + tid] = bf16_rne(y[0]);
+        a.key_nope[row * kNope + tid + kT] = bf16_rne(y[1]);
+        if (wave < 2)
+          a.key_nope[row * kNope + tid + 2 * kT] = bf16_rne(y[kPer - 1]);
+        else
+          a.key_rope[row * kRope + lane] = bf16_rne(y[kPer - 1]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) a.key_nope[row * kC + tid + k * kT] = bf16_rne(y[k]);
+      }
     }
   }
 }
