@@ -163,6 +163,57 @@ def test_compressed_entry_feeds_scfa(sfa_lib):
     assert rep["fails"] == 0, rep
 
 
+def test_compressed_entry_feeds_int8_scfa(sfa_lib):
+    """An INT8 compressed pool: the compressor writes its newest entry into a bf16 staging pool
+    (same block table), sfa_cache_write quantises that row into the INT8 pool at the entry's
+    position, and INT8 SCFA reads it. The staged rows match the compressor oracle; the codes and
+    scales equal the cache oracle's quantisation of the staged bf16 rows (bit for bit, the rule
+    decided in the same fp32 on both sides); the attention over the pool the GPU wrote matches the
+    window oracle."""
+    import torch
+
+    import oracle.cache_oracle as CO
+    import oracle.window_oracle as WO
+
+    ratio = 4
+    win = W.window_generate(batch=2, s1=2, n_q=32, ori_lens=[512, 300], window=64, ratio=ratio, cmp_mode="sparse",
+                            topk_cmp=24, kv_dtype="int8", seed=13)
+    for b in range(win.batch):
+        win.cmp_indices[b * win.s1 + 1, 0] = int(win.cmp_len[b]) - 1   # closed by position ori_len - 1
+    cmp = W.compress_generate(batch=2, s1=2, ratio=ratio, start_pos=[int(v) - 2 for v in win.ori_len],
+                              rope_positions=1024, max_blocks=win.block_table_cmp.shape[1], seed=14)
+    rows = win.key_rope.shape[0]
+    cmp.block_table_cmp = win.block_table_cmp
+    cmp.key_nope = np.zeros((rows, 512), dtype=np.uint16)      # the bf16 staging pool
+    cmp.key_rope = np.zeros((rows, 64), dtype=np.uint16)
+    dw = sfa_lib.window_to_device(win)
+    dc = sfa_lib.compress_to_device(cmp)
+    sfa_lib.run_compress(cmp, dc)
+    torch.cuda.synchronize()
+    staged = _host(dc)
+    assert _assert_matches(cmp, staged, pool=(cmp.key_nope, cmp.key_rope)) == 2
+    # the two new entries (one per sequence) go into the INT8 pool at their positions
+    entries = [int(win.cmp_len[b]) - 1 for b in range(win.batch)]
+    srow = [int(win.block_table_cmp[b, c // 128]) * 128 + c % 128 for b, c in enumerate(entries)]
+    new_nope = dc["key_nope"][srow].contiguous()
+    new_rope = dc["key_rope"][srow].contiguous()
+    pos = torch.tensor(entries, dtype=torch.int32, device="cuda")
+    sfa_lib.cache_write(new_nope, new_rope, pos, dw["block_table_cmp"], dw["key_nope"], dw["key_rope"],
+                        dw["k_nope_scales"], batch=win.batch, s1=1)
+    out = sfa_lib.run_window(win, dw)
+    torch.cuda.synchronize()
+    codes = dw["key_nope"].cpu().numpy()
+    scales = dw["k_nope_scales"].cpu().numpy()
+    want_c, want_s = CO.quantize_groups(staged[2][srow])
+    np.testing.assert_array_equal(codes[srow], want_c)
+    np.testing.assert_array_equal(scales[srow].view(np.uint32), want_s.view(np.uint32))
+    win.key_nope, win.k_nope_scales = codes, scales
+    win.key_rope = dw["key_rope"].cpu().view(torch.int16).numpy().view(np.uint16)
+    ref = WO.window_attention(win)
+    rep = O.allclose_report(out.float().cpu().numpy().astype(np.float64).reshape(ref.shape), ref)
+    assert rep["fails"] == 0, rep
+
+
 # ---- 128-channel rows (index keys) and the rotate = true branch (Hadamard transform) ----
 
 @pytest.mark.parametrize("seed", [0, 1])

@@ -350,6 +350,24 @@ def test_prefill_4096_sampled(seed):
     _check(inp, got, tokens=toks, label=f"prefill4096_sampled_seed{seed}")
 
 
+@pytest.mark.slow
+def test_prefill_4096_every_token():
+    """Prefill S1=4096 (seed 0) checked on every token, in chunks of 512 tokens (the sampled
+    test above covers seeds 1 and 2 and the chunk edges): online-softmax faults that depend on
+    the token (its causal prefix, long -1 tails, the reverse work order) cannot hide between
+    samples. About half a minute of oracle time on the host."""
+    inp = W.prefill(seed=0)
+    got = _gpu(inp, prefill=True).view(inp.n_tokens, inp.n_q, 512)
+    worst = 0.0
+    for t0 in range(0, inp.n_tokens, 512):
+        toks = range(t0, min(inp.n_tokens, t0 + 512))
+        ref = O.sparse_mla_attention(inp, tokens=toks)
+        rep = O.allclose_report(_as_f64(got[t0:t0 + len(toks)]), ref, RTOL, ATOL)
+        assert rep["fails"] == 0, (t0, rep)
+        worst = max(worst, rep["worst_ratio"])
+    print(f"[parity] prefill4096 every token: worst={worst:.3f}", flush=True)
+
+
 @pytest.mark.parametrize("name", W.PAGE_CASES)
 def test_page_cases(name):
     inp = W.page_case(name)
