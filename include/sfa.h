@@ -94,11 +94,13 @@ typedef struct {
  * needs for `dims`. Host-only: no GPU is touched. *bytes_out may be 0, in which case the
  * workspace pointer may be NULL.
  *
- * The workspace holds per-partition partial results and fourteen 64-bit counter words per
- * token (partitions arrived, partials published, and the flags of the two-partition merge, in
- * which each partition merges half of the heads). It needs no initialisation: every call tags
+ * The workspace holds per-partition partial results and 82 64-bit counter words per token
+ * (partitions arrived, partials published, and the flags of the spread merge, in which each of
+ * 2 to 16 partitions merges a share of the output). It needs no initialisation: every call tags
  * its counters with a 48-bit generation of its own, so whatever the buffer held before counts
- * as zero.
+ * as zero. The environment variable SFA_MERGE_WAIT_NS bounds, in nanoseconds, how long an early
+ * partition waits for the others' partials before leaving its share to the last (default
+ * 50,000; 0 turns the spread merge off): the result is the same either way.
  */
 int sfa_workspace_size(const sfa_dims* dims, int is_prefill, size_t* bytes_out);
 

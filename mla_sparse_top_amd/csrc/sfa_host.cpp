@@ -21,7 +21,7 @@ constexpr size_t kAlignWs = 256;
 // kernel runs one workgroup per CU (its register and LDS footprint allow no more).
 constexpr int kTargetWorkgroups = 256;
 constexpr int kMaxAutoSplits = 8;
-constexpr int kMinSlots = 512;  // top-k slots per partition at least, in the automatic choice
+constexpr int kMinSlots = 256;  // top-k slots per partition at least, in the automatic choice
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -52,11 +52,11 @@ int pick_splits(const sfa_dims* d, int is_prefill) {
     s = 1;
   } else {
     // Enough (token, partition) work items to give every CU one, but at least kMinSlots slots
-    // per partition and at most kMaxAutoSplits partitions: every partition but one writes a
-    // 256 KB partial that the last arriver reads back, which only pays for itself against
-    // about 512 gathered rows (measured: a 128-slot window runs in 20.6 us as one partition
-    // and 31.4 us as two; 32 single-token sequences with top-k 2048 in 68.8 us with 4
-    // partitions and 79.0 us with 8).
+    // per partition and at most kMaxAutoSplits partitions: the merge moves a 256 KB partial per
+    // partition through memory, which only pays for itself against a few hundred gathered rows
+    // (measured with the spread merge: a 128-slot window runs in 20.6 us as one partition and
+    // 32.2 us as two; 32 single-token sequences with top-k 2048 in 64.6 us with 4 partitions,
+    // 60.9 us with 8).
     const int64_t items = tokens;
     const int64_t want = items > 0 ? (kTargetWorkgroups + items - 1) / items : 1;
     s = (int)(want < kMaxAutoSplits ? want : kMaxAutoSplits);
@@ -108,17 +108,17 @@ DeviceInfo device_info(hipStream_t stream) {
   return DeviceInfo{(int)(v >> 40), v & ((int64_t{1} << 40) - 1)};
 }
 
-// The first arriver's wait for the other partition in the paired merge: long against the
-// spread of two equal partitions' finishing times (a few microseconds), short enough that a
-// partner that is not running costs little. SFA_PAIR_WAIT_NS overrides it (nanoseconds; 0 turns
-// the paired merge off), so that both outcomes of the wait can be exercised.
-constexpr int64_t kPairWaitNanos = 50000;
-int64_t pair_wait_nanos() {
-  const char* e = getenv("SFA_PAIR_WAIT_NS");
-  if (!e || !*e) return kPairWaitNanos;
+// An early arrival's wait for the other partitions in the spread merge: long against the spread
+// of equal partitions' finishing times (a few microseconds), short enough that a partner that is
+// not running costs little. SFA_MERGE_WAIT_NS overrides it (nanoseconds; 0 turns the spread
+// merge off), so that every outcome of the wait can be exercised.
+constexpr int64_t kMergeWaitNanos = 50000;
+int64_t merge_wait_nanos() {
+  const char* e = getenv("SFA_MERGE_WAIT_NS");
+  if (!e || !*e) return kMergeWaitNanos;
   char* end = nullptr;
   const long long v = strtoll(e, &end, 10);
-  return (end && *end == 0 && v >= 0) ? (int64_t)v : kPairWaitNanos;
+  return (end && *end == 0 && v >= 0) ? (int64_t)v : kMergeWaitNanos;
 }
 
 // [p, p + n) overlaps [q, q + m)
@@ -214,14 +214,14 @@ int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void*
   a.chunk = (d->topk + splits - 1) / splits;
   a.reverse = is_prefill ? 1 : 0;
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);  // log2(e)
-  if (splits == 2) {
-    // the paired merge needs both partitions of a token running at once: every workgroup of
-    // the grid (one per compute unit) resident
+  if (splits >= 2 && splits <= kMaxSpread) {
+    // the spread merge needs the partitions of a token running at once: every workgroup of the
+    // grid (one per compute unit) resident
     const DeviceInfo di = device_info(stream);
-    const int64_t ns = pair_wait_nanos();
-    if (di.cus > 0 && 2 * tokens <= di.cus && ns > 0) {
+    const int64_t ns = merge_wait_nanos();
+    if (di.cus > 0 && splits * tokens <= di.cus && ns > 0) {
       const int64_t ticks = di.clock_khz * ns / 1000000;
-      a.pair_wait_ticks = ticks > 0 ? ticks : 1;
+      a.merge_wait_ticks = ticks > 0 ? ticks : 1;
     }
   }
   if (win) {

@@ -23,11 +23,14 @@ constexpr int kMaxTopk = kMaxSlots * kMaxSplits;
 // 4 waves x 16 blocks of 32 columns x 4 row quads x 64 lanes x float4 (256 KB)
 constexpr size_t kPartialBytes = (size_t)kWaves * 16 * 4 * 64 * 16;
 constexpr size_t kPartialMlBytes = kMaxHeads * 2 * sizeof(float);
+// The spread merge: up to this many partitions share a token's merge, one output unit (a wave's
+// heads x 128 columns) each at most.
+constexpr int kMaxSpread = kWaves * 4;
 // 64-bit counter words per token in the workspace, each tagged with the call's generation:
-// partitions arrived, partials counted ready, the paired merge's published flags (2 partitions
-// x 4 waves) and the first arriver's decision for each of its waves
-constexpr int kCntArrive = 0, kCntReady = 1, kCntPublished = 2, kCntDecision = 2 + 2 * kWaves;
-constexpr int kCounterWords = kCntDecision + kWaves;
+// partitions arrived, partials counted ready, the spread merge's published flags (partition x
+// wave) and the merging partition's decision for each output unit (wave x 128-column block)
+constexpr int kCntArrive = 0, kCntReady = 1, kCntPublished = 2, kCntDecision = 2 + kMaxSpread * kWaves;
+constexpr int kCounterWords = kCntDecision + kWaves * 4;
 
 struct KernelArgs {
   const uint16_t* q_nope;     // bf16 bits (T*n_q, 512)
@@ -43,10 +46,10 @@ struct KernelArgs {
   float* part_ml;             // (T, splits, 128, 2): running max and sum per head
   uint64_t* counters;         // (T, kCounterWords), tagged with the call's generation
   uint64_t gen;               // this call's generation: 48 bits, never 0
-  // Two partitions whose workgroups are all resident: the paired merge, with the first
-  // arriver's wait for the other partition bounded by this many wall-clock ticks; 0: the last
-  // arriver merges everything.
-  int64_t pair_wait_ticks;
+  // 2 to 16 partitions whose workgroups are all resident: the spread merge, with an early
+  // arrival's wait for the others bounded by this many wall-clock ticks; 0: the last arrival
+  // merges everything.
+  int64_t merge_wait_ticks;
   int64_t num_rows;
   int32_t n_tokens, s1, n_q, topk, mb, n_splits, chunk, reverse;
   float scale_log2;           // softmax_scale * log2(e)

@@ -38,10 +38,11 @@
 //   * Software pipeline, one barrier per tile interval: the 36 S^T steps of tile i+1 alternate
 //     with the P.V steps of tile i's first 16 keys; then tile i's last 16 keys' P.V steps run
 //     while the VALU computes tile i+1's softmax, so MFMA and VALU work overlap in every phase.
-//   * Partitions of one token merge in the same kernel: each takes an arrival ticket; all but
-//     the last write their unnormalised O, running max and running sum and count themselves
-//     ready. The last to arrive combines all of them in partition order (its own from
-//     registers), so the result does not depend on arrival order:
+//   * Partitions of one token merge in the same kernel: each takes an arrival ticket and
+//     publishes the unnormalised O, running max and running sum of the heads it does not merge;
+//     with 2 to 4 resident partitions the heads of each wave are merged by one of them (the
+//     merge spread over the token's workgroups), otherwise by the last to arrive. Whoever merges
+//     combines all partitions in partition order, so the result does not depend on arrival order:
 //     O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j. This is the prefill update rule applied
 //     across partitions.
 //   * Work items are mapped so that consecutive logical ids land on the same XCD and share its
@@ -114,7 +115,7 @@ __device__ __forceinline__ uint64_t tagged_add(uint64_t* p, uint64_t gen) {
 // Bound on the last arriver's wait for the other partitions' partials (each try sleeps ~128
 // clocks): far beyond the time a partial takes to be stored.
 constexpr int kSpinLimit = 1 << 24;
-// The first arriver's decision on the heads of one of its waves (paired merge).
+// A merging partition's decision on the heads of one of its waves (spread merge).
 constexpr uint64_t kMergedByFirst = 1, kPublishedByFirst = 2;
 
 template <bool kInt8>
@@ -399,7 +400,7 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   __shared__ __attribute__((aligned(1024))) char smem[L::kBytes];
   __shared__ __attribute__((aligned(16))) int32_t s_rows[kMaxSlots];
   __shared__ int32_t s_wcnt[kWaves];
-  __shared__ int32_t s_last;
+  __shared__ int32_t s_rank;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
@@ -1069,13 +1070,15 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   };
   // read back (the wave's own LDS accesses complete in order): lane L takes chunk L of row r.
   // The stores are non-temporal: the output is not read again here.
-  auto flush_out = [&]() __attribute__((always_inline)) {
+  // Only the 128-column blocks set in `blocks` are stored (lane L holds columns 8L .. 8L + 7).
+  auto flush_out = [&](int blocks) __attribute__((always_inline)) {
     uint16_t* orow = a.out + ((int64_t)t * a.n_q + h0) * kNope + 8 * lane;
+    const bool mine = (blocks >> (lane >> 4)) & 1;
 #pragma unroll 8
     for (int r = 0; r < kHeadsPerWave; ++r) {
       const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
           ob + r * kNopeRowBytes + ((lane ^ r) & 63) * 16);
-      if (h0 + r < a.n_q) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(orow + (int64_t)r * kNope));
+      if (h0 + r < a.n_q && mine) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(orow + (int64_t)r * kNope));
     }
   };
 
@@ -1089,22 +1092,24 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
         for (int rq = 0; rq < 4; ++rq)
           put_out(dc, rq, agpr_quad(oacc[dc], rq) * inv);
       }
-      flush_out();
+      flush_out(0xf);
     }
     return;
   }
 
-  // Partitions of one token: each takes an arrival ticket first, and whoever merges a head
-  // combines the partials in partition order, so the result does not depend on the arrival
-  // order or on who merges. Two protocols:
+  // Partitions of one token: each takes an arrival ticket (its arrival rank), and whoever merges
+  // a head combines all partitions' partials of it in partition order, with one arithmetic shape,
+  // so the result does not depend on the arrival order or on who merges. Two protocols:
   //
-  // Paired (two partitions, every workgroup of the grid resident at once): each wave's 32 heads
-  // are merged by one of the two, the first arriver taking waves 0 and 1 and the last arriver
-  // waves 2 and 3; each publishes only the waves the other merges (128 KB instead of 256), so
-  // the two halves of the merge run side by side. The first arriver waits a bounded time for
-  // the other's partial of its waves (the other may not have started); on a time-out it
-  // publishes its own partial of those waves too and leaves their merge to the last arriver,
-  // which waits for that decision (the first arriver is running, so the wait ends).
+  // Spread (up to 16 partitions, every workgroup of the grid resident at once): the output is cut
+  // into 16 units, (wave w, block hh of 128 columns), and unit (w, hh) is merged by the partition
+  // whose arrival rank is w mod S (S <= 4: whole waves) or (w + 4 hh) mod S (S > 4). A partition
+  // publishes each wave partial (64 KB) that another partition needs, so the merge is spread over
+  // all S workgroups instead of funnelled through the last. A merging wave waits for the other
+  // partitions' partials of its wave; partitions that arrived later may not be running, so an
+  // early arrival's wait is bounded, and on a time-out it publishes its own partial and leaves
+  // its units to the last arrival, which waits for that decision (every earlier arrival is
+  // running, so the last arrival's waits end).
   //
   // Otherwise: all but the last publish their whole partial (unnormalised O in register-image
   // order [wave][dc][rq][lane] float4, and the running max and sum per head) and count
@@ -1122,8 +1127,9 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   uint64_t* const cw = a.counters + (int64_t)t * kCounterWords;
   uint64_t* arrive = cw + kCntArrive;
   uint64_t* ready = cw + kCntReady;
-  if (tid == 0) s_last = tagged_add(arrive, a.gen) == (uint64_t)(S - 1) ? 1 : 0;
+  if (tid == 0) s_rank = (int)tagged_add(arrive, a.gen);
   lds_barrier();
+  const int rank = s_rank;
   floatx4* part = reinterpret_cast<floatx4*>(a.part_o);
   constexpr int kWaveImage = 16 * 4 * 64;  // float4s per wave
   // this wave's partial: its O image and its heads' running max and sum
@@ -1147,41 +1153,100 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
   };
-  // Two partitions: O = w0 O0 + w1 O1 for this wave's heads, with partition so's partial read
-  // from the workspace in two batches of 32 loads per lane. The arithmetic has one shape
-  // whichever partition is this one (w0 * O0, then w1 * O1 added with one fused multiply-add).
-  auto merge_pair = [&](int so) __attribute__((always_inline)) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other partition's partial
-    const float2 other = reinterpret_cast<const float2*>(a.part_ml)[((int64_t)t * 2 + so) * kMaxHeads + h];
-    const float2 ml0 = sp == 0 ? make_float2(m_run, l_run) : other;
-    const float2 ml1 = sp == 0 ? other : make_float2(m_run, l_run);
-    const float mmax = fmaxf(ml0.x, ml1.x);
-    const float w0 = ml0.x != -INFINITY ? __builtin_amdgcn_exp2f(ml0.x - mmax) : 0.f;
-    const float w1 = ml1.x != -INFINITY ? __builtin_amdgcn_exp2f(ml1.x - mmax) : 0.f;
-    const float lsum = __builtin_fmaf(w1, ml1.y, w0 * ml0.y);
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    const floatx4* ps0 = part + (((int64_t)t * 2 + so) * kWaves + wave) * kWaveImage + lane;
+  // O = sum_s w_s O_s / sum_s w_s l_s for this wave's heads, w_s = 2^(m_s - M), in partition
+  // order as fused multiply-adds from zero, with this partition's own partial from its registers
+  // and the others' from the workspace: the (m, l) of every partition first, then O four column
+  // blocks at a time, each batch of loads issued together.
+  auto merge = [&](int blocks) __attribute__((always_inline)) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other partitions' partials
+    const float2* mlp = reinterpret_cast<const float2*>(a.part_ml) + (int64_t)t * S * kMaxHeads + h;
+    if (S == 2) {
+      // the operations of the general case below for two partitions, with the other partition's
+      // partial read in two batches of 32 loads per lane (two column blocks each)
+      const float2 other = mlp[(1 - sp) * kMaxHeads];
+      const float2 ml0 = sp == 0 ? make_float2(m_run, l_run) : other;
+      const float2 ml1 = sp == 0 ? other : make_float2(m_run, l_run);
+      const float mmax = fmaxf(ml0.x, ml1.x);
+      const float w0 = ml0.x != -INFINITY ? __builtin_amdgcn_exp2f(ml0.x - mmax) : 0.f;
+      const float w1 = ml1.x != -INFINITY ? __builtin_amdgcn_exp2f(ml1.x - mmax) : 0.f;
+      const float lsum = __builtin_fmaf(w1, ml1.y, __builtin_fmaf(w0, ml0.y, 0.f));
+      const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+      const floatx4* ps = part + (((int64_t)t * 2 + (1 - sp)) * kWaves + wave) * kWaveImage + lane;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const floatx4* ps = ps0 + 32 * hh * 64;
-      floatx4 buf[32];
+      for (int hp = 0; hp < 2; ++hp) {
+        if (!((blocks >> (2 * hp)) & 3)) continue;
+        floatx4 buf[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) buf[i] = ps[i * 64];
+        for (int i = 0; i < 32; ++i) buf[i] = ps[(32 * hp + i) * 64];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int dc = 8 * hh + (i >> 2), rq = i & 3;
-        const floatx4 own = agpr_quad(oacc[dc], rq);
-        const floatx4 o0 = sp == 0 ? own : buf[i], o1 = sp == 0 ? buf[i] : own;
-        floatx4 acc;
+        for (int i = 0; i < 32; ++i) {
+          const int dc = 8 * hp + (i >> 2), rq = i & 3;
+          const floatx4 own = agpr_quad(oacc[dc], rq);
+          const floatx4 o0 = sp == 0 ? own : buf[i], o1 = sp == 0 ? buf[i] : own;
+          floatx4 acc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w1, o1[e], w0 * o0[e]);
-        put_out(dc, rq, acc * inv);
+          for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w1, o1[e], __builtin_fmaf(w0, o0[e], 0.f));
+          put_out(dc, rq, acc * inv);
+        }
       }
+      flush_out(blocks);
+      return;
     }
-    flush_out();
+    float2 mlv[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+      mlv[s] = s == sp ? make_float2(m_run, l_run) : s < S ? mlp[s * kMaxHeads] : make_float2(-INFINITY, 0.f);
+    float mmax = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) mmax = s < S ? fmaxf(mmax, mlv[s].x) : mmax;
+    float wv[kMaxSplits];
+    float lsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      wv[s] = (s < S && mlv[s].x != -INFINITY) ? __builtin_amdgcn_exp2f(mlv[s].x - mmax) : 0.f;
+      if (s < S) lsum = __builtin_fmaf(wv[s], mlv[s].y, lsum);
+    }
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    const floatx4* pbase = part + ((int64_t)t * S * kWaves + wave) * kWaveImage + lane;
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {  // column blocks 4hh .. 4hh + 3
+      if (!((blocks >> hh) & 1)) continue;
+      floatx4 acc[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma nounroll
+      for (int s = 0; s < S; ++s) {
+        float w = 0.f;
+#pragma unroll
+        for (int u = 0; u < kMaxSplits; ++u) w = (u == s) ? wv[u] : w;
+        // acc = fma(w, O_s, acc) in partition order, the same operations whether O_s comes from
+        // this partition's registers or from memory
+        if (s == sp) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int dc = 4 * hh + (i >> 2), rq = i & 3;
+            const floatx4 o = agpr_quad(oacc[dc], rq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] = __builtin_fmaf(w, o[e], acc[i][e]);
+          }
+        } else {
+          const floatx4* ps = pbase + (int64_t)s * kWaves * kWaveImage + 16 * hh * 64;
+          floatx4 buf[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) buf[i] = ps[i * 64];
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] = __builtin_fmaf(w, buf[i][e], acc[i][e]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) put_out(4 * hh + (i >> 2), i & 3, acc[i] * inv);
+    }
+    flush_out(blocks);
   };
-  // Lane 0 polls a tagged word until it reaches `want` (or, with a deadline, until the wall
-  // clock passes it); the wave gets lane 0's last reading.
+  // Lane 0 polls a tagged word until it is set (or, with a deadline, until the wall clock passes
+  // it); the wave gets lane 0's last reading.
   auto poll = [&](uint64_t* p, uint64_t deadline) __attribute__((always_inline)) -> int {
     int v = 0;
     if (lane == 0) {
@@ -1193,43 +1258,75 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     }
     return __builtin_amdgcn_readlane(v, 0);
   };
+  auto set_word = [&](uint64_t* p, uint64_t v) __attribute__((always_inline)) {
+    if (lane == 0) __hip_atomic_store(p, (a.gen << 16) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
 
-  if (S == 2 && a.pair_wait_ticks > 0) {
+  if (S <= kMaxSpread && a.merge_wait_ticks > 0) {
     if (!wave_active) return;
-    const bool last = s_last != 0;
-    const int so = 1 - sp;
-    const bool first_merges = wave < kWaves / 2;  // this wave's heads are the first arriver's
-    uint64_t* pub_mine = cw + kCntPublished + sp * kWaves + wave;
-    uint64_t* pub_other = cw + kCntPublished + so * kWaves + wave;
-    uint64_t* decision = cw + kCntDecision + wave;
-    if (last != first_merges) {  // this wave merges its heads
-      if (last) {
-        // the first arriver publishes these waves before anything else
-        poll(pub_other, 0);
-        merge_pair(so);
-        return;
-      }
-      const uint64_t deadline = wall_clock64() + (uint64_t)a.pair_wait_ticks;
-      if (poll(pub_other, deadline) == 0) {
-        // the other partition has not arrived: publish and let it merge these heads
-        publish();
-        if (lane == 0) __hip_atomic_store(decision, (a.gen << 16) | kPublishedByFirst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-      }
-      if (lane == 0) __hip_atomic_store(decision, (a.gen << 16) | kMergedByFirst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      merge_pair(so);
-      return;
+    const bool last = rank == S - 1;
+    int mine = 0, others = 0;  // this wave's column blocks merged here / by other partitions
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const int m = S <= kWaves ? wave % S : (wave + kWaves * hh) % S;
+      if (m == rank)
+        mine |= 1 << hh;
+      else
+        others |= 1 << hh;
     }
-    publish();
-    if (lane == 0) __hip_atomic_store(pub_mine, (a.gen << 16) | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!last) return;
-    // the first arriver's waves 0 and 1 decide who merges these heads
-    if (poll(decision, 0) == (int)kMergedByFirst) return;
-    merge_pair(so);
+    uint64_t* pub_mine = cw + kCntPublished + sp * kWaves + wave;
+    uint64_t* decision = cw + kCntDecision + wave * 4;  // + hh
+    // every other partition's partial of this wave (a bounded wait for an early arrival)
+    auto others_published = [&](uint64_t deadline) __attribute__((always_inline)) -> bool {
+      for (int q = 0; q < S; ++q)
+        if (q != sp && poll(cw + kCntPublished + q * kWaves + wave, deadline) == 0) return false;
+      return true;
+    };
+    if (others) {
+      publish();
+      set_word(pub_mine, 1);
+    }
+    int todo = 0;
+    if (mine) {
+      if (others_published(last ? 0 : wall_clock64() + (uint64_t)a.merge_wait_ticks)) {
+        todo = mine;
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh)
+          if ((mine >> hh) & 1) set_word(decision + hh, kMergedByFirst);
+      } else {
+        // a later partition has not published: leave these blocks to the last arrival
+        if (!others) {
+          publish();
+          set_word(pub_mine, 1);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh)
+          if ((mine >> hh) & 1) set_word(decision + hh, kPublishedByFirst);
+      }
+    }
+    if (last && others) {
+      // the mergers of the other blocks arrived earlier and are running: they decide, one word
+      // per block, all of a merger's blocks at once (so one reading per merger)
+      int left = 0, asked = 0;
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        if (!((others >> hh) & 1) || ((asked >> hh) & 1)) continue;
+        const int m = S <= kWaves ? wave % S : (wave + kWaves * hh) % S;
+        int same = 0;  // the blocks of this wave that merger m takes
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if ((S <= kWaves ? wave % S : (wave + kWaves * k) % S) == m) same |= 1 << k;
+        asked |= same;
+        if (poll(decision + hh, 0) == (int)kPublishedByFirst) left |= same;
+      }
+      if (left && !mine) others_published(0);
+      todo |= left;
+    }
+    if (todo) merge(todo);
     return;
   }
 
-  if (!s_last) {
+  if (rank != S - 1) {
     if (wave_active) publish();
     lds_barrier();
     if (tid == 0) tagged_add(ready, a.gen);
@@ -1240,73 +1337,10 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
       if (tagged_count(ready, a.gen) >= (uint64_t)(S - 1)) break;
       __builtin_amdgcn_s_sleep(2);
     }
-    // every partition of this token has taken its ticket and counted itself ready: nothing
-    // else touches the two words in this call, and cleared they cannot match a later call
-    __hip_atomic_store(arrive, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(ready, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   lds_barrier();
   if (!wave_active) return;
-  if (S == 2) {
-    merge_pair(1 - sp);
-    return;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other partitions' partials
-
-  // The last arriver combines all S partials in partition order (its own from its registers):
-  // the (m, l) of every partition for this lane's head first, then O four column blocks at a time.
-  const float2* mlp = reinterpret_cast<const float2*>(a.part_ml) + (int64_t)t * S * kMaxHeads + h;
-  float2 mlv[kMaxSplits];
-#pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s)
-    mlv[s] = s == sp ? make_float2(m_run, l_run) : s < S ? mlp[s * kMaxHeads] : make_float2(-INFINITY, 0.f);
-  float mmax = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) mmax = s < S ? fmaxf(mmax, mlv[s].x) : mmax;
-  float wv[kMaxSplits];
-  float lsum = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    wv[s] = (s < S && mlv[s].x != -INFINITY) ? __builtin_amdgcn_exp2f(mlv[s].x - mmax) : 0.f;
-    lsum += s < S ? wv[s] * mlv[s].y : 0.f;
-  }
-  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-  const floatx4* pbase = part + ((int64_t)t * S * kWaves + wave) * kWaveImage + lane;
-#pragma unroll
-  for (int hh = 0; hh < 4; ++hh) {  // column blocks 4hh .. 4hh + 3
-    floatx4 acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma nounroll
-    for (int s = 0; s < S; ++s) {
-      float w = 0.f;
-#pragma unroll
-      for (int u = 0; u < kMaxSplits; ++u) w = (u == s) ? wv[u] : w;
-      // acc = fma(w, O_s, acc) in partition order, the same operations whether O_s comes from
-      // this partition's registers or from memory
-      if (s == sp) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int dc = 4 * hh + (i >> 2), rq = i & 3;
-          const floatx4 o = agpr_quad(oacc[dc], rq);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][e] = __builtin_fmaf(w, o[e], acc[i][e]);
-        }
-      } else {
-        const floatx4* ps = pbase + (int64_t)s * kWaves * kWaveImage + 16 * hh * 64;
-        floatx4 buf[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) buf[i] = ps[i * 64];
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][e] = __builtin_fmaf(w, buf[i][e], acc[i][e]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) put_out(4 * hh + (i >> 2), i & 3, acc[i] * inv);
-  }
-  flush_out();
+  merge(0xf);
 }
 
 // rows_out[t, k] = physical row of slot k, or -1. The same predicate as the attention

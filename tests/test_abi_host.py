@@ -49,15 +49,18 @@ def _dims(**kw):
 def test_partition_choice():
     # one workgroup per (token, partition): 64 x 2 tokens need 2 partitions to fill 256 CUs
     assert sfa.num_splits(_dims()) == 2
-    # 32 single-token batches would want 8, but a partition needs >= 512 slots: 4
-    assert sfa.num_splits(_dims(batch=32, s1=1)) == 4
+    # 32 single-token batches want 8 (256 slots each)
+    assert sfa.num_splits(_dims(batch=32, s1=1)) == 8
+    # 64 single-token batches want 4; a partition needs >= 256 slots: top-k 512 gives 2
+    assert sfa.num_splits(_dims(batch=64, s1=1)) == 4
+    assert sfa.num_splits(_dims(batch=64, s1=1, topk=512)) == 2
     # 256 tokens or more already fill the CUs
     assert sfa.num_splits(_dims(batch=128, s1=2)) == 1
     # short lists are not partitioned (a window of 128 slots, 64 slots)
     assert sfa.num_splits(_dims(batch=64, s1=2, topk=128)) == 1
     assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=64)) == 1
     # at most 8 partitions unless topk needs more
-    assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=2048)) == 4
+    assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=2048)) == 8
     assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=8192)) == 8
     assert sfa.num_splits(_dims(batch=1, s1=1, n_q=16, topk=30000)) == 15
     # prefill never partitions while topk <= 2048
@@ -70,13 +73,13 @@ def test_partition_choice():
 
 
 def test_workspace_size_formula():
-    d = _dims(batch=32, s1=1)  # 4 partitions
+    d = _dims(batch=32, s1=1)  # 8 partitions
     tokens = 32
-    items = tokens * 4
+    items = tokens * 8
     part = items * 4 * 16 * 4 * 64 * 16   # 4 waves x 16 column blocks x 4 row quads x 64 lanes x float4
     ml = items * 128 * 2 * 4              # (max, sum) per head
-    cnt = 14 * tokens * 8                  # counter words per token (64-bit, tagged): arrival, ready,
-                                           # 8 published flags and 4 decisions of the two-partition merge
+    cnt = 82 * tokens * 8                  # counter words per token (64-bit, tagged): arrival, ready,
+                                           # 64 published flags and 16 decisions of the spread merge
 
     def up(x):
         return (x + 255) // 256 * 256

@@ -294,12 +294,14 @@ def test_run_to_run_determinism(splits):
         assert np.array_equal(outs[0], o)
 
 
-@pytest.mark.parametrize("n_q", [128, 64, 32])
-def test_paired_merge_both_outcomes(n_q, monkeypatch):
-    """Two partitions with every workgroup resident merge in pairs: the first arriver waits a
-    bounded time for the other's partial of its heads. Whichever way the wait ends (the default
-    wait, a 1 ns wait that nearly always times out, or the paired merge switched off), the bits
-    are the same, and they meet the bar."""
+@pytest.mark.parametrize("n_q,splits", [(128, 2), (64, 2), (32, 2), (128, 3), (128, 4), (96, 4), (128, 5),
+                                         (128, 8), (64, 8), (128, 16)])
+def test_spread_merge_every_outcome(n_q, splits, monkeypatch):
+    """2 to 16 partitions with every workgroup resident spread the merge over 16 output units (a
+    wave's heads x 128 columns), each merged by one partition chosen by arrival rank, and an early
+    arrival waits a bounded time for the others' partials. Whichever way the waits end (the default wait, a 1 ns wait that nearly
+    always times out, or the spread merge switched off), the bits are the same, and they meet
+    the bar."""
     inp = W.generate(batch=8, s1=2, n_q=n_q, act_seqs=[4000, 3000, 2500, 4000, 129, 4000, 3999, 2048],
                      topk=2048, seed=11, max_blocks_per_batch=32)
     sfa = _lib()
@@ -307,15 +309,15 @@ def test_paired_merge_both_outcomes(n_q, monkeypatch):
     outs = {}
     for wait in (None, "1", "0"):
         if wait is None:
-            monkeypatch.delenv("SFA_PAIR_WAIT_NS", raising=False)
+            monkeypatch.delenv("SFA_MERGE_WAIT_NS", raising=False)
         else:
-            monkeypatch.setenv("SFA_PAIR_WAIT_NS", wait)
-        outs[wait] = [_gpu(inp, dev=dev, num_splits=2) for _ in range(3)]
+            monkeypatch.setenv("SFA_MERGE_WAIT_NS", wait)
+        outs[wait] = [_gpu(inp, dev=dev, num_splits=splits) for _ in range(3)]
     ref = outs[None][0]
     for wait, runs in outs.items():
         for o in runs:
             assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), wait
-    _check(inp, ref, label=f"paired_nq{n_q}")
+    _check(inp, ref, label=f"spread_nq{n_q}_s{splits}")
 
 
 # ----------------------------------------------------------------------------------------
