@@ -214,6 +214,14 @@ int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void*
   a.chunk = (d->topk + splits - 1) / splits;
   a.reverse = is_prefill ? 1 : 0;
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);  // log2(e)
+  // One partition with fewer than half as many tokens as CUs: two workgroups of 64 heads per
+  // token instead of one of 128, so that twice as many CUs gather and compute; it needs no
+  // merge. (Short slot lists, such as a 128-position window, do not pay for partitions.)
+  a.head_groups = 1;
+  {
+    const DeviceInfo di = device_info(stream);
+    if (splits == 1 && d->n_q > kMaxHeads / 2 && di.cus > 0 && 2 * tokens <= di.cus) a.head_groups = 2;
+  }
   if (splits >= 2 && splits <= kMaxSpread) {
     // the spread merge needs the partitions of a token running at once: every workgroup of the
     // grid (one per compute unit) resident

@@ -52,6 +52,8 @@ struct KernelArgs {
   int64_t merge_wait_ticks;
   int64_t num_rows;
   int32_t n_tokens, s1, n_q, topk, mb, n_splits, chunk, reverse;
+  // 1, or 2 when a token's heads are split over two workgroups of 64 heads (one partition only)
+  int32_t head_groups;
   float scale_log2;           // softmax_scale * log2(e)
   // Window variants (the kernel instantiated with its window flag): slot g < window of token
   // t = b*s1 + s is original-cache position act[b] - s1 + s - window + 1 + g, through

@@ -407,21 +407,24 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   const int lane = tid & 63;
   const int n = lane & 31;  // row (A operand) or column (B operand, result) of the 32x32 MFMA
   const int g = lane >> 5;  // k-group of an operand / row-quad parity of a result
-  const int h0 = wave * kHeadsPerWave;  // first head of this wave
-  const bool wave_active = h0 < a.n_q;  // wave-uniform
-  const int h = h0 + n;                 // this lane's head
-  const bool head_ok = h < a.n_q;
-
-  // ---- work item: XCD-aware remap of the workgroup id, then (token, partition)
+  // ---- work item: XCD-aware remap of the workgroup id, then (token, partition, head group)
   const int nwg = gridDim.x;
   const int bid = blockIdx.x;
   const int per_xcd = nwg >> 3;
   int lid = bid;
   if (per_xcd > 0 && bid < (per_xcd << 3)) lid = (bid & 7) * per_xcd + (bid >> 3);
-  int t = lid / a.n_splits;
-  const int sp = lid - t * a.n_splits;
+  const int per_token = a.n_splits * a.head_groups;
+  int t = lid / per_token;
+  const int sp = (lid - t * per_token) / a.head_groups;
+  const int hg = lid - t * per_token - sp * a.head_groups;
   if (a.reverse) t = a.n_tokens - 1 - t;
   const int b = t / a.s1;
+  // With two head groups a workgroup covers 64 heads: waves 0 and 1 compute them, and waves 2
+  // and 3 only help gather the tiles.
+  const int h0 = hg * (kMaxHeads / 2) + wave * kHeadsPerWave;  // first head of this wave
+  const bool wave_active = (a.head_groups == 1 || wave < 2) && h0 < a.n_q;  // wave-uniform
+  const int h = h0 + n;                 // this lane's head
+  const bool head_ok = h < a.n_q;
 
   // The scores are used as fma(S, c, -m) with c = |scale * log2 e|. A negative scale is moved
   // into Q by flipping the sign bits of its bf16 elements, which is exact.
@@ -1364,7 +1367,7 @@ __global__ void __launch_bounds__(256) sfa_resolve_kernel(const ResolveArgs a) {
 }  // namespace
 
 hipError_t launch_attention(const KernelArgs& a, bool int8_cache, bool window_slots, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.n_tokens * a.n_splits));
+  const dim3 grid((unsigned)(a.n_tokens * a.n_splits * a.head_groups));
   const dim3 block(kThreads);
   KernelArgs copy = a;
   void* args[] = {&copy};
