@@ -294,6 +294,15 @@ def test_run_to_run_determinism(splits):
         assert np.array_equal(outs[0], o)
 
 
+@pytest.mark.parametrize("n_q,kv_dtype", [(128, "bf16"), (96, "bf16"), (80, "int8"), (128, "int8")])
+def test_head_groups_split(n_q, kv_dtype):
+    """One partition and few tokens: each token's heads are split over two workgroups of 64 (the
+    second one partly empty below 128 heads). Every element against the oracle."""
+    inp = W.generate(batch=4, s1=2, n_q=n_q, act_seqs=[300, 256, 129, 1000], topk=256, kv_dtype=kv_dtype, seed=12,
+                     max_blocks_per_batch=8)
+    _check(inp, _gpu(inp), label=f"head_groups_nq{n_q}_{kv_dtype}")
+
+
 @pytest.mark.parametrize("n_q,splits", [(128, 2), (64, 2), (32, 2), (128, 3), (128, 4), (96, 4), (128, 5),
                                          (128, 8), (64, 8), (128, 16)])
 def test_spread_merge_every_outcome(n_q, splits, monkeypatch):
