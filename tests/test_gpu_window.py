@@ -76,9 +76,13 @@ def test_swa_decode_shape_full(sfa_lib):
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
-def test_scfa_decode_shape_sampled(sfa_lib, kv_dtype):
-    inp = W.scfa_decode(seed=1, kv_dtype=kv_dtype)
-    _check(sfa_lib, inp, tokens=range(0, inp.n_tokens, 9))
+def test_scfa_decode_shape_full(sfa_lib, kv_dtype):
+    _check(sfa_lib, W.scfa_decode(seed=1, kv_dtype=kv_dtype))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+def test_cfa_decode_shape_full(sfa_lib, kv_dtype):
+    _check(sfa_lib, W.cfa_decode(seed=2, kv_dtype=kv_dtype))
 
 
 @pytest.mark.parametrize("mode", ["none", "sparse"])
