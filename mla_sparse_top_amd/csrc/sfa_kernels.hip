@@ -7,10 +7,10 @@
 // scale*S, times V = k_nope. How it is computed here is a gfx950 design of its own:
 //
 //   * A workgroup of 4 waves (one per SIMD) owns one (token, top-k partition) and every query
-//     head of the token: wave w owns heads 32w..32w+31 over the whole 576-wide d. It computes
-//     those heads' full scores itself, so no wave waits on another's partial scores, and every
-//     gathered 32-row tile feeds 128 heads: 36 S^T steps and 64 P.V steps of the 32x32x16 MFMA
-//     per wave and tile.
+//     head of the token (or 64 of them, with two head groups): wave w owns heads 32w..32w+31
+//     over the whole 576-wide d, so no wave waits on another's partial scores, and every
+//     gathered 32-row tile feeds all the workgroup's heads: 36 S^T steps and 64 P.V steps of the
+//     32x32x16 MFMA per wave and tile.
 //   * Registers: the wave's Q (32 heads x 576, the B operand of S^T = K . Q^T) stays in 144
 //     VGPRs, its O^T (32 heads x 512 fp32) in all 256 AGPRs.
 //   * Resolve + compaction: the partition's slots are resolved (index -> block_table -> row),
@@ -39,12 +39,12 @@
 //     with the P.V steps of tile i's first 16 keys; then tile i's last 16 keys' P.V steps run
 //     while the VALU computes tile i+1's softmax, so MFMA and VALU work overlap in every phase.
 //   * Partitions of one token merge in the same kernel: each takes an arrival ticket and
-//     publishes the unnormalised O, running max and running sum of the heads it does not merge;
-//     with 2 to 4 resident partitions the heads of each wave are merged by one of them (the
-//     merge spread over the token's workgroups), otherwise by the last to arrive. Whoever merges
-//     combines all partitions in partition order, so the result does not depend on arrival order:
-//     O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j. This is the prefill update rule applied
-//     across partitions.
+//     publishes the unnormalised O, running max and running sum other partitions need; with 2
+//     to 16 resident partitions each output unit (a wave's heads x 128 columns) is merged by one
+//     of them (the merge spread over the token's workgroups), otherwise all by the last to
+//     arrive. Whoever merges combines all partitions in partition order, so the result does not
+//     depend on arrival order: O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j, the prefill
+//     update rule applied across partitions.
 //   * Work items are mapped so that consecutive logical ids land on the same XCD and share its
 //     L2 (the hardware deals workgroups to the 8 XCDs round-robin): the partitions of a token,
 //     and the tokens of one sequence, which draw on the same rows.
