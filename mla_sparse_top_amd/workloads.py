@@ -515,8 +515,9 @@ def cache_decode_step(seed: int = 0, kv_dtype: str = "int8") -> CacheWriteInputs
 @dataclasses.dataclass
 class WindowInputs:
     """Shapes (T = batch * s1):
-      query_nope/query_rope  uint16 (T*n_q, 512/64)     bf16 bits
-      key_nope/key_rope      the shared pool, as in SfaInputs (k_nope_scales for int8)
+      query_nope/query_rope  uint16 (T*n_q, 512/64)     bf16 bits (rope (T*n_q, 0) for 512-wide rows)
+      key_nope/key_rope      the shared pool, as in SfaInputs (k_nope_scales for int8; key_rope
+                             (rows, 0) for 512-wide rows)
       cmp_indices            int32 (T, topk_cmp) or None  compressed-entry indices, -1 padded
       block_table_ori/_cmp   int32 (batch, mb_ori/mb_cmp)
       ori_len, cmp_len       int32 (batch,)
@@ -549,17 +550,24 @@ class WindowInputs:
     def num_cache_rows(self) -> int:
         return int(self.key_rope.shape[0])
 
+    @property
+    def rope_dim(self) -> int:
+        return int(self.key_rope.shape[1])
+
 
 def window_generate(*, batch: int, s1: int, n_q: int, ori_lens: Sequence[int], window: int, ratio: int = 4,
                     cmp_mode: str = "sparse", topk_cmp: int = 0, kv_dtype: str = "bf16", seed: int = 0,
-                    name: str = "") -> WindowInputs:
+                    name: str = "", rope_dim: int = ROPE_DIM) -> WindowInputs:
     """cmp_mode: "none" (SWA: window only), "all" (CFA: every causal compressed entry, in order)
     or "sparse" (SCFA: min(topk_cmp, causal) distinct causal entries in random order). A query at
     position p sees the compressed entries c with (c + 1) * ratio <= p + 1 (entry c summarises
     positions c*ratio .. c*ratio + ratio - 1). cmp_len[b] = ori_len[b] // ratio. Both caches' blocks
     are drawn in one random order from a shared pool with one trailing NaN poison block, which
-    every unused block-table entry names; rows past a cache's length are NaN too."""
-    assert kv_dtype in ("bf16", "int8") and cmp_mode in ("none", "all", "sparse")
+    every unused block-table entry names; rows past a cache's length are NaN too.
+    rope_dim 64: 512 nope + 64 rope channels per row, scale 1/sqrt(576). rope_dim 0: the 512-wide
+    rows of the DeepSeek-V4 layout, whose rotary channels sit inside the row; the rope arrays are
+    then zero-width and the scale is 1/sqrt(512)."""
+    assert kv_dtype in ("bf16", "int8") and cmp_mode in ("none", "all", "sparse") and rope_dim in (0, ROPE_DIM)
     g = torch.Generator().manual_seed(90_000 + int(seed))
     ori = [int(v) for v in ori_lens]
     cmp_len = [v // ratio for v in ori]
@@ -579,7 +587,7 @@ def window_generate(*, batch: int, s1: int, n_q: int, ori_lens: Sequence[int], w
         off += nb_c[b]
     rows = (n_used + 1) * BLOCK_SIZE
     nope, scales = _normal_nope(g, rows, kv_dtype == "int8")
-    rope = _normal_bf16(g, rows, ROPE_DIM)
+    rope = _normal_bf16(g, rows, ROPE_DIM) if rope_dim else np.zeros((rows, 0), dtype=np.uint16)
     dead = np.zeros(rows, dtype=bool)
     dead[poison * BLOCK_SIZE:] = True
     for b in range(batch):
@@ -597,7 +605,7 @@ def window_generate(*, batch: int, s1: int, n_q: int, ori_lens: Sequence[int], w
     rope[dead_rows] = BF16_QNAN
     t_count = batch * s1
     qn = _normal_bf16(g, t_count * n_q, KV_LORA_RANK)
-    qr = _normal_bf16(g, t_count * n_q, ROPE_DIM)
+    qr = _normal_bf16(g, t_count * n_q, ROPE_DIM) if rope_dim else np.zeros((t_count * n_q, 0), dtype=np.uint16)
     cmp_idx = None
     if cmp_mode != "none":
         causal = [max(0, (ori[t // s1] - s1 + t % s1 + 1) // ratio) for t in range(t_count)]
@@ -610,7 +618,7 @@ def window_generate(*, batch: int, s1: int, n_q: int, ori_lens: Sequence[int], w
             elif n > 0:
                 m = min(k, n)
                 cmp_idx[t, :m] = torch.randperm(n, generator=g)[:m].numpy().astype(np.int32)
-    scale = float(np.float32(1.0 / math.sqrt(KV_LORA_RANK + ROPE_DIM)))
+    scale = float(np.float32(1.0 / math.sqrt(KV_LORA_RANK + rope_dim)))
     return WindowInputs(batch=batch, s1=s1, n_q=n_q, window=int(window),
                         topk_cmp=0 if cmp_idx is None else int(cmp_idx.shape[1]), kv_dtype=kv_dtype,
                         query_nope=qn, query_rope=qr, key_nope=nope, key_rope=rope, k_nope_scales=scales,
@@ -640,6 +648,26 @@ def scfa_decode(seed: int = 0, kv_dtype: str = "bf16") -> WindowInputs:
     readings; 512 entries of ratio 4 cover 2048 original positions, the top-k of the SFA page)."""
     return window_generate(batch=64, s1=2, n_q=128, ori_lens=[8192] * 64, window=128, ratio=4, cmp_mode="sparse",
                            topk_cmp=512, kv_dtype=kv_dtype, seed=seed, name=f"scfa_b64_s2_w128_k512_{kv_dtype}")
+
+
+def swa_decode_d512(seed: int = 0, kv_dtype: str = "bf16") -> WindowInputs:
+    """SWA as swa_decode, on the 512-wide rows of the DeepSeek-V4 layout (D = 512, the head size
+    the page's timing table gives the FA-class operators)."""
+    return window_generate(batch=64, s1=2, n_q=128, ori_lens=[8192] * 64, window=128, cmp_mode="none",
+                           kv_dtype=kv_dtype, seed=seed, rope_dim=0, name=f"swa_b64_s2_w128_d512_{kv_dtype}")
+
+
+def cfa_decode_d512(seed: int = 0, kv_dtype: str = "bf16") -> WindowInputs:
+    """CFA as cfa_decode (ratio 128), on 512-wide rows."""
+    return window_generate(batch=64, s1=2, n_q=128, ori_lens=[8192] * 64, window=128, ratio=128, cmp_mode="all",
+                           kv_dtype=kv_dtype, seed=seed, rope_dim=0, name=f"cfa_b64_s2_w128_r128_d512_{kv_dtype}")
+
+
+def scfa_decode_d512(seed: int = 0, kv_dtype: str = "bf16") -> WindowInputs:
+    """SCFA as scfa_decode (ratio 4, 512 listed entries), on 512-wide rows."""
+    return window_generate(batch=64, s1=2, n_q=128, ori_lens=[8192] * 64, window=128, ratio=4, cmp_mode="sparse",
+                           topk_cmp=512, kv_dtype=kv_dtype, seed=seed, rope_dim=0,
+                           name=f"scfa_b64_s2_w128_k512_d512_{kv_dtype}")
 
 
 # ----------------------------------------------------------------------------------------
@@ -728,6 +756,14 @@ def compress_generate(*, batch: int, s1: int, ratio: int, start_pos: Sequence[in
                           score_state=f32(score_state),
                           block_table_cmp=np.ascontiguousarray(block_table, dtype=np.int32),
                           key_nope=kn, key_rope=kr, name=name, rotate=bool(rotate))
+
+
+def compress_c128a(seed: int = 0) -> CompressInputs:
+    """The page's c128a compressor case (ratio 128, one state window, D = 512) at the decode
+    step: 64 sequences, two new tokens at positions 8190 and 8191, so 8191 closes a window and
+    writes entry 63 into 512-wide rows (the rotary channels are the last 64 of the row)."""
+    return compress_generate(batch=64, s1=2, ratio=128, start_pos=[8190] * 64, rope_positions=8192,
+                             max_blocks=1, seed=seed, channels=KV_LORA_RANK, name="compress_c128a_b64_s2_d512")
 
 
 def compress_decode(seed: int = 0, ratio: int = 4) -> CompressInputs:

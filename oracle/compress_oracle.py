@@ -16,9 +16,10 @@ design notes):
   * the projections are plain GEMMs outside this step: kv and score arrive as fp32 (T, C), the
     precision the page gives the matmul outputs;
   * C = 576 channels, the row of the compressed cache the window attention reads (512 nope
-    channels, then 64 rope channels), or C = 128, the row of a compressed index-key cache (the
+    channels, then 64 rope channels), C = 512, the same row in the page's D = 512 layout (the
+    rotary channels inside the row), or C = 128, the row of a compressed index-key cache (the
     page's D = 128 configuration, whose keys the Lightning Indexer scores); the last 64 channels
-    are the rotary ones in both;
+    are the rotary ones in all three;
   * the state of sequence b holds `ratio` slots of C channels; the token at position p writes
     slot p mod ratio; ape is (ratio, C), indexed by that slot; the stored score is the fp32 sum
     score + ape[slot];

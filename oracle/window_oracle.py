@@ -21,7 +21,12 @@ its reason in the design notes):
   * compressed entries come as an index list per token (-1 padding), valid iff
     0 <= j < cmp_len[b]; for CFA the caller lists every causal entry;
   * both caches are rows of one paged pool with block_size 128; each has its own block table;
-  * duplicates across the two sources count once per occurrence (a gather list).
+  * duplicates across the two sources count once per occurrence (a gather list);
+  * rows of the page's D = 512 configuration (the head size its timing table gives these
+    operators): query and cache rows are 512 channels whose last 64 already carry the rotary
+    embedding (the page's MlaProlog and Compressor rotate them in place), the score runs over
+    all 512 and V is the same row. Such inputs carry zero-width rope arrays, so the formula
+    below applies unchanged (the rope term of the score is an empty sum).
 """
 
 from __future__ import annotations

@@ -144,7 +144,7 @@ def _brute(x):
 
 
 def _pin_brute_force():
-    for ch, rot in ((576, False), (128, False), (128, True)):
+    for ch, rot in ((576, False), (512, False), (128, False), (128, True)):
         x = _small(seed=3, ratio=3, s1=5, start=1, n_pos=5, channels=ch, rotate=rot)  # positions 1..5; 5 past the tables
         ks, ss, e = C.compress(x)
         bk, bs, be = _brute(x)

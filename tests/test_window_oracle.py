@@ -107,6 +107,51 @@ def test_cfa_lists_every_causal_entry():
     assert len(rows) == 4 + 4
 
 
+def _scalar_shared_kv_attention(q, rows_k, scale):
+    """One head over rows that serve as both key and value, in scalar loops: softmax over the
+    rows of scale * <q, k_j>, then the weighted sum of the rows."""
+    s = [scale * sum(qd * kd for qd, kd in zip(q, k)) for k in rows_k]
+    m = max(s)
+    w = [math.exp(v - m) for v in s]
+    tot = sum(w)
+    return [sum(w[j] * rows_k[j][d] for j in range(len(rows_k))) / tot for d in range(len(q))]
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+def test_d512_rows_match_scalar_attention_with_shared_kv(kv_dtype):
+    """The 512-wide row layout (zero-width rope): each head's output is the softmax-weighted sum
+    of the attended 512-channel rows themselves, the score taken over all 512 channels."""
+    inp = W.window_generate(batch=2, s1=2, n_q=2, ori_lens=[9, 140], window=3, ratio=2, cmp_mode="sparse",
+                            topk_cmp=3, kv_dtype=kv_dtype, rope_dim=0, seed=7)
+    assert inp.rope_dim == 0 and inp.query_rope.shape == (8, 0)
+    assert inp.softmax_scale == float(np.float32(1 / math.sqrt(512)))
+    out = WO.window_attention(inp)
+    for t in range(4):
+        rows = WO.token_rows(t, 2, 3, inp.cmp_indices, inp.block_table_ori, inp.block_table_cmp, inp.ori_len,
+                             inp.cmp_len, inp.num_cache_rows)
+        assert len(rows) == 6
+        if kv_dtype == "int8":
+            ks = O.dequant_int8_chain(inp.key_nope[rows], inp.k_nope_scales[rows])
+        else:
+            ks = O.bf16_bits_to_f64(inp.key_nope[rows])
+        ks = [list(map(float, r)) for r in ks]
+        for hh in range(2):
+            q = list(map(float, O.bf16_bits_to_f64(inp.query_nope[2 * t + hh])))
+            want = _scalar_shared_kv_attention(q, ks, inp.softmax_scale)
+            np.testing.assert_allclose(out[t // 2, t % 2, hh], want, rtol=1e-12, atol=1e-13)
+
+
+def test_d512_equals_the_576_layout_with_zero_rope():
+    """Appending 64 zero rope channels to every query and row changes no score, so the 576-wide
+    formula gives the same output, bit for bit."""
+    inp = W.window_generate(batch=2, s1=2, n_q=4, ori_lens=[300, 77], window=20, ratio=4, cmp_mode="sparse",
+                            topk_cmp=10, rope_dim=0, seed=8)
+    out = WO.window_attention(inp)
+    inp.key_rope = np.zeros((inp.key_nope.shape[0], 64), dtype=np.uint16)
+    inp.query_rope = np.zeros((inp.query_nope.shape[0], 64), dtype=np.uint16)
+    assert np.array_equal(WO.window_attention(inp), out)
+
+
 # ---- planted mistakes (CPU only) ----------------------------------------------------------
 
 _real_wp = WO.window_positions
@@ -128,6 +173,23 @@ def _cmp_through_ori_table(t, s1, window, cmp, bt_o, bt_c, ol, cl, n):
 _PINS = [test_window_positions_hand_worked, test_token_rows_hand_worked,
          test_full_window_equals_dense_causal_attention, test_one_position_window_returns_its_value_row,
          test_single_sequence_sources_match_sparse_attention_oracle]
+
+
+_real_token = O.sparse_mla_attention_token
+
+
+def _d512_scores_skip_rotary_channels(qn, qr, kn, kr, scale):
+    # a 512-wide row taken as 448 nope channels plus 64 rope channels that have no query part
+    if qr.shape[1] == 0:
+        qn = qn.copy()
+        qn[:, 448:] = 0.0
+    return _real_token(qn, qr, kn, kr, scale)
+
+
+def test_d512_pin_catches_planted_mistake(monkeypatch):
+    monkeypatch.setattr(O, "sparse_mla_attention_token", _d512_scores_skip_rotary_channels)
+    with pytest.raises(AssertionError):
+        test_d512_rows_match_scalar_attention_with_shared_kv("bf16")
 
 
 @pytest.mark.parametrize("name", ["excludes_query", "one_short", "cmp_through_ori_table"])
