@@ -19,6 +19,8 @@ Algorithmic work per call (fixed by the workload, not by the implementation):
           512 + 128 + 16 scale bytes), plus per token Q (n_q*576*2) + out (n_q*512*2) + indices
           (4*topk)
   flop  = sum over valid (token, slot) of 2 * n_q * (576 + 512)
+The window workloads on 512-wide rows (rotary channels inside the row) count 1024 (bf16) or 528
+(int8: 512 + 16) bytes per row, Q at n_q*512*2 and 2 * n_q * (512 + 512) flop per row.
 """
 
 from __future__ import annotations
@@ -447,6 +449,11 @@ WINDOW_WORKLOADS = {
     "cfa_b64_s2_w128_r128_bf16": ("cfa_decode", "bf16"),
     "scfa_b64_s2_w128_k512_bf16": ("scfa_decode", "bf16"),
     "scfa_b64_s2_w128_k512_int8": ("scfa_decode", "int8"),
+    # the same on 512-wide rows, the head size the pages' timing table gives these operators
+    "swa_b64_s2_w128_d512_bf16": ("swa_decode_d512", "bf16"),
+    "cfa_b64_s2_w128_r128_d512_bf16": ("cfa_decode_d512", "bf16"),
+    "scfa_b64_s2_w128_k512_d512_bf16": ("scfa_decode_d512", "bf16"),
+    "scfa_b64_s2_w128_k512_d512_int8": ("scfa_decode_d512", "int8"),
 }
 
 
@@ -514,9 +521,10 @@ def bench_window(args):
     T = inp.n_tokens
     valid = sum(len(WO.token_rows(t, inp.s1, inp.window, inp.cmp_indices, inp.block_table_ori, inp.block_table_cmp,
                                   inp.ori_len, inp.cmp_len, inp.num_cache_rows)) for t in range(T))
-    row = 1152 if dtype == "bf16" else 656
-    nbytes = valid * row + T * (inp.n_q * 576 * 2 + inp.n_q * 512 * 2 + 4 * inp.topk_cmp)
-    flop = valid * 2 * inp.n_q * (576 + 512)
+    d_qk = 512 + inp.rope_dim   # score width: 576, or 512 for rows with the rotary channels inside
+    row = (512 * 2 if dtype == "bf16" else 512 + 16) + inp.rope_dim * 2
+    nbytes = valid * row + T * (inp.n_q * d_qk * 2 + inp.n_q * 512 * 2 + 4 * inp.topk_cmp)
+    flop = valid * 2 * inp.n_q * (d_qk + 512)
     gbps = nbytes / (launch_ms * 1e-3) / 1e9
     tflops = flop / (launch_ms * 1e-3) / 1e12
     rec = {
@@ -533,7 +541,7 @@ def bench_window(args):
         "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": inp.batch, "s1": inp.s1, "n_q": inp.n_q,
-                   "window": inp.window, "topk_cmp": inp.topk_cmp, "ori_len": int(inp.ori_len.max()),
+                   "head_dim": d_qk, "window": inp.window, "topk_cmp": inp.topk_cmp, "ori_len": int(inp.ori_len.max()),
                    "compress_ratio": (int(inp.ori_len[0]) // int(inp.cmp_len[0])) if inp.topk_cmp else None,
                    "valid_slots": valid, "cold_sets": len(sets)},
         "kernel_ms_mean": round(launch_ms, 5),
@@ -544,7 +552,7 @@ def bench_window(args):
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profile(kernel_source_hash(), f"{args.workload}_traffic.txt")},
         "rotated_outputs_identical": bool(same),
-        "context_pages_one_die_us": {"swa_decode": 65, "cfa_decode": 90, "scfa_decode": 160}[fn_name],
+        "context_pages_one_die_us": {"swa": 65, "cfa": 90, "scfa": 160}[fn_name.split("_")[0]],
     }
     if args.cpu_seconds > 0:
         got = outs[(args.steps - 1) % len(sets)].float().cpu().numpy().astype(np.float64).reshape(T, inp.n_q, 512)
@@ -691,7 +699,8 @@ def bench_cache_write(args):
 
 
 COMPRESS_WORKLOADS = {"compress_b64_s2_r4": ("compress_decode", 4),
-                      "compress_b64_s2_r4_c128_rot": ("compress_index_decode", 4)}
+                      "compress_b64_s2_r4_c128_rot": ("compress_index_decode", 4),
+                      "compress_c128a_b64_s2_d512": ("compress_c128a", None)}
 
 
 def compress_algorithmic_bytes(inp) -> int:
@@ -724,7 +733,7 @@ def bench_compress(args):
     from mla_sparse_top_amd import sfa, workloads
 
     fn_name, ratio = COMPRESS_WORKLOADS[args.workload]
-    inp = getattr(workloads, fn_name)(seed=args.seed, ratio=ratio)
+    inp = getattr(workloads, fn_name)(seed=args.seed, **({} if ratio is None else {"ratio": ratio}))
     print(f"[bench] generated {inp.name}", file=sys.stderr, flush=True)
     d = sfa.compress_to_device(inp)
     call = sfa.prepare_compress(inp, d)
@@ -775,6 +784,9 @@ def bench_compress(args):
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profile(src_hash, f"{args.workload}_traffic.txt")},
         "kernel_source_sha256": src_hash,
+        # the pages' c128a figure at this shape (ratio 128, one state window, D = 512), on one die
+        # of another machine: context only
+        "context_pages_one_die_us": 55 if fn_name == "compress_c128a" else None,
     }
     if args.cpu_seconds > 0:
         # the oracle over the whole call, repeated until the budget is spent; its first result is

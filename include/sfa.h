@@ -235,6 +235,13 @@ int sfa_cache_write(const sfa_dims* dims, const void* new_nope, const void* new_
  *   Both caches are rows of one paged pool (key_nope_2d, key_rope_2d, k_nope_scales as in
  *   sfa_decode, blocks of 128 rows); each has its own block table and length.
  *
+ *   rope_dim 64: rows and queries of 512 nope + 64 rope channels, as in sfa_decode.
+ *   rope_dim 0: the page's D = 512 layout (the head size its timing table gives these
+ *     operators): 512-channel rows whose last 64 channels already carry the rotary embedding
+ *     (applied in place by the prolog or the compressor). The score is q . k over the 512
+ *     channels and V is the same row; query_rope and key_rope are not read and may be NULL.
+ *     An INT8 pool holds the whole row as codes, with 4 group scales per row as in sfa_decode.
+ *
  *   query_nope/query_rope/out/key_*    as for sfa_decode
  *   cmp_indices      int32 (T, topk_cmp)                    NULL when topk_cmp == 0
  *   block_table_ori  int32 (batch, max_blocks_ori)
@@ -248,12 +255,13 @@ int sfa_cache_write(const sfa_dims* dims, const void* new_nope, const void* new_
  * compressed entries through block_table_cmp) and runs unchanged after it. Queued on `stream`;
  * nothing is allocated. Errors as for sfa_decode, plus SFA_ERR_DIMS for window < 0,
  * topk_cmp < 0, window + topk_cmp < 1 (or above the attention's top-k limit),
- * max_blocks_ori < 1, or topk_cmp > 0 with max_blocks_cmp < 1.
+ * max_blocks_ori < 1, topk_cmp > 0 with max_blocks_cmp < 1, or rope_dim other than 64 or 0.
  * Preconditions as for sfa_decode, on both block tables; also ori_len[b] >= s1 for a full window
  * (positions below 0 are simply absent).
  */
 typedef struct {
-  int32_t batch, s1, n_q, n_kv, kv_lora_rank, rope_dim, block_size;  /* as in sfa_dims         */
+  int32_t batch, s1, n_q, n_kv, kv_lora_rank, rope_dim, block_size;  /* as in sfa_dims, but
+                                                                        rope_dim 64 or 0      */
   int32_t window;          /* original-cache positions each query reads, >= 0               */
   int32_t topk_cmp;        /* row length of cmp_indices, >= 0 (0: SWA, no compressed source)  */
   int32_t max_blocks_ori;  /* row length of block_table_ori, >= 1                            */
@@ -350,11 +358,12 @@ int sfa_topk_select(const sfa_indexer_dims* dims, const float* scores, const int
  * matrix in natural order (H_2n = [[H_n, H_n], [H_n, -H_n]]), the page's rotate = true branch.
  * y is stored as bf16 (round to nearest even) at row block_table_cmp[b][c / 128] * 128 + c % 128:
  * with 576 channels, channels 0..511 to key_nope_2d and 512..575 to key_rope_2d (the row layout
- * of the cache sfa_window_decode reads); with 128 channels (the page's D = 128 configuration,
- * an index-key row for the Lightning Indexer), the whole row to key_nope_2d, rows of 128
+ * of the cache sfa_window_decode reads with rope_dim 64); with 512 channels (the page's D = 512
+ * layout, the row sfa_window_decode reads with rope_dim 0) or 128 channels (the page's D = 128
+ * configuration, an index-key row for the Lightning Indexer), the whole row to key_nope_2d
  * (key_rope_2d is not used and may be NULL). The softmax, sum, norm and rotations are fp32.
  *
- *   dims              channels C = 576 or 128, rotate 0 or 1 (1 only with 128), block_size
+ *   dims              channels C = 576, 512 or 128, rotate 0 or 1 (1 only with 128), block_size
  *                     128; ratio in [1, 1024]; T = batch*s1 up to 2^26; max_blocks = row
  *                     length of block_table_cmp
  *   kv, score         fp32  (T, C)
@@ -366,8 +375,8 @@ int sfa_topk_select(const sfa_indexer_dims* dims, const float* scores, const int
  *   kv_state,
  *   score_state       fp32  (batch, ratio, C), read and refreshed in place
  *   block_table_cmp   int32 (batch, max_blocks)
- *   key_nope_2d       bf16  (num_cache_rows, 512), or (num_cache_rows, 128) for C = 128,
- *                     written in place
+ *   key_nope_2d       bf16  (num_cache_rows, 512) for C = 576 or 512, or (num_cache_rows, 128)
+ *                     for C = 128, written in place
  *   key_rope_2d       bf16  (num_cache_rows, 64) written in place (C = 576 only)
  *
  * With batch * s1 = 0 the call reads nothing and returns SFA_OK (the pointers may then be NULL).
@@ -381,7 +390,8 @@ int sfa_topk_select(const sfa_indexer_dims* dims, const float* scores, const int
 typedef struct {
   int32_t batch;
   int32_t s1;                   /* new tokens per sequence                                      */
-  int32_t channels;             /* 576 (kv_lora_rank + rope_dim) or 128 (an index-key row)       */
+  int32_t channels;             /* 576 (kv_lora_rank + rope_dim), 512 (rotary channels inside the
+                                   row) or 128 (an index-key row)                                */
   int32_t ratio;                /* compression ratio                                            */
   int32_t rope_positions;       /* rows of rope_cos and rope_sin                                */
   int32_t max_blocks;           /* row length of block_table_cmp                                */

@@ -22,8 +22,9 @@ bool overlaps(const void* p, size_t n, const void* q, size_t m) {
 int check_compress_dims(const sfa_compress_dims* d, float eps) {
   if (!d) return SFA_ERR_NULL;
   const bool cache_row = d->channels == SFA_KV_LORA_RANK + SFA_ROPE_DIM;
-  if ((!cache_row && d->channels != 128) || d->block_size != SFA_BLOCK_SIZE) return SFA_ERR_DIMS;
-  if (d->rotate != 0 && (d->rotate != 1 || cache_row)) return SFA_ERR_DIMS;  // Hadamard: 128 channels
+  if ((!cache_row && d->channels != SFA_KV_LORA_RANK && d->channels != 128) || d->block_size != SFA_BLOCK_SIZE)
+    return SFA_ERR_DIMS;
+  if (d->rotate != 0 && (d->rotate != 1 || d->channels != 128)) return SFA_ERR_DIMS;  // Hadamard: 128 channels
   if (d->batch < 0 || d->s1 < 0 || (int64_t)d->batch * d->s1 > (1 << 26)) return SFA_ERR_DIMS;
   if (d->batch > (1 << 20)) return SFA_ERR_DIMS;
   if (d->ratio < 1 || d->ratio > 1024) return SFA_ERR_DIMS;
@@ -48,7 +49,7 @@ extern "C" int sfa_compress(const sfa_compress_dims* dims, const float* kv, cons
   if (!kv || !score || !ape || !gamma || !rope_cos || !rope_sin || !start_pos || !kv_state || !score_state ||
       !block_table_cmp || !key_nope_2d || (cache_row && !key_rope_2d))
     return SFA_ERR_NULL;
-  if (!cache_row) key_rope_2d = nullptr;  // a 128-channel row goes whole to key_nope_2d
+  if (!cache_row) key_rope_2d = nullptr;  // a 512- or 128-channel row goes whole to key_nope_2d
   const void* ins[] = {kv, score, ape, gamma, rope_cos, rope_sin, start_pos, block_table_cmp};
   void* outs[] = {kv_state, score_state, key_nope_2d, key_rope_2d};
   for (const void* p : ins)

@@ -19,12 +19,12 @@ struct CompressArgs {
   float* kv_state;              // (batch, ratio, C)
   float* score_state;           // (batch, ratio, C)
   const int32_t* block_table;   // (batch, mb)
-  uint16_t* key_nope;           // bf16 bits (rows, 512), or (rows, 128) for C = 128
-  uint16_t* key_rope;           // bf16 bits (rows, 64); unused for C = 128
+  uint16_t* key_nope;           // bf16 bits (rows, 512) for C = 576 or 512, or (rows, 128) for C = 128
+  uint16_t* key_rope;           // bf16 bits (rows, 64) for C = 576; unused otherwise
   int64_t num_rows;
   float eps;
   int32_t batch, s1, ratio, rope_positions, mb;
-  int32_t channels;             // 576 or 128
+  int32_t channels;             // 576, 512 or 128
   int32_t rotate;               // 128 channels: the Hadamard transform after RoPE
 };
 

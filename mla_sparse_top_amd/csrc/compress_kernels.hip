@@ -9,7 +9,8 @@
 // gamma), its last 64 channels are rotated in adjacent pairs by the RoPE angle of position p,
 // with rotate = true the row then goes through the Sylvester Hadamard transform scaled by
 // 1/sqrt(n), and the row is stored as bf16 at the entry's row of the compressed pool. Rows are
-// 576 channels (the attention cache row: 512 to key_nope, 64 to key_rope) or 128 (an index-key
+// 576 channels (the attention cache row: 512 to key_nope, 64 to key_rope), 512 (the same row in
+// the page's D = 512 layout, rotary channels inside, whole to key_nope) or 128 (an index-key
 // row, the page's D = 128 configuration, whole to key_nope).
 //
 // How: one workgroup per sequence, each thread owning a few channels, so every per-channel step
@@ -41,11 +42,17 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
 }
 
 // kC channels: 576 (the attention cache row, three waves, thread i owning channels i, i + 192,
-// i + 384) or 128 (an index-key row, one wave, lane i owning channels i and i + 64). The rotary
-// channels, the last 64, are the last register of the last wave's lanes in both.
+// i + 384), 512 (two waves, thread i owning channels i + 128k, k < 4) or 128 (an index-key row,
+// one wave, lane i owning channels i and i + 64). The rotary channels, the last 64, are the last
+// register of the last wave's lanes in all three.
+template <int kC>
+constexpr int compress_threads() {
+  return kC == 576 ? 192 : kC == 512 ? 128 : 64;
+}
 template <int kC, bool kRotate>
-__global__ void __launch_bounds__(kC == 576 ? 192 : 64) compress_kernel(const CompressArgs a) {
-  constexpr int kT = kC == 576 ? 192 : 64;  // threads
+__global__ void __launch_bounds__(compress_threads<kC>()) compress_kernel(const CompressArgs a) {
+  static_assert(!kRotate || kC == 128, "the Hadamard transform is built for 128 channels");
+  constexpr int kT = compress_threads<kC>();  // threads
   constexpr int kPer = kC / kT;             // channels per thread
   constexpr int kWaves = kT / 64;
   const int b = blockIdx.x;
@@ -222,6 +229,8 @@ __global__ void __launch_bounds__(kC == 576 ? 192 : 64) compress_kernel(const Co
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
   if (a.channels == 576)
     hipLaunchKernelGGL((compress_kernel<576, false>), dim3(a.batch), dim3(192), 0, stream, a);
+  else if (a.channels == 512)
+    hipLaunchKernelGGL((compress_kernel<512, false>), dim3(a.batch), dim3(128), 0, stream, a);
   else if (a.rotate)
     hipLaunchKernelGGL((compress_kernel<128, true>), dim3(a.batch), dim3(64), 0, stream, a);
   else

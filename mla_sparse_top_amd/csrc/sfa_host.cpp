@@ -27,10 +27,11 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int check_dims(const sfa_dims* d) {
+// rope_dim 0 (512-wide rows with the rotary channels inside) is accepted for the window variants
+int check_dims(const sfa_dims* d, bool allow_no_rope = false) {
   if (!d) return SFA_ERR_NULL;
-  if (d->n_kv != 1 || d->kv_lora_rank != kNope || d->rope_dim != kRope || d->block_size != kBlock)
-    return SFA_ERR_DIMS;
+  if (d->n_kv != 1 || d->kv_lora_rank != kNope || d->block_size != kBlock) return SFA_ERR_DIMS;
+  if (d->rope_dim != kRope && !(allow_no_rope && d->rope_dim == 0)) return SFA_ERR_DIMS;
   if (d->n_q < 16 || d->n_q > SFA_MAX_HEADS || (d->n_q % 16) != 0) return SFA_ERR_DIMS;
   if (d->batch < 0 || d->s1 < 0) return SFA_ERR_DIMS;
   if ((int64_t)d->batch * d->s1 > (1 << 24)) return SFA_ERR_DIMS;
@@ -139,12 +140,15 @@ int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void*
                   const void* kr, const float* scales, const int32_t* idx, const int32_t* bt,
                   const int32_t* act, float softmax_scale, void* out, void* ws, size_t ws_bytes,
                   hipStream_t stream, const WindowSource* win = nullptr) {
-  int st = check_dims(d);
+  int st = check_dims(d, win != nullptr);
   if (st != SFA_OK) return st;
   const int64_t tokens = (int64_t)d->batch * d->s1;
   // the window variants take no index list when they have no compressed source (SWA)
   const bool need_idx = !win || win->topk_cmp > 0;
-  if (!qn || !qr || !kn || !kr || (need_idx && !idx) || !bt || !act || !out) return SFA_ERR_NULL;
+  // rows without rope channels: query_rope and key_rope are not read (and may be null)
+  const bool rope = d->rope_dim > 0;
+  if (!rope) qr = kr = nullptr;
+  if (!qn || (rope && !qr) || !kn || (rope && !kr) || (need_idx && !idx) || !bt || !act || !out) return SFA_ERR_NULL;
   if (win && win->topk_cmp > 0 && (!win->bt_cmp || !win->cmp_len)) return SFA_ERR_NULL;
   const bool int8 = d->kv_dtype == SFA_KV_INT8;
   if (int8 && !scales) return SFA_ERR_SCALES;
@@ -166,9 +170,9 @@ int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void*
   const void* ins[] = {qn, qr, kn, kr, scales, idx, bt, act, lay.total ? ws : nullptr,
                        win ? win->bt_cmp : nullptr, win ? win->cmp_len : nullptr};
   const size_t sizes[] = {(size_t)tokens * d->n_q * kNope * 2,
-                          (size_t)tokens * d->n_q * kRope * 2,
+                          (size_t)tokens * d->n_q * d->rope_dim * 2,
                           rows * kNope * (int8 ? 1 : 2),
-                          rows * kRope * 2,
+                          rows * d->rope_dim * 2,
                           int8 ? rows * 4 * sizeof(float) : 0,
                           (size_t)tokens * idx_cols * sizeof(int32_t),
                           (size_t)d->batch * d->max_blocks_per_batch * sizeof(int32_t),
@@ -238,7 +242,7 @@ int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void*
     a.block_table_cmp = win->topk_cmp > 0 ? win->bt_cmp : nullptr;
     a.act_cmp = win->topk_cmp > 0 ? win->cmp_len : nullptr;
   }
-  return launch_attention(a, int8, win != nullptr, stream) == hipSuccess ? SFA_OK : SFA_ERR_HIP;
+  return launch_attention(a, int8, win != nullptr, rope, stream) == hipSuccess ? SFA_OK : SFA_ERR_HIP;
 }
 
 int check_window_dims(const sfa_window_dims* d) {
@@ -272,10 +276,14 @@ sfa_dims window_attention_dims(const sfa_window_dims* w) {
 extern "C" {
 
 int sfa_window_workspace_size(const sfa_window_dims* dims, size_t* bytes_out) {
-  const int st = check_window_dims(dims);
+  if (!bytes_out) return SFA_ERR_NULL;
+  int st = check_window_dims(dims);
   if (st != SFA_OK) return st;
   const sfa_dims c = window_attention_dims(dims);
-  return sfa_workspace_size(&c, 0, bytes_out);
+  st = check_dims(&c, true);
+  if (st != SFA_OK) return st;
+  *bytes_out = ws_layout(&c, pick_splits(&c, 0)).total;
+  return SFA_OK;
 }
 
 int sfa_window_decode(const sfa_window_dims* dims, const void* query_nope, const void* query_rope,

@@ -73,7 +73,7 @@ struct ResolveArgs {
   int32_t n_tokens, s1, topk, mb;
 };
 
-hipError_t launch_attention(const KernelArgs& a, bool int8_cache, bool window_slots, hipStream_t stream);
+hipError_t launch_attention(const KernelArgs& a, bool int8_cache, bool window_slots, bool rope, hipStream_t stream);
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t stream);
 
 }  // namespace sfa

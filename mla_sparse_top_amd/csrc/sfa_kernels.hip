@@ -4,7 +4,10 @@
 // Quantization" (sections "Algorithm overview", "Implementation notes: compute pipeline", "INT8
 // quantisation path", "Flash online softmax update"): for every query token, gather the top-k
 // latent rows through the block table, S = [q_nope|q_rope] . [k_nope|k_rope]^T, softmax of
-// scale*S, times V = k_nope. How it is computed here is a gfx950 design of its own:
+// scale*S, times V = k_nope. The window variants ("NPU DeepSeek-V4 model PyPTO fused-operator
+// optimisation", FA-class operators) also take 512-wide rows with the rotary channels inside the
+// row (its D = 512): no rope part, S = q . k^T over the 512 channels, V = the row. How it is
+// computed here is a gfx950 design of its own:
 //
 //   * A workgroup of 4 waves (one per SIMD) owns one (token, top-k partition) and every query
 //     head of the token (or 64 of them, with two head groups): wave w owns heads 32w..32w+31
@@ -90,7 +93,6 @@ constexpr int kStageBytes = kNopeTileBytes + kRopeTileBytes;
 constexpr int kCodeTileBytes = kTile * kNope;        // 16 KB
 constexpr int kCodeBufBytes = kCodeTileBytes + kWaves * 256;
 constexpr float kRescaleThreshold = 8.0f;           // log2 units: p stays <= 256 between rescales
-constexpr int kQkSteps = (kNope + kRope) / 16;      // 36 k-steps of 16 over the 576 columns
 constexpr int kQkDepthBf16 = 4;
 constexpr int kPvDepthBf16 = 3;
 constexpr int kOutWaveBytes = kHeadsPerWave * kNopeRowBytes;  // a wave's bf16 output rows (32 KB)
@@ -390,9 +392,17 @@ __device__ __forceinline__ float pair_sum(float x) {
 // with 32-bit byte offsets (pools below 4 Mi rows); otherwise through 64-bit global addresses.
 // kWindow: the window variants' slot list (see KernelArgs), resolved here instead of read from
 // topk_indices; the rest of the kernel is the same.
-template <bool kInt8, bool kBufDma, bool kWindow>
+// kRopeW: 64, rows of 512 nope + 64 rope channels (scores over both, V = nope); or 0, the
+// 512-wide rows whose rotary channels sit inside the row (scores over the 512, V = the row).
+template <bool kInt8, bool kBufDma, bool kWindow, int kRopeW>
 __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const KernelArgs a) {
   using L = Lds<kInt8>;
+  static_assert(kRopeW == kRope || kRopeW == 0, "rows carry 64 rope channels or none");
+  // S^T k-steps of 16 over the row (36 over 576 channels, 32 over 512); DMA pieces and INT8
+  // dequantisation parts are spread over them at these strides
+  constexpr int kQk = (kNope + kRopeW) / 16;
+  constexpr int kPieceStride = kRopeW ? 7 : 6;
+  constexpr int kDqStride = kRopeW ? 8 : 6;
   // S^T operand loads in flight ahead of the MFMA (INT8 keeps one fewer: its dequantisation
   // needs the registers)
   constexpr int kQkDepth = kInt8 ? 3 : kQkDepthBf16;
@@ -484,19 +494,21 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     }
   }
   // ---- Q^T fragments (B operand, k = d): step c < 32 covers nope chunks 2c + {0, 1}, steps
-  // 32..35 rope chunks 2(c - 32) + {0, 1}; lane (n, g) holds chunk +g.
+  // 32..35 (with rope channels) rope chunks 2(c - 32) + {0, 1}; lane (n, g) holds chunk +g.
   // Issued after the index and block-table loads: load completion is counted in issue order,
   // so Q's 147 KB per token must not sit in front of the two dependent index round trips.
   // A lane past n_q reads head 0's row; its scores are computed and never stored.
-  uint4 qv[kQkSteps];
+  uint4 qv[kQk];
   {
     const int64_t qrow = (int64_t)t * a.n_q + (head_ok ? h : 0);
     const uint4* qn = reinterpret_cast<const uint4*>(a.q_nope + qrow * kNope);
-    const uint4* qr = reinterpret_cast<const uint4*>(a.q_rope + qrow * kRope);
 #pragma unroll
     for (int c = 0; c < 32; ++c) qv[c] = qn[2 * c + g];
+    if constexpr (kRopeW > 0) {
+      const uint4* qr = reinterpret_cast<const uint4*>(a.q_rope + qrow * kRope);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qv[32 + c] = qr[2 * c + g];
+      for (int c = 0; c < 4; ++c) qv[32 + c] = qr[2 * c + g];
+    }
   }
   int rowv[8];
   int cnt = 0;
@@ -557,12 +569,13 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   auto stage_of = [&](int tile) -> uint32_t { return (uint32_t)((tile % L::kStages) * kStageBytes); };
   auto codes_of = [&](int tile) -> uint32_t { return (uint32_t)(L::kCodesOff + (tile & 1) * kCodeBufBytes); };
   const u32x4 rs_nope = make_rsrc(a.k_nope, (uint64_t)a.num_rows * (kInt8 ? kNope : kNopeRowBytes));
-  const u32x4 rs_rope = make_rsrc(a.k_rope, (uint64_t)a.num_rows * kRopeRowBytes);
+  const u32x4 rs_rope = make_rsrc(a.k_rope, kRopeW ? (uint64_t)a.num_rows * kRopeRowBytes : 0);
   const u32x4 rs_scale = make_rsrc(a.k_scales, kInt8 ? (uint64_t)a.num_rows * 16 : 0);
   // lane L's row: key 8w + L/8 of the tile (rope DMA; its readlanes give the wave's 8 rows)
   auto lane_row = [&](int tile) -> int { return s_rows[tile * kTile + wave * 8 + (lane_id_here() >> 3)]; };
   // rope: lane L fetches chunk ((L & 7) ^ rope_swz(key)) of key = 8w + L/8
   auto issue_rope = [&](int row, uint32_t stage) __attribute__((always_inline)) {
+    if constexpr (kRopeW == 0) return;
     const int ln = lane_id_here();
     const int key = wave * 8 + (ln >> 3);
     const uint32_t chunk = 16 * ((ln & 7) ^ rope_swz(key));
@@ -621,7 +634,8 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     }
   };
   // DMA instructions per tile and wave: bf16 8 nope rows + 1 rope; INT8 4 code + 1 scale + 1 rope
-  constexpr int kDmaPerTile = kInt8 ? 6 : 9;
+  // (no rope instruction for rows without rope channels)
+  constexpr int kDmaPerTile = (kInt8 ? 5 : 8) + (kRopeW ? 1 : 0);
   // The same DMA in five pieces, to be spread between MFMAs: piece k < 4 moves the wave's rows
   // 2k and 2k + 1 (bf16 nope rows, or INT8 codes), piece 4 the rope rows (and INT8 scales).
   auto issue_piece = [&](int tile, int row, int k) __attribute__((always_inline)) {
@@ -750,7 +764,7 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     }
   }
   auto qk_operand = [&](uint32_t kst, uint32_t rst, int c) __attribute__((always_inline)) -> bf16x8 {
-    if (c < 32) return lds_b128(smem_p + ((kst ^ (32u * (c & 7))) + 256u * (c >> 3)));
+    if (kRopeW == 0 || c < 32) return lds_b128(smem_p + ((kst ^ (32u * (c & 7))) + 256u * (c >> 3)));
     return lds_b128(smem_p + (rst ^ (32u * (c - 32))));
   };
   // u = 16*kb + dc
@@ -762,7 +776,7 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  bf16x8 qf[kQkSteps];
+  bf16x8 qf[kQk];
   // S^T(tile) in one piece (the prologue's first tile)
   auto qk_tile = [&](uint32_t stage, floatx16& s) __attribute__((always_inline)) {
     const uint32_t kst = kbase + stage, rst = rbase + stage;
@@ -770,9 +784,9 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
 #pragma unroll
     for (int c = 0; c < kQkDepth; ++c) qa[c] = qk_operand(kst, rst, c);
 #pragma unroll
-    for (int c = 0; c < kQkSteps; ++c) {
+    for (int c = 0; c < kQk; ++c) {
       const bf16x8 cur = qa[c % kQkDepth];
-      if (c + kQkDepth < kQkSteps) qa[c % kQkDepth] = qk_operand(kst, rst, c + kQkDepth);
+      if (c + kQkDepth < kQk) qa[c % kQkDepth] = qk_operand(kst, rst, c + kQkDepth);
       if (c == 0)
         mfma_qk_first(s, cur, qf[0]);
       else
@@ -851,9 +865,9 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   // One tile interval (tile i: P.V; tile i + 1: S^T and softmax), with the LDS reads of the two
   // kinds of MFMA spread over the whole interval (S^T operands at full LDS rate and the P.V
   // transpose reads together need about as many LDS clocks as the MFMAs take):
-  //   A. the 36 S^T(i + 1) steps, each followed by one P.V(i) MFMA of key half 0 (32 of them),
-  //      with the DMA of a later tile issued in five pieces between them (INT8: and the
-  //      dequantisation of tile i + 2);
+  //   A. the 36 (without rope channels 32) S^T(i + 1) steps, each followed by one P.V(i) MFMA
+  //      of key half 0 (32 of them), with the DMA of a later tile issued in five pieces between
+  //      them (INT8: and the dequantisation of tile i + 2);
   //   B. the 32 P.V(i) MFMAs of key half 1 with the softmax of tile i + 1 between them;
   //   C. an O rescale when tile i + 1 moved the running max (rare), after the P.V MFMAs, which
   //      still use the old max;
@@ -889,14 +903,14 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
       __builtin_amdgcn_sched_barrier(0);
       // part A: S^T step c, then P.V MFMA c of key half 0 (u = c / 2, hi for even c, lo for odd)
 #pragma unroll
-      for (int c = 0; c < kQkSteps; ++c) {
+      for (int c = 0; c < kQk; ++c) {
         const bf16x8 cur = qa[c % kQkDepth];
-        if (c + kQkDepth < kQkSteps) qa[c % kQkDepth] = qk_operand(kst, rst, c + kQkDepth);
+        if (c + kQkDepth < kQk) qa[c % kQkDepth] = qk_operand(kst, rst, c + kQkDepth);
         if (c == 0)
           mfma_qk_first(s_next, cur, qf[0]);
-        else if (c + 1 == kQkSteps)
+        else if (c + 1 == kQk)
           mfma_qk_last(s_next, cur, qf[c]);
-        else if (c % 7 == 5)
+        else if (c % kPieceStride == 5)
           mfma_qk_pad(s_next, cur, qf[c]);  // follows the conditional DMA piece of step c - 1
         else
           mfma_qk(s_next, cur, qf[c]);
@@ -911,20 +925,23 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
           }
         }
         if constexpr (kInt8) {
-          // part m's codes are read at step 6 + 8m and converted a quarter at a time at steps
-          // 8 + 8m .. 11 + 8m
+          // part m's codes are read at step 6 + kDqStride m and converted a quarter at a time at
+          // steps 8 + kDqStride m .. 11 + kDqStride m
           if (c == 6) {
             // tile i + 2's codes and scales have landed once at most its rope instruction (its
-            // last) and this interval's first piece (one instruction, step 4) are in flight
+            // last, if any) and this interval's first piece (one instruction, step 4) are in
+            // flight
             if (do_dma)
-              wait_vmcnt<2>();
+              wait_vmcnt<kRopeW ? 2 : 1>();
             else
-              wait_vmcnt<1>();
+              wait_vmcnt<kRopeW ? 1 : 0>();
           }
-          if (c >= 6 && (c - 6) % 8 == 0) dq_part = dq_load(ti + 2, (c - 6) / 8);
-          if (c >= 8 && (c - 8) % 8 < 4) dq_quarter((c - 8) % 8, dq_part, dq_out);
+          if (c >= 6 && (c - 6) % kDqStride == 0 && (c - 6) / kDqStride < 4)
+            dq_part = dq_load(ti + 2, (c - 6) / kDqStride);
+          if (c >= 8 && (c - 8) % kDqStride < 4 && (c - 8) / kDqStride < 4)
+            dq_quarter((c - 8) % kDqStride, dq_part, dq_out);
         }
-        if (do_dma && c % 7 == 4) issue_piece(ti + 3, row_dma, c / 7);
+        if (do_dma && c % kPieceStride == 4) issue_piece(ti + 3, row_dma, c / kPieceStride);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -1024,14 +1041,14 @@ __global__ void __launch_bounds__(kThreads, 1) sfa_attention_kernel(const Kernel
   {
     const uint32_t keep = head_ok ? 0xffffffffu : 0u;
 #pragma unroll
-    for (int c = 0; c < kQkSteps; ++c) {
+    for (int c = 0; c < kQk; ++c) {
       const uint4 v = {(qv[c].x ^ q_sign) & keep, (qv[c].y ^ q_sign) & keep, (qv[c].z ^ q_sign) & keep,
                        (qv[c].w ^ q_sign) & keep};
       qf[c] = __builtin_bit_cast(bf16x8, v);
     }
   }
 #pragma unroll
-  for (int c = 0; c < kQkSteps; ++c) asm volatile("" : "+v"(qf[c]));
+  for (int c = 0; c < kQk; ++c) asm volatile("" : "+v"(qf[c]));
 
   if (ntiles > 0) {
     if constexpr (!kInt8) {
@@ -1366,7 +1383,7 @@ __global__ void __launch_bounds__(256) sfa_resolve_kernel(const ResolveArgs a) {
 
 }  // namespace
 
-hipError_t launch_attention(const KernelArgs& a, bool int8_cache, bool window_slots, hipStream_t stream) {
+hipError_t launch_attention(const KernelArgs& a, bool int8_cache, bool window_slots, bool rope, hipStream_t stream) {
   const dim3 grid((unsigned)(a.n_tokens * a.n_splits * a.head_groups));
   const dim3 block(kThreads);
   KernelArgs copy = a;
@@ -1375,16 +1392,22 @@ hipError_t launch_attention(const KernelArgs& a, bool int8_cache, bool window_sl
   // than 4 Mi rows (4 GiB of bf16 nope)
   const bool buf = a.num_rows < (int64_t{1} << 22);
   const void* fn;
-  if (window_slots)
-    fn = int8_cache ? (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<true, true, true>)
-                           : reinterpret_cast<const void*>(&sfa_attention_kernel<true, false, true>))
-                    : (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<false, true, true>)
-                           : reinterpret_cast<const void*>(&sfa_attention_kernel<false, false, true>));
+  // rows without rope channels come only through the window variants
+  if (window_slots && !rope)
+    fn = int8_cache ? (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<true, true, true, 0>)
+                           : reinterpret_cast<const void*>(&sfa_attention_kernel<true, false, true, 0>))
+                    : (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<false, true, true, 0>)
+                           : reinterpret_cast<const void*>(&sfa_attention_kernel<false, false, true, 0>));
+  else if (window_slots)
+    fn = int8_cache ? (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<true, true, true, kRope>)
+                           : reinterpret_cast<const void*>(&sfa_attention_kernel<true, false, true, kRope>))
+                    : (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<false, true, true, kRope>)
+                           : reinterpret_cast<const void*>(&sfa_attention_kernel<false, false, true, kRope>));
   else
-    fn = int8_cache ? (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<true, true, false>)
-                           : reinterpret_cast<const void*>(&sfa_attention_kernel<true, false, false>))
-                    : (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<false, true, false>)
-                           : reinterpret_cast<const void*>(&sfa_attention_kernel<false, false, false>));
+    fn = int8_cache ? (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<true, true, false, kRope>)
+                           : reinterpret_cast<const void*>(&sfa_attention_kernel<true, false, false, kRope>))
+                    : (buf ? reinterpret_cast<const void*>(&sfa_attention_kernel<false, true, false, kRope>)
+                           : reinterpret_cast<const void*>(&sfa_attention_kernel<false, false, false, kRope>));
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

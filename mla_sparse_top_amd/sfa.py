@@ -459,11 +459,17 @@ def _marshal_window(query_nope, query_rope, key_nope, key_rope, k_nope_scales, c
         raise ValueError("tensors must live on a GPU device")
     t_tokens = batch * s1
     n_q = query_nope.shape[0] // t_tokens if t_tokens else 0
-    rows = key_rope.shape[0]
+    # query_rope and key_rope both None: 512-wide rows with the rotary channels inside (rope_dim 0)
+    if (query_rope is None) != (key_rope is None):
+        raise ValueError("query_rope and key_rope must both be given (512 + 64 channels) or both be None "
+                         "(512-wide rows)")
+    rope_dim = 0 if key_rope is None else ROPE_DIM
+    rows = key_nope.shape[0]
     _check(query_nope, "query_nope", (torch.bfloat16,), (t_tokens * n_q, KV_LORA_RANK), dev)
-    _check(query_rope, "query_rope", (torch.bfloat16,), (t_tokens * n_q, ROPE_DIM), dev)
     _check(key_nope, "key_nope", (torch.bfloat16, torch.int8), (rows, KV_LORA_RANK), dev)
-    _check(key_rope, "key_rope", (torch.bfloat16,), (rows, ROPE_DIM), dev)
+    if rope_dim:
+        _check(query_rope, "query_rope", (torch.bfloat16,), (t_tokens * n_q, ROPE_DIM), dev)
+        _check(key_rope, "key_rope", (torch.bfloat16,), (rows, ROPE_DIM), dev)
     int8 = key_nope.dtype == torch.int8
     if int8:
         if k_nope_scales is None:
@@ -476,7 +482,7 @@ def _marshal_window(query_nope, query_rope, key_nope, key_rope, k_nope_scales, c
         _check(cmp_indices, "cmp_indices", (torch.int32,), (t_tokens, topk_cmp), dev)
         _check(block_table_cmp, "block_table_cmp", (torch.int32,), None, dev)
         _check(cmp_len, "cmp_len", (torch.int32,), (batch,), dev)
-    dims = SfaWindowDims(batch, s1, n_q, 1, KV_LORA_RANK, ROPE_DIM, BLOCK_SIZE, int(window), topk_cmp,
+    dims = SfaWindowDims(batch, s1, n_q, 1, KV_LORA_RANK, rope_dim, BLOCK_SIZE, int(window), topk_cmp,
                          block_table_ori.shape[1], block_table_cmp.shape[1] if topk_cmp else 0, rows,
                          KV_INT8 if int8 else KV_BF16, num_splits)
     if out is None:
@@ -500,7 +506,8 @@ def _marshal_window(query_nope, query_rope, key_nope, key_rope, k_nope_scales, c
 
 
 def window_decode(*tensors, **kw):
-    """sfa_window_decode (SWA / CFA / SCFA): returns out (batch, s1, n_q, 512) bf16."""
+    """sfa_window_decode (SWA / CFA / SCFA): returns out (batch, s1, n_q, 512) bf16. With
+    query_rope and key_rope None the rows are 512 wide with the rotary channels inside them."""
     args, out, _keep = _marshal_window(*tensors, **kw)
     st = _lib.sfa_window_decode(*args)
     if st != 0:
@@ -522,11 +529,12 @@ def window_to_device(inp, device="cuda"):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
 
     cmp = inp.cmp_indices is not None
+    rope = inp.key_rope.shape[1] > 0  # zero-width rope arrays: 512-wide rows
     return {
         "query_nope": bf16(inp.query_nope),
-        "query_rope": bf16(inp.query_rope),
+        "query_rope": bf16(inp.query_rope) if rope else None,
         "key_nope": bf16(inp.key_nope) if inp.kv_dtype == "bf16" else torch.from_numpy(inp.key_nope).to(device),
-        "key_rope": bf16(inp.key_rope),
+        "key_rope": bf16(inp.key_rope) if rope else None,
         "k_nope_scales": None if inp.k_nope_scales is None else torch.from_numpy(inp.k_nope_scales).to(device),
         "cmp_indices": torch.from_numpy(inp.cmp_indices).to(device) if cmp else None,
         "block_table_ori": torch.from_numpy(inp.block_table_ori).to(device),
@@ -757,8 +765,8 @@ def _marshal_compress(kv, score, ape, gamma, eps, rope_cos, rope_sin, start_pos,
         raise ValueError("tensors must live on a GPU device")
     t_tokens = batch * s1
     c = kv.shape[1]
-    if c not in (COMPRESS_CHANNELS, 128):
-        raise ValueError("kv must have 576 or 128 channels")
+    if c not in (COMPRESS_CHANNELS, KV_LORA_RANK, 128):
+        raise ValueError("kv must have 576, 512 or 128 channels")
     ratio = ape.shape[0]
     n_pos = rope_cos.shape[0]
     rows = key_nope.shape[0]
@@ -798,7 +806,7 @@ def compress(kv, score, ape, gamma, eps, rope_cos, rope_sin, start_pos, kv_state
              key_nope, key_rope, *, batch, s1, rotate=False, stream=None):
     """sfa_compress: refreshes kv_state / score_state in place and writes the compressed entries
     of the windows the new tokens close into key_nope / key_rope (576 channels) or key_nope alone
-    (128 channels; key_rope may be None). Returns key_nope."""
+    (512 or 128 channels; key_rope may be None). Returns key_nope."""
     args, _keep = _marshal_compress(kv, score, ape, gamma, eps, rope_cos, rope_sin, start_pos, kv_state, score_state,
                                     block_table_cmp, key_nope, key_rope, batch=batch, s1=s1, rotate=rotate,
                                     stream=stream)

@@ -89,7 +89,8 @@ def test_workspace_size_formula():
 
 
 @pytest.mark.parametrize("field,value", [
-    ("n_kv", 2), ("kv_lora_rank", 256), ("rope_dim", 32), ("block_size", 64), ("n_q", 8), ("n_q", 24),
+    ("n_kv", 2), ("kv_lora_rank", 256), ("rope_dim", 32), ("rope_dim", 0), ("block_size", 64), ("n_q", 8),
+    ("n_q", 24),
     ("n_q", 144), ("topk", 0), ("topk", 40000), ("batch", -1), ("s1", -2), ("max_blocks_per_batch", 0),
     ("num_cache_rows", -1), ("num_splits", 17), ("num_splits", -1), ("kv_dtype", 3),
 ])
@@ -303,6 +304,18 @@ def test_window_validation():
     assert _wcall(_wdims(block_size=64)) == -2               # the attention's own dims are checked too
     assert _wcall(_wdims(window=40000)) == -2                # above the attention's top-k limit
     assert _wcall(_wdims(batch=0, num_splits=2), ws_bytes=need) == 0  # nothing to do, nothing queued
+    # rope_dim 0 (512-wide rows): accepted by the window variants only; query_rope and key_rope
+    # are then not needed (the null pointers pass, and the missing workspace is what fails)
+    d0 = _wdims(rope_dim=0, num_splits=2)
+    assert sfa.window_workspace_size(d0) == need
+    assert _wcall(d0, qr=None, kr=None, ws=None) == -4
+    assert _wcall(d0, qr=0x200004, kr=0x20000004, ws=None) == -4   # not read, so not checked
+    assert _wcall(d0, qn=None, qr=None, kr=None, ws=None) == -1
+    assert _wcall(d0, out=0x200000, qr=None, kr=None, ws=None) == -4  # no rope array to overlap
+    assert _wcall(_wdims(rope_dim=0, batch=0, num_splits=2), qr=None, kr=None, ws_bytes=need) == 0
+    assert _wcall(_wdims(rope_dim=32)) == -2
+    assert _wcall(d, qr=None) == -1                          # with rope channels both are needed
+    assert _wcall(d, kr=None) == -1
 
 
 def _cdims(**kw):
@@ -334,7 +347,7 @@ def test_compress_validation():
     assert _cmp(d, ss=0x4000000 + 16) == -6              # score state inside kv state
     assert _cmp(d, kn=0x3400000) == -6                   # pool over start_pos
     assert _cmp(d, kr=0x10000000 + 1024) == -6           # rope rows inside nope rows
-    for field, value in (("channels", 512), ("block_size", 64), ("ratio", 0), ("ratio", 1025), ("batch", -1),
+    for field, value in (("channels", 256), ("channels", 575), ("block_size", 64), ("ratio", 0), ("ratio", 1025), ("batch", -1),
                          ("s1", -1), ("max_blocks", 0), ("rope_positions", -1), ("num_cache_rows", -1)):
         assert _cmp(_cdims(**{field: value})) == -2, field
     assert _cmp(d, eps=-1.0) == -2
@@ -350,6 +363,11 @@ def test_compress_validation():
     c128 = _cdims(channels=128, rotate=1)
     assert _cmp(c128, kn=None) == -1
     assert _cmp(c128, ks=0x1000000 + 1024) == -6          # state overlaps kv (2 KB at 128 channels)
+    # 512 channels (rotary channels inside the row): whole to key_nope_2d, no Hadamard branch
+    c512 = _cdims(channels=512)
+    assert _cmp(c512, kn=None) == -1
+    assert _cmp(_cdims(channels=512, rotate=1)) == -2
+    assert _cmp(_cdims(channels=512, s1=0), kr=None) == 0
 
 
 def test_noalloc_rejects_calls_beyond_its_scratch():

@@ -243,3 +243,48 @@ def test_index_keys_ratio_one_peaky(sfa_lib):
     inp = W.compress_generate(batch=4, s1=1, ratio=128, start_pos=[127 + 128 * k for k in range(4)],
                               rope_positions=1024, max_blocks=2, seed=15, score_scale=4.0, channels=128, rotate=True)
     assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 4
+
+
+# ---- 512-channel rows (the DeepSeek-V4 D = 512 layout: the rotary channels inside the row) ----
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_d512_c128a_full_size(sfa_lib, seed):
+    """The page's c128a case at the decode step: ratio 128, every sequence closes a window."""
+    inp = W.compress_c128a(seed=seed)
+    assert inp.channels == 512 and inp.key_rope is None
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 64
+
+
+def test_d512_windows_and_ragged_positions(sfa_lib):
+    inp = W.compress_generate(batch=3, s1=7, ratio=4, start_pos=[5, -2, 60], rope_positions=64, max_blocks=2,
+                              seed=25, channels=512)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 2 + 1 + 1
+
+
+def test_d512_compressed_entry_feeds_scfa(sfa_lib):
+    """The 512-wide chain: the compressor writes each sequence's newest entry into a 512-wide
+    pool, and SCFA on 512-wide rows reads it through the token's compressed list."""
+    import torch
+
+    import oracle.window_oracle as WO
+
+    ratio = 4
+    win = W.window_generate(batch=2, s1=2, n_q=32, ori_lens=[512, 300], window=64, ratio=ratio, cmp_mode="sparse",
+                            topk_cmp=24, seed=26, rope_dim=0)
+    for b in range(win.batch):
+        win.cmp_indices[b * win.s1 + 1, 0] = int(win.cmp_len[b]) - 1   # closed by position ori_len - 1
+    cmp = W.compress_generate(batch=2, s1=2, ratio=ratio, start_pos=[int(v) - 2 for v in win.ori_len],
+                              rope_positions=1024, max_blocks=win.block_table_cmp.shape[1], seed=27, channels=512)
+    cmp.block_table_cmp, cmp.key_nope = win.block_table_cmp, win.key_nope
+    dw = sfa_lib.window_to_device(win)
+    dc = sfa_lib.compress_to_device(cmp)
+    dc["key_nope"] = dw["key_nope"]
+    sfa_lib.run_compress(cmp, dc)
+    out = sfa_lib.run_window(win, dw)
+    torch.cuda.synchronize()
+    got = _host(dc)
+    assert _assert_matches(cmp, got) == 2
+    win.key_nope = got[2]
+    ref = WO.window_attention(win)
+    rep = O.allclose_report(out.float().cpu().numpy().astype(np.float64).reshape(ref.shape), ref)
+    assert rep["fails"] == 0, rep
