@@ -16,8 +16,11 @@
 // How: one workgroup per sequence, each thread owning a few channels, so every per-channel step
 // (refresh, online softmax over the slots, scaling) runs in registers with no communication;
 // the RMS needs one block reduction, RoPE pairs are adjacent lanes of the last wave (one xor
-// shuffle), and the Hadamard transform's butterflies are xor shuffles across one wave. The
-// tokens of a sequence are taken in order. A slot written earlier in the same call is read from
+// shuffle), and the Hadamard transform's butterflies are xor shuffles across one wave. With a
+// long window (ratio 10 and up) the workgroup holds several such channel groups, each taking a
+// share of the slots with its own running max, sum and weighted sum, merged through LDS, so
+// that the slot loads of a pooling go out several groups at a time. The tokens of a sequence
+// are taken in order. A slot written earlier in the same call is read from
 // the token's inputs rather than from the state, and only each slot's last writer stores it, so
 // no address is both written and read in one call; every load can therefore be issued early, and
 // the loads of a chunk of tokens, and of a batch of slots, go out together. The work is a few
@@ -49,17 +52,22 @@ template <int kC>
 constexpr int compress_threads() {
   return kC == 576 ? 192 : kC == 512 ? 128 : 64;
 }
-template <int kC, bool kRotate>
-__global__ void __launch_bounds__(compress_threads<kC>()) compress_kernel(const CompressArgs a) {
+// kSplit channel groups of compress_threads<kC>() threads each: group g pools the slot batches
+// g, g + kSplit, g + 2 kSplit, ... (all groups then hold the same merged row; group 0 stores).
+template <int kC, bool kRotate, int kSplit>
+__global__ void __launch_bounds__(compress_threads<kC>() * kSplit) compress_kernel(const CompressArgs a) {
   static_assert(!kRotate || kC == 128, "the Hadamard transform is built for 128 channels");
-  constexpr int kT = compress_threads<kC>();  // threads
+  constexpr int kT = compress_threads<kC>();  // threads of a channel group
   constexpr int kPer = kC / kT;             // channels per thread
   constexpr int kWaves = kT / 64;
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int sg = threadIdx.x / kT;          // channel group
+  const int tid = threadIdx.x - sg * kT;    // thread within the group
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  __shared__ float part[kWaves];
+  __shared__ float part[kSplit][kWaves];
+  // the groups' running max, sum and weighted sum per channel, for the merge
+  __shared__ float mrg[kSplit > 1 ? 3 * kSplit * kC : 1];
 
   const int64_t p0 = a.start_pos[b];
   // tokens with 0 <= p < rope_positions: a contiguous range of s
@@ -71,7 +79,7 @@ __global__ void __launch_bounds__(compress_threads<kC>()) compress_kernel(const 
   // pooling reads are loaded kSlotBatch at a time, so that a call waits on few memory round
   // trips (each load's address depends on nothing loaded).
   constexpr int kTokChunk = 4;
-  constexpr int kSlotBatch = 8;
+  constexpr int kSlotBatch = kSplit > 1 ? 4 : 8;  // the groups supply the rest of the parallelism
   for (int64_t s0 = s_lo; s0 < s_hi; s0 += kTokChunk) {
     float kv_c[kTokChunk][kPer], sc_c[kTokChunk][kPer];
 #pragma unroll
@@ -94,7 +102,7 @@ __global__ void __launch_bounds__(compress_threads<kC>()) compress_kernel(const 
       const int slot = p % a.ratio;
       const float* kv_t = kv_c[j];
       const float* sc_t = sc_c[j];
-      if (s + a.ratio >= s_hi) {  // no later token of this call refreshes this slot
+      if (sg == 0 && s + a.ratio >= s_hi) {  // no later token of this call refreshes this slot
         const int64_t o = ((int64_t)b * a.ratio + slot) * C;
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
@@ -104,16 +112,18 @@ __global__ void __launch_bounds__(compress_threads<kC>()) compress_kernel(const 
       }
       if ((p + 1) % a.ratio != 0) continue;  // uniform over the workgroup
 
-      // ---- pool: online softmax over the slots, per channel
+      // ---- pool: online softmax over the slots, per channel (group 0 starts from the token's
+      // own slot, the others from nothing)
       float m[kPer], l[kPer], acc[kPer];
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        m[k] = sc_t[k];
-        l[k] = 1.0f;
-        acc[k] = kv_t[k];
+        m[k] = sg == 0 ? sc_t[k] : -INFINITY;
+        l[k] = sg == 0 ? 1.0f : 0.0f;
+        acc[k] = sg == 0 ? kv_t[k] : 0.0f;
       }
-      // the other slots r = slot + 1 .. slot + ratio - 1 (mod ratio), kSlotBatch at a time
-      for (int r0 = 1; r0 < a.ratio; r0 += kSlotBatch) {
+      // the other slots r = slot + 1 .. slot + ratio - 1 (mod ratio), kSlotBatch at a time, the
+      // batches dealt to the groups in turn
+      for (int r0 = 1 + sg * kSlotBatch; r0 < a.ratio; r0 += kSlotBatch * kSplit) {
         float kr[kSlotBatch][kPer], sr[kSlotBatch][kPer];
 #pragma unroll
         for (int i = 0; i < kSlotBatch; ++i) {
@@ -151,6 +161,34 @@ __global__ void __launch_bounds__(compress_threads<kC>()) compress_kernel(const 
           }
         }
       }
+      if constexpr (kSplit > 1) {
+        // merge the groups' partial poolings in group order: M = max m_g, L = sum l_g 2^.., A = ..
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          const int c = tid + k * kT;
+          mrg[(0 * kSplit + sg) * kC + c] = m[k];
+          mrg[(1 * kSplit + sg) * kC + c] = l[k];
+          mrg[(2 * kSplit + sg) * kC + c] = acc[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          const int c = tid + k * kT;
+          float mx = mrg[c];
+#pragma unroll 4
+          for (int g = 1; g < kSplit; ++g) mx = fmaxf(mx, mrg[g * kC + c]);
+          float lt = 0.0f, at = 0.0f;
+#pragma unroll 4
+          for (int g = 0; g < kSplit; ++g) {
+            const float e = expf(mrg[g * kC + c] - mx);  // 0 for a group that saw no slot
+            lt = fmaf(mrg[(kSplit + g) * kC + c], e, lt);
+            at = fmaf(mrg[(2 * kSplit + g) * kC + c], e, at);
+          }
+          l[k] = lt;
+          acc[k] = at;
+        }
+        __syncthreads();  // mrg is rewritten by the next entry
+      }
       float x[kPer], ss = 0.0f;
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
@@ -163,11 +201,11 @@ __global__ void __launch_bounds__(compress_threads<kC>()) compress_kernel(const 
       for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, 64);
       float total = ss;
       if (kWaves > 1) {
-        if (lane == 0) part[wave] = ss;
+        if (lane == 0) part[sg][wave] = ss;
         __syncthreads();
         total = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) total += part[w];
+        for (int w = 0; w < kWaves; ++w) total += part[sg][w];
         __syncthreads();  // part is rewritten by the next entry
       }
       const float inv = 1.0f / sqrtf(total / (float)kC + a.eps);
@@ -202,7 +240,8 @@ __global__ void __launch_bounds__(compress_threads<kC>()) compress_kernel(const 
         for (int k = 0; k < 2; ++k) y[k] *= 0.08838834764831845f;  // 1/sqrt(128)
       }
 
-      // ---- store at the entry's row
+      // ---- store at the entry's row (group 0)
+      if (sg != 0) continue;
       const int64_t c_entry = (p + 1) / a.ratio - 1;
       if (c_entry >= (int64_t)a.mb * 128) continue;
       const int blk = a.block_table[(int64_t)b * a.mb + (c_entry >> 7)];
@@ -226,15 +265,26 @@ __global__ void __launch_bounds__(compress_threads<kC>()) compress_kernel(const 
 
 }  // namespace
 
+template <int kC, bool kRotate>
+void launch_one(const CompressArgs& a, hipStream_t stream) {
+  // slot groups for a long window: up to 8 channel groups, within 1024 threads
+  constexpr int kT = compress_threads<kC>();
+  constexpr int kMaxSplit = kT <= 128 ? 8 : 4;
+  if (a.ratio >= 10)
+    hipLaunchKernelGGL((compress_kernel<kC, kRotate, kMaxSplit>), dim3(a.batch), dim3(kT * kMaxSplit), 0, stream, a);
+  else
+    hipLaunchKernelGGL((compress_kernel<kC, kRotate, 1>), dim3(a.batch), dim3(kT), 0, stream, a);
+}
+
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
   if (a.channels == 576)
-    hipLaunchKernelGGL((compress_kernel<576, false>), dim3(a.batch), dim3(192), 0, stream, a);
+    launch_one<576, false>(a, stream);
   else if (a.channels == 512)
-    hipLaunchKernelGGL((compress_kernel<512, false>), dim3(a.batch), dim3(128), 0, stream, a);
+    launch_one<512, false>(a, stream);
   else if (a.rotate)
-    hipLaunchKernelGGL((compress_kernel<128, true>), dim3(a.batch), dim3(64), 0, stream, a);
+    launch_one<128, true>(a, stream);
   else
-    hipLaunchKernelGGL((compress_kernel<128, false>), dim3(a.batch), dim3(64), 0, stream, a);
+    launch_one<128, false>(a, stream);
   return hipGetLastError();
 }
 

@@ -288,3 +288,30 @@ def test_d512_compressed_entry_feeds_scfa(sfa_lib):
     ref = WO.window_attention(win)
     rep = O.allclose_report(out.float().cpu().numpy().astype(np.float64).reshape(ref.shape), ref)
     assert rep["fails"] == 0, rep
+
+
+# ---- long windows (ratio >= 10): the slots split over channel groups, merged through LDS ----
+
+@pytest.mark.parametrize("channels", [576, 512, 128])
+def test_long_window_groups_without_slots(sfa_lib, channels):
+    """Ratio 16: 15 other slots in batches of 4 leave some of the channel groups without a slot
+    (their running max stays -inf and they must add nothing to the merge)."""
+    inp = W.compress_generate(batch=5, s1=1, ratio=16, start_pos=[15 + 16 * k for k in range(5)],
+                              rope_positions=256, max_blocks=2, seed=31, score_scale=3.0, channels=channels,
+                              rotate=channels == 128)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 5
+
+
+@pytest.mark.parametrize("channels", [576, 512])
+def test_long_window_two_entries_in_one_call(sfa_lib, channels):
+    """Ratio 12, twenty tokens (positions 5..24): entries 0 and 1 close in one call; the second
+    pools slots that earlier tokens of the same call refreshed, taken from their inputs."""
+    inp = W.compress_generate(batch=3, s1=20, ratio=12, start_pos=[5, 5, 5], rope_positions=64, max_blocks=2,
+                              seed=32, channels=channels)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 6
+
+
+def test_long_window_index_keys_rotated(sfa_lib):
+    inp = W.compress_generate(batch=8, s1=1, ratio=128, start_pos=[127 + 128 * k for k in range(8)],
+                              rope_positions=2048, max_blocks=2, seed=33, score_scale=4.0, channels=128, rotate=True)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 8
