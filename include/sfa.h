@@ -195,9 +195,13 @@ int sfa_resolve_rows(const sfa_dims* dims, const int32_t* topk_indices, const in
  *   and an all-zero group stores scale 0 and codes 0. The attention's dequant chain then reads
  *   code * scale rounded to bf16.
  *
- *   dims           batch, s1, kv_lora_rank (512), rope_dim (64), block_size (128),
+ *   dims           batch, s1, kv_lora_rank (512), rope_dim (64, or 0), block_size (128),
  *                  max_blocks_per_batch, num_cache_rows and kv_dtype are used; n_q, n_kv, topk
- *                  and num_splits are ignored. T = batch * s1 may be up to 2^26.
+ *                  and num_splits are ignored. T = batch * s1 may be up to 2^26. rope_dim 0 is
+ *                  the 512-wide row layout sfa_window_decode reads with rope_dim 0 (rotary
+ *                  channels inside the row): there is no rope part, the 512 channels are new_nope
+ *                  (quantised whole for an INT8 cache), and new_rope and key_rope_2d are not used
+ *                  (they may be NULL).
  *   new_nope       bf16  (T, 512)
  *   new_rope       bf16  (T, 64)
  *   positions      int32 (T)

@@ -6,7 +6,8 @@
 // through block_table. For an INT8 cache the nope part is quantised in groups of 128 elements:
 // scale = absmax / 127 in fp32, code = round-half-even(x / scale) clamped to [-128, 127], with
 // scale 0 and codes 0 for an all-zero group. The rope part (and a bf16 cache's nope part) is
-// copied.
+// copied. Rows of the 512-wide layout ("NPU DeepSeek-V4 model PyPTO fused-operator optimisation",
+// D = 512: the rotary channels inside the row) have no rope part; the row is the 512 channels.
 //
 // How: the operation is a streaming copy with a little arithmetic, bound by HBM. A wave writes
 // four new tokens: lane L holds the 16-byte chunk L of a 1 KB nope row, so a 128-element group
@@ -44,7 +45,7 @@ __device__ __forceinline__ uint32_t code_byte(float x, float scale) {
   return (uint32_t)(int32_t)q & 0xffu;
 }
 
-template <bool kInt8>
+template <bool kInt8, bool kRope>
 __global__ void __launch_bounds__(kCwWaves * 64) cache_write_kernel(const CacheWriteArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -63,7 +64,7 @@ __global__ void __launch_bounds__(kCwWaves * 64) cache_write_kernel(const CacheW
   for (int i = 0; i < kCwRowsPerWave; ++i) {
     const int64_t t = min(t0 + i, a.n_tokens - 1);
     nv[i] = reinterpret_cast<const u32x4*>(a.new_nope + t * 512)[lane];
-    rv[i] = reinterpret_cast<const u32x4*>(a.new_rope + t * 64)[lane & 7];
+    if constexpr (kRope) rv[i] = reinterpret_cast<const u32x4*>(a.new_rope + t * 64)[lane & 7];
   }
   const bool pos_ok = pos >= 0 && pos < a.mb * 128;
   const int blk = pos_ok ? a.block_table[(int64_t)(ti / a.s1) * a.mb + (pos >> 7)] : -1;
@@ -77,7 +78,7 @@ __global__ void __launch_bounds__(kCwWaves * 64) cache_write_kernel(const CacheW
   for (int i = 0; i < kCwRowsPerWave; ++i) {
     if (row[i] < 0) continue;
     const int64_t r = row[i];
-    if (lane < 8) reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.key_rope) + r * kRopeBytes)[lane] = rv[i];
+    if (kRope && lane < 8) reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.key_rope) + r * kRopeBytes)[lane] = rv[i];
     if constexpr (!kInt8) {
       reinterpret_cast<u32x4*>(static_cast<char*>(a.key_nope) + r * kNopeBytes)[lane] = nv[i];
     } else {
@@ -111,12 +112,17 @@ __global__ void __launch_bounds__(kCwWaves * 64) cache_write_kernel(const CacheW
 
 }  // namespace
 
-hipError_t launch_cache_write(const CacheWriteArgs& a, bool int8_cache, hipStream_t stream) {
+hipError_t launch_cache_write(const CacheWriteArgs& a, bool int8_cache, bool rope, hipStream_t stream) {
   const int grid = (a.n_tokens + kCwTokensPerWg - 1) / kCwTokensPerWg;
-  if (int8_cache)
-    hipLaunchKernelGGL(cache_write_kernel<true>, dim3(grid), dim3(kCwWaves * 64), 0, stream, a);
+  const dim3 block(kCwWaves * 64);
+  if (int8_cache && rope)
+    hipLaunchKernelGGL((cache_write_kernel<true, true>), dim3(grid), block, 0, stream, a);
+  else if (int8_cache)
+    hipLaunchKernelGGL((cache_write_kernel<true, false>), dim3(grid), block, 0, stream, a);
+  else if (rope)
+    hipLaunchKernelGGL((cache_write_kernel<false, true>), dim3(grid), block, 0, stream, a);
   else
-    hipLaunchKernelGGL(cache_write_kernel<false>, dim3(grid), dim3(kCwWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((cache_write_kernel<false, false>), dim3(grid), block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -408,22 +408,29 @@ def _marshal_cache_write(new_nope, new_rope, positions, block_table, key_nope, k
     if dev.type != "cuda":
         raise ValueError("tensors must live on a GPU device")
     t_tokens = batch * s1
-    rows = key_rope.shape[0]
+    # new_rope and key_rope both None: 512-wide rows with the rotary channels inside (rope_dim 0)
+    if (new_rope is None) != (key_rope is None):
+        raise ValueError("new_rope and key_rope must both be given (512 + 64 channels) or both be None "
+                         "(512-wide rows)")
+    rope_dim = 0 if key_rope is None else ROPE_DIM
+    rows = key_nope.shape[0]
     _check(new_nope, "new_nope", (torch.bfloat16,), (t_tokens, KV_LORA_RANK), dev)
-    _check(new_rope, "new_rope", (torch.bfloat16,), (t_tokens, ROPE_DIM), dev)
+    if rope_dim:
+        _check(new_rope, "new_rope", (torch.bfloat16,), (t_tokens, ROPE_DIM), dev)
     _check(positions, "positions", (torch.int32,), (t_tokens,), dev)
     _check(block_table, "block_table", (torch.int32,), None, dev)
     if block_table.dim() != 2 or block_table.shape[0] != batch:
         raise ValueError("block_table must be (batch, max_blocks_per_batch)")
     _check(key_nope, "key_nope", (torch.bfloat16, torch.int8), (rows, KV_LORA_RANK), dev)
-    _check(key_rope, "key_rope", (torch.bfloat16,), (rows, ROPE_DIM), dev)
+    if rope_dim:
+        _check(key_rope, "key_rope", (torch.bfloat16,), (rows, ROPE_DIM), dev)
     int8 = key_nope.dtype == torch.int8
     if int8:
         if k_nope_scales is None:
             raise ValueError("an int8 key_nope needs k_nope_scales")
         _check(k_nope_scales, "k_nope_scales", (torch.float32,), (rows, 4), dev)
     dims = make_dims(batch=batch, s1=s1, n_q=128, topk=1, max_blocks_per_batch=block_table.shape[1],
-                     num_cache_rows=rows, kv_dtype=KV_INT8 if int8 else KV_BF16)
+                     num_cache_rows=rows, kv_dtype=KV_INT8 if int8 else KV_BF16, rope_dim=rope_dim)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     args = (ctypes.byref(dims), _ptr(new_nope), _ptr(new_rope), _ptr(positions), _ptr(block_table), _ptr(key_nope),
@@ -719,13 +726,14 @@ def cache_to_device(inp, device="cuda"):
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
 
+    rope = inp.key_rope.shape[1] > 0  # zero-width rope arrays: 512-wide rows
     return {
         "new_nope": bf16(inp.new_nope),
-        "new_rope": bf16(inp.new_rope),
+        "new_rope": bf16(inp.new_rope) if rope else None,
         "positions": torch.from_numpy(inp.positions).to(device),
         "block_table": torch.from_numpy(inp.block_table).to(device),
         "key_nope": bf16(inp.key_nope) if inp.kv_dtype == "bf16" else torch.from_numpy(inp.key_nope).to(device),
-        "key_rope": bf16(inp.key_rope),
+        "key_rope": bf16(inp.key_rope) if rope else None,
         "k_nope_scales": None if inp.k_nope_scales is None else torch.from_numpy(inp.k_nope_scales).to(device),
     }
 

@@ -454,11 +454,13 @@ class CacheWriteInputs:
 def cache_write_generate(*, batch: int, s1: int, n_pool_blocks: int, max_blocks_per_batch: int,
                          kv_dtype: str = "int8", seed: int = 0, positions: Optional[np.ndarray] = None,
                          block_table: Optional[np.ndarray] = None, value_scale: float = 1.0,
-                         name: str = "") -> CacheWriteInputs:
+                         name: str = "", rope_dim: int = ROPE_DIM) -> CacheWriteInputs:
     """New rows are N(0,1) * value_scale rounded to bf16. Unless given, the block table is a
     random permutation of the pool's blocks (it needs n_pool_blocks >= batch * mb) and each
     batch's s1 tokens take distinct random positions in [0, mb * 128). The existing cache is
-    random bytes (bf16: random bit patterns; INT8: random codes, scales uniform in [0, 1))."""
+    random bytes (bf16: random bit patterns; INT8: random codes, scales uniform in [0, 1)).
+    rope_dim 0: 512-wide rows with the rotary channels inside; the rope arrays are zero-width."""
+    assert rope_dim in (0, ROPE_DIM)
     g = torch.Generator().manual_seed(70_000 + int(seed))
     mb = int(max_blocks_per_batch)
     if block_table is None:
@@ -474,9 +476,10 @@ def cache_write_generate(*, batch: int, s1: int, n_pool_blocks: int, max_blocks_
     for r0 in range(0, t, _ROW_CHUNK):
         r1 = min(t, r0 + _ROW_CHUNK)
         nn[r0:r1] = _bf16_bits(torch.randn(r1 - r0, KV_LORA_RANK, generator=g) * float(value_scale))
-    nr = _normal_bf16(g, t, ROPE_DIM)
+    nr = _normal_bf16(g, t, ROPE_DIM) if rope_dim else np.zeros((t, 0), dtype=np.uint16)
     rows = n_pool_blocks * BLOCK_SIZE
-    kr = torch.randint(0, 1 << 16, (rows, ROPE_DIM), generator=g, dtype=torch.int32).numpy().astype(np.uint16)
+    kr = (torch.randint(0, 1 << 16, (rows, ROPE_DIM), generator=g, dtype=torch.int32).numpy().astype(np.uint16)
+          if rope_dim else np.zeros((rows, 0), dtype=np.uint16))
     if kv_dtype == "int8":
         kn = torch.randint(-128, 128, (rows, KV_LORA_RANK), generator=g, dtype=torch.int8).numpy()
         ks = torch.rand(rows, N_GROUPS, generator=g).numpy()

@@ -25,7 +25,10 @@ Readings (the pages leave them open; each is listed with its reason in the desig
   * a token whose position is negative, at or past max_blocks_per_batch * 128, whose block entry
     is negative, or whose row falls outside the pool is not written (the masking rule of the
     attention's slots, applied to the write);
-  * the rope part and a bf16 cache's nope part are copied bit for bit.
+  * the rope part and a bf16 cache's nope part are copied bit for bit;
+  * rows of the 512-wide layout ("NPU DeepSeek-V4 model PyPTO fused-operator optimisation",
+    D = 512, the rotary channels inside the row) come with zero-width rope arrays: the 512
+    channels are the nope part, quantised or copied as above, and there is nothing else.
 
 Inputs are raw bit patterns (bf16 as uint16), the bytes the GPU path receives. The arithmetic is
 numpy float32, whose division and rounding are IEEE binary32 round-to-nearest-even.

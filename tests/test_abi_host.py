@@ -244,6 +244,12 @@ def test_cache_write_validation():
     # nothing to write: no HIP call
     assert _cw(_dims(**{**cw, "batch": 0})) == 0
     assert _cw(_dims(**{**cw, "num_cache_rows": 0})) == 0
+    # rope_dim 0 (512-wide rows): new_rope and key_rope_2d are not used
+    d0 = _dims(**{**cw, "rope_dim": 0})
+    assert _cw(d0, nn=None, nr=None, kr=None) == -1
+    assert _cw(d0, kn=0x300000 - 1024, nr=None, kr=None) == -6   # cache over positions
+    assert _cw(_dims(**{**cw, "rope_dim": 0, "batch": 0}), nr=None, kr=None) == 0
+    assert _cw(_dims(**{**cw, "rope_dim": 32})) == -2
 
 
 def test_probe_library_is_separate_and_exports_its_entry():

@@ -253,6 +253,28 @@ def test_write_then_attention_reads_back_the_dequantised_row():
     assert np.allclose(out.reshape(4, 512), want[None, :], rtol=0, atol=1e-12)
 
 
+def test_512_wide_rows_match_the_nope_part_of_576_rows():
+    """Zero-width rope arrays (the 512-wide layout): the write of the 512 channels is the nope
+    part of the same write with rope rows beside it, bit for bit, for both cache types."""
+    from mla_sparse_top_amd import workloads as W
+
+    for kv in ("int8", "bf16"):
+        inp = W.cache_write_generate(batch=3, s1=7, n_pool_blocks=9, max_blocks_per_batch=3, kv_dtype=kv, seed=12,
+                                     rope_dim=0)
+        assert inp.new_rope.shape == (21, 0) and inp.key_rope.shape == (9 * 128, 0)
+        n0, r0, s0 = C.cache_write(inp.new_nope, inp.new_rope, inp.positions, inp.block_table, 7, inp.key_nope,
+                                   inp.key_rope, inp.k_nope_scales)
+        rng = np.random.default_rng(13)
+        nr = rng.integers(0, 1 << 16, (21, 64)).astype(np.uint16)
+        kr = rng.integers(0, 1 << 16, (9 * 128, 64)).astype(np.uint16)
+        n1, r1, s1 = C.cache_write(inp.new_nope, nr, inp.positions, inp.block_table, 7, inp.key_nope, kr,
+                                   inp.k_nope_scales)
+        assert r0.shape == (9 * 128, 0) and np.array_equal(n0, n1)
+        if kv == "int8":
+            assert np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
+        assert inp.n_written() == 21 and np.sum(np.any(n0 != inp.key_nope, axis=1)) > 0
+
+
 def test_duplicate_targets_rejected():
     rng = np.random.default_rng(9)
     kn, kr, ks = _pool(rng, 1, False)

@@ -24,7 +24,8 @@ def _run(sfa, inp):
     torch.cuda.synchronize()
     kn = d["key_nope"].cpu()
     kn = kn.numpy() if inp.kv_dtype == "int8" else kn.view(torch.int16).numpy().view(np.uint16)
-    kr = d["key_rope"].cpu().view(torch.int16).numpy().view(np.uint16)
+    kr = (np.zeros((kn.shape[0], 0), dtype=np.uint16) if d["key_rope"] is None
+          else d["key_rope"].cpu().view(torch.int16).numpy().view(np.uint16))
     ks = None if d["k_nope_scales"] is None else d["k_nope_scales"].cpu().numpy()
     return kn, kr, ks
 
@@ -64,10 +65,11 @@ def test_small_ragged_with_masked_tokens(sfa_lib, kv_dtype, seed):
     _assert_same(_run(sfa_lib, inp), _oracle(inp), f"{kv_dtype} seed {seed}")
 
 
+@pytest.mark.parametrize("rope_dim", [64, 0])
 @pytest.mark.parametrize("kv_dtype", ["int8", "bf16"])
-def test_many_tokens_random_positions(sfa_lib, kv_dtype):
+def test_many_tokens_random_positions(sfa_lib, kv_dtype, rope_dim):
     inp = W.cache_write_generate(batch=7, s1=301, n_pool_blocks=64, max_blocks_per_batch=9, kv_dtype=kv_dtype,
-                                 seed=5, value_scale=3.0)
+                                 seed=5, value_scale=3.0, rope_dim=rope_dim)
     _assert_same(_run(sfa_lib, inp), _oracle(inp), kv_dtype)
 
 
@@ -126,4 +128,43 @@ def test_write_then_attention_reads_it(sfa_lib):
     out = sfa_lib.run(base).float().cpu().numpy()
     ref = O.sparse_mla_attention(base)
     rep = O.allclose_report(out, ref)
+    assert rep["fails"] == 0, rep
+
+
+@pytest.mark.parametrize("kv_dtype", ["int8", "bf16"])
+def test_512_wide_rows_small_ragged(sfa_lib, kv_dtype):
+    """512-wide rows (rope_dim 0): masked tokens as in the 576-wide case, nothing but the 512
+    channels written."""
+    bt = np.array([[4, 7, -1], [0, 11, 3], [9, 15, 2]], dtype=np.int32)  # block 15 is past the pool
+    inp = W.cache_write_generate(batch=3, s1=5, n_pool_blocks=12, max_blocks_per_batch=3, kv_dtype=kv_dtype,
+                                 seed=21, block_table=bt, rope_dim=0)
+    inp.positions = np.array([0, -1, 3 * 128, 255, 2 * 128 + 5, 1, 127, 128, 300, 383, 127, 1 * 128 + 7, 256, 2, 300],
+                             dtype=np.int32)
+    assert inp.n_written() == 15 - 4
+    _assert_same(_run(sfa_lib, inp), _oracle(inp), f"512-wide {kv_dtype}")
+
+
+def test_512_wide_write_then_window_attention_reads_it(sfa_lib):
+    """The 512-wide chain: the decode step's two new rows per sequence are quantised into an INT8
+    pool of 512-wide rows, and SWA on that pool (rope_dim 0) reads them: the cache equals the
+    oracle-written one and the attention meets the accuracy standard against the window oracle."""
+    import torch
+
+    import oracle.window_oracle as WO
+
+    win = W.window_generate(batch=3, s1=2, n_q=32, ori_lens=[700, 300, 130], window=64, cmp_mode="none",
+                            kv_dtype="int8", seed=22, rope_dim=0)
+    pos = np.array([[int(v) - 2, int(v) - 1] for v in win.ori_len], dtype=np.int32).reshape(-1)
+    cw = W.cache_write_generate(batch=3, s1=2, n_pool_blocks=win.num_cache_rows // 128,
+                                max_blocks_per_batch=win.block_table_ori.shape[1], kv_dtype="int8", seed=23,
+                                positions=pos, block_table=win.block_table_ori, rope_dim=0)
+    cw.key_nope, cw.k_nope_scales = win.key_nope, win.k_nope_scales
+    cw.key_rope = np.zeros((win.num_cache_rows, 0), dtype=np.uint16)
+    kn, kr, ks = _run(sfa_lib, cw)
+    _assert_same((kn, kr, ks), _oracle(cw), "512-wide chain cache")
+    win.key_nope, win.k_nope_scales = kn, ks
+    out = sfa_lib.run_window(win).float().cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    ref = WO.window_attention(win)
+    rep = O.allclose_report(out.reshape(ref.shape), ref)
     assert rep["fails"] == 0, rep
