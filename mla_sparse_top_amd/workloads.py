@@ -858,6 +858,62 @@ def prolog_decode(seed: int = 0) -> PrologInputs:
     return prolog_generate(tokens=128, n_q=128, seed=seed, name="mla_prolog_b64_s2")
 
 
+@dataclasses.dataclass
+class PrologV4Inputs:
+    tokens: int
+    n_q: int
+    x: np.ndarray               # uint16 bf16 bits (T, hidden)
+    w_dq: np.ndarray            # uint16 (q_lora_rank, hidden)
+    gamma_cq: np.ndarray        # uint16 (q_lora_rank)
+    w_uq: np.ndarray            # uint16 (n_q * 512, q_lora_rank)
+    w_dkv: np.ndarray           # uint16 (512, hidden)
+    gamma_ckv: np.ndarray       # uint16 (512)
+    positions: np.ndarray       # int32 (T)
+    rope_cos: np.ndarray        # float32 (rope_positions, 32)
+    rope_sin: np.ndarray        # float32 (rope_positions, 32)
+    eps: float
+    name: str = ""
+
+    @property
+    def hidden(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def q_lora_rank(self) -> int:
+        return int(self.w_dq.shape[0])
+
+    @property
+    def rope_positions(self) -> int:
+        return int(self.rope_cos.shape[0])
+
+
+def prolog_v4_generate(*, tokens: int, n_q: int, hidden: int = 4096, q_lora_rank: int = 1536,
+                       positions: Optional[Sequence[int]] = None, rope_positions: int = 8192, seed: int = 0,
+                       name: str = "") -> PrologV4Inputs:
+    """The V4 prolog's inputs, drawn as prolog_generate's: x N(0,1), weights N(0, 1/fan_in), RMSNorm
+    scales 1 + N(0, 0.1^2), all rounded to bf16; positions 8190, 8191 alternating; eps 1e-6."""
+    g = torch.Generator().manual_seed(120_000 + int(seed))
+    x = _scaled_bf16(g, (tokens, hidden), 1.0)
+    w_dq = _scaled_bf16(g, (q_lora_rank, hidden), hidden ** -0.5)
+    gamma_cq = _bf16_bits(1.0 + torch.randn(q_lora_rank, generator=g) * 0.1)
+    w_uq = _scaled_bf16(g, (n_q * KV_LORA_RANK, q_lora_rank), q_lora_rank ** -0.5)
+    w_dkv = _scaled_bf16(g, (KV_LORA_RANK, hidden), hidden ** -0.5)
+    gamma_ckv = _bf16_bits(1.0 + torch.randn(KV_LORA_RANK, generator=g) * 0.1)
+    if positions is None:
+        positions = [8190 + (t % 2) for t in range(tokens)]
+    cos, sin = rope_tables(rope_positions)
+    return PrologV4Inputs(tokens=int(tokens), n_q=int(n_q), x=x, w_dq=w_dq, gamma_cq=gamma_cq, w_uq=w_uq,
+                          w_dkv=w_dkv, gamma_ckv=gamma_ckv, positions=np.ascontiguousarray(positions, dtype=np.int32),
+                          rope_cos=cos, rope_sin=sin, eps=1e-6, name=name)
+
+
+def prolog_v4_decode(seed: int = 0) -> PrologV4Inputs:
+    """The V4 prolog at the decode step: 64 sequences x 2 new tokens, 128 heads of 512 channels,
+    hidden 4096 (the page's MlaProlog shapes), query rank 1536 (not given by the page: the V3
+    value), positions 8190 and 8191."""
+    return prolog_v4_generate(tokens=128, n_q=128, seed=seed, name="mla_prolog_v4_b64_s2")
+
+
 def compress_index_decode(seed: int = 0, ratio: int = 4) -> CompressInputs:
     """The page's D = 128 compressor configuration (the index keys the Lightning Indexer scores
     over the compressed cache) on the same decode step: 64 sequences, positions 8190 and 8191,

@@ -45,6 +45,18 @@ Pinned by tests/test_prolog_oracle.py: a pure-Python scalar brute force on tiny 
 forms (identity absorption, quarter-turn and zero-angle rotation, scale invariance of the
 normalised outputs, unit mean square), head permutation, and planted mistakes. The indexer
 prolog at the end of this module is pinned in tests/test_indexer_prolog_oracle.py.
+
+The V4 form (mla_prolog_v4 below) follows "NPU DeepSeek-V4 model PyPTO fused-operator
+optimisation", section "MlaProlog", computation steps, in its own layout: the query of head h is
+RMSNorm(cq . w_uq^T) over that head's 512 channels with unit weight (the page's second RMSNorm,
+whose weight is fixed at 1), then RoPE in place on its last 64 channels; the latent row is
+RMSNorm(x . w_dkv^T) * gamma_ckv over 512 channels, then RoPE in place on its last 64. No
+weight absorption and no separate rotary outputs: query rows and the latent row are 512 wide
+with the rotary part inside, the rows the 512-wide window attention reads. Its readings:
+per-head normalisation (the rotation is applied to the last axis, so the query's last axis is
+the head's 512 channels); the same RoPE, table and out-of-table rule as above; cq unrounded
+between the steps. Pinned in tests/test_prolog_oracle.py (scalar brute force, unit mean square,
+scale invariance, quarter turn, planted mistakes).
 """
 
 from __future__ import annotations
@@ -129,6 +141,35 @@ def mla_prolog(x, w_dq, gamma_cq, w_uq_qr, w_uk, w_dkv_kr, gamma_ckv, positions,
     kv_rope = rope_interleaved(kv[:, LATENT:LATENT + ROPE], cos, sin)
     kv_rope[~live] = 0.0
     return q_nope, q_rope, kv_nope, kv_rope
+
+
+def head_rms_norm(q: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm with unit weight over the last axis (each head's channels)."""
+    return rms_norm(q, np.ones(q.shape[-1]), eps)
+
+
+def rope_last(v: np.ndarray, cos: np.ndarray, sin: np.ndarray, live: np.ndarray) -> np.ndarray:
+    """v with its last ROPE channels rotated in place (pairs as rope_interleaved; cos / sin
+    broadcast against them), zero where the token's position is outside the tables."""
+    out = np.array(v, dtype=np.float64, copy=True)
+    out[..., -ROPE:] = rope_interleaved(out[..., -ROPE:], cos, sin)
+    out[~live, ..., -ROPE:] = 0.0
+    return out
+
+
+def mla_prolog_v4(x, w_dq, gamma_cq, w_uq, w_dkv, gamma_ckv, positions, rope_cos, rope_sin, eps, n_q: int):
+    """The V4 prolog over T tokens. bf16 arrays arrive as uint16 bit patterns: x (T, H),
+    w_dq (Q, H), gamma_cq (Q), w_uq (n_q*512, Q) (head h owns rows h*512 .. +512), w_dkv (512, H),
+    gamma_ckv (512). Returns float64 before the final bf16 rounding: q (T, n_q, 512) and
+    kv (T, 512), each with its rotary part in its last 64 channels."""
+    X = bf16_bits_to_f64(x)
+    cos, sin, live = rope_rows(positions, rope_cos, rope_sin)
+    cq = rms_norm(X @ bf16_bits_to_f64(w_dq).T, bf16_bits_to_f64(gamma_cq), eps)
+    q = (cq @ bf16_bits_to_f64(w_uq).T).reshape(X.shape[0], n_q, LATENT)
+    q = rope_last(head_rms_norm(q, eps), cos[:, None, :], sin[:, None, :], live)
+    kv = rms_norm(X @ bf16_bits_to_f64(w_dkv).T, bf16_bits_to_f64(gamma_ckv), eps)
+    kv = rope_last(kv, cos, sin, live)
+    return q, kv
 
 
 # ---- Indexer prolog ---------------------------------------------------------------------

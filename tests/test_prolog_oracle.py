@@ -297,3 +297,152 @@ def test_key_norm_covering_the_rotary_part_is_caught(monkeypatch):
         except AssertionError:
             failed += 1
     assert failed > 0
+
+
+# ---- the V4 form (mla_prolog_v4): 512-wide query heads and latent row, rotary part inside ----
+
+def _tiny_v4(seed=0, *, tokens=3, hidden=16, q=8, n_q=2, n_pos=16, positions=(3, 0, 17)):
+    return W.prolog_v4_generate(tokens=tokens, n_q=n_q, hidden=hidden, q_lora_rank=q, positions=list(positions),
+                                rope_positions=n_pos, seed=seed)
+
+
+def _run_v4(p, **over):
+    a = dict(x=p.x, w_dq=p.w_dq, gamma_cq=p.gamma_cq, w_uq=p.w_uq, w_dkv=p.w_dkv, gamma_ckv=p.gamma_ckv,
+             positions=p.positions, rope_cos=p.rope_cos, rope_sin=p.rope_sin, eps=p.eps, n_q=p.n_q)
+    a.update(over)
+    return P.mla_prolog_v4(**a)
+
+
+def _brute_v4(p):
+    """Scalar route: struct decode, loops, math.sqrt, each pair turned by hand."""
+    t_n, h_n = p.x.shape
+    qr_n = p.w_dq.shape[0]
+    x = [[_dec(p.x[t, k]) for k in range(h_n)] for t in range(t_n)]
+    out = []
+    for t in range(t_n):
+        pos = int(p.positions[t])
+        live = 0 <= pos < p.rope_cos.shape[0]
+
+        def turn(v):
+            for i in range(32):
+                a, b = v[448 + 2 * i], v[449 + 2 * i]
+                if live:
+                    c, s = float(p.rope_cos[pos, i]), float(p.rope_sin[pos, i])
+                    v[448 + 2 * i], v[449 + 2 * i] = a * c - b * s, a * s + b * c
+                else:
+                    v[448 + 2 * i], v[449 + 2 * i] = 0.0, 0.0
+            return v
+
+        c = [sum(x[t][k] * _dec(p.w_dq[i, k]) for k in range(h_n)) for i in range(qr_n)]
+        inv = 1.0 / math.sqrt(sum(v * v for v in c) / qr_n + p.eps)
+        cq = [c[i] * inv * _dec(p.gamma_cq[i]) for i in range(qr_n)]
+        heads = []
+        for h in range(p.n_q):
+            u = [sum(cq[i] * _dec(p.w_uq[h * 512 + j, i]) for i in range(qr_n)) for j in range(512)]
+            iu = 1.0 / math.sqrt(sum(v * v for v in u) / 512 + p.eps)
+            heads.append(turn([v * iu for v in u]))
+        k = [sum(x[t][m] * _dec(p.w_dkv[j, m]) for m in range(h_n)) for j in range(512)]
+        ik = 1.0 / math.sqrt(sum(v * v for v in k) / 512 + p.eps)
+        out.append((heads, turn([k[j] * ik * _dec(p.gamma_ckv[j]) for j in range(512)])))
+    return out
+
+
+def _pin_v4_brute_force():
+    """The vectorised V4 form equals the scalar route (one token past the tables)."""
+    for seed, pos in ((0, (3, 0, 17)), (1, (15, -1, 8))):
+        p = _tiny_v4(seed, positions=pos)
+        q, kv = _run_v4(p)
+        for t, (bq, bkv) in enumerate(_brute_v4(p)):
+            np.testing.assert_allclose(q[t], np.array(bq), rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(kv[t], np.array(bkv), rtol=1e-11, atol=1e-12)
+
+
+def _pin_v4_unit_mean_square():
+    """At angle zero (table row 0) each query head has mean square ms / (ms + eps) of its raw
+    projection (unit weight), and kv / gamma the same for the latent row."""
+    p = _tiny_v4(2, positions=(0, 0, 0))
+    q, kv = _run_v4(p)
+    X = P.bf16_bits_to_f64(p.x)
+    cq = P.rms_norm(X @ P.bf16_bits_to_f64(p.w_dq).T, P.bf16_bits_to_f64(p.gamma_cq), p.eps)
+    raw = (cq @ P.bf16_bits_to_f64(p.w_uq).T).reshape(3, p.n_q, 512)
+    ms = np.mean(raw * raw, axis=-1)
+    np.testing.assert_allclose(np.mean(q * q, axis=-1), ms / (ms + p.eps), rtol=1e-12)
+    rk = X @ P.bf16_bits_to_f64(p.w_dkv).T
+    mk = np.mean(rk * rk, axis=-1)
+    kn = kv / P.bf16_bits_to_f64(p.gamma_ckv)
+    np.testing.assert_allclose(np.mean(kn * kn, axis=-1), mk / (mk + p.eps), rtol=1e-12)
+
+
+def _pin_v4_scale_invariance_and_quarter_turn():
+    """With eps 0, scaling x by 2 (exact in bf16) changes nothing; a quarter turn (cos 0, sin 1)
+    maps each rotary pair (a, b) of the zero-angle result to (-b, a) and leaves the rest alone."""
+    p = _tiny_v4(3, positions=(0, 1, 2))
+    q0, k0 = _run_v4(p, eps=0.0)
+    x2 = (p.x.astype(np.uint32) + (1 << 7)).astype(np.uint16)  # bf16 exponent + 1: times 2
+    q1, k1 = _run_v4(p, x=x2, eps=0.0)
+    np.testing.assert_allclose(q1, q0, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(k1, k0, rtol=1e-12, atol=1e-13)
+    cos = np.zeros((3, 32), np.float32)
+    sin = np.ones((3, 32), np.float32)
+    one = np.ones((3, 32), np.float32)
+    qz, kz = _run_v4(p, rope_cos=one, rope_sin=np.zeros((3, 32), np.float32))
+    qt, kt = _run_v4(p, rope_cos=cos, rope_sin=sin)
+    for a, b in ((qz, qt), (kz, kt)):
+        np.testing.assert_array_equal(b[..., :448], a[..., :448])
+        np.testing.assert_array_equal(b[..., 448::2], -a[..., 449::2])
+        np.testing.assert_array_equal(b[..., 449::2], a[..., 448::2])
+
+
+V4_PINS = [_pin_v4_brute_force, _pin_v4_unit_mean_square, _pin_v4_scale_invariance_and_quarter_turn]
+
+
+@pytest.mark.parametrize("pin", V4_PINS, ids=[f.__name__[5:] for f in V4_PINS])
+def test_v4_pin(pin):
+    pin()
+
+
+def test_v4_decode_workload_shapes():
+    p = W.prolog_v4_decode()
+    assert p.x.shape == (128, 4096) and p.w_uq.shape == (128 * 512, 1536) and p.w_dkv.shape == (512, 4096)
+    assert set(p.positions.tolist()) == {8190, 8191}
+
+
+_ORIG_V4 = {n: getattr(P, n) for n in ("head_rms_norm", "rope_last")}
+
+
+def _norm_whole_row(q, eps):
+    t = q.shape[0]
+    return _ORIG_V4["head_rms_norm"](q.reshape(t, -1), eps).reshape(q.shape)
+
+
+def _rope_first(v, c, s, live):
+    out = np.array(v, dtype=np.float64, copy=True)
+    out[..., :64] = P.rope_interleaved(out[..., :64], c, s)
+    out[~live, ..., :64] = 0.0
+    return out
+
+
+def _rope_no_zeroing(v, c, s, live):
+    return _ORIG_V4["rope_last"](v, c, s, np.ones_like(live))
+
+
+V4_MUTANTS = {
+    "query norm over all heads at once": ("head_rms_norm", _norm_whole_row),
+    "query norm with the key's gamma": ("head_rms_norm", lambda q, e: P.rms_norm(q, 1.0 + 0.1 * np.arange(
+        q.shape[-1]) / q.shape[-1], e)),
+    "rope on the first 64 channels": ("rope_last", _rope_first),
+    "out-of-table positions rotated by row 0": ("rope_last", _rope_no_zeroing),
+}
+
+
+@pytest.mark.parametrize("name", list(V4_MUTANTS))
+def test_v4_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = V4_MUTANTS[name]
+    monkeypatch.setattr(P, attr, fn)
+    failed = 0
+    for pin in V4_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    assert failed > 0, f"no pin catches: {name}"
