@@ -815,7 +815,8 @@ def bench_compress(args):
     print(json.dumps(rec), flush=True)
 
 
-PROLOG_WORKLOADS = {"mla_prolog_b64_s2": "prolog_decode", "indexer_prolog_b64_s2": "indexer_prolog_decode"}
+PROLOG_WORKLOADS = {"mla_prolog_b64_s2": "prolog_decode", "indexer_prolog_b64_s2": "indexer_prolog_decode",
+                    "mla_prolog_v4_b64_s2": "prolog_v4_decode"}
 
 
 def prolog_work(inp):
@@ -828,6 +829,11 @@ def prolog_work(inp):
         weights = (n * d * q + d * h + 2 * d + n * h) * 2
         nbytes = weights + t * h * 2 + t * q * 2 + t * n * d * 2 + t * d * 2 + t * n * 4 + t * 4 + rows * 32 * 4 * 2
         return nbytes, 2 * t * (q * n * d + h * (d + n))
+    if hasattr(inp, "w_uq"):  # the V4 form: 512-wide query heads and latent row, rotary part inside
+        t, h, q, n = inp.tokens, inp.hidden, inp.q_lora_rank, inp.n_q
+        weights = (q * h + n * 512 * q + 512 * h + q + 512) * 2
+        nbytes = weights + t * h * 2 + t * n * 512 * 2 + t * 512 * 2 + t * 4 + rows * 32 * 4 * 2
+        return nbytes, 2 * t * (h * (q + 512) + q * n * 512)
     t, h, q, n, dn = inp.tokens, inp.hidden, inp.q_lora_rank, inp.n_q, inp.nope_dim
     weights = (q * h + n * (dn + 64) * q + n * 512 * dn + 576 * h + q + 512) * 2
     nbytes = weights + t * h * 2 + t * n * 576 * 2 + t * 576 * 2 + t * 4 + rows * 32 * 4 * 2
@@ -838,7 +844,9 @@ def prolog_work(inp):
 def bench_prolog(args):
     """The MLA prolog (sfa_mla_prolog) of the decode step: 64 sequences x 2 new tokens, hidden
     7168, query rank 1536, 128 heads. The call streams ~122 MB of weights; it rotates over --sets
-    copies of them so that the 256 MB MALL cannot serve the previous call's weights."""
+    copies of them so that the 256 MB MALL cannot serve the previous call's weights. The V4 form
+    (sfa_mla_prolog_v4: hidden 4096, 128 heads of 512 channels) streams ~218 MB; the indexer
+    prolog (sfa_indexer_prolog) is timed the same way."""
     import numpy as np
     import torch
 
@@ -848,9 +856,10 @@ def bench_prolog(args):
     inp = getattr(workloads, PROLOG_WORKLOADS[args.workload])(seed=args.seed)
     print(f"[bench] generated {inp.name}", file=sys.stderr, flush=True)
     indexer = hasattr(inp, "w_idx_qb")
-    to_dev = sfa.indexer_prolog_to_device if indexer else sfa.prolog_to_device
-    run = sfa.run_indexer_prolog if indexer else sfa.run_prolog
-    prep = sfa.prepare_indexer_prolog_run if indexer else sfa.prepare_prolog_run
+    v4 = hasattr(inp, "w_uq")
+    to_dev = sfa.indexer_prolog_to_device if indexer else sfa.prolog_v4_to_device if v4 else sfa.prolog_to_device
+    run = sfa.run_indexer_prolog if indexer else sfa.run_prolog_v4 if v4 else sfa.run_prolog
+    prep = sfa.prepare_indexer_prolog_run if indexer else sfa.prepare_prolog_v4_run if v4 else sfa.prepare_prolog_run
     d0 = to_dev(inp)
     sets = [d0] + [{k: v.clone() for k, v in d0.items()} for _ in range(1, max(1, args.sets))]
     outs = [tuple(torch.empty_like(o) for o in run(inp, d0)) for _ in sets]
@@ -898,6 +907,9 @@ def bench_prolog(args):
                     "q_lora_rank": inp.q_lora_rank, "n_heads": inp.n_heads, "head_dim": inp.head_dim,
                     "rotate": inp.rotate, "cold_sets": len(sets)} if indexer else
                    {"workload": args.workload, "tokens": inp.tokens, "hidden": inp.hidden,
+                    "q_lora_rank": inp.q_lora_rank, "n_q": inp.n_q, "head_dim": 512, "cold_sets": len(sets)}
+                   if v4 else
+                   {"workload": args.workload, "tokens": inp.tokens, "hidden": inp.hidden,
                     "q_lora_rank": inp.q_lora_rank, "n_q": inp.n_q, "qk_nope_dim": inp.nope_dim,
                     "cold_sets": len(sets)}),
         "kernel_ms_mean": round(launch_ms, 5),
@@ -909,6 +921,8 @@ def bench_prolog(args):
                      "traffic": traffic_from_profile(src_hash, f"{args.workload}_traffic.txt")},
         "rotated_outputs_identical": bool(same),
         "kernel_source_sha256": src_hash,
+        # the pages' mla_prolog figure at B = 64, S1 = 2 on one die of another machine: context
+        "context_pages_one_die_us": 130 if v4 else None,
     }
     if args.cpu_seconds > 0:
         # the oracle over the whole call until the budget is spent; its first result is checked
@@ -922,6 +936,9 @@ def bench_prolog(args):
                 want = PO.indexer_prolog(inp.x, inp.qr, inp.w_idx_qb, inp.w_idx_k, inp.ln_gamma_k, inp.ln_beta_k,
                                          inp.w_idx_proj, inp.positions, inp.rope_cos, inp.rope_sin, inp.eps,
                                          inp.n_heads, inp.rotate)
+            elif v4:
+                want = PO.mla_prolog_v4(inp.x, inp.w_dq, inp.gamma_cq, inp.w_uq, inp.w_dkv, inp.gamma_ckv,
+                                        inp.positions, inp.rope_cos, inp.rope_sin, inp.eps, inp.n_q)
             else:
                 want = PO.mla_prolog(inp.x, inp.w_dq, inp.gamma_cq, inp.w_uq_qr, inp.w_uk, inp.w_dkv_kr,
                                      inp.gamma_ckv, inp.positions, inp.rope_cos, inp.rope_sin, inp.eps, inp.n_q)

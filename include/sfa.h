@@ -470,6 +470,59 @@ int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq,
                    size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * MLA prolog, V4 form: the new tokens' hidden states to 512-wide query heads and a 512-wide
+ * latent row, each with its rotary part inside ("NPU DeepSeek-V4 model PyPTO fused-operator
+ * optimisation", section "MlaProlog", computation steps: two projections and RMSNorms for the
+ * query, the second RMSNorm with its weight fixed at 1, one projection and RMSNorm for the key,
+ * and interleaved RoPE in place on the last rope_dim channels of both). For token t with hidden
+ * row x and position p = positions[t]:
+ *
+ *   cq      = RMSNorm(x . w_dq^T) * gamma_cq                      (Q channels)
+ *   q[t,h]  = RMSNorm(cq . w_uq[h]^T), unit weight, over the head's 512 channels;
+ *             then RoPE(p) in place on channels 448 .. 511
+ *   kv[t]   = RMSNorm(x . w_dkv^T) * gamma_ckv over 512 channels; then RoPE(p) in place on
+ *             channels 448 .. 511
+ *
+ * These are the rows sfa_window_decode reads with rope_dim 0 (query_nope) and sfa_cache_write
+ * writes with rope_dim 0 (new_nope). RMSNorm and RoPE as for sfa_mla_prolog (a token with p
+ * outside [0, rope_positions) gets zeros in its rotary channels); products accumulate in fp32, cq
+ * is carried as a bf16 hi + lo pair into the up-projection, outputs are rounded to bf16.
+ *
+ *   x          bf16 (T, H)
+ *   w_dq       bf16 (Q, H)              (out_features, in_features)
+ *   gamma_cq   bf16 (Q)
+ *   w_uq       bf16 (n_q*512, Q)        head h owns rows h*512 .. h*512 + 511
+ *   w_dkv      bf16 (512, H)
+ *   gamma_ckv  bf16 (512)
+ *   positions  int32 (T); rope_cos, rope_sin fp32 (rope_positions, 32)
+ *   q          bf16 (T*n_q, 512)        row t*n_q + h
+ *   kv         bf16 (T, 512)
+ *   cq_out     bf16 (T, Q), or NULL: cq rounded to bf16
+ *   workspace  >= sfa_mla_prolog_v4_workspace_size bytes, 256-byte aligned, no initialisation
+ *
+ * Errors: SFA_ERR_NULL, SFA_ERR_DIMS (hidden and q_lora_rank multiples of 64 in [64, 65536] and
+ * [64, 4096], n_q in [1, 128], head_dim 512, rope_positions >= 1, eps finite and >= 0, tokens up
+ * to 2^20), SFA_ERR_ALIGN (16 bytes), SFA_ERR_ALIAS (an output overlapping an input, another
+ * output or the workspace), SFA_ERR_WORKSPACE, SFA_ERR_HIP. With tokens = 0 nothing is read.
+ * Asynchronous on `stream`, no allocation.
+ */
+typedef struct {
+  int32_t tokens;               /* T >= 0 new tokens                                          */
+  int32_t hidden;               /* H                                                          */
+  int32_t q_lora_rank;          /* Q                                                          */
+  int32_t n_q;                  /* query heads                                                */
+  int32_t head_dim;             /* must be 512                                                */
+  int32_t rope_positions;       /* rows of rope_cos and rope_sin, >= 1                        */
+  float eps;                    /* RMSNorm epsilon                                            */
+} sfa_prolog_v4_dims;
+
+int sfa_mla_prolog_v4_workspace_size(const sfa_prolog_v4_dims* dims, size_t* bytes_out);
+int sfa_mla_prolog_v4(const sfa_prolog_v4_dims* dims, const void* x, const void* w_dq, const void* gamma_cq,
+                      const void* w_uq, const void* w_dkv, const void* gamma_ckv, const int32_t* positions,
+                      const float* rope_cos, const float* rope_sin, void* q, void* kv, void* cq_out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Indexer prolog: the new tokens' inputs of the Lightning Indexer ("CANN DeepSeek Indexer
  * attention optimisation", section "Indexer Prolog": the index query RoPE(RMSNorm(X W_qa) W_qb),
  * the index key RoPE(LayerNorm(X W_k)), RoPE on the second half of the head dimension, the

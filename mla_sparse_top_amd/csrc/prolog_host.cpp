@@ -76,6 +76,56 @@ Layout layout(const sfa_prolog_dims* d, int splits) {
   return l;
 }
 
+// ---- the V4 form of the MLA prolog
+
+int check_v4(const sfa_prolog_v4_dims* d) {
+  if (!d) return SFA_ERR_NULL;
+  if (d->tokens < 0 || d->tokens > (1 << 20)) return SFA_ERR_DIMS;
+  if (d->hidden < 64 || d->hidden > (1 << 16) || d->hidden % 64) return SFA_ERR_DIMS;
+  if (d->q_lora_rank < 64 || d->q_lora_rank > 4096 || d->q_lora_rank % 64) return SFA_ERR_DIMS;
+  if (d->n_q < 1 || d->n_q > SFA_MAX_HEADS) return SFA_ERR_DIMS;
+  if (d->head_dim != kPrLatent) return SFA_ERR_DIMS;
+  if (d->rope_positions < 1) return SFA_ERR_DIMS;
+  if (!(d->eps >= 0.0f) || !isfinite(d->eps)) return SFA_ERR_DIMS;
+  return SFA_OK;
+}
+
+// k splits of a weight-streaming GEMM over `feat_total` features: as many as keep the launch
+// within one workgroup per compute unit, each a whole number of 64-wide chunks of k
+int gemm_splits(int64_t feat_total, int mode, int64_t tokens, int k) {
+  const int feat = 32 * prolog_feat_blocks(mode);
+  const int64_t tiles = (feat_total + feat - 1) / feat;
+  const int64_t tok_blocks = (tokens + kPrTokBlock - 1) / kPrTokBlock;
+  const int units = k / 64;
+  int best = 1;
+  for (int s = 1; s <= units; ++s)
+    if (units % s == 0 && tiles * tok_blocks * s <= kTargetWorkgroups) best = s;
+  return best;
+}
+
+struct V4Layout {
+  size_t part_down, cq_hi, cq_lo, part_up, total;
+  int split_down, split_up;
+};
+
+V4Layout v4_layout(const sfa_prolog_v4_dims* d) {
+  const size_t t = (size_t)d->tokens, q = (size_t)d->q_lora_rank, nf = (size_t)d->n_q * kPrLatent;
+  V4Layout l{};
+  l.split_down = gemm_splits((int64_t)q + kPrLatent, 0, d->tokens, d->hidden);
+  l.split_up = gemm_splits((int64_t)nf, 3, d->tokens, d->q_lora_rank);
+  size_t o = 0;
+  l.part_down = o;
+  o += align_up((size_t)l.split_down * t * (q + kPrLatent) * 4, kAlign);
+  l.cq_hi = o;
+  o += align_up(t * q * 2, kAlign);
+  l.cq_lo = o;
+  o += align_up(t * q * 2, kAlign);
+  l.part_up = o;
+  o += align_up((size_t)l.split_up * t * nf * 4, kAlign);
+  l.total = t ? o : 0;
+  return l;
+}
+
 // ---- indexer prolog
 
 constexpr int kIpDim = 128;  // index head width (the Lightning Indexer's)
@@ -205,7 +255,7 @@ int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq,
   if (launch_prolog_gemm(g1, 0, stream) != hipSuccess) return SFA_ERR_HIP;
 
   // 2. partial sums, RMSNorms, the key's RoPE
-  PrologNormArgs nm;
+  PrologNormArgs nm{};
   nm.part = part;
   nm.n_split = splits;
   nm.tokens = (int32_t)t;
@@ -256,6 +306,131 @@ int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq,
   g3.q_nope = static_cast<uint16_t*>(q_nope);
   if (launch_prolog_gemm(g3, 2, stream) != hipSuccess) return SFA_ERR_HIP;
   return SFA_OK;
+}
+
+int sfa_mla_prolog_v4_workspace_size(const sfa_prolog_v4_dims* dims, size_t* bytes_out) {
+  if (!bytes_out) return SFA_ERR_NULL;
+  const int st = check_v4(dims);
+  if (st != SFA_OK) return st;
+  *bytes_out = v4_layout(dims).total;
+  return SFA_OK;
+}
+
+int sfa_mla_prolog_v4(const sfa_prolog_v4_dims* dims, const void* x, const void* w_dq, const void* gamma_cq,
+                      const void* w_uq, const void* w_dkv, const void* gamma_ckv, const int32_t* positions,
+                      const float* rope_cos, const float* rope_sin, void* q, void* kv, void* cq_out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_v4(dims);
+  if (st != SFA_OK) return st;
+  if (dims->tokens == 0) return SFA_OK;  // nothing to read or write; pointers may be NULL
+  const void* ins[] = {x, w_dq, gamma_cq, w_uq, w_dkv, gamma_ckv, positions, rope_cos, rope_sin};
+  void* outs[] = {q, kv};
+  for (const void* p : ins)
+    if (!p) return SFA_ERR_NULL;
+  for (const void* p : outs)
+    if (!p) return SFA_ERR_NULL;
+  for (const void* p : ins)
+    if (!aligned16(p)) return SFA_ERR_ALIGN;
+  for (const void* p : outs)
+    if (!aligned16(p)) return SFA_ERR_ALIGN;
+  if (cq_out && !aligned16(cq_out)) return SFA_ERR_ALIGN;
+  const V4Layout lay = v4_layout(dims);
+  if (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace % kAlign) != 0) return SFA_ERR_WORKSPACE;
+
+  const size_t t = (size_t)dims->tokens, h = (size_t)dims->hidden, qr = (size_t)dims->q_lora_rank;
+  const size_t n = (size_t)dims->n_q, np = (size_t)dims->rope_positions;
+  const size_t in_bytes[] = {t * h * 2, qr * h * 2, qr * 2, n * kPrLatent * qr * 2, (size_t)kPrLatent * h * 2,
+                             kPrLatent * 2, t * 4, np * 32 * 4, np * 32 * 4};
+  const size_t out_bytes[] = {t * n * kPrLatent * 2, t * kPrLatent * 2, cq_out ? t * qr * 2 : 0};
+  const void* all_outs[] = {q, kv, cq_out};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 9; ++j)
+      if (overlaps(all_outs[i], out_bytes[i], ins[j], in_bytes[j])) return SFA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(all_outs[i], out_bytes[i], all_outs[j], out_bytes[j])) return SFA_ERR_ALIAS;
+    if (overlaps(all_outs[i], out_bytes[i], workspace, lay.total)) return SFA_ERR_ALIAS;
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* part_down = reinterpret_cast<float*>(ws + lay.part_down);
+  uint16_t* cq_hi = reinterpret_cast<uint16_t*>(ws + lay.cq_hi);
+  uint16_t* cq_lo = reinterpret_cast<uint16_t*>(ws + lay.cq_lo);
+  float* part_up = reinterpret_cast<float*>(ws + lay.part_up);
+  const int tok_blocks = (int)((t + kPrTokBlock - 1) / kPrTokBlock);
+
+  PrologGemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.tokens = (int32_t)t;
+  g.tok_blocks = tok_blocks;
+  g.positions = positions;
+  g.rope_cos = rope_cos;
+  g.rope_sin = rope_sin;
+  g.rope_positions = dims->rope_positions;
+  g.n_q = dims->n_q;
+
+  // 1. both down-projections (query rank, then the 512-wide latent row), k split: fp32 partials
+  PrologGemmArgs g1 = g;
+  g1.w0 = static_cast<const uint16_t*>(w_dq);
+  g1.w1 = static_cast<const uint16_t*>(w_dkv);
+  g1.f_split = (int32_t)qr;
+  g1.n_feat = (int32_t)(qr + kPrLatent);
+  g1.k = (int32_t)h;
+  g1.n_split = lay.split_down;
+  g1.k_chunk = (int32_t)(h / lay.split_down);
+  g1.b_hi = static_cast<const uint16_t*>(x);
+  g1.b_stride = (int64_t)h;
+  g1.part = part_down;
+  if (launch_prolog_gemm(g1, 0, stream) != hipSuccess) return SFA_ERR_HIP;
+
+  // 2. partial sums, the query-rank RMSNorm (cq as hi/lo), the latent row's RMSNorm and RoPE
+  PrologNormArgs nm{};
+  nm.part = part_down;
+  nm.n_split = lay.split_down;
+  nm.tokens = (int32_t)t;
+  nm.q_rank = (int32_t)qr;
+  nm.gamma_cq = static_cast<const uint16_t*>(gamma_cq);
+  nm.gamma_ckv = static_cast<const uint16_t*>(gamma_ckv);
+  nm.eps = dims->eps;
+  nm.cq_hi = cq_hi;
+  nm.cq_lo = cq_lo;
+  nm.kv_nope = static_cast<uint16_t*>(kv);
+  nm.kv_rope = nullptr;
+  nm.cq_out = static_cast<uint16_t*>(cq_out);
+  nm.positions = positions;
+  nm.rope_cos = rope_cos;
+  nm.rope_sin = rope_sin;
+  nm.rope_positions = dims->rope_positions;
+  nm.kv_inside = 1;
+  if (launch_prolog_norm(nm, stream) != hipSuccess) return SFA_ERR_HIP;
+
+  // 3. query up-projection over cq (hi and lo): fp32 sums per head channel
+  PrologGemmArgs g2 = g;
+  g2.w0 = static_cast<const uint16_t*>(w_uq);
+  g2.w1 = g2.w0;
+  g2.n_feat = (int32_t)(n * kPrLatent);
+  g2.f_split = g2.n_feat;
+  g2.k = (int32_t)qr;
+  g2.n_split = lay.split_up;
+  g2.k_chunk = (int32_t)(qr / lay.split_up);
+  g2.b_hi = cq_hi;
+  g2.b_lo = cq_lo;
+  g2.b_stride = (int64_t)qr;
+  g2.part = part_up;
+  if (launch_prolog_gemm(g2, 3, stream) != hipSuccess) return SFA_ERR_HIP;
+
+  // 4. per head: RMSNorm with unit weight, RoPE on its last 64 channels, bf16 rows
+  PrologV4HeadArgs hd{};
+  hd.part = part_up;
+  hd.n_split = lay.split_up;
+  hd.tokens = (int32_t)t;
+  hd.n_q = dims->n_q;
+  hd.n_feat = g2.n_feat;
+  hd.eps = dims->eps;
+  hd.positions = positions;
+  hd.rope_cos = rope_cos;
+  hd.rope_sin = rope_sin;
+  hd.rope_positions = dims->rope_positions;
+  hd.q = static_cast<uint16_t*>(q);
+  return launch_prolog_v4_head(hd, stream) == hipSuccess ? SFA_OK : SFA_ERR_HIP;
 }
 
 int sfa_indexer_prolog_workspace_size(const sfa_indexer_prolog_dims* dims, size_t* bytes_out) {

@@ -13,9 +13,12 @@ constexpr int kPrRope = 64;         // rotary channels
 constexpr int kPrTokBlock = 128;    // tokens per workgroup (4 MFMA blocks of 32)
 // 32-feature MFMA blocks per workgroup of each GEMM: the down-projections (64 features; with
 // their k split, 33 tiles x 7 splits at hidden 7168), the query up-projection (96 features: 256
-// tiles at 128 heads) and the absorption (256 of a head's 512 channels: 256 tiles at 128 heads)
-constexpr int kPrFb0 = 2, kPrFb1 = 3, kPrFb2 = 8;
-constexpr int prolog_feat_blocks(int mode) { return mode == 0 ? kPrFb0 : mode == 1 ? kPrFb1 : kPrFb2; }
+// tiles at 128 heads), the absorption (256 of a head's 512 channels: 256 tiles at 128 heads)
+// and the V4 query up-projection (128 features: 512 tiles at 128 heads of 512 channels)
+constexpr int kPrFb0 = 2, kPrFb1 = 3, kPrFb2 = 8, kPrFb3 = 4;
+constexpr int prolog_feat_blocks(int mode) {
+  return mode == 0 ? kPrFb0 : mode == 1 ? kPrFb1 : mode == 2 ? kPrFb2 : kPrFb3;
+}
 
 // One launch of the weight-streaming GEMM: out[t, f] = sum over k of W[f, k] * B[t, k] for the
 // workgroup's features, tokens and k range; the epilogue depends on the mode.
@@ -26,7 +29,7 @@ struct PrologGemmArgs {
   const uint16_t* b_lo;      // low halves (hi + lo carries the fp32 value), or null
   int64_t b_stride;
   int32_t f_split, n_feat, k, tokens, n_split, k_chunk, tok_blocks;
-  // mode 0: fp32 partial sums (n_split, tokens, n_feat)
+  // modes 0 and 3: fp32 partial sums (n_split, tokens, n_feat)
   float* part;
   // mode 1: per-head nope part as hi/lo bf16 (tokens, n_q, dn); rotary part -> q_rope
   uint16_t* qn_hi;
@@ -57,6 +60,22 @@ struct PrologNormArgs {
   const float* rope_cos;
   const float* rope_sin;
   int32_t rope_positions;
+  // V4 form: the latent row is 512 channels normalised whole (no separate rotary key), its last
+  // 64 channels rotated in place; part then holds q_rank + 512 features per token
+  int32_t kv_inside;
+};
+
+// The V4 query heads after their up-projection: RMSNorm with unit weight per head, RoPE in
+// place on the head's last 64 channels.
+struct PrologV4HeadArgs {
+  const float* part;         // (n_split, tokens, n_feat), n_feat = n_q * 512
+  int32_t n_split, tokens, n_q, n_feat;
+  float eps;
+  const int32_t* positions;
+  const float* rope_cos;
+  const float* rope_sin;
+  int32_t rope_positions;
+  uint16_t* q;               // bf16 (tokens * n_q, 512)
 };
 
 // The indexer prolog's per-token step: sums the split partials of the index query (n_heads x
@@ -82,5 +101,6 @@ struct IndexerFinishArgs {
 hipError_t launch_prolog_gemm(const PrologGemmArgs& a, int mode, hipStream_t stream);
 hipError_t launch_indexer_finish(const IndexerFinishArgs& a, hipStream_t stream);
 hipError_t launch_prolog_norm(const PrologNormArgs& a, hipStream_t stream);
+hipError_t launch_prolog_v4_head(const PrologV4HeadArgs& a, hipStream_t stream);
 
 }  // namespace sfa

@@ -139,7 +139,8 @@ __device__ __forceinline__ bf16x8 lds16(const lds_char_t* p) {
 }
 
 // Mode 0: down-projections (fp32 partials). Mode 1: query up-projection (B = cq hi/lo).
-// Mode 2: absorption (B = the heads' nope parts hi/lo).
+// Mode 2: absorption (B = the heads' nope parts hi/lo). Mode 3: the V4 query up-projection
+// (B = cq hi/lo, fp32 sums out, normalised per head by prolog_v4_head_kernel).
 //
 // A workgroup owns 32 * kFb features x 128 tokens and walks its k range in chunks of 64 (one
 // 128-byte line per row). Wave w owns tokens 32w .. 32w + 31 and all the workgroup's features,
@@ -165,7 +166,8 @@ struct GemmShape {
   // output staging: 128 token rows of the workgroup's features (fp32 partials, bf16 q_nope),
   // each row padded by 16 bytes so that the 32 rows a store instruction touches spread over
   // the LDS banks
-  static constexpr int kOutRow = kFeat * (kMode == 0 ? 4 : 2);
+  static constexpr bool kF32Out = kMode == 0 || kMode == 3;    // fp32 partial sums out
+  static constexpr int kOutRow = kFeat * (kF32Out ? 4 : 2);
   static constexpr int kOutStride = kOutRow + 16;
   static_assert(kWStages >= 2 && kLdsBytes <= 160 * 1024, "LDS budget");
   static_assert(kMode == 1 || kPrTokBlock * kOutStride <= kLdsBytes, "output staging fits");
@@ -332,7 +334,7 @@ __global__ void __launch_bounds__(kThreads, 1) prolog_gemm_kernel(const PrologGe
     return;
   }
 
-  // modes 0 and 2: stage the wave's 32 token rows in LDS (its own rows: no other wave reads
+  // modes 0, 2 and 3: stage the wave's 32 token rows in LDS (its own rows: no other wave reads
   // them), then store whole rows, 16 bytes per lane
   wait_vmcnt<0>();
   lds_barrier();  // every wave is done with the operand slots
@@ -343,7 +345,7 @@ __global__ void __launch_bounds__(kThreads, 1) prolog_gemm_kernel(const PrologGe
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int fl = 32 * fb + 8 * g + 4 * hb;  // feature within the tile
-      if (kMode == 0)
+      if (G::kF32Out)
         *reinterpret_cast<floatx4*>(orow + r * kStride + fl * 4) =
             floatx4{acc[fb][4 * g], acc[fb][4 * g + 1], acc[fb][4 * g + 2], acc[fb][4 * g + 3]};
       else
@@ -352,7 +354,7 @@ __global__ void __launch_bounds__(kThreads, 1) prolog_gemm_kernel(const PrologGe
     }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are done before its reads
   constexpr int kPieces = kRow / 16;   // 16-byte pieces per row
-  const int nvalid = kMode == 0 ? min(kFeat, a.n_feat - f0) * 4 / 16 : kPieces;
+  const int nvalid = G::kF32Out ? min(kFeat, a.n_feat - f0) * 4 / 16 : kPieces;
 #pragma unroll
   for (int i = 0; i < 32 * kPieces / 64; ++i) {
     const int idx = i * 64 + lane;
@@ -361,7 +363,7 @@ __global__ void __launch_bounds__(kThreads, 1) prolog_gemm_kernel(const PrologGe
     if (t >= a.tokens || pc >= nvalid) continue;
     const u32x4 v = *reinterpret_cast<const u32x4*>(orow + rr * kStride + pc * 16);
     char* dst;
-    if (kMode == 0)
+    if (G::kF32Out)
       dst = reinterpret_cast<char*>(a.part + ((size_t)split * a.tokens + t) * a.n_feat + f0) + pc * 16;
     else
       dst = reinterpret_cast<char*>(a.q_nope + ((size_t)t * a.n_q + head) * kPrLatent + f0) + pc * 16;
@@ -383,7 +385,8 @@ __device__ __forceinline__ float block_sum(float x, float* sh) {
 __global__ void __launch_bounds__(kThreads) prolog_norm_kernel(const PrologNormArgs a) {
   __shared__ float sh[4];
   const int t = blockIdx.x;
-  const int nf = a.q_rank + kPrLatent + kPrRope;
+  // the V4 form: a 512-wide latent row, normalised whole, its last 64 channels rotated in place
+  const int nf = a.q_rank + kPrLatent + (a.kv_inside ? 0 : kPrRope);
   const int nq4 = a.q_rank / 4, nkv4 = nq4 + kPrLatent / 4, nch = nf / 4;
   floatx4 v[kNormMaxChunks];
 #pragma unroll
@@ -432,7 +435,10 @@ __global__ void __launch_bounds__(kThreads) prolog_norm_kernel(const PrologNormA
       floatx4 y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = v[i][e] * inv_kv * bf16_value(gk[j + e]);
-      *reinterpret_cast<u32x2*>(a.kv_nope + (size_t)t * kPrLatent + j) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+      const int jr = j - (kPrLatent - kPrRope);  // V4: the row's own rotary channels
+      *reinterpret_cast<u32x2*>(a.kv_nope + (size_t)t * kPrLatent + j) =
+          a.kv_inside && jr >= 0 ? rope4(y, p, a.rope_positions, a.rope_cos, a.rope_sin, jr >> 1)
+                                 : u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
     } else {
       const int j = 4 * (c - nkv4);
       *reinterpret_cast<u32x2*>(a.kv_rope + (size_t)t * kPrRope + j) =
@@ -526,6 +532,42 @@ __global__ void __launch_bounds__(kThreads) indexer_finish_kernel(const IndexerF
   }
 }
 
+// The V4 query heads: one wave per (token, head) sums the up-projection's k-split partials of
+// the head's 512 channels (lane L holds channels 8L .. 8L + 7), normalises them with unit weight
+// (the page's second RMSNorm), rotates the last 64 channels in place (lanes 56 .. 63: lane L's
+// pairs are table columns 4(L - 56) .. + 3) and stores the row as bf16, 16 bytes per lane.
+__global__ void __launch_bounds__(kThreads) prolog_v4_head_kernel(const PrologV4HeadArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);  // t * n_q + h
+  if (item >= (int64_t)a.tokens * a.n_q) return;  // whole waves only
+  const int t = (int)(item / a.n_q), h = (int)(item - (int64_t)t * a.n_q);
+  floatx4 v0 = floatx4{}, v1 = floatx4{};
+  for (int s = 0; s < a.n_split; ++s) {
+    const float* src = a.part + ((size_t)s * a.tokens + t) * a.n_feat + (size_t)h * kPrLatent + 8 * lane;
+    v0 += *reinterpret_cast<const floatx4*>(src);
+    v1 += *reinterpret_cast<const floatx4*>(src + 4);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ss += v0[e] * v0[e] + v1[e] * v1[e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float inv = 1.0f / sqrtf(ss / (float)kPrLatent + a.eps);
+  v0 *= inv;
+  v1 *= inv;
+  u32x4 out;
+  if (lane >= (kPrLatent - kPrRope) / 8) {
+    const int p = a.positions[t];
+    const int i = 4 * (lane - (kPrLatent - kPrRope) / 8);
+    const u32x2 r0 = rope4(v0, p, a.rope_positions, a.rope_cos, a.rope_sin, i);
+    const u32x2 r1 = rope4(v1, p, a.rope_positions, a.rope_cos, a.rope_sin, i + 2);
+    out = u32x4{r0[0], r0[1], r1[0], r1[1]};
+  } else {
+    out = u32x4{pack2(v0[0], v0[1]), pack2(v0[2], v0[3]), pack2(v1[0], v1[1]), pack2(v1[2], v1[3])};
+  }
+  *reinterpret_cast<u32x4*>(a.q + (size_t)item * kPrLatent + 8 * lane) = out;
+}
+
 }  // namespace
 
 hipError_t launch_indexer_finish(const IndexerFinishArgs& a, hipStream_t stream) {
@@ -544,8 +586,17 @@ hipError_t launch_prolog_gemm(const PrologGemmArgs& a, int mode, hipStream_t str
     hipLaunchKernelGGL((prolog_gemm_kernel<0, kPrFb0>), dim3(grid), dim3(kThreads), 0, stream, a);
   else if (mode == 1)
     hipLaunchKernelGGL((prolog_gemm_kernel<1, kPrFb1>), dim3(grid), dim3(kThreads), 0, stream, a);
-  else
+  else if (mode == 2)
     hipLaunchKernelGGL((prolog_gemm_kernel<2, kPrFb2>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prolog_gemm_kernel<3, kPrFb3>), dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prolog_v4_head(const PrologV4HeadArgs& a, hipStream_t stream) {
+  const int64_t waves = (int64_t)a.tokens * a.n_q;
+  const int per = kThreads / 64;
+  hipLaunchKernelGGL(prolog_v4_head_kernel, dim3((unsigned)((waves + per - 1) / per)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -151,6 +151,24 @@ _lib.sfa_mla_prolog.argtypes = [ctypes.POINTER(SfaPrologDims)] + [_vp] * 16 + [c
 _lib.sfa_mla_prolog.restype = ctypes.c_int
 
 
+class SfaPrologV4Dims(ctypes.Structure):
+    _fields_ = [
+        ("tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("q_lora_rank", ctypes.c_int32),
+        ("n_q", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rope_positions", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+    ]
+
+
+_lib.sfa_mla_prolog_v4_workspace_size.argtypes = [ctypes.POINTER(SfaPrologV4Dims), ctypes.POINTER(ctypes.c_size_t)]
+_lib.sfa_mla_prolog_v4_workspace_size.restype = ctypes.c_int
+_lib.sfa_mla_prolog_v4.argtypes = [ctypes.POINTER(SfaPrologV4Dims)] + [_vp] * 13 + [ctypes.c_size_t, _vp]
+_lib.sfa_mla_prolog_v4.restype = ctypes.c_int
+
+
 class SfaIndexerPrologDims(ctypes.Structure):
     _fields_ = [
         ("tokens", ctypes.c_int32),
@@ -175,8 +193,8 @@ _lib.sfa_indexer_prolog.restype = ctypes.c_int
 EXPORTED_SYMBOLS = ("sfa_workspace_size", "sfa_num_splits", "sfa_decode", "sfa_prefill", "sfa_resolve_rows",
                     "sfa_status_string", "sfa_indexer_scores", "sfa_topk_select", "sfa_cache_write",
                     "sfa_window_workspace_size", "sfa_window_decode", "sfa_compress", "sfa_decode_noalloc",
-                    "sfa_mla_prolog_workspace_size", "sfa_mla_prolog", "sfa_indexer_prolog_workspace_size",
-                    "sfa_indexer_prolog")
+                    "sfa_mla_prolog_workspace_size", "sfa_mla_prolog", "sfa_mla_prolog_v4_workspace_size",
+                    "sfa_mla_prolog_v4", "sfa_indexer_prolog_workspace_size", "sfa_indexer_prolog")
 
 
 class SfaError(RuntimeError):
@@ -961,6 +979,102 @@ def run_prolog(inp, d=None, *, out=None, cq_out=None):
 
 def prepare_prolog_run(inp, d, *, out=None) -> PreparedCall:
     return prepare_mla_prolog(*_prolog_args(inp, d), out=out)
+
+
+# ---- MLA prolog, V4 form ----------------------------------------------------------------
+
+def prolog_v4_workspace_size(dims: SfaPrologV4Dims) -> int:
+    out = ctypes.c_size_t(0)
+    st = _lib.sfa_mla_prolog_v4_workspace_size(ctypes.byref(dims), ctypes.byref(out))
+    if st != 0:
+        raise SfaError(st, "sfa_mla_prolog_v4_workspace_size")
+    return out.value
+
+
+def _marshal_prolog_v4(x, w_dq, gamma_cq, w_uq, w_dkv, gamma_ckv, positions, rope_cos, rope_sin, eps, *,
+                       out=None, workspace=None, stream=None, cq_out=None):
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    t, hidden = x.shape
+    q = w_dq.shape[0]
+    n_q = w_uq.shape[0] // KV_LORA_RANK
+    n_pos = rope_cos.shape[0]
+    b16 = (torch.bfloat16,)
+    _check(x, "x", b16, (t, hidden), dev)
+    _check(w_dq, "w_dq", b16, (q, hidden), dev)
+    _check(gamma_cq, "gamma_cq", b16, (q,), dev)
+    _check(w_uq, "w_uq", b16, (n_q * KV_LORA_RANK, q), dev)
+    _check(w_dkv, "w_dkv", b16, (KV_LORA_RANK, hidden), dev)
+    _check(gamma_ckv, "gamma_ckv", b16, (KV_LORA_RANK,), dev)
+    _check(positions, "positions", (torch.int32,), (t,), dev)
+    _check(rope_cos, "rope_cos", (torch.float32,), (n_pos, ROPE_DIM // 2), dev)
+    _check(rope_sin, "rope_sin", (torch.float32,), (n_pos, ROPE_DIM // 2), dev)
+    dims = SfaPrologV4Dims(t, hidden, q, n_q, KV_LORA_RANK, n_pos, float(eps))
+    shapes = ((t * n_q, KV_LORA_RANK), (t, KV_LORA_RANK))
+    if out is None:
+        out = tuple(torch.empty(sh, dtype=torch.bfloat16, device=dev) for sh in shapes)
+    for o, sh, name in zip(out, shapes, ("q", "kv")):
+        _check(o, name, b16, sh, dev)
+    need = prolog_v4_workspace_size(dims)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    if workspace is None and need:
+        workspace = get_workspace(dev, need, stream)
+    if workspace is not None:
+        _check(workspace, "workspace", (torch.uint8,), None, dev)
+    if cq_out is not None:
+        _check(cq_out, "cq_out", b16, (t, q), dev)
+    args = (ctypes.byref(dims), _ptr(x), _ptr(w_dq), _ptr(gamma_cq), _ptr(w_uq), _ptr(w_dkv), _ptr(gamma_ckv),
+            _ptr(positions), _ptr(rope_cos), _ptr(rope_sin), *[_ptr(o) for o in out], _ptr(cq_out),
+            _ptr(workspace), ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
+            ctypes.c_void_p(stream.cuda_stream))
+    keep = (dims, x, w_dq, gamma_cq, w_uq, w_dkv, gamma_ckv, positions, rope_cos, rope_sin, out, cq_out, workspace,
+            stream)
+    return args, out, keep
+
+
+def mla_prolog_v4(x, w_dq, gamma_cq, w_uq, w_dkv, gamma_ckv, positions, rope_cos, rope_sin, eps, *, out=None,
+                  workspace=None, stream=None, cq_out=None):
+    """sfa_mla_prolog_v4: returns (q (T*n_q, 512), kv (T, 512)) bf16, each with its rotary part in
+    its last 64 channels; cq_out (T, Q) bf16, when given, receives cq rounded to bf16."""
+    args, out, _keep = _marshal_prolog_v4(x, w_dq, gamma_cq, w_uq, w_dkv, gamma_ckv, positions, rope_cos, rope_sin,
+                                          eps, out=out, workspace=workspace, stream=stream, cq_out=cq_out)
+    st = _lib.sfa_mla_prolog_v4(*args)
+    if st != 0:
+        raise SfaError(st, "sfa_mla_prolog_v4")
+    return out
+
+
+def prolog_v4_to_device(inp, device="cuda"):
+    """Upload a workloads.PrologV4Inputs instance."""
+    import numpy as np
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    return {
+        "x": bf16(inp.x), "w_dq": bf16(inp.w_dq), "gamma_cq": bf16(inp.gamma_cq), "w_uq": bf16(inp.w_uq),
+        "w_dkv": bf16(inp.w_dkv), "gamma_ckv": bf16(inp.gamma_ckv),
+        "positions": torch.from_numpy(inp.positions).to(device),
+        "rope_cos": torch.from_numpy(inp.rope_cos).to(device), "rope_sin": torch.from_numpy(inp.rope_sin).to(device),
+    }
+
+
+def _prolog_v4_args(inp, d):
+    return (d["x"], d["w_dq"], d["gamma_cq"], d["w_uq"], d["w_dkv"], d["gamma_ckv"], d["positions"], d["rope_cos"],
+            d["rope_sin"], inp.eps)
+
+
+def run_prolog_v4(inp, d=None, *, out=None, cq_out=None):
+    """sfa_mla_prolog_v4 on an uploaded PrologV4Inputs instance."""
+    d = d if d is not None else prolog_v4_to_device(inp)
+    return mla_prolog_v4(*_prolog_v4_args(inp, d), out=out, cq_out=cq_out)
+
+
+def prepare_prolog_v4_run(inp, d, *, out=None) -> PreparedCall:
+    args, out, keep = _marshal_prolog_v4(*_prolog_v4_args(inp, d), out=out)
+    return PreparedCall([(_lib.sfa_mla_prolog_v4, args, "sfa_mla_prolog_v4")], out, keep)
 
 
 # ---- indexer prolog ---------------------------------------------------------------------

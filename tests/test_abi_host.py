@@ -453,6 +453,61 @@ def test_prolog_validation_errors():
     assert _prolog_call(d, {"cq": 0x7000000000 + 4096}) == -6        # inside the workspace
 
 
+def _v4_dims(**kw):
+    base = dict(tokens=128, hidden=4096, q_lora_rank=1536, n_q=128, head_dim=512, rope_positions=8192, eps=1e-6)
+    base.update(kw)
+    return sfa.SfaPrologV4Dims(**base)
+
+
+def _v4_call(d, over=None, ws=0x7000000000, ws_bytes=None):
+    """sfa_mla_prolog_v4 with fake device addresses 4 GiB apart; every case here fails validation
+    (or has no tokens), so nothing is launched."""
+    vp = ctypes.c_void_p
+    names = ["x", "w_dq", "gcq", "w_uq", "w_dkv", "gckv", "pos", "cos", "sin", "q", "kv", "cq"]
+    p = {n: 0x100000000 * (i + 1) for i, n in enumerate(names)}
+    p["cq"] = None
+    p.update(over or {})
+    if ws_bytes is None:
+        ws_bytes = sfa.prolog_v4_workspace_size(d)
+    return sfa._lib.sfa_mla_prolog_v4(ctypes.byref(d), *[vp(p[n]) if p[n] is not None else None for n in names],
+                                      vp(ws) if ws else None, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_prolog_v4_workspace():
+    # 32 feature tiles x 8 k splits of the down-projections; cq as hi/lo; the up-projection's fp32
+    # sums (512 tiles of 128 features: no split)
+    d = _v4_dims()
+    assert sfa.prolog_v4_workspace_size(d) == 8 * 128 * (1536 + 512) * 4 + 2 * 128 * 1536 * 2 + 128 * 65536 * 4
+    assert sfa.prolog_v4_workspace_size(_v4_dims(tokens=0)) == 0
+
+
+@pytest.mark.parametrize("field,value", [("hidden", 0), ("hidden", 4100), ("q_lora_rank", 32), ("q_lora_rank", 8192),
+                                         ("n_q", 0), ("n_q", 129), ("head_dim", 576), ("head_dim", 128),
+                                         ("rope_positions", 0), ("eps", -1.0), ("eps", float("nan")), ("tokens", -1)])
+def test_prolog_v4_bad_dims_rejected(field, value):
+    d = _v4_dims(**{field: value})
+    out = ctypes.c_size_t(0)
+    assert sfa._lib.sfa_mla_prolog_v4_workspace_size(ctypes.byref(d), ctypes.byref(out)) == -2
+    assert _v4_call(d, ws_bytes=0) == -2
+
+
+def test_prolog_v4_validation_errors():
+    d = _v4_dims()
+    assert _v4_call(d, {"x": None}) == -1
+    assert _v4_call(d, {"q": None}) == -1
+    assert _v4_call(d, {"kv": None}) == -1
+    assert _v4_call(d, {"w_uq": 0x400000008}) == -3
+    assert _v4_call(d, ws=None) == -4
+    assert _v4_call(d, ws=0x7000000010) == -4
+    assert _v4_call(d, ws_bytes=sfa.prolog_v4_workspace_size(d) - 1) == -4
+    assert _v4_call(d, {"q": 0x100000000 * 2 + 4096}) == -6        # q inside w_dq
+    assert _v4_call(d, {"kv": 0x7000000000 + 4096}) == -6           # kv inside the workspace
+    assert _v4_call(d, {"kv": 0x100000000 * 10 + 64}) == -6         # kv inside q
+    assert _v4_call(d, {"cq": 0x100000000 * 13 + 8}) == -3
+    assert _v4_call(d, {"cq": 0x100000000 * 1 + 64}) == -6          # inside x
+    assert _v4_call(_v4_dims(tokens=0), {n: None for n in ("x", "q", "kv")}, ws=None, ws_bytes=0) == 0
+
+
 def _ip_dims(**kw):
     base = dict(tokens=128, hidden=7168, q_lora_rank=1536, n_heads=64, head_dim=128, rope_positions=8192, rotate=1,
                 eps=1e-6)

@@ -130,3 +130,89 @@ def test_prolog_feeds_cache_write_and_decode(sfa_lib):
     for t in range(b):
         for h in range(16):
             assert torch.equal(out[t, 0, h].view(torch.int16), kn[t].view(torch.int16))
+
+
+# ---- the V4 form (sfa_mla_prolog_v4): 512-wide query heads and latent row, rotary part inside ----
+
+def _oracle_v4(inp):
+    return P.mla_prolog_v4(inp.x, inp.w_dq, inp.gamma_cq, inp.w_uq, inp.w_dkv, inp.gamma_ckv, inp.positions,
+                           inp.rope_cos, inp.rope_sin, inp.eps, inp.n_q)
+
+
+def _assert_close_v4(inp, got):
+    want = _oracle_v4(inp)
+    for name, g, w, sh in zip(("q", "kv"), got, want, ((inp.tokens, inp.n_q, 512), (inp.tokens, 512))):
+        gv = P.bf16_bits_to_f64(_bits(g)).reshape(sh)
+        err = np.abs(gv - w)
+        bound = 1e-4 + 5e-3 * np.abs(w)
+        bad = np.argwhere(err > bound)
+        assert bad.size == 0, (f"{name}: {len(bad)} elements off, first {bad[:3].tolist()}, worst ratio "
+                               f"{np.max(err / bound):.3f}")
+
+
+@pytest.mark.parametrize("tokens,hidden,q,n_q,seed", [
+    (37, 512, 256, 4, 0),        # one partial token block
+    (200, 1024, 512, 3, 1),      # a full and a ragged token block, odd head count
+    (1, 256, 64, 1, 2),          # the smallest shapes
+    (130, 4096, 1024, 16, 3),    # the page's hidden width
+])
+def test_v4_small_shapes(sfa_lib, tokens, hidden, q, n_q, seed):
+    """Positions (7t) mod 300 against 256 table rows: some tokens get zero rotary channels."""
+    import torch
+
+    pos = [(7 * t) % 300 for t in range(tokens)]
+    inp = W.prolog_v4_generate(tokens=tokens, n_q=n_q, hidden=hidden, q_lora_rank=q, positions=pos,
+                               rope_positions=256, seed=seed)
+    out = sfa_lib.run_prolog_v4(inp)
+    torch.cuda.synchronize()
+    _assert_close_v4(inp, out)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_v4_decode_full_size(sfa_lib, seed):
+    """64 sequences x 2 new tokens, 128 heads of 512 channels, hidden 4096: every element."""
+    import torch
+
+    inp = W.prolog_v4_decode(seed=seed)
+    d = sfa_lib.prolog_v4_to_device(inp)
+    cq = torch.empty((inp.tokens, inp.q_lora_rank), dtype=torch.bfloat16, device="cuda")
+    out = sfa_lib.run_prolog_v4(inp, d, cq_out=cq)
+    again = sfa_lib.run_prolog_v4(inp, d)
+    torch.cuda.synchronize()
+    _assert_close_v4(inp, out)
+    assert all(torch.equal(a, b) for a, b in zip(out, again))  # repeat calls are bit-identical
+    X = P.bf16_bits_to_f64(inp.x)
+    want_cq = P.rms_norm(X @ P.bf16_bits_to_f64(inp.w_dq).T, P.bf16_bits_to_f64(inp.gamma_cq), inp.eps)
+    got_cq = P.bf16_bits_to_f64(_bits(cq))
+    assert np.all(np.abs(got_cq - want_cq) <= 1e-4 + 5e-3 * np.abs(want_cq))
+
+
+def test_v4_feeds_cache_write_and_512_wide_swa(sfa_lib):
+    """The V4 chain on the GPU: the prolog's latent rows go through sfa_cache_write (rope_dim 0)
+    into a 512-wide pool at the new tokens' positions, and SWA on that pool reads the prolog's
+    query heads. The written rows equal the prolog's bits; the attention meets the accuracy
+    standard against the window oracle on the GPU-written pool and queries."""
+    import torch
+
+    import oracle.sfa_oracle as O
+    import oracle.window_oracle as WO
+
+    win = W.window_generate(batch=2, s1=2, n_q=16, ori_lens=[300, 200], window=64, cmp_mode="none", seed=31,
+                            rope_dim=0)
+    pos = [298, 299, 198, 199]
+    pro = W.prolog_v4_generate(tokens=4, n_q=16, hidden=256, q_lora_rank=128, positions=pos, rope_positions=512,
+                               seed=32)
+    dw = sfa_lib.window_to_device(win)
+    q, kv = sfa_lib.run_prolog_v4(pro)
+    sfa_lib.cache_write(kv, None, torch.tensor(pos, dtype=torch.int32, device="cuda"), dw["block_table_ori"],
+                        dw["key_nope"], None, None, batch=2, s1=2)
+    dw["query_nope"] = q
+    out = sfa_lib.run_window(win, dw)
+    torch.cuda.synchronize()
+    pool = _bits(dw["key_nope"])
+    rows = [int(win.block_table_ori[t // 2, p // 128]) * 128 + p % 128 for t, p in enumerate(pos)]
+    assert np.array_equal(pool[rows], _bits(kv))
+    win.key_nope, win.query_nope = pool, _bits(q)
+    ref = WO.window_attention(win)
+    rep = O.allclose_report(out.float().cpu().numpy().astype(np.float64).reshape(ref.shape), ref)
+    assert rep["fails"] == 0, rep
