@@ -14,8 +14,8 @@ constexpr int kPrTokBlock = 128;    // tokens per workgroup (4 MFMA blocks of 32
 // 32-feature MFMA blocks per workgroup of each GEMM: the down-projections (64 features; with
 // their k split, 33 tiles x 7 splits at hidden 7168), the query up-projection (96 features: 256
 // tiles at 128 heads), the absorption (256 of a head's 512 channels: 256 tiles at 128 heads)
-// and the V4 query up-projection (128 features: 512 tiles at 128 heads of 512 channels)
-constexpr int kPrFb0 = 2, kPrFb1 = 3, kPrFb2 = 8, kPrFb3 = 4;
+// and the V4 query up-projection (256 features: 256 tiles at 128 heads of 512 channels)
+constexpr int kPrFb0 = 2, kPrFb1 = 3, kPrFb2 = 8, kPrFb3 = 8;
 constexpr int prolog_feat_blocks(int mode) {
   return mode == 0 ? kPrFb0 : mode == 1 ? kPrFb1 : mode == 2 ? kPrFb2 : kPrFb3;
 }

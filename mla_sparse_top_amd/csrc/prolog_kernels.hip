@@ -23,6 +23,13 @@
 //      Its epilogue writes each head's nope part as a hi + lo pair and rotates the rotary part.
 //   4. prolog_gemm_kernel<2>: the absorption, per head a 512 x dn weight over the nope part
 //      (hi and lo), in tiles of 64 output channels.
+// The V4 form (same page section, its own layout: 512-wide query heads and latent row with the
+// rotary part inside, no absorption) runs four launches too: the down-projections (query rank
+// and the 512-wide latent row) as step 1; the norm kernel with the latent row normalised whole
+// and its last 64 channels rotated in place; prolog_gemm_kernel<3>, the up-projection over cq
+// hi + lo into fp32 sums, 256 features per workgroup (one round of 256 workgroups at 128 heads,
+// each reading cq once); and prolog_v4_head_kernel, per head RMSNorm with unit weight and RoPE
+// in place on the head's last 64 channels.
 // Operands reach LDS through buffer descriptors whose range ends at the last token (or weight
 // row), so the rows of a partial block read zeros, and their outputs are never stored.
 
@@ -157,7 +164,7 @@ struct GemmShape {
   static constexpr int kWBytes = kFeat * 128;                  // weight rows of a chunk
   static constexpr int kABytes = kPrTokBlock * 128;            // token rows of a chunk (hi or lo)
   static constexpr int kAStage = kABytes * (kLo ? 2 : 1);
-  static constexpr int kTStages = kMode == 2 ? 2 : 3;
+  static constexpr int kTStages = kMode == 2 || kMode == 3 ? 2 : 3;
   static constexpr int kWFit = (152 * 1024 - kTStages * kAStage) / kWBytes;
   static constexpr int kWStages = kWFit > 8 ? 8 : kWFit;
   static constexpr int kLdsBytes = kWStages * kWBytes + kTStages * kAStage;
@@ -170,7 +177,7 @@ struct GemmShape {
   static constexpr int kOutRow = kFeat * (kF32Out ? 4 : 2);
   static constexpr int kOutStride = kOutRow + 16;
   static_assert(kWStages >= 2 && kLdsBytes <= 160 * 1024, "LDS budget");
-  static_assert(kMode == 1 || kPrTokBlock * kOutStride <= kLdsBytes, "output staging fits");
+  static_assert(kMode == 1 || kMode == 3 || kPrTokBlock * kOutStride <= kLdsBytes, "output staging fits");
   static_assert(kWDma * (kWStages - 2) <= 63 && kTDma * (kTStages - 2) <= 63, "vmcnt range");
 };
 
@@ -334,7 +341,25 @@ __global__ void __launch_bounds__(kThreads, 1) prolog_gemm_kernel(const PrologGe
     return;
   }
 
-  // modes 0, 2 and 3: stage the wave's 32 token rows in LDS (its own rows: no other wave reads
+  if (kMode == 3) {
+    // fp32 sums straight from the accumulators: 16 bytes per lane, the 8 pieces of a token's
+    // 128-byte feature block come from one instruction's lanes
+    const int t = tb0 + wave_row;
+    if (t >= a.tokens) return;
+    float* dst = a.part + ((size_t)split * a.tokens + t) * a.n_feat;
+#pragma unroll
+    for (int fb = 0; fb < kFb; ++fb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int f = f0 + 32 * fb + 8 * g + 4 * hb;
+        if (f < a.n_feat)
+          *reinterpret_cast<floatx4*>(dst + f) =
+              floatx4{acc[fb][4 * g], acc[fb][4 * g + 1], acc[fb][4 * g + 2], acc[fb][4 * g + 3]};
+      }
+    return;
+  }
+
+  // modes 0 and 2: stage the wave's 32 token rows in LDS (its own rows: no other wave reads
   // them), then store whole rows, 16 bytes per lane
   wait_vmcnt<0>();
   lds_barrier();  // every wave is done with the operand slots

@@ -475,7 +475,7 @@ def _v4_call(d, over=None, ws=0x7000000000, ws_bytes=None):
 
 def test_prolog_v4_workspace():
     # 32 feature tiles x 8 k splits of the down-projections; cq as hi/lo; the up-projection's fp32
-    # sums (512 tiles of 128 features: no split)
+    # sums (256 tiles of 256 features: no split)
     d = _v4_dims()
     assert sfa.prolog_v4_workspace_size(d) == 8 * 128 * (1536 + 512) * 4 + 2 * 128 * 1536 * 2 + 128 * 65536 * 4
     assert sfa.prolog_v4_workspace_size(_v4_dims(tokens=0)) == 0
