@@ -1,0 +1,135 @@
+"""One decode step of a DeepSeek-V4 SCFA layer on 512-wide rows, end to end on the GPU: the V4 MLA
+prolog, the cache write of the new latent rows, the compressor (512 channels) and the index-key
+compressor (128 channels, Hadamard), the indexer prolog on the prolog's cq, the Lightning Indexer
+over the compressed index keys with its top-k, and SCFA over the original and compressed caches
+("NPU DeepSeek-V4 model PyPTO fused-operator optimisation": MlaProlog, Compressor, IndexerProlog,
+FA-class operators; "CANN DeepSeek Indexer attention optimisation": Lightning Indexer).
+
+Every step is checked against its oracle on the GPU's own inputs to that step (the outputs of
+the steps before it), so each comparison tests one kernel: the bf16 outputs to the attention's
+bar (|gpu - ref| <= 1e-4 + 5e-3 |ref|), copies and states bit for bit, the index scores to the
+indexer's fp32 accumulation bound, the selection as an exact top-k of the GPU's scores."""
+
+import numpy as np
+import pytest
+
+import oracle.compress_oracle as C
+import oracle.indexer_oracle as IO
+import oracle.prolog_oracle as P
+import oracle.sfa_oracle as O
+import oracle.window_oracle as WO
+from mla_sparse_top_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    import torch
+
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _close(name, got, want):
+    err = np.abs(got - want)
+    bound = 1e-4 + 5e-3 * np.abs(want)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, f"{name}: {len(bad)} off, first {bad[:3].tolist()}, worst {np.max(err / bound):.3f}"
+
+
+def run_layer(sfa, L):
+    """The step's launches on the current stream; returns the device tensors of every stage."""
+    import torch
+
+    B, S1 = L.window.batch, L.window.s1
+    T, K = B * S1, L.topk_cmp
+    pro_d = sfa.prolog_v4_to_device(L.prolog)
+    win_d = sfa.window_to_device(L.window)
+    catt_d = sfa.compress_to_device(L.compress_att)
+    catt_d["key_nope"] = win_d["key_nope"]          # the compressed entries share the window's pool
+    cidx_d = sfa.compress_to_device(L.compress_idx)  # the index-key pool
+    ip_d = sfa.indexer_prolog_to_device(L.indexer_prolog)
+    pos = torch.from_numpy(L.positions).cuda()
+    cq = torch.empty((T, L.prolog.q_lora_rank), dtype=torch.bfloat16, device="cuda")
+    q, kv = sfa.run_prolog_v4(L.prolog, pro_d, cq_out=cq)
+    sfa.cache_write(kv, None, pos, win_d["block_table_ori"], win_d["key_nope"], None, None, batch=B, s1=S1)
+    sfa.run_compress(L.compress_att, catt_d)
+    sfa.run_compress(L.compress_idx, cidx_d)
+    ip_d["qr"] = cq
+    q_index, _k, w = sfa.run_indexer_prolog(L.indexer_prolog, ip_d)
+    scores = sfa.indexer_scores(q_index, cidx_d["key_nope"], w, win_d["block_table_cmp"], win_d["cmp_len"], batch=B,
+                                s1=S1, topk=K)
+    sel = sfa.topk_select(scores, win_d["cmp_len"], batch=B, s1=S1, topk=K)
+    win_d["query_nope"] = q
+    win_d["cmp_indices"] = sel
+    out = sfa.run_window(L.window, win_d)
+    torch.cuda.synchronize()
+    return dict(q=q, kv=kv, cq=cq, pool=win_d["key_nope"], catt=catt_d, cidx=cidx_d, q_index=q_index, w=w,
+                scores=scores, sel=sel, out=out)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_v4_scfa_layer_step(sfa_lib, seed):
+    L = W.v4_scfa_layer_generate(batch=3, s1=2, n_q=16, hidden=256, q_lora_rank=256, ori_lens=[600, 300, 132],
+                                 window=64, topk_cmp=24, seed=seed)
+    r = run_layer(sfa_lib, L)
+    pro, win = L.prolog, L.window
+    T = pro.tokens
+
+    # 1. the V4 prolog
+    q_ref, kv_ref = P.mla_prolog_v4(pro.x, pro.w_dq, pro.gamma_cq, pro.w_uq, pro.w_dkv, pro.gamma_ckv,
+                                    pro.positions, pro.rope_cos, pro.rope_sin, pro.eps, pro.n_q)
+    q_bits, kv_bits = _bits(r["q"]), _bits(r["kv"])
+    _close("q", P.bf16_bits_to_f64(q_bits).reshape(q_ref.shape), q_ref)
+    _close("kv", P.bf16_bits_to_f64(kv_bits), kv_ref)
+
+    # 2. the cache write: the new rows at the tokens' positions, bit for bit
+    pool = _bits(r["pool"])
+    rows = [int(win.block_table_ori[t // 2, p // 128]) * 128 + p % 128 for t, p in enumerate(pro.positions)]
+    assert np.array_equal(pool[rows], kv_bits)
+
+    # 3-4. both compressors: states bit for bit, every written row to the bar (each sequence's
+    # second token closes a window)
+    for name, inp, d, base in (("compress_att", L.compress_att, r["catt"], None),
+                               ("compress_idx", L.compress_idx, r["cidx"], None)):
+        ks, ss, entries = C.compress(inp)
+        np.testing.assert_array_equal(d["kv_state"].cpu().numpy().view(np.uint32), ks.view(np.uint32))
+        np.testing.assert_array_equal(d["score_state"].cpu().numpy().view(np.uint32), ss.view(np.uint32))
+        got = _bits(d["key_nope"])
+        assert len(entries) == win.batch
+        for b, c, row, y in entries:
+            assert row >= 0 and c == int(win.cmp_len[b]) - 1, name
+            _close(f"{name} row {row}", P.bf16_bits_to_f64(got[row]), y)
+
+    # 5. the indexer prolog on the GPU's cq
+    ip = L.indexer_prolog
+    qi_ref, _, w_ref = P.indexer_prolog(ip.x, _bits(r["cq"]), ip.w_idx_qb, ip.w_idx_k, ip.ln_gamma_k, ip.ln_beta_k,
+                                        ip.w_idx_proj, ip.positions, ip.rope_cos, ip.rope_sin, ip.eps, ip.n_heads,
+                                        ip.rotate)
+    qi_bits = _bits(r["q_index"])
+    _close("q_index", P.bf16_bits_to_f64(qi_bits).reshape(qi_ref.shape), qi_ref)
+    w_gpu = r["w"].cpu().numpy()
+    _close("weights", w_gpu.astype(np.float64), w_ref)
+
+    # 6. index scores over the compressed index keys (the GPU's pool), and an exact top-k of them
+    kpool = _bits(r["cidx"]["key_nope"])
+    n_pos = win.block_table_cmp.shape[1] * 128
+    ref = IO.indexer_scores(qi_bits.reshape(T, 64, 128), w_gpu, kpool, win.block_table_cmp, win.cmp_len, 2, n_pos)
+    got = r["scores"].cpu().numpy().astype(np.float64)
+    live = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), live)
+    qa = np.abs(IO.bf16_bits_to_f64(qi_bits.reshape(T, 64, 128)))
+    ka = np.abs(IO.bf16_bits_to_f64(kpool))
+    mag = np.zeros_like(ref)
+    for t in range(T):
+        act = int(win.cmp_len[t // 2])
+        mag[t, :act] = np.abs(w_gpu[t].astype(np.float64)) @ (qa[t] @ ka[IO.live_rows(win.block_table_cmp, act,
+                                                                                       t // 2)].T)
+    assert np.all(np.abs(got[live] - ref[live]) <= 2.0 ** -15 * mag[live] + 1e-30)
+    sel = r["sel"].cpu().numpy()
+    assert IO.check_topk(sel, r["scores"].cpu().numpy(), L.topk_cmp)["bad"] == []
+
+    # 7. SCFA over the GPU's pools, queries and compressed list
+    win.query_nope, win.key_nope, win.cmp_indices = q_bits, pool, sel
+    out_ref = WO.window_attention(win)
+    rep = O.allclose_report(r["out"].float().cpu().numpy().astype(np.float64).reshape(out_ref.shape), out_ref)
+    assert rep["fails"] == 0, rep
