@@ -1072,8 +1072,8 @@ def run_prolog_v4(inp, d=None, *, out=None, cq_out=None):
     return mla_prolog_v4(*_prolog_v4_args(inp, d), out=out, cq_out=cq_out)
 
 
-def prepare_prolog_v4_run(inp, d, *, out=None) -> PreparedCall:
-    args, out, keep = _marshal_prolog_v4(*_prolog_v4_args(inp, d), out=out)
+def prepare_prolog_v4_run(inp, d, *, out=None, cq_out=None) -> PreparedCall:
+    args, out, keep = _marshal_prolog_v4(*_prolog_v4_args(inp, d), out=out, cq_out=cq_out)
     return PreparedCall([(_lib.sfa_mla_prolog_v4, args, "sfa_mla_prolog_v4")], out, keep)
 
 
