@@ -506,13 +506,21 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_ca
 
 // One workgroup (4 waves) per token: wave w takes heads w, w + 4, ... of the query; wave 0 then
 // the key (LayerNorm over its 128 channels), wave 1 the head weights.
+// One wave per job of a token: n_heads query heads, then the key, then the head weights (jobs
+// t * (n_heads + 2) + j), so that the token's 64 transforms run on 64 waves instead of one
+// workgroup's four; no job shares data with another.
 __global__ void __launch_bounds__(kThreads) indexer_finish_kernel(const IndexerFinishArgs a) {
-  const int t = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int per_token = a.n_heads + 2;
+  const int64_t item = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (item >= (int64_t)a.tokens * per_token) return;  // whole waves only
+  const int t = (int)(item / per_token);
+  const int j = (int)(item - (int64_t)t * per_token);
   const int p = a.positions[t];
   const int nq = a.n_heads * 128;
-  for (int h = wave; h < a.n_heads; h += 4) {
+  const int nkw = 128 + a.n_heads;
+  if (j < a.n_heads) {
+    const int h = j;
     float y[2] = {0.0f, 0.0f};
     for (int s = 0; s < a.split_q; ++s) {
       const float* src = a.part_q + ((size_t)s * a.tokens + t) * nq + h * 128;
@@ -523,9 +531,7 @@ __global__ void __launch_bounds__(kThreads) indexer_finish_kernel(const IndexerF
     uint16_t* dst = a.q_index + ((size_t)t * a.n_heads + h) * 128;
     dst[lane] = bf16_bits(y[0]);
     dst[64 + lane] = bf16_bits(y[1]);
-  }
-  const int nkw = 128 + a.n_heads;
-  if (wave == 0) {
+  } else if (j == a.n_heads) {
     float y[2] = {0.0f, 0.0f};
     for (int s = 0; s < a.split_kw; ++s) {
       const float* src = a.part_kw + ((size_t)s * a.tokens + t) * nkw;
@@ -548,7 +554,7 @@ __global__ void __launch_bounds__(kThreads) indexer_finish_kernel(const IndexerF
     rope_hadamard128(y, lane, p, a);
     a.k_index[(size_t)t * 128 + lane] = bf16_bits(y[0]);
     a.k_index[(size_t)t * 128 + 64 + lane] = bf16_bits(y[1]);
-  } else if (wave == 1) {
+  } else {
     for (int h = lane; h < a.n_heads; h += 64) {
       float w = 0.0f;
       for (int s = 0; s < a.split_kw; ++s) w += a.part_kw[((size_t)s * a.tokens + t) * nkw + 128 + h];
@@ -596,7 +602,9 @@ __global__ void __launch_bounds__(kThreads) prolog_v4_head_kernel(const PrologV4
 }  // namespace
 
 hipError_t launch_indexer_finish(const IndexerFinishArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(indexer_finish_kernel, dim3(a.tokens), dim3(kThreads), 0, stream, a);
+  const int64_t waves = (int64_t)a.tokens * (a.n_heads + 2);
+  const int per = kThreads / 64;
+  hipLaunchKernelGGL(indexer_finish_kernel, dim3((unsigned)((waves + per - 1) / per)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
