@@ -815,51 +815,67 @@ def bench_compress(args):
     print(json.dumps(rec), flush=True)
 
 
-V4_LAYER_WORKLOADS = {"v4_scfa_layer_b64_s2": "v4_scfa_layer_decode"}
+V4_LAYER_WORKLOADS = {"v4_scfa_layer_b64_s2": "v4_scfa_layer_decode", "v4_cfa_layer_b64_s2": "v4_cfa_layer_decode",
+                      "v4_swa_layer_b64_s2": "v4_swa_layer_decode"}
 
 
 def bench_v4_layer(args):
-    """One decode step of a DeepSeek-V4 SCFA layer (compression ratio 4) on 512-wide rows, chained
-    on one stream: the V4 MLA prolog (4 launches), the cache write of the 128 new latent rows, the
-    compressor and the index-key compressor, the indexer prolog (on the prolog's cq), the Lightning
-    Indexer's scores and top-k over the 2,048 compressed index keys, and SCFA (window 128 + the 512
-    selected entries). The step's footprint (~0.5 GB: weights, pools, scores) exceeds the 256 MB
-    MALL, so one input set is used."""
+    """One decode step of a DeepSeek-V4 attention layer on 512-wide rows, chained on one stream.
+    SCFA layer (ratio 4): the V4 MLA prolog (4 launches), the cache write of the 128 new latent
+    rows, the compressor and the index-key compressor, the indexer prolog (on the prolog's cq),
+    the Lightning Indexer's scores and top-k over the 2,048 compressed index keys, and SCFA
+    (window 128 + the 512 selected entries): 13 launches. CFA layer (ratio 128): the prolog, the
+    cache write, the compressor, CFA over every causal entry: 7 launches. SWA layer: the prolog,
+    the cache write, SWA: 6 launches. The SCFA step's footprint (~0.5 GB: weights, pools, scores)
+    exceeds the 256 MB MALL, so one input set is used for all three."""
     import numpy as np
     import torch
 
+    import oracle.window_oracle as WO
     from mla_sparse_top_amd import sfa, workloads
 
     L = getattr(workloads, V4_LAYER_WORKLOADS[args.workload])(seed=args.seed)
-    print("[bench] generated the V4 layer-step inputs", file=sys.stderr, flush=True)
-    pro, win, ip = L.prolog, L.window, L.indexer_prolog
+    print(f"[bench] generated the V4 {L.kind} layer-step inputs", file=sys.stderr, flush=True)
+    pro, win = L.prolog, L.window
     B, S1 = win.batch, win.s1
     T, K = B * S1, L.topk_cmp
     pro_d = sfa.prolog_v4_to_device(pro)
     win_d = sfa.window_to_device(win)
-    catt_d = sfa.compress_to_device(L.compress_att)
-    catt_d["key_nope"] = win_d["key_nope"]
-    cidx_d = sfa.compress_to_device(L.compress_idx)
-    ip_d = sfa.indexer_prolog_to_device(ip)
     pos = torch.from_numpy(L.positions).cuda()
     cq = torch.empty((T, pro.q_lora_rank), dtype=torch.bfloat16, device="cuda")
     q = torch.empty((T * pro.n_q, 512), dtype=torch.bfloat16, device="cuda")
     kv = torch.empty((T, 512), dtype=torch.bfloat16, device="cuda")
-    ip_d["qr"] = cq
-    sel = torch.empty((T, K), dtype=torch.int32, device="cuda")
     out = torch.empty((B, S1, win.n_q, 512), dtype=torch.bfloat16, device="cuda")
-    win_d["query_nope"], win_d["cmp_indices"] = q, sel
+    win_d["query_nope"] = q
     calls = [
         sfa.prepare_prolog_v4_run(pro, pro_d, out=(q, kv), cq_out=cq),
         sfa.prepare_cache_write(kv, None, pos, win_d["block_table_ori"], win_d["key_nope"], None, None, batch=B,
                                 s1=S1),
-        sfa.prepare_compress(L.compress_att, catt_d),
-        sfa.prepare_compress(L.compress_idx, cidx_d),
-        sfa.prepare_indexer_prolog_run(ip, ip_d),
     ]
-    qi, _, w = calls[-1].out
-    calls.append(sfa.prepare_indexer(qi, cidx_d["key_nope"], w, win_d["block_table_cmp"], win_d["cmp_len"], batch=B,
-                                     s1=S1, topk=K, out=sel))
+    bytes_by_stage = {"prolog": prolog_work(pro)[0], "cache_write": T * (1024 + 1024 + 4 + 4)}
+    if L.compress_att is not None:
+        catt_d = sfa.compress_to_device(L.compress_att)
+        catt_d["key_nope"] = win_d["key_nope"]
+        calls.append(sfa.prepare_compress(L.compress_att, catt_d))
+        bytes_by_stage["compressors"] = compress_algorithmic_bytes(L.compress_att)
+    if L.kind == "scfa":
+        cidx_d = sfa.compress_to_device(L.compress_idx)
+        ip_d = sfa.indexer_prolog_to_device(L.indexer_prolog)
+        ip_d["qr"] = cq
+        sel = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        win_d["cmp_indices"] = sel
+        calls.append(sfa.prepare_compress(L.compress_idx, cidx_d))
+        calls.append(sfa.prepare_indexer_prolog_run(L.indexer_prolog, ip_d))
+        qi, _, w = calls[-1].out
+        calls.append(sfa.prepare_indexer(qi, cidx_d["key_nope"], w, win_d["block_table_cmp"], win_d["cmp_len"],
+                                         batch=B, s1=S1, topk=K, out=sel))
+        n_pos = win.block_table_cmp.shape[1] * 128
+        bytes_by_stage["compressors"] += compress_algorithmic_bytes(L.compress_idx)
+        bytes_by_stage["indexer_prolog"] = prolog_work(L.indexer_prolog)[0]
+        # the live index keys once per batch, the tokens' index queries and weights, the scores
+        # written and read back by the selection, the selected positions
+        bytes_by_stage["indexer"] = int(win.cmp_len.astype(np.int64).sum()) * 256 + T * (64 * 128 * 2 + 64 * 4) \
+            + 2 * T * n_pos * 4 + T * K * 4
     calls.append(sfa.prepare_window_run(win, win_d, out=out))
     torch.cuda.synchronize()
 
@@ -876,25 +892,15 @@ def bench_v4_layer(args):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / args.steps * 1e3
-    # algorithmic bytes: each stage's own count (as in its bench line), summed
-    import oracle.window_oracle as WO
-    pro_bytes, pro_flop = prolog_work(pro)
-    ip_bytes, ip_flop = prolog_work(ip)
-    cw_bytes = T * (1024 + 1024 + 4 + 4)
-    cmp_bytes = compress_algorithmic_bytes(L.compress_att) + compress_algorithmic_bytes(L.compress_idx)
-    n_pos = win.block_table_cmp.shape[1] * 128
-    # the live index keys once per batch, the tokens' index queries and weights, the scores written
-    # and read back by the selection, the selected positions
-    idx_bytes = int(win.cmp_len.astype(np.int64).sum()) * 256 + T * (64 * 128 * 2 + 64 * 4) + 2 * T * n_pos * 4 \
-        + T * K * 4
-    valid = sum(len(WO.token_rows(t, S1, win.window, sel.cpu().numpy(), win.block_table_ori, win.block_table_cmp,
-                                  win.ori_len, win.cmp_len, win.num_cache_rows)) for t in range(T))
-    att_bytes = valid * 1024 + T * (win.n_q * 512 * 2 * 2 + 4 * K)
-    nbytes = pro_bytes + cw_bytes + cmp_bytes + ip_bytes + idx_bytes + att_bytes
+    cmp_list = win_d["cmp_indices"].cpu().numpy() if win_d["cmp_indices"] is not None else None
+    valid = sum(len(WO.token_rows(t, S1, win.window, cmp_list, win.block_table_ori, win.block_table_cmp, win.ori_len,
+                                  win.cmp_len, win.num_cache_rows)) for t in range(T))
+    kc = 0 if cmp_list is None else cmp_list.shape[1]
+    bytes_by_stage[L.kind] = valid * 1024 + T * (win.n_q * 512 * 2 * 2 + 4 * kc)
+    nbytes = sum(bytes_by_stage.values())
     gbps = nbytes / (us * 1e-6) / 1e9
     rec = {
-        "metric": "us/step (V4 SCFA layer: prolog, cache write, compressors, indexer prolog, indexer, SCFA), "
-                  "B=64 S1=2 8K decode, D=512",
+        "metric": f"us/step (V4 {L.kind.upper()} layer), B=64 S1=2 8K decode, D=512",
         "value": round(us, 2),
         "unit": "us/step",
         "n_gpus": 1,
@@ -906,12 +912,13 @@ def bench_v4_layer(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": B, "s1": S1, "n_q": win.n_q, "head_dim": 512,
-                   "hidden": pro.hidden, "q_lora_rank": pro.q_lora_rank, "ori_len": int(win.ori_len.max()),
-                   "window": win.window, "compress_ratio": 4, "topk_cmp": K, "launches": 13},
+        "config": {"workload": args.workload, "layer": L.kind, "batch": B, "s1": S1, "n_q": win.n_q,
+                   "head_dim": 512, "hidden": pro.hidden, "q_lora_rank": pro.q_lora_rank,
+                   "ori_len": int(win.ori_len.max()), "window": win.window,
+                   "compress_ratio": {"swa": 1, "cfa": 128, "scfa": 4}[L.kind], "topk_cmp": K,
+                   "abi_calls": sum(len(c._calls) for c in calls)},
         "algorithmic_bytes_per_step": nbytes,
-        "bytes_by_stage": {"prolog": pro_bytes, "cache_write": cw_bytes, "compressors": cmp_bytes,
-                           "indexer_prolog": ip_bytes, "indexer": idx_bytes, "scfa": att_bytes},
+        "bytes_by_stage": bytes_by_stage,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
     }

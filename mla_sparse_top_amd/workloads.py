@@ -916,18 +916,19 @@ def prolog_v4_decode(seed: int = 0) -> PrologV4Inputs:
 
 @dataclasses.dataclass
 class V4LayerInputs:
-    """The inputs of one decode step of a DeepSeek-V4 SCFA layer (compression ratio 4) on 512-wide
-    rows, consistent across its steps: the hidden states go to the V4 MLA prolog and to the
-    indexer prolog (whose qr is the prolog's cq, filled in on the device); the new latent rows go
-    through the cache write into the original cache at the tokens' positions; the compressor
-    (512 channels) and the index-key compressor (128 channels, Hadamard) pool the new tokens into
-    the compressed caches; the Lightning Indexer scores the compressed index keys and its top-k
-    is the SCFA's compressed list; SCFA reads both caches."""
+    """The inputs of one decode step of a DeepSeek-V4 attention layer on 512-wide rows, consistent
+    across its steps. kind "swa" (compression ratio 1): the V4 MLA prolog, the cache write of the
+    new latent rows into the original cache, SWA. kind "cfa" (ratio 128): also the compressor
+    (512 channels) into the compressed cache, and CFA over every causal compressed entry. kind
+    "scfa" (ratio 4): also the index-key compressor (128 channels, Hadamard), the indexer prolog
+    (whose qr is the prolog's cq, filled in on the device), the Lightning Indexer over the
+    compressed index keys, and SCFA over its top-k."""
+    kind: str
     prolog: PrologV4Inputs
-    window: WindowInputs        # pools, block tables and lengths (its cmp_indices are replaced)
-    compress_att: CompressInputs  # 512-channel rows into the window's pool (block_table_cmp)
-    compress_idx: CompressInputs  # 128-channel rows into the index-key pool (same block table)
-    indexer_prolog: IndexerPrologInputs
+    window: WindowInputs        # pools, block tables and lengths (SCFA: its cmp_indices are replaced)
+    compress_att: Optional[CompressInputs]  # 512-channel rows into the window's pool (block_table_cmp)
+    compress_idx: Optional[CompressInputs]  # 128-channel rows into the index-key pool (same block table)
+    indexer_prolog: Optional[IndexerPrologInputs]
     topk_cmp: int
 
     @property
@@ -935,45 +936,69 @@ class V4LayerInputs:
         return self.prolog.positions
 
 
-def v4_scfa_layer_generate(*, batch: int, s1: int, n_q: int, hidden: int, q_lora_rank: int,
-                           ori_lens: Sequence[int], window: int, topk_cmp: int, ratio: int = 4,
-                           seed: int = 0, name: str = "") -> V4LayerInputs:
+def v4_layer_generate(*, kind: str, batch: int, s1: int, n_q: int, hidden: int, q_lora_rank: int,
+                      ori_lens: Sequence[int], window: int, topk_cmp: int = 0, seed: int = 0,
+                      name: str = "") -> V4LayerInputs:
     """Token t = b * s1 + s sits at position ori_len[b] - s1 + s (the window inputs' rule); the
     RoPE tables cover max(ori_lens) positions. The compressors' kv and score are random fp32 (the
-    outputs of projection GEMMs outside the step)."""
+    outputs of projection GEMMs outside the step). SCFA's ratio is 4, CFA's 128."""
+    assert kind in ("swa", "cfa", "scfa")
+    ratio = {"swa": 1, "cfa": 128, "scfa": 4}[kind]
     ori = [int(v) for v in ori_lens]
     pos = [ori[t // s1] - s1 + t % s1 for t in range(batch * s1)]
     n_pos = max(ori)
-    win = window_generate(batch=batch, s1=s1, n_q=n_q, ori_lens=ori, window=window, ratio=ratio,
-                          cmp_mode="sparse", topk_cmp=topk_cmp, seed=seed, rope_dim=0, name=name)
+    mode = {"swa": "none", "cfa": "all", "scfa": "sparse"}[kind]
+    win = window_generate(batch=batch, s1=s1, n_q=n_q, ori_lens=ori, window=window, ratio=max(ratio, 4),
+                          cmp_mode=mode, topk_cmp=topk_cmp, seed=seed, rope_dim=0, name=name)
     pro = prolog_v4_generate(tokens=batch * s1, n_q=n_q, hidden=hidden, q_lora_rank=q_lora_rank, positions=pos,
                              rope_positions=n_pos, seed=seed + 7)
-    starts = [v - s1 for v in ori]
-    mb_cmp = win.block_table_cmp.shape[1]
-    rows = win.num_cache_rows
-    catt = compress_generate(batch=batch, s1=s1, ratio=ratio, start_pos=starts, rope_positions=n_pos,
-                             max_blocks=mb_cmp, n_pool_blocks=rows // BLOCK_SIZE, seed=seed + 11,
-                             block_table=win.block_table_cmp, channels=KV_LORA_RANK)
-    catt.key_nope = win.key_nope
-    cidx = compress_generate(batch=batch, s1=s1, ratio=ratio, start_pos=starts, rope_positions=n_pos,
-                             max_blocks=mb_cmp, n_pool_blocks=rows // BLOCK_SIZE, seed=seed + 13,
-                             block_table=win.block_table_cmp, channels=128, rotate=True)
-    # the index keys already in the compressed index-key cache: N(0,1) bf16 (the generator's
-    # random bit patterns, which catch stray writes in the compressor's own tests, hold NaNs)
-    cidx.key_nope = _normal_bf16(torch.Generator().manual_seed(130_000 + int(seed)), rows, 128)
-    ip = indexer_prolog_generate(tokens=batch * s1, hidden=hidden, q_lora_rank=q_lora_rank, positions=pos,
-                                 rope_positions=n_pos, rotate=True, seed=seed + 17)
-    ip.x = pro.x  # one hidden state per token feeds both prologs
-    return V4LayerInputs(prolog=pro, window=win, compress_att=catt, compress_idx=cidx, indexer_prolog=ip,
+    catt = cidx = ip = None
+    if kind != "swa":
+        starts = [v - s1 for v in ori]
+        mb_cmp = win.block_table_cmp.shape[1]
+        rows = win.num_cache_rows
+        catt = compress_generate(batch=batch, s1=s1, ratio=ratio, start_pos=starts, rope_positions=n_pos,
+                                 max_blocks=mb_cmp, n_pool_blocks=rows // BLOCK_SIZE, seed=seed + 11,
+                                 block_table=win.block_table_cmp, channels=KV_LORA_RANK)
+        catt.key_nope = win.key_nope
+    if kind == "scfa":
+        cidx = compress_generate(batch=batch, s1=s1, ratio=ratio, start_pos=starts, rope_positions=n_pos,
+                                 max_blocks=mb_cmp, n_pool_blocks=rows // BLOCK_SIZE, seed=seed + 13,
+                                 block_table=win.block_table_cmp, channels=128, rotate=True)
+        # the index keys already in the compressed index-key cache: N(0,1) bf16 (the generator's
+        # random bit patterns, which catch stray writes in the compressor's own tests, hold NaNs)
+        cidx.key_nope = _normal_bf16(torch.Generator().manual_seed(130_000 + int(seed)), rows, 128)
+        ip = indexer_prolog_generate(tokens=batch * s1, hidden=hidden, q_lora_rank=q_lora_rank, positions=pos,
+                                     rope_positions=n_pos, rotate=True, seed=seed + 17)
+        ip.x = pro.x  # one hidden state per token feeds both prologs
+    return V4LayerInputs(kind=kind, prolog=pro, window=win, compress_att=catt, compress_idx=cidx, indexer_prolog=ip,
                          topk_cmp=int(topk_cmp))
 
 
+def v4_scfa_layer_generate(**kw) -> V4LayerInputs:
+    return v4_layer_generate(kind="scfa", **kw)
+
+
+def v4_layer_decode(kind: str, seed: int = 0) -> V4LayerInputs:
+    """One decode step of a V4 layer at the pages' shape: 64 sequences x 2 new tokens, 8K of
+    original cache, window 128; SCFA with ratio 4 (2,048 compressed entries) and 512 entries
+    selected per token, CFA with ratio 128 (every causal entry of 64); 128 heads of 512 channels,
+    hidden 4096, query rank 1536."""
+    return v4_layer_generate(kind=kind, batch=64, s1=2, n_q=128, hidden=4096, q_lora_rank=1536, ori_lens=[8192] * 64,
+                             window=128, topk_cmp=512 if kind == "scfa" else 0, seed=seed,
+                             name=f"v4_{kind}_layer_b64_s2")
+
+
 def v4_scfa_layer_decode(seed: int = 0) -> V4LayerInputs:
-    """One decode step of a V4 SCFA layer at the pages' shape: 64 sequences x 2 new tokens, 8K of
-    original cache, window 128, ratio 4 (2,048 compressed entries), 512 entries selected per
-    token; 128 heads of 512 channels, hidden 4096, query rank 1536."""
-    return v4_scfa_layer_generate(batch=64, s1=2, n_q=128, hidden=4096, q_lora_rank=1536, ori_lens=[8192] * 64,
-                                  window=128, topk_cmp=512, seed=seed, name="v4_scfa_layer_b64_s2")
+    return v4_layer_decode("scfa", seed)
+
+
+def v4_swa_layer_decode(seed: int = 0) -> V4LayerInputs:
+    return v4_layer_decode("swa", seed)
+
+
+def v4_cfa_layer_decode(seed: int = 0) -> V4LayerInputs:
+    return v4_layer_decode("cfa", seed)
 
 
 def compress_index_decode(seed: int = 0, ratio: int = 4) -> CompressInputs:

@@ -1,7 +1,9 @@
-"""One decode step of a DeepSeek-V4 SCFA layer on 512-wide rows, end to end on the GPU: the V4 MLA
-prolog, the cache write of the new latent rows, the compressor (512 channels) and the index-key
-compressor (128 channels, Hadamard), the indexer prolog on the prolog's cq, the Lightning Indexer
-over the compressed index keys with its top-k, and SCFA over the original and compressed caches
+"""One decode step of a DeepSeek-V4 attention layer on 512-wide rows, end to end on the GPU. SCFA
+layer: the V4 MLA prolog, the cache write of the new latent rows, the compressor (512 channels)
+and the index-key compressor (128 channels, Hadamard), the indexer prolog on the prolog's cq, the
+Lightning Indexer over the compressed index keys with its top-k, and SCFA over the original and
+compressed caches. CFA layer: the prolog, the cache write, the compressor at ratio 128, CFA over
+every causal compressed entry. SWA layer: the prolog, the cache write, SWA
 ("NPU DeepSeek-V4 model PyPTO fused-operator optimisation": MlaProlog, Compressor, IndexerProlog,
 FA-class operators; "CANN DeepSeek Indexer attention optimisation": Lightning Indexer).
 
@@ -42,35 +44,42 @@ def run_layer(sfa, L):
 
     B, S1 = L.window.batch, L.window.s1
     T, K = B * S1, L.topk_cmp
+    r = {}
     pro_d = sfa.prolog_v4_to_device(L.prolog)
     win_d = sfa.window_to_device(L.window)
-    catt_d = sfa.compress_to_device(L.compress_att)
-    catt_d["key_nope"] = win_d["key_nope"]          # the compressed entries share the window's pool
-    cidx_d = sfa.compress_to_device(L.compress_idx)  # the index-key pool
-    ip_d = sfa.indexer_prolog_to_device(L.indexer_prolog)
     pos = torch.from_numpy(L.positions).cuda()
     cq = torch.empty((T, L.prolog.q_lora_rank), dtype=torch.bfloat16, device="cuda")
     q, kv = sfa.run_prolog_v4(L.prolog, pro_d, cq_out=cq)
     sfa.cache_write(kv, None, pos, win_d["block_table_ori"], win_d["key_nope"], None, None, batch=B, s1=S1)
-    sfa.run_compress(L.compress_att, catt_d)
-    sfa.run_compress(L.compress_idx, cidx_d)
-    ip_d["qr"] = cq
-    q_index, _k, w = sfa.run_indexer_prolog(L.indexer_prolog, ip_d)
-    scores = sfa.indexer_scores(q_index, cidx_d["key_nope"], w, win_d["block_table_cmp"], win_d["cmp_len"], batch=B,
-                                s1=S1, topk=K)
-    sel = sfa.topk_select(scores, win_d["cmp_len"], batch=B, s1=S1, topk=K)
+    if L.compress_att is not None:
+        catt_d = sfa.compress_to_device(L.compress_att)
+        catt_d["key_nope"] = win_d["key_nope"]          # the compressed entries share the window's pool
+        sfa.run_compress(L.compress_att, catt_d)
+        r["catt"] = catt_d
+    if L.kind == "scfa":
+        cidx_d = sfa.compress_to_device(L.compress_idx)  # the index-key pool
+        sfa.run_compress(L.compress_idx, cidx_d)
+        ip_d = sfa.indexer_prolog_to_device(L.indexer_prolog)
+        ip_d["qr"] = cq
+        q_index, _k, w = sfa.run_indexer_prolog(L.indexer_prolog, ip_d)
+        scores = sfa.indexer_scores(q_index, cidx_d["key_nope"], w, win_d["block_table_cmp"], win_d["cmp_len"],
+                                    batch=B, s1=S1, topk=K)
+        sel = sfa.topk_select(scores, win_d["cmp_len"], batch=B, s1=S1, topk=K)
+        win_d["cmp_indices"] = sel
+        r.update(cidx=cidx_d, q_index=q_index, w=w, scores=scores, sel=sel)
     win_d["query_nope"] = q
-    win_d["cmp_indices"] = sel
     out = sfa.run_window(L.window, win_d)
     torch.cuda.synchronize()
-    return dict(q=q, kv=kv, cq=cq, pool=win_d["key_nope"], catt=catt_d, cidx=cidx_d, q_index=q_index, w=w,
-                scores=scores, sel=sel, out=out)
+    r.update(q=q, kv=kv, cq=cq, pool=win_d["key_nope"], out=out)
+    return r
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_v4_scfa_layer_step(sfa_lib, seed):
-    L = W.v4_scfa_layer_generate(batch=3, s1=2, n_q=16, hidden=256, q_lora_rank=256, ori_lens=[600, 300, 132],
-                                 window=64, topk_cmp=24, seed=seed)
+@pytest.mark.parametrize("kind,seed", [("scfa", 0), ("scfa", 1), ("cfa", 0), ("swa", 0)])
+def test_v4_layer_step(sfa_lib, kind, seed):
+    # lengths that are multiples of 128: every sequence's second token closes a window at ratio
+    # 128 as well as at ratio 4
+    L = W.v4_layer_generate(kind=kind, batch=3, s1=2, n_q=16, hidden=256, q_lora_rank=256,
+                            ori_lens=[640, 384, 256], window=64, topk_cmp=24 if kind == "scfa" else 0, seed=seed)
     r = run_layer(sfa_lib, L)
     pro, win = L.prolog, L.window
     T = pro.tokens
@@ -87,10 +96,12 @@ def test_v4_scfa_layer_step(sfa_lib, seed):
     rows = [int(win.block_table_ori[t // 2, p // 128]) * 128 + p % 128 for t, p in enumerate(pro.positions)]
     assert np.array_equal(pool[rows], kv_bits)
 
-    # 3-4. both compressors: states bit for bit, every written row to the bar (each sequence's
+    # 3-4. the compressors: states bit for bit, every written row to the bar (each sequence's
     # second token closes a window)
-    for name, inp, d, base in (("compress_att", L.compress_att, r["catt"], None),
-                               ("compress_idx", L.compress_idx, r["cidx"], None)):
+    comps = [] if kind == "swa" else [("compress_att", L.compress_att, r["catt"])]
+    if kind == "scfa":
+        comps.append(("compress_idx", L.compress_idx, r["cidx"]))
+    for name, inp, d in comps:
         ks, ss, entries = C.compress(inp)
         np.testing.assert_array_equal(d["kv_state"].cpu().numpy().view(np.uint32), ks.view(np.uint32))
         np.testing.assert_array_equal(d["score_state"].cpu().numpy().view(np.uint32), ss.view(np.uint32))
@@ -99,6 +110,15 @@ def test_v4_scfa_layer_step(sfa_lib, seed):
         for b, c, row, y in entries:
             assert row >= 0 and c == int(win.cmp_len[b]) - 1, name
             _close(f"{name} row {row}", P.bf16_bits_to_f64(got[row]), y)
+
+    if kind != "scfa":
+        # 7. SWA / CFA over the GPU's pool and queries (CFA: every causal entry, the newest one
+        # just written by the compressor)
+        win.query_nope, win.key_nope = q_bits, pool
+        out_ref = WO.window_attention(win)
+        rep = O.allclose_report(r["out"].float().cpu().numpy().astype(np.float64).reshape(out_ref.shape), out_ref)
+        assert rep["fails"] == 0, rep
+        return
 
     # 5. the indexer prolog on the GPU's cq
     ip = L.indexer_prolog
