@@ -152,8 +152,11 @@ __device__ __forceinline__ bf16x8 lds16(const lds_char_t* p) {
 // A workgroup owns 32 * kFb features x 128 tokens and walks its k range in chunks of 64 (one
 // 128-byte line per row). Wave w owns tokens 32w .. 32w + 31 and all the workgroup's features,
 // so its accumulators are whole sums. Weight rows and token rows reach LDS by LDS-DMA, eight
-// rows x 128 bytes per instruction, the 16-byte piece p of row r stored at position p ^ (r & 7)
-// so that the operand reads are free of bank conflicts. Waves 0 and 1 issue the weights' DMA
+// rows x 128 bytes per instruction, the 16-byte piece p of row r stored at position
+// p ^ ((r >> 1) & 7) so that the operand reads are free of bank conflicts: a 16-byte-per-lane
+// LDS read is served 16 lanes at a time over 64 banks (256 bytes), and its 16 lanes read 16
+// consecutive rows, whose row pairs fill the two 128-byte halves and take 8 distinct positions
+// in each. Waves 0 and 1 issue the weights' DMA
 // (from HBM, through a deep ring), waves 2 and 3 the token rows' (from L2, a shallow ring):
 // a wave's loads complete in issue order, so a wave that waits for one stream never waits
 // for the other. The outputs are staged through LDS and stored as whole rows.
@@ -231,10 +234,11 @@ __global__ void __launch_bounds__(kThreads, 1) prolog_gemm_kernel(const PrologGe
   const int kc0 = kMode == 2 ? 0 : split * a.k_chunk;
   const int nch = (kMode == 2 ? a.k : a.k_chunk) / 64;
 
-  // DMA lane geometry: lane L carries row (L >> 3) of an 8-row group and stores its piece at
-  // position L & 7, so it loads piece (L & 7) ^ (L >> 3) of its row
+  // DMA lane geometry: lane L carries row (L >> 3) of an 8-row group starting at row 8j and
+  // stores its piece at position L & 7, so it loads piece (L & 7) ^ (L >> 4) ^ 4 (j & 1) of its
+  // row (row >> 1 is 4j + (L >> 4))
   const uint32_t drow = (uint32_t)(lane >> 3);
-  const uint32_t dpiece = 16u * ((uint32_t)(lane & 7) ^ drow);
+  const uint32_t dpiece = 16u * ((uint32_t)(lane & 7) ^ (drow >> 1));
   const bool w_wave = wave < 2;
   u32x4 rs0, rs1;
   uint32_t row_bytes;
@@ -259,16 +263,17 @@ __global__ void __launch_bounds__(kThreads, 1) prolog_gemm_kernel(const PrologGe
       const uint32_t st = lds_base + (uint32_t)((c % kWStages) * kWBytes);
 #pragma unroll
       for (int i = 0; i < 2 * kFb; ++i) {
-        const uint32_t row0 = (uint32_t)(8 * (half + 2 * i));
-        dma16(rs0, (row0 + drow) * row_bytes + dpiece, kb, st + row0 * 128u);
+        const uint32_t row0 = (uint32_t)(8 * (half + 2 * i));  // group half + 2i: odd for wave 1
+        dma16(rs0, (row0 + drow) * row_bytes + (dpiece ^ (64u * (uint32_t)half)), kb, st + row0 * 128u);
       }
     } else {
       const uint32_t st = abase + (uint32_t)((c % kTStages) * kAStage);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t row0 = (uint32_t)(64 * half + 8 * i);
-        dma16(rs0, (row0 + drow) * row_bytes + dpiece, kb, st + row0 * 128u);
-        if (kLo) dma16(rs1, (row0 + drow) * row_bytes + dpiece, kb, st + kABytes + row0 * 128u);
+        const uint32_t row0 = (uint32_t)(64 * half + 8 * i);  // group 8 half + i
+        const uint32_t pc = dpiece ^ (64u * (uint32_t)(i & 1));
+        dma16(rs0, (row0 + drow) * row_bytes + pc, kb, st + row0 * 128u);
+        if (kLo) dma16(rs1, (row0 + drow) * row_bytes + pc, kb, st + kABytes + row0 * 128u);
       }
     }
   };
@@ -289,7 +294,7 @@ __global__ void __launch_bounds__(kThreads, 1) prolog_gemm_kernel(const PrologGe
   for (int c = 0; c < depth - 1; ++c)
     if (c < nch) issue(c);
   const int wave_row = 32 * wave + r;
-  const uint32_t rsw = 16u * (uint32_t)(r & 7);
+  const uint32_t rsw = 16u * (uint32_t)((r >> 1) & 7);  // rows 32 fb + r and 32 w + r
   for (int c = 0; c < nch; ++c) {
     wait_for(c);
     lds_barrier();  // chunk c visible to every wave; chunk c - 1's slots free again

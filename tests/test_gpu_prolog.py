@@ -56,6 +56,7 @@ def _run(sfa_lib, inp):
     (200, 1024, 512, 3, 128, 1),     # a full and a ragged token block, odd head count
     (1, 256, 256, 1, 64, 2),         # the smallest shapes
     (130, 4096, 1024, 16, 128, 3),   # V4's hidden width
+    (70, 512, 192, 128, 64, 4),      # three k chunks in one range: an odd chunk count
 ])
 def test_small_shapes(sfa_lib, tokens, hidden, q, n_q, dn, seed):
     pos = [(7 * t) % 300 for t in range(tokens)]
@@ -155,6 +156,7 @@ def _assert_close_v4(inp, got):
     (200, 1024, 512, 3, 1),      # a full and a ragged token block, odd head count
     (1, 256, 64, 1, 2),          # the smallest shapes
     (130, 4096, 1024, 16, 3),    # the page's hidden width
+    (100, 512, 192, 64, 4),      # three k chunks in one range: an odd chunk count
 ])
 def test_v4_small_shapes(sfa_lib, tokens, hidden, q, n_q, seed):
     """Positions (7t) mod 300 against 256 table rows: some tokens get zero rotary channels."""
