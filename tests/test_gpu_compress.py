@@ -315,3 +315,25 @@ def test_long_window_index_keys_rotated(sfa_lib):
     inp = W.compress_generate(batch=8, s1=1, ratio=128, start_pos=[127 + 128 * k for k in range(8)],
                               rope_positions=2048, max_blocks=2, seed=33, score_scale=4.0, channels=128, rotate=True)
     assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 8
+
+
+@pytest.mark.parametrize("channels", [576, 512, 128])
+def test_long_window_several_entries_in_one_call(sfa_lib, channels):
+    """300 tokens at ratio 128 from positions 0 and 100: two and three entries per sequence in one
+    call, the later ones pooling slots that earlier tokens of the call refreshed."""
+    inp = W.compress_generate(batch=2, s1=300, ratio=128, start_pos=[0, 100], rope_positions=512, max_blocks=2,
+                              seed=34, score_scale=2.0, channels=channels, rotate=channels == 128)
+    assert _assert_matches(inp, _host(_run(sfa_lib, inp))) == 5
+
+
+def test_long_window_c128a_repeats_bit_identically(sfa_lib):
+    """The c128a workload run three times from the same inputs writes the same bits."""
+    inp = W.compress_c128a(seed=3)
+    rows = None
+    for _ in range(3):
+        got = _host(_run(sfa_lib, inp))
+        if rows is None:
+            rows = got[2]
+            assert _assert_matches(inp, got) == 64
+        else:
+            np.testing.assert_array_equal(got[2], rows)
