@@ -62,7 +62,8 @@ typedef enum {
   SFA_ERR_ALIGN = -3,           /* a tensor pointer is not 16-byte aligned                    */
   SFA_ERR_WORKSPACE = -4,       /* workspace missing, misaligned, or smaller than required    */
   SFA_ERR_SCALES = -5,          /* INT8 cache without k_nope_scales                           */
-  SFA_ERR_ALIAS = -6,           /* out (or rows_out) overlaps an input or the workspace       */
+  SFA_ERR_ALIAS = -6,           /* an output overlaps an input or the workspace, or the
+                                   workspace overlaps an input                                */
   SFA_ERR_SCALE_VALUE = -7,     /* softmax_scale is not finite                                */
   SFA_ERR_HIP = -8,             /* a HIP runtime call failed                                  */
   SFA_ERR_SCRATCH_LIMIT = -9    /* sfa_decode_noalloc: the call needs more than its fixed

@@ -218,8 +218,10 @@ int sfa_mla_prolog(const sfa_prolog_dims* dims, const void* x, const void* w_dq,
     if (overlaps(outs[i], out_bytes[i], workspace, lay.total)) return SFA_ERR_ALIAS;
     if (overlaps(outs[i], out_bytes[i], cq_out, t * q * 2)) return SFA_ERR_ALIAS;
   }
-  for (int j = 0; j < 10; ++j)
+  for (int j = 0; j < 10; ++j) {
     if (overlaps(cq_out, t * q * 2, ins[j], in_bytes[j])) return SFA_ERR_ALIAS;
+    if (overlaps(workspace, lay.total, ins[j], in_bytes[j])) return SFA_ERR_ALIAS;  // written by the kernels
+  }
   if (overlaps(cq_out, t * q * 2, workspace, lay.total)) return SFA_ERR_ALIAS;
   char* ws = static_cast<char*>(workspace);
   float* part = reinterpret_cast<float*>(ws + lay.part);
@@ -350,6 +352,8 @@ int sfa_mla_prolog_v4(const sfa_prolog_v4_dims* dims, const void* x, const void*
       if (overlaps(all_outs[i], out_bytes[i], all_outs[j], out_bytes[j])) return SFA_ERR_ALIAS;
     if (overlaps(all_outs[i], out_bytes[i], workspace, lay.total)) return SFA_ERR_ALIAS;
   }
+  for (int j = 0; j < 9; ++j)
+    if (overlaps(workspace, lay.total, ins[j], in_bytes[j])) return SFA_ERR_ALIAS;  // written by the kernels
   char* ws = static_cast<char*>(workspace);
   float* part_down = reinterpret_cast<float*>(ws + lay.part_down);
   uint16_t* cq_hi = reinterpret_cast<uint16_t*>(ws + lay.cq_hi);
@@ -472,6 +476,8 @@ int sfa_indexer_prolog(const sfa_indexer_prolog_dims* dims, const void* x, const
       if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SFA_ERR_ALIAS;
     if (overlaps(outs[i], out_bytes[i], workspace, lay.total)) return SFA_ERR_ALIAS;
   }
+  for (int j = 0; j < 10; ++j)
+    if (overlaps(workspace, lay.total, ins[j], in_bytes[j])) return SFA_ERR_ALIAS;  // written by the kernels
   char* ws = static_cast<char*>(workspace);
   float* part_q = reinterpret_cast<float*>(ws + lay.part_q);
   float* part_kw = reinterpret_cast<float*>(ws + lay.part_kw);

@@ -182,6 +182,9 @@ int run_attention(const sfa_dims* d, int is_prefill, const void* qn, const void*
                           win ? (size_t)d->batch * sizeof(int32_t) : 0};
   for (int i = 0; i < 11; ++i)
     if (overlaps(out, out_bytes, ins[i], sizes[i])) return SFA_ERR_ALIAS;
+  // the kernels write the workspace: it must not hold an input either
+  for (int i = 0; i < 11; ++i)
+    if (i != 8 && overlaps(ins[8], sizes[8], ins[i], sizes[i])) return SFA_ERR_ALIAS;
 
   if (tokens == 0) return SFA_OK;
 
@@ -370,7 +373,7 @@ const char* sfa_status_string(int status) {
     case SFA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case SFA_ERR_WORKSPACE: return "workspace missing, not 256-byte aligned, or smaller than sfa_workspace_size";
     case SFA_ERR_SCALES: return "INT8 cache requires k_nope_scales";
-    case SFA_ERR_ALIAS: return "output overlaps an input or the workspace";
+    case SFA_ERR_ALIAS: return "an output overlaps an input or the workspace, or the workspace overlaps an input";
     case SFA_ERR_SCALE_VALUE: return "softmax_scale is not finite";
     case SFA_ERR_HIP: return "a HIP runtime call failed";
     case SFA_ERR_SCRATCH_LIMIT: return "the call needs more workspace than sfa_decode_noalloc's fixed scratch "

@@ -143,6 +143,7 @@ def test_workspace_errors():
     assert _call("sfa_decode", d, ws=0x50000010, ws_bytes=need) == -4      # not 256-aligned
     # output inside the workspace
     assert _call("sfa_decode", d, {"out": 0x50000000 + 4096}, ws=0x50000000, ws_bytes=need) == -6
+    assert _call("sfa_decode", d, ws=0x10000000, ws_bytes=need) == -6      # workspace over the key pool
 
 
 def test_empty_batch_is_a_no_op():
@@ -544,3 +545,13 @@ def test_indexer_prolog_workspace_and_validation():
     assert _ip_call(d, {"q": 0x100000000 * 2 + 256}) == -6           # q_index inside qr
     assert _ip_call(d, {"w": 0x7000000000 + 1024}) == -6             # weights inside the workspace
     assert _ip_call(_ip_dims(tokens=0), {"x": None, "q": None}, ws=None, ws_bytes=0) == 0
+
+
+def test_workspace_over_an_input_is_rejected():
+    """The kernels write their workspace, so a workspace over an input is an alias error; each
+    call here fails validation before any launch."""
+    assert _prolog_call(_prolog_dims(), ws=0x100000000) == -6        # over x
+    assert _v4_call(_v4_dims(), ws=0x100000000) == -6                # over x
+    assert _v4_call(_v4_dims(), ws=0x400000000) == -6                # over w_uq
+    assert _ip_call(_ip_dims(), ws=0x200000000) == -6                # over qr
+    assert "workspace overlaps an input" in sfa.status_string(-6)
