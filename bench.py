@@ -1147,8 +1147,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sparse attention path has no "
-              f"cross-GPU component in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the sparse attention path has no "
+              f"cross-GPU component.", file=sys.stderr)
         sys.exit(2)
 
     import torch
