@@ -827,7 +827,12 @@ def bench_v4_layer(args):
     (window 128 + the 512 selected entries): 13 launches. CFA layer (ratio 128): the prolog, the
     cache write, the compressor, CFA over every causal entry: 7 launches. SWA layer: the prolog,
     the cache write, SWA: 6 launches. The SCFA step's footprint (~0.5 GB: weights, pools, scores)
-    exceeds the 256 MB MALL, so one input set is used for all three."""
+    exceeds the 256 MB MALL, so one input set is used for all three.
+    The compressors read only the step's projections, not the prolog's outputs, so they run on a
+    second stream beside the prolog: that stream waits for the previous step to end (its pool
+    rows are read there), and the main stream waits for the compressors before the first launch
+    that reads their rows (the indexer, or the attention). A one-stream run of the same launches
+    first gives the reference output, which the two-stream run must match bit for bit."""
     import numpy as np
     import torch
 
@@ -847,16 +852,20 @@ def bench_v4_layer(args):
     kv = torch.empty((T, 512), dtype=torch.bfloat16, device="cuda")
     out = torch.empty((B, S1, win.n_q, 512), dtype=torch.bfloat16, device="cuda")
     win_d["query_nope"] = q
-    calls = [
+    side = torch.cuda.Stream()  # default priority
+    # main stream: prolog, cache write (, indexer prolog) | wait for the compressors | the rest
+    head = [
         sfa.prepare_prolog_v4_run(pro, pro_d, out=(q, kv), cq_out=cq),
         sfa.prepare_cache_write(kv, None, pos, win_d["block_table_ori"], win_d["key_nope"], None, None, batch=B,
                                 s1=S1),
     ]
+    comp, comp_one, tail = [], [], []  # compressors on the side stream (and on the main stream)
     bytes_by_stage = {"prolog": prolog_work(pro)[0], "cache_write": T * (1024 + 1024 + 4 + 4)}
     if L.compress_att is not None:
         catt_d = sfa.compress_to_device(L.compress_att)
         catt_d["key_nope"] = win_d["key_nope"]
-        calls.append(sfa.prepare_compress(L.compress_att, catt_d))
+        comp.append(sfa.prepare_compress(L.compress_att, catt_d, stream=side))
+        comp_one.append(sfa.prepare_compress(L.compress_att, catt_d))
         bytes_by_stage["compressors"] = compress_algorithmic_bytes(L.compress_att)
     if L.kind == "scfa":
         cidx_d = sfa.compress_to_device(L.compress_idx)
@@ -864,11 +873,12 @@ def bench_v4_layer(args):
         ip_d["qr"] = cq
         sel = torch.empty((T, K), dtype=torch.int32, device="cuda")
         win_d["cmp_indices"] = sel
-        calls.append(sfa.prepare_compress(L.compress_idx, cidx_d))
-        calls.append(sfa.prepare_indexer_prolog_run(L.indexer_prolog, ip_d))
-        qi, _, w = calls[-1].out
-        calls.append(sfa.prepare_indexer(qi, cidx_d["key_nope"], w, win_d["block_table_cmp"], win_d["cmp_len"],
-                                         batch=B, s1=S1, topk=K, out=sel))
+        comp.append(sfa.prepare_compress(L.compress_idx, cidx_d, stream=side))
+        comp_one.append(sfa.prepare_compress(L.compress_idx, cidx_d))
+        head.append(sfa.prepare_indexer_prolog_run(L.indexer_prolog, ip_d))
+        qi, _, w = head[-1].out
+        tail.append(sfa.prepare_indexer(qi, cidx_d["key_nope"], w, win_d["block_table_cmp"], win_d["cmp_len"],
+                                        batch=B, s1=S1, topk=K, out=sel))
         n_pos = win.block_table_cmp.shape[1] * 128
         bytes_by_stage["compressors"] += compress_algorithmic_bytes(L.compress_idx)
         bytes_by_stage["indexer_prolog"] = prolog_work(L.indexer_prolog)[0]
@@ -876,12 +886,30 @@ def bench_v4_layer(args):
         # written and read back by the selection, the selected positions
         bytes_by_stage["indexer"] = int(win.cmp_len.astype(np.int64).sum()) * 256 + T * (64 * 128 * 2 + 64 * 4) \
             + 2 * T * n_pos * 4 + T * K * 4
-    calls.append(sfa.prepare_window_run(win, win_d, out=out))
+    tail.append(sfa.prepare_window_run(win, win_d, out=out))
+    calls = head + comp + tail
+    main = torch.cuda.current_stream()
+    step_end, comp_done = torch.cuda.Event(), torch.cuda.Event()
+    # the reference: every launch in order on the main stream, from the inputs as generated
+    for c in head + comp_one + tail:
+        c()
     torch.cuda.synchronize()
+    ref_out = out.clone()
+    step_end.record(main)
 
     def step(i):
-        for c in calls:
+        if comp:
+            side.wait_event(step_end)
+            for c in comp:
+                c()
+            comp_done.record(side)
+        for c in head:
             c()
+        if comp:
+            main.wait_event(comp_done)
+        for c in tail:
+            c()
+        step_end.record(main)
 
     n_warm = warm_up(step, args, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -892,6 +920,9 @@ def bench_v4_layer(args):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / args.steps * 1e3
+    # every step recomputes the same rows from the same inputs, so the output must equal the
+    # one-stream reference bit for bit
+    two_stream_identical = bool(torch.equal(out.view(torch.int16), ref_out.view(torch.int16)))
     cmp_list = win_d["cmp_indices"].cpu().numpy() if win_d["cmp_indices"] is not None else None
     valid = sum(len(WO.token_rows(t, S1, win.window, cmp_list, win.block_table_ori, win.block_table_cmp, win.ori_len,
                                   win.cmp_len, win.num_cache_rows)) for t in range(T))
@@ -921,8 +952,12 @@ def bench_v4_layer(args):
         "bytes_by_stage": bytes_by_stage,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "streams": 2 if comp else 1,
+        "outputs_match_one_stream": two_stream_identical,
     }
     print(json.dumps(rec), flush=True)
+    if not two_stream_identical:
+        sys.exit("the two-stream layer step differs from the one-stream chain")
 
 
 PROLOG_WORKLOADS = {"mla_prolog_b64_s2": "prolog_decode", "indexer_prolog_b64_s2": "indexer_prolog_decode",
