@@ -311,10 +311,11 @@ def bench_indexer(args):
 
 
 def bench_decode_step(args):
-    """One decode step of one layer at B=64, S1=2, 8K of cache, chained on one stream: the cache
-    write of the 128 new latent rows (positions 8190 and 8191), the indexer's scores and top-k
-    (2048 of 8192), and the sparse attention over the selected rows (bf16 cache). --sets
-    copies of both pools in different block orders are rotated."""
+    """One decode step of one layer at B=64, S1=2, 8K of cache: the cache write of the 128 new
+    latent rows (positions 8190 and 8191), the indexer's scores and top-k (2048 of 8192), and
+    the sparse attention over the selected rows (bf16 cache). --sets copies of both pools in
+    different block orders are rotated. The cache write does not feed the indexer, so it runs on
+    a second stream beside it (after the previous step's end); the attention waits for both."""
     import numpy as np
     import torch
 
@@ -332,6 +333,9 @@ def bench_decode_step(args):
     T, K = lat.n_tokens, lat.topk
     lat0 = sfa.to_device(lat)
     ix0 = sfa.indexer_to_device(idx_inp)
+    side = torch.cuda.Stream()  # default priority
+    main = torch.cuda.current_stream()
+    step_end, cw_done = torch.cuda.Event(), torch.cuda.Event()
     nw = sfa.cache_to_device(new)
     sets = []
     for i in range(max(1, args.sets)):
@@ -350,7 +354,7 @@ def bench_decode_step(args):
         topk = torch.empty((T, K), dtype=torch.int32, device="cuda")
         out = torch.empty((lat.batch, lat.s1, lat.n_q, 512), dtype=torch.bfloat16, device="cuda")
         cw = sfa.prepare_cache_write(nw["new_nope"], nw["new_rope"], nw["positions"], ld["block_table"], ld["key_nope"],
-                                     ld["key_rope"], None, batch=64, s1=2)
+                                     ld["key_rope"], None, batch=64, s1=2, stream=side)
         ix = sfa.prepare_indexer(xd["q_index"], xd["k_index"], xd["weights"], xd["block_table"], xd["kv_act_seqs"],
                                  batch=64, s1=2, topk=K, out=topk)
         at = sfa.prepare_decode(ld["query_nope"], ld["query_rope"], ld["key_nope"], ld["key_rope"], None, topk,
@@ -358,11 +362,17 @@ def bench_decode_step(args):
         sets.append((cw, ix, at, topk, out))
     torch.cuda.synchronize()
 
+    step_end.record(main)
+
     def step(i):
         cw, ix, at, _, _ = sets[i % len(sets)]
+        side.wait_event(step_end)  # the previous step's attention has read the pool
         cw()
+        cw_done.record(side)
         ix()
+        main.wait_event(cw_done)
         at()
+        step_end.record(main)
 
     n_warm = warm_up(step, args, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
