@@ -838,11 +838,13 @@ def bench_v4_layer(args):
     cache write, the compressor, CFA over every causal entry: 7 launches. SWA layer: the prolog,
     the cache write, SWA: 6 launches. The SCFA step's footprint (~0.5 GB: weights, pools, scores)
     exceeds the 256 MB MALL, so one input set is used for all three.
-    The compressors read only the step's projections, not the prolog's outputs, so they run on a
-    second stream beside the prolog: that stream waits for the previous step to end (its pool
-    rows are read there), and the main stream waits for the compressors before the first launch
-    that reads their rows (the indexer, or the attention). A one-stream run of the same launches
-    first gives the reference output, which the two-stream run must match bit for bit."""
+    In the CFA and SCFA steps the compressors read only the step's projections, so they run on a
+    second stream beside the prolog, after the previous step's end (its launches read the rows
+    they rewrite); the same stream then waits for the prolog's kv_ready event (kv and cq
+    complete) and runs the cache write and the indexer prolog beside the prolog's query
+    up-projection. The main stream waits for that stream before the indexer and the attention.
+    A one-stream run of the same launches first gives the reference output, which the
+    two-stream run must match bit for bit. The SWA step runs on one stream."""
     import numpy as np
     import torch
 
@@ -863,13 +865,16 @@ def bench_v4_layer(args):
     out = torch.empty((B, S1, win.n_q, 512), dtype=torch.bfloat16, device="cuda")
     win_d["query_nope"] = q
     side = torch.cuda.Stream()  # default priority
-    # main stream: prolog, cache write (, indexer prolog) | wait for the compressors | the rest
-    head = [
-        sfa.prepare_prolog_v4_run(pro, pro_d, out=(q, kv), cq_out=cq),
-        sfa.prepare_cache_write(kv, None, pos, win_d["block_table_ori"], win_d["key_nope"], None, None, batch=B,
-                                s1=S1),
-    ]
-    comp, comp_one, tail = [], [], []  # compressors on the side stream (and on the main stream)
+    main = torch.cuda.current_stream()
+    kv_ready = torch.cuda.Event()  # recorded by the prolog once kv and cq are complete
+    prolog = sfa.prepare_prolog_v4_run(pro, pro_d, out=(q, kv), cq_out=cq, kv_ready=kv_ready)
+    # on the side stream: the compressors (they read only the step's projections), then, once the
+    # prolog's kv and cq are complete, the cache write (and the indexer prolog); the one-stream
+    # reference runs the same launches on the main stream
+    comp, comp_one, post, post_one, tail = [], [], [], [], []
+    for strm, lst in ((side, post), (None, post_one)):
+        lst.append(sfa.prepare_cache_write(kv, None, pos, win_d["block_table_ori"], win_d["key_nope"], None, None,
+                                           batch=B, s1=S1, stream=strm))
     bytes_by_stage = {"prolog": prolog_work(pro)[0], "cache_write": T * (1024 + 1024 + 4 + 4)}
     if L.compress_att is not None:
         catt_d = sfa.compress_to_device(L.compress_att)
@@ -885,8 +890,9 @@ def bench_v4_layer(args):
         win_d["cmp_indices"] = sel
         comp.append(sfa.prepare_compress(L.compress_idx, cidx_d, stream=side))
         comp_one.append(sfa.prepare_compress(L.compress_idx, cidx_d))
-        head.append(sfa.prepare_indexer_prolog_run(L.indexer_prolog, ip_d))
-        qi, _, w = head[-1].out
+        post.append(sfa.prepare_indexer_prolog_run(L.indexer_prolog, ip_d, stream=side))
+        post_one.append(sfa.prepare_indexer_prolog_run(L.indexer_prolog, ip_d, out=post[-1].out))
+        qi, _, w = post[-1].out
         tail.append(sfa.prepare_indexer(qi, cidx_d["key_nope"], w, win_d["block_table_cmp"], win_d["cmp_len"],
                                         batch=B, s1=S1, topk=K, out=sel))
         n_pos = win.block_table_cmp.shape[1] * 128
@@ -897,26 +903,33 @@ def bench_v4_layer(args):
         bytes_by_stage["indexer"] = int(win.cmp_len.astype(np.int64).sum()) * 256 + T * (64 * 128 * 2 + 64 * 4) \
             + 2 * T * n_pos * 4 + T * K * 4
     tail.append(sfa.prepare_window_run(win, win_d, out=out))
-    calls = head + comp + tail
-    main = torch.cuda.current_stream()
-    step_end, comp_done = torch.cuda.Event(), torch.cuda.Event()
+    # without a compressor (SWA) the cache write alone is too short to pay for the cross-stream
+    # waits (measured 113.2 µs on one stream against 118.6 with it on the second), so it stays
+    # on the main stream
+    use_side = bool(comp)
+    calls = [prolog] + comp + (post if use_side else post_one) + tail
+    step_end, side_done = torch.cuda.Event(), torch.cuda.Event()
     # the reference: every launch in order on the main stream, from the inputs as generated
-    for c in head + comp_one + tail:
+    for c in [prolog] + post_one + comp_one + tail:
         c()
     torch.cuda.synchronize()
     ref_out = out.clone()
     step_end.record(main)
 
     def step(i):
-        if comp:
-            side.wait_event(step_end)
-            for c in comp:
+        if not use_side:
+            for c in [prolog] + post_one + tail:
                 c()
-            comp_done.record(side)
-        for c in head:
+            return
+        side.wait_event(step_end)  # the previous step has read every row this step rewrites
+        for c in comp:
             c()
-        if comp:
-            main.wait_event(comp_done)
+        prolog()
+        side.wait_event(kv_ready)
+        for c in post:
+            c()
+        side_done.record(side)
+        main.wait_event(side_done)
         for c in tail:
             c()
         step_end.record(main)
@@ -962,7 +975,7 @@ def bench_v4_layer(args):
         "bytes_by_stage": bytes_by_stage,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
-        "streams": 2 if comp else 1,
+        "streams": 2 if use_side else 1,
         "outputs_match_one_stream": two_stream_identical,
     }
     print(json.dumps(rec), flush=True)

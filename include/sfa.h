@@ -518,10 +518,14 @@ typedef struct {
 } sfa_prolog_v4_dims;
 
 int sfa_mla_prolog_v4_workspace_size(const sfa_prolog_v4_dims* dims, size_t* bytes_out);
+/* kv_ready: NULL, or an event that the call records on `stream` as soon as kv and cq_out are
+ * complete, before the query up-projection (its longest launch): work that reads only kv or cq
+ * (the cache write of kv, the Indexer Prolog on cq) can wait for it on another stream and run
+ * beside the rest of the call. */
 int sfa_mla_prolog_v4(const sfa_prolog_v4_dims* dims, const void* x, const void* w_dq, const void* gamma_cq,
                       const void* w_uq, const void* w_dkv, const void* gamma_ckv, const int32_t* positions,
                       const float* rope_cos, const float* rope_sin, void* q, void* kv, void* cq_out,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+                      void* workspace, size_t workspace_bytes, hipEvent_t kv_ready, hipStream_t stream);
 
 /*
  * Indexer prolog: the new tokens' inputs of the Lightning Indexer ("CANN DeepSeek Indexer

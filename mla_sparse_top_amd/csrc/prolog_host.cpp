@@ -321,7 +321,7 @@ int sfa_mla_prolog_v4_workspace_size(const sfa_prolog_v4_dims* dims, size_t* byt
 int sfa_mla_prolog_v4(const sfa_prolog_v4_dims* dims, const void* x, const void* w_dq, const void* gamma_cq,
                       const void* w_uq, const void* w_dkv, const void* gamma_ckv, const int32_t* positions,
                       const float* rope_cos, const float* rope_sin, void* q, void* kv, void* cq_out,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      void* workspace, size_t workspace_bytes, hipEvent_t kv_ready, hipStream_t stream) {
   const int st = check_v4(dims);
   if (st != SFA_OK) return st;
   if (dims->tokens == 0) return SFA_OK;  // nothing to read or write; pointers may be NULL
@@ -405,6 +405,7 @@ int sfa_mla_prolog_v4(const sfa_prolog_v4_dims* dims, const void* x, const void*
   nm.rope_positions = dims->rope_positions;
   nm.kv_inside = 1;
   if (launch_prolog_norm(nm, stream) != hipSuccess) return SFA_ERR_HIP;
+  if (kv_ready && hipEventRecord(kv_ready, stream) != hipSuccess) return SFA_ERR_HIP;  // kv and cq final
 
   // 3. query up-projection over cq (hi and lo): fp32 sums per head channel
   PrologGemmArgs g2 = g;

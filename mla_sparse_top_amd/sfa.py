@@ -165,7 +165,7 @@ class SfaPrologV4Dims(ctypes.Structure):
 
 _lib.sfa_mla_prolog_v4_workspace_size.argtypes = [ctypes.POINTER(SfaPrologV4Dims), ctypes.POINTER(ctypes.c_size_t)]
 _lib.sfa_mla_prolog_v4_workspace_size.restype = ctypes.c_int
-_lib.sfa_mla_prolog_v4.argtypes = [ctypes.POINTER(SfaPrologV4Dims)] + [_vp] * 13 + [ctypes.c_size_t, _vp]
+_lib.sfa_mla_prolog_v4.argtypes = [ctypes.POINTER(SfaPrologV4Dims)] + [_vp] * 13 + [ctypes.c_size_t, _vp, _vp]
 _lib.sfa_mla_prolog_v4.restype = ctypes.c_int
 
 
@@ -992,7 +992,7 @@ def prolog_v4_workspace_size(dims: SfaPrologV4Dims) -> int:
 
 
 def _marshal_prolog_v4(x, w_dq, gamma_cq, w_uq, w_dkv, gamma_ckv, positions, rope_cos, rope_sin, eps, *,
-                       out=None, workspace=None, stream=None, cq_out=None):
+                       out=None, workspace=None, stream=None, cq_out=None, kv_ready=None):
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on a GPU device")
@@ -1028,9 +1028,10 @@ def _marshal_prolog_v4(x, w_dq, gamma_cq, w_uq, w_dkv, gamma_ckv, positions, rop
     args = (ctypes.byref(dims), _ptr(x), _ptr(w_dq), _ptr(gamma_cq), _ptr(w_uq), _ptr(w_dkv), _ptr(gamma_ckv),
             _ptr(positions), _ptr(rope_cos), _ptr(rope_sin), *[_ptr(o) for o in out], _ptr(cq_out),
             _ptr(workspace), ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
+            None if kv_ready is None else ctypes.c_void_p(_event_handle(kv_ready, stream)),
             ctypes.c_void_p(stream.cuda_stream))
     keep = (dims, x, w_dq, gamma_cq, w_uq, w_dkv, gamma_ckv, positions, rope_cos, rope_sin, out, cq_out, workspace,
-            stream)
+            kv_ready, stream)
     return args, out, keep
 
 
@@ -1072,8 +1073,17 @@ def run_prolog_v4(inp, d=None, *, out=None, cq_out=None):
     return mla_prolog_v4(*_prolog_v4_args(inp, d), out=out, cq_out=cq_out)
 
 
-def prepare_prolog_v4_run(inp, d, *, out=None, cq_out=None) -> PreparedCall:
-    args, out, keep = _marshal_prolog_v4(*_prolog_v4_args(inp, d), out=out, cq_out=cq_out)
+def _event_handle(ev, stream) -> int:
+    """The hipEvent_t of a torch.cuda.Event (recorded once on `stream` first if torch has not
+    created it yet)."""
+    if not ev.cuda_event:
+        ev.record(stream)
+    return ev.cuda_event
+
+
+def prepare_prolog_v4_run(inp, d, *, out=None, cq_out=None, kv_ready=None) -> PreparedCall:
+    """kv_ready: a torch.cuda.Event the call records once kv and cq_out are complete, or None."""
+    args, out, keep = _marshal_prolog_v4(*_prolog_v4_args(inp, d), out=out, cq_out=cq_out, kv_ready=kv_ready)
     return PreparedCall([(_lib.sfa_mla_prolog_v4, args, "sfa_mla_prolog_v4")], out, keep)
 
 
@@ -1171,5 +1181,5 @@ def run_indexer_prolog(inp, d=None, *, out=None):
     return indexer_prolog(*_indexer_prolog_args(inp, d), rotate=inp.rotate, out=out)
 
 
-def prepare_indexer_prolog_run(inp, d, *, out=None) -> PreparedCall:
-    return prepare_indexer_prolog(*_indexer_prolog_args(inp, d), rotate=inp.rotate, out=out)
+def prepare_indexer_prolog_run(inp, d, *, out=None, stream=None) -> PreparedCall:
+    return prepare_indexer_prolog(*_indexer_prolog_args(inp, d), rotate=inp.rotate, out=out, stream=stream)

@@ -471,7 +471,7 @@ def _v4_call(d, over=None, ws=0x7000000000, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = sfa.prolog_v4_workspace_size(d)
     return sfa._lib.sfa_mla_prolog_v4(ctypes.byref(d), *[vp(p[n]) if p[n] is not None else None for n in names],
-                                      vp(ws) if ws else None, ctypes.c_size_t(ws_bytes), None)
+                                      vp(ws) if ws else None, ctypes.c_size_t(ws_bytes), None, None)
 
 
 def test_prolog_v4_workspace():
