@@ -218,3 +218,29 @@ def test_v4_feeds_cache_write_and_512_wide_swa(sfa_lib):
     ref = WO.window_attention(win)
     rep = O.allclose_report(out.float().cpu().numpy().astype(np.float64).reshape(ref.shape), ref)
     assert rep["fails"] == 0, rep
+
+
+def test_v4_kv_ready_event(sfa_lib):
+    """The optional event is recorded once kv and cq are final: a second stream that waits for it
+    copies them while the call's up-projection may still run, and the copies equal the finished
+    outputs; q is unaffected (every element checked against the oracle)."""
+    import torch
+
+    inp = W.prolog_v4_generate(tokens=150, n_q=8, hidden=512, q_lora_rank=256,
+                               positions=[(5 * t) % 300 for t in range(150)], rope_positions=256, seed=9)
+    d = sfa_lib.prolog_v4_to_device(inp)
+    cq = torch.empty((inp.tokens, inp.q_lora_rank), dtype=torch.bfloat16, device="cuda")
+    ev = torch.cuda.Event()
+    side = torch.cuda.Stream()
+    call = sfa_lib.prepare_prolog_v4_run(inp, d, cq_out=cq, kv_ready=ev)
+    q, kv = call.out
+    for _ in range(2):
+        call()
+        side.wait_event(ev)
+        with torch.cuda.stream(side):
+            kv_early, cq_early = kv.clone(), cq.clone()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(kv_early.view(torch.int16), kv.view(torch.int16))
+        assert torch.equal(cq_early.view(torch.int16), cq.view(torch.int16))
+    _assert_close_v4(inp, (q, kv))
